@@ -1,0 +1,281 @@
+"""CPU oracle for block-wise dynamic quantization and the 8-bit AdamW step.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg import this package.  It shares no code with the HIP library
+(`bit_optimizer_states_amd`), and neither imports the other.
+
+The arithmetic lives in `oracle.c` (plain C, one thread, every binary32 operation
+rounded on its own); this module marshals numpy arrays and holds the two steps
+that are clearest in exact integer arithmetic: exact rounding of a rational to
+binary32 and the exact mean used by nested quantization.
+
+Every array argument is a numpy array on the host.  bfloat16 / float16 data
+travel as uint16 bit patterns.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+DYN8, NF4, FP4 = 0, 1, 2
+F32, F16, BF16 = 0, 1, 2
+CODE_SIZE = {DYN8: 256, NF4: 16, FP4: 16}
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, building it from oracle.c if it is missing or stale."""
+    global _lib
+    if _lib is None:
+        path = _build.build(force=False)
+        L = ctypes.CDLL(path)
+        i64, i32, vp, fp, dp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_double
+        sig = {
+            "orc_dyn8_codebook": [vp],
+            "orc_nf4_codebook": [vp],
+            "orc_fp4_codebook": [vp],
+            "orc_encode": [i32, vp, i64, vp],
+            "orc_quantize_blockwise": [vp, i32, i64, i32, i32, vp, vp],
+            "orc_dequantize_blockwise": [vp, vp, i32, i32, i64, vp, i32],
+            "orc_dq_quantize": [vp, i64, fp, i32, vp, vp],
+            "orc_dq_decode": [vp, vp, fp, i32, i64, vp],
+            "orc_adamw32_step": [vp, vp, i32, i64, vp, vp, dp, dp, dp, dp, dp, i32],
+            "orc_adamw8bit_step": [vp, vp, i32, i64, vp, vp, vp, vp, i32, dp, dp, dp, dp, dp, i32],
+            "orc_adam_scalars": [dp, dp, dp, dp, dp, i32, vp],
+        }
+        for name, argtypes in sig.items():
+            f = getattr(L, name)
+            f.argtypes = argtypes
+            f.restype = ctypes.c_int
+        L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_f16_to_f32.restype = ctypes.c_float
+        L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_bf16.restype = ctypes.c_uint16
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_id(a):
+    """numpy dtype of an element array -> oracle dtype id; uint16 arrays are
+    ambiguous, so callers pass the id explicitly for them."""
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError("pass float16/bfloat16 data as uint16 bits with an explicit dtype id")
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed ({rc})")
+
+
+# --------------------------------------------------------------------------
+# codebooks and encoder
+# --------------------------------------------------------------------------
+
+def codebook(code):
+    """Decode table indexed by the stored code (DYN8: 256, NF4/FP4: 16 entries)."""
+    out = np.zeros(CODE_SIZE[code], dtype=np.float32)
+    fn = {DYN8: lib().orc_dyn8_codebook, NF4: lib().orc_nf4_codebook, FP4: lib().orc_fp4_codebook}[code]
+    _check(fn(_p(out)), "codebook")
+    return out
+
+
+def encode(code, x):
+    """Nearest code of every value of x (float32), ties toward zero."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(x.size, dtype=np.uint8)
+    _check(lib().orc_encode(code, _p(x), x.size, _p(out)), "encode")
+    return out
+
+
+# --------------------------------------------------------------------------
+# block-wise quantize / dequantize
+# --------------------------------------------------------------------------
+
+def packed_len(code, n):
+    return (n + 1) // 2 if code in (NF4, FP4) else n
+
+
+def quantize_blockwise(x, code, blocksize, xdt=None):
+    """x: float32 array, or uint16 bits with xdt in (F16, BF16).
+    Returns (codes uint8, absmax float32[ceil(n/B)])."""
+    x = np.ascontiguousarray(x)
+    if xdt is None:
+        xdt = _dtype_id(x)
+    n = x.size
+    nb = (n + blocksize - 1) // blocksize
+    codes = np.zeros(packed_len(code, n), dtype=np.uint8)
+    absmax = np.zeros(nb, dtype=np.float32)
+    _check(lib().orc_quantize_blockwise(_p(x), xdt, n, code, blocksize, _p(codes), _p(absmax)), "quantize")
+    return codes, absmax
+
+
+def dequantize_blockwise(codes, scale, code, blocksize, n, ydt=F32):
+    """Returns float32 (ydt=F32) or uint16 bits (F16/BF16) of length n."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    y = np.zeros(n, dtype=np.float32 if ydt == F32 else np.uint16)
+    _check(lib().orc_dequantize_blockwise(_p(codes), _p(scale), code, blocksize, n, _p(y), ydt), "dequantize")
+    return y
+
+
+# --------------------------------------------------------------------------
+# exact rounding and the exact mean of nested quantization
+# --------------------------------------------------------------------------
+
+def _scaled(num, den, e):
+    """num / (den * 2^e) as an exact pair (numerator, denominator) of integers."""
+    return (num << -e, den) if e < 0 else (num, den << e)
+
+
+def rn32_rational(num, den):
+    """Round the non-negative rational num/den to the nearest binary32
+    (ties to even), exactly, with Python integers.  Result as np.float32."""
+    num, den = int(num), int(den)
+    if num < 0 or den <= 0:
+        raise ValueError("non-negative rational expected")
+    if num == 0:
+        return np.float32(0.0)
+    # Pick e with 2^23 <= num / (den * 2^e) < 2^24: q = floor of that is a 24-bit
+    # significand and the result is q * 2^e after rounding.
+    e = num.bit_length() - den.bit_length() - 24
+    while True:
+        a, b = _scaled(num, den, e)
+        if a >= (b << 24):
+            e += 1
+        elif a < (b << 23):
+            e -= 1
+        else:
+            break
+    e = max(e, -149)                     # subnormal range: the quantum stays 2^-149
+    a, b = _scaled(num, den, e)
+    q, r = divmod(a, b)
+    if 2 * r > b or (2 * r == b and (q & 1)):
+        q += 1
+    if e + q.bit_length() > 128:
+        raise OverflowError("value overflows binary32")
+    return np.float32(np.ldexp(np.float64(q), e))   # q <= 2^24, e >= -149: exact
+
+
+def exact_mean_f32(a):
+    """Mean of non-negative finite binary32 values, computed exactly and rounded
+    once to binary32.
+
+    Reading (nested quantization centres the absmax values on their mean; the
+    pages give no precision): the exact rational sum / count, rounded to the
+    nearest binary32.  Every value is m * 2^(e-150) with an integer significand
+    m < 2^24, so the sum is an exact integer multiple of 2^-149; significands are
+    summed per exponent in int64 (exact) and combined with Python integers."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    nb = a.size
+    if nb == 0:
+        return np.float32(0.0)
+    bits = a.view(np.uint32).astype(np.int64)
+    if np.any(bits >> 31):
+        raise ValueError("absmax values must be non-negative")
+    ex = (bits >> 23) & 0xFF
+    if np.any(ex == 0xFF):
+        raise ValueError("absmax values must be finite")
+    man = np.where(ex > 0, (bits & 0x7FFFFF) | 0x800000, bits & 0x7FFFFF)
+    ex = np.maximum(ex, 1)                      # value = man * 2^(ex - 150)
+    total = 0                                   # sum scaled by 2^149
+    for e in np.unique(ex):
+        total += int(man[ex == e].sum()) << int(e - 1)
+    return rn32_rational(total, nb << 149)
+
+
+# --------------------------------------------------------------------------
+# nested (double) quantization
+# --------------------------------------------------------------------------
+
+def dq_quantize(absmax, blocksize2=256):
+    """Nested quantization of fp32 absmax: returns (c2 uint8[nb], absmax2, mu)."""
+    absmax = np.ascontiguousarray(absmax, dtype=np.float32)
+    nb = absmax.size
+    mu = exact_mean_f32(absmax)
+    c2 = np.zeros(nb, dtype=np.uint8)
+    a2 = np.zeros((nb + blocksize2 - 1) // blocksize2, dtype=np.float32)
+    _check(lib().orc_dq_quantize(_p(absmax), nb, ctypes.c_float(mu), blocksize2, _p(c2), _p(a2)), "dq_quantize")
+    return c2, a2, mu
+
+
+def dq_decode(c2, absmax2, mu, blocksize2=256):
+    c2 = np.ascontiguousarray(c2, dtype=np.uint8)
+    absmax2 = np.ascontiguousarray(absmax2, dtype=np.float32)
+    out = np.zeros(c2.size, dtype=np.float32)
+    _check(lib().orc_dq_decode(_p(c2), _p(absmax2), ctypes.c_float(mu), blocksize2, c2.size, _p(out)), "dq_decode")
+    return out
+
+
+def quantize(x, code, blocksize, xdt=None, double_quant=False, blocksize2=256):
+    """Full quantize: codes, and either absmax (no nesting) or the nested state
+    dict(c2, absmax2, mu, absmax_fp32)."""
+    codes, absmax = quantize_blockwise(x, code, blocksize, xdt)
+    if not double_quant:
+        return codes, absmax
+    c2, a2, mu = dq_quantize(absmax, blocksize2)
+    return codes, {"c2": c2, "absmax2": a2, "mu": mu, "absmax_fp32": absmax}
+
+
+def dequantize(codes, state, code, blocksize, n, ydt=F32, blocksize2=256):
+    """Inverse of quantize(); state is absmax or the nested dict."""
+    if isinstance(state, dict):
+        scale = dq_decode(state["c2"], state["absmax2"], state["mu"], blocksize2)
+    else:
+        scale = state
+    return dequantize_blockwise(codes, scale, code, blocksize, n, ydt)
+
+
+# --------------------------------------------------------------------------
+# AdamW
+# --------------------------------------------------------------------------
+
+def adam_scalars(lr, beta1, beta2, eps, wd, step):
+    out = np.zeros(8, dtype=np.float32)
+    _check(lib().orc_adam_scalars(lr, beta1, beta2, eps, wd, step, _p(out)), "adam_scalars")
+    return dict(zip(["b1", "ob1", "b2", "ob2", "s1", "s2", "dec", "eps"], out))
+
+
+def adamw32_step(p, g, m, v, lr, beta1, beta2, eps, wd, step, gdt=None):
+    """In-place AdamW step with binary32 state (p, m, v float32 arrays)."""
+    if gdt is None:
+        gdt = _dtype_id(g)
+    _check(lib().orc_adamw32_step(_p(p), _p(g), gdt, p.size, _p(m), _p(v),
+                                  lr, beta1, beta2, eps, wd, step), "adamw32")
+
+
+def adamw8bit_step(p, g, cm, cv, am, av, blocksize, lr, beta1, beta2, eps, wd, step, gdt=None):
+    """In-place 8-bit AdamW step: p float32, g float32 (or uint16 bits with gdt),
+    cm/cv uint8 codes, am/av float32 block absmax."""
+    for arr, dt in ((p, np.float32), (cm, np.uint8), (cv, np.uint8), (am, np.float32), (av, np.float32)):
+        if arr.dtype != dt or not arr.flags.c_contiguous:
+            raise TypeError("contiguous arrays of the documented dtypes expected")
+    if gdt is None:
+        gdt = _dtype_id(g)
+    g = np.ascontiguousarray(g)
+    _check(lib().orc_adamw8bit_step(_p(p), _p(g), gdt, p.size, _p(cm), _p(cv), _p(am), _p(av), blocksize,
+                                    lr, beta1, beta2, eps, wd, step), "adamw8bit")
+
+
+def f32_to_bf16_bits(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return np.array([lib().orc_f32_to_bf16(float(v)) for v in x], dtype=np.uint16)
+
+
+def f32_to_f16_bits(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return np.array([lib().orc_f32_to_f16(float(v)) for v in x], dtype=np.uint16)
+
+
+def f16_bits_to_f32(h):
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    return np.array([lib().orc_f16_to_f32(int(v)) for v in h], dtype=np.float32)
