@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-wise quantization hot path on one MI355X.
+
+One step = one pass of the whole hot path over synthetic inputs resident in HBM:
+  1. one fused 8-bit AdamW step over a 7B decoder's 291 fp32 parameter tensors
+     (6,738,415,616 parameters; bf16 gradients ~N(0, 1e-3), the embedding's
+     gradient non-zero on a seeded 10% of its rows; int8 moments on the dynamic
+     code; block size 2048) in ONE multi-tensor launch;
+  2. 4-bit NF4 block-wise quantization (block 64) with nested quantization of
+     the absmax (dynamic 8-bit code, block 256) of the 225 fp16 weight
+     matrices of the same decoder (6,607,077,376 weights ~N(0, 0.02));
+  3. dequantization of those 225 NF4 tensors to bf16.
+Two gradient sets alternate between steps (generated before timing).
+
+Prints one JSON line (rank 0).  `value` is the whole step's algorithmic
+traffic divided by its time; the per-part figures (AdamW GB/s and params/s,
+4-bit dequantize GB/s) are under "components"; "roofline" reports the
+dominant kernel (the multi-tensor AdamW step) against the 8 TB/s HBM peak.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused AdamW8bit step GB/s + params/s; 4-bit dequant GB/s (% of HBM peak)"
+HBM_PEAK_GBS = 8000.0
+ADAM_BLOCK = 2048
+W4_BLOCK, W4_BLOCK2 = 64, 256
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw8bit_multi_7b.traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def adam_bytes_per_param(grad_bytes=2, block=ADAM_BLOCK):
+    # p read+write (8), grad read, m and v codes read+write (4), absmax m and v read+write per block
+    return 8 + grad_bytes + 4 + 16.0 / block
+
+
+def w4_bytes_per_weight():
+    # dequantize: packed codes (0.5), nested codes (1/64), second absmax (4/(64*256)), bf16 out (2)
+    return 0.5 + 1.0 / W4_BLOCK + 4.0 / (W4_BLOCK * W4_BLOCK2) + 2.0
+
+
+def q4_bytes_per_weight():
+    # quantize: fp16 in (2), packed codes (0.5), nested codes and second absmax out
+    return 2.0 + 0.5 + 1.0 / W4_BLOCK + 4.0 / (W4_BLOCK * W4_BLOCK2)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_optimizer_states_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()
+
+
+def traffic_per_launch():
+    """HBM bytes per AdamW launch from the committed counter summary, or None if
+    it is missing or the kernel sources changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Model7B:
+    """Device state of the multi-tensor AdamW step and the 4-bit sweep."""
+
+    def __init__(self, torch, qb, inputs, dev, seed, with_w4=True, grad_sets=2):
+        self.t = torch
+        shapes = inputs.llama7b_param_shapes()
+        self.names = [s[0] for s in shapes]
+        self.sizes = [int(np.prod(s[1])) for s in shapes]
+        self.params = []
+        self.grads = [[] for _ in range(grad_sets)]
+        log(f"allocating {len(shapes)} parameter tensors ({sum(self.sizes):,} params)")
+        for i, (name, shape) in enumerate(shapes):
+            n = self.sizes[i]
+            nb = (n + ADAM_BLOCK - 1) // ADAM_BLOCK
+            p = inputs.normal(n, 0.02, seed=seed * 1000 + i, device=dev)
+            m = torch.full((n,), 127, dtype=torch.uint8, device=dev)
+            v = torch.full((n,), 127, dtype=torch.uint8, device=dev)
+            am = torch.zeros(nb, dtype=torch.float32, device=dev)
+            av = torch.zeros(nb, dtype=torch.float32, device=dev)
+            self.params.append((p, m, v, am, av))
+            for k in range(grad_sets):
+                gs = inputs.grad_seed(seed, i, k)
+                if name == "embed":
+                    g = inputs.sparse_row_grad(shape[0], shape[1], 0.10, 1e-3, gs, device=dev).reshape(-1)
+                else:
+                    g = inputs.normal(n, 1e-3, gs, device=dev, dtype=torch.bfloat16)
+                self.grads[k].append(g)
+        self.tables = [qb.tensor_table([(p, g, m, v, am, av) for (p, m, v, am, av), g in zip(self.params, gset)])
+                       for gset in self.grads]
+        self.ws = torch.empty(qb.qb_multi_tensor_workspace_bytes(len(shapes)), dtype=torch.uint8, device=dev)
+        self.n_params = sum(self.sizes)
+        self.w4 = []
+        if with_w4:
+            wshapes = inputs.llama7b_weight_shapes()
+            log(f"allocating {len(wshapes)} fp16 weight tensors for the 4-bit sweep")
+            wsmax = 0
+            for j, (name, shape) in enumerate(wshapes):
+                n = int(np.prod(shape))
+                nb = (n + W4_BLOCK - 1) // W4_BLOCK
+                w = inputs.normal(n, 0.02, seed=seed * 7919 + j, device=dev, dtype=torch.float16)
+                codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev)
+                c2 = torch.empty(nb, dtype=torch.uint8, device=dev)
+                a2 = torch.empty((nb + W4_BLOCK2 - 1) // W4_BLOCK2, dtype=torch.float32, device=dev)
+                off = torch.empty(4, dtype=torch.float32, device=dev)
+                y = torch.empty(n, dtype=torch.bfloat16, device=dev)
+                self.w4.append((n, w, codes, c2, a2, off, y))
+                wsmax = max(wsmax, qb.qb_dq_workspace_bytes(n, W4_BLOCK))
+            self.w4_ws = torch.empty(wsmax, dtype=torch.uint8, device=dev)
+            self.dq_q = [qb.make_dq(c2, a2, off, W4_BLOCK2, self.w4_ws) for (_, _, _, c2, a2, off, _) in self.w4]
+            self.dq_d = [qb.make_dq(c2, a2, off, W4_BLOCK2) for (_, _, _, c2, a2, off, _) in self.w4]
+        self.n_w4 = sum(e[0] for e in self.w4)
+
+
+def run_adam(qb, model, step):
+    table = model.tables[(step - 1) % len(model.tables)]
+    qb.qb_multi_tensor_step(table, len(table), qb.QB_BF16, ADAM_BLOCK, qb.hparams(step=step, **HP), model.ws)
+
+
+def run_q4(qb, model):
+    for (n, w, codes, *_), dq in zip(model.w4, model.dq_q):
+        qb.qb_quantize(w, n, qb.QB_NF4, W4_BLOCK, codes, None, dq)
+
+
+def run_dq4(qb, model):
+    for (n, _, codes, _, _, _, y), dq in zip(model.w4, model.dq_d):
+        qb.qb_dequantize(codes, None, dq, qb.QB_NF4, W4_BLOCK, n, y)
+
+
+def cpu_baseline(torch, model, seconds_target, rng):
+    """The oracle, single-threaded, on a bounded sample of the same workload:
+    seeded full AdamW blocks of the 7B model (copied from the device) plus one
+    4096x11008 weight quantized (NF4 + nested) and dequantized to bf16."""
+    import oracle
+    nblocks = 65536
+    # sample full blocks in proportion to the tensors' block counts
+    full_blocks = np.array([n // ADAM_BLOCK for n in model.sizes], dtype=np.int64)
+    prob = full_blocks / full_blocks.sum()
+    tensor_of = rng.choice(len(model.sizes), size=nblocks, p=prob)
+    ps, gs, ms, vs, ams, avs = [], [], [], [], [], []
+    for ti in np.unique(tensor_of):
+        k = int(np.sum(tensor_of == ti))
+        blk = torch.from_numpy(rng.choice(full_blocks[ti], size=k, replace=False)).to(model.params[ti][0].device)
+        p, m, v, am, av = model.params[ti]
+        g = model.grads[0][ti]
+        B = ADAM_BLOCK
+        ps.append(p[: full_blocks[ti] * B].view(-1, B).index_select(0, blk).cpu().numpy().reshape(-1))
+        gs.append(g[: full_blocks[ti] * B].view(-1, B).index_select(0, blk).view(torch.int16).cpu().numpy()
+                  .view(np.uint16).reshape(-1))
+        ms.append(m[: full_blocks[ti] * B].view(-1, B).index_select(0, blk).cpu().numpy().reshape(-1))
+        vs.append(v[: full_blocks[ti] * B].view(-1, B).index_select(0, blk).cpu().numpy().reshape(-1))
+        ams.append(am.index_select(0, blk).cpu().numpy())
+        avs.append(av.index_select(0, blk).cpu().numpy())
+    p, g, m, v, am, av = (np.ascontiguousarray(np.concatenate(a)) for a in (ps, gs, ms, vs, ams, avs))
+    n_adam = p.size
+    t0 = time.perf_counter()
+    oracle.adamw8bit_step(p, g, m, v, am, av, ADAM_BLOCK, lr=HP["lr"], beta1=HP["beta1"], beta2=HP["beta2"],
+                          eps=HP["eps"], wd=HP["weight_decay"], step=3, gdt=oracle.BF16)
+    t_adam = time.perf_counter() - t0
+    n4 = 4096 * 11008
+    w = next(e[1] for e in model.w4 if e[0] == n4).cpu().view(torch.int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    codes, st = oracle.quantize(w, oracle.NF4, W4_BLOCK, xdt=oracle.F16, double_quant=True)
+    t_q4 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.dequantize(codes, st, oracle.NF4, W4_BLOCK, n4, oracle.BF16)
+    t_d4 = time.perf_counter() - t0
+    total_bytes = n_adam * adam_bytes_per_param() + n4 * (q4_bytes_per_weight() + w4_bytes_per_weight())
+    total_t = t_adam + t_q4 + t_d4
+    return {
+        "value": total_bytes / total_t / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{nblocks} seeded full 2048-element AdamW blocks of the 7B model ({n_adam:,} params, "
+                   f"{t_adam:.2f} s) + NF4 nested quantize ({t_q4:.2f} s) and bf16 dequantize ({t_d4:.2f} s) "
+                   f"of one 4096x11008 fp16 weight; single-threaded C oracle"),
+        "adamw_params_per_s": n_adam / t_adam,
+        "dequant4_GBps": n4 * w4_bytes_per_weight() / t_d4 / 1e9,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=2024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--adam-only", action="store_true", help="time only the multi-tensor AdamW step")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from bit_optimizer_states_amd import binding as qb
+    from bit_optimizer_states_amd import inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    qb.lib()
+    dev = "cuda:0"
+    rng = np.random.default_rng(args.seed)
+    model = Model7B(torch, qb, inputs, dev, args.seed, with_w4=not args.adam_only)
+    torch.cuda.synchronize()
+    log(f"setup done; warmup {args.warmup} steps")
+
+    def step(k, ev=None):
+        if ev is not None:
+            ev[0].record()
+        run_adam(qb, model, k)
+        if ev is not None:
+            ev[1].record()
+        if not args.adam_only:
+            run_q4(qb, model)
+            if ev is not None:
+                ev[2].record()
+            run_dq4(qb, model)
+            if ev is not None:
+                ev[3].record()
+
+    for k in range(1, args.warmup + 1):
+        step(k)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + 1 + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed region done")
+
+    adam_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    adam_bytes = model.n_params * adam_bytes_per_param()
+    comps = {"adamw8bit_multi_tensor": {
+        "ms": adam_ms, "GB/s": adam_bytes / adam_ms / 1e6, "params_per_s": model.n_params / adam_ms * 1e3,
+        "frac_of_hbm_peak": adam_bytes / adam_ms / 1e6 / HBM_PEAK_GBS, "launches_per_step": 1}}
+    step_bytes = adam_bytes
+    if not args.adam_only:
+        q4_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        d4_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        q4_bytes = model.n_w4 * q4_bytes_per_weight()
+        d4_bytes = model.n_w4 * w4_bytes_per_weight()
+        comps["quantize4_nf4_nested"] = {"ms": q4_ms, "GB/s": q4_bytes / q4_ms / 1e6,
+                                         "frac_of_hbm_peak": q4_bytes / q4_ms / 1e6 / HBM_PEAK_GBS,
+                                         "launches_per_step": 3 * len(model.w4)}
+        comps["dequant4_nf4_nested_bf16"] = {"ms": d4_ms, "GB/s": d4_bytes / d4_ms / 1e6,
+                                             "frac_of_hbm_peak": d4_bytes / d4_ms / 1e6 / HBM_PEAK_GBS,
+                                             "launches_per_step": len(model.w4)}
+        step_bytes += q4_bytes + d4_bytes
+    ms_per_step = wall / args.steps * 1e3
+    traffic = traffic_per_launch()
+    achieved = adam_bytes / adam_ms / 1e6
+    out = {
+        "metric": METRIC,
+        "value": step_bytes / ms_per_step / 1e6,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("7B decoder (291 tensors, 6,738,415,616 fp32 params, bf16 grads, 10% sparse embedding "
+                         "rows): one multi-tensor fused AdamW8bit step, block 2048" +
+                         ("" if args.adam_only else
+                          "; + NF4 nested quantize and bf16 dequantize of its 225 fp16 weights "
+                          "(6,607,077,376), block 64 / 256")),
+            "params": model.n_params,
+            "weights_4bit": model.n_w4,
+            "adam_blocksize": ADAM_BLOCK,
+            "w4_blocksize": W4_BLOCK,
+            "w4_blocksize2": W4_BLOCK2,
+            "parallelism": "single GPU",
+        },
+        "components": comps,
+        "roofline": {
+            "kernel": "k_adamw8<2048, bf16, multi-tensor>",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": adam_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(torch, model, 10.0, rng)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

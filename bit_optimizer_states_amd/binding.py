@@ -1,0 +1,175 @@
+"""ctypes binding of libqb (include/qb.h): same names, argument marshalling only.
+
+Device buffers are torch tensors (contiguous, on the GPU); the binding passes
+their data pointers and the current HIP stream of torch, checks the returned
+status and raises `QbError` on anything but QB_OK.  Every computation runs in
+the library's kernels; nothing here computes on the CPU.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqb.so")
+
+QB_OK, QB_EINVAL, QB_EALIGN, QB_EUNSUPPORTED, QB_EHIP, QB_EWORKSPACE, QB_EINIT = range(7)
+QB_F32, QB_F16, QB_BF16 = 0, 1, 2
+QB_DYN8, QB_NF4, QB_FP4 = 0, 1, 2
+
+_DTYPE = {torch.float32: QB_F32, torch.float16: QB_F16, torch.bfloat16: QB_BF16}
+
+
+class QbError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {qb_status_string(status)} ({status})")
+
+
+class qb_dq(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("absmax2", ctypes.c_void_p), ("offset", ctypes.c_void_p),
+                ("blocksize2", ctypes.c_int32), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+class qb_adamw_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int32)]
+
+
+class qb_tensor(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_void_p), ("g", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("absmax_m", ctypes.c_void_p), ("absmax_v", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libqb.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} is missing: build it with bit_optimizer_states_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.qb_quantize.argtypes = [vp, i32, i64, i32, i32, vp, vp, ctypes.POINTER(qb_dq), vp]
+        L.qb_dequantize.argtypes = [vp, vp, ctypes.POINTER(qb_dq), i32, i32, i64, vp, i32, vp]
+        L.qb_adamw8bit_step.argtypes = [vp, vp, i32, i64, vp, vp, vp, vp, i32, ctypes.POINTER(qb_adamw_hparams), vp]
+        L.qb_multi_tensor_step.argtypes = [ctypes.POINTER(qb_tensor), i32, i32, i32, ctypes.POINTER(qb_adamw_hparams),
+                                           vp, sz, vp]
+        for f in (L.qb_quantize, L.qb_dequantize, L.qb_adamw8bit_step, L.qb_multi_tensor_step):
+            f.restype = ctypes.c_int
+        L.qb_dq_workspace_bytes.argtypes = [i64, i32]
+        L.qb_dq_workspace_bytes.restype = sz
+        L.qb_multi_tensor_workspace_bytes.argtypes = [i32]
+        L.qb_multi_tensor_workspace_bytes.restype = sz
+        L.qb_codebook.argtypes = [i32, vp]
+        L.qb_codebook.restype = i32
+        L.qb_encoder_table.argtypes = [i32, vp, i32]
+        L.qb_encoder_table.restype = i32
+        L.qb_status_string.argtypes = [ctypes.c_int]
+        L.qb_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Data pointer of a device tensor, or None."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("torch tensor expected")
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status, where):
+    if status != QB_OK:
+        raise QbError(status, where)
+
+
+def _dtype(t):
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def qb_status_string(status):
+    return lib().qb_status_string(int(status)).decode()
+
+
+def qb_dq_workspace_bytes(n, blocksize):
+    return lib().qb_dq_workspace_bytes(int(n), int(blocksize))
+
+
+def qb_multi_tensor_workspace_bytes(count):
+    return lib().qb_multi_tensor_workspace_bytes(int(count))
+
+
+def make_dq(codes, absmax2, offset, blocksize2, ws=None):
+    """qb_dq from device tensors (ws may be None for dequantize)."""
+    return qb_dq(_ptr(codes), _ptr(absmax2), _ptr(offset), int(blocksize2), _ptr(ws),
+                 0 if ws is None else ws.numel() * ws.element_size())
+
+
+def qb_quantize(x, n, code, blocksize, codes, absmax=None, dq=None, stream=None):
+    _check(lib().qb_quantize(_ptr(x), _dtype(x), int(n), int(code), int(blocksize), _ptr(codes), _ptr(absmax),
+                             ctypes.byref(dq) if dq is not None else None, _stream(stream)), "qb_quantize")
+
+
+def qb_dequantize(codes, absmax, dq, code, blocksize, n, y, stream=None):
+    _check(lib().qb_dequantize(_ptr(codes), _ptr(absmax), ctypes.byref(dq) if dq is not None else None, int(code),
+                               int(blocksize), int(n), _ptr(y), _dtype(y), _stream(stream)), "qb_dequantize")
+
+
+def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1):
+    return qb_adamw_hparams(lr, beta1, beta2, eps, weight_decay, int(step))
+
+
+def qb_adamw8bit_step(p, g, n, m, v, absmax_m, absmax_v, blocksize, hp, stream=None):
+    _check(lib().qb_adamw8bit_step(_ptr(p), _ptr(g), _dtype(g), int(n), _ptr(m), _ptr(v), _ptr(absmax_m),
+                                   _ptr(absmax_v), int(blocksize), ctypes.byref(hp), _stream(stream)),
+           "qb_adamw8bit_step")
+
+
+def tensor_table(tensors):
+    """ctypes array of qb_tensor from tuples (p, g, m, v, absmax_m, absmax_v)."""
+    arr = (qb_tensor * len(tensors))()
+    for i, (p, g, m, v, am, av) in enumerate(tensors):
+        arr[i] = qb_tensor(_ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(am), _ptr(av), p.numel())
+    return arr
+
+
+def qb_multi_tensor_step(table, count, gdt, blocksize, hp, ws, stream=None):
+    """table: result of tensor_table(); gdt: QB_F32/QB_F16/QB_BF16; ws: device byte tensor."""
+    _check(lib().qb_multi_tensor_step(table, int(count), int(gdt), int(blocksize), ctypes.byref(hp), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)), "qb_multi_tensor_step")
+
+
+def qb_codebook(code):
+    """Host decode table of `code` as a list of floats."""
+    out = (ctypes.c_float * 256)()
+    k = lib().qb_codebook(int(code), out)
+    if k < 0:
+        raise QbError(QB_EINIT, "qb_codebook")
+    return list(out[:k])
+
+
+def qb_encoder_table(code):
+    """Host encoder bucket table as a list of (threshold bits, payload) pairs."""
+    k = lib().qb_encoder_table(int(code), None, 0)
+    if k < 0:
+        raise QbError(QB_EINIT, "qb_encoder_table")
+    out = (ctypes.c_uint32 * (2 * k))()
+    lib().qb_encoder_table(int(code), out, k)
+    return [(out[2 * i], out[2 * i + 1]) for i in range(k)]

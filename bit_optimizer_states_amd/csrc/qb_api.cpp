@@ -1,0 +1,275 @@
+// qb_api.cpp -- the C ABI declared in include/qb.h: argument validation, host
+// scalars, workspace layout and kernel dispatch.  Nothing is enqueued unless
+// every argument checks out.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "qb.h"
+#include "qb_launch.h"
+#include "qb_tables.h"
+
+namespace {
+
+using namespace qb;
+
+bool pow2_block(int32_t b) { return b >= 64 && b <= 4096 && (b & (b - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(qb_dtype d) { return d == QB_F32 || d == QB_F16 || d == QB_BF16; }
+bool valid_code(qb_code c) { return c == QB_DYN8 || c == QB_NF4 || c == QB_FP4; }
+bool is4(qb_code c) { return c == QB_NF4 || c == QB_FP4; }
+int code4_index(qb_code c) { return c == QB_NF4 ? 0 : 1; }
+int64_t nblocks(int64_t n, int32_t b) { return (n + b - 1) / b; }
+
+qb_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return QB_OK;
+    if (e == hipErrorNotInitialized) return QB_EINIT;
+    return QB_EHIP;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Checks shared by quantize and dequantize for the nested state.
+qb_status check_dq(const qb_dq* dq, int64_t nb, bool need_ws)
+{
+    if (!dq->codes || !dq->absmax2 || !dq->offset) return QB_EINVAL;
+    if (!pow2_block(dq->blocksize2)) return QB_EINVAL;
+    if (!aligned16(dq->codes) || !aligned16(dq->absmax2) || !aligned16(dq->offset)) return QB_EALIGN;
+    if (nb >= (int64_t(1) << 31)) return QB_EINVAL;
+    if (need_ws) {
+        if (!dq->ws) return QB_EINVAL;
+        if (!aligned16(dq->ws)) return QB_EALIGN;
+        if (dq->ws_bytes < kBinBytes + round_up((size_t)nb * sizeof(float), 256)) return QB_EWORKSPACE;
+    }
+    return QB_OK;
+}
+
+bool valid_hparams(const qb_adamw_hparams* hp)
+{
+    if (!hp) return false;
+    auto finite = [](double v) { return std::isfinite(v); };
+    return finite(hp->lr) && hp->lr >= 0 && finite(hp->weight_decay) && hp->weight_decay >= 0 &&
+           hp->beta1 >= 0 && hp->beta1 < 1 && hp->beta2 >= 0 && hp->beta2 < 1 && finite(hp->eps) &&
+           hp->eps > 0 && hp->step >= 1;
+}
+
+// beta^t by t repeated binary64 multiplications.  Consecutive steps of the
+// same beta reuse the previous power, so a training loop pays one multiply.
+double beta_power(double beta, int32_t t, int slot)
+{
+    thread_local double last_beta[2] = {-1.0, -1.0};
+    thread_local int32_t last_t[2] = {0, 0};
+    thread_local double last_pow[2] = {1.0, 1.0};
+    double p;
+    int32_t k;
+    if (last_beta[slot] == beta && last_t[slot] <= t) {
+        p = last_pow[slot];
+        k = last_t[slot];
+    } else {
+        p = 1.0;
+        k = 0;
+    }
+    for (; k < t; ++k) p *= beta;
+    last_beta[slot] = beta;
+    last_t[slot] = t;
+    last_pow[slot] = p;
+    return p;
+}
+
+// Per-element scalars: computed in binary64, each rounded once to binary32.
+AdamScalars prepare(const qb_adamw_hparams& hp)
+{
+    const double p1 = beta_power(hp.beta1, hp.step, 0);
+    const double p2 = beta_power(hp.beta2, hp.step, 1);
+    AdamScalars s;
+    s.b1 = (float)hp.beta1;
+    s.ob1 = (float)(1.0 - hp.beta1);
+    s.b2 = (float)hp.beta2;
+    s.ob2 = (float)(1.0 - hp.beta2);
+    s.s1 = (float)(hp.lr / (1.0 - p1));
+    s.s2 = (float)(1.0 / std::sqrt(1.0 - p2));
+    s.dec = (float)(1.0 - hp.lr * hp.weight_decay);
+    s.eps = (float)hp.eps;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qb_status_string(qb_status s)
+{
+    switch (s) {
+    case QB_OK: return "ok";
+    case QB_EINVAL: return "invalid argument";
+    case QB_EALIGN: return "device pointer not 16-byte aligned";
+    case QB_EUNSUPPORTED: return "unsupported combination";
+    case QB_EHIP: return "HIP runtime error";
+    case QB_EWORKSPACE: return "workspace too small";
+    case QB_EINIT: return "constant tables could not be built or uploaded";
+    default: return "unknown status";
+    }
+}
+
+size_t qb_dq_workspace_bytes(int64_t n, int32_t blocksize)
+{
+    if (n < 0 || !pow2_block(blocksize)) return 0;
+    return kBinBytes + round_up((size_t)nblocks(n, blocksize) * sizeof(float), 256);
+}
+
+size_t qb_multi_tensor_workspace_bytes(int32_t count)
+{
+    return count > 0 ? (size_t)count * sizeof(TensorDesc) : 0;
+}
+
+int32_t qb_codebook(qb_code code, float* out)
+{
+    const QbTables* t = host_tables();
+    if (!t || !out || !valid_code(code)) return -1;
+    if (code == QB_DYN8) {
+        std::memcpy(out, t->dyn8, sizeof(t->dyn8));
+        return 256;
+    }
+    std::memcpy(out, code == QB_NF4 ? t->nf4 : t->fp4, 16 * sizeof(float));
+    return 16;
+}
+
+int32_t qb_encoder_table(qb_code code, uint32_t* out, int32_t capacity)
+{
+    const QbTables* t = host_tables();
+    if (!t || !valid_code(code) || capacity < 0 || (capacity > 0 && !out)) return -1;
+    const LutEntry* src = code == QB_DYN8 ? t->dyn8_lut : (code == QB_NF4 ? t->nf4_lut : t->fp4_lut);
+    const int32_t count = code == QB_DYN8 ? kDynLutN : k4LutN;
+    for (int32_t i = 0; i < count && i < capacity; ++i) {
+        out[2 * i] = src[i].t;
+        out[2 * i + 1] = src[i].payload;
+    }
+    return count;
+}
+
+qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int32_t blocksize,
+                      uint8_t* codes, float* absmax, const qb_dq* dq, void* stream)
+{
+    if (n < 0 || !valid_dtype(xdt) || !valid_code(code) || !pow2_block(blocksize)) return QB_EINVAL;
+    if (n == 0) return QB_OK;
+    const int64_t nb = nblocks(n, blocksize);
+    if (nb >= (int64_t(1) << 31)) return QB_EINVAL;
+    if (!x || !codes) return QB_EINVAL;
+    if (!aligned16(x) || !aligned16(codes)) return QB_EALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int mode = dq ? QM_DQ_FIRST : QM_PLAIN;
+    unsigned long long* bins = nullptr;
+    float* first = absmax;
+    if (dq) {
+        if (absmax) return QB_EINVAL;
+        qb_status st = check_dq(dq, nb, true);
+        if (st != QB_OK) return st;
+        bins = static_cast<unsigned long long*>(dq->ws);
+        first = reinterpret_cast<float*>(static_cast<char*>(dq->ws) + kBinBytes);
+    } else {
+        if (!absmax) return QB_EINVAL;
+        if (!aligned16(absmax)) return QB_EALIGN;
+    }
+    if (!device_tables()) return QB_EINIT;
+    hipError_t e = hipSuccess;
+    if (dq) e = launch_clear_bins(bins, s);
+    if (e == hipSuccess) {
+        if (is4(code))
+            e = launch_quant4(x, (int)xdt, n, blocksize, code4_index(code), codes, first, mode, bins, s);
+        else
+            e = launch_quant8(x, (int)xdt, n, blocksize, codes, first, mode, bins, nullptr, s);
+    }
+    if (e == hipSuccess && dq)
+        e = launch_quant8(first, QB_F32, nb, dq->blocksize2, dq->codes, dq->absmax2, QM_DQ_SECOND, bins, dq->offset, s);
+    return hip_status(e);
+}
+
+qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* dq, qb_code code,
+                        int32_t blocksize, int64_t n, void* y, qb_dtype ydt, void* stream)
+{
+    if (n < 0 || !valid_dtype(ydt) || !valid_code(code) || !pow2_block(blocksize)) return QB_EINVAL;
+    if (n == 0) return QB_OK;
+    const int64_t nb = nblocks(n, blocksize);
+    if (nb >= (int64_t(1) << 31)) return QB_EINVAL;
+    if (!codes || !y) return QB_EINVAL;
+    if (!aligned16(codes) || !aligned16(y)) return QB_EALIGN;
+    const uint8_t* c2 = nullptr;
+    const float* a2 = nullptr;
+    const float* off = nullptr;
+    int b2 = 256;
+    if (dq) {
+        if (absmax) return QB_EINVAL;
+        qb_status st = check_dq(dq, nb, false);
+        if (st != QB_OK) return st;
+        c2 = dq->codes;
+        a2 = dq->absmax2;
+        off = dq->offset;
+        b2 = dq->blocksize2;
+    } else {
+        if (!absmax) return QB_EINVAL;
+        if (!aligned16(absmax)) return QB_EALIGN;
+    }
+    if (!device_tables()) return QB_EINIT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = is4(code) ? launch_dequant4(codes, absmax, c2, a2, off, blocksize, b2, n, code4_index(code), y,
+                                               (int)ydt, s)
+                             : launch_dequant8(codes, absmax, c2, a2, off, blocksize, b2, n, y, (int)ydt, s);
+    return hip_status(e);
+}
+
+qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, uint8_t* m, uint8_t* v,
+                            float* absmax_m, float* absmax_v, int32_t blocksize, const qb_adamw_hparams* hp,
+                            void* stream)
+{
+    if (n < 0 || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_hparams(hp)) return QB_EINVAL;
+    if (n == 0) return QB_OK;
+    if (nblocks(n, blocksize) >= (int64_t(1) << 31)) return QB_EINVAL;
+    if (!p || !g || !m || !v || !absmax_m || !absmax_v) return QB_EINVAL;
+    if ((const void*)p == g) return QB_EINVAL;
+    if (!aligned16(p) || !aligned16(g) || !aligned16(m) || !aligned16(v) || !aligned16(absmax_m) ||
+        !aligned16(absmax_v))
+        return QB_EALIGN;
+    if (!device_tables()) return QB_EINIT;
+    TensorDesc d{p, g, m, v, absmax_m, absmax_v, n, 0};
+    const int64_t ntiles = adamw_tiles(n, blocksize);
+    return hip_status(launch_adamw8(d, nullptr, 1, ntiles, blocksize, (int)gdt, prepare(*hp),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
+                               const qb_adamw_hparams* hp, void* ws, size_t ws_bytes, void* stream)
+{
+    if (count < 0 || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_hparams(hp)) return QB_EINVAL;
+    if (count == 0) return QB_OK;
+    if (!tensors || !ws) return QB_EINVAL;
+    if (!aligned16(ws)) return QB_EALIGN;
+    if (ws_bytes < qb_multi_tensor_workspace_bytes(count)) return QB_EWORKSPACE;
+    thread_local std::vector<TensorDesc> table;
+    table.clear();
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const qb_tensor& t = tensors[i];
+        if (t.n < 0) return QB_EINVAL;
+        if (t.n == 0) continue;
+        if (nblocks(t.n, blocksize) >= (int64_t(1) << 31)) return QB_EINVAL;
+        if (!t.p || !t.g || !t.m || !t.v || !t.absmax_m || !t.absmax_v) return QB_EINVAL;
+        if ((const void*)t.p == t.g) return QB_EINVAL;
+        if (!aligned16(t.p) || !aligned16(t.g) || !aligned16(t.m) || !aligned16(t.v) || !aligned16(t.absmax_m) ||
+            !aligned16(t.absmax_v))
+            return QB_EALIGN;
+        table.push_back(TensorDesc{t.p, t.g, t.m, t.v, t.absmax_m, t.absmax_v, t.n, tiles});
+        tiles += adamw_tiles(t.n, blocksize);
+    }
+    if (table.empty()) return QB_OK;
+    if (!device_tables()) return QB_EINIT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(ws, table.data(), table.size() * sizeof(TensorDesc), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return QB_EHIP;
+    return hip_status(launch_adamw8(table[0], static_cast<const TensorDesc*>(ws), (int)table.size(), tiles,
+                                    blocksize, (int)gdt, prepare(*hp), s));
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// qb_launch.h -- internal launchers behind the C ABI (argument checks are done
+// by the callers in qb_api.cpp; these only pick the kernel and enqueue it).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+#include "qb_tables.h"
+
+namespace qb {
+
+enum QuantMode { QM_PLAIN = 0, QM_DQ_FIRST = 1, QM_DQ_SECOND = 2 };
+
+// Exponent bins of the nested-quantization mean: 256 uint64 words at the start
+// of the workspace (254 used), then the fp32 absmax of the first level.
+constexpr size_t kBinWords = 256;
+constexpr size_t kBinBytes = kBinWords * sizeof(unsigned long long);
+
+struct AdamScalars {
+    float b1, ob1, b2, ob2, s1, s2, dec, eps;
+};
+
+// One tensor of a fused AdamW launch; tile_begin is the first global tile.
+struct TensorDesc {
+    float* p;
+    const void* g;
+    uint8_t* m;
+    uint8_t* v;
+    float* am;
+    float* av;
+    int64_t n;
+    int64_t tile_begin;
+};
+static_assert(sizeof(TensorDesc) == 64, "descriptor layout");
+
+// Device copy of the constant tables for the current device (uploaded once).
+const QbTables* device_tables();
+
+// CUs x resident workgroups per CU of a kernel, cached per (device, kernel);
+// `query` returns the kernel's resident workgroups per CU.
+int persistent_grid_cap(const void* kernel, int (*query)(const void*));
+
+// Workgroups to launch for a persistent grid-stride kernel: enough to fill
+// every CU at the kernel's occupancy, never more than there are tiles.
+template <class Kernel>
+int persistent_grid(Kernel kernel, int64_t ntiles)
+{
+    auto query = [](const void* k) -> int {
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<Kernel>(const_cast<void*>(k)), 256, 0)
+                != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        return per_cu;
+    };
+    int cap = persistent_grid_cap(reinterpret_cast<const void*>(kernel), query);
+    return (int)(ntiles < cap ? (ntiles > 0 ? ntiles : 1) : cap);
+}
+
+// Enqueue `kernel` with 256-thread workgroups; returns this launch's own
+// status (a stale error of an earlier call is neither returned nor cleared).
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), int grid, hipStream_t s, Args&&... args)
+{
+    std::tuple<KArgs...> vals(std::forward<Args>(args)...);
+    return std::apply(
+        [&](auto&... v) {
+            void* ptrs[] = {static_cast<void*>(&v)...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(256), ptrs, 0, s);
+        },
+        vals);
+}
+
+hipError_t launch_clear_bins(unsigned long long* bins, hipStream_t s);
+
+hipError_t launch_quant8(const void* x, int xdt, int64_t n, int B, uint8_t* codes, float* absmax, int mode,
+                         unsigned long long* bins, float* offset, hipStream_t s);
+hipError_t launch_quant4(const void* x, int xdt, int64_t n, int B, int code4, uint8_t* codes, float* absmax,
+                         int mode, unsigned long long* bins, hipStream_t s);
+hipError_t launch_dequant8(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
+                           const float* offset, int B, int B2, int64_t n, void* y, int ydt, hipStream_t s);
+hipError_t launch_dequant4(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
+                           const float* offset, int B, int B2, int64_t n, int code4, void* y, int ydt,
+                           hipStream_t s);
+hipError_t launch_adamw8(const TensorDesc& single, const TensorDesc* descs, int count, int64_t ntiles, int B,
+                         int gdt, const AdamScalars& hs, hipStream_t s);
+
+// Tiles of the AdamW kernel for a tensor of n elements at block size B.
+int64_t adamw_tiles(int64_t n, int B);
+
+}  // namespace qb

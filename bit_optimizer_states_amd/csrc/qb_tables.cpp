@@ -1,0 +1,279 @@
+// qb_tables.cpp -- host construction of the codes, their decision thresholds
+// and the bucketed encoder tables.
+//
+// Codes (readings of the pages; the tables are not printed there):
+//  * dynamic 8-bit code (abstract quoted on "Py之bitsandbytes", section 2:
+//    dynamic quantization, precise for large and small magnitudes): for
+//    decades e = 0..6, the 2^e midpoints of equal bins of [0.1, 1] scaled by
+//    10^(e-6), i.e. (2^(e+1) + 18j + 9) / (2^(e+1) 10^(7-e)), their negatives,
+//    0 and +1, sorted (256 entries);
+//  * NF4 ("Bitsandbytes", section Normal Float 4 (NF4)): quantiles of N(0,1)
+//    at 1/2 + (P-1/2)k/8 (k = 1..8) and their mirrored counterparts at k/7
+//    (k = 1..7), plus 0, over the quantile at P = 1 - (1/30 + 1/32)/2;
+//  * FP4 ("Quantize 🤗 Transformers models", section FP4 quantization): E2M1
+//    magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} / 6, sign-magnitude nibble.
+//
+// Encoding is nearest-entry with ties toward the entry of smaller magnitude.
+// Instead of comparing against midpoints at run time, the decision threshold
+// between two adjacent entries is precomputed as the smallest binary32 value
+// that encodes to the upper entry; counting thresholds <= n then gives the
+// code exactly, for every binary32 n.
+#include "qb_tables.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+namespace qb {
+namespace {
+
+uint32_t bits_of(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
+float float_of(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
+
+// Nearest-even binary32 of the positive rational num/den (num, den < 2^44),
+// by integer long division; results lie in the normal range here.
+float rn32_ratio(uint64_t num, uint64_t den)
+{
+    if (num == 0) return 0.0f;
+    int s = 0;  // q = floor(num * 2^s / den) must land in [2^23, 2^24)
+    auto q_of = [&](int sh, unsigned __int128* rem) {
+        unsigned __int128 a = sh >= 0 ? ((unsigned __int128)num << sh) : (unsigned __int128)(num >> -sh);
+        unsigned __int128 q = a / den;
+        if (rem) *rem = a % den;
+        return q;
+    };
+    while (q_of(s, nullptr) >= ((unsigned __int128)1 << 24)) --s;
+    while (q_of(s, nullptr) < ((unsigned __int128)1 << 23)) ++s;
+    unsigned __int128 r;
+    uint64_t q = (uint64_t)q_of(s, &r);
+    unsigned __int128 twice = r * 2;
+    if (twice > den || (twice == den && (q & 1))) ++q;
+    return std::ldexp((float)q, -s);   // q <= 2^24: exact
+}
+
+void build_dyn8(float* out)
+{
+    std::vector<float> pos;
+    for (int e = 0; e <= 6; ++e) {
+        uint64_t p10 = 1;
+        for (int k = 0; k < 7 - e; ++k) p10 *= 10;
+        for (int j = 0; j < (1 << e); ++j)
+            pos.push_back(rn32_ratio((2ull << e) + 18ull * j + 9ull, (2ull << e) * p10));
+    }
+    std::sort(pos.begin(), pos.end());
+    for (int i = 0; i < 127; ++i) out[i] = -pos[126 - i];
+    out[127] = 0.0f;
+    for (int i = 0; i < 127; ++i) out[128 + i] = pos[i];
+    out[255] = 1.0f;
+}
+
+// Standard normal quantile by Newton's method on the CDF 1/2 erfc(-x/sqrt 2).
+long double normal_quantile(long double p)
+{
+    const long double rs2 = 0.70710678118654752440084436210484903928L;
+    const long double rs2pi = 0.39894228040143267793994605993438186848L;
+    long double x = 0.0L;
+    for (int it = 0; it < 200; ++it) {
+        long double cdf = 0.5L * std::erfc(-x * rs2);
+        long double pdf = rs2pi * std::exp(-0.5L * x * x);
+        long double dx = (cdf - p) / pdf;
+        x -= dx;
+        if (std::fabs(dx) <= 1e-19L * (1.0L + std::fabs(x))) break;
+    }
+    return x;
+}
+
+void build_nf4(float* out)
+{
+    const long double P = 1.0L - (1.0L / 30.0L + 1.0L / 32.0L) / 2.0L;
+    const long double top = normal_quantile(P);
+    int n = 0;
+    for (int k = 7; k >= 1; --k)
+        out[n++] = (k == 7) ? -1.0f : (float)(-normal_quantile(0.5L + (P - 0.5L) * k / 7.0L) / top);
+    out[n++] = 0.0f;
+    for (int k = 1; k <= 8; ++k)
+        out[n++] = (k == 8) ? 1.0f : (float)(normal_quantile(0.5L + (P - 0.5L) * k / 8.0L) / top);
+}
+
+void build_fp4(float* out)
+{
+    // E2M1 magnitude / 6 as exact ratios, by bit pattern k
+    static const uint64_t num[8] = {0, 1, 1, 1, 1, 1, 2, 1};
+    static const uint64_t den[8] = {1, 12, 6, 4, 3, 2, 3, 1};
+    for (int k = 0; k < 8; ++k) {
+        float m = rn32_ratio(num[k], den[k]);
+        out[k] = m;
+        out[8 + k] = k ? -m : 0.0f;
+    }
+}
+
+// Smallest binary32 >= d (inclusive) or > d (strict).
+float ceil_f32(double d, bool strict)
+{
+    float f = (float)d;
+    if ((double)f < d || (strict && (double)f == d)) f = std::nextafter(f, INFINITY);
+    return f;
+}
+
+// Decision thresholds of an ascending list: t[i] = smallest binary32 that
+// encodes to vals[i+1] rather than vals[i].
+std::vector<float> thresholds(const std::vector<float>& vals)
+{
+    std::vector<float> t;
+    for (size_t i = 0; i + 1 < vals.size(); ++i) {
+        double mid = ((double)vals[i] + (double)vals[i + 1]) / 2.0;   // exact
+        bool tie_to_lower = std::fabs(vals[i]) < std::fabs(vals[i + 1]);
+        t.push_back(ceil_f32(mid, tie_to_lower));
+    }
+    return t;
+}
+
+int build_dyn8_lut(const float* dyn8, LutEntry* lut)
+{
+    std::vector<float> mags(dyn8 + 127, dyn8 + 256);   // 0, positive entries, 1.0
+    std::vector<float> t = thresholds(mags);           // 128 thresholds
+    std::vector<uint32_t> tb(t.size());
+    for (size_t i = 0; i < t.size(); ++i) tb[i] = bits_of(t[i]);
+    for (int b = 0; b < kDynLutN; ++b) {
+        uint32_t lo = b == 0 ? 0u : uint32_t(b + kDynBase) << kDynShift;
+        uint32_t hi = b == kDynLutN - 1 ? kOneBits : (uint32_t(b + kDynBase + 1) << kDynShift) - 1u;
+        int k = 0;
+        while (k < (int)tb.size() && tb[k] <= lo) ++k;
+        if (k + 1 < (int)tb.size() && tb[k + 1] <= hi) return -1;   // two thresholds in one bucket
+        lut[b].t = k < (int)tb.size() ? tb[k] : 0x7F800000u;
+        lut[b].payload = 127u + (uint32_t)k;
+    }
+    return 0;
+}
+
+int bucket4(float n)
+{
+    float u = n * 16.0f + 16.0f;
+    int b = (int)u;
+    return b < 0 ? 0 : (b > k4LutN - 1 ? k4LutN - 1 : b);
+}
+
+uint32_t order_key(float f)
+{
+    uint32_t u = bits_of(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+float from_key(uint32_t k)
+{
+    return float_of((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Smallest binary32 n in [-1, 1] with bucket4(n) >= b (bisection on the order).
+float bucket_start(int b)
+{
+    uint32_t lo = order_key(-1.0f), hi = order_key(1.0f);
+    if (bucket4(-1.0f) >= b) return -1.0f;
+    while (hi - lo > 1) {
+        uint32_t mid = lo + (hi - lo) / 2;
+        if (bucket4(from_key(mid)) >= b) hi = mid; else lo = mid;
+    }
+    return from_key(hi);
+}
+
+// vals: distinct values ascending; codes: the stored code of each value.
+int build_4bit_lut(const std::vector<float>& vals, const std::vector<uint32_t>& codes, LutEntry* lut)
+{
+    std::vector<float> t = thresholds(vals);
+    const int nt = (int)t.size();
+    for (int b = 0; b < k4LutN; ++b) {
+        float lo = bucket_start(b);
+        float hi = b + 1 < k4LutN ? std::nextafter(bucket_start(b + 1), -INFINITY) : 1.0f;
+        int k = 0;
+        while (k < nt && t[k] <= lo) ++k;
+        if (k + 1 < nt && t[k + 1] <= hi) return -1;
+        lut[b].t = k < nt ? bits_of(t[k]) : 0x7F800000u;
+        uint32_t below = codes[k], above = codes[k < nt ? k + 1 : k];
+        lut[b].payload = below | (above << 8);
+    }
+    return 0;
+}
+
+// Direct nearest search (ties toward zero), used only to self-check the tables.
+int nearest(const std::vector<float>& vals, float x)
+{
+    int best = 0;
+    for (int i = 1; i < (int)vals.size(); ++i) {
+        double db = std::fabs((double)x - vals[best]), di = std::fabs((double)x - vals[i]);
+        if (di < db || (di == db && std::fabs(vals[i]) < std::fabs(vals[best]))) best = i;
+    }
+    return best;
+}
+
+int self_check(const QbTables* T)
+{
+    // a deterministic sweep of [-1, 1]: the bucket encoders against the direct search
+    std::vector<float> dyn(T->dyn8, T->dyn8 + 256);
+    std::vector<float> nf4(T->nf4, T->nf4 + 16);
+    uint32_t state = 12345u;
+    for (int i = 0; i < 200000; ++i) {
+        state = state * 1664525u + 1013904223u;
+        float x = (i & 1) ? std::ldexp((float)(state >> 8) / 16777216.0f, -(int)(i % 30))
+                          : (float)(state >> 8) / 8388608.0f - 1.0f;
+        if (i & 2) x = -x;
+        if (!(x >= -1.0f && x <= 1.0f)) continue;
+        uint32_t mag = bits_of(x) & 0x7FFFFFFFu;
+        uint32_t cl = std::min(std::max(mag, kDynLowBits), kOneBits);
+        const LutEntry& e = T->dyn8_lut[(cl >> kDynShift) - kDynBase];
+        int cp = (int)e.payload + (mag >= e.t ? 1 : 0);
+        int code = x < 0 ? std::max(254 - cp, 0) : cp;
+        if (code != nearest(dyn, x)) return -10;
+        const LutEntry& f = T->nf4_lut[bucket4(x)];
+        int c4 = (x >= float_of(f.t)) ? (int)((f.payload >> 8) & 0xFF) : (int)(f.payload & 0xFF);
+        if (c4 != nearest(nf4, x)) return -11;
+    }
+    return 0;
+}
+
+}  // namespace
+
+int build_tables(QbTables* T)
+{
+    std::memset(T, 0, sizeof(*T));
+    build_dyn8(T->dyn8);
+    build_nf4(T->nf4);
+    build_fp4(T->fp4);
+    for (int i = 0; i < 255; ++i)
+        if (!(T->dyn8[i] < T->dyn8[i + 1])) return -2;
+    if (build_dyn8_lut(T->dyn8, T->dyn8_lut) != 0) return -3;
+
+    std::vector<float> nf4(T->nf4, T->nf4 + 16);
+    std::vector<uint32_t> nf4_codes(16);
+    for (int i = 0; i < 16; ++i) nf4_codes[i] = (uint32_t)i;
+    if (build_4bit_lut(nf4, nf4_codes, T->nf4_lut) != 0) return -4;
+
+    // FP4 as a line of 15 distinct values: -mag[7..1], 0, mag[1..7]
+    std::vector<float> fp4;
+    std::vector<uint32_t> fp4_codes;
+    for (int k = 7; k >= 1; --k) { fp4.push_back(T->fp4[8 + k]); fp4_codes.push_back(8u | (uint32_t)k); }
+    fp4.push_back(0.0f); fp4_codes.push_back(0u);
+    for (int k = 1; k <= 7; ++k) { fp4.push_back(T->fp4[k]); fp4_codes.push_back((uint32_t)k); }
+    if (build_4bit_lut(fp4, fp4_codes, T->fp4_lut) != 0) return -5;
+
+    for (int c = 0; c < 2; ++c) {
+        const float* val = c == 0 ? T->nf4 : T->fp4;
+        for (int byte = 0; byte < 256; ++byte) {
+            T->pair[c][byte][0] = val[byte >> 4];
+            T->pair[c][byte][1] = val[byte & 15];
+        }
+    }
+    return self_check(T);
+}
+
+const QbTables* host_tables()
+{
+    static QbTables tables;
+    static int status = 1;
+    static std::once_flag once;
+    std::call_once(once, [] { status = build_tables(&tables); });
+    return status == 0 ? &tables : nullptr;
+}
+
+}  // namespace qb

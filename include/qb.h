@@ -1,0 +1,204 @@
+/*
+ * qb.h -- C ABI of libqb: block-wise dynamic quantization, nested quantization
+ * of the block constants, and the fused 8-bit AdamW step, for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method: a tensor is cut into blocks of `blocksize` consecutive elements;
+ * every block is scaled by its own absolute maximum and each scaled value is
+ * replaced by the index of the nearest entry of a fixed code, so blocks are
+ * quantized independently and in parallel (abstract of "8-bit Optimizers via
+ * Block-wise Quantization", quoted on the page "Py之bitsandbytes：bitsandbytes的
+ * 简介、安装、使用方法之详细攻略", section 2; page "bitsandbytes深度解析",
+ * section 核心量化原理与实现机制).
+ *
+ * Codes (QB_DYN8, QB_NF4, QB_FP4) -- see qb_codebook() for the exact tables:
+ *   QB_DYN8  256-entry signed dynamic code (decimal exponent + linear fraction),
+ *            one byte per element; index 127 is 0.0, 255 is +1.0.
+ *   QB_NF4   16 normal-quantile values in [-1, 1], two codes per byte.
+ *   QB_FP4   E2M1 minifloat / 6, sign-magnitude nibble, two codes per byte.
+ * 4-bit packing: element 2k is the high nibble of byte k, element 2k+1 the low
+ * nibble; an odd count leaves the last low nibble 0.
+ * Encoding: nearest entry of value/absmax, a tie going to the entry of smaller
+ * magnitude; a block whose absmax is 0 gets the code of 0.0.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers unless marked "host".  The caller
+ *     owns every buffer: libqb never allocates device memory, keeps no state
+ *     between calls except its constant tables, and is safe to call from
+ *     several host threads.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously on it; no entry point synchronizes the device.
+ *   - Arguments are validated before anything is enqueued; on any error
+ *     nothing runs and nothing is written.  A failed launch returns QB_EHIP.
+ *     No C++ exception crosses this interface.
+ *   - Device pointers must be 16-byte aligned (QB_EALIGN otherwise).
+ *   - n == 0 is a no-op returning QB_OK.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified codes.
+ *   - blocksize is a power of two in [64, 4096]; the number of blocks must be
+ *     below 2^31.
+ */
+#ifndef QB_H
+#define QB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QB_OK = 0,
+    QB_EINVAL = 1,        /* a null pointer, bad size, bad enum or bad hyperparameter */
+    QB_EALIGN = 2,        /* a device pointer is not 16-byte aligned */
+    QB_EUNSUPPORTED = 3,  /* a valid but unsupported combination */
+    QB_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
+    QB_EWORKSPACE = 5,    /* the workspace is too small */
+    QB_EINIT = 6          /* the constant tables could not be built or uploaded */
+} qb_status;
+
+typedef enum { QB_F32 = 0, QB_F16 = 1, QB_BF16 = 2 } qb_dtype;
+
+typedef enum { QB_DYN8 = 0, QB_NF4 = 1, QB_FP4 = 2 } qb_code;
+
+/*
+ * Nested ("double") quantization state of the per-block absmax (page
+ * "Bitsandbytes" (Transformers docs), section İç içe nicelleştirme: a second
+ * quantization of the constants of the first, about 0.4 bit per parameter).
+ * The nb = ceil(n / blocksize) fp32 absmax values a_j are centred on their mean
+ *   offset = the exact mean of a_j, rounded once to fp32,
+ * and d_j = a_j - offset (fp32) is quantized with QB_DYN8 in blocks of
+ * blocksize2.  The decoded constant is dyn8[codes_j] * absmax2[j / blocksize2]
+ * + offset (two rounded fp32 operations).
+ */
+typedef struct {
+    uint8_t* codes;      /* [nb] QB_DYN8 codes of a_j - offset */
+    float*   absmax2;    /* [ceil(nb / blocksize2)] */
+    float*   offset;     /* [1] */
+    int32_t  blocksize2; /* power of two in [64, 4096]; 256 is the usual value */
+    void*    ws;         /* workspace of qb_dq_workspace_bytes(n, blocksize) bytes; used by qb_quantize only */
+    size_t   ws_bytes;
+} qb_dq;
+
+/*
+ * Hyperparameters of one AdamW step (pages: "bitsandbytes - Quantização de
+ * LLM", section Workflow 3, where the 8-bit optimizer replaces AdamW with the
+ * same lr, betas and eps; "Py之bitsandbytes", section 使用8位优化器).  They are
+ * real numbers: every per-element scalar (beta1, 1-beta1, beta2, 1-beta2,
+ * lr/(1-beta1^t), 1/sqrt(1-beta2^t), 1-lr*weight_decay, eps) is computed in
+ * binary64 and rounded once to binary32.  step is the 1-based step t.
+ * Requirements: 0 <= beta1, beta2 < 1; eps > 0; lr, weight_decay finite, >= 0;
+ * step >= 1.
+ */
+typedef struct {
+    double  lr;
+    double  beta1;
+    double  beta2;
+    double  eps;
+    double  weight_decay;
+    int32_t step;
+} qb_adamw_hparams;
+
+/* One tensor of a multi-tensor step; the fields are those of qb_adamw8bit_step. */
+typedef struct {
+    float*      p;
+    const void* g;
+    uint8_t*    m;
+    uint8_t*    v;
+    float*      absmax_m;
+    float*      absmax_v;
+    int64_t     n;
+} qb_tensor;
+
+/*
+ * qb_quantize -- block-wise quantization (pages cited at the top; NF4: page
+ * "Bitsandbytes", section Normal Float 4 (NF4); FP4: page "Quantize 🤗
+ * Transformers models", section FP4 quantization).
+ *   x       [n] input of dtype xdt (fp32, fp16 or bf16).
+ *   code    QB_DYN8 (codes: n bytes) or QB_NF4 / QB_FP4 (codes: ceil(n/2) bytes).
+ *   absmax  [ceil(n/blocksize)] fp32 block absmax out; must be NULL when dq is given.
+ *   dq      NULL, or the nested state to fill (codes, absmax2, offset; the
+ *           workspace holds the fp32 absmax while the call runs).
+ * Outputs are fully overwritten.  Four kernels at most (with dq: clear the
+ * workspace counters, quantize, nested quantize), all on `stream`.
+ */
+qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int32_t blocksize,
+                      uint8_t* codes, float* absmax, const qb_dq* dq, void* stream);
+
+/*
+ * qb_dequantize -- y_i = ydt(table[c_i] * s_b), one fp32 multiply then a
+ * round-to-nearest-even conversion (page "Bitsandbytes", section on
+ * dequantizing a model; compute dtype: page "Quantize 🤗 Transformers models",
+ * section Change the compute dtype).  s_b is absmax[b], or with dq the decoded
+ * nested constant of block b (dq->ws is not used).
+ *   codes  [n] (DYN8) or [ceil(n/2)] (NF4/FP4);  y [n] of dtype ydt.
+ */
+qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* dq, qb_code code,
+                        int32_t blocksize, int64_t n, void* y, qb_dtype ydt, void* stream);
+
+/*
+ * qb_adamw8bit_step -- one fused AdamW step with both moments held as block-wise
+ * QB_DYN8 codes (abstract quoted on "Py之bitsandbytes", section 2: 8-bit
+ * optimizer state with block-wise dynamic quantization; "bitsandbytes -
+ * Quantização de LLM", section Workflow 3: 2 bytes of state per parameter).
+ * Per block of `blocksize` elements, in one kernel:
+ *   m = dyn8[m_i]*absmax_m[b], v = dyn8[v_i]*absmax_v[b]
+ *   m' = b1*m + (1-b1)*g,  v' = b2*v + (1-b2)*g*g
+ *   p' = p*(1-lr*wd) - lr/(1-b1^t) * m' / (sqrt(v')/sqrt(1-b2^t) + eps)
+ *   absmax_m[b] = max|m'|, absmax_v[b] = max|v'|, m_i, v_i = codes of m', v'.
+ *   p          [n] fp32, in place.     g [n] of dtype gdt, read only; must not alias p.
+ *   m, v       [n] uint8 codes, in place.  Fresh state: every code 127 (0.0), absmax 0.
+ *   absmax_*   [ceil(n/blocksize)] fp32, in place.
+ * The state codes and absmax are bit-exact against an IEEE binary32 evaluation
+ * of the formulas above; p' uses hardware square root and reciprocal and is
+ * within 1e-6 relative of it.
+ */
+qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, uint8_t* m, uint8_t* v,
+                            float* absmax_m, float* absmax_v, int32_t blocksize,
+                            const qb_adamw_hparams* hp, void* stream);
+
+/*
+ * qb_multi_tensor_step -- qb_adamw8bit_step on `count` tensors in ONE kernel
+ * launch (blocks never span tensors; the result equals a loop of single-tensor
+ * calls, bit for bit).
+ *   tensors   host array of `count` descriptors (read during the call only).
+ *   ws        device workspace of qb_multi_tensor_workspace_bytes(count) bytes;
+ *             the call copies the descriptor table into it on `stream`, so ws
+ *             must not be reused by another stream until the step has run.
+ * Tensors with n == 0 are skipped.  count == 0 is a no-op.
+ */
+qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
+                               const qb_adamw_hparams* hp, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace sizes (bytes) for qb_quantize with nesting and for qb_multi_tensor_step. */
+size_t qb_dq_workspace_bytes(int64_t n, int32_t blocksize);
+size_t qb_multi_tensor_workspace_bytes(int32_t count);
+
+/*
+ * qb_codebook -- host: copy the decode table of `code` (indexed by stored code)
+ * into out (256 floats for DYN8, 16 for NF4/FP4).  Returns the entry count, or
+ * -1 for a bad code or a failed table build.
+ */
+int32_t qb_codebook(qb_code code, float* out);
+
+/*
+ * qb_encoder_table -- host: the encoder's bucket table, for inspection and
+ * tests.  Each entry is two uint32 words {threshold bits, payload}:
+ *   DYN8: bucket b = (clamp(bits(|n|), 2^-22, 1.0) >> 17) - (bits(2^-22) >> 17);
+ *         the magnitude code is payload + (|n| >= threshold); a negative n maps
+ *         to max(254 - code, 0).
+ *   NF4/FP4: bucket b = (int)(n*16 + 16) in binary32 (0..32); the code is byte
+ *         0 of payload if n < threshold, else byte 1.
+ * Copies at most `capacity` entries (2*capacity words) into out and returns the
+ * table's entry count, or -1 on error.
+ */
+int32_t qb_encoder_table(qb_code code, uint32_t* out, int32_t capacity);
+
+/* Static text for a status code. */
+const char* qb_status_string(qb_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QB_H */

@@ -1,0 +1,149 @@
+"""Host-side checks of the HIP library (no GPU needed, no kernel runs).
+
+  * libqb.so loads and exports every function include/qb.h declares;
+  * its constant tables (built independently of the oracle) equal the oracle's;
+  * the bucketed encoder the kernels run, emulated here in numpy from the
+    library's own tables, equals the oracle's exact nearest-code encoder on
+    every binary32 value tried (all thresholds and their neighbours included);
+  * invalid arguments are rejected before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def qb():
+    from bit_optimizer_states_amd import binding
+    binding.lib()
+    return binding
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "qb.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(qb):
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(qb.lib(), name), name
+
+
+@pytest.mark.parametrize("code", [0, 1, 2])
+def test_codebooks_equal_oracle(qb, code):
+    lib_cb = np.array(qb.qb_codebook(code), dtype=np.float32)
+    assert np.array_equal(lib_cb.view(np.uint32), oracle.codebook(code).view(np.uint32))
+
+
+def emulate_dyn8(table, x):
+    """The kernels' dynamic-code encoder, from the library's bucket table."""
+    t = np.array([e[0] for e in table], dtype=np.uint32)
+    pay = np.array([e[1] for e in table], dtype=np.int64)
+    bits = x.astype(np.float32).view(np.uint32)
+    mag = bits & np.uint32(0x7FFFFFFF)
+    low, one = np.uint32(105 << 23), np.uint32(0x3F800000)
+    cl = np.minimum(np.maximum(mag, low), one)
+    b = (cl >> np.uint32(17)).astype(np.int64) - (105 << 6)
+    cp = pay[b] + (mag >= t[b])
+    return np.where(bits >> np.uint32(31) == 1, np.maximum(254 - cp, 0), cp).astype(np.uint8)
+
+
+def emulate_4bit(table, x):
+    t = np.array([e[0] for e in table], dtype=np.uint32).view(np.float32)
+    pay = np.array([e[1] for e in table], dtype=np.int64)
+    x = x.astype(np.float32)
+    u = (x * np.float32(16.0)).astype(np.float32) + np.float32(16.0)
+    b = np.minimum(u.astype(np.int64), 32)
+    return np.where(x >= t[b], (pay[b] >> 8) & 0xFF, pay[b] & 0xFF).astype(np.uint8)
+
+
+def probe_values(code, rng):
+    cb = oracle.codebook(code)
+    vals = [rng.uniform(-1, 1, 200000), rng.standard_normal(50000) * 1e-3,
+            np.exp(rng.uniform(np.log(1e-9), 0, 100000)) * rng.choice([-1, 1], 100000)]
+    srt = np.sort(np.unique(np.abs(cb) if code == oracle.FP4 else cb))
+    mids = ((srt[:-1].astype(np.float64) + srt[1:]) / 2).astype(np.float32)
+    near = [mids]
+    for _ in range(3):
+        near.append(np.nextafter(near[-1], np.float32(2)))
+    down = [mids]
+    for _ in range(3):
+        down.append(np.nextafter(down[-1], np.float32(-2)))
+    edges = np.concatenate(near + down + [cb])
+    x = np.concatenate(vals + [edges, -edges, [0.0, -0.0, 1.0, -1.0, 1e-45, -1e-45, 2.0 ** -22, -(2.0 ** -22)]])
+    x = x.astype(np.float32)
+    return x[np.abs(x) <= 1]
+
+
+def test_dyn8_bucket_encoder_equals_oracle(qb):
+    x = probe_values(oracle.DYN8, np.random.default_rng(31))
+    assert np.array_equal(emulate_dyn8(qb.qb_encoder_table(0), x), oracle.encode(oracle.DYN8, x))
+
+
+def test_dyn8_bucket_encoder_all_floats_in_a_binade(qb):
+    # every binary32 in [0.5, 1] and [-1, -0.5]: the densest thresholds
+    x = np.arange(0x3F000000, 0x3F800001, dtype=np.uint32).view(np.float32)
+    x = np.concatenate([x, -x])
+    assert np.array_equal(emulate_dyn8(qb.qb_encoder_table(0), x), oracle.encode(oracle.DYN8, x))
+
+
+@pytest.mark.parametrize("code", [1, 2])
+def test_4bit_bucket_encoder_equals_oracle(qb, code):
+    x = probe_values(code, np.random.default_rng(32 + code))
+    assert np.array_equal(emulate_4bit(qb.qb_encoder_table(code), x), oracle.encode(code, x))
+
+
+def test_workspace_sizes(qb):
+    assert qb.qb_dq_workspace_bytes(64 * 1000, 64) == 2048 + 4096
+    assert qb.qb_dq_workspace_bytes(0, 64) == 2048
+    assert qb.qb_dq_workspace_bytes(100, 63) == 0
+    assert qb.qb_multi_tensor_workspace_bytes(291) == 291 * 64
+    assert qb.qb_multi_tensor_workspace_bytes(0) == 0
+
+
+def test_invalid_arguments_rejected_before_launch(qb):
+    L = qb.lib()
+    A = 0x100000  # an aligned fake device address: validation must fail before any use
+    hp = qb.hparams(step=1)
+    assert L.qb_quantize(A, 0, -1, 0, 256, A, A, None, None) == qb.QB_EINVAL         # n < 0
+    assert L.qb_quantize(A, 0, 0, 0, 256, A, A, None, None) == qb.QB_OK              # n == 0: no-op
+    assert L.qb_quantize(A, 0, 100, 0, 100, A, A, None, None) == qb.QB_EINVAL        # blocksize not a power of 2
+    assert L.qb_quantize(A, 0, 100, 0, 8192, A, A, None, None) == qb.QB_EINVAL       # blocksize too large
+    assert L.qb_quantize(A, 7, 100, 0, 256, A, A, None, None) == qb.QB_EINVAL        # bad dtype
+    assert L.qb_quantize(A, 0, 100, 5, 256, A, A, None, None) == qb.QB_EINVAL        # bad code
+    assert L.qb_quantize(None, 0, 100, 0, 256, A, A, None, None) == qb.QB_EINVAL     # null input
+    assert L.qb_quantize(A + 4, 0, 100, 0, 256, A, A, None, None) == qb.QB_EALIGN    # misaligned
+    assert L.qb_quantize(A, 0, 100, 0, 256, A, None, None, None) == qb.QB_EINVAL     # no absmax, no dq
+    dq = qb.qb_dq(A, A, A, 256, A, 16)
+    assert L.qb_quantize(A, 0, 100, 1, 64, A, A, ctypes.byref(dq), None) == qb.QB_EINVAL        # absmax and dq
+    assert L.qb_quantize(A, 0, 6400, 1, 64, A, None, ctypes.byref(dq), None) == qb.QB_EWORKSPACE
+    dq_bad = qb.qb_dq(A, A, A, 100, A, 1 << 20)
+    assert L.qb_quantize(A, 0, 6400, 1, 64, A, None, ctypes.byref(dq_bad), None) == qb.QB_EINVAL
+    assert L.qb_dequantize(A, None, None, 0, 256, 100, A, 0, None) == qb.QB_EINVAL   # no scale at all
+    assert L.qb_dequantize(A, A, None, 0, 256, 100, A + 2, 2, None) == qb.QB_EALIGN
+    assert L.qb_adamw8bit_step(A, A, 2, 100, A, A, A, A, 2048, ctypes.byref(hp), None) == qb.QB_EINVAL  # p aliases g
+    A2 = A + 0x10000
+    assert L.qb_adamw8bit_step(A, A2, 2, 100, A, A, A, A, 2048, None, None) == qb.QB_EINVAL
+    for bad in (qb.hparams(step=0), qb.hparams(beta1=1.0), qb.hparams(eps=0.0), qb.hparams(lr=float("nan"))):
+        assert L.qb_adamw8bit_step(A, A2, 2, 100, A, A, A, A, 2048, ctypes.byref(bad), None) == qb.QB_EINVAL
+    assert L.qb_adamw8bit_step(A, A2, 2, 0, A, A, A, A, 2048, ctypes.byref(hp), None) == qb.QB_OK
+    tab = (qb.qb_tensor * 1)(qb.qb_tensor(A, A2, A, A, A, A, 100))
+    assert L.qb_multi_tensor_step(tab, 1, 2, 2048, ctypes.byref(hp), A, 10, None) == qb.QB_EWORKSPACE
+    assert L.qb_multi_tensor_step(tab, 0, 2, 2048, ctypes.byref(hp), A, 0, None) == qb.QB_OK
+    tab_bad = (qb.qb_tensor * 1)(qb.qb_tensor(A, A2 + 8, A, A, A, A, 100))
+    assert L.qb_multi_tensor_step(tab_bad, 1, 2, 2048, ctypes.byref(hp), A, 64, None) == qb.QB_EALIGN
+
+
+def test_status_strings(qb):
+    assert qb.qb_status_string(0) == "ok"
+    assert "workspace" in qb.qb_status_string(5)
