@@ -11,7 +11,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqb.so")
+# QB_LIBRARY may name another build of the same library (tuning builds)
+LIB_PATH = os.environ.get("QB_LIBRARY") or os.path.join(_HERE, "libqb.so")
 
 QB_OK, QB_EINVAL, QB_EALIGN, QB_EUNSUPPORTED, QB_EHIP, QB_EWORKSPACE, QB_EINIT = range(7)
 QB_F32, QB_F16, QB_BF16 = 0, 1, 2

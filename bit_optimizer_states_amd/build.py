@@ -29,9 +29,9 @@ def _hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [_hipcc(), *COMMON]
+def _compile(src, build_dir=BUILD, extra=()):
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [_hipcc(), *COMMON, *extra]
     if src.endswith(".hip"):
         cmd += ["-x", "hip", *DEVICE]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -46,19 +46,21 @@ def _compile(src):
     return obj
 
 
-def build(jobs=None):
-    """Compile every source (always) and link libqb.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs=None, out=LIB, extra=()):
+    """Compile every source (always) and link the library (libqb.so by
+    default; `extra` adds compiler flags); returns its path."""
+    build_dir = BUILD if out == LIB else os.path.join(os.path.dirname(os.path.abspath(out)), "_build")
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, tuple(extra)), SOURCES))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -6,30 +6,40 @@
 // parameter: "bitsandbytes - Quantização de LLM", section Workflow 3) and is a
 // drop-in replacement for AdamW (same lr, betas, eps).  One pass per block, in
 // registers: decode m and v, update m, v and p, reduce the new block absmax of
-// m' and v', encode m' and v' again.  Each parameter's 14-16 bytes cross HBM
-// once.
+// m' and v', encode m' and v' again.  Each parameter's bytes cross HBM once.
 //
-// One kernel serves one tensor (descriptor passed by value) or many tensors
-// (a descriptor table in device memory; a persistent workgroup walks the
-// global tile index upward, so its cursor into the table only moves forward).
+// One 256-thread workgroup per tile (a tile is one block for B >= 1024), in
+// tile order.  For many tensors, the tiles of all tensors are numbered in one
+// range; a workgroup finds its tensor by a binary search over the tensors'
+// first tile numbers (uniform, scalar loads that stay in the scalar cache).
 #include "qb_device.h"
 #include "qb_launch.h"
 
 namespace qb {
 
+// Threads per workgroup of the AdamW kernel: a 2048-element block takes one
+// workgroup of kAdamThreads threads, i.e. 2048 / kAdamThreads elements per
+// thread; more elements per thread spread the per-block fixed work (tensor
+// lookup, table staging, block reduction, reciprocals) thinner.
+#ifndef QB_ADAM_THREADS
+#define QB_ADAM_THREADS 256
+#endif
+constexpr int kAdamThreads = QB_ADAM_THREADS;
+
 template <int B>
 struct TileA {
-    static constexpr int EPT = B >= 1024 ? B / 256 : 4;
+    static constexpr int NT = kAdamThreads;
+    static constexpr int EPT = B >= 4 * NT ? B / NT : 4;
     static constexpr int LPB = B / EPT;
-    static constexpr int BPT = kThreads / LPB;
+    static constexpr int BPT = NT / LPB;
     static constexpr int CH = EPT / 4;
-    static constexpr int ELEMS = kThreads * EPT;
+    static constexpr int ELEMS = NT * EPT;
     static constexpr int WPB = LPB > 64 ? LPB / 64 : 1;
 };
 
-// Block maxima of two non-negative values (as bits), one barrier per tile.
+// Block maxima of two non-negative values (as bits).
 template <class T>
-__device__ __forceinline__ void block_max2(uint32_t& x, uint32_t& y, uint32_t (*red)[4], int tid)
+__device__ __forceinline__ void block_max2(uint32_t& x, uint32_t& y, uint32_t (*red)[T::NT / 64], int tid)
 {
     constexpr int L = T::LPB < 64 ? T::LPB : 64;
     x = lanes_max<L>(x);
@@ -54,177 +64,192 @@ __device__ __forceinline__ void block_max2(uint32_t& x, uint32_t& y, uint32_t (*
 }
 
 template <int B, int GDT, bool MULTI>
-__global__ __launch_bounds__(256) void k_adamw8(TensorDesc single, const TensorDesc* __restrict__ descs, int count,
-                                                int64_t ntiles, AdamScalars hs, const QbTables* __restrict__ tab)
+__global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, const TensorDesc* __restrict__ descs,
+                                                const int64_t* __restrict__ tile_begin, int count, AdamScalars hs,
+                                                const QbTables* __restrict__ tab)
 {
     using T = TileA<B>;
     __shared__ float s_dyn[256];
-    __shared__ uint2 s_lut[kDynLutN];
-    __shared__ uint32_t s_red[2][2][4];
+    __shared__ DynEncLds s_enc;
+    __shared__ uint32_t s_red[2][T::NT / 64];
     const int tid = threadIdx.x;
-    s_dyn[tid] = tab->dyn8[tid];
-    const uint2* glut = reinterpret_cast<const uint2*>(tab->dyn8_lut);
-    for (int i = tid; i < kDynLutN; i += kThreads) s_lut[i] = glut[i];
+    const int64_t tile = blockIdx.x;
+
+    TensorDesc d;
+    int64_t lt;
+    if constexpr (MULTI) {
+        int lo = 0, hi = count;                 // tile_begin[lo] <= tile < tile_begin[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tile_begin[mid] <= tile) lo = mid; else hi = mid;
+        }
+        d = descs[lo];
+        lt = tile - tile_begin[lo];
+    } else {
+        d = single;
+        lt = tile;
+    }
+    const int bt = tid / T::LPB, l = tid % T::LPB;
+    const int64_t nloc = d.n;
+    const int64_t nbl = (nloc + B - 1) / B;
+    const int64_t blk = lt * T::BPT + bt;
+    const bool full = (lt + 1) * T::ELEMS <= nloc;
+    // uniform tile base pointers; per-lane offsets stay 32-bit
+    const int64_t tbase = lt * T::ELEMS;
+    float* const pt = d.p + tbase;
+    const void* const gt = static_cast<const char*>(d.g) + tbase * (GDT == DT_F32 ? 4 : 2);
+    uint8_t* const mt = d.m + tbase;
+    uint8_t* const vt = d.v + tbase;
+    const uint32_t lofs = (uint32_t)(bt * B + l * 4);      // element offset of chunk 0 in the tile
+    const int64_t lrem = nloc - tbase;                      // elements left in the tensor from the tile start
+
+    // loads first; the tables are staged while they are in flight
+    float am0 = 0.0f, av0 = 0.0f;
+    if (blk < nbl) {
+        am0 = gld<float>(d.am + blk);
+        av0 = gld<float>(d.av + blk);
+    }
+    float p[T::EPT], g[T::EPT];
+    uint32_t cmw[T::CH], cvw[T::CH];
+    if (full) {
+#pragma unroll
+        for (int c = 0; c < T::CH; ++c) {
+            const uint32_t e = lofs + c * T::LPB * 4;
+            load4o<DT_F32>(pt, e, &p[c * 4]);
+            load4o<GDT>(gt, e, &g[c * 4]);
+            cmw[c] = gldo<uint32_t>(mt, e);
+            cvw[c] = gldo<uint32_t>(vt, e);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < T::CH; ++c) {
+            uint32_t wm = 0x7F7F7F7Fu, wv = 0x7F7F7F7Fu;   // code of 0.0 in every byte
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = lofs + c * T::LPB * 4 + j;
+                float pv = 0.0f, gv = 0.0f;
+                if ((int64_t)e < lrem) {
+                    pv = load1<DT_F32>(pt, e);
+                    gv = load1<GDT>(gt, e);
+                    wm = (wm & ~(0xFFu << (8 * j))) | ((uint32_t)gldo<uint8_t>(mt, e) << (8 * j));
+                    wv = (wv & ~(0xFFu << (8 * j))) | ((uint32_t)gldo<uint8_t>(vt, e) << (8 * j));
+                }
+                p[c * 4 + j] = pv;
+                g[c * 4 + j] = gv;
+            }
+            cmw[c] = wm;
+            cvw[c] = wv;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < (256 + T::NT - 1) / T::NT; ++r)
+        if (T::NT <= 256 || tid < 256) s_dyn[r * T::NT + tid] = tab->dyn8[r * T::NT + tid];
+    stage_dyn_enc<T::NT>(s_enc, tab, tid);
     __syncthreads();
 
-    const int bt = tid / T::LPB, l = tid % T::LPB;
-    int cur = 0;
-    int par = 0;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x, par ^= 1) {
-        TensorDesc d;
-        int64_t lt;
-        if constexpr (MULTI) {
-            while (cur + 1 < count && tile >= descs[cur + 1].tile_begin) ++cur;
-            d = descs[cur];
-            lt = tile - d.tile_begin;
-        } else {
-            d = single;
-            lt = tile;
-        }
-        const int64_t nloc = d.n;
-        const int64_t nbl = (nloc + B - 1) / B;
-        const int64_t blk = lt * T::BPT + bt;
-        const int64_t bstart = blk * B;
-        const bool full = (lt + 1) * T::ELEMS <= nloc;
+    // decode, update (binary32, every operation rounded on its own)
+    float m1[T::EPT], v1[T::EPT];
+    float mxm = 0.0f, mxv = 0.0f;
+#pragma unroll
+    for (int i = 0; i < T::EPT; ++i) {
+        const uint32_t sh = 8 * (i & 3);
+        const float m0 = s_dyn[(cmw[i >> 2] >> sh) & 0xFFu] * am0;
+        const float v0 = s_dyn[(cvw[i >> 2] >> sh) & 0xFFu] * av0;
+        const float gi = g[i];
+        const float mm = hs.b1 * m0 + hs.ob1 * gi;
+        const float vv = hs.b2 * v0 + hs.ob2 * (gi * gi);
+        // the parameter update takes hardware square root and reciprocal
+        // (about 1 ulp each) and fused multiply-adds: within 1e-6 relative
+        // of the separately rounded formula; the moments and codes do not
+        // depend on it
+        const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(vv), hs.s2, hs.eps);
+        const float upd = mm * __builtin_amdgcn_rcpf(den);
+        p[i] = __builtin_fmaf(-hs.s1, upd, p[i] * hs.dec);
+        m1[i] = mm;
+        v1[i] = vv;
+        mxm = __builtin_fmaxf(mxm, __builtin_fabsf(mm));
+        mxv = __builtin_fmaxf(mxv, vv);                     // v' >= 0
+    }
+    if (full) {
+#pragma unroll
+        for (int c = 0; c < T::CH; ++c) store4o<DT_F32>(pt, lofs + c * T::LPB * 4, &p[c * 4]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < T::CH; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = lofs + c * T::LPB * 4 + j;
+                if ((int64_t)e < lrem) gsto<float>(pt, e * 4u, p[c * 4 + j]);
+            }
+    }
 
-        float am0 = 0.0f, av0 = 0.0f;
-        if (blk < nbl) {
-            am0 = d.am[blk];
-            av0 = d.av[blk];
-        }
-        float p[T::EPT], g[T::EPT];
-        uint32_t cmw[T::CH], cvw[T::CH];
-        if (full) {
-#pragma unroll
-            for (int c = 0; c < T::CH; ++c) {
-                const int64_t e0 = bstart + c * T::LPB * 4 + l * 4;
-                load4<DT_F32>(d.p, e0, &p[c * 4]);
-                load4<GDT>(d.g, e0, &g[c * 4]);
-                cmw[c] = *reinterpret_cast<const uint32_t*>(d.m + e0);
-                cvw[c] = *reinterpret_cast<const uint32_t*>(d.v + e0);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < T::CH; ++c) {
-                uint32_t wm = 0x7F7F7F7Fu, wv = 0x7F7F7F7Fu;   // code of 0.0 in every byte
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t idx = bstart + c * T::LPB * 4 + l * 4 + j;
-                    float pv = 0.0f, gv = 0.0f;
-                    if (idx < nloc) {
-                        pv = d.p[idx];
-                        gv = load1<GDT>(d.g, idx);
-                        wm = (wm & ~(0xFFu << (8 * j))) | ((uint32_t)d.m[idx] << (8 * j));
-                        wv = (wv & ~(0xFFu << (8 * j))) | ((uint32_t)d.v[idx] << (8 * j));
-                    }
-                    p[c * 4 + j] = pv;
-                    g[c * 4 + j] = gv;
-                }
-                cmw[c] = wm;
-                cvw[c] = wv;
-            }
-        }
+    // new block absmax of m' and v' (non-negative floats compare as their bits)
+    uint32_t bm = fbits(mxm), bv = fbits(mxv);
+    block_max2<T>(bm, bv, s_red, tid);
+    const float am1 = ffrom(bm), av1 = ffrom(bv);
+    if (l == 0 && blk < nbl) {
+        gst<float>(d.am + blk, am1);
+        gst<float>(d.av + blk, av1);
+    }
 
-        // decode, update (binary32, every operation rounded on its own)
-        float m1[T::EPT], v1[T::EPT];
-        uint32_t mxm = 0, mxv = 0;
+    // encode m' (signed) and v' (non-negative) with the dynamic code
+    const float rm = rcp_rn(am1);        // used only where fast_div_ok(am1)
+    const float rv = rcp_rn(av1);
+    const bool fast = fast_div_ok(am1) && fast_div_ok(av1);
+    uint32_t om[T::CH], ov[T::CH];
+    if (__all(fast)) {
 #pragma unroll
-        for (int i = 0; i < T::EPT; ++i) {
-            const uint32_t sh = 8 * (i & 3);
-            const float m0 = s_dyn[(cmw[i >> 2] >> sh) & 0xFFu] * am0;
-            const float v0 = s_dyn[(cvw[i >> 2] >> sh) & 0xFFu] * av0;
-            const float gi = g[i];
-            const float mm = hs.b1 * m0 + hs.ob1 * gi;
-            const float vv = hs.b2 * v0 + hs.ob2 * (gi * gi);
-            const float den = sqrtf(vv) * hs.s2 + hs.eps;
-            p[i] = p[i] * hs.dec - hs.s1 * (mm / den);
-            m1[i] = mm;
-            v1[i] = vv;
-            mxm = max(mxm, fbits(mm) & 0x7FFFFFFFu);
-            mxv = max(mxv, fbits(vv) & 0x7FFFFFFFu);
-        }
-        if (full) {
+        for (int c = 0; c < T::CH; ++c) {
+            uint32_t wm = 0, wv = 0;
 #pragma unroll
-            for (int c = 0; c < T::CH; ++c)
-                *reinterpret_cast<float4*>(d.p + bstart + c * T::LPB * 4 + l * 4) =
-                    make_float4(p[c * 4], p[c * 4 + 1], p[c * 4 + 2], p[c * 4 + 3]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < T::CH; ++c)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t idx = bstart + c * T::LPB * 4 + l * 4 + j;
-                    if (idx < nloc) d.p[idx] = p[c * 4 + j];
-                }
-        }
-
-        // new block absmax of m' and v'
-        block_max2<T>(mxm, mxv, s_red[par], tid);
-        const float am1 = ffrom(mxm), av1 = ffrom(mxv);
-        if (l == 0 && blk < nbl) {
-            d.am[blk] = am1;
-            d.av[blk] = av1;
-        }
-
-        // encode m' (signed) and v' (non-negative) with the dynamic code
-        const float rm = am1 > 0.0f ? 1.0f / am1 : 0.0f;
-        const float rv = av1 > 0.0f ? 1.0f / av1 : 0.0f;
-        const bool fast = fast_div_ok(am1) && fast_div_ok(av1);
-        uint32_t om[T::CH], ov[T::CH];
-        if (__all(fast)) {
-#pragma unroll
-            for (int c = 0; c < T::CH; ++c) {
-                uint32_t wm = 0, wv = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    wm |= enc_dyn8(div_by_block(m1[c * 4 + j], am1, rm), s_lut) << (8 * j);
-                    wv |= enc_dyn8_pos(div_by_block(v1[c * 4 + j], av1, rv), s_lut) << (8 * j);
-                }
-                om[c] = wm;
-                ov[c] = wv;
+            for (int j = 0; j < 4; ++j) {
+                wm |= enc_dyn8(div_by_block(m1[c * 4 + j], am1, rm), s_enc) << (8 * j);
+                wv |= enc_dyn8_pos(div_by_block(v1[c * 4 + j], av1, rv), s_enc) << (8 * j);
             }
-        } else {
-            const bool fm = fast_div_ok(am1), fv = fast_div_ok(av1);
-#pragma unroll
-            for (int c = 0; c < T::CH; ++c) {
-                uint32_t wm = 0, wv = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float mm = m1[c * 4 + j], vv = v1[c * 4 + j];
-                    const float nm = fm ? div_by_block(mm, am1, rm) : (am1 > 0.0f ? mm / am1 : 0.0f);
-                    const float nv = fv ? div_by_block(vv, av1, rv) : (av1 > 0.0f ? vv / av1 : 0.0f);
-                    wm |= enc_dyn8(nm, s_lut) << (8 * j);
-                    wv |= enc_dyn8_pos(nv, s_lut) << (8 * j);
-                }
-                om[c] = wm;
-                ov[c] = wv;
-            }
+            om[c] = wm;
+            ov[c] = wv;
         }
-        if (full) {
+    } else {
+        const bool fm = fast_div_ok(am1), fv = fast_div_ok(av1);
 #pragma unroll
-            for (int c = 0; c < T::CH; ++c) {
-                const int64_t e0 = bstart + c * T::LPB * 4 + l * 4;
-                *reinterpret_cast<uint32_t*>(d.m + e0) = om[c];
-                *reinterpret_cast<uint32_t*>(d.v + e0) = ov[c];
+        for (int c = 0; c < T::CH; ++c) {
+            uint32_t wm = 0, wv = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float mm = m1[c * 4 + j], vv = v1[c * 4 + j];
+                const float nm = fm ? div_by_block(mm, am1, rm) : (am1 > 0.0f ? mm / am1 : 0.0f);
+                const float nv = fv ? div_by_block(vv, av1, rv) : (av1 > 0.0f ? vv / av1 : 0.0f);
+                wm |= enc_dyn8(nm, s_enc) << (8 * j);
+                wv |= enc_dyn8_pos(nv, s_enc) << (8 * j);
             }
-        } else {
-#pragma unroll
-            for (int c = 0; c < T::CH; ++c)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t idx = bstart + c * T::LPB * 4 + l * 4 + j;
-                    if (idx < nloc) {
-                        d.m[idx] = (uint8_t)(om[c] >> (8 * j));
-                        d.v[idx] = (uint8_t)(ov[c] >> (8 * j));
-                    }
-                }
+            om[c] = wm;
+            ov[c] = wv;
         }
+    }
+    if (full) {
+#pragma unroll
+        for (int c = 0; c < T::CH; ++c) {
+            const uint32_t e = lofs + c * T::LPB * 4;
+            gsto<uint32_t>(mt, e, om[c]);
+            gsto<uint32_t>(vt, e, ov[c]);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < T::CH; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = lofs + c * T::LPB * 4 + j;
+                if ((int64_t)e < lrem) {
+                    gsto<uint8_t>(mt, e, (uint8_t)(om[c] >> (8 * j)));
+                    gsto<uint8_t>(vt, e, (uint8_t)(ov[c] >> (8 * j)));
+                }
+            }
     }
 }
 
 int64_t adamw_tiles(int64_t n, int B)
 {
-    const int64_t elems = (int64_t)kThreads * (B >= 1024 ? B / 256 : 4);
+    const int64_t elems = (int64_t)kAdamThreads * (B >= 4 * kAdamThreads ? B / kAdamThreads : 4);
     return (n + elems - 1) / elems;
 }
 
@@ -234,13 +259,15 @@ template <int B, int GDT>
 hipError_t adamw_as(const TensorDesc& single, const TensorDesc* descs, int count, int64_t ntiles,
                     const AdamScalars& hs, const QbTables* tab, hipStream_t s)
 {
-    static_assert(TileA<B>::ELEMS == kThreads * (B >= 1024 ? B / 256 : 4), "tile size");
+    static_assert(TileA<B>::ELEMS == kAdamThreads * (B >= 4 * kAdamThreads ? B / kAdamThreads : 4), "tile size");
+    if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     if (descs) {
-        auto kern = k_adamw8<B, GDT, true>;
-        return launch_kernel(kern, persistent_grid(kern, ntiles), s, single, descs, count, ntiles, hs, tab);
+        const int64_t* tile_begin = reinterpret_cast<const int64_t*>(descs + count);
+        return launch_kernel_nt(k_adamw8<B, GDT, true>, (int)ntiles, kAdamThreads, s, single, descs, tile_begin, count,
+                                hs, tab);
     }
-    auto kern = k_adamw8<B, GDT, false>;
-    return launch_kernel(kern, persistent_grid(kern, ntiles), s, single, descs, count, ntiles, hs, tab);
+    return launch_kernel_nt(k_adamw8<B, GDT, false>, (int)ntiles, kAdamThreads, s, single, descs,
+                            (const int64_t*)nullptr, count, hs, tab);
 }
 
 template <int B>

@@ -122,7 +122,8 @@ size_t qb_dq_workspace_bytes(int64_t n, int32_t blocksize)
 
 size_t qb_multi_tensor_workspace_bytes(int32_t count)
 {
-    return count > 0 ? (size_t)count * sizeof(TensorDesc) : 0;
+    // descriptors, then count + 1 int64 first-tile numbers
+    return count > 0 ? (size_t)count * sizeof(TensorDesc) + ((size_t)count + 1) * sizeof(int64_t) : 0;
 }
 
 int32_t qb_codebook(qb_code code, float* out)
@@ -141,13 +142,20 @@ int32_t qb_encoder_table(qb_code code, uint32_t* out, int32_t capacity)
 {
     const QbTables* t = host_tables();
     if (!t || !valid_code(code) || capacity < 0 || (capacity > 0 && !out)) return -1;
-    const LutEntry* src = code == QB_DYN8 ? t->dyn8_lut : (code == QB_NF4 ? t->nf4_lut : t->fp4_lut);
-    const int32_t count = code == QB_DYN8 ? kDynLutN : k4LutN;
-    for (int32_t i = 0; i < count && i < capacity; ++i) {
+    if (code == QB_DYN8) {
+        for (int32_t i = 0; i < 2 * kDynLutN && i < capacity; ++i) {
+            const int c = t->dyn8_base[i / kDynLutN][i % kDynLutN];
+            out[2 * i] = t->dyn8_thr[c];
+            out[2 * i + 1] = (uint32_t)c;
+        }
+        return 2 * kDynLutN;
+    }
+    const LutEntry* src = code == QB_NF4 ? t->nf4_lut : t->fp4_lut;
+    for (int32_t i = 0; i < k4LutN && i < capacity; ++i) {
         out[2 * i] = src[i].t;
         out[2 * i + 1] = src[i].payload;
     }
-    return count;
+    return k4LutN;
 }
 
 qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int32_t blocksize,
@@ -248,7 +256,10 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
     if (!aligned16(ws)) return QB_EALIGN;
     if (ws_bytes < qb_multi_tensor_workspace_bytes(count)) return QB_EWORKSPACE;
     thread_local std::vector<TensorDesc> table;
+    thread_local std::vector<int64_t> begins;
+    thread_local std::vector<unsigned char> staging;
     table.clear();
+    begins.clear();
     int64_t tiles = 0;
     for (int32_t i = 0; i < count; ++i) {
         const qb_tensor& t = tensors[i];
@@ -261,12 +272,19 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
             !aligned16(t.absmax_v))
             return QB_EALIGN;
         table.push_back(TensorDesc{t.p, t.g, t.m, t.v, t.absmax_m, t.absmax_v, t.n, tiles});
+        begins.push_back(tiles);
         tiles += adamw_tiles(t.n, blocksize);
     }
     if (table.empty()) return QB_OK;
+    if (tiles >= (int64_t(1) << 31)) return QB_EINVAL;
+    begins.push_back(tiles);
     if (!device_tables()) return QB_EINIT;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(ws, table.data(), table.size() * sizeof(TensorDesc), hipMemcpyHostToDevice, s);
+    const size_t dbytes = table.size() * sizeof(TensorDesc), bbytes = begins.size() * sizeof(int64_t);
+    staging.resize(dbytes + bbytes);
+    std::memcpy(staging.data(), table.data(), dbytes);
+    std::memcpy(staging.data() + dbytes, begins.data(), bbytes);
+    hipError_t e = hipMemcpyAsync(ws, staging.data(), staging.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return QB_EHIP;
     return hip_status(launch_adamw8(table[0], static_cast<const TensorDesc*>(ws), (int)table.size(), tiles,
                                     blocksize, (int)gdt, prepare(*hp), s));

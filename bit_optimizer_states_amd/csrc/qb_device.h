@@ -15,6 +15,60 @@ __device__ __forceinline__ uint32_t fbits(float f) { return __float_as_uint(f); 
 __device__ __forceinline__ float ffrom(uint32_t u) { return __uint_as_float(u); }
 
 // ---------------------------------------------------------------------------
+// global-memory access
+// ---------------------------------------------------------------------------
+//
+// Pointers read from memory (the multi-tensor descriptor table) are generic;
+// casting to the global address space makes every access a GLOBAL
+// instruction instead of FLAT (which also counts against the LDS counter).
+
+#define QB_G __attribute__((address_space(1)))
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <class T>
+__device__ __forceinline__ T gld(const void* p)
+{
+    return *(const QB_G T*)p;
+}
+
+template <class T>
+__device__ __forceinline__ void gst(void* p, T v)
+{
+    *(QB_G T*)p = v;
+}
+
+// Access at a uniform base pointer plus a 32-bit byte offset: the form the
+// GLOBAL instructions take directly (scalar base, vector offset), with no
+// 64-bit address arithmetic per lane.
+// Streaming data (read once, written once) takes non-temporal loads and
+// stores: measured on MI355X, the fused AdamW step runs about 10% faster than
+// with ordinary accesses (the same bytes reach HBM either way).
+#ifndef QB_NT_LOADS
+#define QB_NT_LOADS 1
+#endif
+#ifndef QB_NT_STORES
+#define QB_NT_STORES 1
+#endif
+
+template <class T>
+__device__ __forceinline__ T gldo(const void* base, uint32_t byte_off)
+{
+    const QB_G T* p = (const QB_G T*)(static_cast<const char*>(base) + byte_off);
+    if constexpr (QB_NT_LOADS) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <class T>
+__device__ __forceinline__ void gsto(void* base, uint32_t byte_off, T v)
+{
+    QB_G T* p = (QB_G T*)(static_cast<char*>(base) + byte_off);
+    if constexpr (QB_NT_STORES) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// ---------------------------------------------------------------------------
 // element loads / stores (16-bit types travel as raw halves)
 // ---------------------------------------------------------------------------
 
@@ -29,49 +83,80 @@ __device__ __forceinline__ float f16_lo(uint32_t w)
 }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return f16_lo(w >> 16); }
 
+template <int DT>
+__device__ __forceinline__ float half_lo(uint32_t w) { return DT == DT_BF16 ? bf16_lo(w) : f16_lo(w); }
+template <int DT>
+__device__ __forceinline__ float half_hi(uint32_t w) { return DT == DT_BF16 ? bf16_hi(w) : f16_hi(w); }
+
 // 4 consecutive elements at element index i (16-byte aligned for fp32, 8 for 16-bit).
 template <int DT>
-__device__ __forceinline__ void load4(const void* __restrict__ base, int64_t i, float* v)
+__device__ __forceinline__ void load4(const void* base, int64_t i, float* v)
 {
     if constexpr (DT == DT_F32) {
-        float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+        f32x4 x = gld<f32x4>(static_cast<const float*>(base) + i);
         v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     } else {
-        uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
-        if constexpr (DT == DT_BF16) {
-            v[0] = bf16_lo(x.x); v[1] = bf16_hi(x.x); v[2] = bf16_lo(x.y); v[3] = bf16_hi(x.y);
-        } else {
-            v[0] = f16_lo(x.x); v[1] = f16_hi(x.x); v[2] = f16_lo(x.y); v[3] = f16_hi(x.y);
-        }
+        u32x2 x = gld<u32x2>(static_cast<const uint16_t*>(base) + i);
+        v[0] = half_lo<DT>(x.x); v[1] = half_hi<DT>(x.x); v[2] = half_lo<DT>(x.y); v[3] = half_hi<DT>(x.y);
+    }
+}
+
+// 4 consecutive elements at element offset i (uint32) from a uniform base.
+template <int DT>
+__device__ __forceinline__ void load4o(const void* base, uint32_t i, float* v)
+{
+    if constexpr (DT == DT_F32) {
+        f32x4 x = gldo<f32x4>(base, i * 4u);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+        u32x2 x = gldo<u32x2>(base, i * 2u);
+        v[0] = half_lo<DT>(x.x); v[1] = half_hi<DT>(x.x); v[2] = half_lo<DT>(x.y); v[3] = half_hi<DT>(x.y);
     }
 }
 
 // 8 consecutive elements at element index i (16-byte aligned for every type).
 template <int DT>
-__device__ __forceinline__ void load8(const void* __restrict__ base, int64_t i, float* v)
+__device__ __forceinline__ void load8(const void* base, int64_t i, float* v)
 {
     if constexpr (DT == DT_F32) {
         load4<DT_F32>(base, i, v);
         load4<DT_F32>(base, i + 4, v + 4);
     } else {
-        uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + i);
+        u32x4 x = gld<u32x4>(static_cast<const uint16_t*>(base) + i);
         uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            v[2 * k] = DT == DT_BF16 ? bf16_lo(w[k]) : f16_lo(w[k]);
-            v[2 * k + 1] = DT == DT_BF16 ? bf16_hi(w[k]) : f16_hi(w[k]);
+            v[2 * k] = half_lo<DT>(w[k]);
+            v[2 * k + 1] = half_hi<DT>(w[k]);
+        }
+    }
+}
+
+// 8 consecutive elements at element offset i (uint32) from a uniform base.
+template <int DT>
+__device__ __forceinline__ void load8o(const void* base, uint32_t i, float* v)
+{
+    if constexpr (DT == DT_F32) {
+        load4o<DT_F32>(base, i, v);
+        load4o<DT_F32>(base, i + 4u, v + 4);
+    } else {
+        u32x4 x = gldo<u32x4>(base, i * 2u);
+        uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = half_lo<DT>(w[k]);
+            v[2 * k + 1] = half_hi<DT>(w[k]);
         }
     }
 }
 
 template <int DT>
-__device__ __forceinline__ float load1(const void* __restrict__ base, int64_t i)
+__device__ __forceinline__ float load1(const void* base, int64_t i)
 {
     if constexpr (DT == DT_F32) {
-        return static_cast<const float*>(base)[i];
+        return gld<float>(static_cast<const float*>(base) + i);
     } else {
-        uint32_t h = static_cast<const uint16_t*>(base)[i];
-        return DT == DT_BF16 ? bf16_lo(h) : f16_lo(h);
+        return half_lo<DT>(gld<uint16_t>(static_cast<const uint16_t*>(base) + i));
     }
 }
 
@@ -104,12 +189,64 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
 }
 
 template <int DT>
-__device__ __forceinline__ void store1(void* __restrict__ base, int64_t i, float v)
+__device__ __forceinline__ void store1(void* base, int64_t i, float v)
 {
     if constexpr (DT == DT_F32)
-        static_cast<float*>(base)[i] = v;
+        gst<float>(static_cast<float*>(base) + i, v);
     else
-        static_cast<uint16_t*>(base)[i] = (uint16_t)to_half_bits<DT>(v);
+        gst<uint16_t>(static_cast<uint16_t*>(base) + i, (uint16_t)to_half_bits<DT>(v));
+}
+
+// 4 consecutive outputs at element index i.
+template <int DT>
+__device__ __forceinline__ void store4(void* y, int64_t i, const float* o)
+{
+    if constexpr (DT == DT_F32) {
+        f32x4 v = {o[0], o[1], o[2], o[3]};
+        gst<f32x4>(static_cast<float*>(y) + i, v);
+    } else {
+        u32x2 v = {pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
+        gst<u32x2>(static_cast<uint16_t*>(y) + i, v);
+    }
+}
+
+// 4 consecutive outputs at element offset i (uint32) from a uniform base.
+template <int DT>
+__device__ __forceinline__ void store4o(void* y, uint32_t i, const float* o)
+{
+    if constexpr (DT == DT_F32) {
+        f32x4 v = {o[0], o[1], o[2], o[3]};
+        gsto<f32x4>(y, i * 4u, v);
+    } else {
+        u32x2 v = {pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
+        gsto<u32x2>(y, i * 2u, v);
+    }
+}
+
+// 8 consecutive outputs at element offset i (uint32) from a uniform base.
+template <int DT>
+__device__ __forceinline__ void store8o(void* y, uint32_t i, const float* o)
+{
+    if constexpr (DT == DT_F32) {
+        store4o<DT_F32>(y, i, o);
+        store4o<DT_F32>(y, i + 4u, o + 4);
+    } else {
+        u32x4 v = {pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3]), pack2<DT>(o[4], o[5]), pack2<DT>(o[6], o[7])};
+        gsto<u32x4>(y, i * 2u, v);
+    }
+}
+
+// 8 consecutive outputs at element index i.
+template <int DT>
+__device__ __forceinline__ void store8(void* y, int64_t i, const float* o)
+{
+    if constexpr (DT == DT_F32) {
+        store4<DT_F32>(y, i, o);
+        store4<DT_F32>(y, i + 4, o + 4);
+    } else {
+        u32x4 v = {pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3]), pack2<DT>(o[4], o[5]), pack2<DT>(o[6], o[7])};
+        gst<u32x4>(static_cast<uint16_t*>(y) + i, v);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -125,8 +262,18 @@ __device__ __forceinline__ uint32_t lanes_max(uint32_t x)
     if constexpr (L >= 4) x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
     if constexpr (L >= 8) x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
     if constexpr (L >= 16) x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false)); // row_mirror
-    if constexpr (L >= 32) x = max(x, (uint32_t)__shfl_xor((int)x, 16));
-    if constexpr (L >= 64) x = max(x, (uint32_t)__shfl_xor((int)x, 32));
+    if constexpr (L == 32) {
+        // rows are 16 lanes: the maxima of rows 0|1 and 2|3, taken from one
+        // lane of each row (uniform scalar values)
+        const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+        const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+        x = (__lane_id() < 32) ? a : b;
+    }
+    if constexpr (L == 64) {
+        const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+        const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+        x = max(a, b);
+    }
     return x;
 }
 
@@ -151,29 +298,69 @@ __device__ __forceinline__ bool fast_div_ok(float a)
     return a >= 0x1p-60f && a <= 0x1p60f;
 }
 
+// RN(1/a) for 2^-60 <= a <= 2^60: the hardware reciprocal (about 1 ulp) and
+// one Newton step with fused multiply-adds.  Checked on gfx950 against the
+// IEEE quotient 1.0f / a for every significand at exponents -60, -20, -1, 0,
+// 1, 20 and 60 (no difference); the significand of the result does not
+// depend on the exponent of a in this range.
+__device__ __forceinline__ float rcp_rn(float a)
+{
+    const float r0 = __builtin_amdgcn_rcpf(a);
+    const float e = __builtin_fmaf(-a, r0, 1.0f);
+    return __builtin_fmaf(e, r0, r0);
+}
+
 // ---------------------------------------------------------------------------
 // encoders (tables staged in LDS)
 // ---------------------------------------------------------------------------
 
-// Dynamic 8-bit code of a normalized value in [-1, 1].
-__device__ __forceinline__ uint32_t enc_dyn8(float nv, const uint2* __restrict__ lut)
+// LDS copy of the dynamic-code encoder.  The base-code table is indexed
+// directly by (bits of the clamped |n|) >> 17, with the sign bit moved to bit
+// 13: the used entries sit at [kDynBase, kDynBase + 1409) and the same plus
+// 8192; the rest of the array is never read (it saves the index arithmetic).
+constexpr int kDynIdxSign = 8192;
+constexpr int kDynIdxBytes = kDynIdxSign + kDynBase + kDynBucketBytes;   // 16324
+
+struct DynEncLds {
+    uint32_t base[kDynIdxBytes / 4];
+    float thr[256];
+};
+
+// Stage the encoder tables (about 3.8 KB used) into LDS with NT threads.
+template <int NT = kThreads>
+__device__ __forceinline__ void stage_dyn_enc(DynEncLds& s, const QbTables* __restrict__ tab, int tid)
 {
-    uint32_t bits = fbits(nv);
-    uint32_t mag = bits & 0x7FFFFFFFu;
-    uint32_t cl = min(max(mag, kDynLowBits), kOneBits);
-    uint2 e = lut[(cl >> kDynShift) - kDynBase];
-    int cp = (int)e.y + (mag >= e.x ? 1 : 0);          // 127 .. 255
-    int cn = max(254 - cp, 0);                          // mirrored; -1.0 is not in the code
-    return (uint32_t)((int)bits < 0 ? cn : cp);
+    constexpr int W = kDynBucketBytes / 4;                     // 353 words per sign
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&tab->dyn8_base[0][0]);
+    constexpr int P = kDynBase / 4, N = (kDynIdxSign + kDynBase) / 4;
+#pragma unroll
+    for (int r = 0; r < (W + NT - 1) / NT; ++r) {
+        const int i = r * NT + tid;
+        if ((r + 1) * NT <= W || i < W) {
+            s.base[P + i] = src[i];
+            s.base[N + i] = src[W + i];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < (256 + NT - 1) / NT; ++r)
+        if (NT <= 256 || tid < 256) s.thr[r * NT + tid] = __uint_as_float(tab->dyn8_thr[r * NT + tid]);
+}
+
+// Dynamic 8-bit code of a normalized value in [-1, 1].
+__device__ __forceinline__ uint32_t enc_dyn8(float nv, const DynEncLds& s)
+{
+    const float cl = __builtin_amdgcn_fmed3f(__builtin_fabsf(nv), 0x1p-22f, 1.0f);
+    const uint32_t idx = (fbits(cl) >> kDynShift) | ((fbits(nv) >> 31) << 13);
+    const uint32_t c = reinterpret_cast<const uint8_t*>(s.base)[idx];
+    return c + (nv >= s.thr[c] ? 1u : 0u);
 }
 
 // Same for a value known to be >= 0 (+0 included).
-__device__ __forceinline__ uint32_t enc_dyn8_pos(float nv, const uint2* __restrict__ lut)
+__device__ __forceinline__ uint32_t enc_dyn8_pos(float nv, const DynEncLds& s)
 {
-    uint32_t mag = fbits(nv);
-    uint32_t cl = min(max(mag, kDynLowBits), kOneBits);
-    uint2 e = lut[(cl >> kDynShift) - kDynBase];
-    return e.y + (mag >= e.x ? 1u : 0u);
+    const float cl = __builtin_amdgcn_fmed3f(nv, 0x1p-22f, 1.0f);
+    const uint32_t c = reinterpret_cast<const uint8_t*>(s.base)[fbits(cl) >> kDynShift];
+    return c + (nv >= s.thr[c] ? 1u : 0u);
 }
 
 // 4-bit code (NF4 or FP4 by the table) of a normalized value in [-1, 1].

@@ -13,9 +13,11 @@ namespace qb {
 
 enum QuantMode { QM_PLAIN = 0, QM_DQ_FIRST = 1, QM_DQ_SECOND = 2 };
 
-// Exponent bins of the nested-quantization mean: 256 uint64 words at the start
-// of the workspace (254 used), then the fp32 absmax of the first level.
-constexpr size_t kBinWords = 256;
+// Exponent bins of the nested-quantization mean at the start of the workspace:
+// kBinCopies copies of 256 uint64 words (254 used; the copies spread the
+// atomics of different workgroups), then the fp32 absmax of the first level.
+constexpr int kBinCopies = 8;
+constexpr size_t kBinWords = (size_t)kBinCopies * 256;
 constexpr size_t kBinBytes = kBinWords * sizeof(unsigned long long);
 
 struct AdamScalars {
@@ -61,15 +63,21 @@ int persistent_grid(Kernel kernel, int64_t ntiles)
 // Enqueue `kernel` with 256-thread workgroups; returns this launch's own
 // status (a stale error of an earlier call is neither returned nor cleared).
 template <typename... KArgs, typename... Args>
-hipError_t launch_kernel(void (*kernel)(KArgs...), int grid, hipStream_t s, Args&&... args)
+hipError_t launch_kernel_nt(void (*kernel)(KArgs...), int grid, int threads, hipStream_t s, Args&&... args)
 {
     std::tuple<KArgs...> vals(std::forward<Args>(args)...);
     return std::apply(
         [&](auto&... v) {
             void* ptrs[] = {static_cast<void*>(&v)...};
-            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(256), ptrs, 0, s);
+            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(threads), ptrs, 0, s);
         },
         vals);
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), int grid, hipStream_t s, Args&&... args)
+{
+    return launch_kernel_nt(kernel, grid, 256, s, std::forward<Args>(args)...);
 }
 
 hipError_t launch_clear_bins(unsigned long long* bins, hipStream_t s);
@@ -83,6 +91,8 @@ hipError_t launch_dequant8(const uint8_t* codes, const float* absmax, const uint
 hipError_t launch_dequant4(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
                            const float* offset, int B, int B2, int64_t n, int code4, void* y, int ydt,
                            hipStream_t s);
+// descs: device table of `count` descriptors followed by count + 1 int64 tile
+// offsets (tile_begin of each tensor, then the total); nullptr for one tensor.
 hipError_t launch_adamw8(const TensorDesc& single, const TensorDesc* descs, int count, int64_t ntiles, int B,
                          int gdt, const AdamScalars& hs, hipStream_t s);
 

@@ -49,12 +49,12 @@ int persistent_grid_cap(const void* kernel, int (*query)(const void*))
 
 __global__ __launch_bounds__(256) void k_clear_bins(unsigned long long* __restrict__ bins)
 {
-    bins[threadIdx.x] = 0ull;
+#pragma unroll
+    for (int k = 0; k < kBinCopies; ++k) bins[k * 256 + threadIdx.x] = 0ull;
 }
 
 hipError_t launch_clear_bins(unsigned long long* bins, hipStream_t s)
 {
-    static_assert(kBinWords == 256, "one workgroup clears the bins");
     return launch_kernel(k_clear_bins, 1, s, bins);
 }
 

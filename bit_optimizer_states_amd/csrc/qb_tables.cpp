@@ -130,20 +130,23 @@ std::vector<float> thresholds(const std::vector<float>& vals)
     return t;
 }
 
-int build_dyn8_lut(const float* dyn8, LutEntry* lut)
+int build_dyn8_lut(const float* dyn8, uint8_t (*base)[kDynBucketBytes], uint32_t* thr)
 {
-    std::vector<float> mags(dyn8 + 127, dyn8 + 256);   // 0, positive entries, 1.0
-    std::vector<float> t = thresholds(mags);           // 128 thresholds
-    std::vector<uint32_t> tb(t.size());
-    for (size_t i = 0; i < t.size(); ++i) tb[i] = bits_of(t[i]);
-    for (int b = 0; b < kDynLutN; ++b) {
-        uint32_t lo = b == 0 ? 0u : uint32_t(b + kDynBase) << kDynShift;
-        uint32_t hi = b == kDynLutN - 1 ? kOneBits : (uint32_t(b + kDynBase + 1) << kDynShift) - 1u;
-        int k = 0;
-        while (k < (int)tb.size() && tb[k] <= lo) ++k;
-        if (k + 1 < (int)tb.size() && tb[k + 1] <= hi) return -1;   // two thresholds in one bucket
-        lut[b].t = k < (int)tb.size() ? tb[k] : 0x7F800000u;
-        lut[b].payload = 127u + (uint32_t)k;
+    std::vector<float> vals(dyn8, dyn8 + 256);
+    std::vector<float> T = thresholds(vals);            // 255 signed thresholds, ascending
+    for (int c = 0; c < 256; ++c) thr[c] = c < 255 ? bits_of(T[c]) : 0x7F800000u;
+    for (int sign = 0; sign < 2; ++sign) {
+        for (int b = 0; b < kDynLutN; ++b) {
+            // magnitudes of bucket b: [mlo, mhi] (bucket 0 also takes every |n| below 2^-22,
+            // the last bucket only 1.0)
+            const float mlo = b == 0 ? 0.0f : float_of(uint32_t(b + kDynBase) << kDynShift);
+            const float mhi = b == kDynLutN - 1 ? 1.0f : float_of((uint32_t(b + kDynBase + 1) << kDynShift) - 1u);
+            const float lo = sign ? -mhi : mlo, hi = sign ? -mlo : mhi;   // n in [lo, hi]
+            int c = 0;
+            while (c < 255 && T[c] <= lo) ++c;            // code at n = lo
+            if (c + 1 < 255 && T[c + 1] <= hi) return -1;  // two thresholds in one bucket
+            base[sign][b] = (uint8_t)c;
+        }
     }
     return 0;
 }
@@ -221,9 +224,8 @@ int self_check(const QbTables* T)
         if (!(x >= -1.0f && x <= 1.0f)) continue;
         uint32_t mag = bits_of(x) & 0x7FFFFFFFu;
         uint32_t cl = std::min(std::max(mag, kDynLowBits), kOneBits);
-        const LutEntry& e = T->dyn8_lut[(cl >> kDynShift) - kDynBase];
-        int cp = (int)e.payload + (mag >= e.t ? 1 : 0);
-        int code = x < 0 ? std::max(254 - cp, 0) : cp;
+        const int c0 = T->dyn8_base[bits_of(x) >> 31][(cl >> kDynShift) - kDynBase];
+        int code = c0 + (x >= float_of(T->dyn8_thr[c0]) ? 1 : 0);
         if (code != nearest(dyn, x)) return -10;
         const LutEntry& f = T->nf4_lut[bucket4(x)];
         int c4 = (x >= float_of(f.t)) ? (int)((f.payload >> 8) & 0xFF) : (int)(f.payload & 0xFF);
@@ -242,7 +244,7 @@ int build_tables(QbTables* T)
     build_fp4(T->fp4);
     for (int i = 0; i < 255; ++i)
         if (!(T->dyn8[i] < T->dyn8[i + 1])) return -2;
-    if (build_dyn8_lut(T->dyn8, T->dyn8_lut) != 0) return -3;
+    if (build_dyn8_lut(T->dyn8, T->dyn8_base, T->dyn8_thr) != 0) return -3;
 
     std::vector<float> nf4(T->nf4, T->nf4 + 16);
     std::vector<uint32_t> nf4_codes(16);
@@ -256,14 +258,6 @@ int build_tables(QbTables* T)
     fp4.push_back(0.0f); fp4_codes.push_back(0u);
     for (int k = 1; k <= 7; ++k) { fp4.push_back(T->fp4[k]); fp4_codes.push_back((uint32_t)k); }
     if (build_4bit_lut(fp4, fp4_codes, T->fp4_lut) != 0) return -5;
-
-    for (int c = 0; c < 2; ++c) {
-        const float* val = c == 0 ? T->nf4 : T->fp4;
-        for (int byte = 0; byte < 256; ++byte) {
-            T->pair[c][byte][0] = val[byte >> 4];
-            T->pair[c][byte][1] = val[byte & 15];
-        }
-    }
     return self_check(T);
 }
 

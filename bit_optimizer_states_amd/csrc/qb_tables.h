@@ -25,14 +25,23 @@ struct LutEntry {
     uint32_t payload;  // DYN8: 127 + thresholds below the bucket; 4-bit: code below | code above << 8
 };
 
+// Dynamic 8-bit encoder.  The code is monotone in n, so with the 255 signed
+// decision thresholds T[c] (smallest binary32 that encodes to c+1 or above;
+// T[255] = +inf) the code of n is c + (n >= T[c]) once c, the code at the
+// start of n's bucket, is known.  Buckets split |n| by its bit pattern (6
+// mantissa bits each), separately for each sign; no bucket holds two
+// thresholds.  dyn8_base[s][b] is c for sign s (0: n >= 0, 1: n < 0) and
+// bucket b; dyn8_thr[c] holds T[c] as binary32 bits.
+constexpr int kDynBucketBytes = (kDynLutN + 3) / 4 * 4;   // 1412
+
 struct QbTables {
     float dyn8[256];               // decode, by stored code
     float nf4[16];
     float fp4[16];
-    LutEntry dyn8_lut[kDynLutN];
+    uint8_t dyn8_base[2][kDynBucketBytes];
+    uint32_t dyn8_thr[256];
     LutEntry nf4_lut[k4LutN];
     LutEntry fp4_lut[k4LutN];
-    float pair[2][256][2];         // [nf4, fp4][byte] -> {value of high nibble, value of low nibble}
 };
 
 // Builds every table; returns 0, or a negative value if a self-check fails.

@@ -47,15 +47,16 @@ def test_codebooks_equal_oracle(qb, code):
 
 def emulate_dyn8(table, x):
     """The kernels' dynamic-code encoder, from the library's bucket table."""
-    t = np.array([e[0] for e in table], dtype=np.uint32)
+    assert len(table) == 2 * 1409
+    t = np.array([e[0] for e in table], dtype=np.uint32).view(np.float32)
     pay = np.array([e[1] for e in table], dtype=np.int64)
-    bits = x.astype(np.float32).view(np.uint32)
+    x = x.astype(np.float32)
+    bits = x.view(np.uint32)
     mag = bits & np.uint32(0x7FFFFFFF)
     low, one = np.uint32(105 << 23), np.uint32(0x3F800000)
     cl = np.minimum(np.maximum(mag, low), one)
-    b = (cl >> np.uint32(17)).astype(np.int64) - (105 << 6)
-    cp = pay[b] + (mag >= t[b])
-    return np.where(bits >> np.uint32(31) == 1, np.maximum(254 - cp, 0), cp).astype(np.uint8)
+    b = (cl >> np.uint32(17)).astype(np.int64) - (105 << 6) + 1409 * (bits >> np.uint32(31)).astype(np.int64)
+    return (pay[b] + (x >= t[b])).astype(np.uint8)
 
 
 def emulate_4bit(table, x):
@@ -104,10 +105,10 @@ def test_4bit_bucket_encoder_equals_oracle(qb, code):
 
 
 def test_workspace_sizes(qb):
-    assert qb.qb_dq_workspace_bytes(64 * 1000, 64) == 2048 + 4096
-    assert qb.qb_dq_workspace_bytes(0, 64) == 2048
+    assert qb.qb_dq_workspace_bytes(64 * 1000, 64) == 16384 + 4096
+    assert qb.qb_dq_workspace_bytes(0, 64) == 16384
     assert qb.qb_dq_workspace_bytes(100, 63) == 0
-    assert qb.qb_multi_tensor_workspace_bytes(291) == 291 * 64
+    assert qb.qb_multi_tensor_workspace_bytes(291) == 291 * 64 + 292 * 8
     assert qb.qb_multi_tensor_workspace_bytes(0) == 0
 
 
@@ -141,7 +142,7 @@ def test_invalid_arguments_rejected_before_launch(qb):
     assert L.qb_multi_tensor_step(tab, 1, 2, 2048, ctypes.byref(hp), A, 10, None) == qb.QB_EWORKSPACE
     assert L.qb_multi_tensor_step(tab, 0, 2, 2048, ctypes.byref(hp), A, 0, None) == qb.QB_OK
     tab_bad = (qb.qb_tensor * 1)(qb.qb_tensor(A, A2 + 8, A, A, A, A, 100))
-    assert L.qb_multi_tensor_step(tab_bad, 1, 2, 2048, ctypes.byref(hp), A, 64, None) == qb.QB_EALIGN
+    assert L.qb_multi_tensor_step(tab_bad, 1, 2, 2048, ctypes.byref(hp), A, 80, None) == qb.QB_EALIGN
 
 
 def test_status_strings(qb):
