@@ -200,6 +200,40 @@ def cpu_baseline(torch, model, seconds_target, rng):
     }
 
 
+def bench_flat(torch, qb, inputs, dev, args):
+    """Single-tensor fused AdamW8bit step on a flat 1,500,000,000-parameter fp32
+    buffer (bf16 gradients ~N(0, 1e-3), two sets alternating; block 2048)."""
+    n = 1_500_000_000
+    nb = (n + ADAM_BLOCK - 1) // ADAM_BLOCK
+    log(f"allocating a flat buffer of {n:,} params")
+    p = inputs.normal(n, 0.02, seed=args.seed, device=dev)
+    m = torch.full((n,), 127, dtype=torch.uint8, device=dev)
+    v = torch.full((n,), 127, dtype=torch.uint8, device=dev)
+    am = torch.zeros(nb, device=dev)
+    av = torch.zeros(nb, device=dev)
+    grads = [inputs.normal(n, 1e-3, inputs.grad_seed(args.seed, 0, k), device=dev, dtype=torch.bfloat16) for k in range(2)]
+    torch.cuda.synchronize()
+    for k in range(1, args.warmup + 1):
+        qb.qb_adamw8bit_step(p, grads[k % 2], n, m, v, am, av, ADAM_BLOCK, qb.hparams(step=k, **HP))
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        k = args.warmup + 1 + i
+        evs[i][0].record()
+        qb.qb_adamw8bit_step(p, grads[k % 2], n, m, v, am, av, ADAM_BLOCK, qb.hparams(step=k, **HP))
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    med = ms[len(ms) // 2]
+    nbytes = n * adam_bytes_per_param()
+    print(json.dumps({"workload": "flat 1.5e9 fp32 params, bf16 grads, block 2048, single-tensor AdamW8bit",
+                      "steps": args.steps, "median_ms": med, "GB/s": nbytes / med / 1e6,
+                      "params_per_s": n / med * 1e3, "frac_of_hbm_peak": nbytes / med / 1e6 / HBM_PEAK_GBS,
+                      "wall_ms_per_step": wall / args.steps * 1e3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +242,8 @@ def main():
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adam-only", action="store_true", help="time only the multi-tensor AdamW step")
+    ap.add_argument("--flat", action="store_true",
+                    help="time the single-tensor AdamW step on a flat 1.5e9-parameter buffer instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1",
@@ -223,6 +259,8 @@ def main():
     qb.lib()
     dev = "cuda:0"
     rng = np.random.default_rng(args.seed)
+    if args.flat:
+        return bench_flat(torch, qb, inputs, dev, args)
     model = Model7B(torch, qb, inputs, dev, args.seed, with_w4=not args.adam_only)
     torch.cuda.synchronize()
     log(f"setup done; warmup {args.warmup} steps")
