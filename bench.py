@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0
 ADAM_BLOCK = 2048
 W4_BLOCK, W4_BLOCK2 = 64, 256
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw8bit_multi_7b.traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_adamw8_multi.llama7b_step.traffic.json")
 
 
 def log(msg):
@@ -151,7 +151,7 @@ def cpu_baseline(torch, model, seconds_target, rng):
     seeded full AdamW blocks of the 7B model (copied from the device) plus one
     4096x11008 weight quantized (NF4 + nested) and dequantized to bf16."""
     import oracle
-    nblocks = 65536
+    nblocks = 98304
     # sample full blocks in proportion to the tensors' block counts
     full_blocks = np.array([n // ADAM_BLOCK for n in model.sizes], dtype=np.int64)
     prob = full_blocks / full_blocks.sum()
@@ -234,6 +234,19 @@ def bench_flat(torch, qb, inputs, dev, args):
                       "wall_ms_per_step": wall / args.steps * 1e3}), flush=True)
 
 
+def copy_calibration(torch, dev):
+    """Five device-to-device copies of exactly 1 GiB: 1,073,741,824 bytes read and
+    written per dispatch.  Profiling this under FETCH_SIZE / WRITE_SIZE gives the
+    factor that turns those counters into HBM bytes for the kernels above."""
+    a = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": 1 << 30, "dispatches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +257,8 @@ def main():
     ap.add_argument("--adam-only", action="store_true", help="time only the multi-tensor AdamW step")
     ap.add_argument("--flat", action="store_true",
                     help="time the single-tensor AdamW step on a flat 1.5e9-parameter buffer instead")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device-to-device five times (the reference kernel for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1",
@@ -256,8 +271,10 @@ def main():
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
-    qb.lib()
     dev = "cuda:0"
+    if args.copy_calibration:
+        return copy_calibration(torch, dev)
+    qb.lib()
     rng = np.random.default_rng(args.seed)
     if args.flat:
         return bench_flat(torch, qb, inputs, dev, args)
