@@ -10,8 +10,10 @@
 //
 // One 256-thread workgroup per tile (a tile is one block for B >= 1024), in
 // tile order.  For many tensors, the tiles of all tensors are numbered in one
-// range; a workgroup finds its tensor by a binary search over the tensors'
-// first tile numbers (uniform, scalar loads that stay in the scalar cache).
+// range; a workgroup finds its tensor from a coarse bucket index (the tensor
+// holding the bucket's first tile) and, only where a bucket spans several
+// tensors, a binary search among those (uniform, scalar loads that stay in
+// the scalar cache).
 #include "qb_device.h"
 #include "qb_launch.h"
 
@@ -123,9 +125,8 @@ __device__ __forceinline__ void block_max2(uint32_t& x, uint32_t& y, uint32_t (*
 }
 
 template <int B, int GDT, bool MULTI>
-__global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, const TensorDesc* __restrict__ descs,
-                                                const int64_t* __restrict__ tile_begin, int count, AdamScalars hs,
-                                                const QbTables* __restrict__ tab)
+__global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, TileMap map, AdamScalars hs,
+                                                         const QbTables* __restrict__ tab)
 {
     using T = TileA<B>;
     __shared__ float s_dyn[256];
@@ -137,13 +138,16 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, cons
     TensorDesc d;
     int64_t lt;
     if constexpr (MULTI) {
-        int lo = 0, hi = count;                 // tile_begin[lo] <= tile < tile_begin[hi]
+        // tile_begin[lo] <= tile < tile_begin[hi]: the tensor holding the
+        // bucket's first tile, up to the one holding the next bucket's
+        const int64_t k = tile >> map.shift;
+        int lo = map.bucket_first[k], hi = map.bucket_first[k + 1] + 1;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (tile_begin[mid] <= tile) lo = mid; else hi = mid;
+            if (map.tile_begin[mid] <= tile) lo = mid; else hi = mid;
         }
-        d = descs[lo];
-        lt = tile - tile_begin[lo];
+        d = map.descs[lo];
+        lt = tile - d.tile_begin;
     } else {
         d = single;
         lt = tile;
@@ -315,47 +319,42 @@ int64_t adamw_tiles(int64_t n, int B)
 namespace {
 
 template <int B, int GDT>
-hipError_t adamw_as(const TensorDesc& single, const TensorDesc* descs, int count, int64_t ntiles,
-                    const AdamScalars& hs, const QbTables* tab, hipStream_t s)
+hipError_t adamw_as(const TensorDesc& single, const TileMap* map, int64_t ntiles, const AdamScalars& hs,
+                    const QbTables* tab, hipStream_t s)
 {
     static_assert(TileA<B>::ELEMS == kAdamThreads * (B >= 4 * kAdamThreads ? B / kAdamThreads : 4), "tile size");
     if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    if (descs) {
-        const int64_t* tile_begin = reinterpret_cast<const int64_t*>(descs + count);
-        return launch_kernel_nt(k_adamw8<B, GDT, true>, (int)ntiles, kAdamThreads, s, single, descs, tile_begin, count,
-                                hs, tab);
-    }
-    return launch_kernel_nt(k_adamw8<B, GDT, false>, (int)ntiles, kAdamThreads, s, single, descs,
-                            (const int64_t*)nullptr, count, hs, tab);
+    if (map) return launch_kernel_nt(k_adamw8<B, GDT, true>, (int)ntiles, kAdamThreads, s, single, *map, hs, tab);
+    return launch_kernel_nt(k_adamw8<B, GDT, false>, (int)ntiles, kAdamThreads, s, single, TileMap{}, hs, tab);
 }
 
 template <int B>
-hipError_t adamw_dt(int gdt, const TensorDesc& single, const TensorDesc* descs, int count, int64_t ntiles,
-                    const AdamScalars& hs, const QbTables* tab, hipStream_t s)
+hipError_t adamw_dt(int gdt, const TensorDesc& single, const TileMap* map, int64_t ntiles, const AdamScalars& hs,
+                    const QbTables* tab, hipStream_t s)
 {
     switch (gdt) {
-    case DT_F32: return adamw_as<B, DT_F32>(single, descs, count, ntiles, hs, tab, s);
-    case DT_F16: return adamw_as<B, DT_F16>(single, descs, count, ntiles, hs, tab, s);
-    case DT_BF16: return adamw_as<B, DT_BF16>(single, descs, count, ntiles, hs, tab, s);
+    case DT_F32: return adamw_as<B, DT_F32>(single, map, ntiles, hs, tab, s);
+    case DT_F16: return adamw_as<B, DT_F16>(single, map, ntiles, hs, tab, s);
+    case DT_BF16: return adamw_as<B, DT_BF16>(single, map, ntiles, hs, tab, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_adamw8(const TensorDesc& single, const TensorDesc* descs, int count, int64_t ntiles, int B,
-                         int gdt, const AdamScalars& hs, hipStream_t s)
+hipError_t launch_adamw8(const TensorDesc& single, const TileMap* map, int64_t ntiles, int B, int gdt,
+                         const AdamScalars& hs, hipStream_t s)
 {
     const QbTables* tab = device_tables();
     if (!tab) return hipErrorNotInitialized;
     switch (B) {
-    case 64: return adamw_dt<64>(gdt, single, descs, count, ntiles, hs, tab, s);
-    case 128: return adamw_dt<128>(gdt, single, descs, count, ntiles, hs, tab, s);
-    case 256: return adamw_dt<256>(gdt, single, descs, count, ntiles, hs, tab, s);
-    case 512: return adamw_dt<512>(gdt, single, descs, count, ntiles, hs, tab, s);
-    case 1024: return adamw_dt<1024>(gdt, single, descs, count, ntiles, hs, tab, s);
-    case 2048: return adamw_dt<2048>(gdt, single, descs, count, ntiles, hs, tab, s);
-    case 4096: return adamw_dt<4096>(gdt, single, descs, count, ntiles, hs, tab, s);
+    case 64: return adamw_dt<64>(gdt, single, map, ntiles, hs, tab, s);
+    case 128: return adamw_dt<128>(gdt, single, map, ntiles, hs, tab, s);
+    case 256: return adamw_dt<256>(gdt, single, map, ntiles, hs, tab, s);
+    case 512: return adamw_dt<512>(gdt, single, map, ntiles, hs, tab, s);
+    case 1024: return adamw_dt<1024>(gdt, single, map, ntiles, hs, tab, s);
+    case 2048: return adamw_dt<2048>(gdt, single, map, ntiles, hs, tab, s);
+    case 4096: return adamw_dt<4096>(gdt, single, map, ntiles, hs, tab, s);
     default: return hipErrorInvalidValue;
     }
 }

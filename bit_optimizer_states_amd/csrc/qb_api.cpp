@@ -122,8 +122,11 @@ size_t qb_dq_workspace_bytes(int64_t n, int32_t blocksize)
 
 size_t qb_multi_tensor_workspace_bytes(int32_t count)
 {
-    // descriptors, then count + 1 int64 first-tile numbers
-    return count > 0 ? (size_t)count * sizeof(TensorDesc) + ((size_t)count + 1) * sizeof(int64_t) : 0;
+    // descriptors, count + 1 int64 first-tile numbers, then the coarse bucket
+    // index (max_tile_buckets(count) + 1 int32 entries)
+    if (count <= 0) return 0;
+    return (size_t)count * sizeof(TensorDesc) + ((size_t)count + 1) * sizeof(int64_t) +
+           ((size_t)max_tile_buckets(count) + 1) * sizeof(int32_t);
 }
 
 int32_t qb_codebook(qb_code code, float* out)
@@ -243,7 +246,7 @@ qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, ui
     if (!device_tables()) return QB_EINIT;
     TensorDesc d{p, g, m, v, absmax_m, absmax_v, n, 0};
     const int64_t ntiles = adamw_tiles(n, blocksize);
-    return hip_status(launch_adamw8(d, nullptr, 1, ntiles, blocksize, (int)gdt, prepare(*hp),
+    return hip_status(launch_adamw8(d, nullptr, ntiles, blocksize, (int)gdt, prepare(*hp),
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -257,9 +260,11 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
     if (ws_bytes < qb_multi_tensor_workspace_bytes(count)) return QB_EWORKSPACE;
     thread_local std::vector<TensorDesc> table;
     thread_local std::vector<int64_t> begins;
+    thread_local std::vector<int32_t> buckets;
     thread_local std::vector<unsigned char> staging;
     table.clear();
     begins.clear();
+    buckets.clear();
     int64_t tiles = 0;
     for (int32_t i = 0; i < count; ++i) {
         const qb_tensor& t = tensors[i];
@@ -278,16 +283,32 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
     if (table.empty()) return QB_OK;
     if (tiles >= (int64_t(1) << 31)) return QB_EINVAL;
     begins.push_back(tiles);
+    // coarse index: the smallest bucket width 2^shift that needs at most
+    // max_tile_buckets(count) buckets; bucket k starts at tile k << shift
+    const int32_t used = (int32_t)table.size();
+    int shift = 0;
+    while (((tiles - 1) >> shift) + 1 > max_tile_buckets(count)) ++shift;
+    const int64_t nbk = ((tiles - 1) >> shift) + 1;
+    for (int64_t k = 0, i = 0; k < nbk; ++k) {
+        const int64_t first = k << shift;
+        while (begins[i + 1] <= first) ++i;          // begins[used] = tiles > first
+        buckets.push_back((int32_t)i);
+    }
+    buckets.push_back(used - 1);
     if (!device_tables()) return QB_EINIT;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t dbytes = table.size() * sizeof(TensorDesc), bbytes = begins.size() * sizeof(int64_t);
-    staging.resize(dbytes + bbytes);
+    const size_t dbytes = table.size() * sizeof(TensorDesc), bbytes = begins.size() * sizeof(int64_t),
+                 kbytes = buckets.size() * sizeof(int32_t);
+    staging.resize(dbytes + bbytes + kbytes);
     std::memcpy(staging.data(), table.data(), dbytes);
     std::memcpy(staging.data() + dbytes, begins.data(), bbytes);
+    std::memcpy(staging.data() + dbytes + bbytes, buckets.data(), kbytes);
     hipError_t e = hipMemcpyAsync(ws, staging.data(), staging.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return QB_EHIP;
-    return hip_status(launch_adamw8(table[0], static_cast<const TensorDesc*>(ws), (int)table.size(), tiles,
-                                    blocksize, (int)gdt, prepare(*hp), s));
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    const TileMap map{reinterpret_cast<const TensorDesc*>(w), reinterpret_cast<const int64_t*>(w + dbytes),
+                      reinterpret_cast<const int32_t*>(w + dbytes + bbytes), used, shift};
+    return hip_status(launch_adamw8(table[0], &map, tiles, blocksize, (int)gdt, prepare(*hp), s));
 }
 
 }  // extern "C"

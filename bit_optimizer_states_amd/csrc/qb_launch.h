@@ -37,6 +37,23 @@ struct TensorDesc {
 };
 static_assert(sizeof(TensorDesc) == 64, "descriptor layout");
 
+// Device tables of a multi-tensor launch: `count` descriptors; the first tile
+// of every tensor (count + 1 entries, the last one the total); and a coarse
+// index, bucket_first[k] = the tensor that holds tile k << shift (one entry
+// per bucket plus a last one = count - 1), so that a workgroup finds its tensor
+// with two dependent loads instead of a binary search over all tensors.
+struct TileMap {
+    const TensorDesc* descs;
+    const int64_t* tile_begin;
+    const int32_t* bucket_first;
+    int32_t count;
+    int32_t shift;
+};
+
+// Most buckets of the coarse index for `count` tensors (the workspace holds
+// this many + 1 int32 entries).
+constexpr int64_t max_tile_buckets(int64_t count) { return 2 * count + 64; }
+
 // Device copy of the constant tables for the current device (uploaded once).
 const QbTables* device_tables();
 
@@ -91,10 +108,10 @@ hipError_t launch_dequant8(const uint8_t* codes, const float* absmax, const uint
 hipError_t launch_dequant4(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
                            const float* offset, int B, int B2, int64_t n, int code4, void* y, int ydt,
                            hipStream_t s);
-// descs: device table of `count` descriptors followed by count + 1 int64 tile
-// offsets (tile_begin of each tensor, then the total); nullptr for one tensor.
-hipError_t launch_adamw8(const TensorDesc& single, const TensorDesc* descs, int count, int64_t ntiles, int B,
-                         int gdt, const AdamScalars& hs, hipStream_t s);
+// map: the device tables of a multi-tensor launch, or nullptr for the one
+// tensor `single`.
+hipError_t launch_adamw8(const TensorDesc& single, const TileMap* map, int64_t ntiles, int B, int gdt,
+                         const AdamScalars& hs, hipStream_t s);
 
 // Tiles of the AdamW kernel for a tensor of n elements at block size B.
 int64_t adamw_tiles(int64_t n, int B);

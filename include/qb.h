@@ -164,8 +164,9 @@ qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, ui
  *   tensors   host array of `count` descriptors (read during the call only).
  *   ws        device workspace of qb_multi_tensor_workspace_bytes(count) bytes;
  *             the call copies a table of the tensors (pointers, sizes, first
- *             tile numbers) into it on `stream`, so ws must not be reused by
- *             another stream until the step has run.
+ *             tile numbers, and a coarse index from tile ranges to tensors)
+ *             into it on `stream`, so ws must not be reused by another stream
+ *             until the step has run.
  * Tensors with n == 0 are skipped.  count == 0 is a no-op.
  */
 qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,

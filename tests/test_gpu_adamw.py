@@ -126,6 +126,41 @@ def test_multi_tensor_equals_loop_and_oracle():
             assert_state_equal(a, s, f"step {step}")
 
 
+@pytest.mark.parametrize("B", [256, 2048])
+def test_multi_tensor_many_small_tensors(B):
+    # far more tensors than tiles per bucket of the coarse tile index: buckets
+    # that span many tensors, empty tensors between them, one-element tensors
+    rng = np.random.default_rng(B)
+    sizes = [int(x) for x in rng.integers(1, 5000, size=300)]
+    for i in (0, 17, 150, 299):
+        sizes[i] = 0
+    sizes[5] = 1
+    sizes[200] = 2048 * 40 + 3
+    gdt = oracle.BF16
+    L = qb()
+    states = [State(n, B, 900 + i) for i, n in enumerate(sizes)]
+    dm = [s.device() for s in states]
+    ds = [s.device() for s in states]
+    ws = torch.empty(L.qb_multi_tensor_workspace_bytes(len(sizes)), dtype=torch.uint8, device=DEV)
+    for step in range(1, 3):
+        gs = [grad(max(n, 1), 80000 + 10 * i + step, gdt)[:n] for i, n in enumerate(sizes)]
+        gd = [to_device(g if g.size else np.zeros(1, np.uint16), TORCH_DT[gdt]) for g in gs]
+        table = L.tensor_table([(d[0], g, d[1], d[2], d[3], d[4]) for d, g in zip(dm, gd)])
+        for i, n in enumerate(sizes):
+            table[i].n = n
+        L.qb_multi_tensor_step(table, len(sizes), L.QB_BF16, B, hparams(step), ws)
+        for d, g, n in zip(ds, gd, sizes):
+            L.qb_adamw8bit_step(d[0], g, n, d[1], d[2], d[3], d[4], B, hparams(step))
+        for s, g in zip(states, gs):
+            if s.n:
+                oracle.adamw8bit_step(s.p, g, s.m, s.v, s.am, s.av, B, step=step, gdt=gdt, **HP)
+        torch.cuda.synchronize()
+        for a, b, s in zip(dm, ds, states):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y), "multi-tensor differs from the single-tensor loop"
+            assert_state_equal(a, s, f"step {step}")
+
+
 def test_resume_equals_straight_run():
     n, B, gdt = 2048 * 40 + 99, 2048, oracle.BF16
     L = qb()

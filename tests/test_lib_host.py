@@ -108,7 +108,7 @@ def test_workspace_sizes(qb):
     assert qb.qb_dq_workspace_bytes(64 * 1000, 64) == 16384 + 4096
     assert qb.qb_dq_workspace_bytes(0, 64) == 16384
     assert qb.qb_dq_workspace_bytes(100, 63) == 0
-    assert qb.qb_multi_tensor_workspace_bytes(291) == 291 * 64 + 292 * 8
+    assert qb.qb_multi_tensor_workspace_bytes(291) == 291 * 64 + 292 * 8 + (2 * 291 + 64 + 1) * 4
     assert qb.qb_multi_tensor_workspace_bytes(0) == 0
 
 
@@ -142,7 +142,7 @@ def test_invalid_arguments_rejected_before_launch(qb):
     assert L.qb_multi_tensor_step(tab, 1, 2, 2048, ctypes.byref(hp), A, 10, None) == qb.QB_EWORKSPACE
     assert L.qb_multi_tensor_step(tab, 0, 2, 2048, ctypes.byref(hp), A, 0, None) == qb.QB_OK
     tab_bad = (qb.qb_tensor * 1)(qb.qb_tensor(A, A2 + 8, A, A, A, A, 100))
-    assert L.qb_multi_tensor_step(tab_bad, 1, 2, 2048, ctypes.byref(hp), A, 80, None) == qb.QB_EALIGN
+    assert L.qb_multi_tensor_step(tab_bad, 1, 2, 2048, ctypes.byref(hp), A, L.qb_multi_tensor_workspace_bytes(1), None) == qb.QB_EALIGN
 
 
 def test_status_strings(qb):
