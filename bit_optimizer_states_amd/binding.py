@@ -42,6 +42,12 @@ class qb_tensor(ctypes.Structure):
                 ("absmax_m", ctypes.c_void_p), ("absmax_v", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
+class qb_dequant_tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p), ("c2", ctypes.c_void_p),
+                ("absmax2", ctypes.c_void_p), ("offset", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("n", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -58,7 +64,10 @@ def lib():
         L.qb_adamw8bit_step.argtypes = [vp, vp, i32, i64, vp, vp, vp, vp, i32, ctypes.POINTER(qb_adamw_hparams), vp]
         L.qb_multi_tensor_step.argtypes = [ctypes.POINTER(qb_tensor), i32, i32, i32, ctypes.POINTER(qb_adamw_hparams),
                                            vp, sz, vp]
-        for f in (L.qb_quantize, L.qb_dequantize, L.qb_adamw8bit_step, L.qb_multi_tensor_step):
+        L.qb_multi_tensor_dequantize.argtypes = [ctypes.POINTER(qb_dequant_tensor), i32, i32, i32, i32, i32, vp, sz,
+                                                 vp]
+        for f in (L.qb_quantize, L.qb_dequantize, L.qb_adamw8bit_step, L.qb_multi_tensor_step,
+                  L.qb_multi_tensor_dequantize):
             f.restype = ctypes.c_int
         L.qb_dq_workspace_bytes.argtypes = [i64, i32]
         L.qb_dq_workspace_bytes.restype = sz
@@ -155,6 +164,24 @@ def qb_multi_tensor_step(table, count, gdt, blocksize, hp, ws, stream=None):
     """table: result of tensor_table(); gdt: QB_F32/QB_F16/QB_BF16; ws: device byte tensor."""
     _check(lib().qb_multi_tensor_step(table, int(count), int(gdt), int(blocksize), ctypes.byref(hp), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)), "qb_multi_tensor_step")
+
+
+def dequant_table(entries):
+    """Host array of qb_dequant_tensor from (codes, absmax, dq, n, y) tuples;
+    absmax is None for a nested tensor, whose dq is a qb_dq (make_dq)."""
+    arr = (qb_dequant_tensor * len(entries))()
+    for i, (codes, absmax, dq, n, y) in enumerate(entries):
+        arr[i] = qb_dequant_tensor(_ptr(codes), _ptr(absmax), dq.codes if dq is not None else None,
+                                   dq.absmax2 if dq is not None else None, dq.offset if dq is not None else None,
+                                   _ptr(y), int(n))
+    return arr
+
+
+def qb_multi_tensor_dequantize(table, count, code, blocksize, blocksize2, ydt, ws, stream=None):
+    """table: result of dequant_table(); ydt: QB_F32/QB_F16/QB_BF16; ws: device byte tensor."""
+    _check(lib().qb_multi_tensor_dequantize(table, int(count), int(code), int(blocksize), int(blocksize2), int(ydt),
+                                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qb_multi_tensor_dequantize")
 
 
 def qb_codebook(code):

@@ -125,7 +125,7 @@ __device__ __forceinline__ void block_max2(uint32_t& x, uint32_t& y, uint32_t (*
 }
 
 template <int B, int GDT, bool MULTI>
-__global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, TileMap map, AdamScalars hs,
+__global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, TileMap<TensorDesc> map, AdamScalars hs,
                                                          const QbTables* __restrict__ tab)
 {
     using T = TileA<B>;
@@ -138,15 +138,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, Tile
     TensorDesc d;
     int64_t lt;
     if constexpr (MULTI) {
-        // tile_begin[lo] <= tile < tile_begin[hi]: the tensor holding the
-        // bucket's first tile, up to the one holding the next bucket's
-        const int64_t k = tile >> map.shift;
-        int lo = map.bucket_first[k], hi = map.bucket_first[k + 1] + 1;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (map.tile_begin[mid] <= tile) lo = mid; else hi = mid;
-        }
-        d = map.descs[lo];
+        d = map.descs[find_tensor(map, tile)];
         lt = tile - d.tile_begin;
     } else {
         d = single;
@@ -319,17 +311,17 @@ int64_t adamw_tiles(int64_t n, int B)
 namespace {
 
 template <int B, int GDT>
-hipError_t adamw_as(const TensorDesc& single, const TileMap* map, int64_t ntiles, const AdamScalars& hs,
+hipError_t adamw_as(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, const AdamScalars& hs,
                     const QbTables* tab, hipStream_t s)
 {
     static_assert(TileA<B>::ELEMS == kAdamThreads * (B >= 4 * kAdamThreads ? B / kAdamThreads : 4), "tile size");
     if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     if (map) return launch_kernel_nt(k_adamw8<B, GDT, true>, (int)ntiles, kAdamThreads, s, single, *map, hs, tab);
-    return launch_kernel_nt(k_adamw8<B, GDT, false>, (int)ntiles, kAdamThreads, s, single, TileMap{}, hs, tab);
+    return launch_kernel_nt(k_adamw8<B, GDT, false>, (int)ntiles, kAdamThreads, s, single, TileMap<TensorDesc>{}, hs, tab);
 }
 
 template <int B>
-hipError_t adamw_dt(int gdt, const TensorDesc& single, const TileMap* map, int64_t ntiles, const AdamScalars& hs,
+hipError_t adamw_dt(int gdt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, const AdamScalars& hs,
                     const QbTables* tab, hipStream_t s)
 {
     switch (gdt) {
@@ -342,7 +334,7 @@ hipError_t adamw_dt(int gdt, const TensorDesc& single, const TileMap* map, int64
 
 }  // namespace
 
-hipError_t launch_adamw8(const TensorDesc& single, const TileMap* map, int64_t ntiles, int B, int gdt,
+hipError_t launch_adamw8(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B, int gdt,
                          const AdamScalars& hs, hipStream_t s)
 {
     const QbTables* tab = device_tables();

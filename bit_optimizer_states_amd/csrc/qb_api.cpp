@@ -96,6 +96,77 @@ AdamScalars prepare(const qb_adamw_hparams& hp)
     return s;
 }
 
+// Checks one tensor of a dequantization and fills its descriptor (tile_begin
+// left 0); dq_mode: -1 = not fixed yet, 0 = plain, 1 = nested (all tensors of
+// a grouped call must agree).
+qb_status dequant_desc(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
+                              const float* offset, int32_t blocksize2, int64_t n, void* y, int32_t blocksize,
+                              int* dq_mode, DequantDesc* out)
+{
+    if (n < 0) return QB_EINVAL;
+    const int64_t nb = nblocks(n, blocksize);
+    if (nb >= (int64_t(1) << 31)) return QB_EINVAL;
+    if (!codes || !y) return QB_EINVAL;
+    if (!aligned16(codes) || !aligned16(y)) return QB_EALIGN;
+    const int mode = c2 ? 1 : 0;
+    if (*dq_mode >= 0 && *dq_mode != mode) return QB_EUNSUPPORTED;
+    *dq_mode = mode;
+    if (mode) {
+        if (absmax) return QB_EINVAL;
+        qb_dq tmp{const_cast<uint8_t*>(c2), const_cast<float*>(absmax2), const_cast<float*>(offset), blocksize2,
+                  nullptr, 0};
+        qb_status st = check_dq(&tmp, nb, false);
+        if (st != QB_OK) return st;
+    } else {
+        if (!absmax) return QB_EINVAL;
+        if (!aligned16(absmax)) return QB_EALIGN;
+    }
+    *out = DequantDesc{codes, absmax, c2, absmax2, offset, y, n, 0};
+    return QB_OK;
+}
+
+// Copies the descriptors of a multi-tensor launch, their first tiles and the
+// coarse bucket index (see TileMap) into ws on stream s; `tiles` is the total.
+// The host staging buffer is per thread and per descriptor type; a copy from
+// pageable memory has read it before hipMemcpyAsync returns.
+template <class Desc>
+qb_status upload_tile_map(const std::vector<Desc>& table, int64_t tiles, int32_t count, void* ws,
+                                 hipStream_t s, TileMap<Desc>* map)
+{
+    thread_local std::vector<int64_t> begins;
+    thread_local std::vector<int32_t> buckets;
+    thread_local std::vector<unsigned char> staging;
+    begins.clear();
+    buckets.clear();
+    for (const Desc& d : table) begins.push_back(d.tile_begin);
+    begins.push_back(tiles);
+    // the smallest bucket width 2^shift that needs at most
+    // max_tile_buckets(count) buckets; bucket k starts at tile k << shift
+    const int32_t used = (int32_t)table.size();
+    int shift = 0;
+    while (((tiles - 1) >> shift) + 1 > max_tile_buckets(count)) ++shift;
+    const int64_t nbk = ((tiles - 1) >> shift) + 1;
+    for (int64_t k = 0, i = 0; k < nbk; ++k) {
+        const int64_t first = k << shift;
+        while (begins[i + 1] <= first) ++i;          // begins[used] = tiles > first
+        buckets.push_back((int32_t)i);
+    }
+    buckets.push_back(used - 1);
+    const size_t dbytes = table.size() * sizeof(Desc), bbytes = begins.size() * sizeof(int64_t),
+                 kbytes = buckets.size() * sizeof(int32_t);
+    staging.resize(dbytes + bbytes + kbytes);
+    std::memcpy(staging.data(), table.data(), dbytes);
+    std::memcpy(staging.data() + dbytes, begins.data(), bbytes);
+    std::memcpy(staging.data() + dbytes + bbytes, buckets.data(), kbytes);
+    if (hipMemcpyAsync(ws, staging.data(), staging.size(), hipMemcpyHostToDevice, s) != hipSuccess) return QB_EHIP;
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    *map = TileMap<Desc>{reinterpret_cast<const Desc*>(w), reinterpret_cast<const int64_t*>(w + dbytes),
+                         reinterpret_cast<const int32_t*>(w + dbytes + bbytes), used, shift};
+    return QB_OK;
+}
+
+int64_t dequant_tiles(int64_t n) { return (n + kDequantTile - 1) / kDequantTile; }
+
 }  // namespace
 
 extern "C" {
@@ -203,32 +274,51 @@ qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* 
 {
     if (n < 0 || !valid_dtype(ydt) || !valid_code(code) || !pow2_block(blocksize)) return QB_EINVAL;
     if (n == 0) return QB_OK;
-    const int64_t nb = nblocks(n, blocksize);
-    if (nb >= (int64_t(1) << 31)) return QB_EINVAL;
-    if (!codes || !y) return QB_EINVAL;
-    if (!aligned16(codes) || !aligned16(y)) return QB_EALIGN;
-    const uint8_t* c2 = nullptr;
-    const float* a2 = nullptr;
-    const float* off = nullptr;
-    int b2 = 256;
-    if (dq) {
-        if (absmax) return QB_EINVAL;
-        qb_status st = check_dq(dq, nb, false);
+    int mode = dq ? 1 : 0;
+    if (dq && !dq->codes) return QB_EINVAL;
+    DequantDesc d;
+    qb_status st = dequant_desc(codes, absmax, dq ? dq->codes : nullptr, dq ? dq->absmax2 : nullptr,
+                                dq ? dq->offset : nullptr, dq ? dq->blocksize2 : 0, n, y, blocksize, &mode, &d);
+    if (st != QB_OK) return st;
+    if (!device_tables()) return QB_EINIT;
+    return hip_status(launch_dequant(d, nullptr, dequant_tiles(n), is4(code) ? 4 : 8, is4(code) ? code4_index(code) : 0,
+                                     blocksize, dq ? dq->blocksize2 : 256, dq != nullptr, (int)ydt,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t count, qb_code code,
+                                     int32_t blocksize, int32_t blocksize2, qb_dtype ydt, void* ws, size_t ws_bytes,
+                                     void* stream)
+{
+    if (count < 0 || !valid_dtype(ydt) || !valid_code(code) || !pow2_block(blocksize)) return QB_EINVAL;
+    if (count == 0) return QB_OK;
+    if (!tensors || !ws) return QB_EINVAL;
+    if (!aligned16(ws)) return QB_EALIGN;
+    if (ws_bytes < qb_multi_tensor_workspace_bytes(count)) return QB_EWORKSPACE;
+    thread_local std::vector<DequantDesc> table;
+    table.clear();
+    int mode = -1;
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const qb_dequant_tensor& t = tensors[i];
+        DequantDesc d;
+        qb_status st = dequant_desc(t.codes, t.absmax, t.c2, t.absmax2, t.offset, blocksize2, t.n, t.y, blocksize,
+                                    &mode, &d);
         if (st != QB_OK) return st;
-        c2 = dq->codes;
-        a2 = dq->absmax2;
-        off = dq->offset;
-        b2 = dq->blocksize2;
-    } else {
-        if (!absmax) return QB_EINVAL;
-        if (!aligned16(absmax)) return QB_EALIGN;
+        if (t.n == 0) continue;
+        d.tile_begin = tiles;
+        table.push_back(d);
+        tiles += dequant_tiles(t.n);
     }
+    if (table.empty()) return QB_OK;
+    if (tiles >= (int64_t(1) << 31)) return QB_EINVAL;
     if (!device_tables()) return QB_EINIT;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = is4(code) ? launch_dequant4(codes, absmax, c2, a2, off, blocksize, b2, n, code4_index(code), y,
-                                               (int)ydt, s)
-                             : launch_dequant8(codes, absmax, c2, a2, off, blocksize, b2, n, y, (int)ydt, s);
-    return hip_status(e);
+    TileMap<DequantDesc> map;
+    qb_status st = upload_tile_map(table, tiles, count, ws, s, &map);
+    if (st != QB_OK) return st;
+    return hip_status(launch_dequant(table[0], &map, tiles, is4(code) ? 4 : 8, is4(code) ? code4_index(code) : 0,
+                                     blocksize, mode == 1 ? blocksize2 : 256, mode == 1, (int)ydt, s));
 }
 
 qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, uint8_t* m, uint8_t* v,
@@ -259,12 +349,7 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
     if (!aligned16(ws)) return QB_EALIGN;
     if (ws_bytes < qb_multi_tensor_workspace_bytes(count)) return QB_EWORKSPACE;
     thread_local std::vector<TensorDesc> table;
-    thread_local std::vector<int64_t> begins;
-    thread_local std::vector<int32_t> buckets;
-    thread_local std::vector<unsigned char> staging;
     table.clear();
-    begins.clear();
-    buckets.clear();
     int64_t tiles = 0;
     for (int32_t i = 0; i < count; ++i) {
         const qb_tensor& t = tensors[i];
@@ -277,37 +362,15 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
             !aligned16(t.absmax_v))
             return QB_EALIGN;
         table.push_back(TensorDesc{t.p, t.g, t.m, t.v, t.absmax_m, t.absmax_v, t.n, tiles});
-        begins.push_back(tiles);
         tiles += adamw_tiles(t.n, blocksize);
     }
     if (table.empty()) return QB_OK;
     if (tiles >= (int64_t(1) << 31)) return QB_EINVAL;
-    begins.push_back(tiles);
-    // coarse index: the smallest bucket width 2^shift that needs at most
-    // max_tile_buckets(count) buckets; bucket k starts at tile k << shift
-    const int32_t used = (int32_t)table.size();
-    int shift = 0;
-    while (((tiles - 1) >> shift) + 1 > max_tile_buckets(count)) ++shift;
-    const int64_t nbk = ((tiles - 1) >> shift) + 1;
-    for (int64_t k = 0, i = 0; k < nbk; ++k) {
-        const int64_t first = k << shift;
-        while (begins[i + 1] <= first) ++i;          // begins[used] = tiles > first
-        buckets.push_back((int32_t)i);
-    }
-    buckets.push_back(used - 1);
     if (!device_tables()) return QB_EINIT;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t dbytes = table.size() * sizeof(TensorDesc), bbytes = begins.size() * sizeof(int64_t),
-                 kbytes = buckets.size() * sizeof(int32_t);
-    staging.resize(dbytes + bbytes + kbytes);
-    std::memcpy(staging.data(), table.data(), dbytes);
-    std::memcpy(staging.data() + dbytes, begins.data(), bbytes);
-    std::memcpy(staging.data() + dbytes + bbytes, buckets.data(), kbytes);
-    hipError_t e = hipMemcpyAsync(ws, staging.data(), staging.size(), hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return QB_EHIP;
-    unsigned char* w = static_cast<unsigned char*>(ws);
-    const TileMap map{reinterpret_cast<const TensorDesc*>(w), reinterpret_cast<const int64_t*>(w + dbytes),
-                      reinterpret_cast<const int32_t*>(w + dbytes + bbytes), used, shift};
+    TileMap<TensorDesc> map;
+    qb_status st = upload_tile_map(table, tiles, count, ws, s, &map);
+    if (st != QB_OK) return st;
     return hip_status(launch_adamw8(table[0], &map, tiles, blocksize, (int)gdt, prepare(*hp), s));
 }
 

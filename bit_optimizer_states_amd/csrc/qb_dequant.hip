@@ -1,0 +1,209 @@
+// qb_dequant.hip -- block-wise dequantization (8-bit dynamic code, 4-bit NF4 /
+// FP4 packed two per byte), with the nested absmax decoded in the same pass.
+//
+// Method: element i of block b comes back as code[c_i] times the block's
+// absmax, rounded once to the output dtype ("Bitsandbytes", section on
+// dequantizing; compute dtype: "Quantize 🤗 Transformers models", section
+// Change the compute dtype).  With nested quantization the absmax itself is
+// decoded first, a_b = dyn8[c2_b] * absmax2[b / B2] + mean, two rounded binary32
+// operations ("Bitsandbytes", section İç içe nicelleştirme).
+//
+// Kernel shape: one 256-thread workgroup per tile of 8192 elements, launched in
+// tile order.  A thread takes 4 units of 8 consecutive elements (one u32 of
+// 4-bit codes or two of 8-bit codes), consecutive lanes on consecutive units,
+// so every load and store instruction of a wave covers one contiguous span.
+// At the start a workgroup issues the loads of its codes and of the scale
+// inputs of its tile's blocks (one block per thread, at most 128 blocks per
+// tile since B >= 64), then stages the code tables in LDS; the blocks' scales
+// are decoded once into LDS, and every element is one LDS lookup, one multiply
+// and a round-to-nearest-even store.  Streamed codes and outputs take
+// non-temporal accesses.
+//
+// Many tensors go in one launch: tiles of all tensors are numbered in one
+// range and a workgroup finds its tensor through the coarse bucket index.
+#include "qb_device.h"
+
+namespace qb {
+
+namespace {
+
+constexpr int kDqThreads = 256;
+constexpr int kDqUnits = 4;                    // units of 8 elements per thread
+constexpr int kDqElems = kDqThreads * kDqUnits * 8;
+static_assert(kDqElems == kDequantTile, "tile size");
+constexpr int kDqMaxBlocks = kDqElems / 64;    // blocks per tile at B = 64
+
+// The 8 codes of the unit at element offset e (a multiple of 8) from base.
+template <int BITS>
+__device__ __forceinline__ u32x2 load_unit(const uint8_t* base, uint32_t e)
+{
+    if constexpr (BITS == 8) {
+        return gldo<u32x2>(base, e);
+    } else {
+        u32x2 w = {gldo<uint32_t>(base, e / 2), 0u};
+        return w;
+    }
+}
+
+// Code of element j (0..7) of a unit.
+template <int BITS>
+__device__ __forceinline__ uint32_t unit_code(const u32x2& w, int j)
+{
+    if constexpr (BITS == 8) {
+        return ((j < 4 ? w.x : w.y) >> (8 * (j & 3))) & 0xFFu;
+    } else {
+        // byte k holds element 2k in its high nibble and 2k+1 in its low one
+        const uint32_t byte = (w.x >> (8 * (j >> 1))) & 0xFFu;
+        return (j & 1) ? (byte & 15u) : (byte >> 4);
+    }
+}
+
+// Code of element idx of a tensor (scalar path of the last tile).
+template <int BITS>
+__device__ __forceinline__ uint32_t elem_code(const uint8_t* codes, int64_t idx)
+{
+    if constexpr (BITS == 8) {
+        return gld<uint8_t>(codes + idx);
+    } else {
+        const uint32_t byte = gld<uint8_t>(codes + idx / 2);
+        return (idx & 1) ? (byte & 15u) : (byte >> 4);
+    }
+}
+
+template <int BITS, int YDT, bool DQ, bool MULTI>
+__global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, TileMap<DequantDesc> map, int log2B,
+                                                        int log2B2, int code4, const QbTables* __restrict__ tab)
+{
+    __shared__ float s_val[BITS == 8 ? 256 : 16];   // decode table of the codes
+    __shared__ float s_dyn[DQ && BITS == 4 ? 256 : 1];
+    __shared__ float s_scale[kDqMaxBlocks];
+    const int tid = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+
+    DequantDesc d;
+    int64_t lt;
+    if constexpr (MULTI) {
+        d = map.descs[find_tensor(map, tile)];
+        lt = tile - d.tile_begin;
+    } else {
+        d = single;
+        lt = tile;
+    }
+    const int64_t n = d.n;
+    const int64_t tbase = lt * kDqElems;                 // first element of the tile
+    const bool full = tbase + kDqElems <= n;
+    const uint8_t* const ct = d.codes + (tbase * BITS) / 8;
+
+    // codes of the tile
+    u32x2 w[kDqUnits];
+    if (full) {
+#pragma unroll
+        for (int k = 0; k < kDqUnits; ++k) w[k] = load_unit<BITS>(ct, (uint32_t)(k * kDqThreads + tid) * 8);
+    }
+    // scale inputs of the tile's blocks, one block per thread
+    const int nbt = kDqElems >> log2B;                   // blocks per tile (B <= 4096 < tile)
+    const int64_t blk = (tbase >> log2B) + tid;
+    const int64_t nb = (n + (int64_t(1) << log2B) - 1) >> log2B;
+    const bool owner = tid < nbt && blk < nb;
+    float sa = 0.0f;
+    uint32_t sc = 0;
+    if (owner) {
+        if constexpr (DQ) {
+            sc = gld<uint8_t>(d.c2 + blk);
+            sa = gld<float>(d.absmax2 + (blk >> log2B2));
+        } else {
+            sa = gld<float>(d.absmax + blk);
+        }
+    }
+    const float mu = DQ ? gld<float>(d.offset) : 0.0f;
+
+    // decode tables
+    if constexpr (BITS == 8) {
+        s_val[tid] = tab->dyn8[tid];
+    } else {
+        if (tid < 16) s_val[tid] = (code4 == 0 ? tab->nf4 : tab->fp4)[tid];
+        if constexpr (DQ) s_dyn[tid] = tab->dyn8[tid];
+    }
+    __syncthreads();
+    if (owner) {
+        if constexpr (DQ) {
+            const float prod = (BITS == 8 ? s_val : s_dyn)[sc] * sa;
+            s_scale[tid] = prod + mu;
+        } else {
+            s_scale[tid] = sa;
+        }
+    }
+    __syncthreads();
+
+    char* const yt = static_cast<char*>(d.y) + tbase * (YDT == DT_F32 ? 4 : 2);
+    if (full) {
+#pragma unroll
+        for (int k = 0; k < kDqUnits; ++k) {
+            const uint32_t e = (uint32_t)(k * kDqThreads + tid) * 8;
+            const float s = s_scale[e >> log2B];
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = s_val[unit_code<BITS>(w[k], j)] * s;
+            store8o<YDT>(yt, e, o);
+        }
+    } else {
+        for (int k = 0; k < kDqUnits; ++k)
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t e = (uint32_t)(k * kDqThreads + tid) * 8 + j;
+                if ((int64_t)e < n - tbase) {
+                    const float s = s_scale[e >> log2B];
+                    store1<YDT>(yt, e, s_val[elem_code<BITS>(ct, e)] * s);
+                }
+            }
+    }
+}
+
+int ilog2(int v)
+{
+    int k = 0;
+    while ((1 << k) < v) ++k;
+    return k;
+}
+
+template <int BITS, int YDT, bool DQ>
+hipError_t dequant_as(const DequantDesc& single, const TileMap<DequantDesc>* map, int64_t ntiles, int code4, int B,
+                      int B2, const QbTables* tab, hipStream_t s)
+{
+    if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if (map)
+        return launch_kernel_nt(k_dequant<BITS, YDT, DQ, true>, (int)ntiles, kDqThreads, s, single, *map, ilog2(B),
+                                ilog2(B2), code4, tab);
+    return launch_kernel_nt(k_dequant<BITS, YDT, DQ, false>, (int)ntiles, kDqThreads, s, single,
+                            TileMap<DequantDesc>{}, ilog2(B), ilog2(B2), code4, tab);
+}
+
+template <int BITS, bool DQ>
+hipError_t dequant_y(int ydt, const DequantDesc& single, const TileMap<DequantDesc>* map, int64_t ntiles, int code4,
+                     int B, int B2, const QbTables* tab, hipStream_t s)
+{
+    switch (ydt) {
+    case DT_F32: return dequant_as<BITS, DT_F32, DQ>(single, map, ntiles, code4, B, B2, tab, s);
+    case DT_F16: return dequant_as<BITS, DT_F16, DQ>(single, map, ntiles, code4, B, B2, tab, s);
+    case DT_BF16: return dequant_as<BITS, DT_BF16, DQ>(single, map, ntiles, code4, B, B2, tab, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dequant(const DequantDesc& single, const TileMap<DequantDesc>* map, int64_t ntiles, int bits,
+                          int code4, int B, int B2, bool dq, int ydt, hipStream_t s)
+{
+    const QbTables* tab = device_tables();
+    if (!tab) return hipErrorNotInitialized;
+    if (B < 64 || B > 4096 || (B & (B - 1))) return hipErrorInvalidValue;
+    if (bits == 8)
+        return dq ? dequant_y<8, true>(ydt, single, map, ntiles, code4, B, B2, tab, s)
+                  : dequant_y<8, false>(ydt, single, map, ntiles, code4, B, B2, tab, s);
+    if (bits == 4)
+        return dq ? dequant_y<4, true>(ydt, single, map, ntiles, code4, B, B2, tab, s)
+                  : dequant_y<4, false>(ydt, single, map, ntiles, code4, B, B2, tab, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qb

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qb_launch.h"
 #include "qb_tables.h"
 
 namespace qb {
@@ -247,6 +248,26 @@ __device__ __forceinline__ void store8(void* y, int64_t i, const float* o)
         u32x4 v = {pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3]), pack2<DT>(o[4], o[5]), pack2<DT>(o[6], o[7])};
         gst<u32x4>(static_cast<uint16_t*>(y) + i, v);
     }
+}
+
+// ---------------------------------------------------------------------------
+// multi-tensor launches
+// ---------------------------------------------------------------------------
+
+// Index of the tensor holding global tile `tile`: between the tensor holding
+// the first tile of tile's bucket and the one holding the next bucket's first
+// tile (usually the same or adjacent ones), by binary search on tile_begin
+// (tile_begin[lo] <= tile < tile_begin[hi]).  Uniform: scalar loads.
+template <class Desc>
+__device__ __forceinline__ int find_tensor(const TileMap<Desc>& map, int64_t tile)
+{
+    const int64_t k = tile >> map.shift;
+    int lo = map.bucket_first[k], hi = map.bucket_first[k + 1] + 1;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (map.tile_begin[mid] <= tile) lo = mid; else hi = mid;
+    }
+    return lo;
 }
 
 // ---------------------------------------------------------------------------

@@ -37,21 +37,33 @@ struct TensorDesc {
 };
 static_assert(sizeof(TensorDesc) == 64, "descriptor layout");
 
+// One tensor of a grouped dequantization; tile_begin is its first global tile.
+struct DequantDesc {
+    const uint8_t* codes;
+    const float* absmax;      // per-block absmax (plain), or nullptr (nested)
+    const uint8_t* c2;        // nested state: codes, second-level absmax, mean
+    const float* absmax2;
+    const float* offset;
+    void* y;
+    int64_t n;
+    int64_t tile_begin;
+};
+static_assert(sizeof(DequantDesc) == 64, "descriptor layout");
+
 // Device tables of a multi-tensor launch: `count` descriptors; the first tile
 // of every tensor (count + 1 entries, the last one the total); and a coarse
 // index, bucket_first[k] = the tensor that holds tile k << shift (one entry
 // per bucket plus a last one = count - 1), so that a workgroup finds its tensor
 // with two dependent loads instead of a binary search over all tensors.
+template <class Desc>
 struct TileMap {
-    const TensorDesc* descs;
+    const Desc* descs;
     const int64_t* tile_begin;
     const int32_t* bucket_first;
     int32_t count;
     int32_t shift;
 };
 
-// Most buckets of the coarse index for `count` tensors (the workspace holds
-// this many + 1 int32 entries).
 constexpr int64_t max_tile_buckets(int64_t count) { return 2 * count + 64; }
 
 // Device copy of the constant tables for the current device (uploaded once).
@@ -103,14 +115,16 @@ hipError_t launch_quant8(const void* x, int xdt, int64_t n, int B, uint8_t* code
                          unsigned long long* bins, float* offset, hipStream_t s);
 hipError_t launch_quant4(const void* x, int xdt, int64_t n, int B, int code4, uint8_t* codes, float* absmax,
                          int mode, unsigned long long* bins, hipStream_t s);
-hipError_t launch_dequant8(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
-                           const float* offset, int B, int B2, int64_t n, void* y, int ydt, hipStream_t s);
-hipError_t launch_dequant4(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
-                           const float* offset, int B, int B2, int64_t n, int code4, void* y, int ydt,
-                           hipStream_t s);
+// Dequantize one tensor (map == nullptr) or the tensors of `map` (ntiles in
+// all); bits 8 (dynamic code) or 4 (code4: 0 NF4, 1 FP4); dq: nested absmax.
+hipError_t launch_dequant(const DequantDesc& single, const TileMap<DequantDesc>* map, int64_t ntiles, int bits,
+                          int code4, int B, int B2, bool dq, int ydt, hipStream_t s);
+
+// Elements per tile of the dequantization kernel.
+constexpr int64_t kDequantTile = 8192;
 // map: the device tables of a multi-tensor launch, or nullptr for the one
 // tensor `single`.
-hipError_t launch_adamw8(const TensorDesc& single, const TileMap* map, int64_t ntiles, int B, int gdt,
+hipError_t launch_adamw8(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B, int gdt,
                          const AdamScalars& hs, hipStream_t s);
 
 // Tiles of the AdamW kernel for a tensor of n elements at block size B.

@@ -1,5 +1,5 @@
-// qb_quant.hip -- block-wise quantize / dequantize kernels (8-bit dynamic code
-// and 4-bit NF4 / FP4), with the nested quantization of the block absmax.
+// qb_quant.hip -- block-wise quantization kernels (8-bit dynamic code and 4-bit
+// NF4 / FP4), with the nested quantization of the block absmax.
 //
 // Method: every block of B consecutive elements is scaled by its own absolute
 // maximum and each scaled value is encoded as the nearest code entry, blocks
@@ -426,129 +426,10 @@ __global__ __launch_bounds__(256) void k_quant4_binned(const void* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// dequantize
-// ---------------------------------------------------------------------------
-
-// Scale of block `blk`: its absmax, or with nesting dyn8[c2] * absmax2 + mean
-// (two rounded binary32 operations).
-template <bool DQ>
-__device__ __forceinline__ float block_scale(int64_t blk, const float* __restrict__ absmax,
-                                             const uint8_t* __restrict__ c2, const float* __restrict__ absmax2,
-                                             int log2B2, float mu, const float* s_dyn)
-{
-    if constexpr (DQ) {
-        const float prod = s_dyn[gld<uint8_t>(c2 + blk)] * gld<float>(absmax2 + (blk >> log2B2));
-        return prod + mu;
-    } else {
-        return gld<float>(absmax + blk);
-    }
-}
-
-constexpr int kDq8Units = 4;    // units of 4 codes per thread per tile
-constexpr int kDq8Elems = kThreads * kDq8Units * 4;
-
-template <int YDT, bool DQ>
-__global__ __launch_bounds__(256) void k_dequant8(const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
-                                                  const uint8_t* __restrict__ c2, const float* __restrict__ absmax2,
-                                                  const float* __restrict__ offset, int log2B, int log2B2, int64_t n,
-                                                  void* __restrict__ y, const QbTables* __restrict__ tab)
-{
-    __shared__ float s_dyn[256];
-    const int tid = threadIdx.x;
-    const int64_t base = (int64_t)blockIdx.x * kDq8Elems;
-    const bool full = base + kDq8Elems <= n;
-    uint32_t w[kDq8Units];
-    if (full) {
-#pragma unroll
-        for (int k = 0; k < kDq8Units; ++k) w[k] = gld<uint32_t>(codes + base + k * kThreads * 4 + tid * 4);
-    }
-    s_dyn[tid] = tab->dyn8[tid];
-    const float mu = DQ ? gld<float>(offset) : 0.0f;
-    __syncthreads();
-    if (full) {
-#pragma unroll
-        for (int k = 0; k < kDq8Units; ++k) {
-            const int64_t e0 = base + k * kThreads * 4 + tid * 4;
-            const float s = block_scale<DQ>(e0 >> log2B, absmax, c2, absmax2, log2B2, mu, s_dyn);
-            float o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = s_dyn[(w[k] >> (8 * j)) & 0xFFu] * s;
-            store4<YDT>(y, e0, o);
-        }
-    } else {
-        for (int k = 0; k < kDq8Units; ++k)
-            for (int j = 0; j < 4; ++j) {
-                const int64_t idx = base + k * kThreads * 4 + tid * 4 + j;
-                if (idx < n) {
-                    const float s = block_scale<DQ>(idx >> log2B, absmax, c2, absmax2, log2B2, mu, s_dyn);
-                    store1<YDT>(y, idx, s_dyn[gld<uint8_t>(codes + idx)] * s);
-                }
-            }
-    }
-}
-
-constexpr int kDq4Units = 4;    // units of 8 codes (one u32) per thread per tile
-constexpr int kDq4Elems = kThreads * kDq4Units * 8;
-
-template <int YDT, bool DQ>
-__global__ __launch_bounds__(256) void k_dequant4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
-                                                  const uint8_t* __restrict__ c2, const float* __restrict__ absmax2,
-                                                  const float* __restrict__ offset, int log2B, int log2B2, int64_t n,
-                                                  int code4, void* __restrict__ y, const QbTables* __restrict__ tab)
-{
-    __shared__ float s_val[16];
-    __shared__ float s_dyn[DQ ? 256 : 1];
-    const int tid = threadIdx.x;
-    const int64_t base = (int64_t)blockIdx.x * kDq4Elems;
-    const bool full = base + kDq4Elems <= n;
-    uint32_t w[kDq4Units];
-    if (full) {
-#pragma unroll
-        for (int k = 0; k < kDq4Units; ++k) w[k] = gld<uint32_t>(codes + (base + k * kThreads * 8 + tid * 8) / 2);
-    }
-    if (tid < 16) s_val[tid] = (code4 == 0 ? tab->nf4 : tab->fp4)[tid];
-    if constexpr (DQ) s_dyn[tid] = tab->dyn8[tid];
-    const float mu = DQ ? gld<float>(offset) : 0.0f;
-    __syncthreads();
-    if (full) {
-#pragma unroll
-        for (int k = 0; k < kDq4Units; ++k) {
-            const int64_t e0 = base + k * kThreads * 8 + tid * 8;
-            const float s = block_scale<DQ>(e0 >> log2B, absmax, c2, absmax2, log2B2, mu, s_dyn);
-            float o[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t byte = (w[k] >> (8 * j)) & 0xFFu;
-                o[2 * j] = s_val[byte >> 4] * s;
-                o[2 * j + 1] = s_val[byte & 15u] * s;
-            }
-            store8<YDT>(y, e0, o);
-        }
-    } else {
-        for (int k = 0; k < kDq4Units; ++k)
-            for (int j = 0; j < 8; ++j) {
-                const int64_t idx = base + k * kThreads * 8 + tid * 8 + j;
-                if (idx < n) {
-                    const float s = block_scale<DQ>(idx >> log2B, absmax, c2, absmax2, log2B2, mu, s_dyn);
-                    const uint32_t byte = gld<uint8_t>(codes + idx / 2);
-                    store1<YDT>(y, idx, s_val[(idx & 1) ? (byte & 15u) : (byte >> 4)] * s);
-                }
-            }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
 namespace {
-
-int ilog2(int v)
-{
-    int k = 0;
-    while ((1 << k) < v) ++k;
-    return k;
-}
 
 template <int B, int XDT>
 hipError_t quant8_as(int mode, const void* x, int64_t n, uint8_t* codes, float* absmax, const QbTables* tab,
@@ -604,25 +485,6 @@ hipError_t quant4_dt(int mode, int xdt, const void* x, int64_t n, int code4, uin
     }
 }
 
-template <int YDT, bool DQ>
-hipError_t dequant8_as(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
-                       const float* offset, int B, int B2, int64_t n, void* y, const QbTables* tab, hipStream_t s)
-{
-    const int64_t ntiles = (n + kDq8Elems - 1) / kDq8Elems;
-    return launch_kernel(k_dequant8<YDT, DQ>, (int)ntiles, s, codes, absmax, c2, absmax2, offset, ilog2(B),
-                         ilog2(B2), n, y, tab);
-}
-
-template <int YDT, bool DQ>
-hipError_t dequant4_as(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
-                       const float* offset, int B, int B2, int64_t n, int code4, void* y, const QbTables* tab,
-                       hipStream_t s)
-{
-    const int64_t ntiles = (n + kDq4Elems - 1) / kDq4Elems;
-    return launch_kernel(k_dequant4<YDT, DQ>, (int)ntiles, s, codes, absmax, c2, absmax2, offset, ilog2(B),
-                         ilog2(B2), n, code4, y, tab);
-}
-
 }  // namespace
 
 #define QB_SWITCH_B(B, CALL)                           \
@@ -653,41 +515,6 @@ hipError_t launch_quant4(const void* x, int xdt, int64_t n, int B, int code4, ui
     if (!tab) return hipErrorNotInitialized;
     if (mode != QM_PLAIN && mode != QM_DQ_FIRST) return hipErrorInvalidValue;
     QB_SWITCH_B(B, quant4_dt<kB>(mode, xdt, x, n, code4, codes, absmax, tab, bins, s));
-}
-
-hipError_t launch_dequant8(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
-                           const float* offset, int B, int B2, int64_t n, void* y, int ydt, hipStream_t s)
-{
-    const QbTables* tab = device_tables();
-    if (!tab) return hipErrorNotInitialized;
-    const bool dq = c2 != nullptr;
-    switch (ydt) {
-    case DT_F32: return dq ? dequant8_as<DT_F32, true>(codes, absmax, c2, absmax2, offset, B, B2, n, y, tab, s)
-                           : dequant8_as<DT_F32, false>(codes, absmax, c2, absmax2, offset, B, B2, n, y, tab, s);
-    case DT_F16: return dq ? dequant8_as<DT_F16, true>(codes, absmax, c2, absmax2, offset, B, B2, n, y, tab, s)
-                           : dequant8_as<DT_F16, false>(codes, absmax, c2, absmax2, offset, B, B2, n, y, tab, s);
-    case DT_BF16: return dq ? dequant8_as<DT_BF16, true>(codes, absmax, c2, absmax2, offset, B, B2, n, y, tab, s)
-                            : dequant8_as<DT_BF16, false>(codes, absmax, c2, absmax2, offset, B, B2, n, y, tab, s);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_dequant4(const uint8_t* codes, const float* absmax, const uint8_t* c2, const float* absmax2,
-                           const float* offset, int B, int B2, int64_t n, int code4, void* y, int ydt,
-                           hipStream_t s)
-{
-    const QbTables* tab = device_tables();
-    if (!tab) return hipErrorNotInitialized;
-    const bool dq = c2 != nullptr;
-    switch (ydt) {
-    case DT_F32: return dq ? dequant4_as<DT_F32, true>(codes, absmax, c2, absmax2, offset, B, B2, n, code4, y, tab, s)
-                           : dequant4_as<DT_F32, false>(codes, absmax, c2, absmax2, offset, B, B2, n, code4, y, tab, s);
-    case DT_F16: return dq ? dequant4_as<DT_F16, true>(codes, absmax, c2, absmax2, offset, B, B2, n, code4, y, tab, s)
-                           : dequant4_as<DT_F16, false>(codes, absmax, c2, absmax2, offset, B, B2, n, code4, y, tab, s);
-    case DT_BF16: return dq ? dequant4_as<DT_BF16, true>(codes, absmax, c2, absmax2, offset, B, B2, n, code4, y, tab, s)
-                            : dequant4_as<DT_BF16, false>(codes, absmax, c2, absmax2, offset, B, B2, n, code4, y, tab, s);
-    default: return hipErrorInvalidValue;
-    }
 }
 
 }  // namespace qb

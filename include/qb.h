@@ -111,6 +111,22 @@ typedef struct {
 } qb_tensor;
 
 /*
+ * One tensor of a grouped dequantization; the fields are those of
+ * qb_dequantize.  A plain tensor gives absmax and leaves c2, absmax2, offset
+ * NULL; a nested one gives c2, absmax2, offset (the qb_dq fields) and absmax
+ * NULL.
+ */
+typedef struct {
+    const uint8_t* codes;
+    const float*   absmax;
+    const uint8_t* c2;
+    const float*   absmax2;
+    const float*   offset;
+    void*          y;
+    int64_t        n;
+} qb_dequant_tensor;
+
+/*
  * qb_quantize -- block-wise quantization (pages cited at the top; NF4: page
  * "Bitsandbytes", section Normal Float 4 (NF4); FP4: page "Quantize 🤗
  * Transformers models", section FP4 quantization).
@@ -135,6 +151,24 @@ qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int3
  */
 qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* dq, qb_code code,
                         int32_t blocksize, int64_t n, void* y, qb_dtype ydt, void* stream);
+
+/*
+ * qb_multi_tensor_dequantize -- qb_dequantize on `count` tensors in ONE kernel
+ * launch (same code, block size, nested block size and output dtype for all;
+ * the result equals a loop of single-tensor calls, bit for bit).  Dequantizing
+ * the weights of many layers at once (page "Bitsandbytes", section on
+ * dequantizing a model) this way avoids one launch ramp per tensor.
+ *   tensors     host array of `count` descriptors (read during the call only);
+ *               either every tensor is nested or none (else QB_EUNSUPPORTED).
+ *   blocksize2  block size of the nested level (ignored without nesting).
+ *   ws          device workspace of qb_multi_tensor_workspace_bytes(count)
+ *               bytes, filled with a table of the tensors on `stream` (so it
+ *               must not be reused by another stream until the call has run).
+ * Tensors with n == 0 are skipped.  count == 0 is a no-op.
+ */
+qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t count, qb_code code,
+                                     int32_t blocksize, int32_t blocksize2, qb_dtype ydt, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /*
  * qb_adamw8bit_step -- one fused AdamW step with both moments held as block-wise
@@ -172,7 +206,8 @@ qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, ui
 qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
                                const qb_adamw_hparams* hp, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace sizes (bytes) for qb_quantize with nesting and for qb_multi_tensor_step. */
+/* Workspace sizes (bytes) for qb_quantize with nesting, and for
+ * qb_multi_tensor_step and qb_multi_tensor_dequantize. */
 size_t qb_dq_workspace_bytes(int64_t n, int32_t blocksize);
 size_t qb_multi_tensor_workspace_bytes(int32_t count);
 

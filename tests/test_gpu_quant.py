@@ -129,3 +129,67 @@ def test_nested_mean_wide_dynamic_range():
     c2, a2, mu = oracle.dq_quantize(want_a, 256)
     assert np.float32(got_s["mu"]) == mu
     assert np.array_equal(got_s["c2"], c2) and np.array_equal(got_s["absmax2"], a2)
+
+
+@pytest.mark.parametrize("code", CODES)
+@pytest.mark.parametrize("nested", [False, True])
+@pytest.mark.parametrize("B", [64, 4096])
+def test_multi_tensor_dequantize_equals_oracle(code, nested, B):
+    """One grouped launch over many tensors (ragged, tiny, empty, several tiles)
+    equals the oracle tensor by tensor; bytes past each output stay untouched."""
+    from gpu_helpers import qb
+    L = qb()
+    rng = np.random.default_rng(300 + 10 * code + B + nested)
+    sizes = [8192 * 3 + 77, 1, 0, 65, 8192, 64 * 256 * 3 + 5, 2, 4097, 0, 8191] + \
+        [int(v) for v in rng.integers(1, 20000, 40)]
+    ydt = oracle.BF16
+    keep, entries, wants = [], [], []
+    for i, n in enumerate(sizes):
+        x = (rng.standard_normal(max(n, 1)) * 0.02).astype(np.float32)[:n]
+        codes, absmax = oracle.quantize_blockwise(x, code, B) if n else (np.zeros(0, np.uint8), np.zeros(0, np.float32))
+        y = torch.full((n + 8,), 7.0, dtype=TORCH_DT[ydt], device=DEV)
+        cd = to_device(codes if codes.size else np.zeros(1, np.uint8))
+        if nested:
+            c2, a2, mu = oracle.dq_quantize(absmax, 256) if n else (np.zeros(1, np.uint8), np.zeros(1, np.float32),
+                                                                     np.float32(0))
+            st = {"c2": to_device(c2 if c2.size else np.zeros(1, np.uint8)),
+                  "a2": to_device(a2 if a2.size else np.zeros(1, np.float32)),
+                  "off": to_device(np.array([mu, 0, 0, 0], np.float32))}
+            dq = L.make_dq(st["c2"], st["a2"], st["off"], 256)
+            keep.append((cd, st, y))
+            entries.append((cd, None, dq, n, y))
+            want = oracle.dequantize(codes, {"c2": c2, "absmax2": a2, "mu": mu}, code, B, n, ydt) if n else None
+        else:
+            ad = to_device(absmax if absmax.size else np.zeros(1, np.float32))
+            keep.append((cd, ad, y))
+            entries.append((cd, ad, None, n, y))
+            want = oracle.dequantize_blockwise(codes, absmax, code, B, n, ydt) if n else None
+        wants.append(want)
+    table = L.dequant_table(entries)
+    ws = torch.empty(L.qb_multi_tensor_workspace_bytes(len(sizes)), dtype=torch.uint8, device=DEV)
+    L.qb_multi_tensor_dequantize(table, len(sizes), code, B, 256, L.QB_BF16, ws)
+    torch.cuda.synchronize()
+    sentinel = torch.full((8,), 7.0, dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for (n, want, (_, _, y)) in zip(sizes, wants, keep):
+        got = host_bits(y)
+        if n:
+            assert np.array_equal(got[:n], want), f"tensor of {n} differs"
+        assert np.array_equal(got[n:], sentinel), f"tensor of {n}: wrote past its end"
+
+
+def test_multi_tensor_dequantize_rejects_mixed_nesting():
+    from gpu_helpers import qb
+    L = qb()
+    n = 1000
+    codes = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    absmax = torch.ones(16, device=DEV)
+    c2 = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    a2 = torch.ones(4, device=DEV)
+    off = torch.zeros(4, device=DEV)
+    y = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    dq = L.make_dq(c2, a2, off, 256)
+    table = L.dequant_table([(codes, absmax, None, n, y), (codes, None, dq, n, y)])
+    ws = torch.empty(L.qb_multi_tensor_workspace_bytes(2), dtype=torch.uint8, device=DEV)
+    with pytest.raises(L.QbError) as e:
+        L.qb_multi_tensor_dequantize(table, 2, L.QB_DYN8, 64, 256, L.QB_BF16, ws)
+    assert e.value.status == L.QB_EUNSUPPORTED

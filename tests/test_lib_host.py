@@ -145,6 +145,31 @@ def test_invalid_arguments_rejected_before_launch(qb):
     assert L.qb_multi_tensor_step(tab_bad, 1, 2, 2048, ctypes.byref(hp), A, L.qb_multi_tensor_workspace_bytes(1), None) == qb.QB_EALIGN
 
 
+def test_grouped_dequantize_arguments_rejected_before_launch(qb):
+    L = qb.lib()
+    A = 0x100000
+    ws = L.qb_multi_tensor_workspace_bytes(2)
+    plain = qb.qb_dequant_tensor(A, A, None, None, None, A, 1000)
+    nested = qb.qb_dequant_tensor(A, None, A, A, A, A, 1000)
+    both = qb.qb_dequant_tensor(A, A, A, A, A, A, 1000)
+    tab = lambda *e: (qb.qb_dequant_tensor * len(e))(*e)
+    f = L.qb_multi_tensor_dequantize
+    assert f(tab(plain), -1, 0, 64, 256, 2, A, ws, None) == qb.QB_EINVAL              # count < 0
+    assert f(tab(plain), 0, 0, 64, 256, 2, A, 0, None) == qb.QB_OK                    # count == 0: no-op
+    assert f(tab(plain), 1, 0, 64, 256, 2, A, 10, None) == qb.QB_EWORKSPACE
+    assert f(tab(plain), 1, 0, 64, 256, 2, A + 8, ws, None) == qb.QB_EALIGN
+    assert f(tab(plain), 1, 0, 100, 256, 2, A, ws, None) == qb.QB_EINVAL             # blocksize
+    assert f(tab(plain), 1, 5, 64, 256, 2, A, ws, None) == qb.QB_EINVAL               # code
+    assert f(tab(plain), 1, 0, 64, 256, 9, A, ws, None) == qb.QB_EINVAL               # dtype
+    assert f(tab(plain, nested), 2, 0, 64, 256, 2, A, ws, None) == qb.QB_EUNSUPPORTED # mixed nesting
+    assert f(tab(both), 1, 0, 64, 256, 2, A, ws, None) == qb.QB_EINVAL                # absmax and nested state
+    assert f(tab(nested), 1, 0, 64, 100, 2, A, ws, None) == qb.QB_EINVAL              # blocksize2
+    bad = qb.qb_dequant_tensor(A, A, None, None, None, A + 2, 1000)
+    assert f(tab(bad), 1, 0, 64, 256, 2, A, ws, None) == qb.QB_EALIGN                 # misaligned output
+    neg = qb.qb_dequant_tensor(A, A, None, None, None, A, -5)
+    assert f(tab(neg), 1, 0, 64, 256, 2, A, ws, None) == qb.QB_EINVAL
+
+
 def test_status_strings(qb):
     assert qb.qb_status_string(0) == "ok"
     assert "workspace" in qb.qb_status_string(5)
