@@ -8,9 +8,13 @@ One step = one pass of the whole hot path over synthetic inputs resident in HBM:
      code; block size 2048) in ONE multi-tensor launch;
   2. 4-bit NF4 block-wise quantization (block 64) with nested quantization of
      the absmax (dynamic 8-bit code, block 256) of the 225 fp16 weight
-     matrices of the same decoder (6,607,077,376 weights ~N(0, 0.02));
-  3. dequantization of those 225 NF4 tensors to bf16.
-Two gradient sets alternate between steps (generated before timing).
+     matrices of the same decoder (6,607,077,376 weights ~N(0, 0.02)), in one
+     grouped call (qb_multi_tensor_quantize: four launches);
+  3. dequantization of those 225 NF4 tensors to bf16 in one grouped launch
+     (qb_multi_tensor_dequantize).
+Two gradient sets alternate between steps (generated before timing).  After
+the timed steps the two 4-bit sweeps are also timed with one qb_quantize /
+qb_dequantize call per tensor (reported under "components", not in `value`).
 
 Prints one JSON line (rank 0).  `value` is the whole step's algorithmic
 traffic divided by its time; the per-part figures (AdamW GB/s and params/s,
@@ -128,6 +132,14 @@ class Model7B:
             self.w4_ws = torch.empty(wsmax, dtype=torch.uint8, device=dev)
             self.dq_q = [qb.make_dq(c2, a2, off, W4_BLOCK2, self.w4_ws) for (_, _, _, c2, a2, off, _) in self.w4]
             self.dq_d = [qb.make_dq(c2, a2, off, W4_BLOCK2) for (_, _, _, c2, a2, off, _) in self.w4]
+            # grouped calls: the whole sweep in one quantize call (4 launches) and one dequantize launch
+            self.q_table = qb.quant_table([(w, n, codes, None, dq)
+                                           for (n, w, codes, *_), dq in zip(self.w4, self.dq_d)])
+            self.q_ws = torch.empty(qb.qb_multi_tensor_quantize_workspace_bytes(self.q_table, len(self.w4), W4_BLOCK),
+                                    dtype=torch.uint8, device=dev)
+            self.d_table = qb.dequant_table([(codes, None, dq, n, y)
+                                             for (n, _, codes, _, _, _, y), dq in zip(self.w4, self.dq_d)])
+            self.d_ws = torch.empty(qb.qb_multi_tensor_workspace_bytes(len(self.w4)), dtype=torch.uint8, device=dev)
         self.n_w4 = sum(e[0] for e in self.w4)
 
 
@@ -137,13 +149,35 @@ def run_adam(qb, model, step):
 
 
 def run_q4(qb, model):
+    qb.qb_multi_tensor_quantize(model.q_table, len(model.w4), qb.QB_F16, qb.QB_NF4, W4_BLOCK, W4_BLOCK2, model.q_ws)
+
+
+def run_dq4(qb, model):
+    qb.qb_multi_tensor_dequantize(model.d_table, len(model.w4), qb.QB_NF4, W4_BLOCK, W4_BLOCK2, qb.QB_BF16,
+                                  model.d_ws)
+
+
+def run_q4_per_tensor(qb, model):
     for (n, w, codes, *_), dq in zip(model.w4, model.dq_q):
         qb.qb_quantize(w, n, qb.QB_NF4, W4_BLOCK, codes, None, dq)
 
 
-def run_dq4(qb, model):
+def run_dq4_per_tensor(qb, model):
     for (n, _, codes, _, _, _, y), dq in zip(model.w4, model.dq_d):
         qb.qb_dequantize(codes, None, dq, qb.QB_NF4, W4_BLOCK, n, y)
+
+
+def time_calls(torch, fn, reps=5):
+    """Mean HIP-event time (ms) of fn() over reps calls after one warmup call."""
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
 def cpu_baseline(torch, model, seconds_target, rng):
@@ -322,12 +356,22 @@ def main():
         d4_bytes = model.n_w4 * w4_bytes_per_weight()
         comps["quantize4_nf4_nested"] = {"ms": q4_ms, "GB/s": q4_bytes / q4_ms / 1e6,
                                          "frac_of_hbm_peak": q4_bytes / q4_ms / 1e6 / HBM_PEAK_GBS,
-                                         "launches_per_step": 3 * len(model.w4)}
+                                         "launches_per_step": 4, "call": "qb_multi_tensor_quantize"}
         comps["dequant4_nf4_nested_bf16"] = {"ms": d4_ms, "GB/s": d4_bytes / d4_ms / 1e6,
                                              "frac_of_hbm_peak": d4_bytes / d4_ms / 1e6 / HBM_PEAK_GBS,
-                                             "launches_per_step": len(model.w4)}
+                                             "launches_per_step": 1, "call": "qb_multi_tensor_dequantize"}
         step_bytes += q4_bytes + d4_bytes
     ms_per_step = wall / args.steps * 1e3
+    if not args.adam_only:
+        # the same sweeps with one qb_quantize / qb_dequantize call per tensor (outside the timed step)
+        q1 = time_calls(torch, lambda: run_q4_per_tensor(qb, model))
+        d1 = time_calls(torch, lambda: run_dq4_per_tensor(qb, model))
+        comps["quantize4_nf4_nested_per_tensor_calls"] = {
+            "ms": q1, "GB/s": q4_bytes / q1 / 1e6, "frac_of_hbm_peak": q4_bytes / q1 / 1e6 / HBM_PEAK_GBS,
+            "launches": 4 * len(model.w4), "call": "qb_quantize"}
+        comps["dequant4_nf4_nested_bf16_per_tensor_calls"] = {
+            "ms": d1, "GB/s": d4_bytes / d1 / 1e6, "frac_of_hbm_peak": d4_bytes / d1 / 1e6 / HBM_PEAK_GBS,
+            "launches": len(model.w4), "call": "qb_dequantize"}
     traffic = traffic_per_launch()
     achieved = adam_bytes / adam_ms / 1e6
     out = {

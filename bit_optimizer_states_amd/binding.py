@@ -42,6 +42,12 @@ class qb_tensor(ctypes.Structure):
                 ("absmax_m", ctypes.c_void_p), ("absmax_v", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
+class qb_quant_tensor(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+                ("c2", ctypes.c_void_p), ("absmax2", ctypes.c_void_p), ("offset", ctypes.c_void_p),
+                ("n", ctypes.c_int64)]
+
+
 class qb_dequant_tensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p), ("c2", ctypes.c_void_p),
                 ("absmax2", ctypes.c_void_p), ("offset", ctypes.c_void_p), ("y", ctypes.c_void_p),
@@ -66,8 +72,11 @@ def lib():
                                            vp, sz, vp]
         L.qb_multi_tensor_dequantize.argtypes = [ctypes.POINTER(qb_dequant_tensor), i32, i32, i32, i32, i32, vp, sz,
                                                  vp]
+        L.qb_multi_tensor_quantize.argtypes = [ctypes.POINTER(qb_quant_tensor), i32, i32, i32, i32, i32, vp, sz, vp]
+        L.qb_multi_tensor_quantize_workspace_bytes.argtypes = [ctypes.POINTER(qb_quant_tensor), i32, i32]
+        L.qb_multi_tensor_quantize_workspace_bytes.restype = sz
         for f in (L.qb_quantize, L.qb_dequantize, L.qb_adamw8bit_step, L.qb_multi_tensor_step,
-                  L.qb_multi_tensor_dequantize):
+                  L.qb_multi_tensor_dequantize, L.qb_multi_tensor_quantize):
             f.restype = ctypes.c_int
         L.qb_dq_workspace_bytes.argtypes = [i64, i32]
         L.qb_dq_workspace_bytes.restype = sz
@@ -164,6 +173,28 @@ def qb_multi_tensor_step(table, count, gdt, blocksize, hp, ws, stream=None):
     """table: result of tensor_table(); gdt: QB_F32/QB_F16/QB_BF16; ws: device byte tensor."""
     _check(lib().qb_multi_tensor_step(table, int(count), int(gdt), int(blocksize), ctypes.byref(hp), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)), "qb_multi_tensor_step")
+
+
+def quant_table(entries):
+    """Host array of qb_quant_tensor from (x, n, codes, absmax, dq) tuples;
+    absmax is None for a nested tensor, whose dq is a qb_dq (make_dq; its ws
+    is not used)."""
+    arr = (qb_quant_tensor * len(entries))()
+    for i, (x, n, codes, absmax, dq) in enumerate(entries):
+        arr[i] = qb_quant_tensor(_ptr(x), _ptr(codes), _ptr(absmax), dq.codes if dq is not None else None,
+                                 dq.absmax2 if dq is not None else None, dq.offset if dq is not None else None, int(n))
+    return arr
+
+
+def qb_multi_tensor_quantize_workspace_bytes(table, count, blocksize):
+    return lib().qb_multi_tensor_quantize_workspace_bytes(table, int(count), int(blocksize))
+
+
+def qb_multi_tensor_quantize(table, count, xdt, code, blocksize, blocksize2, ws, stream=None):
+    """table: result of quant_table(); xdt: QB_F32/QB_F16/QB_BF16; ws: device byte tensor."""
+    _check(lib().qb_multi_tensor_quantize(table, int(count), int(xdt), int(code), int(blocksize), int(blocksize2),
+                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qb_multi_tensor_quantize")
 
 
 def dequant_table(entries):

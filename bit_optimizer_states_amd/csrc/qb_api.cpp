@@ -125,17 +125,16 @@ qb_status dequant_desc(const uint8_t* codes, const float* absmax, const uint8_t*
     return QB_OK;
 }
 
-// Copies the descriptors of a multi-tensor launch, their first tiles and the
-// coarse bucket index (see TileMap) into ws on stream s; `tiles` is the total.
-// The host staging buffer is per thread and per descriptor type; a copy from
-// pageable memory has read it before hipMemcpyAsync returns.
+// Appends the device tables of a multi-tensor launch (descriptors, the first
+// tile of every tensor, the coarse bucket index: see TileMap) to the host
+// staging buffer at byte `at` (a multiple of 16), for a copy to ws + at; fills
+// *map with those device addresses.  `tiles` is the total.
 template <class Desc>
-qb_status upload_tile_map(const std::vector<Desc>& table, int64_t tiles, int32_t count, void* ws,
-                                 hipStream_t s, TileMap<Desc>* map)
+void stage_tile_map(std::vector<unsigned char>& staging, size_t at, const std::vector<Desc>& table, int64_t tiles,
+                    int32_t count, void* ws, TileMap<Desc>* map)
 {
     thread_local std::vector<int64_t> begins;
     thread_local std::vector<int32_t> buckets;
-    thread_local std::vector<unsigned char> staging;
     begins.clear();
     buckets.clear();
     for (const Desc& d : table) begins.push_back(d.tile_begin);
@@ -154,18 +153,60 @@ qb_status upload_tile_map(const std::vector<Desc>& table, int64_t tiles, int32_t
     buckets.push_back(used - 1);
     const size_t dbytes = table.size() * sizeof(Desc), bbytes = begins.size() * sizeof(int64_t),
                  kbytes = buckets.size() * sizeof(int32_t);
-    staging.resize(dbytes + bbytes + kbytes);
-    std::memcpy(staging.data(), table.data(), dbytes);
-    std::memcpy(staging.data() + dbytes, begins.data(), bbytes);
-    std::memcpy(staging.data() + dbytes + bbytes, buckets.data(), kbytes);
-    if (hipMemcpyAsync(ws, staging.data(), staging.size(), hipMemcpyHostToDevice, s) != hipSuccess) return QB_EHIP;
-    unsigned char* w = static_cast<unsigned char*>(ws);
+    staging.resize(at + dbytes + bbytes + kbytes);
+    std::memcpy(staging.data() + at, table.data(), dbytes);
+    std::memcpy(staging.data() + at + dbytes, begins.data(), bbytes);
+    std::memcpy(staging.data() + at + dbytes + bbytes, buckets.data(), kbytes);
+    unsigned char* w = static_cast<unsigned char*>(ws) + at;
     *map = TileMap<Desc>{reinterpret_cast<const Desc*>(w), reinterpret_cast<const int64_t*>(w + dbytes),
                          reinterpret_cast<const int32_t*>(w + dbytes + bbytes), used, shift};
-    return QB_OK;
 }
 
-int64_t dequant_tiles(int64_t n) { return (n + kDequantTile - 1) / kDequantTile; }
+// One copy of the staged tables to ws on stream s (from pageable memory: the
+// copy has read the host buffer when hipMemcpyAsync returns).
+qb_status copy_staging(const std::vector<unsigned char>& staging, void* ws, hipStream_t s)
+{
+    return hipMemcpyAsync(ws, staging.data(), staging.size(), hipMemcpyHostToDevice, s) == hipSuccess ? QB_OK
+                                                                                                       : QB_EHIP;
+}
+
+// Bytes of one multi-tensor table region (qb_multi_tensor_workspace_bytes).
+size_t map_region_bytes(int32_t count)
+{
+    return count > 0 ? round_up((size_t)count * 64 + ((size_t)count + 1) * sizeof(int64_t) +
+                                    ((size_t)max_tile_buckets(count) + 1) * sizeof(int32_t), 256)
+                     : 0;
+}
+
+int64_t quant_tiles(int64_t n, int32_t B)
+{
+    const int64_t t = quant_tile_elems(B);
+    return (n + t - 1) / t;
+}
+
+// Checks one tensor of a quantization; nested: -1 = not fixed yet, 0 =
+// plain, 1 = nested (all tensors of a grouped call must agree).
+qb_status check_quant_tensor(const void* x, uint8_t* codes, float* absmax, uint8_t* c2, float* absmax2,
+                             float* offset, int64_t n, int32_t blocksize, int32_t blocksize2, int* nested)
+{
+    if (n < 0) return QB_EINVAL;
+    const int64_t nb = nblocks(n, blocksize);
+    if (nb >= (int64_t(1) << 31)) return QB_EINVAL;
+    if (!x || !codes) return QB_EINVAL;
+    if (!aligned16(x) || !aligned16(codes)) return QB_EALIGN;
+    const int mode = c2 ? 1 : 0;
+    if (*nested >= 0 && *nested != mode) return QB_EUNSUPPORTED;
+    *nested = mode;
+    if (mode) {
+        if (absmax) return QB_EINVAL;
+        qb_dq tmp{c2, absmax2, offset, blocksize2, nullptr, 0};
+        return check_dq(&tmp, nb, false);
+    }
+    if (!absmax) return QB_EINVAL;
+    return aligned16(absmax) ? QB_OK : QB_EALIGN;
+}
+
+int64_t dequant_tiles(int64_t n, int64_t tile) { return (n + tile - 1) / tile; }
 
 }  // namespace
 
@@ -237,35 +278,106 @@ qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int3
 {
     if (n < 0 || !valid_dtype(xdt) || !valid_code(code) || !pow2_block(blocksize)) return QB_EINVAL;
     if (n == 0) return QB_OK;
+    int nested = dq ? 1 : 0;
+    if (dq && !dq->codes) return QB_EINVAL;
+    qb_status st = check_quant_tensor(x, codes, absmax, dq ? dq->codes : nullptr, dq ? dq->absmax2 : nullptr,
+                                      dq ? dq->offset : nullptr, n, blocksize, dq ? dq->blocksize2 : 0, &nested);
+    if (st != QB_OK) return st;
     const int64_t nb = nblocks(n, blocksize);
-    if (nb >= (int64_t(1) << 31)) return QB_EINVAL;
-    if (!x || !codes) return QB_EINVAL;
-    if (!aligned16(x) || !aligned16(codes)) return QB_EALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int mode = dq ? QM_DQ_FIRST : QM_PLAIN;
-    unsigned long long* bins = nullptr;
-    float* first = absmax;
     if (dq) {
-        if (absmax) return QB_EINVAL;
-        qb_status st = check_dq(dq, nb, true);
+        st = check_dq(dq, nb, true);
         if (st != QB_OK) return st;
-        bins = static_cast<unsigned long long*>(dq->ws);
-        first = reinterpret_cast<float*>(static_cast<char*>(dq->ws) + kBinBytes);
-    } else {
-        if (!absmax) return QB_EINVAL;
-        if (!aligned16(absmax)) return QB_EALIGN;
     }
     if (!device_tables()) return QB_EINIT;
-    hipError_t e = hipSuccess;
-    if (dq) e = launch_clear_bins(bins, s);
-    if (e == hipSuccess) {
-        if (is4(code))
-            e = launch_quant4(x, (int)xdt, n, blocksize, code4_index(code), codes, first, mode, bins, s);
-        else
-            e = launch_quant8(x, (int)xdt, n, blocksize, codes, first, mode, bins, nullptr, s);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int bits = is4(code) ? 4 : 8, c4 = is4(code) ? code4_index(code) : 0;
+    if (!dq)
+        return hip_status(launch_quant(QuantDesc{x, codes, absmax, nullptr, n, 0, {0, 0}}, nullptr,
+                                       quant_tiles(n, blocksize), bits, c4, blocksize, (int)xdt, false, nullptr, s));
+    // nested: bins, then the fp32 absmax, in the workspace
+    unsigned long long* bins = static_cast<unsigned long long*>(dq->ws);
+    float* first = reinterpret_cast<float*>(static_cast<char*>(dq->ws) + kBinBytes);
+    const QuantDesc d1{x, codes, first, nullptr, n, 0, {0, 0}};
+    const QuantDesc d2{first, dq->codes, dq->absmax2, dq->offset, nb, 0, {0, 0}};
+    hipError_t e = launch_clear_bins(bins, 1, s);
+    if (e == hipSuccess)
+        e = launch_quant(d1, nullptr, quant_tiles(n, blocksize), bits, c4, blocksize, (int)xdt, false, bins, s);
+    if (e == hipSuccess) e = launch_dq_mean(d2, nullptr, 1, bins, s);
+    if (e == hipSuccess)
+        e = launch_quant(d2, nullptr, quant_tiles(nb, dq->blocksize2), 8, 0, dq->blocksize2, QB_F32, true, nullptr, s);
+    return hip_status(e);
+}
+
+size_t qb_multi_tensor_quantize_workspace_bytes(const qb_quant_tensor* tensors, int32_t count, int32_t blocksize)
+{
+    if (count <= 0 || !tensors || !pow2_block(blocksize)) return 0;
+    bool nested = false;
+    size_t temps = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        if (tensors[i].n < 0) return 0;
+        if (tensors[i].c2) nested = true;
+        temps += round_up((size_t)nblocks(tensors[i].n, blocksize) * sizeof(float), 256);
     }
-    if (e == hipSuccess && dq)
-        e = launch_quant8(first, QB_F32, nb, dq->blocksize2, dq->codes, dq->absmax2, QM_DQ_SECOND, bins, dq->offset, s);
+    const size_t m = map_region_bytes(count);
+    return nested ? 2 * m + (size_t)count * kBinBytes + temps : m;
+}
+
+qb_status qb_multi_tensor_quantize(const qb_quant_tensor* tensors, int32_t count, qb_dtype xdt, qb_code code,
+                                   int32_t blocksize, int32_t blocksize2, void* ws, size_t ws_bytes, void* stream)
+{
+    if (count < 0 || !valid_dtype(xdt) || !valid_code(code) || !pow2_block(blocksize)) return QB_EINVAL;
+    if (count == 0) return QB_OK;
+    if (!tensors || !ws) return QB_EINVAL;
+    if (!aligned16(ws)) return QB_EALIGN;
+    thread_local std::vector<QuantDesc> t1, t2;
+    t1.clear();
+    t2.clear();
+    int nested = -1;
+    int64_t tiles1 = 0, tiles2 = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const qb_quant_tensor& t = tensors[i];
+        qb_status st = check_quant_tensor(t.x, t.codes, t.absmax, t.c2, t.absmax2, t.offset, t.n, blocksize,
+                                          blocksize2, &nested);
+        if (st != QB_OK) return st;
+    }
+    if (ws_bytes < qb_multi_tensor_quantize_workspace_bytes(tensors, count, blocksize)) return QB_EWORKSPACE;
+    const size_t m = map_region_bytes(count);
+    unsigned char* const w = static_cast<unsigned char*>(ws);
+    unsigned long long* const bins = reinterpret_cast<unsigned long long*>(w + 2 * m);
+    unsigned char* temp = w + 2 * m + (size_t)count * kBinBytes;
+    for (int32_t i = 0; i < count; ++i) {
+        const qb_quant_tensor& t = tensors[i];
+        if (t.n == 0) continue;
+        const int64_t nb = nblocks(t.n, blocksize);
+        if (nested == 1) {
+            float* first = reinterpret_cast<float*>(temp);
+            temp += round_up((size_t)nb * sizeof(float), 256);
+            t1.push_back(QuantDesc{t.x, t.codes, first, nullptr, t.n, tiles1, {0, 0}});
+            t2.push_back(QuantDesc{first, t.c2, t.absmax2, t.offset, nb, tiles2, {0, 0}});
+            tiles2 += quant_tiles(nb, blocksize2);
+        } else {
+            t1.push_back(QuantDesc{t.x, t.codes, t.absmax, nullptr, t.n, tiles1, {0, 0}});
+        }
+        tiles1 += quant_tiles(t.n, blocksize);
+    }
+    if (t1.empty()) return QB_OK;
+    if (tiles1 >= (int64_t(1) << 31)) return QB_EINVAL;
+    if (!device_tables()) return QB_EINIT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    thread_local std::vector<unsigned char> staging;
+    staging.clear();
+    TileMap<QuantDesc> map1, map2;
+    stage_tile_map(staging, 0, t1, tiles1, count, ws, &map1);
+    if (nested == 1) stage_tile_map(staging, m, t2, tiles2, count, ws, &map2);
+    qb_status st = copy_staging(staging, ws, s);
+    if (st != QB_OK) return st;
+    const int bits = is4(code) ? 4 : 8, c4 = is4(code) ? code4_index(code) : 0;
+    if (nested != 1)
+        return hip_status(launch_quant(t1[0], &map1, tiles1, bits, c4, blocksize, (int)xdt, false, nullptr, s));
+    hipError_t e = launch_clear_bins(bins, (int)t1.size(), s);
+    if (e == hipSuccess) e = launch_quant(t1[0], &map1, tiles1, bits, c4, blocksize, (int)xdt, false, bins, s);
+    if (e == hipSuccess) e = launch_dq_mean(t2[0], &map2, (int)t2.size(), bins, s);
+    if (e == hipSuccess) e = launch_quant(t2[0], &map2, tiles2, 8, 0, blocksize2, QB_F32, true, nullptr, s);
     return hip_status(e);
 }
 
@@ -281,9 +393,9 @@ qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* 
                                 dq ? dq->offset : nullptr, dq ? dq->blocksize2 : 0, n, y, blocksize, &mode, &d);
     if (st != QB_OK) return st;
     if (!device_tables()) return QB_EINIT;
-    return hip_status(launch_dequant(d, nullptr, dequant_tiles(n), is4(code) ? 4 : 8, is4(code) ? code4_index(code) : 0,
-                                     blocksize, dq ? dq->blocksize2 : 256, dq != nullptr, (int)ydt,
-                                     static_cast<hipStream_t>(stream)));
+    return hip_status(launch_dequant(d, nullptr, dequant_tiles(n, kDequantTile), is4(code) ? 4 : 8,
+                                     is4(code) ? code4_index(code) : 0, blocksize, dq ? dq->blocksize2 : 256,
+                                     dq != nullptr, (int)ydt, static_cast<hipStream_t>(stream)));
 }
 
 qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t count, qb_code code,
@@ -308,14 +420,17 @@ qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t c
         if (t.n == 0) continue;
         d.tile_begin = tiles;
         table.push_back(d);
-        tiles += dequant_tiles(t.n);
+        tiles += dequant_tiles(t.n, kDequantTileMulti);
     }
     if (table.empty()) return QB_OK;
     if (tiles >= (int64_t(1) << 31)) return QB_EINVAL;
     if (!device_tables()) return QB_EINIT;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    thread_local std::vector<unsigned char> staging;
+    staging.clear();
     TileMap<DequantDesc> map;
-    qb_status st = upload_tile_map(table, tiles, count, ws, s, &map);
+    stage_tile_map(staging, 0, table, tiles, count, ws, &map);
+    qb_status st = copy_staging(staging, ws, s);
     if (st != QB_OK) return st;
     return hip_status(launch_dequant(table[0], &map, tiles, is4(code) ? 4 : 8, is4(code) ? code4_index(code) : 0,
                                      blocksize, mode == 1 ? blocksize2 : 256, mode == 1, (int)ydt, s));
@@ -368,8 +483,11 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
     if (tiles >= (int64_t(1) << 31)) return QB_EINVAL;
     if (!device_tables()) return QB_EINIT;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    thread_local std::vector<unsigned char> staging;
+    staging.clear();
     TileMap<TensorDesc> map;
-    qb_status st = upload_tile_map(table, tiles, count, ws, s, &map);
+    stage_tile_map(staging, 0, table, tiles, count, ws, &map);
+    qb_status st = copy_staging(staging, ws, s);
     if (st != QB_OK) return st;
     return hip_status(launch_adamw8(table[0], &map, tiles, blocksize, (int)gdt, prepare(*hp), s));
 }

@@ -8,10 +8,11 @@
 // decoded first, a_b = dyn8[c2_b] * absmax2[b / B2] + mean, two rounded binary32
 // operations ("Bitsandbytes", section İç içe nicelleştirme).
 //
-// Kernel shape: one 256-thread workgroup per tile of 8192 elements, launched in
-// tile order.  A thread takes 4 units of 8 consecutive elements (one u32 of
-// 4-bit codes or two of 8-bit codes), consecutive lanes on consecutive units,
-// so every load and store instruction of a wave covers one contiguous span.
+// Kernel shape: one 256-thread workgroup per tile of 256 x 8 x U elements
+// (U = 4: 8192; measured on MI355X, 2 and 8 are slower), in tile order.  A
+// thread takes U units of 8 consecutive elements (one u32 of 4-bit codes or
+// two of 8-bit codes), consecutive lanes on consecutive units, so every load
+// and store instruction of a wave covers one contiguous span.
 // At the start a workgroup issues the loads of its codes and of the scale
 // inputs of its tile's blocks (one block per thread, at most 128 blocks per
 // tile since B >= 64), then stages the code tables in LDS; the blocks' scales
@@ -27,11 +28,21 @@ namespace qb {
 
 namespace {
 
+// XCD-contiguous tile order (tile_of) for grouped launches; measured on
+// MI355X it speeds up the grouped 7B-weight sweep by about 3% and slows
+// single-tensor launches by about 10%, so those keep the plain order.
+#ifndef QB_DQ_MULTI_REMAP
+#define QB_DQ_MULTI_REMAP 1
+#endif
+// Decode the nested absmax with the dynamic code read from global memory (L2)
+// by the threads that own a block, instead of staging the whole code in LDS.
+#ifndef QB_DQ_DIRECT_DYN
+#define QB_DQ_DIRECT_DYN 0
+#endif
+
 constexpr int kDqThreads = 256;
-constexpr int kDqUnits = 4;                    // units of 8 elements per thread
-constexpr int kDqElems = kDqThreads * kDqUnits * 8;
-static_assert(kDqElems == kDequantTile, "tile size");
-constexpr int kDqMaxBlocks = kDqElems / 64;    // blocks per tile at B = 64
+static_assert(kDequantTile / 64 <= kDqThreads && kDequantTileMulti / 64 <= kDqThreads,
+              "one thread per block of a tile");
 
 // The 8 codes of the unit at element offset e (a multiple of 8) from base.
 template <int BITS>
@@ -75,10 +86,12 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
                                                         int log2B2, int code4, const QbTables* __restrict__ tab)
 {
     __shared__ float s_val[BITS == 8 ? 256 : 16];   // decode table of the codes
-    __shared__ float s_dyn[DQ && BITS == 4 ? 256 : 1];
-    __shared__ float s_scale[kDqMaxBlocks];
+    __shared__ float s_dyn[DQ && BITS == 4 && !QB_DQ_DIRECT_DYN ? 256 : 1];
+    constexpr int kDqUnits = MULTI ? QB_DQ_MULTI_UNITS : QB_DQ_UNITS;   // units of 8 elements per thread
+    constexpr int kDqElems = kDqThreads * kDqUnits * 8;
+    __shared__ float s_scale[kDqElems / 64];                            // blocks per tile at B = 64
     const int tid = threadIdx.x;
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = tile_of<MULTI && QB_DQ_MULTI_REMAP>(blockIdx.x, gridDim.x);
 
     DequantDesc d;
     int64_t lt;
@@ -100,8 +113,9 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
 #pragma unroll
         for (int k = 0; k < kDqUnits; ++k) w[k] = load_unit<BITS>(ct, (uint32_t)(k * kDqThreads + tid) * 8);
     }
-    // scale inputs of the tile's blocks, one block per thread
-    const int nbt = kDqElems >> log2B;                   // blocks per tile (B <= 4096 < tile)
+    // scale inputs of the tile's blocks, one block per thread (B and the tile
+    // are powers of two: a tile holds whole blocks, or lies within one block)
+    const int nbt = (kDqElems >> log2B) > 0 ? (kDqElems >> log2B) : 1;
     const int64_t blk = (tbase >> log2B) + tid;
     const int64_t nb = (n + (int64_t(1) << log2B) - 1) >> log2B;
     const bool owner = tid < nbt && blk < nb;
@@ -111,6 +125,7 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
         if constexpr (DQ) {
             sc = gld<uint8_t>(d.c2 + blk);
             sa = gld<float>(d.absmax2 + (blk >> log2B2));
+            if constexpr (BITS == 4 && QB_DQ_DIRECT_DYN) sa = tab->dyn8[sc] * sa;
         } else {
             sa = gld<float>(d.absmax + blk);
         }
@@ -122,12 +137,12 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
         s_val[tid] = tab->dyn8[tid];
     } else {
         if (tid < 16) s_val[tid] = (code4 == 0 ? tab->nf4 : tab->fp4)[tid];
-        if constexpr (DQ) s_dyn[tid] = tab->dyn8[tid];
+        if constexpr (DQ && !QB_DQ_DIRECT_DYN) s_dyn[tid] = tab->dyn8[tid];
     }
     __syncthreads();
     if (owner) {
         if constexpr (DQ) {
-            const float prod = (BITS == 8 ? s_val : s_dyn)[sc] * sa;
+            const float prod = (BITS == 4 && QB_DQ_DIRECT_DYN) ? sa : (BITS == 8 ? s_val : s_dyn)[sc] * sa;
             s_scale[tid] = prod + mu;
         } else {
             s_scale[tid] = sa;

@@ -254,6 +254,23 @@ __device__ __forceinline__ void store8(void* y, int64_t i, const float* o)
 // multi-tensor launches
 // ---------------------------------------------------------------------------
 
+// Tile handled by workgroup b of ntiles.  The hardware deals workgroups
+// round-robin to the 8 XCDs; with REMAP each XCD takes one contiguous range of
+// tiles instead of every eighth tile (a bijection of [0, ntiles): XCD x holds
+// q + (x < r) workgroups, q = ntiles / 8, r = ntiles % 8).
+template <bool REMAP>
+__device__ __forceinline__ int64_t tile_of(int64_t b, int64_t ntiles)
+{
+    if constexpr (REMAP) {
+        constexpr int X = 8;
+        const int64_t q = ntiles / X, r = ntiles % X;
+        const int64_t x = b % X, k = b / X;
+        return x * q + (x < r ? x : r) + k;
+    } else {
+        return b;
+    }
+}
+
 // Index of the tensor holding global tile `tile`: between the tensor holding
 // the first tile of tile's bucket and the one holding the next bucket's first
 // tile (usually the same or adjacent ones), by binary search on tile_begin
@@ -384,13 +401,14 @@ __device__ __forceinline__ uint32_t enc_dyn8_pos(float nv, const DynEncLds& s)
     return c + (nv >= s.thr[c] ? 1u : 0u);
 }
 
-// 4-bit code (NF4 or FP4 by the table) of a normalized value in [-1, 1].
+// 4-bit code (NF4 or FP4 by the table) of a normalized value in [-1, 1]:
+// bucket (int)(16 nv + 16) in [0, 32] (16 nv is exact, so the fused form
+// rounds like the separate operations), then below or above the bucket's one
+// threshold.  |nv| <= 1 holds for every finite input (nv = x / absmax).
 __device__ __forceinline__ uint32_t enc_4bit(float nv, const uint2* __restrict__ lut)
 {
-    float u = nv * 16.0f + 16.0f;
-    int b = min((int)u, k4LutN - 1);
-    uint2 e = lut[b];
-    return (nv >= ffrom(e.x)) ? ((e.y >> 8) & 0xFFu) : (e.y & 0xFFu);
+    const uint2 e = lut[(int)__builtin_fmaf(nv, 16.0f, 16.0f)];
+    return __builtin_amdgcn_ubfe(e.y, nv >= ffrom(e.x) ? 8u : 0u, 8u);
 }
 
 }  // namespace qb

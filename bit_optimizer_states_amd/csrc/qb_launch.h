@@ -11,8 +11,6 @@
 
 namespace qb {
 
-enum QuantMode { QM_PLAIN = 0, QM_DQ_FIRST = 1, QM_DQ_SECOND = 2 };
-
 // Exponent bins of the nested-quantization mean at the start of the workspace:
 // kBinCopies copies of 256 uint64 words (254 used; the copies spread the
 // atomics of different workgroups), then the fp32 absmax of the first level.
@@ -36,6 +34,22 @@ struct TensorDesc {
     int64_t tile_begin;
 };
 static_assert(sizeof(TensorDesc) == 64, "descriptor layout");
+
+// One tensor of a quantization pass; tile_begin is its first global tile.
+// First pass: x [n] of the input dtype, codes out, absmax out (the caller's,
+// or the fp32 workspace of a nested quantization).  Second pass of
+// a nested quantization: x = that fp32 absmax [n = its count], codes = the
+// nested codes, absmax = the second-level absmax, offset[0] = the mean.
+struct QuantDesc {
+    const void* x;
+    uint8_t* codes;
+    float* absmax;
+    float* offset;
+    int64_t n;
+    int64_t tile_begin;
+    int64_t pad[2];
+};
+static_assert(sizeof(QuantDesc) == 64, "descriptor layout");
 
 // One tensor of a grouped dequantization; tile_begin is its first global tile.
 struct DequantDesc {
@@ -109,19 +123,43 @@ hipError_t launch_kernel(void (*kernel)(KArgs...), int grid, hipStream_t s, Args
     return launch_kernel_nt(kernel, grid, 256, s, std::forward<Args>(args)...);
 }
 
-hipError_t launch_clear_bins(unsigned long long* bins, hipStream_t s);
+// Zero `sets` sets of nested-quantization exponent bins (kBinWords each).
+hipError_t launch_clear_bins(unsigned long long* bins, int sets, hipStream_t s);
 
-hipError_t launch_quant8(const void* x, int xdt, int64_t n, int B, uint8_t* codes, float* absmax, int mode,
-                         unsigned long long* bins, float* offset, hipStream_t s);
-hipError_t launch_quant4(const void* x, int xdt, int64_t n, int B, int code4, uint8_t* codes, float* absmax,
-                         int mode, unsigned long long* bins, hipStream_t s);
+// Elements per tile of the quantization kernel: QB_Q_TILE, or one sub-tile of
+// 256 threads x B / 256 elements where that is larger (B = 4096).
+#ifndef QB_Q_TILE
+#define QB_Q_TILE 4096
+#endif
+constexpr int64_t quant_tile_elems(int B) { return B > QB_Q_TILE ? B : QB_Q_TILE; }
+
+// Quantize one tensor (map == nullptr) or the tensors of `map` (ntiles in
+// all); bits 8 (dynamic code) or 4 (code4: 0 NF4, 1 FP4).  bins: the exponent
+// bins of a nested first pass (tensor i of the map uses set i), else nullptr.
+// second: the nested second pass (bits 8, fp32 input, mean in offset[0]).
+hipError_t launch_quant(const QuantDesc& single, const TileMap<QuantDesc>* map, int64_t ntiles, int bits, int code4,
+                        int B, int xdt, bool second, unsigned long long* bins, hipStream_t s);
+
+// Exact mean of the absmax of one tensor (map == nullptr) or of the `count`
+// tensors of map (second-pass descriptors) into offset[0].
+hipError_t launch_dq_mean(const QuantDesc& single, const TileMap<QuantDesc>* map, int count,
+                          const unsigned long long* bins, hipStream_t s);
+
 // Dequantize one tensor (map == nullptr) or the tensors of `map` (ntiles in
 // all); bits 8 (dynamic code) or 4 (code4: 0 NF4, 1 FP4); dq: nested absmax.
 hipError_t launch_dequant(const DequantDesc& single, const TileMap<DequantDesc>* map, int64_t ntiles, int bits,
                           int code4, int B, int B2, bool dq, int ydt, hipStream_t s);
 
-// Elements per tile of the dequantization kernel.
-constexpr int64_t kDequantTile = 8192;
+// Units of 8 elements per thread of the dequantization kernel (256 threads)
+// for one tensor and for a grouped launch, and the elements of their tiles.
+#ifndef QB_DQ_UNITS
+#define QB_DQ_UNITS 4
+#endif
+#ifndef QB_DQ_MULTI_UNITS
+#define QB_DQ_MULTI_UNITS 4
+#endif
+constexpr int64_t kDequantTile = 256 * 8 * QB_DQ_UNITS;
+constexpr int64_t kDequantTileMulti = 256 * 8 * QB_DQ_MULTI_UNITS;
 // map: the device tables of a multi-tensor launch, or nullptr for the one
 // tensor `single`.
 hipError_t launch_adamw8(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B, int gdt,

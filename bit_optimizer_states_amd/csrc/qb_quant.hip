@@ -9,50 +9,60 @@
 // de LLM", section Etapa 1); the absmax may itself be quantized a second time
 // ("Bitsandbytes", section İç içe nicelleştirme).
 //
-// Kernel shape: one 256-thread workgroup per tile, launched in tile order, so
-// the HBM accesses of all resident workgroups form one narrow moving front
-// (measured on MI355X: a copy reaches 6.2 TB/s this way against 4.6 TB/s for a
-// persistent grid-stride loop).  Each workgroup issues its tile's loads before
-// staging its small LDS tables, so the staging hides under the load latency.
+// Kernel shape: one 256-thread workgroup per tile of 4096 elements, launched in
+// tile order, so the HBM accesses of all resident workgroups form one narrow
+// moving front (measured on MI355X: a copy reaches 6.2 TB/s this way against
+// 4.6 TB/s for a persistent grid-stride loop).  A tile is R sub-tiles of
+// 256 x EPT elements; a thread owns EPT elements of one block in every
+// sub-tile (LPB lanes share a block).  Each workgroup issues all its loads
+// before staging its LDS tables, so the staging hides under the load latency.
 // A tile whose elements all lie below n takes unguarded vector loads and
-// stores; only the last tile is guarded element by element.  The first pass of
-// a nested quantization is the exception: it strides persistently so that each
-// workgroup flushes its exponent bins with few global atomics.
+// stores; only the last tile of a tensor is guarded element by element.
+//
+// Nested quantization takes four launches: clear the exponent bins, quantize
+// (the fp32 absmax goes to a workspace and into the bins), compute the exact
+// mean of the absmax from the bins, quantize absmax - mean with the dynamic
+// code.  Many tensors go in one launch per step: tiles of all tensors are
+// numbered in one range and a workgroup finds its tensor through the coarse
+// bucket index.
+#include <type_traits>
+
 #include "qb_device.h"
-#include "qb_launch.h"
 
 namespace qb {
+
+// XCD-contiguous tile order (tile_of) for grouped launches.
+#ifndef QB_Q_MULTI_REMAP
+#define QB_Q_MULTI_REMAP 1
+#endif
 
 // ---------------------------------------------------------------------------
 // tile geometry
 // ---------------------------------------------------------------------------
 
-// 8-bit quantize: chunks of 4 elements (16 bytes of fp32 in, one u32 of codes
-// out); at least 8 elements per thread.
-template <int B>
-struct Tile8 {
-    static constexpr int EPT = B >= 2048 ? B / 256 : 8;   // elements per thread
-    static constexpr int LPB = B / EPT;                   // lanes per block: 8 .. 256
-    static constexpr int BPT = kThreads / LPB;            // blocks per tile
-    static constexpr int CH = EPT / 4;                    // chunks per thread
-    static constexpr int ELEMS = kThreads * EPT;          // elements per tile
-    static constexpr int WPB = LPB > 64 ? LPB / 64 : 1;   // waves per block
+// BITS 8: chunks of 4 elements (one u32 of codes); BITS 4: chunks of 8 (one
+// u32 of packed codes).  At least 8 elements per thread and sub-tile.
+template <int BITS, int B>
+struct QGeo {
+    static constexpr int CW = BITS == 8 ? 4 : 8;                      // elements per chunk
+    static constexpr int EPT = B / kThreads >= 8 ? B / kThreads : 8;  // elements per thread and sub-tile
+    static constexpr int LPB = B / EPT;                               // lanes per block: 8 .. 256
+    static constexpr int BPS = kThreads / LPB;                        // blocks per sub-tile
+    static constexpr int CH = EPT / CW;                               // chunks per thread
+    static constexpr int SUB = kThreads * EPT;                        // elements per sub-tile
+    static constexpr int ELEMS = (int)quant_tile_elems(B);            // elements per tile
+    static constexpr int R = ELEMS / SUB;                             // sub-tiles per tile
+    static constexpr int WPB = LPB > 64 ? LPB / 64 : 1;               // waves per block
+    static_assert(R >= 1 && ELEMS == SUB * R && EPT % CW == 0 && LPB <= kThreads, "quantize tile geometry");
 };
 
-// 4-bit quantize: chunks of 8 elements (one u32 of packed codes out).
-template <int B>
-struct Tile4 {
-    static constexpr int EPT = B >= 4096 ? B / 256 : 8;
-    static constexpr int LPB = B / EPT;                   // 8 .. 256
-    static constexpr int BPT = kThreads / LPB;
-    static constexpr int CH = EPT / 8;
-    static constexpr int ELEMS = kThreads * EPT;
-    static constexpr int WPB = LPB > 64 ? LPB / 64 : 1;
-};
+// ---------------------------------------------------------------------------
+// reductions and the exact mean
+// ---------------------------------------------------------------------------
 
 // Block maximum of non-negative values (as bits); every lane of the block gets
-// it.  `red` is a double-buffered LDS scratch half: with persistent loops the
-// next tile's barrier orders its reuse, so one barrier per tile suffices.
+// it.  `red` is LDS scratch of its own per call site (no reuse, so one barrier
+// per call suffices).
 template <class T>
 __device__ __forceinline__ uint32_t block_max(uint32_t x, uint32_t* red, int tid)
 {
@@ -180,249 +190,187 @@ __device__ __forceinline__ float exact_mean_wg(const unsigned long long* __restr
 }
 
 // ---------------------------------------------------------------------------
-// 8-bit dynamic-code quantize
+// quantize kernel
 // ---------------------------------------------------------------------------
 
-// One tile of the 8-bit quantizer.  MODE: QM_PLAIN writes absmax; QM_DQ_FIRST
-// also bins it; QM_DQ_SECOND quantizes x - mu.
-template <int B, int XDT, int MODE>
-__device__ __forceinline__ void quant8_tile(int64_t tile, const void* __restrict__ x, int64_t n,
-                                           uint8_t* __restrict__ codes, float* __restrict__ absmax,
-                                           float mu, unsigned long long* s_bins, uint32_t* red,
-                                           const DynEncLds& enc, const QbTables* __restrict__ tab,
-                                           DynEncLds* stage, int tid)
-{
-    using T = Tile8<B>;
-    const int bt = tid / T::LPB, l = tid % T::LPB;
-    const int64_t nb = (n + B - 1) / B;
-    const int64_t blk = tile * T::BPT + bt;
-    const int64_t bstart = blk * B;
-    const bool full = (tile + 1) * T::ELEMS <= n;
-    float v[T::EPT];
-    if (full) {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c) load4<XDT>(x, bstart + c * T::LPB * 4 + l * 4, &v[c * 4]);
-    } else {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t idx = bstart + c * T::LPB * 4 + l * 4 + j;
-                v[c * 4 + j] = idx < n ? load1<XDT>(x, idx) : 0.0f;
-            }
-    }
-    if (stage) {            // one-tile launches: stage the tables while the loads fly
-        stage_dyn_enc(*stage, tab, tid);
-        __syncthreads();
-    }
-    if constexpr (MODE == QM_DQ_SECOND) {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (full || bstart + c * T::LPB * 4 + l * 4 + j < n) v[c * 4 + j] = v[c * 4 + j] - mu;
-    }
-    uint32_t mx = 0;
-#pragma unroll
-    for (int i = 0; i < T::EPT; ++i) mx = max(mx, fbits(v[i]) & 0x7FFFFFFFu);
-    mx = block_max<T>(mx, red, tid);
-    const float a = ffrom(mx);
-    if (l == 0 && blk < nb) {
-        gst<float>(absmax + blk, a);
-        if constexpr (MODE == QM_DQ_FIRST) bin_absmax(s_bins, mx);
-    }
+struct Lut4Lds {
+    uint2 e[k4LutN];
+};
 
-    const float r = rcp_rn(a);            // used only where fast_div_ok(a)
-    const bool fast = fast_div_ok(a);
-    uint32_t packed[T::CH];
-    if (__all(fast)) {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w |= enc_dyn8(div_by_block(v[c * 4 + j], a, r), enc) << (8 * j);
-            packed[c] = w;
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float xv = v[c * 4 + j];
-                const float nv = fast ? div_by_block(xv, a, r) : (a > 0.0f ? xv / a : 0.0f);
-                w |= enc_dyn8(nv, enc) << (8 * j);
-            }
-            packed[c] = w;
-        }
-    }
-    if (full) {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c) gst<uint32_t>(codes + bstart + c * T::LPB * 4 + l * 4, packed[c]);
-    } else {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t idx = bstart + c * T::LPB * 4 + l * 4 + j;
-                if (idx < n) gst<uint8_t>(codes + idx, (uint8_t)(packed[c] >> (8 * j)));
-            }
-    }
+// CW consecutive elements of dtype DT at element offset e from a uniform base.
+template <int DT, int CW>
+__device__ __forceinline__ void load_chunk(const void* base, uint32_t e, float* v)
+{
+    if constexpr (CW == 4) load4o<DT>(base, e, v);
+    else load8o<DT>(base, e, v);
 }
 
-// One workgroup per tile (QM_PLAIN, QM_DQ_SECOND).
-template <int B, int XDT, int MODE>
-__global__ __launch_bounds__(256) void k_quant8(const void* __restrict__ x, int64_t n,
-                                                uint8_t* __restrict__ codes, float* __restrict__ absmax,
-                                                const QbTables* __restrict__ tab,
-                                                const unsigned long long* __restrict__ bins,
-                                                float* __restrict__ offset)
+// One tile.  SECOND: the input is the fp32 absmax of a first pass and the
+// tensor's mean (offset[0], written by k_dq_mean) is subtracted first.  With
+// bins != nullptr (first pass of a nested quantization) every block absmax is
+// also added to the tensor's exponent bins.
+template <int BITS, int B, int XDT, bool SECOND, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<QuantDesc> map,
+                                                   unsigned long long* __restrict__ bins,
+                                                   const QbTables* __restrict__ tab, int code4)
 {
-    __shared__ DynEncLds s_enc;
-    __shared__ uint32_t s_red[4];
-    const int tid = threadIdx.x;
-    float mu = 0.0f;
-    if constexpr (MODE == QM_DQ_SECOND) {
-        mu = exact_mean_wg(bins, (uint32_t)n, tid);
-        if (blockIdx.x == 0 && tid == 0) gst<float>(offset, mu);
-    }
-    quant8_tile<B, XDT, MODE>(blockIdx.x, x, n, codes, absmax, mu, nullptr, s_red, s_enc, tab, &s_enc, tid);
-}
-
-// Persistent grid-stride variant for the first pass of a nested quantization.
-template <int B, int XDT>
-__global__ __launch_bounds__(256) void k_quant8_binned(const void* __restrict__ x, int64_t n,
-                                                       uint8_t* __restrict__ codes, float* __restrict__ absmax,
-                                                       const QbTables* __restrict__ tab,
-                                                       unsigned long long* __restrict__ bins, int64_t ntiles)
-{
-    __shared__ DynEncLds s_enc;
-    __shared__ uint32_t s_red[2][4];
+    using G = QGeo<BITS, B>;
+    using EncLds = std::conditional_t<BITS == 8, DynEncLds, Lut4Lds>;
+    __shared__ EncLds s_enc;
+    __shared__ uint32_t s_red[G::R][4];
     __shared__ unsigned long long s_bins[256];
     const int tid = threadIdx.x;
-    stage_dyn_enc(s_enc, tab, tid);
-    s_bins[tid] = 0ull;
-    __syncthreads();
-    int par = 0;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x, par ^= 1)
-        quant8_tile<B, XDT, QM_DQ_FIRST>(tile, x, n, codes, absmax, 0.0f, s_bins, s_red[par], s_enc, tab, nullptr, tid);
-    __syncthreads();
-    if (tid < 254 && s_bins[tid]) atomicAdd(&bins[(blockIdx.x % kBinCopies) * 256 + tid], s_bins[tid]);
-}
+    const int64_t tile = tile_of<MULTI && QB_Q_MULTI_REMAP>(blockIdx.x, gridDim.x);
 
-// ---------------------------------------------------------------------------
-// 4-bit (NF4 / FP4) quantize
-// ---------------------------------------------------------------------------
-
-template <int B, int XDT, int MODE>
-__device__ __forceinline__ void quant4_tile(int64_t tile, const void* __restrict__ x, int64_t n,
-                                           uint8_t* __restrict__ codes, float* __restrict__ absmax,
-                                           unsigned long long* s_bins, uint32_t* red, uint2* s_lut,
-                                           const uint2* __restrict__ glut, bool stage, int tid)
-{
-    using T = Tile4<B>;
-    const int bt = tid / T::LPB, l = tid % T::LPB;
-    const int64_t nb = (n + B - 1) / B;
-    const int64_t blk = tile * T::BPT + bt;
-    const int64_t bstart = blk * B;
-    const bool full = (tile + 1) * T::ELEMS <= n;
-    float v[T::EPT];
-    if (full) {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c) load8<XDT>(x, bstart + c * T::LPB * 8 + l * 8, &v[c * 8]);
+    QuantDesc d;
+    int64_t lt;
+    int ti;
+    if constexpr (MULTI) {
+        ti = find_tensor(map, tile);
+        d = map.descs[ti];
+        lt = tile - d.tile_begin;
     } else {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t idx = bstart + c * T::LPB * 8 + l * 8 + j;
-                v[c * 8 + j] = idx < n ? load1<XDT>(x, idx) : 0.0f;
-            }
+        ti = 0;
+        d = single;
+        lt = tile;
     }
-    if (stage) {
-        if (tid < k4LutN) s_lut[tid] = glut[tid];
-        __syncthreads();
-    }
-    uint32_t mx = 0;
-#pragma unroll
-    for (int i = 0; i < T::EPT; ++i) mx = max(mx, fbits(v[i]) & 0x7FFFFFFFu);
-    mx = block_max<T>(mx, red, tid);
-    const float a = ffrom(mx);
-    if (l == 0 && blk < nb) {
-        gst<float>(absmax + blk, a);
-        if constexpr (MODE == QM_DQ_FIRST) bin_absmax(s_bins, mx);
-    }
+    const int64_t n = d.n;
+    const int64_t tbase = lt * G::ELEMS;                  // first element of the tile
+    const bool full = tbase + G::ELEMS <= n;
+    const int64_t rem = n - tbase;                        // elements of the tensor from the tile start
+    const int bt = tid / G::LPB, l = tid % G::LPB;
+    const void* const xt = static_cast<const char*>(d.x) + tbase * (XDT == DT_F32 ? 4 : 2);
 
-    const float r = rcp_rn(a);            // used only where fast_div_ok(a)
-    const bool fast = fast_div_ok(a);
-    const bool all_fast = __all(fast);
-    uint32_t packed[T::CH];
+    // loads of every sub-tile first
+    float v[G::R][G::EPT];
 #pragma unroll
-    for (int c = 0; c < T::CH; ++c) {
-        uint32_t w = 0;
+    for (int r = 0; r < G::R; ++r) {
+        const uint32_t e0 = (uint32_t)((r * G::BPS + bt) * B + l * G::CW);   // chunk 0 of this thread
+        if (full) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float n0 = v[c * 8 + 2 * k], n1 = v[c * 8 + 2 * k + 1];
-            if (all_fast) {
-                n0 = div_by_block(n0, a, r);
-                n1 = div_by_block(n1, a, r);
-            } else {
-                n0 = fast ? div_by_block(n0, a, r) : (a > 0.0f ? n0 / a : 0.0f);
-                n1 = fast ? div_by_block(n1, a, r) : (a > 0.0f ? n1 / a : 0.0f);
-            }
-            const uint32_t byte = (enc_4bit(n0, s_lut) << 4) | enc_4bit(n1, s_lut);
-            w |= byte << (8 * k);
+            for (int c = 0; c < G::CH; ++c) load_chunk<XDT, G::CW>(xt, e0 + c * G::LPB * G::CW, &v[r][c * G::CW]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < G::CH; ++c)
+#pragma unroll
+                for (int j = 0; j < G::CW; ++j) {
+                    const uint32_t e = e0 + c * G::LPB * G::CW + j;
+                    v[r][c * G::CW + j] = (int64_t)e < rem ? load1<XDT>(xt, e) : 0.0f;
+                }
         }
-        packed[c] = w;
     }
-    if (full) {
-#pragma unroll
-        for (int c = 0; c < T::CH; ++c) gst<uint32_t>(codes + (bstart + c * T::LPB * 8 + l * 8) / 2, packed[c]);
+    const bool binning = !SECOND && bins != nullptr;
+    float mu = 0.0f;
+    if constexpr (SECOND) mu = gld<float>(d.offset);
+    if constexpr (BITS == 8) {
+        stage_dyn_enc(s_enc, tab, tid);
     } else {
+        const uint2* glut = reinterpret_cast<const uint2*>(code4 == 0 ? tab->nf4_lut : tab->fp4_lut);
+        if (tid < k4LutN) s_enc.e[tid] = glut[tid];
+    }
+    if (binning) s_bins[tid] = 0ull;
+    __syncthreads();
+
+    const int64_t nb = (n + B - 1) / B;
+    const int64_t blk0 = tbase / B;                       // a tile holds whole blocks
+    uint32_t packed[G::R][G::CH];
 #pragma unroll
-        for (int c = 0; c < T::CH; ++c)
+    for (int r = 0; r < G::R; ++r) {
+        float* const vr = v[r];
+        const int64_t blk = blk0 + r * G::BPS + bt;
+        if constexpr (SECOND) {
+            const uint32_t e0 = (uint32_t)((r * G::BPS + bt) * B + l * G::CW);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int64_t e0 = bstart + c * T::LPB * 8 + l * 8 + 2 * k;
-                if (e0 < n) {
-                    uint32_t byte = (packed[c] >> (8 * k)) & 0xFFu;
-                    if (e0 + 1 >= n) byte &= 0xF0u;        // odd n: the last low nibble is 0
-                    gst<uint8_t>(codes + e0 / 2, (uint8_t)byte);
+            for (int c = 0; c < G::CH; ++c)
+#pragma unroll
+                for (int j = 0; j < G::CW; ++j)
+                    if (full || (int64_t)(e0 + c * G::LPB * G::CW + j) < rem) vr[c * G::CW + j] = vr[c * G::CW + j] - mu;
+        }
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < G::EPT; ++i) mx = max(mx, fbits(vr[i]) & 0x7FFFFFFFu);
+        mx = block_max<G>(mx, s_red[r], tid);
+        const float a = ffrom(mx);
+        if (l == 0 && blk < nb) {
+            gst<float>(d.absmax + blk, a);
+            if (binning) bin_absmax(s_bins, mx);
+        }
+        const float rc = rcp_rn(a);                      // used only where fast_div_ok(a)
+        const bool fast = fast_div_ok(a);
+        float nv[G::EPT];
+        if (__all(fast)) {                               // the usual case: one straight-line pass
+#pragma unroll
+            for (int i = 0; i < G::EPT; ++i) nv[i] = div_by_block(vr[i], a, rc);
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::EPT; ++i)
+                nv[i] = fast ? div_by_block(vr[i], a, rc) : (a > 0.0f ? vr[i] / a : 0.0f);
+        }
+#pragma unroll
+        for (int c = 0; c < G::CH; ++c) {
+            uint32_t w = 0;
+            if constexpr (BITS == 8) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w |= enc_dyn8(nv[c * 4 + j], s_enc) << (8 * j);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    w |= ((enc_4bit(nv[c * 8 + 2 * k], s_enc.e) << 4) | enc_4bit(nv[c * 8 + 2 * k + 1], s_enc.e))
+                         << (8 * k);
+            }
+            packed[r][c] = w;
+        }
+    }
+
+    // codes: one u32 per chunk (4 codes of 8 bits or 8 of 4 bits)
+    uint8_t* const ct = d.codes + (tbase * BITS) / 8;
+#pragma unroll
+    for (int r = 0; r < G::R; ++r) {
+        const uint32_t e0 = (uint32_t)((r * G::BPS + bt) * B + l * G::CW);
+        if (full) {
+#pragma unroll
+            for (int c = 0; c < G::CH; ++c)
+                gsto<uint32_t>(ct, (e0 + c * G::LPB * G::CW) * BITS / 8, packed[r][c]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < G::CH; ++c) {
+                const uint32_t ec = e0 + c * G::LPB * G::CW;
+                if constexpr (BITS == 8) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if ((int64_t)(ec + j) < rem) gst<uint8_t>(ct + ec + j, (uint8_t)(packed[r][c] >> (8 * j)));
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t e = ec + 2 * k;
+                        if ((int64_t)e < rem) {
+                            uint32_t byte = (packed[r][c] >> (8 * k)) & 0xFFu;
+                            if ((int64_t)e + 1 >= rem) byte &= 0xF0u;   // odd n: the last low nibble is 0
+                            gst<uint8_t>(ct + e / 2, (uint8_t)byte);
+                        }
+                    }
                 }
             }
+        }
+    }
+
+    if (binning) {
+        __syncthreads();
+        unsigned long long* const tb = bins + (size_t)ti * kBinWords + (blockIdx.x % kBinCopies) * 256;
+        if (tid < 254 && s_bins[tid]) atomicAdd(&tb[tid], s_bins[tid]);
     }
 }
 
-template <int B, int XDT>
-__global__ __launch_bounds__(256) void k_quant4(const void* __restrict__ x, int64_t n, uint8_t* __restrict__ codes,
-                                                float* __restrict__ absmax, const QbTables* __restrict__ tab,
-                                                int code4)
+// Exact mean of each tensor's absmax from its bins into offset[0]; one
+// workgroup per tensor (descriptors of the second pass: n = absmax count).
+template <bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_dq_mean(QuantDesc single, TileMap<QuantDesc> map,
+                                                     const unsigned long long* __restrict__ bins)
 {
-    __shared__ uint2 s_lut[k4LutN];
-    __shared__ uint32_t s_red[4];
-    const uint2* glut = reinterpret_cast<const uint2*>(code4 == 0 ? tab->nf4_lut : tab->fp4_lut);
-    quant4_tile<B, XDT, QM_PLAIN>(blockIdx.x, x, n, codes, absmax, nullptr, s_red, s_lut, glut, true, threadIdx.x);
-}
-
-template <int B, int XDT>
-__global__ __launch_bounds__(256) void k_quant4_binned(const void* __restrict__ x, int64_t n,
-                                                       uint8_t* __restrict__ codes, float* __restrict__ absmax,
-                                                       const QbTables* __restrict__ tab, int code4,
-                                                       unsigned long long* __restrict__ bins, int64_t ntiles)
-{
-    __shared__ uint2 s_lut[k4LutN];
-    __shared__ uint32_t s_red[2][4];
-    __shared__ unsigned long long s_bins[256];
-    const int tid = threadIdx.x;
-    const uint2* glut = reinterpret_cast<const uint2*>(code4 == 0 ? tab->nf4_lut : tab->fp4_lut);
-    if (tid < k4LutN) s_lut[tid] = glut[tid];
-    s_bins[tid] = 0ull;
-    __syncthreads();
-    int par = 0;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x, par ^= 1)
-        quant4_tile<B, XDT, QM_DQ_FIRST>(tile, x, n, codes, absmax, s_bins, s_red[par], s_lut, glut, false, tid);
-    __syncthreads();
-    if (tid < 254 && s_bins[tid]) atomicAdd(&bins[(blockIdx.x % kBinCopies) * 256 + tid], s_bins[tid]);
+    const int ti = MULTI ? (int)blockIdx.x : 0;
+    const QuantDesc d = MULTI ? map.descs[ti] : single;
+    const float mu = exact_mean_wg(bins + (size_t)ti * kBinWords, (uint32_t)d.n, threadIdx.x);
+    if (threadIdx.x == 0) gst<float>(d.offset, mu);
 }
 
 // ---------------------------------------------------------------------------
@@ -431,90 +379,66 @@ __global__ __launch_bounds__(256) void k_quant4_binned(const void* __restrict__ 
 
 namespace {
 
-template <int B, int XDT>
-hipError_t quant8_as(int mode, const void* x, int64_t n, uint8_t* codes, float* absmax, const QbTables* tab,
-                     unsigned long long* bins, float* offset, hipStream_t s)
+template <int BITS, int B, int XDT, bool SECOND>
+hipError_t quant_as(const QuantDesc& single, const TileMap<QuantDesc>* map, int64_t ntiles,
+                    unsigned long long* bins, const QbTables* tab, int code4, hipStream_t s)
 {
-    const int64_t ntiles = (n + Tile8<B>::ELEMS - 1) / Tile8<B>::ELEMS;
-    if (mode == QM_DQ_FIRST) {
-        auto kern = k_quant8_binned<B, XDT>;
-        return launch_kernel(kern, persistent_grid(kern, ntiles), s, x, n, codes, absmax, tab, bins, ntiles);
-    }
-    if (mode == QM_DQ_SECOND) {
-        auto kern = k_quant8<B, XDT, QM_DQ_SECOND>;
-        return launch_kernel(kern, (int)ntiles, s, x, n, codes, absmax, tab, bins, offset);
-    }
-    auto kern = k_quant8<B, XDT, QM_PLAIN>;
-    return launch_kernel(kern, (int)ntiles, s, x, n, codes, absmax, tab, bins, offset);
+    if (map)
+        return launch_kernel(k_quant<BITS, B, XDT, SECOND, true>, (int)ntiles, s, single, *map, bins, tab, code4);
+    return launch_kernel(k_quant<BITS, B, XDT, SECOND, false>, (int)ntiles, s, single, TileMap<QuantDesc>{}, bins,
+                         tab, code4);
 }
 
-template <int B>
-hipError_t quant8_dt(int mode, int xdt, const void* x, int64_t n, uint8_t* codes, float* absmax, const QbTables* tab,
-                     unsigned long long* bins, float* offset, hipStream_t s)
+template <int BITS, int B>
+hipError_t quant_x(int xdt, bool second, const QuantDesc& single, const TileMap<QuantDesc>* map, int64_t ntiles,
+                   unsigned long long* bins, const QbTables* tab, int code4, hipStream_t s)
 {
+    if (second) {
+        if constexpr (BITS == 8) return quant_as<8, B, DT_F32, true>(single, map, ntiles, nullptr, tab, 0, s);
+        return hipErrorInvalidValue;
+    }
     switch (xdt) {
-    case DT_F32: return quant8_as<B, DT_F32>(mode, x, n, codes, absmax, tab, bins, offset, s);
-    case DT_F16: return quant8_as<B, DT_F16>(mode, x, n, codes, absmax, tab, bins, offset, s);
-    case DT_BF16: return quant8_as<B, DT_BF16>(mode, x, n, codes, absmax, tab, bins, offset, s);
+    case DT_F32: return quant_as<BITS, B, DT_F32, false>(single, map, ntiles, bins, tab, code4, s);
+    case DT_F16: return quant_as<BITS, B, DT_F16, false>(single, map, ntiles, bins, tab, code4, s);
+    case DT_BF16: return quant_as<BITS, B, DT_BF16, false>(single, map, ntiles, bins, tab, code4, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int B, int XDT>
-hipError_t quant4_as(int mode, const void* x, int64_t n, int code4, uint8_t* codes, float* absmax,
-                     const QbTables* tab, unsigned long long* bins, hipStream_t s)
+template <int BITS>
+hipError_t quant_b(int B, int xdt, bool second, const QuantDesc& single, const TileMap<QuantDesc>* map,
+                   int64_t ntiles, unsigned long long* bins, const QbTables* tab, int code4, hipStream_t s)
 {
-    const int64_t ntiles = (n + Tile4<B>::ELEMS - 1) / Tile4<B>::ELEMS;
-    if (mode == QM_DQ_FIRST) {
-        auto kern = k_quant4_binned<B, XDT>;
-        return launch_kernel(kern, persistent_grid(kern, ntiles), s, x, n, codes, absmax, tab, code4, bins, ntiles);
-    }
-    auto kern = k_quant4<B, XDT>;
-    return launch_kernel(kern, (int)ntiles, s, x, n, codes, absmax, tab, code4);
-}
-
-template <int B>
-hipError_t quant4_dt(int mode, int xdt, const void* x, int64_t n, int code4, uint8_t* codes, float* absmax,
-                     const QbTables* tab, unsigned long long* bins, hipStream_t s)
-{
-    switch (xdt) {
-    case DT_F32: return quant4_as<B, DT_F32>(mode, x, n, code4, codes, absmax, tab, bins, s);
-    case DT_F16: return quant4_as<B, DT_F16>(mode, x, n, code4, codes, absmax, tab, bins, s);
-    case DT_BF16: return quant4_as<B, DT_BF16>(mode, x, n, code4, codes, absmax, tab, bins, s);
+    switch (B) {
+    case 64: return quant_x<BITS, 64>(xdt, second, single, map, ntiles, bins, tab, code4, s);
+    case 128: return quant_x<BITS, 128>(xdt, second, single, map, ntiles, bins, tab, code4, s);
+    case 256: return quant_x<BITS, 256>(xdt, second, single, map, ntiles, bins, tab, code4, s);
+    case 512: return quant_x<BITS, 512>(xdt, second, single, map, ntiles, bins, tab, code4, s);
+    case 1024: return quant_x<BITS, 1024>(xdt, second, single, map, ntiles, bins, tab, code4, s);
+    case 2048: return quant_x<BITS, 2048>(xdt, second, single, map, ntiles, bins, tab, code4, s);
+    case 4096: return quant_x<BITS, 4096>(xdt, second, single, map, ntiles, bins, tab, code4, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-#define QB_SWITCH_B(B, CALL)                           \
-    switch (B) {                                       \
-    case 64: { constexpr int kB = 64; return CALL; }     \
-    case 128: { constexpr int kB = 128; return CALL; }   \
-    case 256: { constexpr int kB = 256; return CALL; }   \
-    case 512: { constexpr int kB = 512; return CALL; }   \
-    case 1024: { constexpr int kB = 1024; return CALL; } \
-    case 2048: { constexpr int kB = 2048; return CALL; } \
-    case 4096: { constexpr int kB = 4096; return CALL; } \
-    default: return hipErrorInvalidValue;              \
-    }
-
-hipError_t launch_quant8(const void* x, int xdt, int64_t n, int B, uint8_t* codes, float* absmax, int mode,
-                         unsigned long long* bins, float* offset, hipStream_t s)
+hipError_t launch_quant(const QuantDesc& single, const TileMap<QuantDesc>* map, int64_t ntiles, int bits, int code4,
+                        int B, int xdt, bool second, unsigned long long* bins, hipStream_t s)
 {
     const QbTables* tab = device_tables();
     if (!tab) return hipErrorNotInitialized;
-    if (mode == QM_DQ_SECOND) xdt = DT_F32;     // the second level reads the fp32 absmax
-    QB_SWITCH_B(B, quant8_dt<kB>(mode, xdt, x, n, codes, absmax, tab, bins, offset, s));
+    if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if (bits == 8) return quant_b<8>(B, xdt, second, single, map, ntiles, bins, tab, code4, s);
+    if (bits == 4 && !second) return quant_b<4>(B, xdt, false, single, map, ntiles, bins, tab, code4, s);
+    return hipErrorInvalidValue;
 }
 
-hipError_t launch_quant4(const void* x, int xdt, int64_t n, int B, int code4, uint8_t* codes, float* absmax,
-                         int mode, unsigned long long* bins, hipStream_t s)
+hipError_t launch_dq_mean(const QuantDesc& single, const TileMap<QuantDesc>* map, int count,
+                          const unsigned long long* bins, hipStream_t s)
 {
-    const QbTables* tab = device_tables();
-    if (!tab) return hipErrorNotInitialized;
-    if (mode != QM_PLAIN && mode != QM_DQ_FIRST) return hipErrorInvalidValue;
-    QB_SWITCH_B(B, quant4_dt<kB>(mode, xdt, x, n, code4, codes, absmax, tab, bins, s));
+    if (map) return launch_kernel(k_dq_mean<true>, count, s, single, *map, bins);
+    return launch_kernel(k_dq_mean<false>, 1, s, single, TileMap<QuantDesc>{}, bins);
 }
 
 }  // namespace qb

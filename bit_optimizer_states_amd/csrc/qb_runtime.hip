@@ -47,15 +47,16 @@ int persistent_grid_cap(const void* kernel, int (*query)(const void*))
     return cap;
 }
 
-__global__ __launch_bounds__(256) void k_clear_bins(unsigned long long* __restrict__ bins)
+__global__ __launch_bounds__(256) void k_clear_bins(unsigned long long* __restrict__ bins, int64_t nwords)
 {
-#pragma unroll
-    for (int k = 0; k < kBinCopies; ++k) bins[k * 256 + threadIdx.x] = 0ull;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * 256) bins[i] = 0ull;
 }
 
-hipError_t launch_clear_bins(unsigned long long* bins, hipStream_t s)
+hipError_t launch_clear_bins(unsigned long long* bins, int sets, hipStream_t s)
 {
-    return launch_kernel(k_clear_bins, 1, s, bins);
+    const int64_t nwords = (int64_t)sets * (int64_t)kBinWords;
+    const int64_t grid = (nwords + 1023) / 1024;
+    return launch_kernel(k_clear_bins, (int)(grid < 1024 ? grid : 1024), s, bins, nwords);
 }
 
 }  // namespace qb

@@ -111,6 +111,21 @@ typedef struct {
 } qb_tensor;
 
 /*
+ * One tensor of a grouped quantization; the fields are those of qb_quantize.
+ * A plain tensor gives absmax and leaves c2, absmax2, offset NULL; a nested
+ * one gives c2, absmax2, offset (the outputs of qb_dq) and absmax NULL.
+ */
+typedef struct {
+    const void* x;
+    uint8_t*    codes;
+    float*      absmax;
+    uint8_t*    c2;
+    float*      absmax2;
+    float*      offset;
+    int64_t     n;
+} qb_quant_tensor;
+
+/*
  * One tensor of a grouped dequantization; the fields are those of
  * qb_dequantize.  A plain tensor gives absmax and leaves c2, absmax2, offset
  * NULL; a nested one gives c2, absmax2, offset (the qb_dq fields) and absmax
@@ -135,11 +150,35 @@ typedef struct {
  *   absmax  [ceil(n/blocksize)] fp32 block absmax out; must be NULL when dq is given.
  *   dq      NULL, or the nested state to fill (codes, absmax2, offset; the
  *           workspace holds the fp32 absmax while the call runs).
- * Outputs are fully overwritten.  Four kernels at most (with dq: clear the
- * workspace counters, quantize, nested quantize), all on `stream`.
+ * Outputs are fully overwritten.  One kernel, or four with dq (clear the
+ * workspace's exponent bins, quantize, exact mean of the absmax, quantize
+ * absmax - mean), all on `stream`.
  */
 qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int32_t blocksize,
                       uint8_t* codes, float* absmax, const qb_dq* dq, void* stream);
+
+/*
+ * qb_multi_tensor_quantize -- qb_quantize on `count` tensors (same input
+ * dtype, code, block size and nested block size for all) in one kernel launch,
+ * or four with nesting; the result equals a loop of single-tensor calls, bit
+ * for bit.  Quantizing all weights of a model at load time (page
+ * "Bitsandbytes", sections Normal Float 4 (NF4) and İç içe nicelleştirme) this
+ * way avoids one launch ramp per tensor.
+ *   tensors     host array of `count` descriptors (read during the call only);
+ *               either every tensor is nested or none (else QB_EUNSUPPORTED).
+ *   blocksize2  block size of the nested level (ignored without nesting).
+ *   ws          device workspace of
+ *               qb_multi_tensor_quantize_workspace_bytes(tensors, count,
+ *               blocksize) bytes: tables of the tensors, copied in on
+ *               `stream`, and with nesting the exponent bins and the fp32
+ *               absmax of every tensor (4 bytes per block) while the call runs.
+ * Tensors with n == 0 are skipped.  count == 0 is a no-op.
+ */
+qb_status qb_multi_tensor_quantize(const qb_quant_tensor* tensors, int32_t count, qb_dtype xdt, qb_code code,
+                                   int32_t blocksize, int32_t blocksize2, void* ws, size_t ws_bytes,
+                                   void* stream);
+size_t qb_multi_tensor_quantize_workspace_bytes(const qb_quant_tensor* tensors, int32_t count,
+                                                int32_t blocksize);
 
 /*
  * qb_dequantize -- y_i = ydt(table[c_i] * s_b), one fp32 multiply then a

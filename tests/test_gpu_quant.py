@@ -11,6 +11,7 @@ from gpu_helpers import DEV, TORCH_DT, decorate, gpu_dequantize, gpu_quantize, h
 pytestmark = pytest.mark.gpu
 
 CODES = [oracle.DYN8, oracle.NF4, oracle.FP4]
+QB_DT = {oracle.F32: 0, oracle.F16: 1, oracle.BF16: 2}
 BLOCKS = [64, 128, 256, 512, 1024, 2048, 4096]
 
 
@@ -193,3 +194,88 @@ def test_multi_tensor_dequantize_rejects_mixed_nesting():
     with pytest.raises(L.QbError) as e:
         L.qb_multi_tensor_dequantize(table, 2, L.QB_DYN8, 64, 256, L.QB_BF16, ws)
     assert e.value.status == L.QB_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("code", CODES)
+@pytest.mark.parametrize("nested", [False, True])
+@pytest.mark.parametrize("B,dt", [(64, oracle.F16), (4096, oracle.F32), (256, oracle.BF16)])
+def test_multi_tensor_quantize_equals_oracle(code, nested, B, dt):
+    """One grouped call over many tensors (ragged, tiny, empty, several tiles)
+    gives every tensor's codes, absmax or nested state exactly as the oracle;
+    bytes past each output stay untouched."""
+    from gpu_helpers import qb
+    L = qb()
+    rng = np.random.default_rng(500 + 10 * code + B + nested + 3 * dt)
+    sizes = [8192 * 3 + 77, 1, 0, 65, 8192, 64 * 256 * 3 + 5, 2, 4097, 0, 8191] + \
+        [int(v) for v in rng.integers(1, 30000, 30)]
+    bufs, entries, xs = [], [], []
+    for i, n in enumerate(sizes):
+        xh, _ = make_input(max(n, 1), B, dt, seed=7000 + i)
+        xh = xh[:n]
+        xs.append(xh)
+        nb = (n + B - 1) // B
+        xd = dev(xh if n else np.zeros(1, xh.dtype), dt)
+        codes = torch.full((packed_len(code, n) + 16,), 0xAB, dtype=torch.uint8, device=DEV)
+        if nested:
+            c2 = torch.full((nb + 16,), 0xAB, dtype=torch.uint8, device=DEV)
+            a2 = torch.full(((nb + 255) // 256 + 4,), -7.0, dtype=torch.float32, device=DEV)
+            off = torch.full((4,), -7.0, dtype=torch.float32, device=DEV)
+            dq = L.make_dq(c2, a2, off, 256)
+            bufs.append((xd, codes, c2, a2, off))
+            entries.append((xd, n, codes, None, dq))
+        else:
+            am = torch.full((nb + 4,), -7.0, dtype=torch.float32, device=DEV)
+            bufs.append((xd, codes, am))
+            entries.append((xd, n, codes, am, None))
+    table = L.quant_table(entries)
+    wsb = L.qb_multi_tensor_quantize_workspace_bytes(table, len(sizes), B)
+    ws = torch.full((wsb,), 0xCD, dtype=torch.uint8, device=DEV)
+    L.qb_multi_tensor_quantize(table, len(sizes), QB_DT[dt], code, B, 256, ws)
+    torch.cuda.synchronize()
+    for n, xh, b in zip(sizes, xs, bufs):
+        nb = (n + B - 1) // B
+        got_c = b[1].cpu().numpy()
+        pl = packed_len(code, n)
+        assert np.all(got_c[pl:] == 0xAB), f"tensor of {n}: codes written past the end"
+        if not n:
+            continue
+        want_c, want_a = oracle.quantize_blockwise(xh, code, B, dt)
+        assert np.array_equal(got_c[:pl], want_c), f"tensor of {n}: codes differ"
+        if nested:
+            c2, a2, mu = oracle.dq_quantize(want_a, 256)
+            got_c2, got_a2, got_off = b[2].cpu().numpy(), b[3].cpu().numpy(), b[4].cpu().numpy()
+            assert np.float32(got_off[0]).view(np.uint32) == np.float32(mu).view(np.uint32), f"mean of {n}"
+            assert np.array_equal(got_c2[:nb], c2) and np.all(got_c2[nb:] == 0xAB)
+            k2 = (nb + 255) // 256
+            assert np.array_equal(got_a2[:k2].view(np.uint32), a2.view(np.uint32)) and np.all(got_a2[k2:] == -7.0)
+        else:
+            got_a = b[2].cpu().numpy()
+            assert np.array_equal(got_a[:nb].view(np.uint32), want_a.view(np.uint32)) and np.all(got_a[nb:] == -7.0)
+
+
+def test_multi_tensor_quantize_twice_reuses_workspace():
+    """A second grouped nested call on the same (dirty) workspace gives the same
+    result: the exponent bins are cleared by every call."""
+    from gpu_helpers import qb
+    L = qb()
+    sizes = [64 * 1000 + 3, 8192 * 5, 777]
+    xs = [dev(make_input(n, 64, oracle.F16, seed=40 + n)[0], oracle.F16) for n in sizes]
+    outs = []
+    for rep in range(2):
+        entries, keep = [], []
+        for x, n in zip(xs, sizes):
+            nb = (n + 63) // 64
+            codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=DEV)
+            c2 = torch.empty(nb, dtype=torch.uint8, device=DEV)
+            a2 = torch.empty((nb + 255) // 256, dtype=torch.float32, device=DEV)
+            off = torch.empty(4, dtype=torch.float32, device=DEV)
+            keep.append((codes, c2, a2, off))
+            entries.append((x, n, codes, None, L.make_dq(c2, a2, off, 256)))
+        table = L.quant_table(entries)
+        if rep == 0:
+            ws = torch.empty(L.qb_multi_tensor_quantize_workspace_bytes(table, len(sizes), 64), dtype=torch.uint8,
+                             device=DEV)
+        L.qb_multi_tensor_quantize(table, len(sizes), L.QB_F16, L.QB_NF4, 64, 256, ws)
+        torch.cuda.synchronize()
+        outs.append([tuple(t.cpu().numpy().tobytes() for t in k) for k in keep])
+    assert outs[0] == outs[1]

@@ -170,6 +170,38 @@ def test_grouped_dequantize_arguments_rejected_before_launch(qb):
     assert f(tab(neg), 1, 0, 64, 256, 2, A, ws, None) == qb.QB_EINVAL
 
 
+def test_grouped_quantize_arguments_rejected_before_launch(qb):
+    L = qb.lib()
+    A = 0x100000
+    plain = qb.qb_quant_tensor(A, A, A, None, None, None, 1000)
+    nested = qb.qb_quant_tensor(A, A, None, A, A, A, 1000)
+    tab = lambda *e: (qb.qb_quant_tensor * len(e))(*e)
+    wsz = L.qb_multi_tensor_quantize_workspace_bytes
+    # workspace: tables only without nesting; with nesting two table regions,
+    # 16 KiB of bins per tensor and the fp32 absmax (256-byte rounded)
+    region = -(-(2 * 64 + 3 * 8 + (2 * 2 + 64 + 1) * 4) // 256) * 256
+    assert wsz(tab(plain, plain), 2, 64) == region
+    assert wsz(tab(nested, nested), 2, 64) == 2 * region + 2 * 16384 + 2 * (-(-16 * 4 // 256) * 256)
+    assert wsz(tab(plain), 1, 100) == 0
+    ws = wsz(tab(nested, nested), 2, 64)
+    f = L.qb_multi_tensor_quantize
+    assert f(tab(plain), -1, 0, 0, 64, 256, A, ws, None) == qb.QB_EINVAL               # count < 0
+    assert f(tab(plain), 0, 0, 0, 64, 256, A, 0, None) == qb.QB_OK                     # count == 0: no-op
+    assert f(tab(nested), 1, 0, 0, 64, 256, A, 100, None) == qb.QB_EWORKSPACE
+    assert f(tab(plain), 1, 0, 0, 64, 256, A + 8, ws, None) == qb.QB_EALIGN
+    assert f(tab(plain), 1, 0, 0, 100, 256, A, ws, None) == qb.QB_EINVAL              # blocksize
+    assert f(tab(plain), 1, 0, 7, 64, 256, A, ws, None) == qb.QB_EINVAL               # code
+    assert f(tab(plain), 1, 5, 0, 64, 256, A, ws, None) == qb.QB_EINVAL               # dtype
+    assert f(tab(plain, nested), 2, 0, 0, 64, 256, A, ws, None) == qb.QB_EUNSUPPORTED  # mixed nesting
+    both = qb.qb_quant_tensor(A, A, A, A, A, A, 1000)
+    assert f(tab(both), 1, 0, 0, 64, 256, A, ws, None) == qb.QB_EINVAL                # absmax and nested state
+    assert f(tab(nested), 1, 0, 0, 64, 100, A, ws, None) == qb.QB_EINVAL              # blocksize2
+    bad = qb.qb_quant_tensor(A + 4, A, A, None, None, None, 1000)
+    assert f(tab(bad), 1, 0, 0, 64, 256, A, ws, None) == qb.QB_EALIGN                 # misaligned input
+    neg = qb.qb_quant_tensor(A, A, A, None, None, None, -1)
+    assert f(tab(neg), 1, 0, 0, 64, 256, A, ws, None) == qb.QB_EINVAL
+
+
 def test_status_strings(qb):
     assert qb.qb_status_string(0) == "ok"
     assert "workspace" in qb.qb_status_string(5)
