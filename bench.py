@@ -11,7 +11,9 @@ One step = one pass of the whole hot path over synthetic inputs resident in HBM:
      matrices of the same decoder (6,607,077,376 weights ~N(0, 0.02)), in one
      grouped call (qb_multi_tensor_quantize: four launches);
   3. dequantization of those 225 NF4 tensors to bf16 in one grouped launch
-     (qb_multi_tensor_dequantize).
+     (qb_multi_tensor_dequantize);
+  4. a dynamic 8-bit round trip (quantize, then dequantize to fp32; block 2048)
+     of 268,435,456 fp32 values ~0.02 * Student-t(3).
 Two gradient sets alternate between steps (generated before timing).  After
 the timed steps the two 4-bit sweeps are also timed with one qb_quantize /
 qb_dequantize call per tensor (reported under "components", not in `value`).
@@ -38,6 +40,7 @@ METRIC = "fused AdamW8bit step GB/s + params/s; 4-bit dequant GB/s (% of HBM pea
 HBM_PEAK_GBS = 8000.0
 ADAM_BLOCK = 2048
 W4_BLOCK, W4_BLOCK2 = 64, 256
+Q8_N, Q8_BLOCK = 268_435_456, 2048
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_adamw8_multi.llama7b_step.traffic.json")
 
@@ -54,6 +57,11 @@ def adam_bytes_per_param(grad_bytes=2, block=ADAM_BLOCK):
 def w4_bytes_per_weight():
     # dequantize: packed codes (0.5), nested codes (1/64), second absmax (4/(64*256)), bf16 out (2)
     return 0.5 + 1.0 / W4_BLOCK + 4.0 / (W4_BLOCK * W4_BLOCK2) + 2.0
+
+
+def q8_bytes_per_elem(block=Q8_BLOCK):
+    # quantize: fp32 in (4), code out (1), absmax out; dequantize: code and absmax in, fp32 out (4)
+    return 5.0 + 4.0 / block
 
 
 def q4_bytes_per_weight():
@@ -141,6 +149,12 @@ class Model7B:
                                              for (n, _, codes, _, _, _, y), dq in zip(self.w4, self.dq_d)])
             self.d_ws = torch.empty(qb.qb_multi_tensor_workspace_bytes(len(self.w4)), dtype=torch.uint8, device=dev)
         self.n_w4 = sum(e[0] for e in self.w4)
+        self.q8 = None
+        if with_w4:
+            log(f"allocating the {Q8_N:,}-value fp32 tensor for the 8-bit round trip")
+            x = inputs.student_t3(Q8_N, 0.02, seed=seed * 31 + 2, device=dev)
+            self.q8 = (x, torch.empty(Q8_N, dtype=torch.uint8, device=dev),
+                       torch.empty(Q8_N // Q8_BLOCK, dtype=torch.float32, device=dev), torch.empty_like(x))
 
 
 def run_adam(qb, model, step):
@@ -155,6 +169,12 @@ def run_q4(qb, model):
 def run_dq4(qb, model):
     qb.qb_multi_tensor_dequantize(model.d_table, len(model.w4), qb.QB_NF4, W4_BLOCK, W4_BLOCK2, qb.QB_BF16,
                                   model.d_ws)
+
+
+def run_q8(qb, model):
+    x, codes, absmax, y = model.q8
+    qb.qb_quantize(x, Q8_N, qb.QB_DYN8, Q8_BLOCK, codes, absmax)
+    qb.qb_dequantize(codes, absmax, None, qb.QB_DYN8, Q8_BLOCK, Q8_N, y)
 
 
 def run_q4_per_tensor(qb, model):
@@ -182,8 +202,9 @@ def time_calls(torch, fn, reps=5):
 
 def cpu_baseline(torch, model, seconds_target, rng):
     """The oracle, single-threaded, on a bounded sample of the same workload:
-    seeded full AdamW blocks of the 7B model (copied from the device) plus one
-    4096x11008 weight quantized (NF4 + nested) and dequantized to bf16."""
+    seeded full AdamW blocks of the 7B model (copied from the device), one
+    4096x11008 weight quantized (NF4 + nested) and dequantized to bf16, and the
+    8-bit round trip of the first 2^23 values of the Student-t tensor."""
     import oracle
     nblocks = 98304
     # sample full blocks in proportion to the tensors' block counts
@@ -218,8 +239,15 @@ def cpu_baseline(torch, model, seconds_target, rng):
     t0 = time.perf_counter()
     oracle.dequantize(codes, st, oracle.NF4, W4_BLOCK, n4, oracle.BF16)
     t_d4 = time.perf_counter() - t0
-    total_bytes = n_adam * adam_bytes_per_param() + n4 * (q4_bytes_per_weight() + w4_bytes_per_weight())
-    total_t = t_adam + t_q4 + t_d4
+    n8 = 1 << 23
+    x8 = model.q8[0][:n8].cpu().numpy()
+    t0 = time.perf_counter()
+    c8, a8 = oracle.quantize_blockwise(x8, oracle.DYN8, Q8_BLOCK)
+    oracle.dequantize_blockwise(c8, a8, oracle.DYN8, Q8_BLOCK, n8, oracle.F32)
+    t_q8 = time.perf_counter() - t0
+    total_bytes = (n_adam * adam_bytes_per_param() + n4 * (q4_bytes_per_weight() + w4_bytes_per_weight()) +
+                   n8 * 2 * q8_bytes_per_elem())
+    total_t = t_adam + t_q4 + t_d4 + t_q8
     return {
         "value": total_bytes / total_t / 1e9,
         "unit": "GB/s",
@@ -227,7 +255,8 @@ def cpu_baseline(torch, model, seconds_target, rng):
         "kind": "oracle",
         "sample": (f"{nblocks} seeded full 2048-element AdamW blocks of the 7B model ({n_adam:,} params, "
                    f"{t_adam:.2f} s) + NF4 nested quantize ({t_q4:.2f} s) and bf16 dequantize ({t_d4:.2f} s) "
-                   f"of one 4096x11008 fp16 weight; single-threaded C oracle"),
+                   f"of one 4096x11008 fp16 weight + dynamic 8-bit round trip of the first {n8:,} fp32 values "
+                   f"({t_q8:.2f} s); single-threaded C oracle"),
         "adamw_params_per_s": n_adam / t_adam,
         "dequant4_GBps": n4 * w4_bytes_per_weight() / t_d4 / 1e9,
         "host_cpus": os.cpu_count(),
@@ -329,12 +358,15 @@ def main():
             run_dq4(qb, model)
             if ev is not None:
                 ev[3].record()
+            run_q8(qb, model)
+            if ev is not None:
+                ev[4].record()
 
     for k in range(1, args.warmup + 1):
         step(k)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -360,7 +392,13 @@ def main():
         comps["dequant4_nf4_nested_bf16"] = {"ms": d4_ms, "GB/s": d4_bytes / d4_ms / 1e6,
                                              "frac_of_hbm_peak": d4_bytes / d4_ms / 1e6 / HBM_PEAK_GBS,
                                              "launches_per_step": 1, "call": "qb_multi_tensor_dequantize"}
-        step_bytes += q4_bytes + d4_bytes
+        q8_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
+        q8_bytes = Q8_N * 2 * q8_bytes_per_elem()
+        comps["roundtrip8_dyn8_fp32"] = {"ms": q8_ms, "GB/s": q8_bytes / q8_ms / 1e6,
+                                         "frac_of_hbm_peak": q8_bytes / q8_ms / 1e6 / HBM_PEAK_GBS,
+                                         "elements_per_s": Q8_N / q8_ms * 1e3, "launches_per_step": 2,
+                                         "call": "qb_quantize + qb_dequantize"}
+        step_bytes += q4_bytes + d4_bytes + q8_bytes
     ms_per_step = wall / args.steps * 1e3
     if not args.adam_only:
         # the same sweeps with one qb_quantize / qb_dequantize call per tensor (outside the timed step)
@@ -392,7 +430,8 @@ def main():
                          "rows): one multi-tensor fused AdamW8bit step, block 2048" +
                          ("" if args.adam_only else
                           "; + NF4 nested quantize and bf16 dequantize of its 225 fp16 weights "
-                          "(6,607,077,376), block 64 / 256")),
+                          "(6,607,077,376), block 64 / 256; + dynamic 8-bit quantize and fp32 dequantize of "
+                          "268,435,456 Student-t(3) values, block 2048")),
             "params": model.n_params,
             "weights_4bit": model.n_w4,
             "adam_blocksize": ADAM_BLOCK,

@@ -22,21 +22,22 @@ namespace qb {
 // Threads per workgroup of the AdamW kernel: a 2048-element block takes one
 // workgroup of kAdamThreads threads, i.e. 2048 / kAdamThreads elements per
 // thread; more elements per thread spread the per-block fixed work (tensor
-// lookup, table staging, block reduction, reciprocals) thinner.
+// lookup, table staging, block reduction, reciprocals) thinner.  Measured on
+// MI355X in one process on the 7B step: 128 and 512 threads are 3-5% slower.
 #ifndef QB_ADAM_THREADS
 #define QB_ADAM_THREADS 256
 #endif
 constexpr int kAdamThreads = QB_ADAM_THREADS;
 
-// XCD-contiguous tile order (tile_of): measured on MI355X no worse than the
-// plain order, within noise up to 0.5% better.
+// XCD-contiguous tile order (tile_of): measured on MI355X in one process (the
+// same buffers), 4-6% faster than the plain order on the 7B step.
 #ifndef QB_TILE_REMAP
 #define QB_TILE_REMAP 1
 #endif
 
 // Elements a thread takes per access: 4 (chunks spread over the block) or 8
 // (each thread owns 8 consecutive elements: wider gradient and code accesses).
-// Measured on MI355X (flat 1.5e9 parameters): 3.54 ms with 4, 3.87 ms with 8.
+// Measured on MI355X: 8 is 7-9% slower (flat 1.5e9 parameters and 7B step).
 #ifndef QB_ADAM_CHUNK
 #define QB_ADAM_CHUNK 4
 #endif

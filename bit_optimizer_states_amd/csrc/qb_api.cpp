@@ -393,7 +393,8 @@ qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* 
                                 dq ? dq->offset : nullptr, dq ? dq->blocksize2 : 0, n, y, blocksize, &mode, &d);
     if (st != QB_OK) return st;
     if (!device_tables()) return QB_EINIT;
-    return hip_status(launch_dequant(d, nullptr, dequant_tiles(n, kDequantTile), is4(code) ? 4 : 8,
+    const int bits = is4(code) ? 4 : 8;
+    return hip_status(launch_dequant(d, nullptr, dequant_tiles(n, dequant_tile_elems(bits, false)), bits,
                                      is4(code) ? code4_index(code) : 0, blocksize, dq ? dq->blocksize2 : 256,
                                      dq != nullptr, (int)ydt, static_cast<hipStream_t>(stream)));
 }
@@ -420,7 +421,7 @@ qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t c
         if (t.n == 0) continue;
         d.tile_begin = tiles;
         table.push_back(d);
-        tiles += dequant_tiles(t.n, kDequantTileMulti);
+        tiles += dequant_tiles(t.n, dequant_tile_elems(is4(code) ? 4 : 8, true));
     }
     if (table.empty()) return QB_OK;
     if (tiles >= (int64_t(1) << 31)) return QB_EINVAL;

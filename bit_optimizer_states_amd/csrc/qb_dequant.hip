@@ -8,11 +8,12 @@
 // decoded first, a_b = dyn8[c2_b] * absmax2[b / B2] + mean, two rounded binary32
 // operations ("Bitsandbytes", section İç içe nicelleştirme).
 //
-// Kernel shape: one 256-thread workgroup per tile of 256 x 8 x U elements
-// (U = 4: 8192; measured on MI355X, 2 and 8 are slower), in tile order.  A
-// thread takes U units of 8 consecutive elements (one u32 of 4-bit codes or
-// two of 8-bit codes), consecutive lanes on consecutive units, so every load
-// and store instruction of a wave covers one contiguous span.
+// Kernel shape: one 256-thread workgroup per tile of 8192 elements for 4-bit
+// codes and 4096 for 8-bit codes (the best measured on MI355X), in tile
+// order.  A thread takes units
+// of E consecutive elements, E = 16 bytes of output (8 for 16-bit outputs, 4
+// for fp32), consecutive lanes on consecutive units, so every load and store
+// instruction of a wave covers one contiguous span.
 // At the start a workgroup issues the loads of its codes and of the scale
 // inputs of its tile's blocks (one block per thread, at most 128 blocks per
 // tile since B >= 64), then stages the code tables in LDS; the blocks' scales
@@ -41,22 +42,28 @@ namespace {
 #endif
 
 constexpr int kDqThreads = 256;
-static_assert(kDequantTile / 64 <= kDqThreads && kDequantTileMulti / 64 <= kDqThreads,
+static_assert(dequant_tile_elems(4, false) / 64 <= kDqThreads && dequant_tile_elems(4, true) / 64 <= kDqThreads &&
+                  dequant_tile_elems(8, false) / 64 <= kDqThreads,
               "one thread per block of a tile");
 
-// The 8 codes of the unit at element offset e (a multiple of 8) from base.
-template <int BITS>
+// The E codes of the unit at element offset e (a multiple of E) from base:
+// E * BITS / 8 bytes (2, 4 or 8).
+template <int BITS, int E>
 __device__ __forceinline__ u32x2 load_unit(const uint8_t* base, uint32_t e)
 {
-    if constexpr (BITS == 8) {
+    constexpr int bytes = E * BITS / 8;
+    if constexpr (bytes == 8) {
         return gldo<u32x2>(base, e);
+    } else if constexpr (bytes == 4) {
+        u32x2 w = {gldo<uint32_t>(base, e * BITS / 8), 0u};
+        return w;
     } else {
-        u32x2 w = {gldo<uint32_t>(base, e / 2), 0u};
+        u32x2 w = {(uint32_t)gldo<uint16_t>(base, e * BITS / 8), 0u};
         return w;
     }
 }
 
-// Code of element j (0..7) of a unit.
+// Code of element j (0 .. E-1) of a unit.
 template <int BITS>
 __device__ __forceinline__ uint32_t unit_code(const u32x2& w, int j)
 {
@@ -87,8 +94,10 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
 {
     __shared__ float s_val[BITS == 8 ? 256 : 16];   // decode table of the codes
     __shared__ float s_dyn[DQ && BITS == 4 && !QB_DQ_DIRECT_DYN ? 256 : 1];
-    constexpr int kDqUnits = MULTI ? QB_DQ_MULTI_UNITS : QB_DQ_UNITS;   // units of 8 elements per thread
-    constexpr int kDqElems = kDqThreads * kDqUnits * 8;
+    // a unit is E elements whose output a lane writes with one 16-byte store
+    constexpr int E = YDT == DT_F32 ? 4 : 8;
+    constexpr int kDqElems = (int)dequant_tile_elems(BITS, MULTI);
+    constexpr int kDqUnits = kDqElems / (kDqThreads * E);                // units per thread
     __shared__ float s_scale[kDqElems / 64];                            // blocks per tile at B = 64
     const int tid = threadIdx.x;
     const int64_t tile = tile_of<MULTI && QB_DQ_MULTI_REMAP>(blockIdx.x, gridDim.x);
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
     u32x2 w[kDqUnits];
     if (full) {
 #pragma unroll
-        for (int k = 0; k < kDqUnits; ++k) w[k] = load_unit<BITS>(ct, (uint32_t)(k * kDqThreads + tid) * 8);
+        for (int k = 0; k < kDqUnits; ++k) w[k] = load_unit<BITS, E>(ct, (uint32_t)(k * kDqThreads + tid) * E);
     }
     // scale inputs of the tile's blocks, one block per thread (B and the tile
     // are powers of two: a tile holds whole blocks, or lies within one block)
@@ -154,17 +163,18 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
     if (full) {
 #pragma unroll
         for (int k = 0; k < kDqUnits; ++k) {
-            const uint32_t e = (uint32_t)(k * kDqThreads + tid) * 8;
+            const uint32_t e = (uint32_t)(k * kDqThreads + tid) * E;
             const float s = s_scale[e >> log2B];
-            float o[8];
+            float o[E];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[j] = s_val[unit_code<BITS>(w[k], j)] * s;
-            store8o<YDT>(yt, e, o);
+            for (int j = 0; j < E; ++j) o[j] = s_val[unit_code<BITS>(w[k], j)] * s;
+            if constexpr (E == 4) store4o<YDT>(yt, e, o);
+            else store8o<YDT>(yt, e, o);
         }
     } else {
         for (int k = 0; k < kDqUnits; ++k)
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t e = (uint32_t)(k * kDqThreads + tid) * 8 + j;
+            for (int j = 0; j < E; ++j) {
+                const uint32_t e = (uint32_t)(k * kDqThreads + tid) * E + j;
                 if ((int64_t)e < n - tbase) {
                     const float s = s_scale[e >> log2B];
                     store1<YDT>(yt, e, s_val[elem_code<BITS>(ct, e)] * s);

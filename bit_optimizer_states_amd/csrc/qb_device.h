@@ -255,9 +255,11 @@ __device__ __forceinline__ void store8(void* y, int64_t i, const float* o)
 // ---------------------------------------------------------------------------
 
 // Tile handled by workgroup b of ntiles.  The hardware deals workgroups
-// round-robin to the 8 XCDs; with REMAP each XCD takes one contiguous range of
-// tiles instead of every eighth tile (a bijection of [0, ntiles): XCD x holds
-// q + (x < r) workgroups, q = ntiles / 8, r = ntiles % 8).
+// round-robin to the 8 XCDs (b % 8); with REMAP each XCD takes one contiguous
+// range of tiles instead of every eighth tile (a bijection of [0, ntiles):
+// XCD x holds q + (x < r) workgroups, q = ntiles / 8, r = ntiles % 8).  Each
+// XCD then streams through one region of every array.  Runs of 16 to 1024
+// tiles dealt round-robin measured no better on MI355X.
 template <bool REMAP>
 __device__ __forceinline__ int64_t tile_of(int64_t b, int64_t ntiles)
 {

@@ -150,16 +150,22 @@ hipError_t launch_dq_mean(const QuantDesc& single, const TileMap<QuantDesc>* map
 hipError_t launch_dequant(const DequantDesc& single, const TileMap<DequantDesc>* map, int64_t ntiles, int bits,
                           int code4, int B, int B2, bool dq, int ydt, hipStream_t s);
 
-// Units of 8 elements per thread of the dequantization kernel (256 threads)
-// for one tensor and for a grouped launch, and the elements of their tiles.
-#ifndef QB_DQ_UNITS
-#define QB_DQ_UNITS 4
+// Elements per tile of the dequantization kernel: 4-bit codes for one tensor
+// and for a grouped launch, and 8-bit codes (measured on MI355X: 8192, 8192
+// and 4096 are the best of 4096 / 8192 / 16384).
+#ifndef QB_DQ_TILE
+#define QB_DQ_TILE 8192
 #endif
-#ifndef QB_DQ_MULTI_UNITS
-#define QB_DQ_MULTI_UNITS 4
+#ifndef QB_DQ_MULTI_TILE
+#define QB_DQ_MULTI_TILE 8192
 #endif
-constexpr int64_t kDequantTile = 256 * 8 * QB_DQ_UNITS;
-constexpr int64_t kDequantTileMulti = 256 * 8 * QB_DQ_MULTI_UNITS;
+#ifndef QB_DQ8_TILE
+#define QB_DQ8_TILE 4096
+#endif
+constexpr int64_t dequant_tile_elems(int bits, bool multi)
+{
+    return bits == 8 ? QB_DQ8_TILE : (multi ? QB_DQ_MULTI_TILE : QB_DQ_TILE);
+}
 // map: the device tables of a multi-tensor launch, or nullptr for the one
 // tensor `single`.
 hipError_t launch_adamw8(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B, int gdt,
