@@ -10,7 +10,8 @@ Workloads (seeded, synthetic; shapes of the pages' models):
   * one flat buffer of 1,500,000,000 fp32 parameters, bf16 gradients, fused
     AdamW8bit at block 2048 (ragged last block of 1,792 elements);
   * NF4 / FP4 block-64 quantization with nested quantization (block 256) and a
-    bf16 dequantize of 7B-decoder-shaped fp16 weights;
+    bf16 dequantize of 7B-decoder-shaped fp16 weights, per tensor and with the
+    grouped calls over all 225 tensors;
   * one multi-tensor AdamW8bit launch over the 291 tensors of a 7B decoder
     (6,738,415,616 parameters), with 10%-row-sparse embedding gradients.
 """
@@ -220,3 +221,49 @@ def test_multi_tensor_7b_one_launch():
             np.testing.assert_allclose(host_bits(slc(p, b, n)), s[0], rtol=1e-6, atol=2e-8)
         del grads, table
     assert zero_row_blocks > 0, "the sample must include zero-gradient embedding blocks"
+
+
+def test_grouped_4bit_7b_all_225_tensors():
+    """The grouped NF4 calls the benchmark times, over all 225 7B weight
+    tensors at once: every tensor's nested state (mean, codes, second-level
+    absmax) exactly as the oracle computes it from that tensor's block absmax;
+    sampled blocks of every tensor for the 4-bit codes and the bf16 output."""
+    L = qb()
+    code, B, B2 = oracle.NF4, 64, 256
+    shapes = inputs.llama7b_weight_shapes()
+    rng = np.random.default_rng(77)
+    W = []
+    for j, (name, shape) in enumerate(shapes):
+        n = int(np.prod(shape))
+        nb = (n + B - 1) // B
+        w = inputs.normal(n, 0.02, seed=3331 + j, device=DEV, dtype=torch.float16)
+        W.append((name, n, w, torch.empty((n + 1) // 2, dtype=torch.uint8, device=DEV),
+                  torch.empty(nb, dtype=torch.uint8, device=DEV),
+                  torch.empty((nb + B2 - 1) // B2, dtype=torch.float32, device=DEV),
+                  torch.empty(4, dtype=torch.float32, device=DEV), torch.empty(n, dtype=torch.bfloat16, device=DEV)))
+    dqs = [L.make_dq(c2, a2, off, B2) for (_, _, _, _, c2, a2, off, _) in W]
+    qt = L.quant_table([(w, n, codes, None, dq) for (_, n, w, codes, *_), dq in zip(W, dqs)])
+    qws = torch.empty(L.qb_multi_tensor_quantize_workspace_bytes(qt, len(W), B), dtype=torch.uint8, device=DEV)
+    L.qb_multi_tensor_quantize(qt, len(W), L.QB_F16, code, B, B2, qws)
+    dt = L.dequant_table([(codes, None, dq, n, y) for (_, n, _, codes, _, _, _, y), dq in zip(W, dqs)])
+    dws = torch.empty(L.qb_multi_tensor_workspace_bytes(len(W)), dtype=torch.uint8, device=DEV)
+    L.qb_multi_tensor_dequantize(dt, len(W), code, B, B2, L.QB_BF16, dws)
+    torch.cuda.synchronize()
+    del qws
+    for (name, n, w, codes, c2, a2, off, y) in W:
+        nb = n // B
+        # block absmax (a maximum: exact whatever computes it) for the tensor's nested state
+        a = w.abs().view(nb, B).amax(dim=1).float().cpu().numpy()
+        c2w, a2w, mu = oracle.dq_quantize(a, B2)
+        assert np.float32(off[0].item()) == mu, name
+        assert np.array_equal(c2.cpu().numpy(), c2w) and np.array_equal(a2.cpu().numpy(), a2w), name
+        blocks = np.unique(np.concatenate([rng.choice(nb, 48, replace=False), [0, nb - 1]]))
+        idx = torch.from_numpy(blocks).to(DEV)
+        xs = host_bits(w.view(nb, B).index_select(0, idx)).reshape(-1)
+        want_c, _ = oracle.quantize_blockwise(xs, code, B, oracle.F16)
+        got_c = codes.view(nb, B // 2).index_select(0, idx).cpu().numpy().reshape(-1)
+        assert np.array_equal(got_c, want_c), name
+        ahat = oracle.dq_decode(c2w, a2w, mu)[blocks]
+        want_y = oracle.dequantize_blockwise(want_c, ahat, code, B, len(blocks) * B, oracle.BF16)
+        got_y = host_bits(y.view(nb, B).index_select(0, idx)).reshape(-1)
+        assert np.array_equal(got_y, want_y), name
