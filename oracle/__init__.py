@@ -45,6 +45,8 @@ def lib():
             "orc_adamw32_step": [vp, vp, i32, i64, vp, vp, dp, dp, dp, dp, dp, i32],
             "orc_adamw8bit_step": [vp, vp, i32, i64, vp, vp, vp, vp, i32, dp, dp, dp, dp, dp, i32],
             "orc_adam_scalars": [dp, dp, dp, dp, dp, i32, vp],
+            "orc_optim32_step": [i32, vp, i32, vp, vp, i32, i64, vp, vp],
+            "orc_optim8bit_step": [i32, vp, i32, vp, vp, i32, i64, vp, vp, vp, vp, i32],
         }
         for name, argtypes in sig.items():
             f = getattr(L, name)
@@ -264,6 +266,43 @@ def adamw8bit_step(p, g, cm, cv, am, av, blocksize, lr, beta1, beta2, eps, wd, s
     g = np.ascontiguousarray(g)
     _check(lib().orc_adamw8bit_step(_p(p), _p(g), gdt, p.size, _p(cm), _p(cv), _p(am), _p(av), blocksize,
                                     lr, beta1, beta2, eps, wd, step), "adamw8bit")
+
+
+# the sibling optimizers (oracle.c, section "the sibling 8-bit optimizers")
+ADAMW, ADAM, LION, SGD, RMSPROP = 0, 1, 2, 3, 4
+OPTIMIZER_STATES = {ADAMW: 2, ADAM: 2, LION: 1, SGD: 1, RMSPROP: 1}
+
+
+def _optim_hp(lr, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.0, dampening=0.0, nesterov=False):
+    return np.array([lr, beta1, beta2, eps, wd, dampening, 1.0 if nesterov else 0.0], dtype=np.float64)
+
+
+def optim32_step(kind, p, g, x1, x2=None, step=1, gdt=None, **hp):
+    """In-place step of optimizer `kind` with binary32 states x1 (and x2 for the
+    two-state kinds); hp: lr, beta1, beta2, eps, wd, dampening, nesterov."""
+    if gdt is None:
+        gdt = _dtype_id(g)
+    g = np.ascontiguousarray(g)
+    h = _optim_hp(**hp)
+    _check(lib().orc_optim32_step(kind, _p(h), step, _p(p), _p(g), gdt, p.size, _p(x1),
+                                  _p(x2) if x2 is not None else None), "optim32")
+
+
+def optim8bit_step(kind, p, g, c1, a1, c2=None, a2=None, blocksize=2048, step=1, gdt=None, **hp):
+    """In-place 8-bit step of optimizer `kind`: states as dynamic 8-bit codes
+    c1 (and c2) with block absmax a1 (and a2)."""
+    two = OPTIMIZER_STATES[kind] == 2
+    arrs = [(p, np.float32), (c1, np.uint8), (a1, np.float32)] + ([(c2, np.uint8), (a2, np.float32)] if two else [])
+    for arr, dt in arrs:
+        if arr.dtype != dt or not arr.flags.c_contiguous:
+            raise TypeError("contiguous arrays of the documented dtypes expected")
+    if gdt is None:
+        gdt = _dtype_id(g)
+    g = np.ascontiguousarray(g)
+    h = _optim_hp(**hp)
+    _check(lib().orc_optim8bit_step(kind, _p(h), step, _p(p), _p(g), gdt, p.size, _p(c1),
+                                    _p(c2) if two else None, _p(a1), _p(a2) if two else None, blocksize),
+           "optim8bit")
 
 
 def f32_to_bf16_bits(x):

@@ -517,3 +517,182 @@ int orc_adam_scalars(double lr, double beta1, double beta2, double eps, double w
     out8[4] = s.s1; out8[5] = s.s2; out8[6] = s.dec; out8[7] = s.eps;
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* the sibling 8-bit optimizers                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages list 8-bit Adam, AdamW, SGD (with momentum), RMSprop and Lion
+ * next to each other as drop-in replacements that keep their optimizer's
+ * hyperparameters (page "bitsandbytes深度解析", section 优化器模块深度分析; page
+ * "Py之bitsandbytes", sections 1 and 使用8位优化器).  Reading: each follows its
+ * usual definition (torch.optim.Adam, SGD and RMSprop; Lion as published by
+ * Chen et al., 2023), with every state tensor kept as block-wise dynamic 8-bit
+ * codes exactly as for AdamW.  Binary32, each operation rounded on its own.
+ *
+ * hp[] = {lr, beta1, beta2, eps, weight_decay, dampening, nesterov}; per kind:
+ *   ORC_ADAMW    as orc_adamw8bit_step.
+ *   ORC_ADAM     L2-coupled decay: gw = g + wd*p, then the Adam update with
+ *                bias correction and no decoupled decay.  States m, v.
+ *   ORC_LION     c = b1*m + (1-b1)*g; p' = p*(1 - lr*wd) - lr*sign(c);
+ *                m' = b2*m + (1-b2)*g.  State m.
+ *   ORC_SGD      gw = g + wd*p; buf = gw at step 1, else
+ *                buf' = mu*buf + (1-dampening)*gw (mu = beta1);
+ *                d = nesterov ? gw + mu*buf' : buf'; p' = p - lr*d.  State buf.
+ *   ORC_RMSPROP  gw = g + wd*p; v' = al*v + (1-al)*gw*gw (al = beta2);
+ *                p' = p - lr*(gw / (sqrt(v') + eps)).  State v.
+ */
+enum { ORC_ADAMW = 0, ORC_ADAM = 1, ORC_LION = 2, ORC_SGD = 3, ORC_RMSPROP = 4 };
+
+static int optim_states(int kind) { return (kind == ORC_ADAMW || kind == ORC_ADAM) ? 2 : 1; }
+
+typedef struct {
+    int kind, step, nesterov;
+    adam_scalars a;                 /* Adam(W) scalars */
+    float lr, wd, b1, ob1, b2, ob2, dec, omd, eps;
+} optim_scalars;
+
+static optim_scalars optim_prepare(int kind, const double* hp, int step)
+{
+    optim_scalars s;
+    memset(&s, 0, sizeof s);
+    s.kind = kind;
+    s.step = step;
+    s.nesterov = hp[6] != 0.0;
+    s.a = adam_prepare(hp[0], hp[1], hp[2], hp[3], kind == ORC_ADAMW ? hp[4] : 0.0, step);
+    s.lr = (float)hp[0];
+    s.wd = (float)hp[4];
+    s.b1 = (float)hp[1];
+    s.ob1 = (float)(1.0 - hp[1]);
+    s.b2 = (float)hp[2];
+    s.ob2 = (float)(1.0 - hp[2]);
+    s.dec = (float)(1.0 - hp[0] * hp[4]);
+    s.omd = (float)(1.0 - hp[5]);
+    s.eps = (float)hp[3];
+    return s;
+}
+
+/* One element: x1, x2 are the states (x2 unused by one-state kinds). */
+static void optim_elem(const optim_scalars* s, float g, float* p, float* x1, float* x2)
+{
+    switch (s->kind) {
+    case ORC_ADAMW:
+        adam_elem(&s->a, g, p, x1, x2);
+        break;
+    case ORC_ADAM: {
+        float t = s->wd * *p;
+        float gw = g + t;
+        adam_elem(&s->a, gw, p, x1, x2);   /* decoupled factor is 1: p*1 is exact */
+        break;
+    }
+    case ORC_LION: {
+        float t1 = s->b1 * *x1;
+        float t2 = s->ob1 * g;
+        float c = t1 + t2;
+        float sg = c > 0.0f ? 1.0f : (c < 0.0f ? -1.0f : 0.0f);
+        float pd = *p * s->dec;
+        float u = s->lr * sg;
+        *p = pd - u;
+        float t3 = s->b2 * *x1;
+        float t4 = s->ob2 * g;
+        *x1 = t3 + t4;
+        break;
+    }
+    case ORC_SGD: {
+        float t = s->wd * *p;
+        float gw = g + t;
+        float buf;
+        if (s->step == 1) {
+            buf = gw;
+        } else {
+            float t1 = s->b1 * *x1;
+            float t2 = s->omd * gw;
+            buf = t1 + t2;
+        }
+        float d = buf;
+        if (s->nesterov) {
+            float t3 = s->b1 * buf;
+            d = gw + t3;
+        }
+        float u = s->lr * d;
+        *p = *p - u;
+        *x1 = buf;
+        break;
+    }
+    case ORC_RMSPROP: {
+        float t = s->wd * *p;
+        float gw = g + t;
+        float t3 = s->b2 * *x1;
+        float gg = gw * gw;
+        float t4 = s->ob2 * gg;
+        float v1 = t3 + t4;
+        float den = sqrtf(v1) + s->eps;
+        float q = gw / den;
+        float u = s->lr * q;
+        *p = *p - u;
+        *x1 = v1;
+        break;
+    }
+    }
+}
+
+static int optim_check(int kind, const double* hp, int step)
+{
+    if (kind < ORC_ADAMW || kind > ORC_RMSPROP || step < 1) return -1;
+    if (kind == ORC_SGD && !(hp[1] > 0.0)) return -1;   /* 8-bit SGD keeps a momentum state */
+    return 0;
+}
+
+/* Any kind with binary32 states (no quantization): pins the update rules. */
+int orc_optim32_step(int kind, const double* hp, int step, float* p, const void* g, int gdt, int64_t n,
+                     float* x1, float* x2)
+{
+    if (optim_check(kind, hp, step) != 0) return -1;
+    optim_scalars s = optim_prepare(kind, hp, step);
+    float dummy = 0.0f;
+    for (int64_t i = 0; i < n; i++)
+        optim_elem(&s, load_elem(g, gdt, i), &p[i], &x1[i], optim_states(kind) == 2 ? &x2[i] : &dummy);
+    return 0;
+}
+
+/*
+ * Any kind with block-wise dynamic 8-bit states (c1/a1, and c2/a2 for the
+ * two-state kinds; NULL otherwise): per block, decode the states, update every
+ * element, take each state's new block absmax, encode again.
+ */
+int orc_optim8bit_step(int kind, const double* hp, int step, float* p, const void* g, int gdt, int64_t n,
+                       uint8_t* c1, uint8_t* c2, float* a1, float* a2, int B)
+{
+    if (optim_check(kind, hp, step) != 0) return -1;
+    const int two = optim_states(kind) == 2;
+    optim_scalars s = optim_prepare(kind, hp, step);
+    float cb[256];
+    orc_dyn8_codebook(cb);
+    float* xb = (float*)malloc(sizeof(float) * (size_t)B);
+    float* yb = (float*)malloc(sizeof(float) * (size_t)B);
+    if (!xb || !yb) { free(xb); free(yb); return -1; }
+    int64_t nb = (n + B - 1) / B;
+    for (int64_t b = 0; b < nb; b++) {
+        int64_t lo = b * B, hi = lo + B < n ? lo + B : n;
+        float m1 = 0.0f, m2 = 0.0f;
+        for (int64_t i = lo; i < hi; i++) {
+            float x = cb[c1[i]] * a1[b];
+            float y = two ? cb[c2[i]] * a2[b] : 0.0f;
+            optim_elem(&s, load_elem(g, gdt, i), &p[i], &x, &y);
+            xb[i - lo] = x;
+            yb[i - lo] = y;
+            if (fabsf(x) > m1) m1 = fabsf(x);
+            if (fabsf(y) > m2) m2 = fabsf(y);
+        }
+        a1[b] = m1;
+        if (two) a2[b] = m2;
+        for (int64_t i = lo; i < hi; i++) {
+            c1[i] = (uint8_t)nearest_index(cb, 256, m1 > 0.0f ? xb[i - lo] / m1 : 0.0f);
+            if (two) c2[i] = (uint8_t)nearest_index(cb, 256, m2 > 0.0f ? yb[i - lo] / m2 : 0.0f);
+        }
+    }
+    free(xb);
+    free(yb);
+    return 0;
+}
