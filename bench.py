@@ -263,36 +263,56 @@ def cpu_baseline(torch, model, seconds_target, rng):
     }
 
 
+OPTIMIZERS = {  # name: (qb kind, hyperparameters, states)
+    "adamw": (0, dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01), 2),
+    "adam": (1, dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01), 2),
+    "lion": (2, dict(lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.1), 1),
+    "sgd": (3, dict(lr=1e-2, beta1=0.9, weight_decay=1e-4), 1),
+    "rmsprop": (4, dict(lr=1e-3, beta2=0.99, eps=1e-8, weight_decay=0.0), 1),
+}
+
+
+def optim_bytes_per_param(states, grad_bytes=2, block=ADAM_BLOCK):
+    # p read+write (8), grad read, each state's code read+write (2) and absmax read+write per block
+    return 8 + grad_bytes + states * (2 + 8.0 / block)
+
+
 def bench_flat(torch, qb, inputs, dev, args):
-    """Single-tensor fused AdamW8bit step on a flat 1,500,000,000-parameter fp32
-    buffer (bf16 gradients ~N(0, 1e-3), two sets alternating; block 2048)."""
+    """Single-tensor fused 8-bit optimizer step (AdamW by default) on a flat
+    1,500,000,000-parameter fp32 buffer (bf16 gradients ~N(0, 1e-3), two sets
+    alternating; block 2048)."""
     n = 1_500_000_000
     nb = (n + ADAM_BLOCK - 1) // ADAM_BLOCK
-    log(f"allocating a flat buffer of {n:,} params")
+    kind, hp, states = OPTIMIZERS[args.optimizer]
+    log(f"allocating a flat buffer of {n:,} params ({args.optimizer}, {states} state(s))")
     p = inputs.normal(n, 0.02, seed=args.seed, device=dev)
-    m = torch.full((n,), 127, dtype=torch.uint8, device=dev)
-    v = torch.full((n,), 127, dtype=torch.uint8, device=dev)
-    am = torch.zeros(nb, device=dev)
-    av = torch.zeros(nb, device=dev)
+    s1 = torch.full((n,), 127, dtype=torch.uint8, device=dev)
+    a1 = torch.zeros(nb, device=dev)
+    s2 = torch.full((n,), 127, dtype=torch.uint8, device=dev) if states == 2 else None
+    a2 = torch.zeros(nb, device=dev) if states == 2 else None
     grads = [inputs.normal(n, 1e-3, inputs.grad_seed(args.seed, 0, k), device=dev, dtype=torch.bfloat16) for k in range(2)]
+
+    def step(k):
+        qb.qb_optimizer8bit_step(qb.optim_hparams(kind, step=k, **hp), p, grads[k % 2], n, s1, s2, a1, a2, ADAM_BLOCK)
+
     torch.cuda.synchronize()
     for k in range(1, args.warmup + 1):
-        qb.qb_adamw8bit_step(p, grads[k % 2], n, m, v, am, av, ADAM_BLOCK, qb.hparams(step=k, **HP))
+        step(k)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        k = args.warmup + 1 + i
         evs[i][0].record()
-        qb.qb_adamw8bit_step(p, grads[k % 2], n, m, v, am, av, ADAM_BLOCK, qb.hparams(step=k, **HP))
+        step(args.warmup + 1 + i)
         evs[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = sorted(a.elapsed_time(b) for a, b in evs)
     med = ms[len(ms) // 2]
-    nbytes = n * adam_bytes_per_param()
-    print(json.dumps({"workload": "flat 1.5e9 fp32 params, bf16 grads, block 2048, single-tensor AdamW8bit",
-                      "steps": args.steps, "median_ms": med, "GB/s": nbytes / med / 1e6,
+    nbytes = n * optim_bytes_per_param(states)
+    print(json.dumps({"workload": f"flat 1.5e9 fp32 params, bf16 grads, block 2048, single-tensor {args.optimizer} "
+                                  f"8-bit step", "optimizer": args.optimizer, "steps": args.steps, "median_ms": med,
+                      "bytes_per_param": optim_bytes_per_param(states), "GB/s": nbytes / med / 1e6,
                       "params_per_s": n / med * 1e3, "frac_of_hbm_peak": nbytes / med / 1e6 / HBM_PEAK_GBS,
                       "wall_ms_per_step": wall / args.steps * 1e3}), flush=True)
 
@@ -320,6 +340,8 @@ def main():
     ap.add_argument("--adam-only", action="store_true", help="time only the multi-tensor AdamW step")
     ap.add_argument("--flat", action="store_true",
                     help="time the single-tensor AdamW step on a flat 1.5e9-parameter buffer instead")
+    ap.add_argument("--optimizer", choices=sorted(OPTIMIZERS), default="adamw",
+                    help="optimizer of the --flat run (the 8-bit states of each kind)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device five times (the reference kernel for HBM counters)")
     args = ap.parse_args()

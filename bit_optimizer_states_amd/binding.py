@@ -17,6 +17,7 @@ LIB_PATH = os.environ.get("QB_LIBRARY") or os.path.join(_HERE, "libqb.so")
 QB_OK, QB_EINVAL, QB_EALIGN, QB_EUNSUPPORTED, QB_EHIP, QB_EWORKSPACE, QB_EINIT = range(7)
 QB_F32, QB_F16, QB_BF16 = 0, 1, 2
 QB_DYN8, QB_NF4, QB_FP4 = 0, 1, 2
+QB_ADAMW, QB_ADAM, QB_LION, QB_SGD, QB_RMSPROP = range(5)
 
 _DTYPE = {torch.float32: QB_F32, torch.float16: QB_F16, torch.bfloat16: QB_BF16}
 
@@ -35,6 +36,12 @@ class qb_dq(ctypes.Structure):
 class qb_adamw_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int32)]
+
+
+class qb_optim_hparams(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("dampening", ctypes.c_double), ("nesterov", ctypes.c_int32), ("step", ctypes.c_int32)]
 
 
 class qb_tensor(ctypes.Structure):
@@ -72,11 +79,16 @@ def lib():
                                            vp, sz, vp]
         L.qb_multi_tensor_dequantize.argtypes = [ctypes.POINTER(qb_dequant_tensor), i32, i32, i32, i32, i32, vp, sz,
                                                  vp]
+        L.qb_optimizer8bit_step.argtypes = [ctypes.POINTER(qb_optim_hparams), vp, vp, i32, i64, vp, vp, vp, vp, i32,
+                                            vp]
+        L.qb_multi_tensor_optimizer_step.argtypes = [ctypes.POINTER(qb_optim_hparams), ctypes.POINTER(qb_tensor), i32,
+                                                     i32, i32, vp, sz, vp]
         L.qb_multi_tensor_quantize.argtypes = [ctypes.POINTER(qb_quant_tensor), i32, i32, i32, i32, i32, vp, sz, vp]
         L.qb_multi_tensor_quantize_workspace_bytes.argtypes = [ctypes.POINTER(qb_quant_tensor), i32, i32]
         L.qb_multi_tensor_quantize_workspace_bytes.restype = sz
         for f in (L.qb_quantize, L.qb_dequantize, L.qb_adamw8bit_step, L.qb_multi_tensor_step,
-                  L.qb_multi_tensor_dequantize, L.qb_multi_tensor_quantize):
+                  L.qb_multi_tensor_dequantize, L.qb_multi_tensor_quantize, L.qb_optimizer8bit_step,
+                  L.qb_multi_tensor_optimizer_step):
             f.restype = ctypes.c_int
         L.qb_dq_workspace_bytes.argtypes = [i64, i32]
         L.qb_dq_workspace_bytes.restype = sz
@@ -161,12 +173,32 @@ def qb_adamw8bit_step(p, g, n, m, v, absmax_m, absmax_v, blocksize, hp, stream=N
            "qb_adamw8bit_step")
 
 
+def optim_hparams(kind, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, dampening=0.0, nesterov=False,
+                  step=1):
+    return qb_optim_hparams(int(kind), lr, beta1, beta2, eps, weight_decay, dampening, 1 if nesterov else 0,
+                            int(step))
+
+
+def qb_optimizer8bit_step(hp, p, g, n, state1, state2, absmax1, absmax2, blocksize, stream=None):
+    """state2 / absmax2 may be None for the one-state kinds."""
+    _check(lib().qb_optimizer8bit_step(ctypes.byref(hp), _ptr(p), _ptr(g), _dtype(g), int(n), _ptr(state1),
+                                       _ptr(state2), _ptr(absmax1), _ptr(absmax2), int(blocksize), _stream(stream)),
+           "qb_optimizer8bit_step")
+
+
 def tensor_table(tensors):
-    """ctypes array of qb_tensor from tuples (p, g, m, v, absmax_m, absmax_v)."""
+    """ctypes array of qb_tensor from tuples (p, g, m, v, absmax_m, absmax_v);
+    v and absmax_v may be None for the one-state optimizers."""
     arr = (qb_tensor * len(tensors))()
     for i, (p, g, m, v, am, av) in enumerate(tensors):
         arr[i] = qb_tensor(_ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(am), _ptr(av), p.numel())
     return arr
+
+
+def qb_multi_tensor_optimizer_step(hp, table, count, gdt, blocksize, ws, stream=None):
+    _check(lib().qb_multi_tensor_optimizer_step(ctypes.byref(hp), table, int(count), int(gdt), int(blocksize),
+                                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qb_multi_tensor_optimizer_step")
 
 
 def qb_multi_tensor_step(table, count, gdt, blocksize, hp, ws, stream=None):

@@ -47,14 +47,41 @@ qb_status check_dq(const qb_dq* dq, int64_t nb, bool need_ws)
     return QB_OK;
 }
 
-bool valid_hparams(const qb_adamw_hparams* hp)
+bool finite(double v) { return std::isfinite(v); }
+bool unit(double v) { return v >= 0 && v < 1; }    // [0, 1)
+
+// Hyperparameter checks per optimizer kind (the ranges their definitions need).
+bool valid_optim(const qb_optim_hparams* hp)
 {
-    if (!hp) return false;
-    auto finite = [](double v) { return std::isfinite(v); };
-    return finite(hp->lr) && hp->lr >= 0 && finite(hp->weight_decay) && hp->weight_decay >= 0 &&
-           hp->beta1 >= 0 && hp->beta1 < 1 && hp->beta2 >= 0 && hp->beta2 < 1 && finite(hp->eps) &&
-           hp->eps > 0 && hp->step >= 1;
+    if (!hp || hp->step < 1 || !finite(hp->lr) || hp->lr < 0 || !finite(hp->weight_decay) || hp->weight_decay < 0)
+        return false;
+    switch (hp->kind) {
+    case QB_ADAMW:
+    case QB_ADAM: return unit(hp->beta1) && unit(hp->beta2) && finite(hp->eps) && hp->eps > 0;
+    case QB_LION: return unit(hp->beta1) && unit(hp->beta2);
+    case QB_SGD:
+        // 8-bit SGD keeps a momentum state; Nesterov momentum needs zero dampening
+        return hp->beta1 > 0 && hp->beta1 < 1 && hp->dampening >= 0 && hp->dampening <= 1 &&
+               (hp->nesterov == 0 || (hp->nesterov == 1 && hp->dampening == 0));
+    case QB_RMSPROP: return unit(hp->beta2) && finite(hp->eps) && hp->eps > 0;
+    default: return false;
+    }
 }
+
+qb_optim_hparams as_optim(const qb_adamw_hparams* hp)
+{
+    qb_optim_hparams o{};
+    o.kind = QB_ADAMW;
+    o.lr = hp->lr;
+    o.beta1 = hp->beta1;
+    o.beta2 = hp->beta2;
+    o.eps = hp->eps;
+    o.weight_decay = hp->weight_decay;
+    o.step = hp->step;
+    return o;
+}
+
+int optim_states(qb_optimizer k) { return (k == QB_ADAMW || k == QB_ADAM) ? 2 : 1; }
 
 // beta^t by t repeated binary64 multiplications.  Consecutive steps of the
 // same beta reuse the previous power, so a training loop pays one multiply.
@@ -80,19 +107,25 @@ double beta_power(double beta, int32_t t, int slot)
 }
 
 // Per-element scalars: computed in binary64, each rounded once to binary32.
-AdamScalars prepare(const qb_adamw_hparams& hp)
+OptScalars prepare(const qb_optim_hparams& hp)
 {
-    const double p1 = beta_power(hp.beta1, hp.step, 0);
-    const double p2 = beta_power(hp.beta2, hp.step, 1);
-    AdamScalars s;
+    OptScalars s{};
     s.b1 = (float)hp.beta1;
     s.ob1 = (float)(1.0 - hp.beta1);
     s.b2 = (float)hp.beta2;
     s.ob2 = (float)(1.0 - hp.beta2);
-    s.s1 = (float)(hp.lr / (1.0 - p1));
-    s.s2 = (float)(1.0 / std::sqrt(1.0 - p2));
     s.dec = (float)(1.0 - hp.lr * hp.weight_decay);
     s.eps = (float)hp.eps;
+    s.wd = (float)hp.weight_decay;
+    s.lr = (float)hp.lr;
+    s.omd = (float)(1.0 - hp.dampening);
+    if (hp.kind == QB_ADAMW || hp.kind == QB_ADAM) {
+        const double p1 = beta_power(hp.beta1, hp.step, 0);
+        const double p2 = beta_power(hp.beta2, hp.step, 1);
+        s.s1 = (float)(hp.lr / (1.0 - p1));
+        s.s2 = (float)(1.0 / std::sqrt(1.0 - p2));
+    }
+    s.flags = (hp.nesterov ? kOptNesterov : 0) | (hp.step == 1 ? kOptFirstStep : 0);
     return s;
 }
 
@@ -437,33 +470,38 @@ qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t c
                                      blocksize, mode == 1 ? blocksize2 : 256, mode == 1, (int)ydt, s));
 }
 
-qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, uint8_t* m, uint8_t* v,
-                            float* absmax_m, float* absmax_v, int32_t blocksize, const qb_adamw_hparams* hp,
-                            void* stream)
+qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void* g, qb_dtype gdt, int64_t n,
+                                uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2, int32_t blocksize,
+                                void* stream)
 {
-    if (n < 0 || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_hparams(hp)) return QB_EINVAL;
+    if (n < 0 || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_optim(hp)) return QB_EINVAL;
     if (n == 0) return QB_OK;
+    const bool two = optim_states(hp->kind) == 2;
+    if (!two) {
+        state2 = nullptr;
+        absmax2 = nullptr;
+    }
     if (nblocks(n, blocksize) >= (int64_t(1) << 31)) return QB_EINVAL;
-    if (!p || !g || !m || !v || !absmax_m || !absmax_v) return QB_EINVAL;
+    if (!p || !g || !state1 || !absmax1 || (two && (!state2 || !absmax2))) return QB_EINVAL;
     if ((const void*)p == g) return QB_EINVAL;
-    if (!aligned16(p) || !aligned16(g) || !aligned16(m) || !aligned16(v) || !aligned16(absmax_m) ||
-        !aligned16(absmax_v))
+    if (!aligned16(p) || !aligned16(g) || !aligned16(state1) || !aligned16(absmax1) ||
+        (two && (!aligned16(state2) || !aligned16(absmax2))))
         return QB_EALIGN;
     if (!device_tables()) return QB_EINIT;
-    TensorDesc d{p, g, m, v, absmax_m, absmax_v, n, 0};
-    const int64_t ntiles = adamw_tiles(n, blocksize);
-    return hip_status(launch_adamw8(d, nullptr, ntiles, blocksize, (int)gdt, prepare(*hp),
-                                    static_cast<hipStream_t>(stream)));
+    TensorDesc d{p, g, state1, state2, absmax1, absmax2, n, 0};
+    return hip_status(launch_optim8((int)hp->kind, d, nullptr, adamw_tiles(n, blocksize), blocksize, (int)gdt,
+                                    prepare(*hp), static_cast<hipStream_t>(stream)));
 }
 
-qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
-                               const qb_adamw_hparams* hp, void* ws, size_t ws_bytes, void* stream)
+qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
+                                         qb_dtype gdt, int32_t blocksize, void* ws, size_t ws_bytes, void* stream)
 {
-    if (count < 0 || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_hparams(hp)) return QB_EINVAL;
+    if (count < 0 || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_optim(hp)) return QB_EINVAL;
     if (count == 0) return QB_OK;
     if (!tensors || !ws) return QB_EINVAL;
     if (!aligned16(ws)) return QB_EALIGN;
     if (ws_bytes < qb_multi_tensor_workspace_bytes(count)) return QB_EWORKSPACE;
+    const bool two = optim_states(hp->kind) == 2;
     thread_local std::vector<TensorDesc> table;
     table.clear();
     int64_t tiles = 0;
@@ -472,12 +510,13 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
         if (t.n < 0) return QB_EINVAL;
         if (t.n == 0) continue;
         if (nblocks(t.n, blocksize) >= (int64_t(1) << 31)) return QB_EINVAL;
-        if (!t.p || !t.g || !t.m || !t.v || !t.absmax_m || !t.absmax_v) return QB_EINVAL;
+        if (!t.p || !t.g || !t.m || !t.absmax_m || (two && (!t.v || !t.absmax_v))) return QB_EINVAL;
         if ((const void*)t.p == t.g) return QB_EINVAL;
-        if (!aligned16(t.p) || !aligned16(t.g) || !aligned16(t.m) || !aligned16(t.v) || !aligned16(t.absmax_m) ||
-            !aligned16(t.absmax_v))
+        if (!aligned16(t.p) || !aligned16(t.g) || !aligned16(t.m) || !aligned16(t.absmax_m) ||
+            (two && (!aligned16(t.v) || !aligned16(t.absmax_v))))
             return QB_EALIGN;
-        table.push_back(TensorDesc{t.p, t.g, t.m, t.v, t.absmax_m, t.absmax_v, t.n, tiles});
+        table.push_back(TensorDesc{t.p, t.g, t.m, two ? t.v : nullptr, t.absmax_m, two ? t.absmax_v : nullptr, t.n,
+                                   tiles});
         tiles += adamw_tiles(t.n, blocksize);
     }
     if (table.empty()) return QB_OK;
@@ -490,7 +529,24 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
     stage_tile_map(staging, 0, table, tiles, count, ws, &map);
     qb_status st = copy_staging(staging, ws, s);
     if (st != QB_OK) return st;
-    return hip_status(launch_adamw8(table[0], &map, tiles, blocksize, (int)gdt, prepare(*hp), s));
+    return hip_status(launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)gdt, prepare(*hp), s));
+}
+
+qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, uint8_t* m, uint8_t* v,
+                            float* absmax_m, float* absmax_v, int32_t blocksize, const qb_adamw_hparams* hp,
+                            void* stream)
+{
+    if (!hp) return QB_EINVAL;
+    const qb_optim_hparams o = as_optim(hp);
+    return qb_optimizer8bit_step(&o, p, g, gdt, n, m, v, absmax_m, absmax_v, blocksize, stream);
+}
+
+qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
+                               const qb_adamw_hparams* hp, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!hp) return QB_EINVAL;
+    const qb_optim_hparams o = as_optim(hp);
+    return qb_multi_tensor_optimizer_step(&o, tensors, count, gdt, blocksize, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

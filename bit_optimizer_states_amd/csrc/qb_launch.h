@@ -18,8 +18,20 @@ constexpr int kBinCopies = 8;
 constexpr size_t kBinWords = (size_t)kBinCopies * 256;
 constexpr size_t kBinBytes = kBinWords * sizeof(unsigned long long);
 
-struct AdamScalars {
+// Optimizer kinds of the fused 8-bit step (the values of qb_optimizer).
+enum OptKind { OPT_ADAMW = 0, OPT_ADAM = 1, OPT_LION = 2, OPT_SGD = 3, OPT_RMSPROP = 4 };
+constexpr int32_t kOptNesterov = 1, kOptFirstStep = 2;
+
+// Host scalars of one step, each computed in binary64 and rounded once:
+//   Adam(W)  b1, ob1 = 1 - b1, b2, ob2, s1 = lr / (1 - b1^t), s2 = 1 / sqrt(1 - b2^t),
+//            dec = 1 - lr*wd (AdamW), eps, wd (Adam's L2 term);
+//   Lion     b1, ob1, b2, ob2, lr, dec = 1 - lr*wd;
+//   SGD      b1 = momentum, omd = 1 - dampening, lr, wd, flags;
+//   RMSprop  b2 = alpha, ob2 = 1 - alpha, lr, eps, wd.
+struct OptScalars {
     float b1, ob1, b2, ob2, s1, s2, dec, eps;
+    float wd, lr, omd;
+    int32_t flags;
 };
 
 // One tensor of a fused AdamW launch; tile_begin is the first global tile.
@@ -166,12 +178,12 @@ constexpr int64_t dequant_tile_elems(int bits, bool multi)
 {
     return bits == 8 ? QB_DQ8_TILE : (multi ? QB_DQ_MULTI_TILE : QB_DQ_TILE);
 }
-// map: the device tables of a multi-tensor launch, or nullptr for the one
-// tensor `single`.
-hipError_t launch_adamw8(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B, int gdt,
-                         const AdamScalars& hs, hipStream_t s);
+// Fused 8-bit step of optimizer `opt` (OptKind) on one tensor (map ==
+// nullptr) or on the tensors of map.
+hipError_t launch_optim8(int opt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B,
+                         int gdt, const OptScalars& hs, hipStream_t s);
 
-// Tiles of the AdamW kernel for a tensor of n elements at block size B.
+// Tiles of the optimizer kernel for a tensor of n elements at block size B.
 int64_t adamw_tiles(int64_t n, int B);
 
 }  // namespace qb

@@ -1,12 +1,15 @@
-// qb_adamw.hip -- fused AdamW step with block-wise dynamic 8-bit moments.
+// qb_optim.hip -- fused 8-bit optimizer steps: AdamW, Adam, Lion, SGD with
+// momentum and RMSprop, each state held as block-wise dynamic 8-bit codes.
 //
-// The 8-bit optimizer keeps both Adam moments as block-wise dynamic 8-bit
-// codes plus one fp32 absmax per block (abstract quoted on "Py之bitsandbytes：
+// The 8-bit optimizer keeps its states as block-wise dynamic 8-bit codes plus
+// one fp32 absmax per block (abstract quoted on "Py之bitsandbytes：
 // bitsandbytes的简介、安装、使用方法之详细攻略", section 2; 2 bytes of state per
-// parameter: "bitsandbytes - Quantização de LLM", section Workflow 3) and is a
-// drop-in replacement for AdamW (same lr, betas, eps).  One pass per block, in
-// registers: decode m and v, update m, v and p, reduce the new block absmax of
-// m' and v', encode m' and v' again.  Each parameter's bytes cross HBM once.
+// parameter for Adam: "bitsandbytes - Quantização de LLM", section Workflow
+// 3) and replaces its 32-bit optimizer with the same hyperparameters; 8-bit
+// Adam, SGD, RMSprop and Lion are listed beside AdamW ("bitsandbytes深度解析",
+// section 优化器模块深度分析).  One pass per block, in registers: decode the
+// states, update them and p, reduce each state's new block absmax, encode the
+// states again.  Each parameter's bytes cross HBM once.
 //
 // One 256-thread workgroup per tile (a tile is one block for B >= 1024), in
 // tile order.  For many tensors, the tiles of all tensors are numbered in one
@@ -19,7 +22,7 @@
 
 namespace qb {
 
-// Threads per workgroup of the AdamW kernel: a 2048-element block takes one
+// Threads per workgroup of the optimizer kernel: a 2048-element block takes one
 // workgroup of kAdamThreads threads, i.e. 2048 / kAdamThreads elements per
 // thread; more elements per thread spread the per-block fixed work (tensor
 // lookup, table staging, block reduction, reciprocals) thinner.  Measured on
@@ -111,11 +114,67 @@ __device__ __forceinline__ void block_max2(uint32_t& x, uint32_t& y, uint32_t (*
     }
 }
 
-template <int B, int GDT, bool MULTI>
-__global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, TileMap<TensorDesc> map, AdamScalars hs,
+// States of an optimizer kind: two (m, v) for Adam(W), one otherwise.
+constexpr int opt_states(int opt) { return (opt == OPT_ADAMW || opt == OPT_ADAM) ? 2 : 1; }
+
+// One element of the update, binary32.  x, y: the decoded states (y for the
+// two-state kinds), replaced by the updated ones; p updated in place.  The
+// states are computed with every operation rounded on its own, exactly as the
+// definitions read, because they decide the codes.  Where a state reads p (the
+// L2 term of Adam, SGD and RMSprop) p must be exact too, so those kinds and
+// Lion update p with separately rounded operations and IEEE square root and
+// division: bit-exact.  AdamW's states never read p, so its parameter update
+// takes hardware square root and reciprocal (about 1 ulp each) and fused
+// multiply-adds: within 1e-6 relative of the separately rounded formula.
+template <int OPT>
+__device__ __forceinline__ void opt_elem(const OptScalars& hs, float gi, float& p, float& x, float& y)
+{
+    if constexpr (OPT == OPT_ADAMW) {
+        const float mm = hs.b1 * x + hs.ob1 * gi;
+        const float vv = hs.b2 * y + hs.ob2 * (gi * gi);
+        const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(vv), hs.s2, hs.eps);
+        const float upd = mm * __builtin_amdgcn_rcpf(den);
+        p = __builtin_fmaf(-hs.s1, upd, p * hs.dec);
+        x = mm;
+        y = vv;
+    } else if constexpr (OPT == OPT_ADAM) {               // L2-coupled decay
+        const float t = hs.wd * p;
+        const float gw = gi + t;
+        const float mm = hs.b1 * x + hs.ob1 * gw;
+        const float vv = hs.b2 * y + hs.ob2 * (gw * gw);
+        const float den = __builtin_sqrtf(vv) * hs.s2 + hs.eps;
+        p = p - hs.s1 * (mm / den);
+        x = mm;
+        y = vv;
+    } else if constexpr (OPT == OPT_LION) {
+        const float c = hs.b1 * x + hs.ob1 * gi;
+        const float sg = c > 0.0f ? 1.0f : (c < 0.0f ? -1.0f : 0.0f);
+        p = p * hs.dec - hs.lr * sg;                       // lr * sign is exact
+        x = hs.b2 * x + hs.ob2 * gi;
+    } else if constexpr (OPT == OPT_SGD) {
+        const float t = hs.wd * p;
+        const float gw = gi + t;
+        const float buf = (hs.flags & kOptFirstStep) ? gw : hs.b1 * x + hs.omd * gw;
+        const float dir = (hs.flags & kOptNesterov) ? gw + hs.b1 * buf : buf;
+        p = p - hs.lr * dir;
+        x = buf;
+    } else {                                               // RMSprop
+        const float t = hs.wd * p;
+        const float gw = gi + t;
+        const float vv = hs.b2 * x + hs.ob2 * (gw * gw);
+        const float den = __builtin_sqrtf(vv) + hs.eps;
+        p = p - hs.lr * (gw / den);
+        x = vv;
+    }
+}
+
+template <int OPT, int B, int GDT, bool MULTI>
+__global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, TileMap<TensorDesc> map, OptScalars hs,
                                                          const QbTables* __restrict__ tab)
 {
     using T = TileA<B>;
+    constexpr bool TWO = opt_states(OPT) == 2;
+    constexpr bool X_POS = OPT == OPT_RMSPROP;             // the one state of RMSprop is >= 0
     __shared__ float s_dyn[256];
     __shared__ DynEncLds s_enc;
     __shared__ uint32_t s_red[2][T::NT / 64];
@@ -141,7 +200,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, Tile
     float* const pt = d.p + tbase;
     const void* const gt = static_cast<const char*>(d.g) + tbase * (GDT == DT_F32 ? 4 : 2);
     uint8_t* const mt = d.m + tbase;
-    uint8_t* const vt = d.v + tbase;
+    uint8_t* const vt = TWO ? d.v + tbase : nullptr;
     const uint32_t lofs = (uint32_t)(bt * B + l * T::CW);  // element offset of chunk 0 in the tile
     const int64_t lrem = nloc - tbase;                      // elements left in the tensor from the tile start
 
@@ -149,7 +208,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, Tile
     float am0 = 0.0f, av0 = 0.0f;
     if (blk < nbl) {
         am0 = gld<float>(d.am + blk);
-        av0 = gld<float>(d.av + blk);
+        if constexpr (TWO) av0 = gld<float>(d.av + blk);
     }
     float p[T::EPT], g[T::EPT];
     uint32_t cmw[T::EPT / 4], cvw[T::EPT / 4];             // 4 codes per word
@@ -160,7 +219,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, Tile
             load_chunk<DT_F32, T::CW>(pt, e, &p[c * T::CW]);
             load_chunk<GDT, T::CW>(gt, e, &g[c * T::CW]);
             load_codes<T::CW>(mt, e, &cmw[c * T::CW / 4]);
-            load_codes<T::CW>(vt, e, &cvw[c * T::CW / 4]);
+            if constexpr (TWO) load_codes<T::CW>(vt, e, &cvw[c * T::CW / 4]);
         }
     } else {
 #pragma unroll
@@ -175,7 +234,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, Tile
                     pv = load1<DT_F32>(pt, e);
                     gv = load1<GDT>(gt, e);
                     wm = (wm & ~(0xFFu << (8 * j))) | ((uint32_t)gldo<uint8_t>(mt, e) << (8 * j));
-                    wv = (wv & ~(0xFFu << (8 * j))) | ((uint32_t)gldo<uint8_t>(vt, e) << (8 * j));
+                    if constexpr (TWO) wv = (wv & ~(0xFFu << (8 * j))) | ((uint32_t)gldo<uint8_t>(vt, e) << (8 * j));
                 }
                 p[i] = pv;
                 g[i] = gv;
@@ -190,28 +249,19 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, Tile
     stage_dyn_enc<T::NT>(s_enc, tab, tid);
     __syncthreads();
 
-    // decode, update (binary32, every operation rounded on its own)
+    // decode, update
     float m1[T::EPT], v1[T::EPT];
     float mxm = 0.0f, mxv = 0.0f;
 #pragma unroll
     for (int i = 0; i < T::EPT; ++i) {
         const uint32_t sh = 8 * (i & 3);
-        const float m0 = s_dyn[(cmw[i >> 2] >> sh) & 0xFFu] * am0;
-        const float v0 = s_dyn[(cvw[i >> 2] >> sh) & 0xFFu] * av0;
-        const float gi = g[i];
-        const float mm = hs.b1 * m0 + hs.ob1 * gi;
-        const float vv = hs.b2 * v0 + hs.ob2 * (gi * gi);
-        // the parameter update takes hardware square root and reciprocal
-        // (about 1 ulp each) and fused multiply-adds: within 1e-6 relative
-        // of the separately rounded formula; the moments and codes do not
-        // depend on it
-        const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(vv), hs.s2, hs.eps);
-        const float upd = mm * __builtin_amdgcn_rcpf(den);
-        p[i] = __builtin_fmaf(-hs.s1, upd, p[i] * hs.dec);
-        m1[i] = mm;
-        v1[i] = vv;
-        mxm = __builtin_fmaxf(mxm, __builtin_fabsf(mm));
-        mxv = __builtin_fmaxf(mxv, vv);                     // v' >= 0
+        float x = s_dyn[(cmw[i >> 2] >> sh) & 0xFFu] * am0;
+        float y = TWO ? s_dyn[(cvw[i >> 2] >> sh) & 0xFFu] * av0 : 0.0f;
+        opt_elem<OPT>(hs, g[i], p[i], x, y);
+        m1[i] = x;
+        v1[i] = y;
+        mxm = __builtin_fmaxf(mxm, __builtin_fabsf(x));
+        if constexpr (TWO) mxv = __builtin_fmaxf(mxv, y);  // v' >= 0
     }
     if (full) {
 #pragma unroll
@@ -227,44 +277,47 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, Tile
         }
     }
 
-    // new block absmax of m' and v' (non-negative floats compare as their bits)
+    // new block absmax of the states (non-negative floats compare as their bits)
     uint32_t bm = fbits(mxm), bv = fbits(mxv);
     block_max2<T>(bm, bv, s_red, tid);
     const float am1 = ffrom(bm), av1 = ffrom(bv);
     if (l == 0 && blk < nbl) {
         gst<float>(d.am + blk, am1);
-        gst<float>(d.av + blk, av1);
+        if constexpr (TWO) gst<float>(d.av + blk, av1);
     }
 
-    // encode m' (signed) and v' (non-negative) with the dynamic code
+    // encode the states with the dynamic code (m' signed; v' >= 0)
     const float rm = rcp_rn(am1);        // used only where fast_div_ok(am1)
     const float rv = rcp_rn(av1);
-    const bool fast = fast_div_ok(am1) && fast_div_ok(av1);
+    const bool fm = fast_div_ok(am1), fv = !TWO || fast_div_ok(av1);
     uint32_t om[T::EPT / 4], ov[T::EPT / 4];
-    if (__all(fast)) {
+    auto enc_x = [&](float nv) { return X_POS ? enc_dyn8_pos(nv, s_enc) : enc_dyn8(nv, s_enc); };
+    if (__all(fm && fv)) {
 #pragma unroll
         for (int c = 0; c < T::EPT / 4; ++c) {
             uint32_t wm = 0, wv = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                wm |= enc_dyn8(div_by_block(m1[c * 4 + j], am1, rm), s_enc) << (8 * j);
-                wv |= enc_dyn8_pos(div_by_block(v1[c * 4 + j], av1, rv), s_enc) << (8 * j);
+                wm |= enc_x(div_by_block(m1[c * 4 + j], am1, rm)) << (8 * j);
+                if constexpr (TWO) wv |= enc_dyn8_pos(div_by_block(v1[c * 4 + j], av1, rv), s_enc) << (8 * j);
             }
             om[c] = wm;
             ov[c] = wv;
         }
     } else {
-        const bool fm = fast_div_ok(am1), fv = fast_div_ok(av1);
 #pragma unroll
         for (int c = 0; c < T::EPT / 4; ++c) {
             uint32_t wm = 0, wv = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float mm = m1[c * 4 + j], vv = v1[c * 4 + j];
+                const float mm = m1[c * 4 + j];
                 const float nm = fm ? div_by_block(mm, am1, rm) : (am1 > 0.0f ? mm / am1 : 0.0f);
-                const float nv = fv ? div_by_block(vv, av1, rv) : (av1 > 0.0f ? vv / av1 : 0.0f);
-                wm |= enc_dyn8(nm, s_enc) << (8 * j);
-                wv |= enc_dyn8_pos(nv, s_enc) << (8 * j);
+                wm |= enc_x(nm) << (8 * j);
+                if constexpr (TWO) {
+                    const float vv = v1[c * 4 + j];
+                    const float nv = fv ? div_by_block(vv, av1, rv) : (av1 > 0.0f ? vv / av1 : 0.0f);
+                    wv |= enc_dyn8_pos(nv, s_enc) << (8 * j);
+                }
             }
             om[c] = wm;
             ov[c] = wv;
@@ -275,7 +328,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, Tile
         for (int c = 0; c < T::CH; ++c) {
             const uint32_t e = lofs + c * T::LPB * T::CW;
             store_codes<T::CW>(mt, e, &om[c * T::CW / 4]);
-            store_codes<T::CW>(vt, e, &ov[c * T::CW / 4]);
+            if constexpr (TWO) store_codes<T::CW>(vt, e, &ov[c * T::CW / 4]);
         }
     } else {
 #pragma unroll
@@ -283,7 +336,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw8(TensorDesc single, Tile
             const uint32_t e = lofs + (i / T::CW) * T::LPB * T::CW + (i % T::CW);
             if ((int64_t)e < lrem) {
                 gsto<uint8_t>(mt, e, (uint8_t)(om[i >> 2] >> (8 * (i & 3))));
-                gsto<uint8_t>(vt, e, (uint8_t)(ov[i >> 2] >> (8 * (i & 3))));
+                if constexpr (TWO) gsto<uint8_t>(vt, e, (uint8_t)(ov[i >> 2] >> (8 * (i & 3))));
             }
         }
     }
@@ -297,43 +350,59 @@ int64_t adamw_tiles(int64_t n, int B)
 
 namespace {
 
-template <int B, int GDT>
-hipError_t adamw_as(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, const AdamScalars& hs,
+template <int OPT, int B, int GDT>
+hipError_t optim_as(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, const OptScalars& hs,
                     const QbTables* tab, hipStream_t s)
 {
     static_assert(TileA<B>::ELEMS == kAdamThreads * (B >= 4 * kAdamThreads ? B / kAdamThreads : 4), "tile size");
     if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    if (map) return launch_kernel_nt(k_adamw8<B, GDT, true>, (int)ntiles, kAdamThreads, s, single, *map, hs, tab);
-    return launch_kernel_nt(k_adamw8<B, GDT, false>, (int)ntiles, kAdamThreads, s, single, TileMap<TensorDesc>{}, hs, tab);
+    if (map)
+        return launch_kernel_nt(k_optim8<OPT, B, GDT, true>, (int)ntiles, kAdamThreads, s, single, *map, hs, tab);
+    return launch_kernel_nt(k_optim8<OPT, B, GDT, false>, (int)ntiles, kAdamThreads, s, single,
+                            TileMap<TensorDesc>{}, hs, tab);
 }
 
-template <int B>
-hipError_t adamw_dt(int gdt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, const AdamScalars& hs,
-                    const QbTables* tab, hipStream_t s)
+template <int OPT, int B>
+hipError_t optim_dt(int gdt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles,
+                    const OptScalars& hs, const QbTables* tab, hipStream_t s)
 {
     switch (gdt) {
-    case DT_F32: return adamw_as<B, DT_F32>(single, map, ntiles, hs, tab, s);
-    case DT_F16: return adamw_as<B, DT_F16>(single, map, ntiles, hs, tab, s);
-    case DT_BF16: return adamw_as<B, DT_BF16>(single, map, ntiles, hs, tab, s);
+    case DT_F32: return optim_as<OPT, B, DT_F32>(single, map, ntiles, hs, tab, s);
+    case DT_F16: return optim_as<OPT, B, DT_F16>(single, map, ntiles, hs, tab, s);
+    case DT_BF16: return optim_as<OPT, B, DT_BF16>(single, map, ntiles, hs, tab, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OPT>
+hipError_t optim_b(int B, int gdt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles,
+                   const OptScalars& hs, const QbTables* tab, hipStream_t s)
+{
+    switch (B) {
+    case 64: return optim_dt<OPT, 64>(gdt, single, map, ntiles, hs, tab, s);
+    case 128: return optim_dt<OPT, 128>(gdt, single, map, ntiles, hs, tab, s);
+    case 256: return optim_dt<OPT, 256>(gdt, single, map, ntiles, hs, tab, s);
+    case 512: return optim_dt<OPT, 512>(gdt, single, map, ntiles, hs, tab, s);
+    case 1024: return optim_dt<OPT, 1024>(gdt, single, map, ntiles, hs, tab, s);
+    case 2048: return optim_dt<OPT, 2048>(gdt, single, map, ntiles, hs, tab, s);
+    case 4096: return optim_dt<OPT, 4096>(gdt, single, map, ntiles, hs, tab, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_adamw8(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B, int gdt,
-                         const AdamScalars& hs, hipStream_t s)
+hipError_t launch_optim8(int opt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B,
+                         int gdt, const OptScalars& hs, hipStream_t s)
 {
     const QbTables* tab = device_tables();
     if (!tab) return hipErrorNotInitialized;
-    switch (B) {
-    case 64: return adamw_dt<64>(gdt, single, map, ntiles, hs, tab, s);
-    case 128: return adamw_dt<128>(gdt, single, map, ntiles, hs, tab, s);
-    case 256: return adamw_dt<256>(gdt, single, map, ntiles, hs, tab, s);
-    case 512: return adamw_dt<512>(gdt, single, map, ntiles, hs, tab, s);
-    case 1024: return adamw_dt<1024>(gdt, single, map, ntiles, hs, tab, s);
-    case 2048: return adamw_dt<2048>(gdt, single, map, ntiles, hs, tab, s);
-    case 4096: return adamw_dt<4096>(gdt, single, map, ntiles, hs, tab, s);
+    switch (opt) {
+    case OPT_ADAMW: return optim_b<OPT_ADAMW>(B, gdt, single, map, ntiles, hs, tab, s);
+    case OPT_ADAM: return optim_b<OPT_ADAM>(B, gdt, single, map, ntiles, hs, tab, s);
+    case OPT_LION: return optim_b<OPT_LION>(B, gdt, single, map, ntiles, hs, tab, s);
+    case OPT_SGD: return optim_b<OPT_SGD>(B, gdt, single, map, ntiles, hs, tab, s);
+    case OPT_RMSPROP: return optim_b<OPT_RMSPROP>(B, gdt, single, map, ntiles, hs, tab, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -99,7 +99,47 @@ typedef struct {
     int32_t step;
 } qb_adamw_hparams;
 
-/* One tensor of a multi-tensor step; the fields are those of qb_adamw8bit_step. */
+/*
+ * The fused 8-bit optimizers.  The pages list 8-bit Adam, AdamW, SGD, RMSprop
+ * and Lion as drop-in replacements that keep their optimizer's
+ * hyperparameters (page "bitsandbytes深度解析", section 优化器模块深度分析; page
+ * "Py之bitsandbytes", sections 1 and 使用8位优化器).  Each follows its usual
+ * definition, every state tensor held as block-wise QB_DYN8 codes with one fp32
+ * absmax per block (state 1; state 2 for the two-state kinds):
+ *   QB_ADAMW    state 1 = m, state 2 = v; decoupled weight decay (as
+ *               qb_adamw8bit_step).
+ *   QB_ADAM     state 1 = m, state 2 = v; L2 decay: g <- g + wd*p, then the
+ *               bias-corrected Adam update.
+ *   QB_LION     state 1 = m:  c = b1*m + (1-b1)*g;  p <- p*(1-lr*wd) - lr*sign(c);
+ *               m <- b2*m + (1-b2)*g.
+ *   QB_SGD      state 1 = momentum buffer (beta1 = momentum, in (0, 1)):
+ *               g <- g + wd*p; buf <- g at step 1, else momentum*buf +
+ *               (1-dampening)*g; p <- p - lr*(nesterov ? g + momentum*buf : buf).
+ *   QB_RMSPROP  state 1 = v (beta2 = alpha):  g <- g + wd*p;
+ *               v <- alpha*v + (1-alpha)*g*g;  p <- p - lr*g/(sqrt(v) + eps).
+ * The states and their codes are bit-exact against an IEEE binary32 evaluation
+ * of these formulas (each operation rounded on its own, IEEE square root and
+ * division).  So is p' for every kind but AdamW, whose states never read p:
+ * there p' takes hardware square root and reciprocal and is within 1e-6
+ * relative.
+ */
+typedef enum { QB_ADAMW = 0, QB_ADAM = 1, QB_LION = 2, QB_SGD = 3, QB_RMSPROP = 4 } qb_optimizer;
+
+/* Hyperparameters of one step of any kind (unused fields are ignored). */
+typedef struct {
+    qb_optimizer kind;
+    double  lr;
+    double  beta1;         /* Adam(W), Lion: beta1; SGD: momentum */
+    double  beta2;         /* Adam(W), Lion: beta2; RMSprop: alpha */
+    double  eps;           /* Adam(W), RMSprop */
+    double  weight_decay;
+    double  dampening;     /* SGD */
+    int32_t nesterov;      /* SGD: 0 or 1 (1 needs dampening 0) */
+    int32_t step;          /* t >= 1 */
+} qb_optim_hparams;
+
+/* One tensor of a multi-tensor step; the fields are those of qb_adamw8bit_step
+ * (m, absmax_m: state 1; v, absmax_v: state 2, ignored by one-state kinds). */
 typedef struct {
     float*      p;
     const void* g;
@@ -245,8 +285,29 @@ qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, ui
 qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
                                const qb_adamw_hparams* hp, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * qb_optimizer8bit_step -- one fused 8-bit step of optimizer hp->kind (see
+ * qb_optimizer above) on one tensor.  Arguments as qb_adamw8bit_step, with
+ * state1/absmax1 in place of m/absmax_m and state2/absmax2 in place of
+ * v/absmax_v; state2 and absmax2 are ignored (may be NULL) for the one-state
+ * kinds.  Fresh state: every code 127 (0.0), absmax 0.  Invalid
+ * hyperparameters for the kind (ranges above; lr, weight_decay >= 0) give
+ * QB_EINVAL before anything is launched.
+ */
+qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void* g, qb_dtype gdt, int64_t n,
+                                uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,
+                                int32_t blocksize, void* stream);
+
+/*
+ * qb_multi_tensor_optimizer_step -- qb_optimizer8bit_step on `count` tensors in
+ * one kernel launch; tensors, ws as for qb_multi_tensor_step.
+ */
+qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
+                                         qb_dtype gdt, int32_t blocksize, void* ws, size_t ws_bytes,
+                                         void* stream);
+
 /* Workspace sizes (bytes) for qb_quantize with nesting, and for
- * qb_multi_tensor_step and qb_multi_tensor_dequantize. */
+ * qb_multi_tensor_step, qb_multi_tensor_optimizer_step and qb_multi_tensor_dequantize. */
 size_t qb_dq_workspace_bytes(int64_t n, int32_t blocksize);
 size_t qb_multi_tensor_workspace_bytes(int32_t count);
 

@@ -202,6 +202,43 @@ def test_grouped_quantize_arguments_rejected_before_launch(qb):
     assert f(tab(neg), 1, 0, 0, 64, 256, A, ws, None) == qb.QB_EINVAL
 
 
+def test_optimizer_hyperparameters_rejected_before_launch(qb):
+    L = qb.lib()
+    A, A2 = 0x100000, 0x200000
+    f = L.qb_optimizer8bit_step
+
+    def call(hp, s2=A, a2=A, n=100):
+        return f(ctypes.byref(hp), A, A2, 2, n, A, s2, A, a2, 2048, None)
+
+    H = qb.optim_hparams
+    bad = [H(qb.QB_SGD, 0.1, beta1=0.0),                              # SGD needs momentum
+           H(qb.QB_SGD, 0.1, beta1=0.9, dampening=0.1, nesterov=True), # Nesterov needs zero dampening
+           H(qb.QB_SGD, 0.1, beta1=0.9, dampening=1.5),
+           H(qb.QB_RMSPROP, 0.1, beta2=0.99, eps=0.0),
+           H(qb.QB_RMSPROP, 0.1, beta2=1.0),
+           H(qb.QB_LION, 0.1, beta1=1.0),
+           H(qb.QB_ADAM, 0.1, eps=-1.0),
+           H(qb.QB_ADAM, -0.1),                                        # lr < 0
+           H(qb.QB_LION, 0.1, weight_decay=-1.0),
+           H(qb.QB_LION, 0.1, step=0),
+           H(7, 0.1)]
+    for hp in bad:
+        assert call(hp) == qb.QB_EINVAL, (hp.kind, hp.beta1, hp.beta2, hp.eps, hp.dampening, hp.nesterov)
+    assert f(None, A, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EINVAL
+    # two-state kinds need state 2; zero length is a no-op for every kind
+    assert call(H(qb.QB_ADAM, 1e-3), s2=None) == qb.QB_EINVAL
+    assert call(H(qb.QB_ADAM, 1e-3), a2=A + 4) == qb.QB_EALIGN
+    for k in (qb.QB_ADAMW, qb.QB_ADAM, qb.QB_LION, qb.QB_SGD, qb.QB_RMSPROP):
+        assert call(H(k, 1e-3), s2=None, a2=None, n=0) == qb.QB_OK
+    tab = (qb.qb_tensor * 1)(qb.qb_tensor(A, A2, A, None, A, None, 100))
+    m = L.qb_multi_tensor_optimizer_step
+    assert m(ctypes.byref(H(qb.QB_ADAM, 1e-3)), tab, 1, 2, 2048, A, L.qb_multi_tensor_workspace_bytes(1),
+             None) == qb.QB_EINVAL                                     # Adam without state 2
+    assert m(ctypes.byref(H(qb.QB_SGD, 1e-3, beta1=0.0)), tab, 1, 2, 2048, A,
+             L.qb_multi_tensor_workspace_bytes(1), None) == qb.QB_EINVAL
+    assert m(ctypes.byref(H(qb.QB_LION, 1e-3)), tab, 1, 2, 2048, A, 8, None) == qb.QB_EWORKSPACE
+
+
 def test_status_strings(qb):
     assert qb.qb_status_string(0) == "ok"
     assert "workspace" in qb.qb_status_string(5)
