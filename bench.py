@@ -42,7 +42,7 @@ ADAM_BLOCK = 2048
 W4_BLOCK, W4_BLOCK2 = 64, 256
 Q8_N, Q8_BLOCK = 268_435_456, 2048
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_adamw8_multi.llama7b_step.traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_optim8_adamw_multi.llama7b_step.traffic.json")
 
 
 def log(msg):
@@ -463,7 +463,7 @@ def main():
         },
         "components": comps,
         "roofline": {
-            "kernel": "k_adamw8<2048, bf16, multi-tensor>",
+            "kernel": "k_optim8<AdamW, 2048, bf16, multi-tensor>",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
