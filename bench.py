@@ -286,10 +286,15 @@ def bench_flat(torch, qb, inputs, dev, args):
     kind, hp, states = OPTIMIZERS[args.optimizer]
     log(f"allocating a flat buffer of {n:,} params ({args.optimizer}, {states} state(s))")
     p = inputs.normal(n, 0.02, seed=args.seed, device=dev)
-    s1 = torch.full((n,), 127, dtype=torch.uint8, device=dev)
-    a1 = torch.zeros(nb, device=dev)
-    s2 = torch.full((n,), 127, dtype=torch.uint8, device=dev) if states == 2 else None
-    a2 = torch.zeros(nb, device=dev) if states == 2 else None
+    if args.state_bits == 8:
+        s1 = torch.full((n,), 127, dtype=torch.uint8, device=dev)
+        a1 = torch.zeros(nb, device=dev)
+        s2 = torch.full((n,), 127, dtype=torch.uint8, device=dev) if states == 2 else None
+        a2 = torch.zeros(nb, device=dev) if states == 2 else None
+    else:                       # the 32-bit fallback: binary32 states, no absmax
+        s1 = torch.zeros(n, device=dev)
+        s2 = torch.zeros(n, device=dev) if states == 2 else None
+        a1 = a2 = None
     grads = [inputs.normal(n, 1e-3, inputs.grad_seed(args.seed, 0, k), device=dev, dtype=torch.bfloat16) for k in range(2)]
 
     def step(k):
@@ -309,10 +314,12 @@ def bench_flat(torch, qb, inputs, dev, args):
     wall = time.perf_counter() - t0
     ms = sorted(a.elapsed_time(b) for a, b in evs)
     med = ms[len(ms) // 2]
-    nbytes = n * optim_bytes_per_param(states)
+    bpp = optim_bytes_per_param(states) if args.state_bits == 8 else 8 + 2 + 8 * states
+    nbytes = n * bpp
     print(json.dumps({"workload": f"flat 1.5e9 fp32 params, bf16 grads, block 2048, single-tensor {args.optimizer} "
-                                  f"8-bit step", "optimizer": args.optimizer, "steps": args.steps, "median_ms": med,
-                      "bytes_per_param": optim_bytes_per_param(states), "GB/s": nbytes / med / 1e6,
+                                  f"step, {args.state_bits}-bit states", "optimizer": args.optimizer,
+                      "state_bits": args.state_bits, "steps": args.steps, "median_ms": med,
+                      "bytes_per_param": bpp, "GB/s": nbytes / med / 1e6,
                       "params_per_s": n / med * 1e3, "frac_of_hbm_peak": nbytes / med / 1e6 / HBM_PEAK_GBS,
                       "wall_ms_per_step": wall / args.steps * 1e3}), flush=True)
 
@@ -342,6 +349,8 @@ def main():
                     help="time the single-tensor AdamW step on a flat 1.5e9-parameter buffer instead")
     ap.add_argument("--optimizer", choices=sorted(OPTIMIZERS), default="adamw",
                     help="optimizer of the --flat run (the 8-bit states of each kind)")
+    ap.add_argument("--state-bits", type=int, choices=(8, 32), default=8,
+                    help="state width of the --flat run (32: the binary32 fallback of small or chosen tensors)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device five times (the reference kernel for HBM counters)")
     args = ap.parse_args()

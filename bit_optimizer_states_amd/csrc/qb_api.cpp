@@ -83,6 +83,20 @@ qb_optim_hparams as_optim(const qb_adamw_hparams* hp)
 
 int optim_states(qb_optimizer k) { return (k == QB_ADAMW || k == QB_ADAM) ? 2 : 1; }
 
+// Checks one tensor of an optimizer step.  absmax1 == NULL selects binary32
+// states (state1, state2 are float arrays; absmax2 must be NULL too).
+qb_status check_optim_tensor(bool two, const float* p, const void* g, const void* s1, const void* s2,
+                             const float* a1, const float* a2)
+{
+    const bool s32 = a1 == nullptr;
+    if (!p || !g || !s1 || (two && !s2)) return QB_EINVAL;
+    if (two && (s32 ? a2 != nullptr : a2 == nullptr)) return QB_EINVAL;
+    if ((const void*)p == g) return QB_EINVAL;
+    if (!aligned16(p) || !aligned16(g) || !aligned16(s1) || (two && !aligned16(s2))) return QB_EALIGN;
+    if (!s32 && (!aligned16(a1) || (two && !aligned16(a2)))) return QB_EALIGN;
+    return QB_OK;
+}
+
 // beta^t by t repeated binary64 multiplications.  Consecutive steps of the
 // same beta reuse the previous power, so a training loop pays one multiply.
 double beta_power(double beta, int32_t t, int slot)
@@ -482,11 +496,8 @@ qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void
         absmax2 = nullptr;
     }
     if (nblocks(n, blocksize) >= (int64_t(1) << 31)) return QB_EINVAL;
-    if (!p || !g || !state1 || !absmax1 || (two && (!state2 || !absmax2))) return QB_EINVAL;
-    if ((const void*)p == g) return QB_EINVAL;
-    if (!aligned16(p) || !aligned16(g) || !aligned16(state1) || !aligned16(absmax1) ||
-        (two && (!aligned16(state2) || !aligned16(absmax2))))
-        return QB_EALIGN;
+    qb_status st = check_optim_tensor(two, p, g, state1, state2, absmax1, absmax2);
+    if (st != QB_OK) return st;
     if (!device_tables()) return QB_EINIT;
     TensorDesc d{p, g, state1, state2, absmax1, absmax2, n, 0};
     return hip_status(launch_optim8((int)hp->kind, d, nullptr, adamw_tiles(n, blocksize), blocksize, (int)gdt,
@@ -510,11 +521,8 @@ qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_te
         if (t.n < 0) return QB_EINVAL;
         if (t.n == 0) continue;
         if (nblocks(t.n, blocksize) >= (int64_t(1) << 31)) return QB_EINVAL;
-        if (!t.p || !t.g || !t.m || !t.absmax_m || (two && (!t.v || !t.absmax_v))) return QB_EINVAL;
-        if ((const void*)t.p == t.g) return QB_EINVAL;
-        if (!aligned16(t.p) || !aligned16(t.g) || !aligned16(t.m) || !aligned16(t.absmax_m) ||
-            (two && (!aligned16(t.v) || !aligned16(t.absmax_v))))
-            return QB_EALIGN;
+        qb_status st = check_optim_tensor(two, t.p, t.g, t.m, t.v, t.absmax_m, t.absmax_v);
+        if (st != QB_OK) return st;
         table.push_back(TensorDesc{t.p, t.g, t.m, two ? t.v : nullptr, t.absmax_m, two ? t.absmax_v : nullptr, t.n,
                                    tiles});
         tiles += adamw_tiles(t.n, blocksize);

@@ -47,6 +47,7 @@ constexpr int kAdamThreads = QB_ADAM_THREADS;
 
 template <int B>
 struct TileA {
+    static constexpr int BS = B;                                         // block size
     static constexpr int NT = kAdamThreads;
     static constexpr int EPT = B >= 4 * NT ? B / NT : 4;
     static constexpr int CW = (QB_ADAM_CHUNK == 8 && EPT % 8 == 0) ? 8 : 4;   // elements per chunk
@@ -168,6 +169,68 @@ __device__ __forceinline__ void opt_elem(const OptScalars& hs, float gi, float& 
     }
 }
 
+// A tile of a tensor whose states stay binary32 (the 32-bit fallback for small
+// or chosen tensors: d.am == nullptr, d.m / d.v are float arrays).  The same
+// element update, with no codes and no block absmax.
+template <int OPT, class T, int GDT>
+__device__ __forceinline__ void optim32_tile(const TensorDesc& d, int64_t lt, const OptScalars& hs, int tid)
+{
+    constexpr bool TWO = opt_states(OPT) == 2;
+    const int bt = tid / T::LPB, l = tid % T::LPB;
+    const int64_t tbase = lt * T::ELEMS;
+    float* const pt = d.p + tbase;
+    const void* const gt = static_cast<const char*>(d.g) + tbase * (GDT == DT_F32 ? 4 : 2);
+    float* const xt = reinterpret_cast<float*>(d.m) + tbase;
+    float* const yt = TWO ? reinterpret_cast<float*>(d.v) + tbase : nullptr;
+    const uint32_t lofs = (uint32_t)(bt * T::BS + l * T::CW);
+    const int64_t lrem = d.n - tbase;
+    const bool full = T::ELEMS <= lrem;
+    float p[T::EPT], g[T::EPT], x[T::EPT], y[T::EPT];
+    if (full) {
+#pragma unroll
+        for (int c = 0; c < T::CH; ++c) {
+            const uint32_t e = lofs + c * T::LPB * T::CW;
+            load_chunk<DT_F32, T::CW>(pt, e, &p[c * T::CW]);
+            load_chunk<GDT, T::CW>(gt, e, &g[c * T::CW]);
+            load_chunk<DT_F32, T::CW>(xt, e, &x[c * T::CW]);
+            if constexpr (TWO) load_chunk<DT_F32, T::CW>(yt, e, &y[c * T::CW]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < T::EPT; ++i) {
+            const uint32_t e = lofs + (i / T::CW) * T::LPB * T::CW + (i % T::CW);
+            const bool in = (int64_t)e < lrem;
+            p[i] = in ? load1<DT_F32>(pt, e) : 0.0f;
+            g[i] = in ? load1<GDT>(gt, e) : 0.0f;
+            x[i] = in ? load1<DT_F32>(xt, e) : 0.0f;
+            y[i] = (TWO && in) ? load1<DT_F32>(yt, e) : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < T::EPT; ++i) opt_elem<OPT>(hs, g[i], p[i], x[i], y[i]);
+    if (full) {
+#pragma unroll
+        for (int c = 0; c < T::CH; ++c)
+#pragma unroll
+            for (int h = 0; h < T::CW; h += 4) {
+                const uint32_t e = lofs + c * T::LPB * T::CW + h;
+                store4o<DT_F32>(pt, e, &p[c * T::CW + h]);
+                store4o<DT_F32>(xt, e, &x[c * T::CW + h]);
+                if constexpr (TWO) store4o<DT_F32>(yt, e, &y[c * T::CW + h]);
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < T::EPT; ++i) {
+            const uint32_t e = lofs + (i / T::CW) * T::LPB * T::CW + (i % T::CW);
+            if ((int64_t)e < lrem) {
+                gsto<float>(pt, e * 4u, p[i]);
+                gsto<float>(xt, e * 4u, x[i]);
+                if constexpr (TWO) gsto<float>(yt, e * 4u, y[i]);
+            }
+        }
+    }
+}
+
 template <int OPT, int B, int GDT, bool MULTI>
 __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, TileMap<TensorDesc> map, OptScalars hs,
                                                          const QbTables* __restrict__ tab)
@@ -189,6 +252,10 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
     } else {
         d = single;
         lt = tile;
+    }
+    if (d.am == nullptr) {                                 // binary32 states (uniform per workgroup)
+        optim32_tile<OPT, T, GDT>(d, lt, hs, tid);
+        return;
     }
     const int bt = tid / T::LPB, l = tid % T::LPB;
     const int64_t nloc = d.n;

@@ -293,6 +293,13 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
  * kinds.  Fresh state: every code 127 (0.0), absmax 0.  Invalid
  * hyperparameters for the kind (ranges above; lr, weight_decay >= 0) give
  * QB_EINVAL before anything is launched.
+ * 32-bit fallback: with absmax1 == NULL (and absmax2 == NULL) the states stay
+ * binary32: state1 / state2 are float[n] arrays updated in place by the same
+ * formulas, with no quantization.  This is the pages' policy for small or
+ * chosen tensors (page "Py之bitsandbytes", sections 如果需要高精度的参数 and
+ * 更改单个参数的位数: tensors under min_8bit_size elements, or marked 32-bit,
+ * keep 32-bit state).  The multi-tensor step takes the same per tensor, so one
+ * launch can mix 8-bit and 32-bit tensors.
  */
 qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void* g, qb_dtype gdt, int64_t n,
                                 uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,

@@ -164,3 +164,57 @@ def test_sgd_first_step_ignores_stale_state():
     st.oracle_step(g, 1, oracle.F32, hp)
     torch.cuda.synchronize()
     assert_equal_state(d, st, True, "sgd step 1")
+
+
+@pytest.mark.parametrize("name", ["adamw", "adam", "lion", "sgd", "rmsprop"])
+def test_mixed_8bit_and_32bit_states_in_one_launch(name):
+    """The 32-bit fallback: tensors under min_8bit_size (and one marked 32-bit)
+    keep binary32 states in the same multi-tensor launch.  Their states and
+    parameters are exactly the oracle's binary32 step (within 1e-6 for AdamW's
+    parameters); the 8-bit tensors as before."""
+    from bit_optimizer_states_amd import state as policy
+    kind, hp, exact_p = KINDS[name]
+    L = qb()
+    sizes = [4096, 100, 2048 * 5 + 3, 4095, 1, 30000]
+    B, gdt = 2048, oracle.BF16
+    rng = np.random.default_rng(kind + 5)
+    ps = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+    pd = [to_device(p) for p in ps]
+    states = policy.allocate(pd, kind, blocksize=B, min_8bit_size=4096, force_32bit={5})
+    eight = [policy.uses_8bit(n, 4096, i == 5) for i, n in enumerate(sizes)]
+    assert eight == [True, False, True, False, False, False]
+    two = oracle.OPTIMIZER_STATES[kind] == 2
+    host = []
+    for n, e in zip(sizes, eight):
+        nb = (n + B - 1) // B
+        if e:
+            host.append([np.full(n, 127, np.uint8), np.zeros(nb, np.float32), np.full(n, 127, np.uint8),
+                         np.zeros(nb, np.float32)])
+        else:
+            host.append([np.zeros(n, np.float32), None, np.zeros(n, np.float32), None])
+    ws = torch.empty(L.qb_multi_tensor_workspace_bytes(len(sizes)), dtype=torch.uint8, device=DEV)
+    for step in range(1, 4):
+        gs = [grad(n, 900 + 10 * i + step, gdt) for i, n in enumerate(sizes)]
+        gd = [to_device(g, TORCH_DT[gdt]) for g in gs]
+        table = L.tensor_table([(p, g, s1, s2, a1, a2) for p, g, (s1, s2, a1, a2) in zip(pd, gd, states)])
+        L.qb_multi_tensor_optimizer_step(lib_hp(kind, hp, step), table, len(sizes), L.QB_BF16, B, ws)
+        for p, g, h, e in zip(ps, gs, host, eight):
+            if e:
+                oracle.optim8bit_step(kind, p, g, h[0], h[1], h[2] if two else None, h[3] if two else None, B,
+                                      step=step, gdt=gdt, **hp)
+            else:
+                oracle.optim32_step(kind, p, g, h[0], h[2] if two else None, step=step, gdt=gdt, **hp)
+        torch.cuda.synchronize()
+        for i, (p, h, e, (s1, s2, a1, a2)) in enumerate(zip(ps, host, eight, states)):
+            got_p = host_bits(pd[i])
+            if exact_p:
+                assert np.array_equal(got_p.view(np.uint32), p.view(np.uint32)), (name, step, i)
+            else:
+                np.testing.assert_allclose(got_p, p, rtol=1e-6, atol=1e-6 * 0.02)
+            assert np.array_equal(host_bits(s1).view(np.uint8), h[0].view(np.uint8)), (name, step, i, "state 1")
+            if two:
+                assert np.array_equal(host_bits(s2).view(np.uint8), h[2].view(np.uint8)), (name, step, i, "state 2")
+            if e:
+                assert np.array_equal(host_bits(a1).view(np.uint32), h[1].view(np.uint32))
+                if two:
+                    assert np.array_equal(host_bits(a2).view(np.uint32), h[3].view(np.uint32))

@@ -237,6 +237,11 @@ def test_optimizer_hyperparameters_rejected_before_launch(qb):
     assert m(ctypes.byref(H(qb.QB_SGD, 1e-3, beta1=0.0)), tab, 1, 2, 2048, A,
              L.qb_multi_tensor_workspace_bytes(1), None) == qb.QB_EINVAL
     assert m(ctypes.byref(H(qb.QB_LION, 1e-3)), tab, 1, 2, 2048, A, 8, None) == qb.QB_EWORKSPACE
+    # 32-bit fallback (absmax NULL): both absmax pointers NULL or neither for the two-state kinds
+    assert f(ctypes.byref(H(qb.QB_ADAMW, 1e-3)), A, A2, 2, 100, A, A, None, A, 2048, None) == qb.QB_EINVAL
+    assert f(ctypes.byref(H(qb.QB_ADAMW, 1e-3)), A, A2, 2, 100, A, A, A, None, 2048, None) == qb.QB_EINVAL
+    assert f(ctypes.byref(H(qb.QB_ADAM, 1e-3)), A, A2, 2, 100, A, None, None, None, 2048, None) == qb.QB_EINVAL
+    assert f(ctypes.byref(H(qb.QB_SGD, 1e-3)), A, A2, 2, 100, A + 4, None, None, None, 2048, None) == qb.QB_EALIGN
 
 
 def test_status_strings(qb):
