@@ -46,6 +46,10 @@ def lib():
             "orc_adamw8bit_step": [vp, vp, i32, i64, vp, vp, vp, vp, i32, dp, dp, dp, dp, dp, i32],
             "orc_adam_scalars": [dp, dp, dp, dp, dp, i32, vp],
             "orc_optim32_step": [i32, vp, i32, vp, vp, i32, i64, vp, vp],
+            "orc_linear_codebook": [vp],
+            "orc_quantize_custom": [vp, i32, i64, vp, i32, vp, vp],
+            "orc_dequantize_custom": [vp, vp, vp, i32, i64, vp, i32],
+            "orc_estimate_quantiles": [vp, i32, i64, i32, vp],
             "orc_optim8bit_step": [i32, vp, i32, vp, vp, i32, i64, vp, vp, vp, vp, i32],
         }
         for name, argtypes in sig.items():
@@ -266,6 +270,48 @@ def adamw8bit_step(p, g, cm, cv, am, av, blocksize, lr, beta1, beta2, eps, wd, s
     g = np.ascontiguousarray(g)
     _check(lib().orc_adamw8bit_step(_p(p), _p(g), gdt, p.size, _p(cm), _p(cv), _p(am), _p(av), blocksize,
                                     lr, beta1, beta2, eps, wd, step), "adamw8bit")
+
+
+# user codes (oracle.c, section "user codes")
+QUANTILE_CHUNK = 4096
+
+
+def linear_codebook():
+    out = np.zeros(256, dtype=np.float32)
+    _check(lib().orc_linear_codebook(_p(out)), "linear_codebook")
+    return out
+
+
+def quantize_custom(x, cb, blocksize, xdt=None):
+    """Block-wise quantization of x with the 256-entry ascending code cb."""
+    x = np.ascontiguousarray(x)
+    if xdt is None:
+        xdt = _dtype_id(x)
+    cb = np.ascontiguousarray(cb, dtype=np.float32)
+    n = x.size
+    codes = np.zeros(n, dtype=np.uint8)
+    absmax = np.zeros((n + blocksize - 1) // blocksize, dtype=np.float32)
+    _check(lib().orc_quantize_custom(_p(x), xdt, n, _p(cb), blocksize, _p(codes), _p(absmax)), "quantize_custom")
+    return codes, absmax
+
+
+def dequantize_custom(codes, scale, cb, blocksize, n, ydt=F32):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    cb = np.ascontiguousarray(cb, dtype=np.float32)
+    out = np.zeros(n, dtype=np.float32 if ydt == F32 else np.uint16)
+    _check(lib().orc_dequantize_custom(_p(codes), _p(scale), _p(cb), blocksize, n, _p(out), ydt), "dequantize_custom")
+    return out
+
+
+def estimate_quantiles(x, chunk=QUANTILE_CHUNK, xdt=None):
+    """The estimated quantile code of x (256 ascending entries, max |entry| 1)."""
+    x = np.ascontiguousarray(x)
+    if xdt is None:
+        xdt = _dtype_id(x)
+    out = np.zeros(256, dtype=np.float32)
+    _check(lib().orc_estimate_quantiles(_p(x), xdt, x.size, chunk, _p(out)), "estimate_quantiles")
+    return out
 
 
 # the sibling optimizers (oracle.c, section "the sibling 8-bit optimizers")

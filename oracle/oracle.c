@@ -259,9 +259,11 @@ static int sorted_table(int code, float* t)
  * arithmetic; a tie goes to the entry of smaller magnitude (toward zero).
  * Reading: the pages say only that values are mapped to the code; "nearest"
  * with ties toward zero is the plainest rule and keeps the encoder symmetric
- * under negation.  cb[k] <= x < cb[k+1] is found by bisection, then 2x is
- * compared with cb[k] + cb[k+1] in binary64, where both sides are exact
- * (adjacent entries are within a factor of 64 of each other, or one is 0).
+ * under negation (between entries of equal magnitude, such as -a and a, a tie
+ * goes to the upper one).  cb[k] <= x < cb[k+1] is found by bisection, then 2x
+ * is compared with cb[k] + cb[k+1] in binary64, where both sides are exact for
+ * the built-in codes (adjacent entries are within a factor of 64 of each
+ * other, or one is 0).
  */
 static int nearest_index(const float* cb, int K, float x)
 {
@@ -273,12 +275,12 @@ static int nearest_index(const float* cb, int K, float x)
         if (cb[mid] <= x) lo = mid; else hi = mid;
     }
     double a = cb[lo], b = cb[hi];
-    double sum = a + b;
-    if (sum - a != b) abort(); /* the binary64 sum must be exact */
+    double sum = a + b;           /* exact for the built-in codes; for a user code the
+                                     midpoint is read as computed in binary64 */
     double twice = 2.0 * (double)x;
     if (twice > sum) return hi;
     if (twice < sum) return lo;
-    return (fabs(a) <= fabs(b)) ? lo : hi;
+    return (fabs(a) < fabs(b)) ? lo : hi;   /* equal magnitudes: the upper entry */
 }
 
 /* Encode one normalized value x in [-1, 1] with code `code`. */
@@ -694,5 +696,98 @@ int orc_optim8bit_step(int kind, const double* hp, int step, float* p, const voi
     }
     free(xb);
     free(yb);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* user codes: the linear code and estimated quantile codes                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages list three 8-bit quantization types: quantile, linear and dynamic
+ * (page "Py之bitsandbytes", section 1), and a fast quantile estimation.
+ *
+ * Linear code (reading: the symmetric 8-bit integer grid scaled by 1/127):
+ * entries k/127 for k = -128 .. 127, ascending (index 128 is 0.0, 255 is 1.0).
+ */
+int orc_linear_codebook(float* out /* [256] */)
+{
+    for (int k = -128; k <= 127; k++) out[k + 128] = (float)((double)k / 127.0);
+    return 0;
+}
+
+/* Block-wise quantize / dequantize with a user code (256 ascending entries). */
+int orc_quantize_custom(const void* x, int xdt, int64_t n, const float* cb, int B, uint8_t* codes, float* absmax)
+{
+    for (int k = 0; k + 1 < 256; k++)
+        if (!(cb[k] <= cb[k + 1]) || !isfinite(cb[k]) || !isfinite(cb[k + 1])) return -1;
+    int64_t nb = (n + B - 1) / B;
+    for (int64_t b = 0; b < nb; b++) {
+        int64_t lo = b * B, hi = lo + B < n ? lo + B : n;
+        float a = 0.0f;
+        for (int64_t i = lo; i < hi; i++) {
+            float v = fabsf(load_elem(x, xdt, i));
+            if (v > a) a = v;
+        }
+        absmax[b] = a;
+        for (int64_t i = lo; i < hi; i++) {
+            float nv = (a > 0.0f) ? load_elem(x, xdt, i) / a : 0.0f;
+            codes[i] = (uint8_t)nearest_index(cb, 256, nv);
+        }
+    }
+    return 0;
+}
+
+int orc_dequantize_custom(const uint8_t* codes, const float* scale, const float* cb, int B, int64_t n, void* y,
+                          int ydt)
+{
+    for (int64_t i = 0; i < n; i++) store_elem(y, ydt, i, cb[codes[i]] * scale[i / B]);
+    return 0;
+}
+
+static int cmp_float_asc(const void* a, const void* b)
+{
+    float x = *(const float*)a, y = *(const float*)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * Quantile code estimated from data (reading of the pages' quantile
+ * quantization and fast quantile estimation): the code entries are the
+ * midpoints of adjacent quantiles at probabilities j/257, j = 0..256, of the
+ * data, normalized so that the largest magnitude is 1.  The quantiles are
+ * estimated fast by splitting x into chunks of C consecutive values (the last
+ * may be shorter), sorting each chunk on its own and averaging the chunks'
+ * order statistics:
+ *   E_j(chunk of L sorted values s) = s[floor(j * L / 257)],
+ *   A_j = (sum over chunks, in chunk order, of E_j) / nchunks       (binary64),
+ *   q_i = (A_i + A_{i+1}) / 2,  i = 0..255                           (binary64),
+ *   code_i = binary32(q_i / max_k |q_k|)   (all 0 when max_k |q_k| = 0).
+ * The entries come out ascending (A is non-decreasing); equal neighbours are
+ * possible.
+ */
+int orc_estimate_quantiles(const void* x, int xdt, int64_t n, int C, float* out /* [256] */)
+{
+    if (n < 1 || C < 257) return -1;
+    int64_t nch = (n + C - 1) / C;
+    double acc[257];
+    for (int j = 0; j < 257; j++) acc[j] = 0.0;
+    float* s = (float*)malloc(sizeof(float) * (size_t)C);
+    if (!s) return -1;
+    for (int64_t c = 0; c < nch; c++) {
+        int64_t lo = c * C, hi = lo + C < n ? lo + C : n;
+        int L = (int)(hi - lo);
+        for (int i = 0; i < L; i++) s[i] = load_elem(x, xdt, lo + i);
+        qsort(s, (size_t)L, sizeof(float), cmp_float_asc);
+        for (int j = 0; j < 257; j++) acc[j] += (double)s[(int64_t)j * L / 257];
+    }
+    free(s);
+    double A[257], q[256], m = 0.0;
+    for (int j = 0; j < 257; j++) A[j] = acc[j] / (double)nch;
+    for (int i = 0; i < 256; i++) {
+        q[i] = (A[i] + A[i + 1]) * 0.5;
+        if (fabs(q[i]) > m) m = fabs(q[i]);
+    }
+    for (int i = 0; i < 256; i++) out[i] = m > 0.0 ? (float)(q[i] / m) : 0.0f;
     return 0;
 }
