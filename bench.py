@@ -324,6 +324,34 @@ def bench_flat(torch, qb, inputs, dev, args):
                       "wall_ms_per_step": wall / args.steps * 1e3}), flush=True)
 
 
+def bench_codes(torch, qb, inputs, dev, args):
+    """User codes on the 268,435,456-value Student-t tensor (block 2048): the
+    quantile code estimated from the data, then quantize + fp32 dequantize with
+    it; the linear code's round trip for comparison."""
+    n = Q8_N
+    x = inputs.student_t3(n, 0.02, seed=args.seed * 31 + 2, device=dev)
+    codes = torch.empty(n, dtype=torch.uint8, device=dev)
+    absmax = torch.empty(n // Q8_BLOCK, device=dev)
+    y = torch.empty_like(x)
+    tq = torch.empty(qb.qb_code_table_bytes(), dtype=torch.uint8, device=dev)
+    tl = torch.empty_like(tq)
+    qb.qb_prepare_code(qb.qb_linear_code(), tl)
+    ws = torch.empty(qb.qb_quantile_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    parts = {
+        "estimate_quantiles": (lambda: qb.qb_estimate_quantiles(x, n, tq, ws), n * 4.0),
+        "quantize_quantile_code": (lambda: qb.qb_quantize_code(x, n, tq, Q8_BLOCK, codes, absmax), n * (5 + 4 / Q8_BLOCK)),
+        "dequantize_quantile_code": (lambda: qb.qb_dequantize_code(codes, absmax, tq, Q8_BLOCK, n, y),
+                                     n * (5 + 4 / Q8_BLOCK)),
+        "quantize_linear_code": (lambda: qb.qb_quantize_code(x, n, tl, Q8_BLOCK, codes, absmax), n * (5 + 4 / Q8_BLOCK)),
+    }
+    out = {"workload": "268,435,456 fp32 values ~0.02 * Student-t(3), block 2048, user codes", "n": n}
+    for name, (fn, nbytes) in parts.items():
+        ms = time_calls(torch, fn, reps=args.steps)
+        out[name] = {"ms": ms, "GB/s": nbytes / ms / 1e6, "frac_of_hbm_peak": nbytes / ms / 1e6 / HBM_PEAK_GBS,
+                     "elements_per_s": n / ms * 1e3}
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration(torch, dev):
     """Five device-to-device copies of exactly 1 GiB: 1,073,741,824 bytes read and
     written per dispatch.  Profiling this under FETCH_SIZE / WRITE_SIZE gives the
@@ -351,6 +379,8 @@ def main():
                     help="optimizer of the --flat run (the 8-bit states of each kind)")
     ap.add_argument("--state-bits", type=int, choices=(8, 32), default=8,
                     help="state width of the --flat run (32: the binary32 fallback of small or chosen tensors)")
+    ap.add_argument("--codes", action="store_true",
+                    help="time the user-code calls (quantile estimation, quantile and linear codes) instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device five times (the reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -372,6 +402,8 @@ def main():
     rng = np.random.default_rng(args.seed)
     if args.flat:
         return bench_flat(torch, qb, inputs, dev, args)
+    if args.codes:
+        return bench_codes(torch, qb, inputs, dev, args)
     model = Model7B(torch, qb, inputs, dev, args.seed, with_w4=not args.adam_only)
     torch.cuda.synchronize()
     log(f"setup done; warmup {args.warmup} steps")

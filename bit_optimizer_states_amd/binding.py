@@ -83,12 +83,23 @@ def lib():
                                             vp]
         L.qb_multi_tensor_optimizer_step.argtypes = [ctypes.POINTER(qb_optim_hparams), ctypes.POINTER(qb_tensor), i32,
                                                      i32, i32, vp, sz, vp]
+        L.qb_code_table_bytes.argtypes = []
+        L.qb_code_table_bytes.restype = sz
+        L.qb_linear_code.argtypes = [vp]
+        L.qb_linear_code.restype = i32
+        L.qb_prepare_code.argtypes = [vp, vp, vp]
+        L.qb_quantile_workspace_bytes.argtypes = [i64]
+        L.qb_quantile_workspace_bytes.restype = sz
+        L.qb_estimate_quantiles.argtypes = [vp, i32, i64, vp, vp, sz, vp]
+        L.qb_quantize_code.argtypes = [vp, i32, i64, vp, i32, vp, vp, vp]
+        L.qb_dequantize_code.argtypes = [vp, vp, vp, i32, i64, vp, i32, vp]
         L.qb_multi_tensor_quantize.argtypes = [ctypes.POINTER(qb_quant_tensor), i32, i32, i32, i32, i32, vp, sz, vp]
         L.qb_multi_tensor_quantize_workspace_bytes.argtypes = [ctypes.POINTER(qb_quant_tensor), i32, i32]
         L.qb_multi_tensor_quantize_workspace_bytes.restype = sz
         for f in (L.qb_quantize, L.qb_dequantize, L.qb_adamw8bit_step, L.qb_multi_tensor_step,
                   L.qb_multi_tensor_dequantize, L.qb_multi_tensor_quantize, L.qb_optimizer8bit_step,
-                  L.qb_multi_tensor_optimizer_step):
+                  L.qb_multi_tensor_optimizer_step, L.qb_prepare_code, L.qb_estimate_quantiles, L.qb_quantize_code,
+                  L.qb_dequantize_code):
             f.restype = ctypes.c_int
         L.qb_dq_workspace_bytes.argtypes = [i64, i32]
         L.qb_dq_workspace_bytes.restype = sz
@@ -245,6 +256,42 @@ def qb_multi_tensor_dequantize(table, count, code, blocksize, blocksize2, ydt, w
     _check(lib().qb_multi_tensor_dequantize(table, int(count), int(code), int(blocksize), int(blocksize2), int(ydt),
                                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "qb_multi_tensor_dequantize")
+
+
+def qb_code_table_bytes():
+    return lib().qb_code_table_bytes()
+
+
+def qb_linear_code():
+    """Host list of the linear code's 256 entries."""
+    out = (ctypes.c_float * 256)()
+    lib().qb_linear_code(out)
+    return list(out)
+
+
+def qb_prepare_code(values, table, stream=None):
+    """values: 256 host floats (ascending); table: device byte tensor of qb_code_table_bytes()."""
+    arr = (ctypes.c_float * 256)(*[float(v) for v in values])
+    _check(lib().qb_prepare_code(arr, _ptr(table), _stream(stream)), "qb_prepare_code")
+
+
+def qb_quantile_workspace_bytes(n):
+    return lib().qb_quantile_workspace_bytes(int(n))
+
+
+def qb_estimate_quantiles(x, n, table, ws, stream=None):
+    _check(lib().qb_estimate_quantiles(_ptr(x), _dtype(x), int(n), _ptr(table), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)), "qb_estimate_quantiles")
+
+
+def qb_quantize_code(x, n, table, blocksize, codes, absmax, stream=None):
+    _check(lib().qb_quantize_code(_ptr(x), _dtype(x), int(n), _ptr(table), int(blocksize), _ptr(codes), _ptr(absmax),
+                                  _stream(stream)), "qb_quantize_code")
+
+
+def qb_dequantize_code(codes, absmax, table, blocksize, n, y, stream=None):
+    _check(lib().qb_dequantize_code(_ptr(codes), _ptr(absmax), _ptr(table), int(blocksize), int(n), _ptr(y),
+                                    _dtype(y), _stream(stream)), "qb_dequantize_code")
 
 
 def qb_codebook(code):

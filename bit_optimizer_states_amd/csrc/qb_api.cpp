@@ -484,6 +484,86 @@ qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t c
                                      blocksize, mode == 1 ? blocksize2 : 256, mode == 1, (int)ydt, s));
 }
 
+size_t qb_code_table_bytes(void) { return sizeof(UserCode); }
+
+int32_t qb_linear_code(float* out)
+{
+    if (!out) return -1;
+    linear_code(out);
+    return 256;
+}
+
+qb_status qb_prepare_code(const float* values, void* table, void* stream)
+{
+    if (!values || !table) return QB_EINVAL;
+    if (!aligned16(table)) return QB_EALIGN;
+    thread_local UserCode staged;
+    std::memcpy(staged.values, values, sizeof(staged.values));
+    if (user_code_thresholds(staged.values, staged.thr) != 0) return QB_EINVAL;
+    // from pageable memory: the copy has read `staged` when hipMemcpyAsync returns
+    return hipMemcpyAsync(table, &staged, sizeof(staged), hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? QB_OK
+               : QB_EHIP;
+}
+
+qb_status qb_quantize_code(const void* x, qb_dtype xdt, int64_t n, const void* table, int32_t blocksize,
+                           uint8_t* codes, float* absmax, void* stream)
+{
+    if (n < 0 || !valid_dtype(xdt) || !pow2_block(blocksize)) return QB_EINVAL;
+    if (n == 0) return QB_OK;
+    if (!table) return QB_EINVAL;
+    if (!aligned16(table)) return QB_EALIGN;
+    int nested = 0;
+    qb_status st = check_quant_tensor(x, codes, absmax, nullptr, nullptr, nullptr, n, blocksize, 0, &nested);
+    if (st != QB_OK) return st;
+    return hip_status(launch_quant_user(QuantDesc{x, codes, absmax, nullptr, n, 0, {0, 0}}, quant_tiles(n, blocksize),
+                                        blocksize, (int)xdt, static_cast<const UserCode*>(table),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+qb_status qb_dequantize_code(const uint8_t* codes, const float* absmax, const void* table, int32_t blocksize,
+                             int64_t n, void* y, qb_dtype ydt, void* stream)
+{
+    if (n < 0 || !valid_dtype(ydt) || !pow2_block(blocksize)) return QB_EINVAL;
+    if (n == 0) return QB_OK;
+    if (!table) return QB_EINVAL;
+    if (!aligned16(table)) return QB_EALIGN;
+    int mode = 0;
+    DequantDesc d;
+    qb_status st = dequant_desc(codes, absmax, nullptr, nullptr, nullptr, 0, n, y, blocksize, &mode, &d);
+    if (st != QB_OK) return st;
+    return hip_status(launch_dequant_user(d, dequant_tiles(n, dequant_tile_elems(8, false)), blocksize, (int)ydt,
+                                          static_cast<const UserCode*>(table), static_cast<hipStream_t>(stream)));
+}
+
+size_t qb_quantile_workspace_bytes(int64_t n)
+{
+    // the chunks' order statistics (float [257][nchunks]), then the group sums
+    // (double [257][ngroups], groups of 256 chunks)
+    if (n <= 0) return 0;
+    const int64_t nchunks = (n + kQuantileChunk - 1) / kQuantileChunk;
+    const int64_t ngroups = (nchunks + 255) / 256;
+    return round_up((size_t)nchunks * 257 * sizeof(float), 256) + (size_t)ngroups * 257 * sizeof(double);
+}
+
+qb_status qb_estimate_quantiles(const void* x, qb_dtype xdt, int64_t n, void* table, void* ws, size_t ws_bytes,
+                                void* stream)
+{
+    if (n < 1 || !valid_dtype(xdt)) return QB_EINVAL;
+    if (!x || !table || !ws) return QB_EINVAL;
+    if (!aligned16(x) || !aligned16(table) || !aligned16(ws)) return QB_EALIGN;
+    if ((n + kQuantileChunk - 1) / kQuantileChunk >= (int64_t(1) << 31)) return QB_EINVAL;
+    if (ws_bytes < qb_quantile_workspace_bytes(n)) return QB_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t nchunks = (n + kQuantileChunk - 1) / kQuantileChunk;
+    float* E = static_cast<float*>(ws);
+    double* S = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up((size_t)nchunks * 257 * sizeof(float), 256));
+    hipError_t e = launch_chunk_quantiles(x, (int)xdt, n, E, s);
+    if (e == hipSuccess) e = launch_quantile_code(E, nchunks, S, static_cast<UserCode*>(table), s);
+    return hip_status(e);
+}
+
 qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void* g, qb_dtype gdt, int64_t n,
                                 uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2, int32_t blocksize,
                                 void* stream)

@@ -1,0 +1,210 @@
+// qb_codes.hip -- estimation of a quantile code from data.
+//
+// The pages list quantile quantization among the 8-bit types and a fast
+// quantile estimation ("Py之bitsandbytes：bitsandbytes的简介、安装、使用方法之详细
+// 攻略", section 1).  The code entries are the midpoints of adjacent quantiles
+// of the data at probabilities j/257, j = 0..256, normalized to a largest
+// magnitude of 1.  The quantiles are estimated fast and deterministically:
+//   1. k_chunk_quantiles: one workgroup per chunk of 4096 consecutive values
+//      sorts the chunk (bitonic network: 16 values per thread in registers,
+//      lane shuffles within a wave, LDS only across waves) and keeps its 257 order
+//      statistics s[floor(j L / 257)] (L = the chunk's length);
+//   2. k_quantile_groups sums each statistic over groups of 256 consecutive
+//      chunks (binary64, chunk order), and k_quantile_code sums the groups in
+//      group order, divides by the chunk count, forms the midpoints,
+//      normalizes them and writes the code with its decision thresholds.
+// Every step is exact or a fixed sequence of IEEE operations, so the result is
+// the same bits on every run (and as the oracle's).
+#include "qb_device.h"
+
+namespace qb {
+
+namespace {
+
+constexpr int kSortPerThread = kQuantileChunk / kThreads;   // 16 consecutive elements per thread
+constexpr int kGroup = 256;                                  // chunks per first-level sum
+constexpr int kWaveElems = 64 * kSortPerThread;              // 1024 elements per wave
+constexpr int kWaveShift = 10;
+
+// LDS slot of chunk element i: one pad word per 32 keeps the lane-strided
+// accesses (lane stride 16 words) at two-way bank conflicts.
+__device__ __forceinline__ int slot(int i) { return i + (i >> 5); }
+
+// Compare-exchange of v[a] and v[b] (a < b): ascending if up.
+__device__ __forceinline__ void cas(float& x, float& y, bool up)
+{
+    const float lo = fminf(x, y), hi = fmaxf(x, y);
+    x = up ? lo : hi;
+    y = up ? hi : lo;
+}
+
+// Bitonic sort (ascending) of the chunk: thread t holds elements 16 t .. 16 t + 15
+// in registers; stages whose partner lies in the same thread (stride < 16) run
+// in registers, the others through LDS.
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void k_chunk_quantiles(const void* __restrict__ x, int64_t n, int64_t nchunks,
+                                                              float* __restrict__ E)
+{
+    __shared__ float s[kQuantileChunk + kQuantileChunk / 32];
+    const int tid = threadIdx.x;
+    const int64_t c = blockIdx.x;
+    const int64_t lo = c * kQuantileChunk;
+    const int L = (int)(n - lo < kQuantileChunk ? n - lo : kQuantileChunk);
+    const int base = tid * kSortPerThread;
+    float v[kSortPerThread];
+#pragma unroll
+    for (int r = 0; r < kSortPerThread; ++r) {
+        const int i = base + r;
+        float t = INFINITY;                                    // padding sorts to the end
+        if (i < L) {
+            t = load1<XDT>(x, lo + i);
+            t = t == 0.0f ? 0.0f : t;                          // -0 counts as +0
+        }
+        v[r] = t;
+    }
+    // sizes 2 .. 16: wholly inside a thread
+#pragma unroll
+    for (int size = 2; size <= kSortPerThread; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int r = 0; r < kSortPerThread; ++r)
+                if ((r & stride) == 0) cas(v[r], v[r + stride], ((base + r) & size) == 0);
+    // sizes 32 .. 4096: strides of 1024 and more through LDS (the partner is in
+    // another wave), 16 .. 512 by lane shuffles within the wave (the partner of
+    // element 16 t + r is element r of lane t ^ stride/16), then 8 .. 1 in
+    // registers
+    for (int size = 2 * kSortPerThread; size <= kQuantileChunk; size <<= 1) {
+        const bool up = (base & size) == 0;                    // the same for the thread's 16 elements
+        if (size > kWaveElems) {
+#pragma unroll
+            for (int r = 0; r < kSortPerThread; ++r) s[slot(base + r)] = v[r];
+            __syncthreads();
+            for (int ls = __builtin_ctz(size) - 1; ls >= kWaveShift; --ls) {   // stride = 2^ls >= 1024
+                const int stride = 1 << ls;
+#pragma unroll
+                for (int k = 0; k < kSortPerThread / 2; ++k) {
+                    const int q = k * kThreads + tid;          // pair q: i has a zero at bit `stride`
+                    const int i = ((q >> ls) << (ls + 1)) | (q & (stride - 1));
+                    float a = s[slot(i)], b = s[slot(i + stride)];
+                    cas(a, b, (i & size) == 0);
+                    s[slot(i)] = a;
+                    s[slot(i + stride)] = b;
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int r = 0; r < kSortPerThread; ++r) v[r] = s[slot(base + r)];
+            __syncthreads();                                   // before the next size overwrites s
+        }
+        const int top = size > kWaveElems ? kWaveElems >> 1 : size >> 1;
+        for (int stride = top; stride >= kSortPerThread; stride >>= 1) {
+            const int lanes = stride / kSortPerThread;
+            const bool keep_min = ((tid & lanes) == 0) == up;
+#pragma unroll
+            for (int r = 0; r < kSortPerThread; ++r) {
+                const float w = __shfl_xor(v[r], lanes);
+                v[r] = keep_min ? fminf(v[r], w) : fmaxf(v[r], w);
+            }
+        }
+#pragma unroll
+        for (int stride = kSortPerThread >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int r = 0; r < kSortPerThread; ++r)
+                if ((r & stride) == 0) cas(v[r], v[r + stride], up);
+    }
+#pragma unroll
+    for (int r = 0; r < kSortPerThread; ++r) s[slot(base + r)] = v[r];
+    __syncthreads();
+    for (int j = tid; j < 257; j += kThreads) E[(int64_t)j * nchunks + c] = s[slot((int)((int64_t)j * L / 257))];
+}
+
+// First-level sums: workgroup g adds, for every statistic j, its group's
+// chunks g*256 .. in chunk order (binary64).
+__global__ __launch_bounds__(kThreads) void k_quantile_groups(const float* __restrict__ E, int64_t nchunks,
+                                                              double* __restrict__ S)
+{
+    const int64_t g = blockIdx.x, ngroups = gridDim.x;
+    const int64_t c0 = g * kGroup, c1 = c0 + kGroup < nchunks ? c0 + kGroup : nchunks;
+    for (int j = threadIdx.x; j < 257; j += kThreads) {
+        const float* row = E + (int64_t)j * nchunks;
+        double acc = 0.0;
+        for (int64_t c = c0; c < c1; ++c) acc += (double)row[c];
+        S[(int64_t)j * ngroups + g] = acc;
+    }
+}
+
+// The next binary32 above finite f (above +-0: the smallest subnormal).
+__device__ float next_up(float f)
+{
+    if (f == 0.0f) return ffrom(1u);
+    return ffrom(f > 0.0f ? fbits(f) + 1u : fbits(f) - 1u);
+}
+
+// Smallest binary32 >= d (> d when strict), d finite.
+__device__ float ceil_f32(double d, bool strict)
+{
+    float f = (float)d;
+    if ((double)f < d || (strict && (double)f == d)) f = next_up(f);
+    return f;
+}
+
+__global__ __launch_bounds__(kThreads) void k_quantile_code(const double* __restrict__ S, int64_t ngroups,
+                                                            int64_t nchunks, UserCode* __restrict__ out)
+{
+    __shared__ double A[257];
+    __shared__ double q[256];
+    __shared__ double red[kThreads / 64];
+    __shared__ float vals[256];
+    const int tid = threadIdx.x;
+    for (int j = tid; j < 257; j += kThreads) {
+        const double* row = S + (int64_t)j * ngroups;
+        double acc = 0.0;
+        for (int64_t g = 0; g < ngroups; ++g) acc += row[g];
+        A[j] = acc / (double)nchunks;
+    }
+    __syncthreads();
+    const double qi = (A[tid] + A[tid + 1]) * 0.5;
+    q[tid] = qi;
+    // the largest magnitude (a maximum: exact in any order)
+    double m = fabs(qi);
+    for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    const float v = m > 0.0 ? (float)(q[tid] / m) : 0.0f;
+    vals[tid] = v;
+    out->values[tid] = v;
+    __syncthreads();
+    if (tid < 255) {
+        const float a = vals[tid], b = vals[tid + 1];
+        const double mid = ((double)a + (double)b) / 2.0;   // the binary64 midpoint, as the encoder reads it
+        out->thr[tid] = ceil_f32(mid, fabsf(a) < fabsf(b));
+    } else {
+        out->thr[255] = INFINITY;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_quantiles(const void* x, int xdt, int64_t n, float* E, hipStream_t s)
+{
+    const int64_t nchunks = (n + kQuantileChunk - 1) / kQuantileChunk;
+    if (nchunks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    switch (xdt) {
+    case DT_F32: return launch_kernel(k_chunk_quantiles<DT_F32>, (int)nchunks, s, x, n, nchunks, E);
+    case DT_F16: return launch_kernel(k_chunk_quantiles<DT_F16>, (int)nchunks, s, x, n, nchunks, E);
+    case DT_BF16: return launch_kernel(k_chunk_quantiles<DT_BF16>, (int)nchunks, s, x, n, nchunks, E);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_quantile_code(const float* E, int64_t nchunks, double* S, UserCode* out, hipStream_t s)
+{
+    const int64_t ngroups = (nchunks + kGroup - 1) / kGroup;
+    hipError_t e = launch_kernel(k_quantile_groups, (int)ngroups, s, E, nchunks, S);
+    if (e != hipSuccess) return e;
+    return launch_kernel(k_quantile_code, 1, s, (const double*)S, ngroups, nchunks, out);
+}
+
+}  // namespace qb

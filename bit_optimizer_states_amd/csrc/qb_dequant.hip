@@ -88,10 +88,13 @@ __device__ __forceinline__ uint32_t elem_code(const uint8_t* codes, int64_t idx)
     }
 }
 
-template <int BITS, int YDT, bool DQ, bool MULTI>
+// USER: 8-bit codes of a user code (`user`) instead of the dynamic code.
+template <int BITS, int YDT, bool DQ, bool MULTI, bool USER = false>
 __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, TileMap<DequantDesc> map, int log2B,
-                                                        int log2B2, int code4, const QbTables* __restrict__ tab)
+                                                        int log2B2, int code4, const QbTables* __restrict__ tab,
+                                                        const UserCode* __restrict__ user)
 {
+    static_assert(!USER || (BITS == 8 && !DQ), "user codes are 8-bit, without nesting");
     __shared__ float s_val[BITS == 8 ? 256 : 16];   // decode table of the codes
     __shared__ float s_dyn[DQ && BITS == 4 && !QB_DQ_DIRECT_DYN ? 256 : 1];
     // a unit is E elements whose output a lane writes with one 16-byte store
@@ -142,7 +145,9 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
     const float mu = DQ ? gld<float>(d.offset) : 0.0f;
 
     // decode tables
-    if constexpr (BITS == 8) {
+    if constexpr (USER) {
+        s_val[tid] = user->values[tid];
+    } else if constexpr (BITS == 8) {
         s_val[tid] = tab->dyn8[tid];
     } else {
         if (tid < 16) s_val[tid] = (code4 == 0 ? tab->nf4 : tab->fp4)[tid];
@@ -197,9 +202,9 @@ hipError_t dequant_as(const DequantDesc& single, const TileMap<DequantDesc>* map
     if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     if (map)
         return launch_kernel_nt(k_dequant<BITS, YDT, DQ, true>, (int)ntiles, kDqThreads, s, single, *map, ilog2(B),
-                                ilog2(B2), code4, tab);
+                                ilog2(B2), code4, tab, (const UserCode*)nullptr);
     return launch_kernel_nt(k_dequant<BITS, YDT, DQ, false>, (int)ntiles, kDqThreads, s, single,
-                            TileMap<DequantDesc>{}, ilog2(B), ilog2(B2), code4, tab);
+                            TileMap<DequantDesc>{}, ilog2(B), ilog2(B2), code4, tab, (const UserCode*)nullptr);
 }
 
 template <int BITS, bool DQ>
@@ -215,6 +220,27 @@ hipError_t dequant_y(int ydt, const DequantDesc& single, const TileMap<DequantDe
 }
 
 }  // namespace
+
+hipError_t launch_dequant_user(const DequantDesc& d, int64_t ntiles, int B, int ydt, const UserCode* code,
+                               hipStream_t s)
+{
+    if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if (B < 64 || B > 4096 || (B & (B - 1))) return hipErrorInvalidValue;
+    const int lb = ilog2(B);
+    const TileMap<DequantDesc> none{};
+    switch (ydt) {
+    case DT_F32:
+        return launch_kernel_nt(k_dequant<8, DT_F32, false, false, true>, (int)ntiles, kDqThreads, s, d, none, lb, 0,
+                                0, (const QbTables*)nullptr, code);
+    case DT_F16:
+        return launch_kernel_nt(k_dequant<8, DT_F16, false, false, true>, (int)ntiles, kDqThreads, s, d, none, lb, 0,
+                                0, (const QbTables*)nullptr, code);
+    case DT_BF16:
+        return launch_kernel_nt(k_dequant<8, DT_BF16, false, false, true>, (int)ntiles, kDqThreads, s, d, none, lb,
+                                0, 0, (const QbTables*)nullptr, code);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_dequant(const DequantDesc& single, const TileMap<DequantDesc>* map, int64_t ntiles, int bits,
                           int code4, int B, int B2, bool dq, int ydt, hipStream_t s)

@@ -403,6 +403,18 @@ __device__ __forceinline__ uint32_t enc_dyn8_pos(float nv, const DynEncLds& s)
     return c + (nv >= s.thr[c] ? 1u : 0u);
 }
 
+// 8-bit code of a user code: the number of thresholds <= nv, by a branchless
+// binary search over the 255 ascending thresholds (thr[255] = +inf is never
+// read).
+__device__ __forceinline__ uint32_t enc_user(float nv, const float* thr)
+{
+    uint32_t c = 0;
+#pragma unroll
+    for (uint32_t s = 128; s >= 1; s >>= 1)
+        if (nv >= thr[c + s - 1]) c += s;
+    return c;
+}
+
 // 4-bit code (NF4 or FP4 by the table) of a normalized value in [-1, 1]:
 // bucket (int)(16 nv + 16) in [0, 32] (16 nv is exact, so the fused form
 // rounds like the separate operations), then below or above the bucket's one

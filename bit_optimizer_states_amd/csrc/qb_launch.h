@@ -47,6 +47,15 @@ struct TensorDesc {
 };
 static_assert(sizeof(TensorDesc) == 64, "descriptor layout");
 
+// A user code in device memory (qb_code_table_bytes() bytes): 256 ascending
+// entries and their decision thresholds, thr[k] = the smallest binary32 that
+// encodes to entry k+1 or above (thr[255] = +inf), so code = #{k : n >= thr[k]}.
+struct UserCode {
+    float values[256];
+    float thr[256];
+};
+static_assert(sizeof(UserCode) == 2048, "user code layout");
+
 // One tensor of a quantization pass; tile_begin is its first global tile.
 // First pass: x [n] of the input dtype, codes out, absmax out (the caller's,
 // or the fp32 workspace of a nested quantization).  Second pass of
@@ -151,6 +160,18 @@ constexpr int64_t quant_tile_elems(int B) { return B > QB_Q_TILE ? B : QB_Q_TILE
 // second: the nested second pass (bits 8, fp32 input, mean in offset[0]).
 hipError_t launch_quant(const QuantDesc& single, const TileMap<QuantDesc>* map, int64_t ntiles, int bits, int code4,
                         int B, int xdt, bool second, unsigned long long* bins, hipStream_t s);
+
+// Quantize / dequantize one tensor with a user code (8-bit codes).
+hipError_t launch_quant_user(const QuantDesc& d, int64_t ntiles, int B, int xdt, const UserCode* code, hipStream_t s);
+hipError_t launch_dequant_user(const DequantDesc& d, int64_t ntiles, int B, int ydt, const UserCode* code,
+                               hipStream_t s);
+
+// Quantile estimation: chunks of kQuantileChunk consecutive values, each
+// sorted on its own; E holds 257 order statistics per chunk ([257][nchunks]),
+// S the binary64 sums per group of 256 chunks ([257][ngroups]).
+constexpr int kQuantileChunk = 4096;
+hipError_t launch_chunk_quantiles(const void* x, int xdt, int64_t n, float* E, hipStream_t s);
+hipError_t launch_quantile_code(const float* E, int64_t nchunks, double* S, UserCode* out, hipStream_t s);
 
 // Exact mean of the absmax of one tensor (map == nullptr) or of the `count`
 // tensors of map (second-pass descriptors) into offset[0].

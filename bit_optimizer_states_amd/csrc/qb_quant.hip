@@ -197,6 +197,10 @@ struct Lut4Lds {
     uint2 e[k4LutN];
 };
 
+struct UserThrLds {
+    float thr[256];
+};
+
 // CW consecutive elements of dtype DT at element offset e from a uniform base.
 template <int DT, int CW>
 __device__ __forceinline__ void load_chunk(const void* base, uint32_t e, float* v)
@@ -209,13 +213,17 @@ __device__ __forceinline__ void load_chunk(const void* base, uint32_t e, float* 
 // tensor's mean (offset[0], written by k_dq_mean) is subtracted first.  With
 // bins != nullptr (first pass of a nested quantization) every block absmax is
 // also added to the tensor's exponent bins.
-template <int BITS, int B, int XDT, bool SECOND, bool MULTI>
+// USER: 8-bit codes of a user code (`user`: values and thresholds) instead of
+// the dynamic code.
+template <int BITS, int B, int XDT, bool SECOND, bool MULTI, bool USER = false>
 __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<QuantDesc> map,
                                                    unsigned long long* __restrict__ bins,
-                                                   const QbTables* __restrict__ tab, int code4)
+                                                   const QbTables* __restrict__ tab, int code4,
+                                                   const UserCode* __restrict__ user)
 {
+    static_assert(!USER || (BITS == 8 && !SECOND), "user codes are 8-bit, first pass only");
     using G = QGeo<BITS, B>;
-    using EncLds = std::conditional_t<BITS == 8, DynEncLds, Lut4Lds>;
+    using EncLds = std::conditional_t<USER, UserThrLds, std::conditional_t<BITS == 8, DynEncLds, Lut4Lds>>;
     __shared__ EncLds s_enc;
     __shared__ uint32_t s_red[G::R][4];
     __shared__ unsigned long long s_bins[256];
@@ -262,7 +270,9 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
     const bool binning = !SECOND && bins != nullptr;
     float mu = 0.0f;
     if constexpr (SECOND) mu = gld<float>(d.offset);
-    if constexpr (BITS == 8) {
+    if constexpr (USER) {
+        s_enc.thr[tid] = user->thr[tid];
+    } else if constexpr (BITS == 8) {
         stage_dyn_enc(s_enc, tab, tid);
     } else {
         const uint2* glut = reinterpret_cast<const uint2*>(code4 == 0 ? tab->nf4_lut : tab->fp4_lut);
@@ -311,7 +321,10 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
             uint32_t w = 0;
             if constexpr (BITS == 8) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) w |= enc_dyn8(nv[c * 4 + j], s_enc) << (8 * j);
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (USER) w |= enc_user(nv[c * 4 + j], s_enc.thr) << (8 * j);
+                    else w |= enc_dyn8(nv[c * 4 + j], s_enc) << (8 * j);
+                }
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
@@ -384,9 +397,10 @@ hipError_t quant_as(const QuantDesc& single, const TileMap<QuantDesc>* map, int6
                     unsigned long long* bins, const QbTables* tab, int code4, hipStream_t s)
 {
     if (map)
-        return launch_kernel(k_quant<BITS, B, XDT, SECOND, true>, (int)ntiles, s, single, *map, bins, tab, code4);
+        return launch_kernel(k_quant<BITS, B, XDT, SECOND, true>, (int)ntiles, s, single, *map, bins, tab, code4,
+                             (const UserCode*)nullptr);
     return launch_kernel(k_quant<BITS, B, XDT, SECOND, false>, (int)ntiles, s, single, TileMap<QuantDesc>{}, bins,
-                         tab, code4);
+                         tab, code4, (const UserCode*)nullptr);
 }
 
 template <int BITS, int B>
@@ -432,6 +446,43 @@ hipError_t launch_quant(const QuantDesc& single, const TileMap<QuantDesc>* map, 
     if (bits == 8) return quant_b<8>(B, xdt, second, single, map, ntiles, bins, tab, code4, s);
     if (bits == 4 && !second) return quant_b<4>(B, xdt, false, single, map, ntiles, bins, tab, code4, s);
     return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <int B, int XDT>
+hipError_t quant_user_as(const QuantDesc& d, int64_t ntiles, const UserCode* code, hipStream_t s)
+{
+    return launch_kernel(k_quant<8, B, XDT, false, false, true>, (int)ntiles, s, d, TileMap<QuantDesc>{},
+                         (unsigned long long*)nullptr, (const QbTables*)nullptr, 0, code);
+}
+
+template <int B>
+hipError_t quant_user_x(int xdt, const QuantDesc& d, int64_t ntiles, const UserCode* code, hipStream_t s)
+{
+    switch (xdt) {
+    case DT_F32: return quant_user_as<B, DT_F32>(d, ntiles, code, s);
+    case DT_F16: return quant_user_as<B, DT_F16>(d, ntiles, code, s);
+    case DT_BF16: return quant_user_as<B, DT_BF16>(d, ntiles, code, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_user(const QuantDesc& d, int64_t ntiles, int B, int xdt, const UserCode* code, hipStream_t s)
+{
+    if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    switch (B) {
+    case 64: return quant_user_x<64>(xdt, d, ntiles, code, s);
+    case 128: return quant_user_x<128>(xdt, d, ntiles, code, s);
+    case 256: return quant_user_x<256>(xdt, d, ntiles, code, s);
+    case 512: return quant_user_x<512>(xdt, d, ntiles, code, s);
+    case 1024: return quant_user_x<1024>(xdt, d, ntiles, code, s);
+    case 2048: return quant_user_x<2048>(xdt, d, ntiles, code, s);
+    case 4096: return quant_user_x<4096>(xdt, d, ntiles, code, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_dq_mean(const QuantDesc& single, const TileMap<QuantDesc>* map, int count,

@@ -261,6 +261,24 @@ int build_tables(QbTables* T)
     return self_check(T);
 }
 
+void linear_code(float* out)
+{
+    for (int k = -128; k <= 127; ++k) {
+        const float m = rn32_ratio((uint64_t)(k < 0 ? -k : k), 127);
+        out[k + 128] = k < 0 ? -m : m;
+    }
+}
+
+int user_code_thresholds(const float* values, float* thr)
+{
+    for (int k = 0; k < 256; ++k)
+        if (!std::isfinite(values[k]) || (k > 0 && !(values[k - 1] <= values[k]))) return -1;
+    std::vector<float> t = thresholds(std::vector<float>(values, values + 256));
+    for (int k = 0; k < 255; ++k) thr[k] = t[k];
+    thr[255] = INFINITY;
+    return 0;
+}
+
 const QbTables* host_tables()
 {
     static QbTables tables;

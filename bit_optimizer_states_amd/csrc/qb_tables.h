@@ -50,4 +50,14 @@ int build_tables(QbTables* t);
 // The tables, built on first use (thread-safe); nullptr if the build failed.
 const QbTables* host_tables();
 
+// The linear 8-bit code k/127, k = -128..127 (each entry rounded once).
+void linear_code(float* out /* [256] */);
+
+// Decision thresholds of a user code: values[256] must be finite and
+// non-decreasing; thr[k] = smallest binary32 encoding to entry k+1 or above
+// (the midpoint of the entries computed in binary64; a tie goes to the entry
+// of smaller magnitude, between equal magnitudes to the upper one),
+// thr[255] = +inf.  Returns 0, or -1 for an invalid code.
+int user_code_thresholds(const float* values, float* thr);
+
 }  // namespace qb

@@ -313,6 +313,43 @@ qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_te
                                          qb_dtype gdt, int32_t blocksize, void* ws, size_t ws_bytes,
                                          void* stream);
 
+/*
+ * User codes.  The pages list three 8-bit quantization types, quantile,
+ * linear and dynamic, and a fast quantile estimation (page "Py之bitsandbytes",
+ * section 1).  Besides the built-in dynamic code, a block-wise 8-bit
+ * quantization can use any 256-entry code held in a device table of
+ * qb_code_table_bytes() bytes (16-byte aligned): the entries and their exact
+ * decision thresholds (nearest entry; the midpoint of two entries is taken in
+ * binary64; a tie goes to the entry of smaller magnitude, between equal
+ * magnitudes to the upper one).
+ *   qb_linear_code      host: the linear code k/127, k = -128..127 (returns 256).
+ *   qb_prepare_code     host values[256] (finite, non-decreasing; else
+ *                       QB_EINVAL) -> device table, copied on `stream`.
+ *   qb_estimate_quantiles
+ *                       device: the quantile code of x[n] straight into a
+ *                       device table.  Entries = midpoints of adjacent
+ *                       quantiles at j/257 (j = 0..256), normalized to a largest
+ *                       magnitude of 1.  The quantiles are averaged in binary64
+ *                       over chunks of 4096 consecutive values, each sorted on its
+ *                       own (the chunk's order statistic at floor(j L / 257); -0
+ *                       counts as +0), summed per group of 256 chunks and then
+ *                       over the groups, each in order.  Deterministic.  ws:
+ *                       qb_quantile_workspace_bytes(n) bytes.  Three kernels.
+ *   qb_quantize_code / qb_dequantize_code
+ *                       as qb_quantize / qb_dequantize with 8-bit codes (codes:
+ *                       n bytes) and no nesting, the code given by `table`.
+ */
+size_t    qb_code_table_bytes(void);
+int32_t   qb_linear_code(float* out);
+qb_status qb_prepare_code(const float* values, void* table, void* stream);
+size_t    qb_quantile_workspace_bytes(int64_t n);
+qb_status qb_estimate_quantiles(const void* x, qb_dtype xdt, int64_t n, void* table, void* ws, size_t ws_bytes,
+                                void* stream);
+qb_status qb_quantize_code(const void* x, qb_dtype xdt, int64_t n, const void* table, int32_t blocksize,
+                           uint8_t* codes, float* absmax, void* stream);
+qb_status qb_dequantize_code(const uint8_t* codes, const float* absmax, const void* table, int32_t blocksize,
+                             int64_t n, void* y, qb_dtype ydt, void* stream);
+
 /* Workspace sizes (bytes) for qb_quantize with nesting, and for
  * qb_multi_tensor_step, qb_multi_tensor_optimizer_step and qb_multi_tensor_dequantize. */
 size_t qb_dq_workspace_bytes(int64_t n, int32_t blocksize);

@@ -760,26 +760,36 @@ static int cmp_float_asc(const void* a, const void* b)
  * may be shorter), sorting each chunk on its own and averaging the chunks'
  * order statistics:
  *   E_j(chunk of L sorted values s) = s[floor(j * L / 257)],
- *   A_j = (sum over chunks, in chunk order, of E_j) / nchunks       (binary64),
+ *   A_j = (sum over groups of 256 consecutive chunks, in group order, of the
+ *          group's sum of E_j in chunk order) / nchunks               (binary64),
  *   q_i = (A_i + A_{i+1}) / 2,  i = 0..255                           (binary64),
  *   code_i = binary32(q_i / max_k |q_k|)   (all 0 when max_k |q_k| = 0).
  * The entries come out ascending (A is non-decreasing); equal neighbours are
- * possible.
+ * possible.  A negative zero in x counts as +0.
  */
 int orc_estimate_quantiles(const void* x, int xdt, int64_t n, int C, float* out /* [256] */)
 {
     if (n < 1 || C < 257) return -1;
     int64_t nch = (n + C - 1) / C;
-    double acc[257];
-    for (int j = 0; j < 257; j++) acc[j] = 0.0;
+    double acc[257], grp[257];
+    for (int j = 0; j < 257; j++) acc[j] = grp[j] = 0.0;
     float* s = (float*)malloc(sizeof(float) * (size_t)C);
     if (!s) return -1;
     for (int64_t c = 0; c < nch; c++) {
         int64_t lo = c * C, hi = lo + C < n ? lo + C : n;
         int L = (int)(hi - lo);
-        for (int i = 0; i < L; i++) s[i] = load_elem(x, xdt, lo + i);
+        for (int i = 0; i < L; i++) {
+            float v = load_elem(x, xdt, lo + i);
+            s[i] = v == 0.0f ? 0.0f : v;       /* -0 counts as +0: the sort orders numbers */
+        }
         qsort(s, (size_t)L, sizeof(float), cmp_float_asc);
-        for (int j = 0; j < 257; j++) acc[j] += (double)s[(int64_t)j * L / 257];
+        for (int j = 0; j < 257; j++) grp[j] += (double)s[(int64_t)j * L / 257];
+        if (c % 256 == 255 || c == nch - 1) {          /* a group of 256 chunks ends */
+            for (int j = 0; j < 257; j++) {
+                acc[j] += grp[j];
+                grp[j] = 0.0;
+            }
+        }
     }
     free(s);
     double A[257], q[256], m = 0.0;

@@ -1,0 +1,137 @@
+"""GPU parity: user codes (qb_prepare_code, qb_quantize_code, qb_dequantize_code)
+and the estimated quantile code (qb_estimate_quantiles) against the CPU
+oracle, bit-exact: codes, absmax, outputs, the estimated code's entries, and its
+device thresholds equal the host's for the same entries."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import DEV, TORCH_DT, host_bits, qb, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def table_of(values):
+    L = qb()
+    t = torch.empty(L.qb_code_table_bytes(), dtype=torch.uint8, device=DEV)
+    L.qb_prepare_code(list(values), t)
+    return t
+
+
+def read_table(t):
+    torch.cuda.synchronize()
+    a = t.cpu().numpy().view(np.float32)
+    return a[:256].copy(), a[256:].copy()
+
+
+def codes_of(name):
+    rng = np.random.default_rng(21)
+    if name == "linear":
+        return oracle.linear_codebook()
+    if name == "dynamic":
+        return oracle.codebook(oracle.DYN8)
+    if name == "symmetric_no_zero":
+        half = np.sort(rng.uniform(0.001, 1.0, 128)).astype(np.float32)
+        half[-1] = 1.0
+        return np.concatenate([-half[::-1], half]).astype(np.float32)
+    return oracle.estimate_quantiles((rng.standard_t(3, 50000) * 0.02).astype(np.float32))
+
+
+def make_x(n, dt, seed):
+    x = (np.random.default_rng(seed).standard_t(3, n) * 0.02).astype(np.float32)
+    if dt == oracle.F32:
+        return x, x
+    t = torch.from_numpy(x).to(TORCH_DT[dt])
+    return t.view(torch.int16).numpy().view(np.uint16).copy(), t
+
+
+@pytest.mark.parametrize("name", ["linear", "dynamic", "symmetric_no_zero", "quantile"])
+@pytest.mark.parametrize("B,dt", [(64, oracle.F32), (256, oracle.BF16), (2048, oracle.F16), (4096, oracle.F32)])
+def test_user_code_roundtrip_equals_oracle(name, B, dt):
+    L = qb()
+    cb = codes_of(name)
+    t = table_of(cb)
+    n = B * 7 + 4096 * 3 + 123
+    xh, _ = make_x(n, dt, seed=B + dt)
+    xd = to_device(xh, TORCH_DT[dt])
+    nb = (n + B - 1) // B
+    codes = torch.full((n + 8,), 0xAB, dtype=torch.uint8, device=DEV)
+    absmax = torch.full((nb + 2,), -7.0, device=DEV)
+    L.qb_quantize_code(xd, n, t, B, codes, absmax)
+    want_c, want_a = oracle.quantize_custom(xh, cb, B, dt)
+    got_c, got_a = host_bits(codes), host_bits(absmax)
+    assert np.array_equal(got_c[:n], want_c) and np.all(got_c[n:] == 0xAB)
+    assert np.array_equal(got_a[:nb].view(np.uint32), want_a.view(np.uint32)) and np.all(got_a[nb:] == -7.0)
+    for ydt in (oracle.F32, oracle.BF16):
+        y = torch.empty(n, dtype=TORCH_DT[ydt], device=DEV)
+        L.qb_dequantize_code(codes, absmax, t, B, n, y)
+        want = oracle.dequantize_custom(want_c, want_a, cb, B, n, ydt)
+        assert np.array_equal(host_bits(y).view(np.uint8), want.view(np.uint8))
+    if name == "dynamic":                   # the user-code path reproduces the built-in code
+        c2 = torch.empty(n, dtype=torch.uint8, device=DEV)
+        a2 = torch.empty(nb, device=DEV)
+        L.qb_quantize(xd, n, L.QB_DYN8, B, c2, a2)
+        torch.cuda.synchronize()
+        assert torch.equal(c2, codes[:n]) and torch.equal(a2, absmax[:nb])
+
+
+@pytest.mark.parametrize("n", [1, 2, 257, 4096, 4097, 4096 * 10 + 5, 1_000_003])
+@pytest.mark.parametrize("dt", [oracle.F32, oracle.BF16])
+def test_estimated_quantile_code_equals_oracle(n, dt):
+    L = qb()
+    xh, _ = make_x(n, dt, seed=n)
+    if n > 1000:
+        xh[::97] = 0 if dt != oracle.F32 else np.float32(0.0)        # repeated values
+        if dt == oracle.F32:
+            xh[5::211] = np.float32(-0.0)                             # negative zeros count as +0
+    xd = to_device(xh, TORCH_DT[dt])
+    t = torch.empty(L.qb_code_table_bytes(), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(L.qb_quantile_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    L.qb_estimate_quantiles(xd, n, t, ws)
+    vals, thr = read_table(t)
+    want = oracle.estimate_quantiles(xh, xdt=dt)
+    assert np.array_equal(vals.view(np.uint32), want.view(np.uint32))
+    # the device thresholds are the host's for the same entries
+    _, host_thr = read_table(table_of(vals))
+    assert np.array_equal(thr.view(np.uint32), host_thr.view(np.uint32))
+
+
+def test_quantile_code_of_a_uniform_grid():
+    # one chunk (257 k <= 4096 values) holding a shuffled 0, 1, ..., 257 k - 1:
+    # the closed form (i + 1/2) / 255.5 of the oracle's pin
+    L = qb()
+    k = 15
+    t = torch.empty(L.qb_code_table_bytes(), dtype=torch.uint8, device=DEV)
+    one = np.random.default_rng(1).permutation(257 * k).astype(np.float32)
+    ws = torch.empty(L.qb_quantile_workspace_bytes(one.size), dtype=torch.uint8, device=DEV)
+    L.qb_estimate_quantiles(to_device(one), one.size, t, ws)
+    vals, _ = read_table(t)
+    want = np.array([(i + 0.5) / 255.5 for i in range(256)], dtype=np.float32)
+    assert np.array_equal(vals, want)
+
+
+def test_estimate_then_quantize_a_large_tensor():
+    """The full quantile flow on 16M values: estimate the code on the device,
+    quantize and dequantize with it; sampled blocks against the oracle."""
+    L = qb()
+    n, B = 1 << 24, 2048
+    x = torch.empty(n, device=DEV).normal_(0, 0.02, generator=torch.Generator(device=DEV).manual_seed(3))
+    t = torch.empty(L.qb_code_table_bytes(), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(L.qb_quantile_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    L.qb_estimate_quantiles(x, n, t, ws)
+    codes = torch.empty(n, dtype=torch.uint8, device=DEV)
+    absmax = torch.empty(n // B, device=DEV)
+    L.qb_quantize_code(x, n, t, B, codes, absmax)
+    y = torch.empty(n, device=DEV)
+    L.qb_dequantize_code(codes, absmax, t, B, n, y)
+    vals, _ = read_table(t)
+    assert np.array_equal(vals, oracle.estimate_quantiles(x.cpu().numpy()))
+    blocks = np.random.default_rng(4).choice(n // B, 256, replace=False)
+    idx = torch.from_numpy(blocks).to(DEV)
+    xs = x.view(-1, B).index_select(0, idx).cpu().numpy().reshape(-1)
+    want_c, want_a = oracle.quantize_custom(xs, vals, B)
+    assert np.array_equal(codes.view(-1, B).index_select(0, idx).cpu().numpy().reshape(-1), want_c)
+    assert np.array_equal(absmax.index_select(0, idx).cpu().numpy(), want_a)
+    want_y = oracle.dequantize_custom(want_c, want_a, vals, B, xs.size)
+    assert np.array_equal(y.view(-1, B).index_select(0, idx).cpu().numpy().reshape(-1), want_y)

@@ -244,6 +244,38 @@ def test_optimizer_hyperparameters_rejected_before_launch(qb):
     assert f(ctypes.byref(H(qb.QB_SGD, 1e-3)), A, A2, 2, 100, A + 4, None, None, None, 2048, None) == qb.QB_EALIGN
 
 
+def test_linear_code_equals_oracle(qb):
+    got = np.array(qb.qb_linear_code(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), oracle.linear_codebook().view(np.uint32))
+    assert qb.qb_code_table_bytes() == 2048
+
+
+def test_user_code_arguments_rejected_before_launch(qb):
+    L = qb.lib()
+    A = 0x100000
+    good = (ctypes.c_float * 256)(*[k / 255.0 for k in range(256)])
+    bad_order = (ctypes.c_float * 256)(*([0.5] + [k / 255.0 for k in range(1, 256)]))
+    bad_nan = (ctypes.c_float * 256)(*([float("nan")] + [k / 255.0 for k in range(1, 256)]))
+    assert L.qb_prepare_code(bad_order, A, None) == qb.QB_EINVAL
+    assert L.qb_prepare_code(bad_nan, A, None) == qb.QB_EINVAL
+    assert L.qb_prepare_code(good, A + 4, None) == qb.QB_EALIGN
+    assert L.qb_prepare_code(None, A, None) == qb.QB_EINVAL
+    assert L.qb_quantize_code(A, 0, 0, A, 256, A, A, None) == qb.QB_OK          # n == 0
+    assert L.qb_quantize_code(A, 0, 100, None, 256, A, A, None) == qb.QB_EINVAL  # no table
+    assert L.qb_quantize_code(A, 0, 100, A, 100, A, A, None) == qb.QB_EINVAL    # blocksize
+    assert L.qb_quantize_code(A, 0, 100, A + 8, 256, A, A, None) == qb.QB_EALIGN
+    assert L.qb_quantize_code(A, 0, 100, A, 256, A, None, None) == qb.QB_EINVAL  # no absmax
+    assert L.qb_dequantize_code(A, A, A, 256, 0, A, 2, None) == qb.QB_OK
+    assert L.qb_dequantize_code(A, None, A, 256, 100, A, 2, None) == qb.QB_EINVAL
+    assert L.qb_dequantize_code(A, A, A, 256, 100, A + 2, 2, None) == qb.QB_EALIGN
+    ws = L.qb_quantile_workspace_bytes(10000)
+    assert ws == -(-(3 * 257 * 4) // 256) * 256 + 257 * 8
+    assert L.qb_estimate_quantiles(A, 0, 0, A, A, ws, None) == qb.QB_EINVAL      # n < 1
+    assert L.qb_estimate_quantiles(A, 0, 10000, A, A, ws - 256, None) == qb.QB_EWORKSPACE
+    assert L.qb_estimate_quantiles(A, 5, 10000, A, A, ws, None) == qb.QB_EINVAL
+    assert L.qb_estimate_quantiles(A, 0, 10000, A + 4, A, ws, None) == qb.QB_EALIGN
+
+
 def test_status_strings(qb):
     assert qb.qb_status_string(0) == "ok"
     assert "workspace" in qb.qb_status_string(5)
