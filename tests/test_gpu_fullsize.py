@@ -13,7 +13,9 @@ Workloads (seeded, synthetic; shapes of the pages' models):
     bf16 dequantize of 7B-decoder-shaped fp16 weights, per tensor and with the
     grouped calls over all 225 tensors;
   * one multi-tensor AdamW8bit launch over the 291 tensors of a 7B decoder
-    (6,738,415,616 parameters), with 10%-row-sparse embedding gradients.
+    (6,738,415,616 parameters), with 10%-row-sparse embedding gradients;
+  * beyond 32-bit offsets: an AdamW8bit step on 2^31 + 4097 parameters and an
+    NF4 nested round trip on 2^32 + 131 weights.
 """
 import numpy as np
 import pytest
@@ -267,3 +269,80 @@ def test_grouped_4bit_7b_all_225_tensors():
         want_y = oracle.dequantize_blockwise(want_c, ahat, code, B, len(blocks) * B, oracle.BF16)
         got_y = host_bits(y.view(nb, B).index_select(0, idx)).reshape(-1)
         assert np.array_equal(got_y, want_y), name
+
+
+def _sample_blocks(nb, around, rng, k=64):
+    """Block indices: random ones, the first and last, and those around the given element offsets."""
+    pick = set(rng.choice(nb, k, replace=False).tolist()) | {0, nb - 1}
+    for e in around:
+        b = e // 64
+        pick |= {max(0, min(nb - 1, b + d)) for d in (-2, -1, 0, 1, 2)}
+    return np.array(sorted(pick))
+
+
+def test_adamw8bit_beyond_int32_elements():
+    """One tensor of 2^31 + 4097 parameters: every element offset above 2^31
+    (the ragged last block included) reaches the right place."""
+    L = qb()
+    n, B = (1 << 31) + 4097, 2048
+    nb = (n + B - 1) // B
+    p = inputs.normal(n, 0.02, seed=71, device=DEV)
+    g = inputs.normal(n, 1e-3, seed=72, device=DEV, dtype=torch.bfloat16)
+    m = torch.full((n,), 127, dtype=torch.uint8, device=DEV)
+    v = torch.full((n,), 127, dtype=torch.uint8, device=DEV)
+    am = torch.zeros(nb, device=DEV)
+    av = torch.zeros(nb, device=DEV)
+    rng = np.random.default_rng(73)
+    blocks = np.unique(np.concatenate([rng.choice(nb, 96, replace=False), [0, nb - 2, nb - 1],
+                                       np.arange((1 << 31) // B - 2, (1 << 31) // B + 3)]))
+    p0 = block_rows(p, B, blocks)
+    g0 = block_rows(g, B, blocks)
+    L.qb_adamw8bit_step(p, g, n, m, v, am, av, B, hparams(1))
+    torch.cuda.synchronize()
+    pm, mm, vm = block_rows(p, B, blocks), block_rows(m, B, blocks), block_rows(v, B, blocks)
+    amh, avh = am.cpu().numpy()[blocks], av.cpu().numpy()[blocks]
+    for k, b in enumerate(blocks):
+        ph = p0[k].copy()
+        cm, cv = np.full(ph.size, 127, np.uint8), np.full(ph.size, 127, np.uint8)
+        a1, a2 = np.zeros(1, np.float32), np.zeros(1, np.float32)
+        oracle.adamw8bit_step(ph, g0[k], cm, cv, a1, a2, B, step=1, gdt=oracle.BF16, **HP)
+        assert np.array_equal(mm[k], cm) and np.array_equal(vm[k], cv), b
+        assert amh[k] == a1[0] and avh[k] == a2[0], b
+        np.testing.assert_allclose(pm[k], ph, rtol=1e-6, atol=2e-8)
+
+
+def test_nf4_nested_beyond_uint32_elements():
+    """NF4 block-64 quantization with nesting and a bf16 dequantize of one
+    tensor of 2^32 + 131 fp16 weights (odd length: the last byte's low nibble is
+    0): sampled blocks around 2^31 and 2^32 against the oracle, and the whole
+    nested state."""
+    L = qb()
+    n, B, B2 = (1 << 32) + 131, 64, 256
+    nb = (n + B - 1) // B
+    w = inputs.normal(n, 0.02, seed=74, device=DEV, dtype=torch.float16)
+    codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=DEV)
+    c2 = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    a2 = torch.empty((nb + B2 - 1) // B2, dtype=torch.float32, device=DEV)
+    off = torch.empty(4, dtype=torch.float32, device=DEV)
+    ws = torch.empty(L.qb_dq_workspace_bytes(n, B), dtype=torch.uint8, device=DEV)
+    L.qb_quantize(w, n, qb().QB_NF4, B, codes, None, L.make_dq(c2, a2, off, B2, ws))
+    del ws
+    y = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    L.qb_dequantize(codes, None, L.make_dq(c2, a2, off, B2), qb().QB_NF4, B, n, y)
+    torch.cuda.synchronize()
+    full = n // B
+    a = w[:full * B].abs().view(full, B).amax(dim=1).float().cpu().numpy()
+    a = np.concatenate([a, [float(w[full * B:].abs().max())]]).astype(np.float32)
+    c2w, a2w, mu = oracle.dq_quantize(a, B2)
+    assert np.float32(off[0].item()) == mu
+    assert np.array_equal(c2.cpu().numpy(), c2w) and np.array_equal(a2.cpu().numpy(), a2w)
+    ahat = oracle.dq_decode(c2w, a2w, mu)
+    rng = np.random.default_rng(75)
+    for b in _sample_blocks(nb, [1 << 31, 1 << 32, n - 1], rng):
+        lo, hi = int(b) * B, min(n, (int(b) + 1) * B)
+        xs = host_bits(w[lo:hi])
+        want_c, _ = oracle.quantize_blockwise(xs, oracle.NF4, B, oracle.F16)
+        got_c = codes[lo // 2:(hi + 1) // 2].cpu().numpy()
+        assert np.array_equal(got_c, want_c), b
+        want_y = oracle.dequantize_blockwise(want_c, ahat[b:b + 1], oracle.NF4, B, hi - lo, oracle.BF16)
+        assert np.array_equal(host_bits(y[lo:hi]), want_y), b
