@@ -315,17 +315,18 @@ def estimate_quantiles(x, chunk=QUANTILE_CHUNK, xdt=None):
 
 
 # the sibling optimizers (oracle.c, section "the sibling 8-bit optimizers")
-ADAMW, ADAM, LION, SGD, RMSPROP = 0, 1, 2, 3, 4
-OPTIMIZER_STATES = {ADAMW: 2, ADAM: 2, LION: 1, SGD: 1, RMSPROP: 1}
+ADAMW, ADAM, LION, SGD, RMSPROP, LAMB, LARS = 0, 1, 2, 3, 4, 5, 6
+OPTIMIZER_STATES = {ADAMW: 2, ADAM: 2, LION: 1, SGD: 1, RMSPROP: 1, LAMB: 2, LARS: 1}
 
 
-def _optim_hp(lr, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.0, dampening=0.0, nesterov=False):
-    return np.array([lr, beta1, beta2, eps, wd, dampening, 1.0 if nesterov else 0.0], dtype=np.float64)
+def _optim_hp(lr, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.0, dampening=0.0, nesterov=False, trust=0.0):
+    return np.array([lr, beta1, beta2, eps, wd, dampening, 1.0 if nesterov else 0.0, trust], dtype=np.float64)
 
 
 def optim32_step(kind, p, g, x1, x2=None, step=1, gdt=None, **hp):
     """In-place step of optimizer `kind` with binary32 states x1 (and x2 for the
-    two-state kinds); hp: lr, beta1, beta2, eps, wd, dampening, nesterov."""
+    two-state kinds); hp: lr, beta1, beta2, eps, wd, dampening, nesterov, trust
+    (the layer-wise kinds take one call per layer)."""
     if gdt is None:
         gdt = _dtype_id(g)
     g = np.ascontiguousarray(g)

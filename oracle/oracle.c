@@ -533,7 +533,7 @@ int orc_adam_scalars(double lr, double beta1, double beta2, double eps, double w
  * Chen et al., 2023), with every state tensor kept as block-wise dynamic 8-bit
  * codes exactly as for AdamW.  Binary32, each operation rounded on its own.
  *
- * hp[] = {lr, beta1, beta2, eps, weight_decay, dampening, nesterov}; per kind:
+ * hp[] = {lr, beta1, beta2, eps, weight_decay, dampening, nesterov, trust}; per kind:
  *   ORC_ADAMW    as orc_adamw8bit_step.
  *   ORC_ADAM     L2-coupled decay: gw = g + wd*p, then the Adam update with
  *                bias correction and no decoupled decay.  States m, v.
@@ -544,10 +544,13 @@ int orc_adam_scalars(double lr, double beta1, double beta2, double eps, double w
  *                d = nesterov ? gw + mu*buf' : buf'; p' = p - lr*d.  State buf.
  *   ORC_RMSPROP  gw = g + wd*p; v' = al*v + (1-al)*gw*gw (al = beta2);
  *                p' = p - lr*(gw / (sqrt(v') + eps)).  State v.
+ * The layer-wise kinds ORC_LAMB and ORC_LARS (hp[7] = trust coefficient) are
+ * described at layerwise32 below.
  */
-enum { ORC_ADAMW = 0, ORC_ADAM = 1, ORC_LION = 2, ORC_SGD = 3, ORC_RMSPROP = 4 };
+enum { ORC_ADAMW = 0, ORC_ADAM = 1, ORC_LION = 2, ORC_SGD = 3, ORC_RMSPROP = 4, ORC_LAMB = 5, ORC_LARS = 6 };
 
-static int optim_states(int kind) { return (kind == ORC_ADAMW || kind == ORC_ADAM) ? 2 : 1; }
+static int optim_states(int kind) { return (kind == ORC_ADAMW || kind == ORC_ADAM || kind == ORC_LAMB) ? 2 : 1; }
+static int is_layerwise(int kind) { return kind == ORC_LAMB || kind == ORC_LARS; }
 
 typedef struct {
     int kind, step, nesterov;
@@ -562,7 +565,8 @@ static optim_scalars optim_prepare(int kind, const double* hp, int step)
     s.kind = kind;
     s.step = step;
     s.nesterov = hp[6] != 0.0;
-    s.a = adam_prepare(hp[0], hp[1], hp[2], hp[3], kind == ORC_ADAMW ? hp[4] : 0.0, step);
+    /* LAMB takes Adam's direction without lr: s1 = 1/(1 - beta1^t) */
+    s.a = adam_prepare(kind == ORC_LAMB ? 1.0 : hp[0], hp[1], hp[2], hp[3], kind == ORC_ADAMW ? hp[4] : 0.0, step);
     s.lr = (float)hp[0];
     s.wd = (float)hp[4];
     s.b1 = (float)hp[1];
@@ -641,8 +645,84 @@ static void optim_elem(const optim_scalars* s, float g, float* p, float* x1, flo
 
 static int optim_check(int kind, const double* hp, int step)
 {
-    if (kind < ORC_ADAMW || kind > ORC_RMSPROP || step < 1) return -1;
+    if (kind < ORC_ADAMW || kind > ORC_LARS || step < 1) return -1;
     if (kind == ORC_SGD && !(hp[1] > 0.0)) return -1;   /* 8-bit SGD keeps a momentum state */
+    if (kind == ORC_LARS && !(hp[7] > 0.0)) return -1;  /* LARS needs a trust coefficient */
+    return 0;
+}
+
+/*
+ * The layer-wise kinds.  The pages list 8-bit LARS and LAMB among the 8-bit
+ * optimizers (page "Py之bitsandbytes", section 1: 8-bit optimizers) and give
+ * no formulas.  Reading: their published definitions, one call being one layer
+ * (the norms run over the whole tensor) -- LARS as You, Gitman and Ginsburg
+ * (2017) define it, with the local rate inside the momentum; LAMB as You et al.
+ * (2019) define it, with bias correction and phi the identity.  The norms and
+ * the ratio are binary64 (squares of binary32 values are exact in binary64;
+ * the sums run in index order), and the ratio reaches the binary32 update as
+ * one scalar S = (float)(lr * ratio); a zero norm makes the ratio 1:
+ *   ORC_LAMB  states m, v:  m' = b1*m + (1-b1)*g,  v' = b2*v + (1-b2)*g*g,
+ *             r = s1*(m' / (sqrt(v')*s2 + eps)) with s1 = 1/(1-b1^t) and
+ *             s2 = 1/sqrt(1-b2^t) (adam_elem's order without lr),
+ *             u = r + wd*p;  ratio = |p| / |u|;  p' = p - S*u.
+ *   ORC_LARS  state buf (mu = beta1, eta = trust coefficient):
+ *             ratio = eta*|p| / (|g| + wd*|p|);  gw = g + wd*p;
+ *             buf' = mu*buf + S*gw;  p' = p - buf'.
+ * x1, x2: binary32 states, updated in place.
+ */
+static int layerwise32(int kind, const double* hp, const optim_scalars* s, float* p, const void* g, int gdt,
+                       int64_t n, float* x1, float* x2)
+{
+    double sp = 0.0, sq = 0.0;           /* |p|^2 and |u|^2 (LAMB) or |g|^2 (LARS) */
+    float* u = NULL;
+    if (kind == ORC_LAMB) {
+        u = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+        if (!u) return -1;
+        for (int64_t i = 0; i < n; i++) {
+            float gi = load_elem(g, gdt, i);
+            float t1 = s->a.b1 * x1[i];
+            float t2 = s->a.ob1 * gi;
+            float m1 = t1 + t2;
+            float gg = gi * gi;
+            float t3 = s->a.b2 * x2[i];
+            float t4 = s->a.ob2 * gg;
+            float v1 = t3 + t4;
+            float den = sqrtf(v1) * s->a.s2 + s->a.eps;
+            float r = s->a.s1 * (m1 / den);
+            float t = s->wd * p[i];
+            u[i] = r + t;
+            x1[i] = m1;
+            x2[i] = v1;
+            sp += (double)p[i] * (double)p[i];
+            sq += (double)u[i] * (double)u[i];
+        }
+    } else {
+        for (int64_t i = 0; i < n; i++) {
+            double gi = (double)load_elem(g, gdt, i);
+            sp += (double)p[i] * (double)p[i];
+            sq += gi * gi;
+        }
+    }
+    double pn = sqrt(sp), qn = sqrt(sq);
+    double ratio = 1.0;
+    if (pn > 0.0 && qn > 0.0) ratio = (kind == ORC_LAMB) ? pn / qn : (hp[7] * pn) / (qn + hp[4] * pn);
+    float S = (float)(hp[0] * ratio);
+    for (int64_t i = 0; i < n; i++) {
+        if (kind == ORC_LAMB) {
+            float t = S * u[i];
+            p[i] = p[i] - t;
+        } else {
+            float gi = load_elem(g, gdt, i);
+            float t = s->wd * p[i];
+            float gw = gi + t;
+            float t1 = s->b1 * x1[i];
+            float t2 = S * gw;
+            float buf = t1 + t2;
+            p[i] = p[i] - buf;
+            x1[i] = buf;
+        }
+    }
+    free(u);
     return 0;
 }
 
@@ -652,6 +732,7 @@ int orc_optim32_step(int kind, const double* hp, int step, float* p, const void*
 {
     if (optim_check(kind, hp, step) != 0) return -1;
     optim_scalars s = optim_prepare(kind, hp, step);
+    if (is_layerwise(kind)) return layerwise32(kind, hp, &s, p, g, gdt, n, x1, x2);
     float dummy = 0.0f;
     for (int64_t i = 0; i < n; i++)
         optim_elem(&s, load_elem(g, gdt, i), &p[i], &x1[i], optim_states(kind) == 2 ? &x2[i] : &dummy);
@@ -669,6 +750,24 @@ int orc_optim8bit_step(int kind, const double* hp, int step, float* p, const voi
     if (optim_check(kind, hp, step) != 0) return -1;
     const int two = optim_states(kind) == 2;
     optim_scalars s = optim_prepare(kind, hp, step);
+    if (is_layerwise(kind)) {
+        /* the norms span the whole tensor: decode every block, take the
+         * binary32 step, quantize every block again */
+        size_t bytes = sizeof(float) * (size_t)(n > 0 ? n : 1);
+        float* x = (float*)malloc(bytes);
+        float* y = (float*)malloc(bytes);
+        int rc = -1;
+        if (x && y) {
+            orc_dequantize_blockwise(c1, a1, ORC_DYN8, B, n, x, ORC_F32);
+            if (two) orc_dequantize_blockwise(c2, a2, ORC_DYN8, B, n, y, ORC_F32);
+            rc = layerwise32(kind, hp, &s, p, g, gdt, n, x, two ? y : NULL);
+            if (rc == 0) rc = orc_quantize_blockwise(x, ORC_F32, n, ORC_DYN8, B, c1, a1);
+            if (rc == 0 && two) rc = orc_quantize_blockwise(y, ORC_F32, n, ORC_DYN8, B, c2, a2);
+        }
+        free(x);
+        free(y);
+        return rc;
+    }
     float cb[256];
     orc_dyn8_codebook(cb);
     float* xb = (float*)malloc(sizeof(float) * (size_t)B);
