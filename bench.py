@@ -269,12 +269,22 @@ OPTIMIZERS = {  # name: (qb kind, hyperparameters, states)
     "lion": (2, dict(lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.1), 1),
     "sgd": (3, dict(lr=1e-2, beta1=0.9, weight_decay=1e-4), 1),
     "rmsprop": (4, dict(lr=1e-3, beta2=0.99, eps=1e-8, weight_decay=0.0), 1),
+    "lamb": (5, dict(lr=2e-3, beta1=0.9, beta2=0.999, eps=1e-6, weight_decay=0.01), 2),
+    "lars": (6, dict(lr=0.5, beta1=0.9, weight_decay=5e-4, trust_coefficient=1e-3), 1),
 }
+LAYERWISE = ("lamb", "lars")
 
 
 def optim_bytes_per_param(states, grad_bytes=2, block=ADAM_BLOCK):
     # p read+write (8), grad read, each state's code read+write (2) and absmax read+write per block
     return 8 + grad_bytes + states * (2 + 8.0 / block)
+
+
+def layerwise_extra_bytes_per_param(name, state_bits, grad_bytes=2, block=ADAM_BLOCK):
+    # the norm pass before the step: p and g (LARS), plus the states read (LAMB)
+    if name == "lars":
+        return 4 + grad_bytes
+    return 4 + grad_bytes + (2 * (1 + 4.0 / block) if state_bits == 8 else 8)
 
 
 def bench_flat(torch, qb, inputs, dev, args):
@@ -297,8 +307,18 @@ def bench_flat(torch, qb, inputs, dev, args):
         a1 = a2 = None
     grads = [inputs.normal(n, 1e-3, inputs.grad_seed(args.seed, 0, k), device=dev, dtype=torch.bfloat16) for k in range(2)]
 
+    layerwise = args.optimizer in LAYERWISE
+    if layerwise:               # one tensor = one layer, through the multi-tensor call (norm pass + step)
+        tables = [qb.tensor_table([(p, grads[j], s1, s2, a1, a2)]) for j in range(2)]
+        ws = torch.empty(qb.qb_optimizer_workspace_bytes(qb.optim_hparams(kind, **hp), tables[0], 1, ADAM_BLOCK),
+                         dtype=torch.uint8, device=dev)
+
     def step(k):
-        qb.qb_optimizer8bit_step(qb.optim_hparams(kind, step=k, **hp), p, grads[k % 2], n, s1, s2, a1, a2, ADAM_BLOCK)
+        h = qb.optim_hparams(kind, step=k, **hp)
+        if layerwise:
+            qb.qb_multi_tensor_optimizer_step(h, tables[k % 2], 1, qb.QB_BF16, ADAM_BLOCK, ws)
+        else:
+            qb.qb_optimizer8bit_step(h, p, grads[k % 2], n, s1, s2, a1, a2, ADAM_BLOCK)
 
     torch.cuda.synchronize()
     for k in range(1, args.warmup + 1):
@@ -315,8 +335,11 @@ def bench_flat(torch, qb, inputs, dev, args):
     ms = sorted(a.elapsed_time(b) for a, b in evs)
     med = ms[len(ms) // 2]
     bpp = optim_bytes_per_param(states) if args.state_bits == 8 else 8 + 2 + 8 * states
+    if layerwise:
+        bpp += layerwise_extra_bytes_per_param(args.optimizer, args.state_bits)
     nbytes = n * bpp
-    print(json.dumps({"workload": f"flat 1.5e9 fp32 params, bf16 grads, block 2048, single-tensor {args.optimizer} "
+    call = "one-layer multi-tensor call (norm pass + step)" if layerwise else "single-tensor"
+    print(json.dumps({"workload": f"flat 1.5e9 fp32 params, bf16 grads, block 2048, {call} {args.optimizer} "
                                   f"step, {args.state_bits}-bit states", "optimizer": args.optimizer,
                       "state_bits": args.state_bits, "steps": args.steps, "median_ms": med,
                       "bytes_per_param": bpp, "GB/s": nbytes / med / 1e6,

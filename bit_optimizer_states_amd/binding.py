@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("QB_LIBRARY") or os.path.join(_HERE, "libqb.so")
 QB_OK, QB_EINVAL, QB_EALIGN, QB_EUNSUPPORTED, QB_EHIP, QB_EWORKSPACE, QB_EINIT = range(7)
 QB_F32, QB_F16, QB_BF16 = 0, 1, 2
 QB_DYN8, QB_NF4, QB_FP4 = 0, 1, 2
-QB_ADAMW, QB_ADAM, QB_LION, QB_SGD, QB_RMSPROP = range(5)
+QB_ADAMW, QB_ADAM, QB_LION, QB_SGD, QB_RMSPROP, QB_LAMB, QB_LARS = range(7)
 
 _DTYPE = {torch.float32: QB_F32, torch.float16: QB_F16, torch.bfloat16: QB_BF16}
 
@@ -41,7 +41,8 @@ class qb_adamw_hparams(ctypes.Structure):
 class qb_optim_hparams(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("lr", ctypes.c_double), ("beta1", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
-                ("dampening", ctypes.c_double), ("nesterov", ctypes.c_int32), ("step", ctypes.c_int32)]
+                ("dampening", ctypes.c_double), ("nesterov", ctypes.c_int32), ("step", ctypes.c_int32),
+                ("trust_coefficient", ctypes.c_double)]
 
 
 class qb_tensor(ctypes.Structure):
@@ -83,6 +84,9 @@ def lib():
                                             vp]
         L.qb_multi_tensor_optimizer_step.argtypes = [ctypes.POINTER(qb_optim_hparams), ctypes.POINTER(qb_tensor), i32,
                                                      i32, i32, vp, sz, vp]
+        L.qb_optimizer_workspace_bytes.argtypes = [ctypes.POINTER(qb_optim_hparams), ctypes.POINTER(qb_tensor), i32,
+                                                   i32]
+        L.qb_optimizer_workspace_bytes.restype = sz
         L.qb_code_table_bytes.argtypes = []
         L.qb_code_table_bytes.restype = sz
         L.qb_linear_code.argtypes = [vp]
@@ -185,9 +189,9 @@ def qb_adamw8bit_step(p, g, n, m, v, absmax_m, absmax_v, blocksize, hp, stream=N
 
 
 def optim_hparams(kind, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, dampening=0.0, nesterov=False,
-                  step=1):
+                  step=1, trust_coefficient=0.0):
     return qb_optim_hparams(int(kind), lr, beta1, beta2, eps, weight_decay, dampening, 1 if nesterov else 0,
-                            int(step))
+                            int(step), trust_coefficient)
 
 
 def qb_optimizer8bit_step(hp, p, g, n, state1, state2, absmax1, absmax2, blocksize, stream=None):
@@ -204,6 +208,10 @@ def tensor_table(tensors):
     for i, (p, g, m, v, am, av) in enumerate(tensors):
         arr[i] = qb_tensor(_ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(am), _ptr(av), p.numel())
     return arr
+
+
+def qb_optimizer_workspace_bytes(hp, table, count, blocksize):
+    return lib().qb_optimizer_workspace_bytes(ctypes.byref(hp), table, int(count), int(blocksize))
 
 
 def qb_multi_tensor_optimizer_step(hp, table, count, gdt, blocksize, ws, stream=None):

@@ -64,6 +64,8 @@ bool valid_optim(const qb_optim_hparams* hp)
         return hp->beta1 > 0 && hp->beta1 < 1 && hp->dampening >= 0 && hp->dampening <= 1 &&
                (hp->nesterov == 0 || (hp->nesterov == 1 && hp->dampening == 0));
     case QB_RMSPROP: return unit(hp->beta2) && finite(hp->eps) && hp->eps > 0;
+    case QB_LAMB: return unit(hp->beta1) && unit(hp->beta2) && finite(hp->eps) && hp->eps > 0;
+    case QB_LARS: return unit(hp->beta1) && finite(hp->trust_coefficient) && hp->trust_coefficient > 0;
     default: return false;
     }
 }
@@ -81,7 +83,8 @@ qb_optim_hparams as_optim(const qb_adamw_hparams* hp)
     return o;
 }
 
-int optim_states(qb_optimizer k) { return (k == QB_ADAMW || k == QB_ADAM) ? 2 : 1; }
+int optim_states(qb_optimizer k) { return (k == QB_ADAMW || k == QB_ADAM || k == QB_LAMB) ? 2 : 1; }
+bool layerwise(qb_optimizer k) { return k == QB_LAMB || k == QB_LARS; }
 
 // Checks one tensor of an optimizer step.  absmax1 == NULL selects binary32
 // states (state1, state2 are float arrays; absmax2 must be NULL too).
@@ -133,10 +136,10 @@ OptScalars prepare(const qb_optim_hparams& hp)
     s.wd = (float)hp.weight_decay;
     s.lr = (float)hp.lr;
     s.omd = (float)(1.0 - hp.dampening);
-    if (hp.kind == QB_ADAMW || hp.kind == QB_ADAM) {
+    if (hp.kind == QB_ADAMW || hp.kind == QB_ADAM || hp.kind == QB_LAMB) {
         const double p1 = beta_power(hp.beta1, hp.step, 0);
         const double p2 = beta_power(hp.beta2, hp.step, 1);
-        s.s1 = (float)(hp.lr / (1.0 - p1));
+        s.s1 = (float)((hp.kind == QB_LAMB ? 1.0 : hp.lr) / (1.0 - p1));   // LAMB: the direction without lr
         s.s2 = (float)(1.0 / std::sqrt(1.0 - p2));
     }
     s.flags = (hp.nesterov ? kOptNesterov : 0) | (hp.step == 1 ? kOptFirstStep : 0);
@@ -223,6 +226,26 @@ size_t map_region_bytes(int32_t count)
     return count > 0 ? round_up((size_t)count * 64 + ((size_t)count + 1) * sizeof(int64_t) +
                                     ((size_t)max_tile_buckets(count) + 1) * sizeof(int32_t), 256)
                      : 0;
+}
+
+// Norm groups of a tensor: kNormGroupTiles optimizer tiles each.
+int64_t norm_groups(int64_t n, int32_t B)
+{
+    return (adamw_tiles(n, B) + kNormGroupTiles - 1) / kNormGroupTiles;
+}
+
+// Workspace of a layer-wise step: the tile map region, the group map region,
+// then 16 bytes of partial sums per group, then one float S per tensor.
+// Returns the bytes; with ws given, sets *part and *trust to their addresses.
+size_t layerwise_ws_layout(int32_t count, int64_t groups, void* ws, double** part, float** trust)
+{
+    const size_t m = 2 * map_region_bytes(count);
+    const size_t pb = round_up((size_t)groups * 2 * sizeof(double), 256);
+    if (ws) {
+        *part = reinterpret_cast<double*>(static_cast<char*>(ws) + m);
+        *trust = reinterpret_cast<float*>(static_cast<char*>(ws) + m + pb);
+    }
+    return m + pb + round_up((size_t)count * sizeof(float), 256);
 }
 
 int64_t quant_tiles(int64_t n, int32_t B)
@@ -569,6 +592,7 @@ qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void
                                 void* stream)
 {
     if (n < 0 || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_optim(hp)) return QB_EINVAL;
+    if (layerwise(hp->kind)) return QB_EUNSUPPORTED;
     if (n == 0) return QB_OK;
     const bool two = optim_states(hp->kind) == 2;
     if (!two) {
@@ -581,7 +605,20 @@ qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void
     if (!device_tables()) return QB_EINIT;
     TensorDesc d{p, g, state1, state2, absmax1, absmax2, n, 0};
     return hip_status(launch_optim8((int)hp->kind, d, nullptr, adamw_tiles(n, blocksize), blocksize, (int)gdt,
-                                    prepare(*hp), static_cast<hipStream_t>(stream)));
+                                    prepare(*hp), nullptr, static_cast<hipStream_t>(stream)));
+}
+
+size_t qb_optimizer_workspace_bytes(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
+                                    int32_t blocksize)
+{
+    if (!hp || count < 0 || (count > 0 && !tensors) || !pow2_block(blocksize)) return 0;
+    if (!layerwise(hp->kind)) return qb_multi_tensor_workspace_bytes(count);
+    int64_t groups = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        if (tensors[i].n < 0) return 0;
+        groups += norm_groups(tensors[i].n, blocksize);
+    }
+    return layerwise_ws_layout(count, groups, nullptr, nullptr, nullptr);
 }
 
 qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
@@ -609,15 +646,42 @@ qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_te
     }
     if (table.empty()) return QB_OK;
     if (tiles >= (int64_t(1) << 31)) return QB_EINVAL;
+    double* part = nullptr;
+    float* trust = nullptr;
+    thread_local std::vector<TensorDesc> gtable;      // the same tensors, numbered by norm group
+    int64_t groups = 0;
+    if (layerwise(hp->kind)) {
+        gtable = table;
+        for (TensorDesc& d : gtable) {
+            d.tile_begin = groups;
+            groups += norm_groups(d.n, blocksize);
+        }
+        if (ws_bytes < layerwise_ws_layout(count, groups, ws, &part, &trust)) return QB_EWORKSPACE;
+    }
     if (!device_tables()) return QB_EINIT;
     hipStream_t s = static_cast<hipStream_t>(stream);
     thread_local std::vector<unsigned char> staging;
     staging.clear();
     TileMap<TensorDesc> map;
+    const OptScalars hs = prepare(*hp);
+    if (layerwise(hp->kind)) {
+        TileMap<TensorDesc> gmap;
+        stage_tile_map(staging, 0, table, tiles, count, ws, &map);
+        stage_tile_map(staging, map_region_bytes(count), gtable, groups, count, ws, &gmap);
+        qb_status st = copy_staging(staging, ws, s);
+        if (st != QB_OK) return st;
+        hipError_t e = launch_trust_norms((int)hp->kind, gmap, groups, blocksize, (int)gdt, hs, part, s);
+        if (e == hipSuccess)
+            e = launch_trust_scalars((int)hp->kind, gmap, part, hp->lr, hp->weight_decay, hp->trust_coefficient,
+                                     trust, s);
+        if (e == hipSuccess)
+            e = launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)gdt, hs, trust, s);
+        return hip_status(e);
+    }
     stage_tile_map(staging, 0, table, tiles, count, ws, &map);
     qb_status st = copy_staging(staging, ws, s);
     if (st != QB_OK) return st;
-    return hip_status(launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)gdt, prepare(*hp), s));
+    return hip_status(launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)gdt, hs, nullptr, s));
 }
 
 qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, uint8_t* m, uint8_t* v,

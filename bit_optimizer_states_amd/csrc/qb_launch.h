@@ -19,7 +19,8 @@ constexpr size_t kBinWords = (size_t)kBinCopies * 256;
 constexpr size_t kBinBytes = kBinWords * sizeof(unsigned long long);
 
 // Optimizer kinds of the fused 8-bit step (the values of qb_optimizer).
-enum OptKind { OPT_ADAMW = 0, OPT_ADAM = 1, OPT_LION = 2, OPT_SGD = 3, OPT_RMSPROP = 4 };
+enum OptKind { OPT_ADAMW = 0, OPT_ADAM = 1, OPT_LION = 2, OPT_SGD = 3, OPT_RMSPROP = 4, OPT_LAMB = 5, OPT_LARS = 6 };
+constexpr bool opt_layerwise(int opt) { return opt == OPT_LAMB || opt == OPT_LARS; }
 constexpr int32_t kOptNesterov = 1, kOptFirstStep = 2;
 
 // Host scalars of one step, each computed in binary64 and rounded once:
@@ -27,7 +28,11 @@ constexpr int32_t kOptNesterov = 1, kOptFirstStep = 2;
 //            dec = 1 - lr*wd (AdamW), eps, wd (Adam's L2 term);
 //   Lion     b1, ob1, b2, ob2, lr, dec = 1 - lr*wd;
 //   SGD      b1 = momentum, omd = 1 - dampening, lr, wd, flags;
-//   RMSprop  b2 = alpha, ob2 = 1 - alpha, lr, eps, wd.
+//   RMSprop  b2 = alpha, ob2 = 1 - alpha, lr, eps, wd;
+//   LAMB     Adam's b1 .. s2 with s1 = 1 / (1 - b1^t) (no lr), eps, wd;
+//   LARS     b1 = momentum, wd.
+// The layer-wise kinds take their per-tensor S = (float)(lr * ratio) from a
+// device array in place of lr.
 struct OptScalars {
     float b1, ob1, b2, ob2, s1, s2, dec, eps;
     float wd, lr, omd;
@@ -201,8 +206,22 @@ constexpr int64_t dequant_tile_elems(int bits, bool multi)
 }
 // Fused 8-bit step of optimizer `opt` (OptKind) on one tensor (map ==
 // nullptr) or on the tensors of map.
+// trust: the per-tensor step scalars S of the layer-wise kinds (indexed like
+// map->descs), nullptr for the others.
 hipError_t launch_optim8(int opt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B,
-                         int gdt, const OptScalars& hs, hipStream_t s);
+                         int gdt, const OptScalars& hs, const float* trust, hipStream_t s);
+
+// Layer-wise kinds, before launch_optim8: per group of kNormGroupTiles
+// consecutive optimizer tiles of one tensor (gmap: the tensors with
+// tile_begin = their first group; ngroups in all), the partial sums of |p|^2
+// and of |u|^2 (LAMB) or |g|^2 (LARS) in binary64 (part[2 * group],
+// part[2 * group + 1]); then one workgroup per tensor adds its groups' partials
+// in a fixed order and writes trust[tensor] = (float)(lr * ratio).
+constexpr int64_t kNormGroupTiles = 32;
+hipError_t launch_trust_norms(int opt, const TileMap<TensorDesc>& gmap, int64_t ngroups, int B, int gdt,
+                              const OptScalars& hs, double* part, hipStream_t s);
+hipError_t launch_trust_scalars(int opt, const TileMap<TensorDesc>& gmap, const double* part, double lr,
+                                double weight_decay, double trust_coefficient, float* trust, hipStream_t s);
 
 // Tiles of the optimizer kernel for a tensor of n elements at block size B.
 int64_t adamw_tiles(int64_t n, int B);

@@ -1,5 +1,6 @@
 // qb_optim.hip -- fused 8-bit optimizer steps: AdamW, Adam, Lion, SGD with
-// momentum and RMSprop, each state held as block-wise dynamic 8-bit codes.
+// momentum, RMSprop and the layer-wise LAMB and LARS, each state held as
+// block-wise dynamic 8-bit codes.
 //
 // The 8-bit optimizer keeps its states as block-wise dynamic 8-bit codes plus
 // one fp32 absmax per block (abstract quoted on "Py之bitsandbytes：
@@ -115,8 +116,23 @@ __device__ __forceinline__ void block_max2(uint32_t& x, uint32_t& y, uint32_t (*
     }
 }
 
-// States of an optimizer kind: two (m, v) for Adam(W), one otherwise.
-constexpr int opt_states(int opt) { return (opt == OPT_ADAMW || opt == OPT_ADAM) ? 2 : 1; }
+// States of an optimizer kind: two (m, v) for Adam(W) and LAMB, one otherwise.
+constexpr int opt_states(int opt) { return (opt == OPT_ADAMW || opt == OPT_ADAM || opt == OPT_LAMB) ? 2 : 1; }
+
+// LAMB's moments and direction: x, y become m', v' (separately rounded, as
+// they decide the codes); returns u = r + wd*p with r = s1*m'/(sqrt(v')*s2 +
+// eps) from hardware square root and reciprocal.  The norm pass and the step
+// both call this, so they see the same u bit for bit.
+__device__ __forceinline__ float lamb_dir(const OptScalars& hs, float gi, float p, float& x, float& y)
+{
+    const float mm = hs.b1 * x + hs.ob1 * gi;
+    const float vv = hs.b2 * y + hs.ob2 * (gi * gi);
+    const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(vv), hs.s2, hs.eps);
+    const float r = hs.s1 * (mm * __builtin_amdgcn_rcpf(den));
+    x = mm;
+    y = vv;
+    return __builtin_fmaf(hs.wd, p, r);
+}
 
 // One element of the update, binary32.  x, y: the decoded states (y for the
 // two-state kinds), replaced by the updated ones; p updated in place.  The
@@ -159,13 +175,22 @@ __device__ __forceinline__ void opt_elem(const OptScalars& hs, float gi, float& 
         const float dir = (hs.flags & kOptNesterov) ? gw + hs.b1 * buf : buf;
         p = p - hs.lr * dir;
         x = buf;
-    } else {                                               // RMSprop
+    } else if constexpr (OPT == OPT_RMSPROP) {
         const float t = hs.wd * p;
         const float gw = gi + t;
         const float vv = hs.b2 * x + hs.ob2 * (gw * gw);
         const float den = __builtin_sqrtf(vv) + hs.eps;
         p = p - hs.lr * (gw / den);
         x = vv;
+    } else if constexpr (OPT == OPT_LAMB) {               // hs.lr = the tensor's S
+        const float u = lamb_dir(hs, gi, p, x, y);
+        p = __builtin_fmaf(-hs.lr, u, p);
+    } else {                                               // LARS; hs.lr = the tensor's S
+        const float t = hs.wd * p;
+        const float gw = gi + t;
+        const float buf = hs.b1 * x + hs.lr * gw;
+        p = p - buf;
+        x = buf;
     }
 }
 
@@ -232,8 +257,9 @@ __device__ __forceinline__ void optim32_tile(const TensorDesc& d, int64_t lt, co
 }
 
 template <int OPT, int B, int GDT, bool MULTI>
-__global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, TileMap<TensorDesc> map, OptScalars hs,
-                                                         const QbTables* __restrict__ tab)
+__global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, TileMap<TensorDesc> map, OptScalars hs0,
+                                                         const QbTables* __restrict__ tab,
+                                                         const float* __restrict__ trust)
 {
     using T = TileA<B>;
     constexpr bool TWO = opt_states(OPT) == 2;
@@ -246,9 +272,12 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
 
     TensorDesc d;
     int64_t lt;
+    OptScalars hs = hs0;
     if constexpr (MULTI) {
-        d = map.descs[find_tensor(map, tile)];
+        const int ti = find_tensor(map, tile);
+        d = map.descs[ti];
         lt = tile - d.tile_begin;
+        if constexpr (opt_layerwise(OPT)) hs.lr = trust[ti];
     } else {
         d = single;
         lt = tile;
@@ -409,6 +438,171 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
     }
 }
 
+// Layer-wise kinds, first pass: one workgroup per group of kNormGroupTiles
+// consecutive optimizer tiles of one tensor (the tiles of k_optim8) adds |p|^2
+// and |u|^2 (LAMB: u from the decoded states, as the step will compute it) or
+// |g|^2 (LARS) in binary64: each thread over its own elements, tile after
+// tile, then across the wave (butterfly) and the waves (in order).  The same
+// bits on every run.
+template <int OPT, int B, int GDT>
+__global__ __launch_bounds__(kAdamThreads) void k_trust_norms(TileMap<TensorDesc> gmap, OptScalars hs,
+                                                              const QbTables* __restrict__ tab,
+                                                              double* __restrict__ part)
+{
+    using T = TileA<B>;
+    constexpr bool LAMB = OPT == OPT_LAMB;
+    __shared__ float s_dyn[256];
+    __shared__ double s_red[2][T::NT / 64];
+    const int tid = threadIdx.x;
+    const int64_t grp = tile_of<QB_TILE_REMAP>(blockIdx.x, gridDim.x);
+    const TensorDesc d = gmap.descs[find_tensor(gmap, grp)];
+    const int64_t tiles = (d.n + T::ELEMS - 1) / T::ELEMS;
+    const int64_t lt0 = (grp - d.tile_begin) * kNormGroupTiles;
+    const int64_t lt1 = lt0 + kNormGroupTiles < tiles ? lt0 + kNormGroupTiles : tiles;
+    const int bt = tid / T::LPB, l = tid % T::LPB;
+    const int64_t nbl = (d.n + B - 1) / B;
+    const bool s8 = d.am != nullptr;                       // uniform per workgroup
+    const uint32_t lofs = (uint32_t)(bt * B + l * T::CW);
+    if (LAMB && s8) {
+#pragma unroll
+        for (int r = 0; r < (256 + T::NT - 1) / T::NT; ++r)
+            if (T::NT <= 256 || tid < 256) s_dyn[r * T::NT + tid] = tab->dyn8[r * T::NT + tid];
+        __syncthreads();
+    }
+    double sp = 0.0, sq = 0.0;
+    for (int64_t lt = lt0; lt < lt1; ++lt) {
+        const int64_t blk = lt * T::BPT + bt;
+        const int64_t tbase = lt * T::ELEMS;
+        const int64_t lrem = d.n - tbase;
+        const bool full = T::ELEMS <= lrem;
+        float* const pt = d.p + tbase;
+        const void* const gt = static_cast<const char*>(d.g) + tbase * (GDT == DT_F32 ? 4 : 2);
+        float am0 = 0.0f, av0 = 0.0f;
+        if (LAMB && s8 && blk < nbl) {
+            am0 = gld<float>(d.am + blk);
+            av0 = gld<float>(d.av + blk);
+        }
+        // elements past the end read as p = g = 0 and state 0: they add exactly 0
+        float p[T::EPT], g[T::EPT], x[T::EPT], y[T::EPT];
+        uint32_t cmw[T::EPT / 4], cvw[T::EPT / 4];
+#pragma unroll
+        for (int i = 0; i < T::EPT; ++i) x[i] = y[i] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < T::EPT / 4; ++w) cmw[w] = cvw[w] = 0x7F7F7F7Fu;
+        if (full) {
+#pragma unroll
+            for (int c = 0; c < T::CH; ++c) {
+                const uint32_t e = lofs + c * T::LPB * T::CW;
+                load_chunk<DT_F32, T::CW>(pt, e, &p[c * T::CW]);
+                load_chunk<GDT, T::CW>(gt, e, &g[c * T::CW]);
+                if constexpr (LAMB) {
+                    if (s8) {
+                        load_codes<T::CW>(d.m + tbase, e, &cmw[c * T::CW / 4]);
+                        load_codes<T::CW>(d.v + tbase, e, &cvw[c * T::CW / 4]);
+                    } else {
+                        load_chunk<DT_F32, T::CW>(reinterpret_cast<float*>(d.m) + tbase, e, &x[c * T::CW]);
+                        load_chunk<DT_F32, T::CW>(reinterpret_cast<float*>(d.v) + tbase, e, &y[c * T::CW]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < T::EPT; ++i) {
+                const uint32_t e = lofs + (i / T::CW) * T::LPB * T::CW + (i % T::CW);
+                const bool in = (int64_t)e < lrem;
+                p[i] = in ? load1<DT_F32>(pt, e) : 0.0f;
+                g[i] = in ? load1<GDT>(gt, e) : 0.0f;
+                if constexpr (LAMB) {
+                    if (in && s8) {
+                        const uint32_t sh = 8 * (i & 3), keep = ~(0xFFu << sh);
+                        cmw[i >> 2] = (cmw[i >> 2] & keep) | ((uint32_t)gldo<uint8_t>(d.m + tbase, e) << sh);
+                        cvw[i >> 2] = (cvw[i >> 2] & keep) | ((uint32_t)gldo<uint8_t>(d.v + tbase, e) << sh);
+                    } else if (in) {
+                        x[i] = load1<DT_F32>(reinterpret_cast<float*>(d.m) + tbase, e);
+                        y[i] = load1<DT_F32>(reinterpret_cast<float*>(d.v) + tbase, e);
+                    }
+                }
+            }
+        }
+        if (LAMB && s8) {
+#pragma unroll
+            for (int i = 0; i < T::EPT; ++i) {
+                const uint32_t sh = 8 * (i & 3);
+                x[i] = s_dyn[(cmw[i >> 2] >> sh) & 0xFFu] * am0;
+                y[i] = s_dyn[(cvw[i >> 2] >> sh) & 0xFFu] * av0;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < T::EPT; ++i) {
+            const double pd = (double)p[i];
+            sp = __builtin_fma(pd, pd, sp);                // the square is exact in binary64
+            if constexpr (LAMB) {
+                const double u = (double)lamb_dir(hs, g[i], p[i], x[i], y[i]);
+                sq = __builtin_fma(u, u, sq);
+            } else {
+                const double gd = (double)g[i];
+                sq = __builtin_fma(gd, gd, sq);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        sp += __shfl_xor(sp, off);
+        sq += __shfl_xor(sq, off);
+    }
+    if ((tid & 63) == 0) {
+        s_red[0][tid >> 6] = sp;
+        s_red[1][tid >> 6] = sq;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double a = 0.0, b = 0.0;
+#pragma unroll
+        for (int w = 0; w < T::NT / 64; ++w) {
+            a += s_red[0][w];
+            b += s_red[1][w];
+        }
+        part[2 * grp] = a;
+        part[2 * grp + 1] = b;
+    }
+}
+
+// Layer-wise kinds, second pass: workgroup i adds the partial sums of tensor
+// i's groups (thread t: groups t, t + 256, ... in order; then the butterfly
+// and the waves in order), takes the norms and the ratio in binary64 and writes
+// trust[i] = (float)(lr * ratio); a zero norm makes the ratio 1.
+__global__ __launch_bounds__(256) void k_trust_scalars(TileMap<TensorDesc> gmap, const double* __restrict__ part,
+                                                       int lamb, double lr, double wd, double eta,
+                                                       float* __restrict__ trust)
+{
+    __shared__ double s_red[2][4];
+    const int i = blockIdx.x, tid = threadIdx.x;
+    const int64_t t0 = gmap.tile_begin[i], t1 = gmap.tile_begin[i + 1];
+    double a = 0.0, b = 0.0;
+    for (int64_t t = t0 + tid; t < t1; t += 256) {
+        a += part[2 * t];
+        b += part[2 * t + 1];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off);
+        b += __shfl_xor(b, off);
+    }
+    if ((tid & 63) == 0) {
+        s_red[0][tid >> 6] = a;
+        s_red[1][tid >> 6] = b;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const double sp = ((s_red[0][0] + s_red[0][1]) + s_red[0][2]) + s_red[0][3];
+        const double sq = ((s_red[1][0] + s_red[1][1]) + s_red[1][2]) + s_red[1][3];
+        const double pn = __builtin_sqrt(sp), qn = __builtin_sqrt(sq);
+        double ratio = 1.0;
+        if (pn > 0.0 && qn > 0.0) ratio = lamb ? pn / qn : (eta * pn) / (qn + wd * pn);
+        trust[i] = (float)(lr * ratio);
+    }
+}
+
 int64_t adamw_tiles(int64_t n, int B)
 {
     const int64_t elems = (int64_t)kAdamThreads * (B >= 4 * kAdamThreads ? B / kAdamThreads : 4);
@@ -417,42 +611,75 @@ int64_t adamw_tiles(int64_t n, int B)
 
 namespace {
 
+// Launch arguments shared by the optimizer launches.
+struct OptLaunch {
+    const TensorDesc* single;
+    const TileMap<TensorDesc>* map;
+    int64_t ntiles;
+    const OptScalars* hs;
+    const QbTables* tab;
+    const float* trust;      // k_optim8 of the layer-wise kinds
+    double* part;            // non-null: launch k_trust_norms instead
+    hipStream_t s;
+};
+
 template <int OPT, int B, int GDT>
-hipError_t optim_as(const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, const OptScalars& hs,
-                    const QbTables* tab, hipStream_t s)
+hipError_t optim_as(const OptLaunch& a)
 {
     static_assert(TileA<B>::ELEMS == kAdamThreads * (B >= 4 * kAdamThreads ? B / kAdamThreads : 4), "tile size");
-    if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    if (map)
-        return launch_kernel_nt(k_optim8<OPT, B, GDT, true>, (int)ntiles, kAdamThreads, s, single, *map, hs, tab);
-    return launch_kernel_nt(k_optim8<OPT, B, GDT, false>, (int)ntiles, kAdamThreads, s, single,
-                            TileMap<TensorDesc>{}, hs, tab);
+    if (a.ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if constexpr (opt_layerwise(OPT)) {                   // multi-tensor only (the norms need a workspace)
+        if (!a.map) return hipErrorInvalidValue;
+        if (a.part)
+            return launch_kernel_nt(k_trust_norms<OPT, B, GDT>, (int)a.ntiles, kAdamThreads, a.s, *a.map, *a.hs,
+                                    a.tab, a.part);
+        return launch_kernel_nt(k_optim8<OPT, B, GDT, true>, (int)a.ntiles, kAdamThreads, a.s, *a.single, *a.map,
+                                *a.hs, a.tab, a.trust);
+    } else {
+        if (a.map)
+            return launch_kernel_nt(k_optim8<OPT, B, GDT, true>, (int)a.ntiles, kAdamThreads, a.s, *a.single,
+                                    *a.map, *a.hs, a.tab, (const float*)nullptr);
+        return launch_kernel_nt(k_optim8<OPT, B, GDT, false>, (int)a.ntiles, kAdamThreads, a.s, *a.single,
+                                TileMap<TensorDesc>{}, *a.hs, a.tab, (const float*)nullptr);
+    }
 }
 
 template <int OPT, int B>
-hipError_t optim_dt(int gdt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles,
-                    const OptScalars& hs, const QbTables* tab, hipStream_t s)
+hipError_t optim_dt(int gdt, const OptLaunch& a)
 {
     switch (gdt) {
-    case DT_F32: return optim_as<OPT, B, DT_F32>(single, map, ntiles, hs, tab, s);
-    case DT_F16: return optim_as<OPT, B, DT_F16>(single, map, ntiles, hs, tab, s);
-    case DT_BF16: return optim_as<OPT, B, DT_BF16>(single, map, ntiles, hs, tab, s);
+    case DT_F32: return optim_as<OPT, B, DT_F32>(a);
+    case DT_F16: return optim_as<OPT, B, DT_F16>(a);
+    case DT_BF16: return optim_as<OPT, B, DT_BF16>(a);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int OPT>
-hipError_t optim_b(int B, int gdt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles,
-                   const OptScalars& hs, const QbTables* tab, hipStream_t s)
+hipError_t optim_b(int B, int gdt, const OptLaunch& a)
 {
     switch (B) {
-    case 64: return optim_dt<OPT, 64>(gdt, single, map, ntiles, hs, tab, s);
-    case 128: return optim_dt<OPT, 128>(gdt, single, map, ntiles, hs, tab, s);
-    case 256: return optim_dt<OPT, 256>(gdt, single, map, ntiles, hs, tab, s);
-    case 512: return optim_dt<OPT, 512>(gdt, single, map, ntiles, hs, tab, s);
-    case 1024: return optim_dt<OPT, 1024>(gdt, single, map, ntiles, hs, tab, s);
-    case 2048: return optim_dt<OPT, 2048>(gdt, single, map, ntiles, hs, tab, s);
-    case 4096: return optim_dt<OPT, 4096>(gdt, single, map, ntiles, hs, tab, s);
+    case 64: return optim_dt<OPT, 64>(gdt, a);
+    case 128: return optim_dt<OPT, 128>(gdt, a);
+    case 256: return optim_dt<OPT, 256>(gdt, a);
+    case 512: return optim_dt<OPT, 512>(gdt, a);
+    case 1024: return optim_dt<OPT, 1024>(gdt, a);
+    case 2048: return optim_dt<OPT, 2048>(gdt, a);
+    case 4096: return optim_dt<OPT, 4096>(gdt, a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t optim_kind(int opt, int B, int gdt, const OptLaunch& a)
+{
+    switch (opt) {
+    case OPT_ADAMW: return optim_b<OPT_ADAMW>(B, gdt, a);
+    case OPT_ADAM: return optim_b<OPT_ADAM>(B, gdt, a);
+    case OPT_LION: return optim_b<OPT_LION>(B, gdt, a);
+    case OPT_SGD: return optim_b<OPT_SGD>(B, gdt, a);
+    case OPT_RMSPROP: return optim_b<OPT_RMSPROP>(B, gdt, a);
+    case OPT_LAMB: return optim_b<OPT_LAMB>(B, gdt, a);
+    case OPT_LARS: return optim_b<OPT_LARS>(B, gdt, a);
     default: return hipErrorInvalidValue;
     }
 }
@@ -460,18 +687,30 @@ hipError_t optim_b(int B, int gdt, const TensorDesc& single, const TileMap<Tenso
 }  // namespace
 
 hipError_t launch_optim8(int opt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B,
-                         int gdt, const OptScalars& hs, hipStream_t s)
+                         int gdt, const OptScalars& hs, const float* trust, hipStream_t s)
 {
     const QbTables* tab = device_tables();
     if (!tab) return hipErrorNotInitialized;
-    switch (opt) {
-    case OPT_ADAMW: return optim_b<OPT_ADAMW>(B, gdt, single, map, ntiles, hs, tab, s);
-    case OPT_ADAM: return optim_b<OPT_ADAM>(B, gdt, single, map, ntiles, hs, tab, s);
-    case OPT_LION: return optim_b<OPT_LION>(B, gdt, single, map, ntiles, hs, tab, s);
-    case OPT_SGD: return optim_b<OPT_SGD>(B, gdt, single, map, ntiles, hs, tab, s);
-    case OPT_RMSPROP: return optim_b<OPT_RMSPROP>(B, gdt, single, map, ntiles, hs, tab, s);
-    default: return hipErrorInvalidValue;
-    }
+    if (opt_layerwise(opt) && !trust) return hipErrorInvalidValue;
+    return optim_kind(opt, B, gdt, OptLaunch{&single, map, ntiles, &hs, tab, trust, nullptr, s});
+}
+
+hipError_t launch_trust_norms(int opt, const TileMap<TensorDesc>& gmap, int64_t ngroups, int B, int gdt,
+                              const OptScalars& hs, double* part, hipStream_t s)
+{
+    const QbTables* tab = device_tables();
+    if (!tab) return hipErrorNotInitialized;
+    if (!opt_layerwise(opt) || !part) return hipErrorInvalidValue;
+    const TensorDesc none{};
+    return optim_kind(opt, B, gdt, OptLaunch{&none, &gmap, ngroups, &hs, tab, nullptr, part, s});
+}
+
+hipError_t launch_trust_scalars(int opt, const TileMap<TensorDesc>& gmap, const double* part, double lr,
+                                double weight_decay, double trust_coefficient, float* trust, hipStream_t s)
+{
+    if (!opt_layerwise(opt) || gmap.count < 1) return hipErrorInvalidValue;
+    return launch_kernel(k_trust_scalars, gmap.count, s, gmap, part, opt == OPT_LAMB ? 1 : 0, lr, weight_decay,
+                         trust_coefficient, trust);
 }
 
 }  // namespace qb

@@ -10,7 +10,7 @@ absmax buffers as one with binary32 states).
 """
 import torch
 
-TWO_STATE_KINDS = (0, 1)        # QB_ADAMW, QB_ADAM
+TWO_STATE_KINDS = (0, 1, 5)     # QB_ADAMW, QB_ADAM, QB_LAMB
 
 
 def uses_8bit(numel, min_8bit_size=4096, force_32bit=False):

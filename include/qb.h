@@ -117,13 +117,32 @@ typedef struct {
  *               (1-dampening)*g; p <- p - lr*(nesterov ? g + momentum*buf : buf).
  *   QB_RMSPROP  state 1 = v (beta2 = alpha):  g <- g + wd*p;
  *               v <- alpha*v + (1-alpha)*g*g;  p <- p - lr*g/(sqrt(v) + eps).
+ * The layer-wise kinds (8-bit LARS and LAMB are listed beside them on page
+ * "Py之bitsandbytes", section 1; the pages give no formulas, so these follow
+ * the published definitions) scale each tensor's step by a ratio of norms over
+ * that whole tensor, one tensor being one layer:
+ *   QB_LAMB     state 1 = m, state 2 = v (You et al., 2019):  Adam's moments,
+ *               r = (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps),  u = r + wd*p,
+ *               p <- p - lr*ratio*u  with ratio = |p| / |u|.
+ *   QB_LARS     state 1 = momentum buffer (beta1 = momentum, in [0, 1);
+ *               You, Gitman and Ginsburg, 2017):
+ *               ratio = trust_coefficient*|p| / (|g| + wd*|p|),
+ *               buf <- momentum*buf + lr*ratio*(g + wd*p),  p <- p - buf.
+ *   The norms (of p, and of u or g) and the ratio are binary64, a zero norm
+ *   makes the ratio 1, and the step takes S = (float)(lr*ratio) as one
+ *   binary32 scalar.  They need a workspace for the norms: only
+ *   qb_multi_tensor_optimizer_step runs them (one tensor is a call with
+ *   count 1).
  * The states and their codes are bit-exact against an IEEE binary32 evaluation
  * of these formulas (each operation rounded on its own, IEEE square root and
- * division).  So is p' for every kind but AdamW, whose states never read p:
- * there p' takes hardware square root and reciprocal and is within 1e-6
- * relative.
+ * division).  So is p' for every kind but AdamW and LAMB, whose states never
+ * read p: there p' takes hardware square root and reciprocal and is within
+ * 1e-6 relative.  The layer-wise kinds add their norms in a fixed order of
+ * their own (run to run the same bits); an evaluation that adds in another
+ * order can differ in the last bits of the binary64 sums, which changes S only
+ * when the ratio lies that close to a binary32 rounding boundary.
  */
-typedef enum { QB_ADAMW = 0, QB_ADAM = 1, QB_LION = 2, QB_SGD = 3, QB_RMSPROP = 4 } qb_optimizer;
+typedef enum { QB_ADAMW = 0, QB_ADAM = 1, QB_LION = 2, QB_SGD = 3, QB_RMSPROP = 4, QB_LAMB = 5, QB_LARS = 6 } qb_optimizer;
 
 /* Hyperparameters of one step of any kind (unused fields are ignored). */
 typedef struct {
@@ -136,6 +155,7 @@ typedef struct {
     double  dampening;     /* SGD */
     int32_t nesterov;      /* SGD: 0 or 1 (1 needs dampening 0) */
     int32_t step;          /* t >= 1 */
+    double  trust_coefficient;   /* LARS: eta > 0 */
 } qb_optim_hparams;
 
 /* One tensor of a multi-tensor step; the fields are those of qb_adamw8bit_step
@@ -292,7 +312,8 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
  * v/absmax_v; state2 and absmax2 are ignored (may be NULL) for the one-state
  * kinds.  Fresh state: every code 127 (0.0), absmax 0.  Invalid
  * hyperparameters for the kind (ranges above; lr, weight_decay >= 0) give
- * QB_EINVAL before anything is launched.
+ * QB_EINVAL before anything is launched; the layer-wise kinds give
+ * QB_EUNSUPPORTED (they run through qb_multi_tensor_optimizer_step).
  * 32-bit fallback: with absmax1 == NULL (and absmax2 == NULL) the states stay
  * binary32: state1 / state2 are float[n] arrays updated in place by the same
  * formulas, with no quantization.  This is the pages' policy for small or
@@ -307,7 +328,12 @@ qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void
 
 /*
  * qb_multi_tensor_optimizer_step -- qb_optimizer8bit_step on `count` tensors in
- * one kernel launch; tensors, ws as for qb_multi_tensor_step.
+ * one kernel launch; tensors, ws as for qb_multi_tensor_step, except that ws
+ * holds qb_optimizer_workspace_bytes(hp, tensors, count, blocksize) bytes.
+ * The layer-wise kinds (QB_LAMB, QB_LARS) take three launches on `stream`:
+ * partial sums of the squared norms per group of optimizer tiles, one
+ * workgroup per tensor that adds them in a fixed order and forms S, then the
+ * fused step; the partial sums and the S of every tensor live in ws.
  */
 qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
                                          qb_dtype gdt, int32_t blocksize, void* ws, size_t ws_bytes,
@@ -354,6 +380,14 @@ qb_status qb_dequantize_code(const uint8_t* codes, const float* absmax, const vo
  * qb_multi_tensor_step, qb_multi_tensor_optimizer_step and qb_multi_tensor_dequantize. */
 size_t qb_dq_workspace_bytes(int64_t n, int32_t blocksize);
 size_t qb_multi_tensor_workspace_bytes(int32_t count);
+
+/* Workspace bytes of qb_multi_tensor_optimizer_step: qb_multi_tensor_workspace_bytes(count)
+ * for the element-wise kinds; for the layer-wise kinds two tables of the
+ * tensors (by optimizer tile and by norm group), 16 bytes per norm group (32
+ * optimizer tiles of max(blocksize, 1024) elements of one tensor) and 4 bytes
+ * per tensor.  0 when hp, tensors or a size is invalid. */
+size_t qb_optimizer_workspace_bytes(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
+                                    int32_t blocksize);
 
 /*
  * qb_codebook -- host: copy the decode table of `code` (indexed by stored code)

@@ -244,6 +244,42 @@ def test_optimizer_hyperparameters_rejected_before_launch(qb):
     assert f(ctypes.byref(H(qb.QB_SGD, 1e-3)), A, A2, 2, 100, A + 4, None, None, None, 2048, None) == qb.QB_EALIGN
 
 
+def test_layerwise_arguments_and_workspace(qb):
+    L = qb.lib()
+    A, A2 = 0x100000, 0x200000
+    H = qb.optim_hparams
+    f = L.qb_optimizer8bit_step
+    bad = [H(qb.QB_LARS, 0.1, beta1=0.9),                                       # no trust coefficient
+           H(qb.QB_LARS, 0.1, beta1=1.0, trust_coefficient=1e-3),
+           H(qb.QB_LARS, 0.1, beta1=0.9, trust_coefficient=float("inf")),
+           H(qb.QB_LAMB, 0.1, eps=0.0),
+           H(qb.QB_LAMB, 0.1, beta2=1.0)]
+    for hp in bad:
+        assert f(ctypes.byref(hp), A, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EINVAL
+    # valid, but the norms need a workspace: the single-tensor call refuses them
+    for hp in (H(qb.QB_LAMB, 1e-3), H(qb.QB_LARS, 0.1, beta1=0.9, trust_coefficient=1e-3)):
+        assert f(ctypes.byref(hp), A, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EUNSUPPORTED
+    # workspace: two tensor tables, 16 bytes per group of 32 tiles (tiles of max(B, 1024) elements),
+    # 4 per tensor
+    tab = (qb.qb_tensor * 3)(qb.qb_tensor(A, A2, A, A, A, A, 5000), qb.qb_tensor(A, A2, A, A, A, A, 0),
+                             qb.qb_tensor(A, A2, A, A, A, A, 2048 * 3 + 1))
+    assert L.qb_multi_tensor_workspace_bytes(3) == 3 * 64 + 4 * 8 + (2 * 3 + 64 + 1) * 4   # 508
+    region = 2 * 512                                   # two map regions, each rounded up to 256 bytes
+    lamb = H(qb.QB_LAMB, 1e-3)
+    assert L.qb_optimizer_workspace_bytes(ctypes.byref(lamb), tab, 3, 2048) == region + 256 + 256    # 2 groups
+    assert L.qb_optimizer_workspace_bytes(ctypes.byref(lamb), tab, 3, 256) == region + 256 + 256
+    assert L.qb_optimizer_workspace_bytes(ctypes.byref(H(qb.QB_ADAMW, 1e-3)), tab, 3, 2048) == 508
+    big = (qb.qb_tensor * 1)(qb.qb_tensor(A, A2, A, A, A, A, 2048 * 32 * 20 + 1))   # 641 tiles: 21 groups
+    assert L.qb_optimizer_workspace_bytes(ctypes.byref(lamb), big, 1, 2048) == 2 * 512 + 512 + 256
+    assert L.qb_optimizer_workspace_bytes(None, tab, 3, 2048) == 0
+    assert L.qb_optimizer_workspace_bytes(ctypes.byref(lamb), tab, 3, 100) == 0
+    # the step checks the larger workspace before touching the device
+    m = L.qb_multi_tensor_optimizer_step
+    assert m(ctypes.byref(lamb), tab, 3, 2, 2048, A, region, None) == qb.QB_EWORKSPACE
+    assert m(ctypes.byref(lamb), tab, 3, 2, 2048, A, region + 511, None) == qb.QB_EWORKSPACE
+    assert m(ctypes.byref(lamb), tab, 3, 2, 2048, A, 512, None) == qb.QB_EWORKSPACE
+
+
 def test_linear_code_equals_oracle(qb):
     got = np.array(qb.qb_linear_code(), dtype=np.float32)
     assert np.array_equal(got.view(np.uint32), oracle.linear_codebook().view(np.uint32))
