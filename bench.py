@@ -295,7 +295,9 @@ def bench_flat(torch, qb, inputs, dev, args):
     nb = (n + ADAM_BLOCK - 1) // ADAM_BLOCK
     kind, hp, states = OPTIMIZERS[args.optimizer]
     log(f"allocating a flat buffer of {n:,} params ({args.optimizer}, {states} state(s))")
-    p = inputs.normal(n, 0.02, seed=args.seed, device=dev)
+    pdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[args.param_dtype]
+    gdt = torch.bfloat16 if args.param_dtype == "fp32" else pdt      # 16-bit params take grads of their dtype
+    p = inputs.normal(n, 0.02, seed=args.seed, device=dev, dtype=pdt)
     if args.state_bits == 8:
         s1 = torch.full((n,), 127, dtype=torch.uint8, device=dev)
         a1 = torch.zeros(nb, device=dev)
@@ -305,7 +307,7 @@ def bench_flat(torch, qb, inputs, dev, args):
         s1 = torch.zeros(n, device=dev)
         s2 = torch.zeros(n, device=dev) if states == 2 else None
         a1 = a2 = None
-    grads = [inputs.normal(n, 1e-3, inputs.grad_seed(args.seed, 0, k), device=dev, dtype=torch.bfloat16) for k in range(2)]
+    grads = [inputs.normal(n, 1e-3, inputs.grad_seed(args.seed, 0, k), device=dev, dtype=gdt) for k in range(2)]
 
     layerwise = args.optimizer in LAYERWISE
     if layerwise:               # one tensor = one layer, through the multi-tensor call (norm pass + step)
@@ -316,7 +318,8 @@ def bench_flat(torch, qb, inputs, dev, args):
     def step(k):
         h = qb.optim_hparams(kind, step=k, **hp)
         if layerwise:
-            qb.qb_multi_tensor_optimizer_step(h, tables[k % 2], 1, qb.QB_BF16, ADAM_BLOCK, ws)
+            qb.qb_multi_tensor_optimizer_step(h, tables[k % 2], 1, qb._DTYPE[gdt], ADAM_BLOCK, ws,
+                                              pdt=qb._DTYPE[pdt])
         else:
             qb.qb_optimizer8bit_step(h, p, grads[k % 2], n, s1, s2, a1, a2, ADAM_BLOCK)
 
@@ -337,10 +340,14 @@ def bench_flat(torch, qb, inputs, dev, args):
     bpp = optim_bytes_per_param(states) if args.state_bits == 8 else 8 + 2 + 8 * states
     if layerwise:
         bpp += layerwise_extra_bytes_per_param(args.optimizer, args.state_bits)
+    if args.param_dtype != "fp32":
+        bpp -= 4 if not layerwise else 6            # p read + written in 2 bytes (and read in the norm pass)
     nbytes = n * bpp
     call = "one-layer multi-tensor call (norm pass + step)" if layerwise else "single-tensor"
-    print(json.dumps({"workload": f"flat 1.5e9 fp32 params, bf16 grads, block 2048, {call} {args.optimizer} "
-                                  f"step, {args.state_bits}-bit states", "optimizer": args.optimizer,
+    print(json.dumps({"workload": f"flat 1.5e9 params, {args.param_dtype if args.param_dtype != 'fp32' else 'bf16'} "
+                                  f"grads, block 2048, {call} {args.optimizer} "
+                                  f"step, {args.state_bits}-bit states, {args.param_dtype} params",
+                      "optimizer": args.optimizer, "param_dtype": args.param_dtype,
                       "state_bits": args.state_bits, "steps": args.steps, "median_ms": med,
                       "bytes_per_param": bpp, "GB/s": nbytes / med / 1e6,
                       "params_per_s": n / med * 1e3, "frac_of_hbm_peak": nbytes / med / 1e6 / HBM_PEAK_GBS,
@@ -398,6 +405,8 @@ def main():
     ap.add_argument("--adam-only", action="store_true", help="time only the multi-tensor AdamW step")
     ap.add_argument("--flat", action="store_true",
                     help="time the single-tensor AdamW step on a flat 1.5e9-parameter buffer instead")
+    ap.add_argument("--param-dtype", choices=["fp32", "bf16", "fp16"], default="fp32",
+                    help="parameter dtype of the --flat run (16-bit parameters take gradients of their dtype)")
     ap.add_argument("--optimizer", choices=sorted(OPTIMIZERS), default="adamw",
                     help="optimizer of the --flat run (the 8-bit states of each kind)")
     ap.add_argument("--state-bits", type=int, choices=(8, 32), default=8,

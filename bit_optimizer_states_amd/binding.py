@@ -80,10 +80,10 @@ def lib():
                                            vp, sz, vp]
         L.qb_multi_tensor_dequantize.argtypes = [ctypes.POINTER(qb_dequant_tensor), i32, i32, i32, i32, i32, vp, sz,
                                                  vp]
-        L.qb_optimizer8bit_step.argtypes = [ctypes.POINTER(qb_optim_hparams), vp, vp, i32, i64, vp, vp, vp, vp, i32,
-                                            vp]
+        L.qb_optimizer8bit_step.argtypes = [ctypes.POINTER(qb_optim_hparams), vp, i32, vp, i32, i64, vp, vp, vp, vp,
+                                            i32, vp]
         L.qb_multi_tensor_optimizer_step.argtypes = [ctypes.POINTER(qb_optim_hparams), ctypes.POINTER(qb_tensor), i32,
-                                                     i32, i32, vp, sz, vp]
+                                                     i32, i32, i32, vp, sz, vp]
         L.qb_optimizer_workspace_bytes.argtypes = [ctypes.POINTER(qb_optim_hparams), ctypes.POINTER(qb_tensor), i32,
                                                    i32]
         L.qb_optimizer_workspace_bytes.restype = sz
@@ -195,8 +195,9 @@ def optim_hparams(kind, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, 
 
 
 def qb_optimizer8bit_step(hp, p, g, n, state1, state2, absmax1, absmax2, blocksize, stream=None):
-    """state2 / absmax2 may be None for the one-state kinds."""
-    _check(lib().qb_optimizer8bit_step(ctypes.byref(hp), _ptr(p), _ptr(g), _dtype(g), int(n), _ptr(state1),
+    """state2 / absmax2 may be None for the one-state kinds; the parameter and
+    gradient dtypes are those of p and g."""
+    _check(lib().qb_optimizer8bit_step(ctypes.byref(hp), _ptr(p), _dtype(p), _ptr(g), _dtype(g), int(n), _ptr(state1),
                                        _ptr(state2), _ptr(absmax1), _ptr(absmax2), int(blocksize), _stream(stream)),
            "qb_optimizer8bit_step")
 
@@ -214,9 +215,10 @@ def qb_optimizer_workspace_bytes(hp, table, count, blocksize):
     return lib().qb_optimizer_workspace_bytes(ctypes.byref(hp), table, int(count), int(blocksize))
 
 
-def qb_multi_tensor_optimizer_step(hp, table, count, gdt, blocksize, ws, stream=None):
-    _check(lib().qb_multi_tensor_optimizer_step(ctypes.byref(hp), table, int(count), int(gdt), int(blocksize),
-                                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+def qb_multi_tensor_optimizer_step(hp, table, count, gdt, blocksize, ws, stream=None, pdt=QB_F32):
+    _check(lib().qb_multi_tensor_optimizer_step(ctypes.byref(hp), table, int(count), int(pdt), int(gdt),
+                                                int(blocksize), _ptr(ws), ws.numel() * ws.element_size(),
+                                                _stream(stream)),
            "qb_multi_tensor_optimizer_step")
 
 

@@ -88,16 +88,24 @@ bool layerwise(qb_optimizer k) { return k == QB_LAMB || k == QB_LARS; }
 
 // Checks one tensor of an optimizer step.  absmax1 == NULL selects binary32
 // states (state1, state2 are float arrays; absmax2 must be NULL too).
-qb_status check_optim_tensor(bool two, const float* p, const void* g, const void* s1, const void* s2,
+qb_status check_optim_tensor(bool two, const void* p, const void* g, const void* s1, const void* s2,
                              const float* a1, const float* a2)
 {
     const bool s32 = a1 == nullptr;
     if (!p || !g || !s1 || (two && !s2)) return QB_EINVAL;
     if (two && (s32 ? a2 != nullptr : a2 == nullptr)) return QB_EINVAL;
-    if ((const void*)p == g) return QB_EINVAL;
+    if (p == g) return QB_EINVAL;
     if (!aligned16(p) || !aligned16(g) || !aligned16(s1) || (two && !aligned16(s2))) return QB_EALIGN;
     if (!s32 && (!aligned16(a1) || (two && !aligned16(a2)))) return QB_EALIGN;
     return QB_OK;
+}
+
+// Parameter / gradient dtype pairs of the optimizer steps: binary32
+// parameters with any gradient dtype, 16-bit parameters with the same dtype.
+qb_status check_optim_dtypes(qb_dtype pdt, qb_dtype gdt)
+{
+    if (!valid_dtype(pdt) || !valid_dtype(gdt)) return QB_EINVAL;
+    return (pdt == QB_F32 || pdt == gdt) ? QB_OK : QB_EUNSUPPORTED;
 }
 
 // beta^t by t repeated binary64 multiplications.  Consecutive steps of the
@@ -587,12 +595,13 @@ qb_status qb_estimate_quantiles(const void* x, qb_dtype xdt, int64_t n, void* ta
     return hip_status(e);
 }
 
-qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void* g, qb_dtype gdt, int64_t n,
-                                uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2, int32_t blocksize,
-                                void* stream)
+qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, void* p, qb_dtype pdt, const void* g, qb_dtype gdt,
+                                int64_t n, uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,
+                                int32_t blocksize, void* stream)
 {
-    if (n < 0 || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_optim(hp)) return QB_EINVAL;
-    if (layerwise(hp->kind)) return QB_EUNSUPPORTED;
+    if (n < 0 || !valid_dtype(pdt) || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_optim(hp))
+        return QB_EINVAL;
+    if (check_optim_dtypes(pdt, gdt) != QB_OK || layerwise(hp->kind)) return QB_EUNSUPPORTED;
     if (n == 0) return QB_OK;
     const bool two = optim_states(hp->kind) == 2;
     if (!two) {
@@ -604,8 +613,8 @@ qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void
     if (st != QB_OK) return st;
     if (!device_tables()) return QB_EINIT;
     TensorDesc d{p, g, state1, state2, absmax1, absmax2, n, 0};
-    return hip_status(launch_optim8((int)hp->kind, d, nullptr, adamw_tiles(n, blocksize), blocksize, (int)gdt,
-                                    prepare(*hp), nullptr, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_optim8((int)hp->kind, d, nullptr, adamw_tiles(n, blocksize), blocksize, (int)pdt,
+                                    (int)gdt, prepare(*hp), nullptr, static_cast<hipStream_t>(stream)));
 }
 
 size_t qb_optimizer_workspace_bytes(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
@@ -622,9 +631,12 @@ size_t qb_optimizer_workspace_bytes(const qb_optim_hparams* hp, const qb_tensor*
 }
 
 qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
-                                         qb_dtype gdt, int32_t blocksize, void* ws, size_t ws_bytes, void* stream)
+                                         qb_dtype pdt, qb_dtype gdt, int32_t blocksize, void* ws, size_t ws_bytes,
+                                         void* stream)
 {
-    if (count < 0 || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_optim(hp)) return QB_EINVAL;
+    if (count < 0 || !valid_dtype(pdt) || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_optim(hp))
+        return QB_EINVAL;
+    if (check_optim_dtypes(pdt, gdt) != QB_OK) return QB_EUNSUPPORTED;
     if (count == 0) return QB_OK;
     if (!tensors || !ws) return QB_EINVAL;
     if (!aligned16(ws)) return QB_EALIGN;
@@ -670,18 +682,19 @@ qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_te
         stage_tile_map(staging, map_region_bytes(count), gtable, groups, count, ws, &gmap);
         qb_status st = copy_staging(staging, ws, s);
         if (st != QB_OK) return st;
-        hipError_t e = launch_trust_norms((int)hp->kind, gmap, groups, blocksize, (int)gdt, hs, part, s);
+        hipError_t e = launch_trust_norms((int)hp->kind, gmap, groups, blocksize, (int)pdt, (int)gdt, hs, part, s);
         if (e == hipSuccess)
             e = launch_trust_scalars((int)hp->kind, gmap, part, hp->lr, hp->weight_decay, hp->trust_coefficient,
                                      trust, s);
         if (e == hipSuccess)
-            e = launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)gdt, hs, trust, s);
+            e = launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)pdt, (int)gdt, hs, trust, s);
         return hip_status(e);
     }
     stage_tile_map(staging, 0, table, tiles, count, ws, &map);
     qb_status st = copy_staging(staging, ws, s);
     if (st != QB_OK) return st;
-    return hip_status(launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)gdt, hs, nullptr, s));
+    return hip_status(
+        launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)pdt, (int)gdt, hs, nullptr, s));
 }
 
 qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, uint8_t* m, uint8_t* v,
@@ -690,7 +703,7 @@ qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, ui
 {
     if (!hp) return QB_EINVAL;
     const qb_optim_hparams o = as_optim(hp);
-    return qb_optimizer8bit_step(&o, p, g, gdt, n, m, v, absmax_m, absmax_v, blocksize, stream);
+    return qb_optimizer8bit_step(&o, p, QB_F32, g, gdt, n, m, v, absmax_m, absmax_v, blocksize, stream);
 }
 
 qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
@@ -698,7 +711,7 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
 {
     if (!hp) return QB_EINVAL;
     const qb_optim_hparams o = as_optim(hp);
-    return qb_multi_tensor_optimizer_step(&o, tensors, count, gdt, blocksize, ws, ws_bytes, stream);
+    return qb_multi_tensor_optimizer_step(&o, tensors, count, QB_F32, gdt, blocksize, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -198,6 +198,16 @@ __device__ __forceinline__ void store1(void* base, int64_t i, float v)
         gst<uint16_t>(static_cast<uint16_t*>(base) + i, (uint16_t)to_half_bits<DT>(v));
 }
 
+// One output at element offset i (uint32) from a uniform base.
+template <int DT>
+__device__ __forceinline__ void store1o(void* base, uint32_t i, float v)
+{
+    if constexpr (DT == DT_F32)
+        gsto<float>(base, i * 4u, v);
+    else
+        gsto<uint16_t>(base, i * 2u, (uint16_t)to_half_bits<DT>(v));
+}
+
 // 4 consecutive outputs at element index i.
 template <int DT>
 __device__ __forceinline__ void store4(void* y, int64_t i, const float* o)

@@ -39,9 +39,10 @@ struct OptScalars {
     int32_t flags;
 };
 
-// One tensor of a fused AdamW launch; tile_begin is the first global tile.
+// One tensor of a fused optimizer launch (p of the launch's parameter dtype);
+// tile_begin is the first global tile.
 struct TensorDesc {
-    float* p;
+    void* p;
     const void* g;
     uint8_t* m;
     uint8_t* v;
@@ -208,8 +209,9 @@ constexpr int64_t dequant_tile_elems(int bits, bool multi)
 // nullptr) or on the tensors of map.
 // trust: the per-tensor step scalars S of the layer-wise kinds (indexed like
 // map->descs), nullptr for the others.
+// pdt: the parameters' dtype (binary32, or a 16-bit type equal to gdt).
 hipError_t launch_optim8(int opt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B,
-                         int gdt, const OptScalars& hs, const float* trust, hipStream_t s);
+                         int pdt, int gdt, const OptScalars& hs, const float* trust, hipStream_t s);
 
 // Layer-wise kinds, before launch_optim8: per group of kNormGroupTiles
 // consecutive optimizer tiles of one tensor (gmap: the tensors with
@@ -218,7 +220,7 @@ hipError_t launch_optim8(int opt, const TensorDesc& single, const TileMap<Tensor
 // part[2 * group + 1]); then one workgroup per tensor adds its groups' partials
 // in a fixed order and writes trust[tensor] = (float)(lr * ratio).
 constexpr int64_t kNormGroupTiles = 32;
-hipError_t launch_trust_norms(int opt, const TileMap<TensorDesc>& gmap, int64_t ngroups, int B, int gdt,
+hipError_t launch_trust_norms(int opt, const TileMap<TensorDesc>& gmap, int64_t ngroups, int B, int pdt, int gdt,
                               const OptScalars& hs, double* part, hipStream_t s);
 hipError_t launch_trust_scalars(int opt, const TileMap<TensorDesc>& gmap, const double* part, double lr,
                                 double weight_decay, double trust_coefficient, float* trust, hipStream_t s);

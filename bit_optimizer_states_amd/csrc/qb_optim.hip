@@ -197,13 +197,13 @@ __device__ __forceinline__ void opt_elem(const OptScalars& hs, float gi, float& 
 // A tile of a tensor whose states stay binary32 (the 32-bit fallback for small
 // or chosen tensors: d.am == nullptr, d.m / d.v are float arrays).  The same
 // element update, with no codes and no block absmax.
-template <int OPT, class T, int GDT>
+template <int OPT, class T, int GDT, int PDT>
 __device__ __forceinline__ void optim32_tile(const TensorDesc& d, int64_t lt, const OptScalars& hs, int tid)
 {
     constexpr bool TWO = opt_states(OPT) == 2;
     const int bt = tid / T::LPB, l = tid % T::LPB;
     const int64_t tbase = lt * T::ELEMS;
-    float* const pt = d.p + tbase;
+    void* const pt = static_cast<char*>(d.p) + tbase * (PDT == DT_F32 ? 4 : 2);
     const void* const gt = static_cast<const char*>(d.g) + tbase * (GDT == DT_F32 ? 4 : 2);
     float* const xt = reinterpret_cast<float*>(d.m) + tbase;
     float* const yt = TWO ? reinterpret_cast<float*>(d.v) + tbase : nullptr;
@@ -215,7 +215,7 @@ __device__ __forceinline__ void optim32_tile(const TensorDesc& d, int64_t lt, co
 #pragma unroll
         for (int c = 0; c < T::CH; ++c) {
             const uint32_t e = lofs + c * T::LPB * T::CW;
-            load_chunk<DT_F32, T::CW>(pt, e, &p[c * T::CW]);
+            load_chunk<PDT, T::CW>(pt, e, &p[c * T::CW]);
             load_chunk<GDT, T::CW>(gt, e, &g[c * T::CW]);
             load_chunk<DT_F32, T::CW>(xt, e, &x[c * T::CW]);
             if constexpr (TWO) load_chunk<DT_F32, T::CW>(yt, e, &y[c * T::CW]);
@@ -225,7 +225,7 @@ __device__ __forceinline__ void optim32_tile(const TensorDesc& d, int64_t lt, co
         for (int i = 0; i < T::EPT; ++i) {
             const uint32_t e = lofs + (i / T::CW) * T::LPB * T::CW + (i % T::CW);
             const bool in = (int64_t)e < lrem;
-            p[i] = in ? load1<DT_F32>(pt, e) : 0.0f;
+            p[i] = in ? load1<PDT>(pt, e) : 0.0f;
             g[i] = in ? load1<GDT>(gt, e) : 0.0f;
             x[i] = in ? load1<DT_F32>(xt, e) : 0.0f;
             y[i] = (TWO && in) ? load1<DT_F32>(yt, e) : 0.0f;
@@ -239,7 +239,7 @@ __device__ __forceinline__ void optim32_tile(const TensorDesc& d, int64_t lt, co
 #pragma unroll
             for (int h = 0; h < T::CW; h += 4) {
                 const uint32_t e = lofs + c * T::LPB * T::CW + h;
-                store4o<DT_F32>(pt, e, &p[c * T::CW + h]);
+                store4o<PDT>(pt, e, &p[c * T::CW + h]);
                 store4o<DT_F32>(xt, e, &x[c * T::CW + h]);
                 if constexpr (TWO) store4o<DT_F32>(yt, e, &y[c * T::CW + h]);
             }
@@ -248,7 +248,7 @@ __device__ __forceinline__ void optim32_tile(const TensorDesc& d, int64_t lt, co
         for (int i = 0; i < T::EPT; ++i) {
             const uint32_t e = lofs + (i / T::CW) * T::LPB * T::CW + (i % T::CW);
             if ((int64_t)e < lrem) {
-                gsto<float>(pt, e * 4u, p[i]);
+                store1o<PDT>(pt, e, p[i]);
                 gsto<float>(xt, e * 4u, x[i]);
                 if constexpr (TWO) gsto<float>(yt, e * 4u, y[i]);
             }
@@ -256,7 +256,7 @@ __device__ __forceinline__ void optim32_tile(const TensorDesc& d, int64_t lt, co
     }
 }
 
-template <int OPT, int B, int GDT, bool MULTI>
+template <int OPT, int B, int GDT, bool MULTI, int PDT>
 __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, TileMap<TensorDesc> map, OptScalars hs0,
                                                          const QbTables* __restrict__ tab,
                                                          const float* __restrict__ trust)
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
         lt = tile;
     }
     if (d.am == nullptr) {                                 // binary32 states (uniform per workgroup)
-        optim32_tile<OPT, T, GDT>(d, lt, hs, tid);
+        optim32_tile<OPT, T, GDT, PDT>(d, lt, hs, tid);
         return;
     }
     const int bt = tid / T::LPB, l = tid % T::LPB;
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
     const bool full = (lt + 1) * T::ELEMS <= nloc;
     // uniform tile base pointers; per-lane offsets stay 32-bit
     const int64_t tbase = lt * T::ELEMS;
-    float* const pt = d.p + tbase;
+    void* const pt = static_cast<char*>(d.p) + tbase * (PDT == DT_F32 ? 4 : 2);
     const void* const gt = static_cast<const char*>(d.g) + tbase * (GDT == DT_F32 ? 4 : 2);
     uint8_t* const mt = d.m + tbase;
     uint8_t* const vt = TWO ? d.v + tbase : nullptr;
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
 #pragma unroll
         for (int c = 0; c < T::CH; ++c) {
             const uint32_t e = lofs + c * T::LPB * T::CW;
-            load_chunk<DT_F32, T::CW>(pt, e, &p[c * T::CW]);
+            load_chunk<PDT, T::CW>(pt, e, &p[c * T::CW]);
             load_chunk<GDT, T::CW>(gt, e, &g[c * T::CW]);
             load_codes<T::CW>(mt, e, &cmw[c * T::CW / 4]);
             if constexpr (TWO) load_codes<T::CW>(vt, e, &cvw[c * T::CW / 4]);
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
                 const uint32_t e = lofs + (i / T::CW) * T::LPB * T::CW + (i % T::CW);
                 float pv = 0.0f, gv = 0.0f;
                 if ((int64_t)e < lrem) {
-                    pv = load1<DT_F32>(pt, e);
+                    pv = load1<PDT>(pt, e);
                     gv = load1<GDT>(gt, e);
                     wm = (wm & ~(0xFFu << (8 * j))) | ((uint32_t)gldo<uint8_t>(mt, e) << (8 * j));
                     if constexpr (TWO) wv = (wv & ~(0xFFu << (8 * j))) | ((uint32_t)gldo<uint8_t>(vt, e) << (8 * j));
@@ -362,14 +362,14 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
     if (full) {
 #pragma unroll
         for (int c = 0; c < T::CH; ++c) {
-            store4o<DT_F32>(pt, lofs + c * T::LPB * T::CW, &p[c * T::CW]);
-            if constexpr (T::CW == 8) store4o<DT_F32>(pt, lofs + c * T::LPB * T::CW + 4, &p[c * T::CW + 4]);
+            store4o<PDT>(pt, lofs + c * T::LPB * T::CW, &p[c * T::CW]);
+            if constexpr (T::CW == 8) store4o<PDT>(pt, lofs + c * T::LPB * T::CW + 4, &p[c * T::CW + 4]);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < T::EPT; ++i) {
             const uint32_t e = lofs + (i / T::CW) * T::LPB * T::CW + (i % T::CW);
-            if ((int64_t)e < lrem) gsto<float>(pt, e * 4u, p[i]);
+            if ((int64_t)e < lrem) store1o<PDT>(pt, e, p[i]);
         }
     }
 
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
 // |g|^2 (LARS) in binary64: each thread over its own elements, tile after
 // tile, then across the wave (butterfly) and the waves (in order).  The same
 // bits on every run.
-template <int OPT, int B, int GDT>
+template <int OPT, int B, int GDT, int PDT>
 __global__ __launch_bounds__(kAdamThreads) void k_trust_norms(TileMap<TensorDesc> gmap, OptScalars hs,
                                                               const QbTables* __restrict__ tab,
                                                               double* __restrict__ part)
@@ -475,7 +475,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_trust_norms(TileMap<TensorDesc
         const int64_t tbase = lt * T::ELEMS;
         const int64_t lrem = d.n - tbase;
         const bool full = T::ELEMS <= lrem;
-        float* const pt = d.p + tbase;
+        const void* const pt = static_cast<const char*>(d.p) + tbase * (PDT == DT_F32 ? 4 : 2);
         const void* const gt = static_cast<const char*>(d.g) + tbase * (GDT == DT_F32 ? 4 : 2);
         float am0 = 0.0f, av0 = 0.0f;
         if (LAMB && s8 && blk < nbl) {
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_trust_norms(TileMap<TensorDesc
 #pragma unroll
             for (int c = 0; c < T::CH; ++c) {
                 const uint32_t e = lofs + c * T::LPB * T::CW;
-                load_chunk<DT_F32, T::CW>(pt, e, &p[c * T::CW]);
+                load_chunk<PDT, T::CW>(pt, e, &p[c * T::CW]);
                 load_chunk<GDT, T::CW>(gt, e, &g[c * T::CW]);
                 if constexpr (LAMB) {
                     if (s8) {
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_trust_norms(TileMap<TensorDesc
             for (int i = 0; i < T::EPT; ++i) {
                 const uint32_t e = lofs + (i / T::CW) * T::LPB * T::CW + (i % T::CW);
                 const bool in = (int64_t)e < lrem;
-                p[i] = in ? load1<DT_F32>(pt, e) : 0.0f;
+                p[i] = in ? load1<PDT>(pt, e) : 0.0f;
                 g[i] = in ? load1<GDT>(gt, e) : 0.0f;
                 if constexpr (LAMB) {
                     if (in && s8) {
@@ -620,10 +620,11 @@ struct OptLaunch {
     const QbTables* tab;
     const float* trust;      // k_optim8 of the layer-wise kinds
     double* part;            // non-null: launch k_trust_norms instead
+    int pdt;                 // parameter dtype
     hipStream_t s;
 };
 
-template <int OPT, int B, int GDT>
+template <int OPT, int B, int GDT, int PDT>
 hipError_t optim_as(const OptLaunch& a)
 {
     static_assert(TileA<B>::ELEMS == kAdamThreads * (B >= 4 * kAdamThreads ? B / kAdamThreads : 4), "tile size");
@@ -631,26 +632,36 @@ hipError_t optim_as(const OptLaunch& a)
     if constexpr (opt_layerwise(OPT)) {                   // multi-tensor only (the norms need a workspace)
         if (!a.map) return hipErrorInvalidValue;
         if (a.part)
-            return launch_kernel_nt(k_trust_norms<OPT, B, GDT>, (int)a.ntiles, kAdamThreads, a.s, *a.map, *a.hs,
+            return launch_kernel_nt(k_trust_norms<OPT, B, GDT, PDT>, (int)a.ntiles, kAdamThreads, a.s, *a.map, *a.hs,
                                     a.tab, a.part);
-        return launch_kernel_nt(k_optim8<OPT, B, GDT, true>, (int)a.ntiles, kAdamThreads, a.s, *a.single, *a.map,
-                                *a.hs, a.tab, a.trust);
+        return launch_kernel_nt(k_optim8<OPT, B, GDT, true, PDT>, (int)a.ntiles, kAdamThreads, a.s, *a.single,
+                                *a.map, *a.hs, a.tab, a.trust);
     } else {
         if (a.map)
-            return launch_kernel_nt(k_optim8<OPT, B, GDT, true>, (int)a.ntiles, kAdamThreads, a.s, *a.single,
-                                    *a.map, *a.hs, a.tab, (const float*)nullptr);
-        return launch_kernel_nt(k_optim8<OPT, B, GDT, false>, (int)a.ntiles, kAdamThreads, a.s, *a.single,
+            return launch_kernel_nt(k_optim8<OPT, B, GDT, true, PDT>, (int)a.ntiles, kAdamThreads, a.s,
+                                    *a.single, *a.map, *a.hs, a.tab, (const float*)nullptr);
+        return launch_kernel_nt(k_optim8<OPT, B, GDT, false, PDT>, (int)a.ntiles, kAdamThreads, a.s, *a.single,
                                 TileMap<TensorDesc>{}, *a.hs, a.tab, (const float*)nullptr);
     }
 }
 
+// (parameter, gradient) dtypes: binary32 parameters with any gradient dtype,
+// or 16-bit parameters with gradients of the same type.
 template <int OPT, int B>
 hipError_t optim_dt(int gdt, const OptLaunch& a)
 {
+    if (a.pdt == DT_F32) {
+        switch (gdt) {
+        case DT_F32: return optim_as<OPT, B, DT_F32, DT_F32>(a);
+        case DT_F16: return optim_as<OPT, B, DT_F16, DT_F32>(a);
+        case DT_BF16: return optim_as<OPT, B, DT_BF16, DT_F32>(a);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (a.pdt != gdt) return hipErrorInvalidValue;
     switch (gdt) {
-    case DT_F32: return optim_as<OPT, B, DT_F32>(a);
-    case DT_F16: return optim_as<OPT, B, DT_F16>(a);
-    case DT_BF16: return optim_as<OPT, B, DT_BF16>(a);
+    case DT_F16: return optim_as<OPT, B, DT_F16, DT_F16>(a);
+    case DT_BF16: return optim_as<OPT, B, DT_BF16, DT_BF16>(a);
     default: return hipErrorInvalidValue;
     }
 }
@@ -687,22 +698,22 @@ hipError_t optim_kind(int opt, int B, int gdt, const OptLaunch& a)
 }  // namespace
 
 hipError_t launch_optim8(int opt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B,
-                         int gdt, const OptScalars& hs, const float* trust, hipStream_t s)
+                         int pdt, int gdt, const OptScalars& hs, const float* trust, hipStream_t s)
 {
     const QbTables* tab = device_tables();
     if (!tab) return hipErrorNotInitialized;
     if (opt_layerwise(opt) && !trust) return hipErrorInvalidValue;
-    return optim_kind(opt, B, gdt, OptLaunch{&single, map, ntiles, &hs, tab, trust, nullptr, s});
+    return optim_kind(opt, B, gdt, OptLaunch{&single, map, ntiles, &hs, tab, trust, nullptr, pdt, s});
 }
 
-hipError_t launch_trust_norms(int opt, const TileMap<TensorDesc>& gmap, int64_t ngroups, int B, int gdt,
+hipError_t launch_trust_norms(int opt, const TileMap<TensorDesc>& gmap, int64_t ngroups, int B, int pdt, int gdt,
                               const OptScalars& hs, double* part, hipStream_t s)
 {
     const QbTables* tab = device_tables();
     if (!tab) return hipErrorNotInitialized;
     if (!opt_layerwise(opt) || !part) return hipErrorInvalidValue;
     const TensorDesc none{};
-    return optim_kind(opt, B, gdt, OptLaunch{&none, &gmap, ngroups, &hs, tab, nullptr, part, s});
+    return optim_kind(opt, B, gdt, OptLaunch{&none, &gmap, ngroups, &hs, tab, nullptr, part, pdt, s});
 }
 
 hipError_t launch_trust_scalars(int opt, const TileMap<TensorDesc>& gmap, const double* part, double lr,

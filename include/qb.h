@@ -159,9 +159,10 @@ typedef struct {
 } qb_optim_hparams;
 
 /* One tensor of a multi-tensor step; the fields are those of qb_adamw8bit_step
- * (m, absmax_m: state 1; v, absmax_v: state 2, ignored by one-state kinds). */
+ * (m, absmax_m: state 1; v, absmax_v: state 2, ignored by one-state kinds).
+ * p holds n values of the call's parameter dtype (fp32 for qb_multi_tensor_step). */
 typedef struct {
-    float*      p;
+    void*       p;
     const void* g;
     uint8_t*    m;
     uint8_t*    v;
@@ -310,7 +311,13 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
  * qb_optimizer above) on one tensor.  Arguments as qb_adamw8bit_step, with
  * state1/absmax1 in place of m/absmax_m and state2/absmax2 in place of
  * v/absmax_v; state2 and absmax2 are ignored (may be NULL) for the one-state
- * kinds.  Fresh state: every code 127 (0.0), absmax 0.  Invalid
+ * kinds.
+ * Parameter dtype pdt: QB_F32 (any gdt), or QB_F16 / QB_BF16 with gdt equal
+ * to it (16-bit training without binary32 master weights, e.g. fp16 mixed
+ * precision next to the 8-bit optimizer: "bitsandbytes - Quantização de LLM",
+ * section Workflow 3).  A 16-bit parameter is widened to binary32 (exactly),
+ * updated by the same binary32 formulas and rounded once, to nearest even,
+ * back to its dtype; other pairs give QB_EUNSUPPORTED.  Fresh state: every code 127 (0.0), absmax 0.  Invalid
  * hyperparameters for the kind (ranges above; lr, weight_decay >= 0) give
  * QB_EINVAL before anything is launched; the layer-wise kinds give
  * QB_EUNSUPPORTED (they run through qb_multi_tensor_optimizer_step).
@@ -322,13 +329,14 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
  * keep 32-bit state).  The multi-tensor step takes the same per tensor, so one
  * launch can mix 8-bit and 32-bit tensors.
  */
-qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void* g, qb_dtype gdt, int64_t n,
-                                uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,
+qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, void* p, qb_dtype pdt, const void* g, qb_dtype gdt,
+                                int64_t n, uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,
                                 int32_t blocksize, void* stream);
 
 /*
  * qb_multi_tensor_optimizer_step -- qb_optimizer8bit_step on `count` tensors in
- * one kernel launch; tensors, ws as for qb_multi_tensor_step, except that ws
+ * one kernel launch (one parameter dtype pdt and gradient dtype gdt for all);
+ * tensors, ws as for qb_multi_tensor_step, except that ws
  * holds qb_optimizer_workspace_bytes(hp, tensors, count, blocksize) bytes.
  * The layer-wise kinds (QB_LAMB, QB_LARS) take three launches on `stream`:
  * partial sums of the squared norms per group of optimizer tiles, one
@@ -336,7 +344,7 @@ qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, float* p, const void
  * fused step; the partial sums and the S of every tensor live in ws.
  */
 qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
-                                         qb_dtype gdt, int32_t blocksize, void* ws, size_t ws_bytes,
+                                         qb_dtype pdt, qb_dtype gdt, int32_t blocksize, void* ws, size_t ws_bytes,
                                          void* stream);
 
 /*

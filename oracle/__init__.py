@@ -46,6 +46,7 @@ def lib():
             "orc_adamw8bit_step": [vp, vp, i32, i64, vp, vp, vp, vp, i32, dp, dp, dp, dp, dp, i32],
             "orc_adam_scalars": [dp, dp, dp, dp, dp, i32, vp],
             "orc_optim32_step": [i32, vp, i32, vp, vp, i32, i64, vp, vp],
+            "orc_convert": [vp, i32, vp, i32, i64],
             "orc_linear_codebook": [vp],
             "orc_quantize_custom": [vp, i32, i64, vp, i32, vp, vp],
             "orc_dequantize_custom": [vp, vp, vp, i32, i64, vp, i32],
@@ -323,23 +324,57 @@ def _optim_hp(lr, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.0, dampening=0.0, neste
     return np.array([lr, beta1, beta2, eps, wd, dampening, 1.0 if nesterov else 0.0, trust], dtype=np.float64)
 
 
-def optim32_step(kind, p, g, x1, x2=None, step=1, gdt=None, **hp):
+def convert(x, xdt, ydt):
+    """x (float32, or uint16 bits of F16/BF16) converted to dtype ydt: widening
+    exact, narrowing to nearest even."""
+    x = np.ascontiguousarray(x)
+    y = np.empty(x.size, np.float32 if ydt == F32 else np.uint16)
+    _check(lib().orc_convert(_p(x), xdt, _p(y), ydt, x.size), "convert")
+    return y
+
+
+class _Params16:
+    """A 16-bit parameter array as binary32 for the duration of a step: widened
+    exactly on entry, rounded once to nearest even into the caller's array on
+    exit (the update itself is the binary32 one)."""
+
+    def __init__(self, p, pdt):
+        self.p, self.pdt = p, pdt
+
+    def __enter__(self):
+        if self.pdt == F32:
+            return self.p
+        if self.p.dtype != np.uint16 or not self.p.flags.c_contiguous:
+            raise TypeError("16-bit parameters are contiguous uint16 bit patterns")
+        self.w = convert(self.p, self.pdt, F32)
+        return self.w
+
+    def __exit__(self, *exc):
+        if self.pdt != F32 and exc[0] is None:
+            self.p[:] = convert(self.w, F32, self.pdt)
+        return False
+
+
+def optim32_step(kind, p, g, x1, x2=None, step=1, gdt=None, pdt=F32, **hp):
     """In-place step of optimizer `kind` with binary32 states x1 (and x2 for the
     two-state kinds); hp: lr, beta1, beta2, eps, wd, dampening, nesterov, trust
-    (the layer-wise kinds take one call per layer)."""
+    (the layer-wise kinds take one call per layer).  pdt: the parameters'
+    dtype (F16 / BF16 parameters are uint16 bit patterns)."""
     if gdt is None:
         gdt = _dtype_id(g)
     g = np.ascontiguousarray(g)
     h = _optim_hp(**hp)
-    _check(lib().orc_optim32_step(kind, _p(h), step, _p(p), _p(g), gdt, p.size, _p(x1),
-                                  _p(x2) if x2 is not None else None), "optim32")
+    with _Params16(p, pdt) as pw:
+        _check(lib().orc_optim32_step(kind, _p(h), step, _p(pw), _p(g), gdt, pw.size, _p(x1),
+                                      _p(x2) if x2 is not None else None), "optim32")
 
 
-def optim8bit_step(kind, p, g, c1, a1, c2=None, a2=None, blocksize=2048, step=1, gdt=None, **hp):
+def optim8bit_step(kind, p, g, c1, a1, c2=None, a2=None, blocksize=2048, step=1, gdt=None, pdt=F32, **hp):
     """In-place 8-bit step of optimizer `kind`: states as dynamic 8-bit codes
-    c1 (and c2) with block absmax a1 (and a2)."""
+    c1 (and c2) with block absmax a1 (and a2); pdt as for optim32_step."""
     two = OPTIMIZER_STATES[kind] == 2
-    arrs = [(p, np.float32), (c1, np.uint8), (a1, np.float32)] + ([(c2, np.uint8), (a2, np.float32)] if two else [])
+    arrs = [(p, np.float32 if pdt == F32 else np.uint16), (c1, np.uint8), (a1, np.float32)]
+    arrs += [(c2, np.uint8), (a2, np.float32)] if two else []
     for arr, dt in arrs:
         if arr.dtype != dt or not arr.flags.c_contiguous:
             raise TypeError("contiguous arrays of the documented dtypes expected")
@@ -347,9 +382,10 @@ def optim8bit_step(kind, p, g, c1, a1, c2=None, a2=None, blocksize=2048, step=1,
         gdt = _dtype_id(g)
     g = np.ascontiguousarray(g)
     h = _optim_hp(**hp)
-    _check(lib().orc_optim8bit_step(kind, _p(h), step, _p(p), _p(g), gdt, p.size, _p(c1),
-                                    _p(c2) if two else None, _p(a1), _p(a2) if two else None, blocksize),
-           "optim8bit")
+    with _Params16(p, pdt) as pw:
+        _check(lib().orc_optim8bit_step(kind, _p(h), step, _p(pw), _p(g), gdt, pw.size, _p(c1),
+                                        _p(c2) if two else None, _p(a1), _p(a2) if two else None, blocksize),
+               "optim8bit")
 
 
 def f32_to_bf16_bits(x):

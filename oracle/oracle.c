@@ -117,6 +117,14 @@ static void store_elem(void* y, int dt, int64_t i, float v)
 
 /* exported for the tests that pin these conversions against a library routine */
 float orc_f16_to_f32(uint16_t h) { return f16_to_f32(h); }
+
+/* y[i] = x[i] converted from dtype xdt to ydt (widening exact; narrowing to
+ * nearest even). */
+int orc_convert(const void* x, int xdt, void* y, int ydt, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) store_elem(y, ydt, i, load_elem(x, xdt, i));
+    return 0;
+}
 uint16_t orc_f32_to_f16(float f) { return f32_to_f16(f); }
 uint16_t orc_f32_to_bf16(float f) { return f32_to_bf16(f); }
 

@@ -208,7 +208,7 @@ def test_optimizer_hyperparameters_rejected_before_launch(qb):
     f = L.qb_optimizer8bit_step
 
     def call(hp, s2=A, a2=A, n=100):
-        return f(ctypes.byref(hp), A, A2, 2, n, A, s2, A, a2, 2048, None)
+        return f(ctypes.byref(hp), A, 0, A2, 2, n, A, s2, A, a2, 2048, None)
 
     H = qb.optim_hparams
     bad = [H(qb.QB_SGD, 0.1, beta1=0.0),                              # SGD needs momentum
@@ -224,7 +224,7 @@ def test_optimizer_hyperparameters_rejected_before_launch(qb):
            H(7, 0.1)]
     for hp in bad:
         assert call(hp) == qb.QB_EINVAL, (hp.kind, hp.beta1, hp.beta2, hp.eps, hp.dampening, hp.nesterov)
-    assert f(None, A, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EINVAL
+    assert f(None, A, 0, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EINVAL
     # two-state kinds need state 2; zero length is a no-op for every kind
     assert call(H(qb.QB_ADAM, 1e-3), s2=None) == qb.QB_EINVAL
     assert call(H(qb.QB_ADAM, 1e-3), a2=A + 4) == qb.QB_EALIGN
@@ -232,16 +232,16 @@ def test_optimizer_hyperparameters_rejected_before_launch(qb):
         assert call(H(k, 1e-3), s2=None, a2=None, n=0) == qb.QB_OK
     tab = (qb.qb_tensor * 1)(qb.qb_tensor(A, A2, A, None, A, None, 100))
     m = L.qb_multi_tensor_optimizer_step
-    assert m(ctypes.byref(H(qb.QB_ADAM, 1e-3)), tab, 1, 2, 2048, A, L.qb_multi_tensor_workspace_bytes(1),
+    assert m(ctypes.byref(H(qb.QB_ADAM, 1e-3)), tab, 1, 0, 2, 2048, A, L.qb_multi_tensor_workspace_bytes(1),
              None) == qb.QB_EINVAL                                     # Adam without state 2
-    assert m(ctypes.byref(H(qb.QB_SGD, 1e-3, beta1=0.0)), tab, 1, 2, 2048, A,
+    assert m(ctypes.byref(H(qb.QB_SGD, 1e-3, beta1=0.0)), tab, 1, 0, 2, 2048, A,
              L.qb_multi_tensor_workspace_bytes(1), None) == qb.QB_EINVAL
-    assert m(ctypes.byref(H(qb.QB_LION, 1e-3)), tab, 1, 2, 2048, A, 8, None) == qb.QB_EWORKSPACE
+    assert m(ctypes.byref(H(qb.QB_LION, 1e-3)), tab, 1, 0, 2, 2048, A, 8, None) == qb.QB_EWORKSPACE
     # 32-bit fallback (absmax NULL): both absmax pointers NULL or neither for the two-state kinds
-    assert f(ctypes.byref(H(qb.QB_ADAMW, 1e-3)), A, A2, 2, 100, A, A, None, A, 2048, None) == qb.QB_EINVAL
-    assert f(ctypes.byref(H(qb.QB_ADAMW, 1e-3)), A, A2, 2, 100, A, A, A, None, 2048, None) == qb.QB_EINVAL
-    assert f(ctypes.byref(H(qb.QB_ADAM, 1e-3)), A, A2, 2, 100, A, None, None, None, 2048, None) == qb.QB_EINVAL
-    assert f(ctypes.byref(H(qb.QB_SGD, 1e-3)), A, A2, 2, 100, A + 4, None, None, None, 2048, None) == qb.QB_EALIGN
+    assert f(ctypes.byref(H(qb.QB_ADAMW, 1e-3)), A, 0, A2, 2, 100, A, A, None, A, 2048, None) == qb.QB_EINVAL
+    assert f(ctypes.byref(H(qb.QB_ADAMW, 1e-3)), A, 0, A2, 2, 100, A, A, A, None, 2048, None) == qb.QB_EINVAL
+    assert f(ctypes.byref(H(qb.QB_ADAM, 1e-3)), A, 0, A2, 2, 100, A, None, None, None, 2048, None) == qb.QB_EINVAL
+    assert f(ctypes.byref(H(qb.QB_SGD, 1e-3)), A, 0, A2, 2, 100, A + 4, None, None, None, 2048, None) == qb.QB_EALIGN
 
 
 def test_layerwise_arguments_and_workspace(qb):
@@ -255,10 +255,10 @@ def test_layerwise_arguments_and_workspace(qb):
            H(qb.QB_LAMB, 0.1, eps=0.0),
            H(qb.QB_LAMB, 0.1, beta2=1.0)]
     for hp in bad:
-        assert f(ctypes.byref(hp), A, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EINVAL
+        assert f(ctypes.byref(hp), A, 0, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EINVAL
     # valid, but the norms need a workspace: the single-tensor call refuses them
     for hp in (H(qb.QB_LAMB, 1e-3), H(qb.QB_LARS, 0.1, beta1=0.9, trust_coefficient=1e-3)):
-        assert f(ctypes.byref(hp), A, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EUNSUPPORTED
+        assert f(ctypes.byref(hp), A, 0, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EUNSUPPORTED
     # workspace: two tensor tables, 16 bytes per group of 32 tiles (tiles of max(B, 1024) elements),
     # 4 per tensor
     tab = (qb.qb_tensor * 3)(qb.qb_tensor(A, A2, A, A, A, A, 5000), qb.qb_tensor(A, A2, A, A, A, A, 0),
@@ -275,9 +275,9 @@ def test_layerwise_arguments_and_workspace(qb):
     assert L.qb_optimizer_workspace_bytes(ctypes.byref(lamb), tab, 3, 100) == 0
     # the step checks the larger workspace before touching the device
     m = L.qb_multi_tensor_optimizer_step
-    assert m(ctypes.byref(lamb), tab, 3, 2, 2048, A, region, None) == qb.QB_EWORKSPACE
-    assert m(ctypes.byref(lamb), tab, 3, 2, 2048, A, region + 511, None) == qb.QB_EWORKSPACE
-    assert m(ctypes.byref(lamb), tab, 3, 2, 2048, A, 512, None) == qb.QB_EWORKSPACE
+    assert m(ctypes.byref(lamb), tab, 3, 0, 2, 2048, A, region, None) == qb.QB_EWORKSPACE
+    assert m(ctypes.byref(lamb), tab, 3, 0, 2, 2048, A, region + 511, None) == qb.QB_EWORKSPACE
+    assert m(ctypes.byref(lamb), tab, 3, 0, 2, 2048, A, 512, None) == qb.QB_EWORKSPACE
 
 
 def test_linear_code_equals_oracle(qb):
@@ -315,3 +315,17 @@ def test_user_code_arguments_rejected_before_launch(qb):
 def test_status_strings(qb):
     assert qb.qb_status_string(0) == "ok"
     assert "workspace" in qb.qb_status_string(5)
+
+
+def test_parameter_dtype_pairs(qb):
+    """16-bit parameters need gradients of the same dtype; fp32 parameters take any."""
+    L = qb.lib()
+    A, A2 = 0x100000, 0x200000
+    f, m = L.qb_optimizer8bit_step, L.qb_multi_tensor_optimizer_step
+    hp = ctypes.byref(qb.optim_hparams(qb.QB_ADAMW, 1e-3))
+    F32, F16, BF16 = qb.QB_F32, qb.QB_F16, qb.QB_BF16
+    for pdt, gdt, want in [(BF16, F16, qb.QB_EUNSUPPORTED), (F16, BF16, qb.QB_EUNSUPPORTED),
+                           (BF16, F32, qb.QB_EUNSUPPORTED), (9, F32, qb.QB_EINVAL), (F32, 9, qb.QB_EINVAL),
+                           (BF16, BF16, qb.QB_OK), (F16, F16, qb.QB_OK), (F32, BF16, qb.QB_OK)]:
+        assert f(hp, A, pdt, A2, gdt, 0, A, A, A, A, 2048, None) == want, (pdt, gdt)   # n = 0: no launch
+        assert m(hp, None, 0, pdt, gdt, 2048, None, 0, None) == want, (pdt, gdt)       # count = 0: no launch
