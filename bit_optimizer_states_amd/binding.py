@@ -87,6 +87,8 @@ def lib():
         L.qb_optimizer_workspace_bytes.argtypes = [ctypes.POINTER(qb_optim_hparams), ctypes.POINTER(qb_tensor), i32,
                                                    i32]
         L.qb_optimizer_workspace_bytes.restype = sz
+        L.qb_dequant_matmul.argtypes = [vp, i32, i64, i64, vp, vp, ctypes.POINTER(qb_dq), i32, i32, i64, vp, vp]
+        L.qb_dequant_matmul.restype = ctypes.c_int
         L.qb_code_table_bytes.argtypes = []
         L.qb_code_table_bytes.restype = sz
         L.qb_linear_code.argtypes = [vp]
@@ -186,6 +188,15 @@ def qb_adamw8bit_step(p, g, n, m, v, absmax_m, absmax_v, blocksize, hp, stream=N
     _check(lib().qb_adamw8bit_step(_ptr(p), _ptr(g), _dtype(g), int(n), _ptr(m), _ptr(v), _ptr(absmax_m),
                                    _ptr(absmax_v), int(blocksize), ctypes.byref(hp), _stream(stream)),
            "qb_adamw8bit_step")
+
+
+def qb_dequant_matmul(x, codes, absmax, code, blocksize, N, y, dq=None, stream=None):
+    """y [M, N] = x [M, K] W^T with W [N, K] as 4-bit codes (absmax, or the
+    nested constants in dq); x and y of the compute dtype."""
+    M, K = x.shape
+    _check(lib().qb_dequant_matmul(_ptr(x), _dtype(x), int(M), int(K), _ptr(codes), _ptr(absmax),
+                                   ctypes.byref(dq) if dq is not None else None, int(code), int(blocksize), int(N),
+                                   _ptr(y), _stream(stream)), "qb_dequant_matmul")
 
 
 def optim_hparams(kind, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, dampening=0.0, nesterov=False,

@@ -477,6 +477,31 @@ qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* 
                                      dq != nullptr, (int)ydt, static_cast<hipStream_t>(stream)));
 }
 
+qb_status qb_dequant_matmul(const void* x, qb_dtype xdt, int64_t M, int64_t K, const uint8_t* codes,
+                            const float* absmax, const qb_dq* dq, qb_code code, int32_t blocksize, int64_t N,
+                            void* y, void* stream)
+{
+    if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || !valid_dtype(xdt) || !is4(code) || !pow2_block(blocksize))
+        return QB_EINVAL;
+    if (M == 0 || N == 0) return QB_OK;
+    if (!x || !codes || !y) return QB_EINVAL;
+    if (N > INT64_MAX / K) return QB_EINVAL;
+    const int64_t nb = nblocks(N * K, blocksize);
+    if (dq) {
+        if (absmax) return QB_EINVAL;
+        qb_status st = check_dq(dq, nb, false);
+        if (st != QB_OK) return st;
+    } else if (!absmax) {
+        return QB_EINVAL;
+    }
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(y) || (absmax && !aligned16(absmax))) return QB_EALIGN;
+    if (!device_tables()) return QB_EINIT;
+    return hip_status(launch_dq4_matmul(x, (int)xdt, M, K, codes, absmax, dq ? dq->codes : nullptr,
+                                        dq ? dq->absmax2 : nullptr, dq ? dq->offset : nullptr, blocksize,
+                                        dq ? dq->blocksize2 : 256, code4_index(code), N, y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t count, qb_code code,
                                      int32_t blocksize, int32_t blocksize2, qb_dtype ydt, void* ws, size_t ws_bytes,
                                      void* stream)

@@ -179,6 +179,14 @@ constexpr int kQuantileChunk = 4096;
 hipError_t launch_chunk_quantiles(const void* x, int xdt, int64_t n, float* E, hipStream_t s);
 hipError_t launch_quantile_code(const float* E, int64_t nchunks, double* S, UserCode* out, hipStream_t s);
 
+// y [M, N] = x [M, K] W^T in compute dtype xdt (fp32, fp16, bf16; y the same),
+// W [N, K] as 4-bit codes (code4: 0 NF4, 1 FP4) with block size B and either
+// absmax (plain) or c2 / absmax2 / offset (nested, block size B2).  K is a
+// multiple of 32; x, codes and y are 16-byte aligned.
+hipError_t launch_dq4_matmul(const void* x, int xdt, int64_t M, int64_t K, const uint8_t* codes, const float* absmax,
+                             const uint8_t* c2, const float* absmax2, const float* offset, int B, int B2, int code4,
+                             int64_t N, void* y, hipStream_t s);
+
 // Exact mean of the absmax of one tensor (map == nullptr) or of the `count`
 // tensors of map (second-pass descriptors) into offset[0].
 hipError_t launch_dq_mean(const QuantDesc& single, const TileMap<QuantDesc>* map, int count,

@@ -253,6 +253,31 @@ qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* 
                         int32_t blocksize, int64_t n, void* y, qb_dtype ydt, void* stream);
 
 /*
+ * qb_dequant_matmul -- y = x W^T with the weights W held in 4 bits: the
+ * product of a 4-bit layer in its compute dtype (page "Bitsandbytes",
+ * section QLoRA: Hesaplama veri türü; page "Quantize 🤗 Transformers models",
+ * sections Change the compute dtype and Using NF4).  Every weight is first
+ * dequantized exactly as by qb_dequantize into the compute dtype xdt, then the
+ * products are summed in binary32 (fused in one kernel: the dequantized matrix
+ * is never written to memory).
+ *   x       [M, K] row-major, dtype xdt (QB_F32, QB_F16 or QB_BF16), 16-byte aligned.
+ *   codes   W [N, K] row-major (a layer's [out, in] weight), NF4 or FP4 codes,
+ *           two per byte as qb_quantize writes them; 16-byte aligned.
+ *   absmax  [ceil(N*K / blocksize)] fp32, or NULL with dq (nested constants:
+ *           dq->codes, absmax2, offset, blocksize2; dq->ws is not used).
+ *   y       [M, N] row-major, dtype xdt, 16-byte aligned; each output is the
+ *           binary32 sum rounded once to xdt.
+ * Requirements: K a positive multiple of 32; M, N >= 0 (either 0: no-op).
+ * Accuracy: each product of two xdt values is exact in binary32; the K-term
+ * sums are added in an order of the kernel's own (fixed: the same bits on
+ * every run), so y is within (K+2) 2^-23 sum_k |x_mk w_nk| of the exact
+ * product before its final rounding.
+ */
+qb_status qb_dequant_matmul(const void* x, qb_dtype xdt, int64_t M, int64_t K, const uint8_t* codes,
+                            const float* absmax, const qb_dq* dq, qb_code code, int32_t blocksize, int64_t N,
+                            void* y, void* stream);
+
+/*
  * qb_multi_tensor_dequantize -- qb_dequantize on `count` tensors in ONE kernel
  * launch (same code, block size, nested block size and output dtype for all;
  * the result equals a loop of single-tensor calls, bit for bit).  Dequantizing

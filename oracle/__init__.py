@@ -215,6 +215,21 @@ def dq_quantize(absmax, blocksize2=256):
     return c2, a2, mu
 
 
+def dequant_matmul(x, xdt, codes, scale, code, blocksize, N):
+    """The product of a 4-bit layer in its compute dtype xdt ("Bitsandbytes",
+    section QLoRA: Hesaplama veri türü): W [N, K] = the block-wise dequantized
+    weights in xdt (dequantize_blockwise, per-block scale = absmax or the
+    decoded nested constants), then y = x W^T with x [M, K] (float32, or uint16
+    bits of xdt).  Returns (s, a): s [M, N] the product in binary64 (every
+    product of two xdt values is exact there; the sum's own rounding is far
+    below binary32's), a [M, N] = sum_k |x_mk w_nk| (for error bounds)."""
+    M, K = x.shape
+    w = dequantize_blockwise(codes, scale, code, blocksize, N * K, ydt=xdt)
+    xf = (x if xdt == F32 else convert(x.reshape(-1), xdt, F32).reshape(M, K)).astype(np.float64)
+    wf = (w if xdt == F32 else convert(w, xdt, F32)).astype(np.float64).reshape(N, K)
+    return xf @ wf.T, np.abs(xf) @ np.abs(wf).T
+
+
 def dq_decode(c2, absmax2, mu, blocksize2=256):
     c2 = np.ascontiguousarray(c2, dtype=np.uint8)
     absmax2 = np.ascontiguousarray(absmax2, dtype=np.float32)

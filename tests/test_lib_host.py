@@ -329,3 +329,25 @@ def test_parameter_dtype_pairs(qb):
                            (BF16, BF16, qb.QB_OK), (F16, F16, qb.QB_OK), (F32, BF16, qb.QB_OK)]:
         assert f(hp, A, pdt, A2, gdt, 0, A, A, A, A, 2048, None) == want, (pdt, gdt)   # n = 0: no launch
         assert m(hp, None, 0, pdt, gdt, 2048, None, 0, None) == want, (pdt, gdt)       # count = 0: no launch
+
+
+def test_dequant_matmul_arguments_rejected_before_launch(qb):
+    L = qb.lib()
+    A = 0x100000
+    f = L.qb_dequant_matmul
+    dq = qb.qb_dq(A, A, A, 256, None, 0)
+    BF16, NF4, DYN8 = qb.QB_BF16, 1, 0
+    assert f(A, BF16, 0, 64, A, A, None, NF4, 64, 10, A, None) == qb.QB_OK        # M = 0: no-op
+    assert f(A, BF16, 4, 64, A, A, None, NF4, 64, 0, A, None) == qb.QB_OK         # N = 0: no-op
+    assert f(A, BF16, 4, 48, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL    # K not a multiple of 32
+    assert f(A, BF16, 4, 0, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL
+    assert f(A, BF16, -1, 64, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL
+    assert f(A, BF16, 4, 64, A, A, None, DYN8, 64, 10, A, None) == qb.QB_EINVAL   # 4-bit codes only
+    assert f(A, 9, 4, 64, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL
+    assert f(A, BF16, 4, 64, A, A, None, NF4, 100, 10, A, None) == qb.QB_EINVAL   # block size
+    assert f(A, BF16, 4, 64, A, None, None, NF4, 64, 10, A, None) == qb.QB_EINVAL  # no absmax
+    assert f(A, BF16, 4, 64, A, A, ctypes.byref(dq), NF4, 64, 10, A, None) == qb.QB_EINVAL   # both
+    assert f(None, BF16, 4, 64, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL
+    assert f(A + 8, BF16, 4, 64, A, A, None, NF4, 64, 10, A, None) == qb.QB_EALIGN
+    assert f(A, BF16, 4, 64, A + 8, A, None, NF4, 64, 10, A, None) == qb.QB_EALIGN
+    assert f(A, BF16, 4, 64, A, A, None, NF4, 64, 10, A + 4, None) == qb.QB_EALIGN
