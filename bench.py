@@ -200,6 +200,21 @@ def time_calls(torch, fn, reps=5):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
+def time_back_to_back(torch, fn, reps=20):
+    """Mean time (ms) of one fn() call over reps calls run back to back between
+    two HIP events (after one warmup call): for microsecond kernels, whose
+    per-call events would otherwise weigh in."""
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def cpu_baseline(torch, model, seconds_target, rng):
     """The oracle, single-threaded, on a bounded sample of the same workload:
     seeded full AdamW blocks of the 7B model (copied from the device), one
@@ -382,6 +397,58 @@ def bench_codes(torch, qb, inputs, dev, args):
     print(json.dumps(out), flush=True)
 
 
+MM_SHAPES = [(4096, 4096), (11008, 4096), (4096, 11008)]      # (N, K) of the 7B projections
+MM_ROWS = [1, 16, 64, 256, 4096]
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def dq4_matmul_bytes(M, N, K, block=W4_BLOCK, block2=W4_BLOCK2):
+    """Algorithmic HBM bytes of one fused call: NF4 codes, nested constants
+    (one code byte per block, fp32 second-level absmax, the mean), x and y (bf16)."""
+    nb = -(-N * K // block)
+    return N * K / 2 + nb + 4 * -(-nb // block2) + 4 + 2 * M * K + 2 * M * N
+
+
+def bench_matmul(torch, qb, inputs, dev, args):
+    """The 4-bit layer product in bf16: qb_dequant_matmul (NF4, nested, B = 64)
+    against the unfused route (qb_dequantize to bf16, then torch's matmul) on the
+    7B decoder's projection shapes, for M = 1 .. 4096 rows of activations.
+    Codes are uniform random bytes and the nested constants fixed values (the
+    kernels have no data-dependent work)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    out = {"workload": "y = x W^T, W NF4 (B = 64, nested B2 = 256), bf16 compute, 7B projection shapes",
+           "shapes": []}
+    for N, K in MM_SHAPES:
+        nb = N * K // W4_BLOCK
+        codes = torch.randint(0, 256, (N * K // 2,), dtype=torch.uint8, device=dev, generator=g)
+        c2 = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=dev, generator=g)
+        a2 = torch.full((-(-nb // W4_BLOCK2),), 0.02, device=dev)
+        mu = torch.full((4,), 0.03, device=dev)
+        dq = qb.make_dq(c2, a2, mu, W4_BLOCK2)
+        w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        for M in MM_ROWS:
+            x = inputs.normal(M * K, 1.0, seed=args.seed + M, device=dev, dtype=torch.bfloat16).view(M, K)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fused = time_back_to_back(torch, lambda: qb.qb_dequant_matmul(x, codes, None, 1, W4_BLOCK, N, y, dq=dq),
+                                      reps=args.steps)
+
+            def unfused():
+                qb.qb_dequantize(codes, None, dq, 1, W4_BLOCK, N * K, w)
+                torch.matmul(x, w.t(), out=y)
+
+            ref = time_back_to_back(torch, unfused, reps=args.steps)
+            nbytes = dq4_matmul_bytes(M, N, K)
+            flops = 2.0 * M * N * K
+            out["shapes"].append({"N": N, "K": K, "M": M, "fused_us": fused * 1e3, "unfused_us": ref * 1e3,
+                                  "speedup": ref / fused, "GB/s": nbytes / fused / 1e6,
+                                  "frac_of_hbm_peak": nbytes / fused / 1e6 / HBM_PEAK_GBS,
+                                  "TFLOP/s": flops / fused / 1e9,
+                                  "frac_of_bf16_mfma_peak": flops / fused / 1e9 / MFMA_BF16_PEAK_TFLOPS})
+            log(f"N={N} K={K} M={M}: fused {fused * 1e3:.1f} us, unfused {ref * 1e3:.1f} us")
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration(torch, dev):
     """Five device-to-device copies of exactly 1 GiB: 1,073,741,824 bytes read and
     written per dispatch.  Profiling this under FETCH_SIZE / WRITE_SIZE gives the
@@ -413,6 +480,8 @@ def main():
                     help="state width of the --flat run (32: the binary32 fallback of small or chosen tensors)")
     ap.add_argument("--codes", action="store_true",
                     help="time the user-code calls (quantile estimation, quantile and linear codes) instead")
+    ap.add_argument("--matmul", action="store_true",
+                    help="time the fused 4-bit dequantize + product on the 7B projection shapes instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device five times (the reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -436,6 +505,8 @@ def main():
         return bench_flat(torch, qb, inputs, dev, args)
     if args.codes:
         return bench_codes(torch, qb, inputs, dev, args)
+    if args.matmul:
+        return bench_matmul(torch, qb, inputs, dev, args)
     model = Model7B(torch, qb, inputs, dev, args.seed, with_w4=not args.adam_only)
     torch.cuda.synchronize()
     log(f"setup done; warmup {args.warmup} steps")
