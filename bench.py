@@ -313,7 +313,15 @@ def bench_flat(torch, qb, inputs, dev, args):
     pdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[args.param_dtype]
     gdt = torch.bfloat16 if args.param_dtype == "fp32" else pdt      # 16-bit params take grads of their dtype
     p = inputs.normal(n, 0.02, seed=args.seed, device=dev, dtype=pdt)
-    if args.state_bits == 8:
+    if args.paged:                # states in pinned host memory, stepped page by page
+        if args.state_bits != 8 or args.optimizer in LAYERWISE:
+            raise SystemExit("--paged runs the element-wise kinds with 8-bit states")
+        pin = lambda t: torch.empty(t.shape, dtype=t.dtype, pin_memory=True).copy_(t)
+        s1 = pin(torch.full((n,), 127, dtype=torch.uint8))
+        a1 = pin(torch.zeros(nb))
+        s2 = pin(torch.full((n,), 127, dtype=torch.uint8)) if states == 2 else None
+        a2 = pin(torch.zeros(nb)) if states == 2 else None
+    elif args.state_bits == 8:
         s1 = torch.full((n,), 127, dtype=torch.uint8, device=dev)
         a1 = torch.zeros(nb, device=dev)
         s2 = torch.full((n,), 127, dtype=torch.uint8, device=dev) if states == 2 else None
@@ -325,14 +333,20 @@ def bench_flat(torch, qb, inputs, dev, args):
     grads = [inputs.normal(n, 1e-3, inputs.grad_seed(args.seed, 0, k), device=dev, dtype=gdt) for k in range(2)]
 
     layerwise = args.optimizer in LAYERWISE
-    if layerwise:               # one tensor = one layer, through the multi-tensor call (norm pass + step)
+    if args.paged:
+        tables = [qb.paged_tensor_table([(p, grads[j], s1, s2, a1, a2)]) for j in range(2)]
+        ws = torch.empty(qb.qb_paged_workspace_bytes(args.page_params, ADAM_BLOCK), dtype=torch.uint8, device=dev)
+    elif layerwise:             # one tensor = one layer, through the multi-tensor call (norm pass + step)
         tables = [qb.tensor_table([(p, grads[j], s1, s2, a1, a2)]) for j in range(2)]
         ws = torch.empty(qb.qb_optimizer_workspace_bytes(qb.optim_hparams(kind, **hp), tables[0], 1, ADAM_BLOCK),
                          dtype=torch.uint8, device=dev)
 
     def step(k):
         h = qb.optim_hparams(kind, step=k, **hp)
-        if layerwise:
+        if args.paged:
+            qb.qb_paged_optimizer_step(h, tables[k % 2], 1, qb._DTYPE[gdt], ADAM_BLOCK, args.page_params, ws,
+                                       pdt=qb._DTYPE[pdt])
+        elif layerwise:
             qb.qb_multi_tensor_optimizer_step(h, tables[k % 2], 1, qb._DTYPE[gdt], ADAM_BLOCK, ws,
                                               pdt=qb._DTYPE[pdt])
         else:
@@ -359,6 +373,11 @@ def bench_flat(torch, qb, inputs, dev, args):
         bpp -= 4 if not layerwise else 6            # p read + written in 2 bytes (and read in the norm pass)
     nbytes = n * bpp
     call = "one-layer multi-tensor call (norm pass + step)" if layerwise else "single-tensor"
+    extra = {}
+    if args.paged:
+        call = f"paged (states in pinned host memory, pages of {args.page_params:,} params)"
+        state_bytes = n * states * (1 + 4.0 / ADAM_BLOCK)      # each way across PCIe
+        extra = {"pcie_bytes_each_way": state_bytes, "pcie_GB/s_each_way": state_bytes / med / 1e6}
     print(json.dumps({"workload": f"flat 1.5e9 params, {args.param_dtype if args.param_dtype != 'fp32' else 'bf16'} "
                                   f"grads, block 2048, {call} {args.optimizer} "
                                   f"step, {args.state_bits}-bit states, {args.param_dtype} params",
@@ -366,7 +385,7 @@ def bench_flat(torch, qb, inputs, dev, args):
                       "state_bits": args.state_bits, "steps": args.steps, "median_ms": med,
                       "bytes_per_param": bpp, "GB/s": nbytes / med / 1e6,
                       "params_per_s": n / med * 1e3, "frac_of_hbm_peak": nbytes / med / 1e6 / HBM_PEAK_GBS,
-                      "wall_ms_per_step": wall / args.steps * 1e3}), flush=True)
+                      "wall_ms_per_step": wall / args.steps * 1e3, **extra}), flush=True)
 
 
 def bench_codes(torch, qb, inputs, dev, args):
@@ -472,6 +491,9 @@ def main():
     ap.add_argument("--adam-only", action="store_true", help="time only the multi-tensor AdamW step")
     ap.add_argument("--flat", action="store_true",
                     help="time the single-tensor AdamW step on a flat 1.5e9-parameter buffer instead")
+    ap.add_argument("--paged", action="store_true",
+                    help="--flat with the optimizer states in pinned host memory (qb_paged_optimizer_step)")
+    ap.add_argument("--page-params", type=int, default=1 << 26, help="parameters per page of the --paged run")
     ap.add_argument("--param-dtype", choices=["fp32", "bf16", "fp16"], default="fp32",
                     help="parameter dtype of the --flat run (16-bit parameters take gradients of their dtype)")
     ap.add_argument("--optimizer", choices=sorted(OPTIMIZERS), default="adamw",

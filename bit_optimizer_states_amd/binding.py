@@ -87,6 +87,11 @@ def lib():
         L.qb_optimizer_workspace_bytes.argtypes = [ctypes.POINTER(qb_optim_hparams), ctypes.POINTER(qb_tensor), i32,
                                                    i32]
         L.qb_optimizer_workspace_bytes.restype = sz
+        L.qb_paged_optimizer_step.argtypes = [ctypes.POINTER(qb_optim_hparams), ctypes.POINTER(qb_tensor), i32, i32,
+                                              i32, i32, i64, vp, sz, vp]
+        L.qb_paged_optimizer_step.restype = ctypes.c_int
+        L.qb_paged_workspace_bytes.argtypes = [i64, i32]
+        L.qb_paged_workspace_bytes.restype = sz
         L.qb_dequant_matmul.argtypes = [vp, i32, i64, i64, vp, vp, ctypes.POINTER(qb_dq), i32, i32, i64, vp, vp]
         L.qb_dequant_matmul.restype = ctypes.c_int
         L.qb_code_table_bytes.argtypes = []
@@ -129,6 +134,17 @@ def _ptr(t):
         raise TypeError("torch tensor expected")
     if not t.is_cuda:
         raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
+def _pinned_ptr(t):
+    """Data pointer of a pinned host tensor, or None."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.is_cuda or (t.numel() > 0 and not t.is_pinned()):
+        raise ValueError("pinned host tensor expected")      # (an empty tensor has no storage to pin)
     if not t.is_contiguous():
         raise ValueError("contiguous tensor expected")
     return t.data_ptr()
@@ -231,6 +247,29 @@ def qb_multi_tensor_optimizer_step(hp, table, count, gdt, blocksize, ws, stream=
                                                 int(blocksize), _ptr(ws), ws.numel() * ws.element_size(),
                                                 _stream(stream)),
            "qb_multi_tensor_optimizer_step")
+
+
+def paged_tensor_table(tensors):
+    """ctypes array of qb_tensor for the paged step from tuples (p, g, m, v,
+    absmax_m, absmax_v): p, g device tensors; the states pinned host tensors
+    (v and absmax_v may be None for the one-state optimizers)."""
+    arr = (qb_tensor * len(tensors))()
+    for i, (p, g, m, v, am, av) in enumerate(tensors):
+        arr[i] = qb_tensor(_ptr(p), _ptr(g), _pinned_ptr(m), _pinned_ptr(v), _pinned_ptr(am), _pinned_ptr(av),
+                           p.numel())
+    return arr
+
+
+def qb_paged_workspace_bytes(page_params, blocksize):
+    return lib().qb_paged_workspace_bytes(int(page_params), int(blocksize))
+
+
+def qb_paged_optimizer_step(hp, table, count, gdt, blocksize, page_params, ws, stream=None, pdt=QB_F32):
+    """table: tensor_table() rows with p, g on the device and the states in
+    pinned host memory (torch pin_memory=True)."""
+    _check(lib().qb_paged_optimizer_step(ctypes.byref(hp), table, int(count), int(pdt), int(gdt), int(blocksize),
+                                         int(page_params), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)), "qb_paged_optimizer_step")
 
 
 def qb_multi_tensor_step(table, count, gdt, blocksize, hp, ws, stream=None):

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "qb.h"
@@ -285,6 +286,55 @@ qb_status check_quant_tensor(const void* x, uint8_t* codes, float* absmax, uint8
 }
 
 int64_t dequant_tiles(int64_t n, int64_t tile) { return (n + tile - 1) / tile; }
+
+// Per-device resources of the paged step: the two copy streams (default
+// priority) and the events that order the staging slots; created on first
+// use and kept until the process ends.
+struct PagedRes {
+    hipStream_t h2d = nullptr, d2h = nullptr;
+    hipEvent_t start = nullptr, done = nullptr;
+    hipEvent_t in[2] = {nullptr, nullptr}, kern[2] = {nullptr, nullptr}, out[2] = {nullptr, nullptr};
+};
+
+PagedRes* paged_resources()
+{
+    static std::mutex mu;
+    static std::vector<PagedRes*> per_dev;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)per_dev.size() <= dev) per_dev.resize(dev + 1, nullptr);
+    if (per_dev[dev]) return per_dev[dev];
+    PagedRes* r = new PagedRes;
+    bool ok = hipStreamCreateWithFlags(&r->h2d, hipStreamNonBlocking) == hipSuccess &&
+              hipStreamCreateWithFlags(&r->d2h, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&r->start, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&r->done, hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; ok && i < 2; ++i)
+        ok = hipEventCreateWithFlags(&r->in[i], hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&r->kern[i], hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&r->out[i], hipEventDisableTiming) == hipSuccess;
+    if (!ok) return nullptr;                       // (kept: a later call retries nothing, reports QB_EHIP)
+    per_dev[dev] = r;
+    return r;
+}
+
+// True if p points into pinned (page-locked) host memory.
+bool pinned_host(const void* p)
+{
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();                   // pageable memory: clear the error the query left
+        return false;
+    }
+    return a.type == hipMemoryTypeHost;
+}
+
+// Bytes of one staging region of the paged step.
+size_t paged_region(int64_t P, int32_t B, bool codes)
+{
+    return codes ? round_up((size_t)P, 256) : round_up((size_t)((P + B - 1) / B) * sizeof(float), 256);
+}
 
 }  // namespace
 
@@ -737,6 +787,97 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
     if (!hp) return QB_EINVAL;
     const qb_optim_hparams o = as_optim(hp);
     return qb_multi_tensor_optimizer_step(&o, tensors, count, QB_F32, gdt, blocksize, ws, ws_bytes, stream);
+}
+
+size_t qb_paged_workspace_bytes(int64_t page_params, int32_t blocksize)
+{
+    if (!pow2_block(blocksize) || page_params <= 0 || page_params % blocksize != 0) return 0;
+    return 2 * (2 * paged_region(page_params, blocksize, true) + 2 * paged_region(page_params, blocksize, false));
+}
+
+qb_status qb_paged_optimizer_step(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count, qb_dtype pdt,
+                                  qb_dtype gdt, int32_t blocksize, int64_t page_params, void* ws, size_t ws_bytes,
+                                  void* stream)
+{
+    if (count < 0 || !valid_dtype(pdt) || !valid_dtype(gdt) || !pow2_block(blocksize) || !valid_optim(hp))
+        return QB_EINVAL;
+    if (check_optim_dtypes(pdt, gdt) != QB_OK || layerwise(hp->kind)) return QB_EUNSUPPORTED;
+    if (page_params <= 0 || page_params % blocksize != 0 || page_params >= (int64_t(1) << 31)) return QB_EINVAL;
+    if (count == 0) return QB_OK;
+    if (!tensors || !ws) return QB_EINVAL;
+    if (!aligned16(ws)) return QB_EALIGN;
+    if (ws_bytes < qb_paged_workspace_bytes(page_params, blocksize)) return QB_EWORKSPACE;
+    const bool two = optim_states(hp->kind) == 2;
+    for (int32_t i = 0; i < count; ++i) {
+        const qb_tensor& t = tensors[i];
+        if (t.n < 0) return QB_EINVAL;
+        if (t.n == 0) continue;
+        if (nblocks(t.n, blocksize) >= (int64_t(1) << 31)) return QB_EINVAL;
+        if (!t.absmax_m || (two && !t.absmax_v)) return QB_EUNSUPPORTED;      // 8-bit states only
+        qb_status st = check_optim_tensor(two, t.p, t.g, t.m, two ? t.v : nullptr, t.absmax_m,
+                                          two ? t.absmax_v : nullptr);
+        if (st != QB_OK) return st;
+        if (!pinned_host(t.m) || !pinned_host(t.absmax_m) ||
+            (two && (!pinned_host(t.v) || !pinned_host(t.absmax_v))))
+            return QB_EINVAL;
+    }
+    if (!device_tables()) return QB_EINIT;
+    PagedRes* r = paged_resources();
+    if (!r) return QB_EHIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const OptScalars hs = prepare(*hp);
+    const int64_t P = page_params;
+    const size_t cb = paged_region(P, blocksize, true), ab = paged_region(P, blocksize, false);
+    const size_t slot_bytes = 2 * cb + 2 * ab;
+    auto ck = [](hipError_t e) { return e == hipSuccess; };
+    // the copies start after the work already on `stream`
+    if (!ck(hipEventRecord(r->start, s)) || !ck(hipStreamWaitEvent(r->h2d, r->start, 0)) ||
+        !ck(hipStreamWaitEvent(r->d2h, r->start, 0)))
+        return QB_EHIP;
+    int64_t page = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const qb_tensor& t = tensors[i];
+        for (int64_t off = 0; off < t.n; off += P, ++page) {
+            const int slot = (int)(page & 1);
+            const int64_t n = t.n - off < P ? t.n - off : P;
+            const int64_t b0 = off / blocksize, nb = (n + blocksize - 1) / blocksize;
+            char* base = static_cast<char*>(ws) + slot * slot_bytes;
+            uint8_t* m = reinterpret_cast<uint8_t*>(base);
+            uint8_t* v = reinterpret_cast<uint8_t*>(base + cb);
+            float* am = reinterpret_cast<float*>(base + 2 * cb);
+            float* av = reinterpret_cast<float*>(base + 2 * cb + ab);
+            // host to device, once the slot's previous page has been copied back
+            bool ok = page < 2 || ck(hipStreamWaitEvent(r->h2d, r->out[slot], 0));
+            ok = ok && ck(hipMemcpyAsync(m, t.m + off, (size_t)n, hipMemcpyHostToDevice, r->h2d)) &&
+                 ck(hipMemcpyAsync(am, t.absmax_m + b0, (size_t)nb * sizeof(float), hipMemcpyHostToDevice, r->h2d));
+            if (two)
+                ok = ok && ck(hipMemcpyAsync(v, t.v + off, (size_t)n, hipMemcpyHostToDevice, r->h2d)) &&
+                     ck(hipMemcpyAsync(av, t.absmax_v + b0, (size_t)nb * sizeof(float), hipMemcpyHostToDevice,
+                                       r->h2d));
+            ok = ok && ck(hipEventRecord(r->in[slot], r->h2d)) && ck(hipStreamWaitEvent(s, r->in[slot], 0));
+            if (!ok) return QB_EHIP;
+            // the step of the page, on the caller's stream
+            const size_t ps = pdt == QB_F32 ? 4 : 2, gs = gdt == QB_F32 ? 4 : 2;
+            TensorDesc d{static_cast<char*>(t.p) + off * ps, static_cast<const char*>(t.g) + off * gs, m,
+                         two ? v : nullptr, am, two ? av : nullptr, n, 0};
+            hipError_t e = launch_optim8((int)hp->kind, d, nullptr, adamw_tiles(n, blocksize), blocksize, (int)pdt,
+                                         (int)gdt, hs, nullptr, s);
+            if (e != hipSuccess) return hip_status(e);
+            // device to host after the step
+            ok = ck(hipEventRecord(r->kern[slot], s)) && ck(hipStreamWaitEvent(r->d2h, r->kern[slot], 0)) &&
+                 ck(hipMemcpyAsync(t.m + off, m, (size_t)n, hipMemcpyDeviceToHost, r->d2h)) &&
+                 ck(hipMemcpyAsync(t.absmax_m + b0, am, (size_t)nb * sizeof(float), hipMemcpyDeviceToHost, r->d2h));
+            if (two)
+                ok = ok && ck(hipMemcpyAsync(t.v + off, v, (size_t)n, hipMemcpyDeviceToHost, r->d2h)) &&
+                     ck(hipMemcpyAsync(t.absmax_v + b0, av, (size_t)nb * sizeof(float), hipMemcpyDeviceToHost,
+                                       r->d2h));
+            ok = ok && ck(hipEventRecord(r->out[slot], r->d2h));
+            if (!ok) return QB_EHIP;
+        }
+    }
+    // later work on `stream` waits for the last copy back
+    if (!ck(hipEventRecord(r->done, r->d2h)) || !ck(hipStreamWaitEvent(s, r->done, 0))) return QB_EHIP;
+    return QB_OK;
 }
 
 }  // extern "C"

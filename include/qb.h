@@ -373,6 +373,43 @@ qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_te
                                          void* stream);
 
 /*
+ * qb_paged_optimizer_step -- the multi-tensor 8-bit step with the optimizer
+ * states held in host memory: the paged 8-bit optimizer of page
+ * "bitsandbytes - Quantização de LLM", section Workflow 3 (optimizer
+ * "paged_adamw_8bit"), for models whose states do not fit beside the weights.
+ * Each tensor is cut into pages of page_params parameters; per page the
+ * state codes and absmax are copied to a device staging slot, the fused step
+ * runs on the page, and the states are copied back.  Two staging slots and
+ * two internal copy streams (host to device, device to host; default priority)
+ * overlap the copies of neighbouring pages with the step of the current one.
+ * The result equals qb_multi_tensor_optimizer_step on device-resident states,
+ * bit for bit (the same kernel per block).
+ *   tensors      as for qb_multi_tensor_optimizer_step, with p and g in device
+ *                memory and m, v, absmax_m, absmax_v in pinned host memory
+ *                (hipHostMalloc, or torch's pin_memory); 8-bit states only.
+ *   page_params  parameters per page: a positive multiple of blocksize.
+ *   ws           device staging of qb_paged_workspace_bytes(page_params,
+ *                blocksize) bytes, 16-byte aligned.
+ * Kinds: every element-wise kind (QB_ADAMW .. QB_RMSPROP); the layer-wise ones
+ * give QB_EUNSUPPORTED (their norms need a whole tensor before any page moves).
+ * Ordering: the call's work starts after the work already on `stream` and
+ * `stream` waits for the last copy back, so later work on `stream` sees the
+ * updated parameters and states.  Calls on one device share the internal
+ * streams and events, so they must not be made from several host threads at
+ * once; the states of a call must not be touched by the host until `stream`
+ * has passed the call, and consecutive calls on the same states should use
+ * the same `stream`.
+ */
+qb_status qb_paged_optimizer_step(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count, qb_dtype pdt,
+                                  qb_dtype gdt, int32_t blocksize, int64_t page_params, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Device staging bytes of qb_paged_optimizer_step: two slots, each with two
+ * code pages of page_params bytes and two absmax pages, 256-byte aligned.
+ * 0 if page_params is not a positive multiple of a valid blocksize. */
+size_t qb_paged_workspace_bytes(int64_t page_params, int32_t blocksize);
+
+/*
  * User codes.  The pages list three 8-bit quantization types, quantile,
  * linear and dynamic, and a fast quantile estimation (page "Py之bitsandbytes",
  * section 1).  Besides the built-in dynamic code, a block-wise 8-bit

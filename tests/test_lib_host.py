@@ -351,3 +351,26 @@ def test_dequant_matmul_arguments_rejected_before_launch(qb):
     assert f(A + 8, BF16, 4, 64, A, A, None, NF4, 64, 10, A, None) == qb.QB_EALIGN
     assert f(A, BF16, 4, 64, A + 8, A, None, NF4, 64, 10, A, None) == qb.QB_EALIGN
     assert f(A, BF16, 4, 64, A, A, None, NF4, 64, 10, A + 4, None) == qb.QB_EALIGN
+
+
+def test_paged_step_arguments_and_workspace(qb):
+    L = qb.lib()
+    A, A2 = 0x100000, 0x200000
+    # two slots: two code pages (page_params bytes each) and two absmax pages, 256-byte aligned
+    assert L.qb_paged_workspace_bytes(16384, 2048) == 2 * (2 * 16384 + 2 * 256)
+    assert L.qb_paged_workspace_bytes(2048 * 100, 2048) == 2 * (2 * 204800 + 2 * 512)
+    assert L.qb_paged_workspace_bytes(1000, 2048) == 0 and L.qb_paged_workspace_bytes(4096, 100) == 0
+    f = L.qb_paged_optimizer_step
+    H = qb.optim_hparams
+    tab = (qb.qb_tensor * 1)(qb.qb_tensor(A, A2, A, A, A, A, 5000))
+    ws = L.qb_paged_workspace_bytes(16384, 2048)
+    adamw = ctypes.byref(H(qb.QB_ADAMW, 1e-3))
+    assert f(adamw, tab, 0, 0, 2, 2048, 16384, A, ws, None) == qb.QB_OK                 # count 0: no-op
+    assert f(adamw, tab, 1, 0, 2, 2048, 1000, A, ws, None) == qb.QB_EINVAL              # page not a block multiple
+    assert f(adamw, tab, 1, 0, 2, 2048, 16384, A, ws - 1, None) == qb.QB_EWORKSPACE
+    assert f(adamw, tab, 1, 0, 2, 2048, 16384, A + 8, ws, None) == qb.QB_EALIGN
+    assert f(ctypes.byref(H(qb.QB_LAMB, 1e-3)), tab, 1, 0, 2, 2048, 16384, A, ws, None) == qb.QB_EUNSUPPORTED
+    s32 = (qb.qb_tensor * 1)(qb.qb_tensor(A, A2, A, A, None, None, 5000))           # binary32 states
+    assert f(adamw, s32, 1, 0, 2, 2048, 16384, A, ws, None) == qb.QB_EUNSUPPORTED
+    # states that are not pinned host memory are refused before anything is enqueued
+    assert f(adamw, tab, 1, 0, 2, 2048, 16384, A, ws, None) == qb.QB_EINVAL
