@@ -531,7 +531,9 @@ qb_status qb_dequant_matmul(const void* x, qb_dtype xdt, int64_t M, int64_t K, c
                             const float* absmax, const qb_dq* dq, qb_code code, int32_t blocksize, int64_t N,
                             void* y, void* stream)
 {
-    if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || !valid_dtype(xdt) || !is4(code) || !pow2_block(blocksize))
+    // K < 2^24: the kernel keeps a lane's offsets within a 64-row tile of x in 32 bits
+    if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || K >= (int64_t(1) << 24) || !valid_dtype(xdt) || !is4(code) ||
+        !pow2_block(blocksize))
         return QB_EINVAL;
     if (M == 0 || N == 0) return QB_OK;
     if (!x || !codes || !y) return QB_EINVAL;

@@ -267,7 +267,7 @@ qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* 
  *           dq->codes, absmax2, offset, blocksize2; dq->ws is not used).
  *   y       [M, N] row-major, dtype xdt, 16-byte aligned; each output is the
  *           binary32 sum rounded once to xdt.
- * Requirements: K a positive multiple of 32; M, N >= 0 (either 0: no-op).
+ * Requirements: K a positive multiple of 32 below 2^24; M, N >= 0 (either 0: no-op).
  * Accuracy: each product of two xdt values is exact in binary32; the K-term
  * sums are added in an order of the kernel's own (fixed: the same bits on
  * every run), so y is within (K+2) 2^-23 sum_k |x_mk w_nk| of the exact

@@ -341,6 +341,7 @@ def test_dequant_matmul_arguments_rejected_before_launch(qb):
     assert f(A, BF16, 4, 64, A, A, None, NF4, 64, 0, A, None) == qb.QB_OK         # N = 0: no-op
     assert f(A, BF16, 4, 48, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL    # K not a multiple of 32
     assert f(A, BF16, 4, 0, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL
+    assert f(A, BF16, 4, 1 << 24, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL  # K too large
     assert f(A, BF16, -1, 64, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL
     assert f(A, BF16, 4, 64, A, A, None, DYN8, 64, 10, A, None) == qb.QB_EINVAL   # 4-bit codes only
     assert f(A, 9, 4, 64, A, A, None, NF4, 64, 10, A, None) == qb.QB_EINVAL
