@@ -17,7 +17,10 @@
 // range; a workgroup finds its tensor from a coarse bucket index (the tensor
 // holding the bucket's first tile) and, only where a bucket spans several
 // tensors, a binary search among those (uniform, scalar loads that stay in
-// the scalar cache).
+// the scalar cache).  Parameters are binary32, or 16-bit (widened on load,
+// rounded once to nearest even on store).  The layer-wise kinds LAMB and
+// LARS need each tensor's norms before any parameter moves: a norm pass
+// (k_trust_norms, k_trust_scalars) precedes their step.
 #include "qb_device.h"
 #include "qb_launch.h"
 

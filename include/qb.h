@@ -1,7 +1,8 @@
 /*
  * qb.h -- C ABI of libqb: block-wise dynamic quantization, nested quantization
- * of the block constants, and the fused 8-bit AdamW step, for AMD Instinct
- * MI355X (gfx950).
+ * of the block constants, the fused 8-bit AdamW step and its sibling 8-bit
+ * optimizers (with paged states), user codes, and the product of a 4-bit
+ * layer, for AMD Instinct MI355X (gfx950).
  *
  * The method: a tensor is cut into blocks of `blocksize` consecutive elements;
  * every block is scaled by its own absolute maximum and each scaled value is
