@@ -416,6 +416,52 @@ def bench_codes(torch, qb, inputs, dev, args):
     print(json.dumps(out), flush=True)
 
 
+def roundtrip_error_stats(torch, x, y, block):
+    """Per-block max and mean |x - y| of a round trip, summarised over the
+    blocks (max, mean, p99), absolute and relative to the block's absmax."""
+    nb = x.numel() // block
+    e = (x[:nb * block] - y[:nb * block]).abs().view(nb, block)
+    a = x[:nb * block].abs().view(nb, block).amax(1)
+    bmax, bmean = e.amax(1), e.mean(1, dtype=torch.float64)
+    ok = a > 0
+    rmax = (bmax[ok].double() / a[ok].double())
+    rmean = (bmean[ok] / a[ok].double())
+
+    def summary(t):
+        t = t.double()
+        k = max(1, int(round(0.99 * t.numel())))
+        return {"max": t.max().item(), "mean": t.mean().item(), "p99": t.kthvalue(k).values.item()}
+
+    return {"blocks": nb, "block_max_abs_err": summary(bmax), "block_mean_abs_err": summary(bmean),
+            "block_max_rel_err": summary(rmax), "block_mean_rel_err": summary(rmean)}
+
+
+def bench_roundtrip8(torch, qb, inputs, dev, args):
+    """Dynamic 8-bit quantize + fp32 dequantize of 268,435,456 values
+    ~0.02 * Student-t(3) at block sizes 256, 2048 and 4096: kernel times
+    (HIP events), codes/s and GB/s, and the distribution over blocks of the
+    per-block max and mean |x - x_hat|."""
+    n = Q8_N
+    x = inputs.student_t3(n, 0.02, seed=args.seed * 31 + 2, device=dev)
+    codes = torch.empty(n, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    out = {"workload": "268,435,456 fp32 values ~0.02 * Student-t(3), dynamic 8-bit code, quantize + fp32 dequantize",
+           "n": n, "blocks": []}
+    for B in (256, 2048, 4096):
+        absmax = torch.empty(n // B, device=dev)
+        tq = time_calls(torch, lambda: qb.qb_quantize(x, n, qb.QB_DYN8, B, codes, absmax), reps=args.steps)
+        td = time_calls(torch, lambda: qb.qb_dequantize(codes, absmax, None, qb.QB_DYN8, B, n, y), reps=args.steps)
+        nbytes = n * q8_bytes_per_elem(B)                      # one pass: 4 + 1 + 4/B bytes per element
+        torch.cuda.synchronize()
+        out["blocks"].append({"B": B, "quantize_ms": tq, "dequantize_ms": td, "codes_per_s": n / tq * 1e3,
+                              "quantize_GB/s": nbytes / tq / 1e6, "dequantize_GB/s": nbytes / td / 1e6,
+                              "quantize_frac_of_hbm_peak": nbytes / tq / 1e6 / HBM_PEAK_GBS,
+                              "dequantize_frac_of_hbm_peak": nbytes / td / 1e6 / HBM_PEAK_GBS,
+                              **roundtrip_error_stats(torch, x, y, B)})
+        log(f"B={B}: quantize {tq:.3f} ms, dequantize {td:.3f} ms")
+    print(json.dumps(out), flush=True)
+
+
 MM_SHAPES = [(4096, 4096), (11008, 4096), (4096, 11008)]      # (N, K) of the 7B projections
 MM_ROWS = [1, 16, 64, 256, 4096]
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -502,6 +548,8 @@ def main():
                     help="state width of the --flat run (32: the binary32 fallback of small or chosen tensors)")
     ap.add_argument("--codes", action="store_true",
                     help="time the user-code calls (quantile estimation, quantile and linear codes) instead")
+    ap.add_argument("--roundtrip8", action="store_true",
+                    help="time the dynamic 8-bit round trip at B = 256, 2048, 4096 and report per-block errors")
     ap.add_argument("--matmul", action="store_true",
                     help="time the fused 4-bit dequantize + product on the 7B projection shapes instead")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -529,6 +577,8 @@ def main():
         return bench_codes(torch, qb, inputs, dev, args)
     if args.matmul:
         return bench_matmul(torch, qb, inputs, dev, args)
+    if args.roundtrip8:
+        return bench_roundtrip8(torch, qb, inputs, dev, args)
     model = Model7B(torch, qb, inputs, dev, args.seed, with_w4=not args.adam_only)
     torch.cuda.synchronize()
     log(f"setup done; warmup {args.warmup} steps")
@@ -585,7 +635,8 @@ def main():
         comps["roundtrip8_dyn8_fp32"] = {"ms": q8_ms, "GB/s": q8_bytes / q8_ms / 1e6,
                                          "frac_of_hbm_peak": q8_bytes / q8_ms / 1e6 / HBM_PEAK_GBS,
                                          "elements_per_s": Q8_N / q8_ms * 1e3, "launches_per_step": 2,
-                                         "call": "qb_quantize + qb_dequantize"}
+                                         "call": "qb_quantize + qb_dequantize",
+                                         "error": roundtrip_error_stats(torch, model.q8[0], model.q8[3], Q8_BLOCK)}
         step_bytes += q4_bytes + d4_bytes + q8_bytes
     ms_per_step = wall / args.steps * 1e3
     if not args.adam_only:
