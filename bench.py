@@ -215,6 +215,18 @@ def time_back_to_back(torch, fn, reps=20):
     return a.elapsed_time(b) / reps
 
 
+def host_cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(torch, model, seconds_target, rng):
     """The oracle, single-threaded, on a bounded sample of the same workload:
     seeded full AdamW blocks of the 7B model (copied from the device), one
@@ -275,6 +287,7 @@ def cpu_baseline(torch, model, seconds_target, rng):
         "adamw_params_per_s": n_adam / t_adam,
         "dequant4_GBps": n4 * w4_bytes_per_weight() / t_d4 / 1e9,
         "host_cpus": os.cpu_count(),
+        "host_cpu_model": host_cpu_model(),
     }
 
 
