@@ -148,3 +148,20 @@ def test_zero_layers_and_repeatability(name):
         runs.append([host_bits(a) for a in layers[0].d if a is not None])
     for a, b in zip(*runs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", list(KINDS))
+def test_many_small_layers(name):
+    """300 layers of 0 to 5,000 elements in one call: the coarse index of the
+    tile and group maps spans many tensors per bucket; every layer against its
+    own oracle call."""
+    kind, hp, exact_p = KINDS[name]
+    L = qb()
+    rng = np.random.default_rng(77)
+    sizes = [int(v) for v in rng.integers(0, 5000, 300)]
+    sizes[::37] = [0] * len(sizes[::37])
+    layers = [Layer(kind, n, 256, 1000 + i, scale=float(rng.uniform(0.005, 0.5))) for i, n in enumerate(sizes)]
+    for step in range(1, 3):
+        step_all(L, kind, hp, layers, step, oracle.BF16, 256, 3000)
+        for i, l in enumerate(layers):
+            l.check(exact_p, f"{name} step {step} layer {i}")
