@@ -32,10 +32,17 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-// Steps of a wave whose loads are in flight ahead of its computation.
-// Measured on MI355X (kernel trace, 7B projection shapes, M = 1 .. 64): 2
-// beats 4 by up to 25% on the 11008-row layer (fewer registers: two
-// workgroups per CU) and ties elsewhere.
+// Steps of a wave whose loads are issued ahead of its computation.  Some of
+// them are skipped on some paths (a step past the end, a row past M), so the
+// compiler cannot count the loads in flight and waits for all of them before
+// each step: the steps arrive in batches, not as a pipeline.  Measured on
+// MI355X (kernel trace, 7B projection shapes, M = 1 .. 64): 2 beats 4 by up
+// to 25% on the 11008-row layer (fewer registers: two workgroups per CU) and
+// ties elsewhere.  A version with exact waits (every path issuing the same
+// loads, rows past M read as bounds-checked buffer loads) at depths 2 to 6
+// measured within 10% at M <= 16 and up to 15% slower at M >= 64: at these
+// sizes the launch, the first HBM round trip and the dequantize instructions
+// bound the kernel, not the depth.
 #ifndef QB_MM_DEPTH
 #define QB_MM_DEPTH 2
 #endif
@@ -219,9 +226,9 @@ __global__ __launch_bounds__(kMmThreads) void k_dq4_matmul(const void* __restric
         x_off[t] = (uint32_t)(((16 * t + r) * K + 32 * g) * ES);
     }
 
-    // Software pipeline: the loads of a wave's next PD steps (codes, block
-    // constants, and with one m-tile the activations too) are in flight while
-    // it computes the current step.
+    // The loads of a wave's next PD steps (codes, block constants, and with
+    // one m-tile the activations too) are issued ahead of the current step's
+    // computation.
     constexpr bool PX = MT == 1;
     constexpr int PD = (XDT == DT_F32 && PX) ? 2 : QB_MM_DEPTH;
     struct Pre {
