@@ -89,8 +89,9 @@ def check(y_bits, x, xdt, codes, scale, code, B, N, what):
     return exact
 
 
+# M picks the kernel's m-tiles per workgroup (1 up to 16 rows, 2 up to 32, else 4); K a multiple of 128 or not
 SHAPES = [(1, 4096, 300), (16, 512, 64), (37, 4096, 100), (64, 256, 48), (65, 1024, 33), (3, 32, 17),
-          (16, 160, 40), (130, 96, 16)]
+          (16, 160, 40), (130, 96, 16), (17, 1024, 40), (32, 160, 24), (29, 4096, 33)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
