@@ -19,9 +19,9 @@ import numpy as np
 
 from . import build as _build
 
-DYN8, NF4, FP4 = 0, 1, 2
+DYN8, NF4, FP4, UDYN8 = 0, 1, 2, 3
 F32, F16, BF16 = 0, 1, 2
-CODE_SIZE = {DYN8: 256, NF4: 16, FP4: 16}
+CODE_SIZE = {DYN8: 256, NF4: 16, FP4: 16, UDYN8: 256}
 
 _lib = None
 
@@ -35,6 +35,7 @@ def lib():
         i64, i32, vp, fp, dp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_double
         sig = {
             "orc_dyn8_codebook": [vp],
+            "orc_udyn8_codebook": [vp],
             "orc_nf4_codebook": [vp],
             "orc_fp4_codebook": [vp],
             "orc_encode": [i32, vp, i64, vp],
@@ -51,7 +52,7 @@ def lib():
             "orc_quantize_custom": [vp, i32, i64, vp, i32, vp, vp],
             "orc_dequantize_custom": [vp, vp, vp, i32, i64, vp, i32],
             "orc_estimate_quantiles": [vp, i32, i64, i32, vp],
-            "orc_optim8bit_step": [i32, vp, i32, vp, vp, i32, i64, vp, vp, vp, vp, i32],
+            "orc_optim8bit_step": [i32, vp, i32, vp, vp, i32, i64, vp, vp, vp, vp, i32, i32],
         }
         for name, argtypes in sig.items():
             f = getattr(L, name)
@@ -89,9 +90,10 @@ def _check(rc, what):
 # --------------------------------------------------------------------------
 
 def codebook(code):
-    """Decode table indexed by the stored code (DYN8: 256, NF4/FP4: 16 entries)."""
+    """Decode table indexed by the stored code (DYN8, UDYN8: 256, NF4/FP4: 16 entries)."""
     out = np.zeros(CODE_SIZE[code], dtype=np.float32)
-    fn = {DYN8: lib().orc_dyn8_codebook, NF4: lib().orc_nf4_codebook, FP4: lib().orc_fp4_codebook}[code]
+    fn = {DYN8: lib().orc_dyn8_codebook, NF4: lib().orc_nf4_codebook, FP4: lib().orc_fp4_codebook,
+          UDYN8: lib().orc_udyn8_codebook}[code]
     _check(fn(_p(out)), "codebook")
     return out
 
@@ -384,9 +386,12 @@ def optim32_step(kind, p, g, x1, x2=None, step=1, gdt=None, pdt=F32, **hp):
                                       _p(x2) if x2 is not None else None), "optim32")
 
 
-def optim8bit_step(kind, p, g, c1, a1, c2=None, a2=None, blocksize=2048, step=1, gdt=None, pdt=F32, **hp):
+def optim8bit_step(kind, p, g, c1, a1, c2=None, a2=None, blocksize=2048, step=1, gdt=None, pdt=F32, vcode=DYN8,
+                   **hp):
     """In-place 8-bit step of optimizer `kind`: states as dynamic 8-bit codes
-    c1 (and c2) with block absmax a1 (and a2); pdt as for optim32_step."""
+    c1 (and c2) with block absmax a1 (and a2); pdt as for optim32_step.  vcode:
+    the code of the never-negative state (v of the two-state kinds, the state
+    of RMSprop), DYN8 or UDYN8."""
     two = OPTIMIZER_STATES[kind] == 2
     arrs = [(p, np.float32 if pdt == F32 else np.uint16), (c1, np.uint8), (a1, np.float32)]
     arrs += [(c2, np.uint8), (a2, np.float32)] if two else []
@@ -399,7 +404,8 @@ def optim8bit_step(kind, p, g, c1, a1, c2=None, a2=None, blocksize=2048, step=1,
     h = _optim_hp(**hp)
     with _Params16(p, pdt) as pw:
         _check(lib().orc_optim8bit_step(kind, _p(h), step, _p(pw), _p(g), gdt, pw.size, _p(c1),
-                                        _p(c2) if two else None, _p(a1), _p(a2) if two else None, blocksize),
+                                        _p(c2) if two else None, _p(a1), _p(a2) if two else None, blocksize,
+                                        vcode),
                "optim8bit")
 
 

@@ -40,7 +40,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_DYN8 = 0, ORC_NF4 = 1, ORC_FP4 = 2 };
+enum { ORC_DYN8 = 0, ORC_NF4 = 1, ORC_FP4 = 2, ORC_UDYN8 = 3 };
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
 
 /* ------------------------------------------------------------------------ */
@@ -186,6 +186,39 @@ int orc_dyn8_codebook(float* out /* [256] */)
     return 0;
 }
 
+/*
+ * Unsigned dynamic 8-bit code, for a state that is never negative (v of Adam
+ * and AdamW, the state of RMSprop).  Reading: the pages name only the signed
+ * dynamic code; its plainest unsigned form spends the sign bit on one more
+ * fraction bit, so each of the same seven decades holds twice as many linearly
+ * spaced magnitudes, the midpoints of 2^(e+1) equal bins that split [0.1, 1],
+ * scaled by 10^(e-6):
+ *     u(e, j) = 10^(e-6) * (0.1 + 0.9 * (j + 1/2) / 2^(e+1)),   j = 0 .. 2^(e+1) - 1.
+ * That gives 254 magnitudes; the code is 0, the magnitudes and +1.0, ascending
+ * (index 0 is 0.0 and 255 is +1.0).  Each value is the exact rational
+ *     u(e, j) = (2^(e+2) + 18 j + 9) / (2^(e+2) * 10^(7-e))
+ * rounded once to binary32.
+ */
+int orc_udyn8_codebook(float* out /* [256] */)
+{
+    int n = 0;
+    out[n++] = 0.0f;
+    for (int e = 0; e <= 6; e++) {
+        int64_t pow10 = 1;
+        for (int k = 0; k < 7 - e; k++) pow10 *= 10;
+        for (int j = 0; j < (2 << e); j++) {
+            double num = (double)((4 << e) + 18 * j + 9);            /* exact integer */
+            double den = (double)((int64_t)(4 << e) * pow10);        /* exact integer < 2^53 */
+            float f;
+            if (round_to_f32_checked(num / den, &f) != 0) return -1;
+            out[n++] = f;
+        }
+    }
+    out[n++] = 1.0f;                                   /* n == 256 */
+    qsort(out, 256, sizeof(float), cmp_float);         /* already ascending */
+    return 0;
+}
+
 /* Standard normal CDF from the complementary error function (libm, long double). */
 static long double norm_cdf(long double x) { return 0.5L * erfcl(-x / sqrtl(2.0L)); }
 
@@ -251,6 +284,7 @@ int orc_fp4_codebook(float* out /* [16], indexed by code */)
 static int sorted_table(int code, float* t)
 {
     if (code == ORC_DYN8) { orc_dyn8_codebook(t); return 256; }
+    if (code == ORC_UDYN8) { orc_udyn8_codebook(t); return 256; }
     if (code == ORC_NF4) { orc_nf4_codebook(t); return 16; }
     float f4[16];
     orc_fp4_codebook(f4);
@@ -352,6 +386,7 @@ int orc_quantize_blockwise(const void* x, int xdt, int64_t n, int code, int B,
 static void decode_table(int code, float* t)
 {
     if (code == ORC_DYN8) orc_dyn8_codebook(t);
+    else if (code == ORC_UDYN8) orc_udyn8_codebook(t);
     else if (code == ORC_NF4) orc_nf4_codebook(t);
     else orc_fp4_codebook(t);
 }
@@ -750,13 +785,19 @@ int orc_optim32_step(int kind, const double* hp, int step, float* p, const void*
 /*
  * Any kind with block-wise dynamic 8-bit states (c1/a1, and c2/a2 for the
  * two-state kinds; NULL otherwise): per block, decode the states, update every
- * element, take each state's new block absmax, encode again.
+ * element, take each state's new block absmax, encode again.  vcode is the
+ * code of the state that is never negative (v of the two-state kinds, the
+ * state of RMSprop): ORC_DYN8, or ORC_UDYN8 (the unsigned code above); every
+ * other state takes ORC_DYN8.  A kind with no such state must pass ORC_DYN8.
  */
 int orc_optim8bit_step(int kind, const double* hp, int step, float* p, const void* g, int gdt, int64_t n,
-                       uint8_t* c1, uint8_t* c2, float* a1, float* a2, int B)
+                       uint8_t* c1, uint8_t* c2, float* a1, float* a2, int B, int vcode)
 {
     if (optim_check(kind, hp, step) != 0) return -1;
     const int two = optim_states(kind) == 2;
+    if (vcode != ORC_DYN8 && vcode != ORC_UDYN8) return -1;
+    if (vcode == ORC_UDYN8 && !two && kind != ORC_RMSPROP) return -1;
+    const int code1 = kind == ORC_RMSPROP ? vcode : ORC_DYN8, code2 = vcode;
     optim_scalars s = optim_prepare(kind, hp, step);
     if (is_layerwise(kind)) {
         /* the norms span the whole tensor: decode every block, take the
@@ -766,18 +807,19 @@ int orc_optim8bit_step(int kind, const double* hp, int step, float* p, const voi
         float* y = (float*)malloc(bytes);
         int rc = -1;
         if (x && y) {
-            orc_dequantize_blockwise(c1, a1, ORC_DYN8, B, n, x, ORC_F32);
-            if (two) orc_dequantize_blockwise(c2, a2, ORC_DYN8, B, n, y, ORC_F32);
+            orc_dequantize_blockwise(c1, a1, code1, B, n, x, ORC_F32);
+            if (two) orc_dequantize_blockwise(c2, a2, code2, B, n, y, ORC_F32);
             rc = layerwise32(kind, hp, &s, p, g, gdt, n, x, two ? y : NULL);
-            if (rc == 0) rc = orc_quantize_blockwise(x, ORC_F32, n, ORC_DYN8, B, c1, a1);
-            if (rc == 0 && two) rc = orc_quantize_blockwise(y, ORC_F32, n, ORC_DYN8, B, c2, a2);
+            if (rc == 0) rc = orc_quantize_blockwise(x, ORC_F32, n, code1, B, c1, a1);
+            if (rc == 0 && two) rc = orc_quantize_blockwise(y, ORC_F32, n, code2, B, c2, a2);
         }
         free(x);
         free(y);
         return rc;
     }
-    float cb[256];
-    orc_dyn8_codebook(cb);
+    float cb1[256], cb2[256];
+    decode_table(code1, cb1);
+    decode_table(code2, cb2);
     float* xb = (float*)malloc(sizeof(float) * (size_t)B);
     float* yb = (float*)malloc(sizeof(float) * (size_t)B);
     if (!xb || !yb) { free(xb); free(yb); return -1; }
@@ -786,8 +828,8 @@ int orc_optim8bit_step(int kind, const double* hp, int step, float* p, const voi
         int64_t lo = b * B, hi = lo + B < n ? lo + B : n;
         float m1 = 0.0f, m2 = 0.0f;
         for (int64_t i = lo; i < hi; i++) {
-            float x = cb[c1[i]] * a1[b];
-            float y = two ? cb[c2[i]] * a2[b] : 0.0f;
+            float x = cb1[c1[i]] * a1[b];
+            float y = two ? cb2[c2[i]] * a2[b] : 0.0f;
             optim_elem(&s, load_elem(g, gdt, i), &p[i], &x, &y);
             xb[i - lo] = x;
             yb[i - lo] = y;
@@ -797,8 +839,8 @@ int orc_optim8bit_step(int kind, const double* hp, int step, float* p, const voi
         a1[b] = m1;
         if (two) a2[b] = m2;
         for (int64_t i = lo; i < hi; i++) {
-            c1[i] = (uint8_t)nearest_index(cb, 256, m1 > 0.0f ? xb[i - lo] / m1 : 0.0f);
-            if (two) c2[i] = (uint8_t)nearest_index(cb, 256, m2 > 0.0f ? yb[i - lo] / m2 : 0.0f);
+            c1[i] = (uint8_t)nearest_index(cb1, 256, m1 > 0.0f ? xb[i - lo] / m1 : 0.0f);
+            if (two) c2[i] = (uint8_t)nearest_index(cb2, 256, m2 > 0.0f ? yb[i - lo] / m2 : 0.0f);
         }
     }
     free(xb);
