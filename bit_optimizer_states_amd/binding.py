@@ -16,7 +16,7 @@ LIB_PATH = os.environ.get("QB_LIBRARY") or os.path.join(_HERE, "libqb.so")
 
 QB_OK, QB_EINVAL, QB_EALIGN, QB_EUNSUPPORTED, QB_EHIP, QB_EWORKSPACE, QB_EINIT = range(7)
 QB_F32, QB_F16, QB_BF16 = 0, 1, 2
-QB_DYN8, QB_NF4, QB_FP4 = 0, 1, 2
+QB_DYN8, QB_NF4, QB_FP4, QB_UDYN8 = 0, 1, 2, 3
 QB_ADAMW, QB_ADAM, QB_LION, QB_SGD, QB_RMSPROP, QB_LAMB, QB_LARS = range(7)
 
 _DTYPE = {torch.float32: QB_F32, torch.float16: QB_F16, torch.bfloat16: QB_BF16}
@@ -42,7 +42,7 @@ class qb_optim_hparams(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("lr", ctypes.c_double), ("beta1", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
                 ("dampening", ctypes.c_double), ("nesterov", ctypes.c_int32), ("step", ctypes.c_int32),
-                ("trust_coefficient", ctypes.c_double)]
+                ("trust_coefficient", ctypes.c_double), ("v_code", ctypes.c_int)]
 
 
 class qb_tensor(ctypes.Structure):
@@ -216,9 +216,10 @@ def qb_dequant_matmul(x, codes, absmax, code, blocksize, N, y, dq=None, stream=N
 
 
 def optim_hparams(kind, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, dampening=0.0, nesterov=False,
-                  step=1, trust_coefficient=0.0):
+                  step=1, trust_coefficient=0.0, v_code=QB_DYN8):
+    """v_code: the code of the never-negative state (QB_DYN8 or QB_UDYN8)."""
     return qb_optim_hparams(int(kind), lr, beta1, beta2, eps, weight_decay, dampening, 1 if nesterov else 0,
-                            int(step), trust_coefficient)
+                            int(step), trust_coefficient, int(v_code))
 
 
 def qb_optimizer8bit_step(hp, p, g, n, state1, state2, absmax1, absmax2, blocksize, stream=None):

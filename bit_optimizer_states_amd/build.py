@@ -15,8 +15,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqb.so")
-SOURCES = ["qb_tables.cpp", "qb_api.cpp", "qb_runtime.hip", "qb_quant.hip", "qb_dequant.hip", "qb_optim.hip", "qb_codes.hip",
-           "qb_matmul.hip"]
+# the two optimizer sources first: they take longest, and compile in parallel
+SOURCES = ["qb_optim.hip", "qb_optim_uv.hip", "qb_tables.cpp", "qb_api.cpp", "qb_runtime.hip", "qb_quant.hip",
+           "qb_dequant.hip", "qb_codes.hip", "qb_matmul.hip"]
 ARCH = os.environ.get("QB_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",

@@ -52,10 +52,15 @@ bool finite(double v) { return std::isfinite(v); }
 bool unit(double v) { return v >= 0 && v < 1; }    // [0, 1)
 
 // Hyperparameter checks per optimizer kind (the ranges their definitions need).
+// The kinds with a never-negative state (v; RMSprop's one state), which may
+// hold it in QB_UDYN8.
+bool has_nonneg_state(qb_optimizer k) { return k == QB_ADAMW || k == QB_ADAM || k == QB_LAMB || k == QB_RMSPROP; }
+
 bool valid_optim(const qb_optim_hparams* hp)
 {
     if (!hp || hp->step < 1 || !finite(hp->lr) || hp->lr < 0 || !finite(hp->weight_decay) || hp->weight_decay < 0)
         return false;
+    if (hp->v_code != QB_DYN8 && !(hp->v_code == QB_UDYN8 && has_nonneg_state(hp->kind))) return false;
     switch (hp->kind) {
     case QB_ADAMW:
     case QB_ADAM: return unit(hp->beta1) && unit(hp->beta2) && finite(hp->eps) && hp->eps > 0;
@@ -372,9 +377,9 @@ size_t qb_multi_tensor_workspace_bytes(int32_t count)
 int32_t qb_codebook(qb_code code, float* out)
 {
     const QbTables* t = host_tables();
-    if (!t || !out || !valid_code(code)) return -1;
-    if (code == QB_DYN8) {
-        std::memcpy(out, t->dyn8, sizeof(t->dyn8));
+    if (!t || !out || !(valid_code(code) || code == QB_UDYN8)) return -1;
+    if (code == QB_DYN8 || code == QB_UDYN8) {
+        std::memcpy(out, code == QB_DYN8 ? t->dyn8 : t->udyn8, sizeof(t->dyn8));
         return 256;
     }
     std::memcpy(out, code == QB_NF4 ? t->nf4 : t->fp4, 16 * sizeof(float));
@@ -384,7 +389,15 @@ int32_t qb_codebook(qb_code code, float* out)
 int32_t qb_encoder_table(qb_code code, uint32_t* out, int32_t capacity)
 {
     const QbTables* t = host_tables();
-    if (!t || !valid_code(code) || capacity < 0 || (capacity > 0 && !out)) return -1;
+    if (!t || !(valid_code(code) || code == QB_UDYN8) || capacity < 0 || (capacity > 0 && !out)) return -1;
+    if (code == QB_UDYN8) {
+        for (int32_t i = 0; i < kUDynLutN && i < capacity; ++i) {
+            const int c = t->udyn8_base[i];
+            out[2 * i] = t->udyn8_thr[c];
+            out[2 * i + 1] = (uint32_t)c;
+        }
+        return kUDynLutN;
+    }
     if (code == QB_DYN8) {
         for (int32_t i = 0; i < 2 * kDynLutN && i < capacity; ++i) {
             const int c = t->dyn8_base[i / kDynLutN][i % kDynLutN];
@@ -691,7 +704,8 @@ qb_status qb_optimizer8bit_step(const qb_optim_hparams* hp, void* p, qb_dtype pd
     if (!device_tables()) return QB_EINIT;
     TensorDesc d{p, g, state1, state2, absmax1, absmax2, n, 0};
     return hip_status(launch_optim8((int)hp->kind, d, nullptr, adamw_tiles(n, blocksize), blocksize, (int)pdt,
-                                    (int)gdt, prepare(*hp), nullptr, static_cast<hipStream_t>(stream)));
+                                    (int)gdt, prepare(*hp), nullptr, hp->v_code == QB_UDYN8,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 size_t qb_optimizer_workspace_bytes(const qb_optim_hparams* hp, const qb_tensor* tensors, int32_t count,
@@ -759,19 +773,21 @@ qb_status qb_multi_tensor_optimizer_step(const qb_optim_hparams* hp, const qb_te
         stage_tile_map(staging, map_region_bytes(count), gtable, groups, count, ws, &gmap);
         qb_status st = copy_staging(staging, ws, s);
         if (st != QB_OK) return st;
-        hipError_t e = launch_trust_norms((int)hp->kind, gmap, groups, blocksize, (int)pdt, (int)gdt, hs, part, s);
+        const bool uv = hp->v_code == QB_UDYN8;
+        hipError_t e = launch_trust_norms((int)hp->kind, gmap, groups, blocksize, (int)pdt, (int)gdt, hs, part, uv, s);
         if (e == hipSuccess)
             e = launch_trust_scalars((int)hp->kind, gmap, part, hp->lr, hp->weight_decay, hp->trust_coefficient,
                                      trust, s);
         if (e == hipSuccess)
-            e = launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)pdt, (int)gdt, hs, trust, s);
+            e = launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)pdt, (int)gdt, hs, trust, uv, s);
         return hip_status(e);
     }
     stage_tile_map(staging, 0, table, tiles, count, ws, &map);
     qb_status st = copy_staging(staging, ws, s);
     if (st != QB_OK) return st;
     return hip_status(
-        launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)pdt, (int)gdt, hs, nullptr, s));
+        launch_optim8((int)hp->kind, table[0], &map, tiles, blocksize, (int)pdt, (int)gdt, hs, nullptr,
+                      hp->v_code == QB_UDYN8, s));
 }
 
 qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, uint8_t* m, uint8_t* v,
@@ -863,7 +879,7 @@ qb_status qb_paged_optimizer_step(const qb_optim_hparams* hp, const qb_tensor* t
             TensorDesc d{static_cast<char*>(t.p) + off * ps, static_cast<const char*>(t.g) + off * gs, m,
                          two ? v : nullptr, am, two ? av : nullptr, n, 0};
             hipError_t e = launch_optim8((int)hp->kind, d, nullptr, adamw_tiles(n, blocksize), blocksize, (int)pdt,
-                                         (int)gdt, hs, nullptr, s);
+                                         (int)gdt, hs, nullptr, hp->v_code == QB_UDYN8, s);
             if (e != hipSuccess) return hip_status(e);
             // device to host after the step
             ok = ck(hipEventRecord(r->kern[slot], s)) && ck(hipStreamWaitEvent(r->d2h, r->kern[slot], 0)) &&

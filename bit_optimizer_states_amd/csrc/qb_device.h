@@ -413,6 +413,36 @@ __device__ __forceinline__ uint32_t enc_dyn8_pos(float nv, const DynEncLds& s)
     return c + (nv >= s.thr[c] ? 1u : 0u);
 }
 
+// LDS copy of the unsigned dynamic-code encoder (n >= 0): the code at the start
+// of each bucket of n (bits of the clamped n >> 16), and the 255 thresholds.
+struct UDynEncLds {
+    uint8_t base[kUDynBucketBytes];
+    float thr[256];
+};
+
+// Stage the unsigned encoder tables (about 3.9 KB) into LDS with NT threads.
+template <int NT = kThreads>
+__device__ __forceinline__ void stage_udyn_enc(UDynEncLds& s, const QbTables* __restrict__ tab, int tid)
+{
+    constexpr int W = kUDynBucketBytes / 4;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tab->udyn8_base);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(s.base);
+#pragma unroll
+    for (int r = 0; r < (W + NT - 1) / NT; ++r)
+        if ((r + 1) * NT <= W || r * NT + tid < W) dst[r * NT + tid] = src[r * NT + tid];
+#pragma unroll
+    for (int r = 0; r < (256 + NT - 1) / NT; ++r)
+        if (NT <= 256 || tid < 256) s.thr[r * NT + tid] = __uint_as_float(tab->udyn8_thr[r * NT + tid]);
+}
+
+// Unsigned dynamic 8-bit code of a normalized value in [0, 1].
+__device__ __forceinline__ uint32_t enc_udyn8(float nv, const UDynEncLds& s)
+{
+    const float cl = __builtin_amdgcn_fmed3f(nv, 0x1p-23f, 1.0f);
+    const uint32_t c = s.base[(fbits(cl) >> kUDynShift) - kUDynBase];
+    return c + (nv >= s.thr[c] ? 1u : 0u);
+}
+
 // 8-bit code of a user code: the number of thresholds <= nv, by a branchless
 // binary search over the 255 ascending thresholds (thr[255] = +inf is never
 // read).

@@ -218,8 +218,10 @@ constexpr int64_t dequant_tile_elems(int bits, bool multi)
 // trust: the per-tensor step scalars S of the layer-wise kinds (indexed like
 // map->descs), nullptr for the others.
 // pdt: the parameters' dtype (binary32, or a 16-bit type equal to gdt).
+// uv: the never-negative state (v of AdamW, Adam and LAMB; RMSprop's state)
+// is held in the unsigned dynamic code (only those kinds).
 hipError_t launch_optim8(int opt, const TensorDesc& single, const TileMap<TensorDesc>* map, int64_t ntiles, int B,
-                         int pdt, int gdt, const OptScalars& hs, const float* trust, hipStream_t s);
+                         int pdt, int gdt, const OptScalars& hs, const float* trust, bool uv, hipStream_t s);
 
 // Layer-wise kinds, before launch_optim8: per group of kNormGroupTiles
 // consecutive optimizer tiles of one tensor (gmap: the tensors with
@@ -229,7 +231,7 @@ hipError_t launch_optim8(int opt, const TensorDesc& single, const TileMap<Tensor
 // in a fixed order and writes trust[tensor] = (float)(lr * ratio).
 constexpr int64_t kNormGroupTiles = 32;
 hipError_t launch_trust_norms(int opt, const TileMap<TensorDesc>& gmap, int64_t ngroups, int B, int pdt, int gdt,
-                              const OptScalars& hs, double* part, hipStream_t s);
+                              const OptScalars& hs, double* part, bool uv, hipStream_t s);
 hipError_t launch_trust_scalars(int opt, const TileMap<TensorDesc>& gmap, const double* part, double lr,
                                 double weight_decay, double trust_coefficient, float* trust, hipStream_t s);
 

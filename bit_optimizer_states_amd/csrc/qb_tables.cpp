@@ -7,6 +7,11 @@
 //    decades e = 0..6, the 2^e midpoints of equal bins of [0.1, 1] scaled by
 //    10^(e-6), i.e. (2^(e+1) + 18j + 9) / (2^(e+1) 10^(7-e)), their negatives,
 //    0 and +1, sorted (256 entries);
+//  * unsigned dynamic 8-bit code, for a state that is never negative (same
+//    abstract; the pages name only the signed code): the sign bit becomes one
+//    more fraction bit, so decade e holds the 2^(e+1) midpoints of equal bins
+//    of [0.1, 1] scaled by 10^(e-6), i.e. (2^(e+2) + 18j + 9) /
+//    (2^(e+2) 10^(7-e)), plus 0 and +1 (256 entries);
 //  * NF4 ("Bitsandbytes", section Normal Float 4 (NF4)): quantiles of N(0,1)
 //    at 1/2 + (P-1/2)k/8 (k = 1..8) and their mirrored counterparts at k/7
 //    (k = 1..7), plus 0, over the quantile at P = 1 - (1/30 + 1/32)/2;
@@ -66,6 +71,21 @@ void build_dyn8(float* out)
     for (int i = 0; i < 127; ++i) out[i] = -pos[126 - i];
     out[127] = 0.0f;
     for (int i = 0; i < 127; ++i) out[128 + i] = pos[i];
+    out[255] = 1.0f;
+}
+
+void build_udyn8(float* out)
+{
+    std::vector<float> pos;
+    for (int e = 0; e <= 6; ++e) {
+        uint64_t p10 = 1;
+        for (int k = 0; k < 7 - e; ++k) p10 *= 10;
+        for (int j = 0; j < (2 << e); ++j)
+            pos.push_back(rn32_ratio((4ull << e) + 18ull * j + 9ull, (4ull << e) * p10));
+    }
+    std::sort(pos.begin(), pos.end());
+    out[0] = 0.0f;
+    for (int i = 0; i < 254; ++i) out[1 + i] = pos[i];
     out[255] = 1.0f;
 }
 
@@ -151,6 +171,23 @@ int build_dyn8_lut(const float* dyn8, uint8_t (*base)[kDynBucketBytes], uint32_t
     return 0;
 }
 
+int build_udyn8_lut(const float* udyn8, uint8_t* base, uint32_t* thr)
+{
+    std::vector<float> vals(udyn8, udyn8 + 256);
+    std::vector<float> T = thresholds(vals);            // 255 thresholds, ascending
+    for (int c = 0; c < 256; ++c) thr[c] = c < 255 ? bits_of(T[c]) : 0x7F800000u;
+    for (int b = 0; b < kUDynLutN; ++b) {
+        // n of bucket b: [lo, hi] (bucket 0 also takes every n below 2^-23, the last only 1.0)
+        const float lo = b == 0 ? 0.0f : float_of(uint32_t(b + kUDynBase) << kUDynShift);
+        const float hi = b == kUDynLutN - 1 ? 1.0f : float_of((uint32_t(b + kUDynBase + 1) << kUDynShift) - 1u);
+        int c = 0;
+        while (c < 255 && T[c] <= lo) ++c;
+        if (c + 1 < 255 && T[c + 1] <= hi) return -1;  // two thresholds in one bucket
+        base[b] = (uint8_t)c;
+    }
+    return 0;
+}
+
 int bucket4(float n)
 {
     float u = n * 16.0f + 16.0f;
@@ -215,6 +252,7 @@ int self_check(const QbTables* T)
     // a deterministic sweep of [-1, 1]: the bucket encoders against the direct search
     std::vector<float> dyn(T->dyn8, T->dyn8 + 256);
     std::vector<float> nf4(T->nf4, T->nf4 + 16);
+    std::vector<float> udyn(T->udyn8, T->udyn8 + 256);
     uint32_t state = 12345u;
     for (int i = 0; i < 200000; ++i) {
         state = state * 1664525u + 1013904223u;
@@ -230,6 +268,11 @@ int self_check(const QbTables* T)
         const LutEntry& f = T->nf4_lut[bucket4(x)];
         int c4 = (x >= float_of(f.t)) ? (int)((f.payload >> 8) & 0xFF) : (int)(f.payload & 0xFF);
         if (c4 != nearest(nf4, x)) return -11;
+        // the unsigned encoder on |x|
+        const float ax = std::fabs(x);
+        const uint32_t ucl = std::min(std::max(bits_of(ax), kUDynLowBits), kOneBits);
+        const int u0 = T->udyn8_base[(ucl >> kUDynShift) - kUDynBase];
+        if (u0 + (ax >= float_of(T->udyn8_thr[u0]) ? 1 : 0) != nearest(udyn, ax)) return -12;
     }
     return 0;
 }
@@ -245,6 +288,10 @@ int build_tables(QbTables* T)
     for (int i = 0; i < 255; ++i)
         if (!(T->dyn8[i] < T->dyn8[i + 1])) return -2;
     if (build_dyn8_lut(T->dyn8, T->dyn8_base, T->dyn8_thr) != 0) return -3;
+    build_udyn8(T->udyn8);
+    for (int i = 0; i < 255; ++i)
+        if (!(T->udyn8[i] < T->udyn8[i + 1])) return -6;
+    if (build_udyn8_lut(T->udyn8, T->udyn8_base, T->udyn8_thr) != 0) return -7;
 
     std::vector<float> nf4(T->nf4, T->nf4 + 16);
     std::vector<uint32_t> nf4_codes(16);

@@ -17,6 +17,16 @@ constexpr int kDynShift = 17;
 constexpr int kDynBase = int(kDynLowBits >> kDynShift);
 constexpr int kDynLutN = int(kOneBits >> kDynShift) - kDynBase + 1;   // 1409
 
+// Unsigned dynamic 8-bit encoder (n >= 0): buckets over the bit pattern of n,
+// 7 mantissa bits per bucket (the unsigned code is twice as dense as the
+// signed one); every n below 2^-23 shares bucket 0 (the smallest decision
+// threshold is 1.625e-7 > 2^-23).
+constexpr uint32_t kUDynLowBits = 104u << 23;   // 2^-23
+constexpr int kUDynShift = 16;
+constexpr int kUDynBase = int(kUDynLowBits >> kUDynShift);
+constexpr int kUDynLutN = int(kOneBits >> kUDynShift) - kUDynBase + 1;   // 2945
+constexpr int kUDynBucketBytes = (kUDynLutN + 3) / 4 * 4;                 // 2948
+
 // 4-bit encoders: linear buckets of n in [-1, 1]: b = (int)(n*16 + 16).
 constexpr int k4LutN = 33;
 
@@ -42,6 +52,11 @@ struct QbTables {
     uint32_t dyn8_thr[256];
     LutEntry nf4_lut[k4LutN];
     LutEntry fp4_lut[k4LutN];
+    // unsigned dynamic code: decode, and the encoder of n >= 0 (udyn8_base[b]
+    // is the code at the start of bucket b, udyn8_thr[c] the threshold T[c])
+    float udyn8[256];
+    uint8_t udyn8_base[kUDynBucketBytes];
+    uint32_t udyn8_thr[256];
 };
 
 // Builds every table; returns 0, or a negative value if a self-check fails.

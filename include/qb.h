@@ -12,9 +12,16 @@
  * 简介、安装、使用方法之详细攻略", section 2; page "bitsandbytes深度解析",
  * section 核心量化原理与实现机制).
  *
- * Codes (QB_DYN8, QB_NF4, QB_FP4) -- see qb_codebook() for the exact tables:
+ * Codes (QB_DYN8, QB_NF4, QB_FP4, QB_UDYN8) -- see qb_codebook() for the exact
+ * tables:
  *   QB_DYN8  256-entry signed dynamic code (decimal exponent + linear fraction),
  *            one byte per element; index 127 is 0.0, 255 is +1.0.
+ *   QB_UDYN8 256-entry unsigned dynamic code for an optimizer state that is
+ *            never negative (see qb_optim_hparams.v_code): the sign bit of
+ *            QB_DYN8 spent on one more fraction bit, so each of the same seven
+ *            decades holds twice as many values; index 0 is 0.0, 255 is +1.0.
+ *            The pages name only the signed code; this is its plainest
+ *            unsigned form.
  *   QB_NF4   16 normal-quantile values in [-1, 1], two codes per byte.
  *   QB_FP4   E2M1 minifloat / 6, sign-magnitude nibble, two codes per byte.
  * 4-bit packing: element 2k is the high nibble of byte k, element 2k+1 the low
@@ -60,7 +67,7 @@ typedef enum {
 
 typedef enum { QB_F32 = 0, QB_F16 = 1, QB_BF16 = 2 } qb_dtype;
 
-typedef enum { QB_DYN8 = 0, QB_NF4 = 1, QB_FP4 = 2 } qb_code;
+typedef enum { QB_DYN8 = 0, QB_NF4 = 1, QB_FP4 = 2, QB_UDYN8 = 3 } qb_code;
 
 /*
  * Nested ("double") quantization state of the per-block absmax (page
@@ -134,6 +141,12 @@ typedef struct {
  *   binary32 scalar.  They need a workspace for the norms: only
  *   qb_multi_tensor_optimizer_step runs them (one tensor is a call with
  *   count 1).
+ * The never-negative state (v of QB_ADAMW, QB_ADAM and QB_LAMB; the state of
+ * QB_RMSPROP) may be held in QB_UDYN8 instead (hp->v_code): the same bytes,
+ * with twice the resolution in every decade, which halves its worst
+ * quantization error relative to the block absmax (0.0035 against 0.0070).
+ * Its fresh state is code 0 (0.0).  A state written with one code must be
+ * stepped with the same code.
  * The states and their codes are bit-exact against an IEEE binary32 evaluation
  * of these formulas (each operation rounded on its own, IEEE square root and
  * division).  So is p' for every kind but AdamW and LAMB, whose states never
@@ -157,6 +170,9 @@ typedef struct {
     int32_t nesterov;      /* SGD: 0 or 1 (1 needs dampening 0) */
     int32_t step;          /* t >= 1 */
     double  trust_coefficient;   /* LARS: eta > 0 */
+    qb_code v_code;        /* code of the never-negative state: QB_DYN8 (0, the
+                              default) or QB_UDYN8 (QB_ADAMW, QB_ADAM, QB_LAMB,
+                              QB_RMSPROP only) */
 } qb_optim_hparams;
 
 /* One tensor of a multi-tensor step; the fields are those of qb_adamw8bit_step
@@ -208,7 +224,8 @@ typedef struct {
  * "Bitsandbytes", section Normal Float 4 (NF4); FP4: page "Quantize 🤗
  * Transformers models", section FP4 quantization).
  *   x       [n] input of dtype xdt (fp32, fp16 or bf16).
- *   code    QB_DYN8 (codes: n bytes) or QB_NF4 / QB_FP4 (codes: ceil(n/2) bytes).
+ *   code    QB_DYN8 (codes: n bytes) or QB_NF4 / QB_FP4 (codes: ceil(n/2) bytes);
+ *           QB_UDYN8 serves only the optimizer states (QB_EINVAL here).
  *   absmax  [ceil(n/blocksize)] fp32 block absmax out; must be NULL when dq is given.
  *   dq      NULL, or the nested state to fill (codes, absmax2, offset; the
  *           workspace holds the fp32 absmax while the call runs).
@@ -343,7 +360,9 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
  * precision next to the 8-bit optimizer: "bitsandbytes - Quantização de LLM",
  * section Workflow 3).  A 16-bit parameter is widened to binary32 (exactly),
  * updated by the same binary32 formulas and rounded once, to nearest even,
- * back to its dtype; other pairs give QB_EUNSUPPORTED.  Fresh state: every code 127 (0.0), absmax 0.  Invalid
+ * back to its dtype; other pairs give QB_EUNSUPPORTED.  Fresh state: every code of 0.0 (127; 0 for a state in
+ * QB_UDYN8), absmax 0.  A v_code other than QB_DYN8 or QB_UDYN8, or QB_UDYN8 for a kind without a never-negative
+ * state, gives QB_EINVAL.  Invalid
  * hyperparameters for the kind (ranges above; lr, weight_decay >= 0) give
  * QB_EINVAL before anything is launched; the layer-wise kinds give
  * QB_EUNSUPPORTED (they run through qb_multi_tensor_optimizer_step).
@@ -462,17 +481,19 @@ size_t qb_optimizer_workspace_bytes(const qb_optim_hparams* hp, const qb_tensor*
 
 /*
  * qb_codebook -- host: copy the decode table of `code` (indexed by stored code)
- * into out (256 floats for DYN8, 16 for NF4/FP4).  Returns the entry count, or
- * -1 for a bad code or a failed table build.
+ * into out (256 floats for DYN8 and UDYN8, 16 for NF4/FP4).  Returns the entry
+ * count, or -1 for a bad code or a failed table build.
  */
 int32_t qb_codebook(qb_code code, float* out);
 
 /*
  * qb_encoder_table -- host: the encoder's bucket table, for inspection and
  * tests.  Each entry is two uint32 words {threshold bits, payload}:
- *   DYN8: bucket b = (clamp(bits(|n|), 2^-22, 1.0) >> 17) - (bits(2^-22) >> 17);
- *         the magnitude code is payload + (|n| >= threshold); a negative n maps
- *         to max(254 - code, 0).
+ *   DYN8: 2 x 1409 entries, those of n >= 0 and then those of n < 0; bucket
+ *         b = (clamp(bits(|n|), 2^-22, 1.0) >> 17) - (bits(2^-22) >> 17), plus
+ *         1409 for n < 0; the code is payload + (n >= threshold).
+ *   UDYN8: 2945 entries, n >= 0; bucket b = (clamp(bits(n), 2^-23, 1.0) >> 16)
+ *         - (bits(2^-23) >> 16); the code is payload + (n >= threshold).
  *   NF4/FP4: bucket b = (int)(n*16 + 16) in binary32 (0..32); the code is byte
  *         0 of payload if n < threshold, else byte 1.
  * Copies at most `capacity` entries (2*capacity words) into out and returns the

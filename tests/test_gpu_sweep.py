@@ -11,7 +11,8 @@ that is compiled:
 - the user-code kernels for every block size and dtype, and the quantile
   estimator for every input dtype;
 - every optimizer kind at every block size and (gradient, parameter) dtype
-  pair, one tensor and grouped (the layer-wise kinds are grouped only);
+  pair, one tensor and grouped (the layer-wise kinds are grouped only), and
+  the kinds with a never-negative state again with it in the unsigned code;
 - the fused 4-bit product for every compute dtype, absmax form, m-tile count
   and K alignment.
 
@@ -212,12 +213,20 @@ PAIRS = [(oracle.F32, oracle.F32), (oracle.F16, oracle.F32), (oracle.BF16, oracl
          (oracle.F16, oracle.F16), (oracle.BF16, oracle.BF16)]
 
 
-@pytest.mark.parametrize("name", list(KINDS))
-def test_optimizer_every_instantiation(name):
+# the kinds with a never-negative state also run with it in the unsigned code
+NONNEG = ("adamw", "adam", "rmsprop", "lamb")
+OPT_CASES = [(n, oracle.DYN8) for n in KINDS] + [(n, oracle.UDYN8) for n in NONNEG]
+
+
+@pytest.mark.parametrize("name,vcode", OPT_CASES)
+def test_optimizer_every_instantiation(name, vcode):
     kind, hp, exact = KINDS[name]
     L = qb()
     two = oracle.OPTIMIZER_STATES[kind] == 2
-    rng = np.random.default_rng(300 + kind)
+    rng = np.random.default_rng(300 + kind + 7 * vcode)
+    zero = {oracle.DYN8: 127, oracle.UDYN8: 0}
+    z1 = zero[vcode] if kind == oracle.RMSPROP else 127     # codes of 0.0 of state 1 and state 2
+    z2 = zero[vcode]
     for B in BLOCKS:
         for gdt, pdt in PAIRS:
             for multi in ((True,) if name in LAYERWISE else (False, True)):
@@ -225,14 +234,15 @@ def test_optimizer_every_instantiation(name):
                 host, dev = [], []
                 for n in sizes:
                     nb = -(-n // B)
-                    h = [host_values(n, pdt, rng, 0.02), np.full(n, 127, np.uint8), np.zeros(nb, np.float32),
-                         np.full(n, 127, np.uint8), np.zeros(nb, np.float32)]
+                    h = [host_values(n, pdt, rng, 0.02), np.full(n, z1, np.uint8), np.zeros(nb, np.float32),
+                         np.full(n, z2, np.uint8), np.zeros(nb, np.float32)]
                     host.append(h)
                     dev.append([to_device(h[0], TORCH_DT[pdt])] + [to_device(a) for a in h[1:]])
                 for step in (1, 2):
                     gs = [host_values(n, gdt, rng, 1e-3) for n in sizes]
                     gd = [to_device(g, TORCH_DT[gdt]) for g in gs]
                     h = lib_hp(kind, hp, step)
+                    h.v_code = vcode
                     if multi:
                         table = L.tensor_table([(d[0], g, d[1], d[3] if two else None, d[2], d[4] if two else None)
                                                 for d, g in zip(dev, gd)])
@@ -245,10 +255,11 @@ def test_optimizer_every_instantiation(name):
                                                 d[4] if two else None, B)
                     for hh, g in zip(host, gs):
                         oracle.optim8bit_step(kind, hh[0], g, hh[1], hh[2], hh[3] if two else None,
-                                              hh[4] if two else None, B, step=step, gdt=gdt, pdt=pdt, **hp)
+                                              hh[4] if two else None, B, step=step, gdt=gdt, pdt=pdt, vcode=vcode,
+                                              **hp)
                     torch.cuda.synchronize()
                     for i, (hh, d) in enumerate(zip(host, dev)):
-                        what = f"{name} B={B} gdt={gdt} pdt={pdt} multi={multi} step {step} tensor {i}"
+                        what = f"{name} v={vcode} B={B} gdt={gdt} pdt={pdt} multi={multi} step {step} tensor {i}"
                         for k in ((1, 2, 3, 4) if two else (1, 2)):
                             assert np.array_equal(host_bits(d[k]).view(np.uint8), hh[k].view(np.uint8)), \
                                 f"{what}: state array {k}"

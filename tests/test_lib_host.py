@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(qb):
         assert hasattr(qb.lib(), name), name
 
 
-@pytest.mark.parametrize("code", [0, 1, 2])
+@pytest.mark.parametrize("code", [0, 1, 2, 3])
 def test_codebooks_equal_oracle(qb, code):
     lib_cb = np.array(qb.qb_codebook(code), dtype=np.float32)
     assert np.array_equal(lib_cb.view(np.uint32), oracle.codebook(code).view(np.uint32))
@@ -56,6 +56,18 @@ def emulate_dyn8(table, x):
     low, one = np.uint32(105 << 23), np.uint32(0x3F800000)
     cl = np.minimum(np.maximum(mag, low), one)
     b = (cl >> np.uint32(17)).astype(np.int64) - (105 << 6) + 1409 * (bits >> np.uint32(31)).astype(np.int64)
+    return (pay[b] + (x >= t[b])).astype(np.uint8)
+
+
+def emulate_udyn8(table, x):
+    """The kernels' unsigned dynamic-code encoder (x >= 0), from the library's bucket table."""
+    assert len(table) == 2945
+    t = np.array([e[0] for e in table], dtype=np.uint32).view(np.float32)
+    pay = np.array([e[1] for e in table], dtype=np.int64)
+    x = x.astype(np.float32)
+    low, one = np.uint32(104 << 23), np.uint32(0x3F800000)
+    cl = np.minimum(np.maximum(x.view(np.uint32), low), one)
+    b = (cl >> np.uint32(16)).astype(np.int64) - (104 << 7)
     return (pay[b] + (x >= t[b])).astype(np.uint8)
 
 
@@ -98,6 +110,15 @@ def test_dyn8_bucket_encoder_all_floats_in_a_binade(qb):
     assert np.array_equal(emulate_dyn8(qb.qb_encoder_table(0), x), oracle.encode(oracle.DYN8, x))
 
 
+def test_udyn8_bucket_encoder_equals_oracle(qb):
+    """Every binary32 in [0.25, 1] (the densest thresholds) and probes down to
+    the smallest entries, non-negative as the state it serves."""
+    dense = np.arange(0x3E800000, 0x3F800001, dtype=np.uint32).view(np.float32)
+    x = np.abs(probe_values(oracle.UDYN8, np.random.default_rng(33)))
+    x = np.concatenate([dense, x, np.float32([0.0, 1e-45, 2.0 ** -23, 1.625e-7, 3.25e-7])]).astype(np.float32)
+    assert np.array_equal(emulate_udyn8(qb.qb_encoder_table(3), x), oracle.encode(oracle.UDYN8, x))
+
+
 @pytest.mark.parametrize("code", [1, 2])
 def test_4bit_bucket_encoder_equals_oracle(qb, code):
     x = probe_values(code, np.random.default_rng(32 + code))
@@ -122,6 +143,8 @@ def test_invalid_arguments_rejected_before_launch(qb):
     assert L.qb_quantize(A, 0, 100, 0, 8192, A, A, None, None) == qb.QB_EINVAL       # blocksize too large
     assert L.qb_quantize(A, 7, 100, 0, 256, A, A, None, None) == qb.QB_EINVAL        # bad dtype
     assert L.qb_quantize(A, 0, 100, 5, 256, A, A, None, None) == qb.QB_EINVAL        # bad code
+    assert L.qb_quantize(A, 0, 100, 3, 256, A, A, None, None) == qb.QB_EINVAL        # the unsigned code: states only
+    assert L.qb_dequantize(A, A, None, 3, 256, 100, A, 0, None) == qb.QB_EINVAL
     assert L.qb_quantize(None, 0, 100, 0, 256, A, A, None, None) == qb.QB_EINVAL     # null input
     assert L.qb_quantize(A + 4, 0, 100, 0, 256, A, A, None, None) == qb.QB_EALIGN    # misaligned
     assert L.qb_quantize(A, 0, 100, 0, 256, A, None, None, None) == qb.QB_EINVAL     # no absmax, no dq
@@ -221,7 +244,12 @@ def test_optimizer_hyperparameters_rejected_before_launch(qb):
            H(qb.QB_ADAM, -0.1),                                        # lr < 0
            H(qb.QB_LION, 0.1, weight_decay=-1.0),
            H(qb.QB_LION, 0.1, step=0),
-           H(7, 0.1)]
+           H(7, 0.1),
+           # the unsigned code only for a never-negative state, and only codes 0 and 3
+           H(qb.QB_LION, 0.1, v_code=qb.QB_UDYN8),
+           H(qb.QB_SGD, 0.1, beta1=0.9, v_code=qb.QB_UDYN8),
+           H(qb.QB_ADAM, 0.1, v_code=qb.QB_NF4),
+           H(qb.QB_ADAM, 0.1, v_code=7)]
     for hp in bad:
         assert call(hp) == qb.QB_EINVAL, (hp.kind, hp.beta1, hp.beta2, hp.eps, hp.dampening, hp.nesterov)
     assert f(None, A, 0, A2, 2, 100, A, A, A, A, 2048, None) == qb.QB_EINVAL
