@@ -301,6 +301,7 @@ OPTIMIZERS = {  # name: (qb kind, hyperparameters, states)
     "lars": (6, dict(lr=0.5, beta1=0.9, weight_decay=5e-4, trust_coefficient=1e-3), 1),
 }
 LAYERWISE = ("lamb", "lars")
+NONNEG_STATE = ("adamw", "adam", "rmsprop", "lamb")    # kinds whose v (RMSprop: its state) is never negative
 
 
 def optim_bytes_per_param(states, grad_bytes=2, block=ADAM_BLOCK):
@@ -322,6 +323,11 @@ def bench_flat(torch, qb, inputs, dev, args):
     n = 1_500_000_000
     nb = (n + ADAM_BLOCK - 1) // ADAM_BLOCK
     kind, hp, states = OPTIMIZERS[args.optimizer]
+    uv = args.v_code == "udyn8"             # the never-negative state in the unsigned code
+    if uv and args.optimizer not in NONNEG_STATE:
+        raise SystemExit(f"--v-code udyn8 needs a kind with a never-negative state: {', '.join(NONNEG_STATE)}")
+    z1 = 0 if uv and args.optimizer == "rmsprop" else 127       # codes of 0.0 of state 1 and state 2
+    z2 = 0 if uv else 127
     log(f"allocating a flat buffer of {n:,} params ({args.optimizer}, {states} state(s))")
     pdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[args.param_dtype]
     gdt = torch.bfloat16 if args.param_dtype == "fp32" else pdt      # 16-bit params take grads of their dtype
@@ -330,14 +336,14 @@ def bench_flat(torch, qb, inputs, dev, args):
         if args.state_bits != 8 or args.optimizer in LAYERWISE:
             raise SystemExit("--paged runs the element-wise kinds with 8-bit states")
         pin = lambda t: torch.empty(t.shape, dtype=t.dtype, pin_memory=True).copy_(t)
-        s1 = pin(torch.full((n,), 127, dtype=torch.uint8))
+        s1 = pin(torch.full((n,), z1, dtype=torch.uint8))
         a1 = pin(torch.zeros(nb))
-        s2 = pin(torch.full((n,), 127, dtype=torch.uint8)) if states == 2 else None
+        s2 = pin(torch.full((n,), z2, dtype=torch.uint8)) if states == 2 else None
         a2 = pin(torch.zeros(nb)) if states == 2 else None
     elif args.state_bits == 8:
-        s1 = torch.full((n,), 127, dtype=torch.uint8, device=dev)
+        s1 = torch.full((n,), z1, dtype=torch.uint8, device=dev)
         a1 = torch.zeros(nb, device=dev)
-        s2 = torch.full((n,), 127, dtype=torch.uint8, device=dev) if states == 2 else None
+        s2 = torch.full((n,), z2, dtype=torch.uint8, device=dev) if states == 2 else None
         a2 = torch.zeros(nb, device=dev) if states == 2 else None
     else:                       # the 32-bit fallback: binary32 states, no absmax
         s1 = torch.zeros(n, device=dev)
@@ -355,7 +361,7 @@ def bench_flat(torch, qb, inputs, dev, args):
                          dtype=torch.uint8, device=dev)
 
     def step(k):
-        h = qb.optim_hparams(kind, step=k, **hp)
+        h = qb.optim_hparams(kind, step=k, v_code=qb.QB_UDYN8 if uv else qb.QB_DYN8, **hp)
         if args.paged:
             qb.qb_paged_optimizer_step(h, tables[k % 2], 1, qb._DTYPE[gdt], ADAM_BLOCK, args.page_params, ws,
                                        pdt=qb._DTYPE[pdt])
@@ -393,8 +399,9 @@ def bench_flat(torch, qb, inputs, dev, args):
         extra = {"pcie_bytes_each_way": state_bytes, "pcie_GB/s_each_way": state_bytes / med / 1e6}
     print(json.dumps({"workload": f"flat 1.5e9 params, {args.param_dtype if args.param_dtype != 'fp32' else 'bf16'} "
                                   f"grads, block 2048, {call} {args.optimizer} "
-                                  f"step, {args.state_bits}-bit states, {args.param_dtype} params",
-                      "optimizer": args.optimizer, "param_dtype": args.param_dtype,
+                                  f"step, {args.state_bits}-bit states"
+                                  f"{' (v in the unsigned dynamic code)' if uv else ''}, {args.param_dtype} params",
+                      "optimizer": args.optimizer, "param_dtype": args.param_dtype, "v_code": args.v_code,
                       "state_bits": args.state_bits, "steps": args.steps, "median_ms": med,
                       "bytes_per_param": bpp, "GB/s": nbytes / med / 1e6,
                       "params_per_s": n / med * 1e3, "frac_of_hbm_peak": nbytes / med / 1e6 / HBM_PEAK_GBS,
@@ -557,6 +564,8 @@ def main():
                     help="parameter dtype of the --flat run (16-bit parameters take gradients of their dtype)")
     ap.add_argument("--optimizer", choices=sorted(OPTIMIZERS), default="adamw",
                     help="optimizer of the --flat run (the 8-bit states of each kind)")
+    ap.add_argument("--v-code", choices=["dyn8", "udyn8"], default="dyn8",
+                    help="code of the never-negative state of the --flat run (udyn8: the unsigned dynamic code)")
     ap.add_argument("--state-bits", type=int, choices=(8, 32), default=8,
                     help="state width of the --flat run (32: the binary32 fallback of small or chosen tensors)")
     ap.add_argument("--codes", action="store_true",

@@ -413,6 +413,41 @@ __device__ __forceinline__ uint32_t enc_dyn8_pos(float nv, const DynEncLds& s)
     return c + (nv >= s.thr[c] ? 1u : 0u);
 }
 
+// Copies WORDS dwords from global memory to LDS with NT threads in two
+// phases: load() reads this thread's words into registers (an index past the
+// end re-reads the last word), store() writes those in range.  Calling the
+// load() of every table, then hold() of every table, before any store() keeps
+// all the loads in flight together, so the waves wait for them once (a load
+// and its store one round at a time would wait once per round).
+template <int NT, int WORDS>
+struct StageWords {
+    static constexpr int R = (WORDS + NT - 1) / NT;
+    uint32_t v[R];
+    __device__ __forceinline__ void load(const void* src, int tid)
+    {
+        const uint32_t* const s = static_cast<const uint32_t*>(src);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = r * NT + tid;
+            v[r] = s[i < WORDS ? i : WORDS - 1];
+        }
+    }
+    // No instruction: the words are in registers here, so the compiler can
+    // neither sink a load into the branch of its store nor delay it.
+    __device__ __forceinline__ void hold()
+    {
+#pragma unroll
+        for (int r = 0; r < R; ++r) asm volatile("" : "+v"(v[r]));
+    }
+    __device__ __forceinline__ void store(void* dst, int tid) const
+    {
+        uint32_t* const d = static_cast<uint32_t*>(dst);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if ((r + 1) * NT <= WORDS || r * NT + tid < WORDS) d[r * NT + tid] = v[r];
+    }
+};
+
 // LDS copy of the unsigned dynamic-code encoder (n >= 0): the code at the start
 // of each bucket of n (bits of the clamped n >> 16), and the 255 thresholds.
 struct UDynEncLds {
@@ -420,25 +455,10 @@ struct UDynEncLds {
     float thr[256];
 };
 
-// Stage the unsigned encoder tables (about 3.9 KB) into LDS with NT threads.
-template <int NT = kThreads>
-__device__ __forceinline__ void stage_udyn_enc(UDynEncLds& s, const QbTables* __restrict__ tab, int tid)
-{
-    constexpr int W = kUDynBucketBytes / 4;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(tab->udyn8_base);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(s.base);
-#pragma unroll
-    for (int r = 0; r < (W + NT - 1) / NT; ++r)
-        if ((r + 1) * NT <= W || r * NT + tid < W) dst[r * NT + tid] = src[r * NT + tid];
-#pragma unroll
-    for (int r = 0; r < (256 + NT - 1) / NT; ++r)
-        if (NT <= 256 || tid < 256) s.thr[r * NT + tid] = __uint_as_float(tab->udyn8_thr[r * NT + tid]);
-}
-
 // Unsigned dynamic 8-bit code of a normalized value in [0, 1].
 __device__ __forceinline__ uint32_t enc_udyn8(float nv, const UDynEncLds& s)
 {
-    const float cl = __builtin_amdgcn_fmed3f(nv, 0x1p-23f, 1.0f);
+    const float cl = __builtin_amdgcn_fmed3f(nv, 0x1p-22f, 1.0f);
     const uint32_t c = s.base[(fbits(cl) >> kUDynShift) - kUDynBase];
     return c + (nv >= s.thr[c] ? 1u : 0u);
 }

@@ -343,17 +343,43 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
             cvw[w] = wv;
         }
     }
+    // the code tables: every word is loaded before any is stored (one wait)
+    constexpr int kBaseW = kDynBucketBytes / 4;           // one sign's buckets
+    StageWords<T::NT, 256> st_dec, st_thr, st_udec, st_uthr;
+    StageWords<T::NT, kBaseW> st_pos, st_neg;
+    StageWords<T::NT, kUDynBucketBytes / 4> st_ubase;
     if constexpr (SIGNED) {
-#pragma unroll
-        for (int r = 0; r < (256 + T::NT - 1) / T::NT; ++r)
-            if (T::NT <= 256 || tid < 256) s_dyn[r * T::NT + tid] = tab->dyn8[r * T::NT + tid];
-        stage_dyn_enc<T::NT>(s_enc, tab, tid);
+        st_dec.load(tab->dyn8, tid);
+        st_pos.load(&tab->dyn8_base[0][0], tid);
+        st_neg.load(&tab->dyn8_base[1][0], tid);
+        st_thr.load(tab->dyn8_thr, tid);
     }
     if constexpr (UV) {
-#pragma unroll
-        for (int r = 0; r < (256 + T::NT - 1) / T::NT; ++r)
-            if (T::NT <= 256 || tid < 256) s_v.dec[r * T::NT + tid] = tab->udyn8[r * T::NT + tid];
-        stage_udyn_enc<T::NT>(s_v.enc, tab, tid);
+        st_udec.load(tab->udyn8, tid);
+        st_ubase.load(tab->udyn8_base, tid);
+        st_uthr.load(tab->udyn8_thr, tid);
+    }
+    if constexpr (SIGNED) {
+        st_dec.hold();
+        st_pos.hold();
+        st_neg.hold();
+        st_thr.hold();
+    }
+    if constexpr (UV) {
+        st_udec.hold();
+        st_ubase.hold();
+        st_uthr.hold();
+    }
+    if constexpr (SIGNED) {
+        st_dec.store(s_dyn, tid);
+        st_pos.store(&s_enc.base[kDynBase / 4], tid);
+        st_neg.store(&s_enc.base[(kDynIdxSign + kDynBase) / 4], tid);
+        st_thr.store(s_enc.thr, tid);
+    }
+    if constexpr (UV) {
+        st_udec.store(s_v.dec, tid);
+        st_ubase.store(s_v.enc.base, tid);
+        st_uthr.store(s_v.enc.thr, tid);
     }
     __syncthreads();
     const float* const dec_x = SIGNED ? s_dyn : s_v.dec;

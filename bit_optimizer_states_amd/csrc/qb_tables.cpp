@@ -177,7 +177,7 @@ int build_udyn8_lut(const float* udyn8, uint8_t* base, uint32_t* thr)
     std::vector<float> T = thresholds(vals);            // 255 thresholds, ascending
     for (int c = 0; c < 256; ++c) thr[c] = c < 255 ? bits_of(T[c]) : 0x7F800000u;
     for (int b = 0; b < kUDynLutN; ++b) {
-        // n of bucket b: [lo, hi] (bucket 0 also takes every n below 2^-23, the last only 1.0)
+        // n of bucket b: [lo, hi] (bucket 0 also takes every n below 2^-22, the last only 1.0)
         const float lo = b == 0 ? 0.0f : float_of(uint32_t(b + kUDynBase) << kUDynShift);
         const float hi = b == kUDynLutN - 1 ? 1.0f : float_of((uint32_t(b + kUDynBase + 1) << kUDynShift) - 1u);
         int c = 0;

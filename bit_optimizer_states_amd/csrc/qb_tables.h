@@ -19,13 +19,15 @@ constexpr int kDynLutN = int(kOneBits >> kDynShift) - kDynBase + 1;   // 1409
 
 // Unsigned dynamic 8-bit encoder (n >= 0): buckets over the bit pattern of n,
 // 7 mantissa bits per bucket (the unsigned code is twice as dense as the
-// signed one); every n below 2^-23 shares bucket 0 (the smallest decision
-// threshold is 1.625e-7 > 2^-23).
-constexpr uint32_t kUDynLowBits = 104u << 23;   // 2^-23
+// signed one); every n below 2^-22 shares bucket 0, which holds the smallest
+// decision threshold (1.625e-7) and ends below the next (5.5e-7).  Starting
+// there rather than a binade lower keeps the two-state optimizer kernel's LDS
+// at 7 workgroups per CU.
+constexpr uint32_t kUDynLowBits = 105u << 23;   // 2^-22
 constexpr int kUDynShift = 16;
 constexpr int kUDynBase = int(kUDynLowBits >> kUDynShift);
-constexpr int kUDynLutN = int(kOneBits >> kUDynShift) - kUDynBase + 1;   // 2945
-constexpr int kUDynBucketBytes = (kUDynLutN + 3) / 4 * 4;                 // 2948
+constexpr int kUDynLutN = int(kOneBits >> kUDynShift) - kUDynBase + 1;   // 2817
+constexpr int kUDynBucketBytes = (kUDynLutN + 3) / 4 * 4;                 // 2820
 
 // 4-bit encoders: linear buckets of n in [-1, 1]: b = (int)(n*16 + 16).
 constexpr int k4LutN = 33;

@@ -492,8 +492,8 @@ int32_t qb_codebook(qb_code code, float* out);
  *   DYN8: 2 x 1409 entries, those of n >= 0 and then those of n < 0; bucket
  *         b = (clamp(bits(|n|), 2^-22, 1.0) >> 17) - (bits(2^-22) >> 17), plus
  *         1409 for n < 0; the code is payload + (n >= threshold).
- *   UDYN8: 2945 entries, n >= 0; bucket b = (clamp(bits(n), 2^-23, 1.0) >> 16)
- *         - (bits(2^-23) >> 16); the code is payload + (n >= threshold).
+ *   UDYN8: 2817 entries, n >= 0; bucket b = (clamp(bits(n), 2^-22, 1.0) >> 16)
+ *         - (bits(2^-22) >> 16); the code is payload + (n >= threshold).
  *   NF4/FP4: bucket b = (int)(n*16 + 16) in binary32 (0..32); the code is byte
  *         0 of payload if n < threshold, else byte 1.
  * Copies at most `capacity` entries (2*capacity words) into out and returns the

@@ -61,13 +61,13 @@ def emulate_dyn8(table, x):
 
 def emulate_udyn8(table, x):
     """The kernels' unsigned dynamic-code encoder (x >= 0), from the library's bucket table."""
-    assert len(table) == 2945
+    assert len(table) == 2817
     t = np.array([e[0] for e in table], dtype=np.uint32).view(np.float32)
     pay = np.array([e[1] for e in table], dtype=np.int64)
     x = x.astype(np.float32)
-    low, one = np.uint32(104 << 23), np.uint32(0x3F800000)
+    low, one = np.uint32(105 << 23), np.uint32(0x3F800000)
     cl = np.minimum(np.maximum(x.view(np.uint32), low), one)
-    b = (cl >> np.uint32(16)).astype(np.int64) - (104 << 7)
+    b = (cl >> np.uint32(16)).astype(np.int64) - (105 << 7)
     return (pay[b] + (x >= t[b])).astype(np.uint8)
 
 
@@ -115,7 +115,8 @@ def test_udyn8_bucket_encoder_equals_oracle(qb):
     the smallest entries, non-negative as the state it serves."""
     dense = np.arange(0x3E800000, 0x3F800001, dtype=np.uint32).view(np.float32)
     x = np.abs(probe_values(oracle.UDYN8, np.random.default_rng(33)))
-    x = np.concatenate([dense, x, np.float32([0.0, 1e-45, 2.0 ** -23, 1.625e-7, 3.25e-7])]).astype(np.float32)
+    x = np.concatenate([dense, x, np.float32([0.0, 1e-45, 2.0 ** -23, 2.0 ** -22, 1.625e-7, 3.25e-7, 2.4e-7,
+                                              5.5e-7])]).astype(np.float32)
     assert np.array_equal(emulate_udyn8(qb.qb_encoder_table(3), x), oracle.encode(oracle.UDYN8, x))
 
 
