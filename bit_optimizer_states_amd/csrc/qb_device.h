@@ -364,55 +364,6 @@ __device__ __forceinline__ float rcp_rn(float a)
 // encoders (tables staged in LDS)
 // ---------------------------------------------------------------------------
 
-// LDS copy of the dynamic-code encoder.  The base-code table is indexed
-// directly by (bits of the clamped |n|) >> 17, with the sign bit moved to bit
-// 13: the used entries sit at [kDynBase, kDynBase + 1409) and the same plus
-// 8192; the rest of the array is never read (it saves the index arithmetic).
-constexpr int kDynIdxSign = 8192;
-constexpr int kDynIdxBytes = kDynIdxSign + kDynBase + kDynBucketBytes;   // 16324
-
-struct DynEncLds {
-    uint32_t base[kDynIdxBytes / 4];
-    float thr[256];
-};
-
-// Stage the encoder tables (about 3.8 KB used) into LDS with NT threads.
-template <int NT = kThreads>
-__device__ __forceinline__ void stage_dyn_enc(DynEncLds& s, const QbTables* __restrict__ tab, int tid)
-{
-    constexpr int W = kDynBucketBytes / 4;                     // 353 words per sign
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(&tab->dyn8_base[0][0]);
-    constexpr int P = kDynBase / 4, N = (kDynIdxSign + kDynBase) / 4;
-#pragma unroll
-    for (int r = 0; r < (W + NT - 1) / NT; ++r) {
-        const int i = r * NT + tid;
-        if ((r + 1) * NT <= W || i < W) {
-            s.base[P + i] = src[i];
-            s.base[N + i] = src[W + i];
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < (256 + NT - 1) / NT; ++r)
-        if (NT <= 256 || tid < 256) s.thr[r * NT + tid] = __uint_as_float(tab->dyn8_thr[r * NT + tid]);
-}
-
-// Dynamic 8-bit code of a normalized value in [-1, 1].
-__device__ __forceinline__ uint32_t enc_dyn8(float nv, const DynEncLds& s)
-{
-    const float cl = __builtin_amdgcn_fmed3f(__builtin_fabsf(nv), 0x1p-22f, 1.0f);
-    const uint32_t idx = (fbits(cl) >> kDynShift) | ((fbits(nv) >> 31) << 13);
-    const uint32_t c = reinterpret_cast<const uint8_t*>(s.base)[idx];
-    return c + (nv >= s.thr[c] ? 1u : 0u);
-}
-
-// Same for a value known to be >= 0 (+0 included).
-__device__ __forceinline__ uint32_t enc_dyn8_pos(float nv, const DynEncLds& s)
-{
-    const float cl = __builtin_amdgcn_fmed3f(nv, 0x1p-22f, 1.0f);
-    const uint32_t c = reinterpret_cast<const uint8_t*>(s.base)[fbits(cl) >> kDynShift];
-    return c + (nv >= s.thr[c] ? 1u : 0u);
-}
-
 // Copies WORDS dwords from global memory to LDS with NT threads in two
 // phases: load() reads this thread's words into registers (an index past the
 // end re-reads the last word), store() writes those in range.  Calling the
@@ -447,6 +398,54 @@ struct StageWords {
             if ((r + 1) * NT <= WORDS || r * NT + tid < WORDS) d[r * NT + tid] = v[r];
     }
 };
+
+// LDS copy of the dynamic-code encoder.  The base-code table is indexed
+// directly by (bits of the clamped |n|) >> 17, with the sign bit moved to bit
+// 13: the used entries sit at [kDynBase, kDynBase + 1409) and the same plus
+// 8192; the rest of the array is never read (it saves the index arithmetic).
+constexpr int kDynIdxSign = 8192;
+constexpr int kDynIdxBytes = kDynIdxSign + kDynBase + kDynBucketBytes;   // 16324
+
+struct DynEncLds {
+    uint32_t base[kDynIdxBytes / 4];
+    float thr[256];
+};
+
+// Stage the encoder tables (about 3.8 KB used) into LDS with NT threads: all
+// loads first, then all stores (one wait).
+template <int NT = kThreads>
+__device__ __forceinline__ void stage_dyn_enc(DynEncLds& s, const QbTables* __restrict__ tab, int tid)
+{
+    constexpr int W = kDynBucketBytes / 4;                     // 353 words per sign
+    StageWords<NT, W> pos, neg;
+    StageWords<NT, 256> thr;
+    pos.load(&tab->dyn8_base[0][0], tid);
+    neg.load(&tab->dyn8_base[1][0], tid);
+    thr.load(tab->dyn8_thr, tid);
+    pos.hold();
+    neg.hold();
+    thr.hold();
+    pos.store(&s.base[kDynBase / 4], tid);
+    neg.store(&s.base[(kDynIdxSign + kDynBase) / 4], tid);
+    thr.store(s.thr, tid);
+}
+
+// Dynamic 8-bit code of a normalized value in [-1, 1].
+__device__ __forceinline__ uint32_t enc_dyn8(float nv, const DynEncLds& s)
+{
+    const float cl = __builtin_amdgcn_fmed3f(__builtin_fabsf(nv), 0x1p-22f, 1.0f);
+    const uint32_t idx = (fbits(cl) >> kDynShift) | ((fbits(nv) >> 31) << 13);
+    const uint32_t c = reinterpret_cast<const uint8_t*>(s.base)[idx];
+    return c + (nv >= s.thr[c] ? 1u : 0u);
+}
+
+// Same for a value known to be >= 0 (+0 included).
+__device__ __forceinline__ uint32_t enc_dyn8_pos(float nv, const DynEncLds& s)
+{
+    const float cl = __builtin_amdgcn_fmed3f(nv, 0x1p-22f, 1.0f);
+    const uint32_t c = reinterpret_cast<const uint8_t*>(s.base)[fbits(cl) >> kDynShift];
+    return c + (nv >= s.thr[c] ? 1u : 0u);
+}
 
 // LDS copy of the unsigned dynamic-code encoder (n >= 0): the code at the start
 // of each bucket of n (bits of the clamped n >> 16), and the 255 thresholds.
