@@ -150,8 +150,15 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
     } else if constexpr (BITS == 8) {
         s_val[tid] = tab->dyn8[tid];
     } else {
-        if (tid < 16) s_val[tid] = (code4 == 0 ? tab->nf4 : tab->fp4)[tid];
-        if constexpr (DQ && !QB_DQ_DIRECT_DYN) s_dyn[tid] = tab->dyn8[tid];
+        // Every thread reads its words of both tables (the 16 code values at
+        // tid % 16) before any is stored: the loads are in flight together
+        // and the waves wait once, not once per table.
+        float tv = (code4 == 0 ? tab->nf4 : tab->fp4)[tid & 15];
+        float td = 0.0f;
+        if constexpr (DQ && !QB_DQ_DIRECT_DYN) td = tab->dyn8[tid];
+        asm volatile("" : "+v"(tv), "+v"(td));      // no instruction: keeps the loads ahead of the stores
+        if (tid < 16) s_val[tid] = tv;
+        if constexpr (DQ && !QB_DQ_DIRECT_DYN) s_dyn[tid] = td;
     }
     __syncthreads();
     if (owner) {
