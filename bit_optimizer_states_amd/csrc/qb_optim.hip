@@ -1,26 +1,7 @@
-// qb_optim.hip -- fused 8-bit optimizer steps: AdamW, Adam, Lion, SGD with
-// momentum, RMSprop and the layer-wise LAMB and LARS, each state held as
-// block-wise dynamic 8-bit codes.
-//
-// The 8-bit optimizer keeps its states as block-wise dynamic 8-bit codes plus
-// one fp32 absmax per block (abstract quoted on "Py之bitsandbytes：
-// bitsandbytes的简介、安装、使用方法之详细攻略", section 2; 2 bytes of state per
-// parameter for Adam: "bitsandbytes - Quantização de LLM", section Workflow
-// 3) and replaces its 32-bit optimizer with the same hyperparameters; 8-bit
-// Adam, SGD, RMSprop and Lion are listed beside AdamW ("bitsandbytes深度解析",
-// section 优化器模块深度分析).  One pass per block, in registers: decode the
-// states, update them and p, reduce each state's new block absmax, encode the
-// states again.  Each parameter's bytes cross HBM once.
-//
-// One 256-thread workgroup per tile (a tile is one block for B >= 1024), in
-// tile order.  For many tensors, the tiles of all tensors are numbered in one
-// range; a workgroup finds its tensor from a coarse bucket index (the tensor
-// holding the bucket's first tile) and, only where a bucket spans several
-// tensors, a binary search among those (uniform, scalar loads that stay in
-// the scalar cache).  Parameters are binary32, or 16-bit (widened on load,
-// rounded once to nearest even on store).  The layer-wise kinds LAMB and
-// LARS need each tensor's norms before any parameter moves: a norm pass
-// (k_trust_norms, k_trust_scalars) precedes their step.
+// qb_optim.hip -- the launches of the fused 8-bit optimizer steps (kernels in
+// qb_optim_kernels.h; here the instantiations with every state in the signed
+// dynamic code, the layer-wise kinds' second norm pass, and the launch entry
+// points that pick them or the unsigned-code ones of qb_optim_uv.hip).
 #include "qb_optim_kernels.h"
 
 namespace qb {
