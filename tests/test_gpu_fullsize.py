@@ -8,7 +8,8 @@ Workloads (seeded, synthetic; shapes of the pages' models):
   * 268,435,456 fp32 values, 0.02 * Student-t(3), dynamic 8-bit code at block
     sizes 256, 2048 and 4096 (quantize + dequantize round trip);
   * one flat buffer of 1,500,000,000 fp32 parameters, bf16 gradients, fused
-    AdamW8bit at block 2048 (ragged last block of 1,792 elements);
+    AdamW8bit at block 2048 (ragged last block of 1,792 elements), with v in
+    the signed and in the unsigned dynamic code;
   * NF4 / FP4 block-64 quantization with nested quantization (block 256) and a
     bf16 dequantize of 7B-decoder-shaped fp16 weights, per tensor and with the
     grouped calls over all 225 tensors;
@@ -105,6 +106,43 @@ def test_adamw8bit_flat_1p5B():
             assert np.array_equal(mm[k], s[1]) and np.array_equal(vm[k], s[2]), (step, blocks[k])
             assert amh[k] == s[3][0] and avh[k] == s[4][0], (step, blocks[k])
             np.testing.assert_allclose(pm[k], s[0], rtol=1e-6, atol=2e-8)
+        del g
+
+
+def test_adamw8bit_flat_1p5B_unsigned_v():
+    """The flat step of bench.py --flat --v-code udyn8: qb_optimizer8bit_step
+    with v in the unsigned dynamic code (fresh v codes 0), sampled blocks
+    against the oracle over three steps."""
+    n, B = 1_500_000_000, 2048
+    L = qb()
+    nb = (n + B - 1) // B
+    p = inputs.normal(n, 0.02, seed=37, device=DEV)
+    m = torch.full((n,), 127, dtype=torch.uint8, device=DEV)
+    v = torch.full((n,), 0, dtype=torch.uint8, device=DEV)
+    am = torch.zeros(nb, device=DEV)
+    av = torch.zeros(nb, device=DEV)
+    rng = np.random.default_rng(4)
+    blocks = np.unique(np.concatenate([rng.choice(nb - 1, 4096, replace=False), [0, nb - 1]]))
+    st = [[host_bits(p[b * B:min(n, (b + 1) * B)]), np.full(min(n, (b + 1) * B) - b * B, 127, np.uint8),
+           np.zeros(min(n, (b + 1) * B) - b * B, np.uint8), np.zeros(1, np.float32), np.zeros(1, np.float32)]
+          for b in blocks]
+    for step in range(1, 4):
+        g = inputs.normal(n, 1e-3, seed=inputs.grad_seed(37, 0, step), device=DEV, dtype=torch.bfloat16)
+        h = L.optim_hparams(L.QB_ADAMW, HP["lr"], beta1=HP["beta1"], beta2=HP["beta2"], eps=HP["eps"],
+                            weight_decay=HP["wd"], step=step, v_code=L.QB_UDYN8)
+        L.qb_optimizer8bit_step(h, p, g, n, m, v, am, av, B)
+        gs = block_rows(g, B, blocks)
+        for s, gb in zip(st, gs):
+            oracle.optim8bit_step(oracle.ADAMW, s[0], gb, s[1], s[3], s[2], s[4], B, step=step, gdt=oracle.BF16,
+                                  vcode=oracle.UDYN8, **HP)
+        torch.cuda.synchronize()
+        pm, mm, vm = block_rows(p, B, blocks), block_rows(m, B, blocks), block_rows(v, B, blocks)
+        amh, avh = am.cpu().numpy()[blocks], av.cpu().numpy()[blocks]
+        for k, s in enumerate(st):
+            assert np.array_equal(mm[k], s[1]) and np.array_equal(vm[k], s[2]), (step, blocks[k])
+            assert amh[k] == s[3][0] and avh[k] == s[4][0], (step, blocks[k])
+            np.testing.assert_allclose(pm[k], s[0], rtol=1e-6, atol=2e-8)
+            s[0][:] = pm[k]          # each step from the device's parameters (AdamW's p is within 1e-6)
         del g
 
 
