@@ -621,6 +621,7 @@ qb_status qb_prepare_code(const float* values, void* table, void* stream)
     thread_local UserCode staged;
     std::memcpy(staged.values, values, sizeof(staged.values));
     if (user_code_thresholds(staged.values, staged.thr) != 0) return QB_EINVAL;
+    user_code_first(staged.thr, staged.first);
     // from pageable memory: the copy has read `staged` when hipMemcpyAsync returns
     return hipMemcpyAsync(table, &staged, sizeof(staged), hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)) ==
                    hipSuccess

@@ -12,7 +12,8 @@
 //   2. k_quantile_groups sums each statistic over groups of 256 consecutive
 //      chunks (binary64, chunk order), and k_quantile_code sums the groups in
 //      group order, divides by the chunk count, forms the midpoints,
-//      normalizes them and writes the code with its decision thresholds.
+//      normalizes them and writes the code with its decision thresholds and
+//      their bucket index.
 // Every step is exact or a fixed sequence of IEEE operations, so the result is
 // the same bits on every run (and as the oracle's).
 #include "qb_device.h"
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_quantile_code(const double* __rest
     __shared__ double q[256];
     __shared__ double red[kThreads / 64];
     __shared__ float vals[256];
+    __shared__ int fb[256];
     const int tid = threadIdx.x;
     for (int j = tid; j < 257; j += kThreads) {
         const double* row = S + (int64_t)j * ngroups;
@@ -179,9 +181,30 @@ __global__ __launch_bounds__(kThreads) void k_quantile_code(const double* __rest
     if (tid < 255) {
         const float a = vals[tid], b = vals[tid + 1];
         const double mid = ((double)a + (double)b) / 2.0;   // the binary64 midpoint, as the encoder reads it
-        out->thr[tid] = ceil_f32(mid, fabsf(a) < fabsf(b));
+        const float t = ceil_f32(mid, fabsf(a) < fabsf(b));
+        out->thr[tid] = t;
+        fb[tid] = user_bucket(t);
     } else {
         out->thr[255] = INFINITY;
+    }
+    __syncthreads();
+    // the bucket index: first[b] = #{k < 255 : fb[k] < b} (fb ascending), by a
+    // lower-bound search per bucket
+    for (int b = tid; b < kUserFirstBytes; b += kThreads) {
+        uint32_t lo = 0;
+        if (b <= kUserBuckets) {
+            uint32_t len = 255;
+            while (len != 0) {
+                const uint32_t h = len >> 1;
+                if (fb[lo + h] < b) {
+                    lo += h + 1;
+                    len -= h + 1;
+                } else {
+                    len = h;
+                }
+            }
+        }
+        out->first[b] = (uint8_t)lo;
     }
 }
 

@@ -462,16 +462,53 @@ __device__ __forceinline__ uint32_t enc_udyn8(float nv, const UDynEncLds& s)
     return c + (nv >= s.thr[c] ? 1u : 0u);
 }
 
-// 8-bit code of a user code: the number of thresholds <= nv, by a branchless
-// binary search over the 255 ascending thresholds (thr[255] = +inf is never
-// read).
-__device__ __forceinline__ uint32_t enc_user(float nv, const float* thr)
+// LDS copy of a user code's encoder: the thresholds and their bucket index.
+struct UserEncLds {
+    float thr[256];
+    uint8_t first[kUserFirstBytes];
+};
+
+// 8-bit code of a user code: the number of thresholds <= nv.  Those of earlier
+// buckets all count and those of later ones none, so only nv's own bucket is
+// searched.  With at most one threshold there (every bucket of the linear
+// code and of quantile codes with no entries crowded within 2^-11) one
+// compare decides: thr[c] then lies in this bucket or a later one
+// (thr[255] = +inf).  A crowded bucket takes a binary search over its own
+// thresholds.
+__device__ __forceinline__ uint32_t enc_user(float nv, const UserEncLds& s)
 {
-    uint32_t c = 0;
-#pragma unroll
-    for (uint32_t s = 128; s >= 1; s >>= 1)
-        if (nv >= thr[c + s - 1]) c += s;
+    const int b = user_bucket(nv);
+    uint32_t c = s.first[b];
+    const uint32_t m = s.first[b + 1] - c;            // thresholds thr[c .. c+m) in bucket b
+    if (m > 1) {
+        uint32_t len = m;
+        while (len != 0) {
+            const uint32_t h = len >> 1;
+            if (nv >= s.thr[c + h]) {
+                c += h + 1;
+                len -= h + 1;
+            } else {
+                len = h;
+            }
+        }
+    } else {
+        c += nv >= s.thr[c] ? 1u : 0u;
+    }
     return c;
+}
+
+// Stage a user code's encoder into LDS with NT threads (one wait).
+template <int NT = kThreads>
+__device__ __forceinline__ void stage_user_enc(UserEncLds& s, const UserCode* __restrict__ code, int tid)
+{
+    StageWords<NT, 256> thr;
+    StageWords<NT, kUserFirstBytes / 4> fst;
+    thr.load(code->thr, tid);
+    fst.load(code->first, tid);
+    thr.hold();
+    fst.hold();
+    thr.store(s.thr, tid);
+    fst.store(s.first, tid);
 }
 
 // 4-bit code (NF4 or FP4 by the table) of a normalized value in [-1, 1]:

@@ -55,12 +55,14 @@ static_assert(sizeof(TensorDesc) == 64, "descriptor layout");
 
 // A user code in device memory (qb_code_table_bytes() bytes): 256 ascending
 // entries and their decision thresholds, thr[k] = the smallest binary32 that
-// encodes to entry k+1 or above (thr[255] = +inf), so code = #{k : n >= thr[k]}.
+// encodes to entry k+1 or above (thr[255] = +inf), so code = #{k : n >= thr[k]};
+// then the index of the thresholds by bucket of n (user_bucket, first[]).
 struct UserCode {
     float values[256];
     float thr[256];
+    uint8_t first[kUserFirstBytes];
 };
-static_assert(sizeof(UserCode) == 2048, "user code layout");
+static_assert(sizeof(UserCode) == 6160, "user code layout");
 
 // One tensor of a quantization pass; tile_begin is its first global tile.
 // First pass: x [n] of the input dtype, codes out, absmax out (the caller's,

@@ -197,10 +197,6 @@ struct Lut4Lds {
     uint2 e[k4LutN];
 };
 
-struct UserThrLds {
-    float thr[256];
-};
-
 // CW consecutive elements of dtype DT at element offset e from a uniform base.
 template <int DT, int CW>
 __device__ __forceinline__ void load_chunk(const void* base, uint32_t e, float* v)
@@ -213,7 +209,7 @@ __device__ __forceinline__ void load_chunk(const void* base, uint32_t e, float* 
 // tensor's mean (offset[0], written by k_dq_mean) is subtracted first.  With
 // bins != nullptr (first pass of a nested quantization) every block absmax is
 // also added to the tensor's exponent bins.
-// USER: 8-bit codes of a user code (`user`: values and thresholds) instead of
+// USER: 8-bit codes of a user code (`user`: thresholds and their bucket index) instead of
 // the dynamic code.
 template <int BITS, int B, int XDT, bool SECOND, bool MULTI, bool USER = false>
 __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<QuantDesc> map,
@@ -223,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
 {
     static_assert(!USER || (BITS == 8 && !SECOND), "user codes are 8-bit, first pass only");
     using G = QGeo<BITS, B>;
-    using EncLds = std::conditional_t<USER, UserThrLds, std::conditional_t<BITS == 8, DynEncLds, Lut4Lds>>;
+    using EncLds = std::conditional_t<USER, UserEncLds, std::conditional_t<BITS == 8, DynEncLds, Lut4Lds>>;
     __shared__ EncLds s_enc;
     __shared__ uint32_t s_red[G::R][4];
     __shared__ unsigned long long s_bins[256];
@@ -271,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
     float mu = 0.0f;
     if constexpr (SECOND) mu = gld<float>(d.offset);
     if constexpr (USER) {
-        s_enc.thr[tid] = user->thr[tid];
+        stage_user_enc(s_enc, user, tid);
     } else if constexpr (BITS == 8) {
         stage_dyn_enc(s_enc, tab, tid);
     } else {
@@ -327,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
             if constexpr (BITS == 8) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    if constexpr (USER) w |= enc_user(nv[c * 4 + j], s_enc.thr) << (8 * j);
+                    if constexpr (USER) w |= enc_user(nv[c * 4 + j], s_enc) << (8 * j);
                     else w |= enc_dyn8(nv[c * 4 + j], s_enc) << (8 * j);
                 }
             } else {

@@ -326,6 +326,16 @@ int user_code_thresholds(const float* values, float* thr)
     return 0;
 }
 
+void user_code_first(const float* thr, uint8_t* first)
+{
+    int k = 0;
+    for (int b = 0; b <= kUserBuckets; ++b) {
+        while (k < 255 && user_bucket(thr[k]) < b) ++k;
+        first[b] = (uint8_t)k;
+    }
+    for (int b = kUserBuckets + 1; b < kUserFirstBytes; ++b) first[b] = 0;
+}
+
 const QbTables* host_tables()
 {
     static QbTables tables;

@@ -32,6 +32,21 @@ constexpr int kUDynBucketBytes = (kUDynLutN + 3) / 4 * 4;                 // 282
 // 4-bit encoders: linear buckets of n in [-1, 1]: b = (int)(n*16 + 16).
 constexpr int k4LutN = 33;
 
+// Encoder of a user code: linear buckets of n clamped to [-1, 1],
+// b = (int)(n*2048 + 2048) in [0, 4096] (n*2048 is exact, so the sum rounds
+// once, fused or not; a NaN n takes bucket 0).  The map is monotone, so a
+// threshold in an earlier bucket is below n and one in a later bucket above
+// it: with first[b] = #{k < 255 : bucket(thr[k]) < b}, b = 0..4097, the code
+// of n is first[b] plus the count of bucket b's thresholds thr[first[b] ..
+// first[b+1]) that are <= n.  One function for the host table and the device
+// encoder (constexpr, so device code may call it).
+constexpr int kUserBuckets = 4097;
+constexpr int kUserFirstBytes = 4112;           // first[0 .. 4097], zero padded
+constexpr int user_bucket(float n)
+{
+    return (int)(__builtin_fminf(__builtin_fmaxf(n, -1.0f), 1.0f) * 2048.0f + 2048.0f);
+}
+
 struct LutEntry {
     uint32_t t;        // decision threshold (binary32 bits)
     uint32_t payload;  // DYN8: 127 + thresholds below the bucket; 4-bit: code below | code above << 8
@@ -76,5 +91,9 @@ void linear_code(float* out /* [256] */);
 // of smaller magnitude, between equal magnitudes to the upper one),
 // thr[255] = +inf.  Returns 0, or -1 for an invalid code.
 int user_code_thresholds(const float* values, float* thr);
+
+// The bucket index of a user code's thresholds (the map above): first[b] for
+// b = 0..4097 from thr[0..254] (ascending), zeros up to kUserFirstBytes.
+void user_code_first(const float* thr, uint8_t* first /* [kUserFirstBytes] */);
 
 }  // namespace qb

@@ -434,10 +434,13 @@ size_t qb_paged_workspace_bytes(int64_t page_params, int32_t blocksize);
  * linear and dynamic, and a fast quantile estimation (page "Py之bitsandbytes",
  * section 1).  Besides the built-in dynamic code, a block-wise 8-bit
  * quantization can use any 256-entry code held in a device table of
- * qb_code_table_bytes() bytes (16-byte aligned): the entries and their exact
- * decision thresholds (nearest entry; the midpoint of two entries is taken in
- * binary64; a tie goes to the entry of smaller magnitude, between equal
- * magnitudes to the upper one).
+ * qb_code_table_bytes() bytes (16-byte aligned): the entries (256 floats at
+ * the start), their exact decision thresholds (nearest entry; the midpoint of
+ * two entries is taken in binary64; a tie goes to the entry of smaller
+ * magnitude, between equal magnitudes to the upper one), and an index of the
+ * thresholds by 2^-11-wide bucket of the normalized value, so the encoder
+ * searches only its value's bucket.  Write tables only through the two calls
+ * below.
  *   qb_linear_code      host: the linear code k/127, k = -128..127 (returns 256).
  *   qb_prepare_code     host values[256] (finite, non-decreasing; else
  *                       QB_EINVAL) -> device table, copied on `stream`.

@@ -21,8 +21,15 @@ def table_of(values):
 
 def read_table(t):
     torch.cuda.synchronize()
-    a = t.cpu().numpy().view(np.float32)
+    a = t.cpu().numpy()[:2048].view(np.float32)
     return a[:256].copy(), a[256:].copy()
+
+
+def bucket_index(t):
+    """The table's index of thresholds by bucket of n (bytes after the entries
+    and thresholds)."""
+    torch.cuda.synchronize()
+    return t.cpu().numpy()[2048:].copy()
 
 
 def codes_of(name):
@@ -35,6 +42,13 @@ def codes_of(name):
         half = np.sort(rng.uniform(0.001, 1.0, 128)).astype(np.float32)
         half[-1] = 1.0
         return np.concatenate([-half[::-1], half]).astype(np.float32)
+    if name == "crowded":
+        # 240 entries (with repeats) inside [0, 2^-11) share one encoder bucket;
+        # the rest spread over [-1, 1]
+        tight = np.sort(np.round(rng.uniform(0, 2.0 ** -11, 240), 7)).astype(np.float32)
+        tight[::17] = tight[1::17][:tight[::17].size]
+        wide = np.linspace(-1, 1, 16).astype(np.float32)
+        return np.sort(np.concatenate([tight, wide])).astype(np.float32)
     return oracle.estimate_quantiles((rng.standard_t(3, 50000) * 0.02).astype(np.float32))
 
 
@@ -46,7 +60,7 @@ def make_x(n, dt, seed):
     return t.view(torch.int16).numpy().view(np.uint16).copy(), t
 
 
-@pytest.mark.parametrize("name", ["linear", "dynamic", "symmetric_no_zero", "quantile"])
+@pytest.mark.parametrize("name", ["linear", "dynamic", "symmetric_no_zero", "quantile", "crowded"])
 @pytest.mark.parametrize("B,dt", [(64, oracle.F32), (256, oracle.BF16), (2048, oracle.F16), (4096, oracle.F32)])
 def test_user_code_roundtrip_equals_oracle(name, B, dt):
     L = qb()
@@ -58,6 +72,11 @@ def test_user_code_roundtrip_equals_oracle(name, B, dt):
     nb = (n + B - 1) // B
     codes = torch.full((n + 8,), 0xAB, dtype=torch.uint8, device=DEV)
     absmax = torch.full((nb + 2,), -7.0, device=DEV)
+    _, thr = read_table(t)
+    fb = [int(np.float32(min(max(v, np.float32(-1)), np.float32(1))) * np.float32(2048) + np.float32(2048))
+          for v in thr[:255]]
+    want_first = (np.array(fb)[None, :] < np.arange(4098)[:, None]).sum(axis=1)
+    assert np.array_equal(bucket_index(t)[:4098], want_first) and not bucket_index(t)[4098:].any()
     L.qb_quantize_code(xd, n, t, B, codes, absmax)
     want_c, want_a = oracle.quantize_custom(xh, cb, B, dt)
     got_c, got_a = host_bits(codes), host_bits(absmax)
@@ -92,9 +111,11 @@ def test_estimated_quantile_code_equals_oracle(n, dt):
     vals, thr = read_table(t)
     want = oracle.estimate_quantiles(xh, xdt=dt)
     assert np.array_equal(vals.view(np.uint32), want.view(np.uint32))
-    # the device thresholds are the host's for the same entries
-    _, host_thr = read_table(table_of(vals))
+    # the device thresholds and bucket index are the host's for the same entries
+    host_t = table_of(vals)
+    _, host_thr = read_table(host_t)
     assert np.array_equal(thr.view(np.uint32), host_thr.view(np.uint32))
+    assert np.array_equal(bucket_index(t), bucket_index(host_t))
 
 
 def test_quantile_code_of_a_uniform_grid():

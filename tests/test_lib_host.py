@@ -312,7 +312,7 @@ def test_layerwise_arguments_and_workspace(qb):
 def test_linear_code_equals_oracle(qb):
     got = np.array(qb.qb_linear_code(), dtype=np.float32)
     assert np.array_equal(got.view(np.uint32), oracle.linear_codebook().view(np.uint32))
-    assert qb.qb_code_table_bytes() == 2048
+    assert qb.qb_code_table_bytes() == 6160          # entries, thresholds, bucket index
 
 
 def test_user_code_arguments_rejected_before_launch(qb):
