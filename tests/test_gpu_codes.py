@@ -156,3 +156,42 @@ def test_estimate_then_quantize_a_large_tensor():
     assert np.array_equal(absmax.index_select(0, idx).cpu().numpy(), want_a)
     want_y = oracle.dequantize_custom(want_c, want_a, vals, B, xs.size)
     assert np.array_equal(y.view(-1, B).index_select(0, idx).cpu().numpy().reshape(-1), want_y)
+
+
+@pytest.mark.parametrize("name", ["edge_grid", "crowded", "dynamic", "linear"])
+def test_user_code_on_bucket_edges(name):
+    """Values at, and one ulp beside, every encoder bucket edge and every
+    threshold, in blocks whose absmax is 1 (so the normalized value is the
+    input itself).  edge_grid is the code (k + 1/2)/128 - 1, whose midpoints are
+    bucket edges: its thresholds sit on an edge (negative side) or one ulp
+    above it (positive side, ties toward the smaller magnitude)."""
+    L = qb()
+    B = 2048
+    if name == "edge_grid":
+        cb = ((np.arange(256) + 0.5) / 128 - 1).astype(np.float32)
+    else:
+        cb = codes_of(name)
+    t = table_of(cb)
+    _, thr = read_table(t)
+    edges = (np.arange(4097) / 2048 - 1).astype(np.float32)
+    core = np.concatenate([edges, thr[:255]])
+    core = core[np.abs(core) <= 1]
+    vals = np.concatenate([core, np.nextafter(core, np.float32(2)), np.nextafter(core, np.float32(-2)),
+                           np.float32([0.0, -0.0, 1e-30, -1e-30])]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 1]
+    per = B - 1
+    nb = -(-vals.size // per)
+    x = np.zeros(nb * B, np.float32)
+    for b in range(nb):
+        chunk = vals[b * per:(b + 1) * per]
+        x[b * B] = 1.0
+        x[b * B + 1:b * B + 1 + chunk.size] = chunk
+    n = x.size - 5                                       # a ragged last block
+    x = x[:n].copy()
+    codes = torch.empty(n, dtype=torch.uint8, device=DEV)
+    absmax = torch.empty(nb, device=DEV)
+    L.qb_quantize_code(to_device(x), n, t, B, codes, absmax)
+    want_c, want_a = oracle.quantize_custom(x, cb, B)
+    assert np.all(want_a == 1.0)
+    got = host_bits(codes)
+    assert np.array_equal(got, want_c), np.flatnonzero(got != want_c)[:8]
