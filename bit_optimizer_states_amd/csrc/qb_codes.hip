@@ -31,17 +31,22 @@ constexpr int kWaveShift = 10;
 // accesses (lane stride 16 words) at two-way bank conflicts.
 __device__ __forceinline__ int slot(int i) { return i + (i >> 5); }
 
-// Compare-exchange of v[a] and v[b] (a < b): ascending if up.
-__device__ __forceinline__ void cas(float& x, float& y, bool up)
+// Compare-exchange, ascending: x takes the smaller value.
+__device__ __forceinline__ void cas(float& x, float& y)
 {
     const float lo = fminf(x, y), hi = fmaxf(x, y);
-    x = up ? lo : hi;
-    y = up ? hi : lo;
+    x = lo;
+    y = hi;
 }
 
-// Bitonic sort (ascending) of the chunk: thread t holds elements 16 t .. 16 t + 15
-// in registers; stages whose partner lies in the same thread (stride < 16) run
-// in registers, the others through LDS.
+// Bitonic sort (ascending) of the chunk, in the form without directions: the
+// merge of two sorted runs of size/2 into a sorted run of `size` first pairs
+// element i with its mirror i ^ (size - 1), then i with i ^ stride for
+// stride = size/4 .. 1; every compare-exchange puts the smaller value at the
+// lower index, so no step selects on a direction.  Thread t holds elements
+// 16 t .. 16 t + 15 in registers; pairs within a thread (stride < 16) run in
+// registers, pairs across lanes by lane shuffles, pairs across waves (stride
+// >= 1024) through LDS.
 template <int XDT>
 __global__ __launch_bounds__(kThreads) void k_chunk_quantiles(const void* __restrict__ x, int64_t n, int64_t nchunks,
                                                               float* __restrict__ E)
@@ -65,54 +70,70 @@ __global__ __launch_bounds__(kThreads) void k_chunk_quantiles(const void* __rest
     }
     // sizes 2 .. 16: wholly inside a thread
 #pragma unroll
-    for (int size = 2; size <= kSortPerThread; size <<= 1)
+    for (int size = 2; size <= kSortPerThread; size <<= 1) {
 #pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1)
+        for (int r = 0; r < kSortPerThread; ++r)
+            if ((r & (size >> 1)) == 0) cas(v[r], v[r ^ (size - 1)]);
+#pragma unroll
+        for (int stride = size >> 2; stride > 0; stride >>= 1)
 #pragma unroll
             for (int r = 0; r < kSortPerThread; ++r)
-                if ((r & stride) == 0) cas(v[r], v[r + stride], ((base + r) & size) == 0);
-    // sizes 32 .. 4096: strides of 1024 and more through LDS (the partner is in
-    // another wave), 16 .. 512 by lane shuffles within the wave (the partner of
-    // element 16 t + r is element r of lane t ^ stride/16), then 8 .. 1 in
-    // registers
+                if ((r & stride) == 0) cas(v[r], v[r + stride]);
+    }
+    // sizes 32 .. 4096
     for (int size = 2 * kSortPerThread; size <= kQuantileChunk; size <<= 1) {
-        const bool up = (base & size) == 0;                    // the same for the thread's 16 elements
+        int top;                                               // the largest lane-shuffle stride
         if (size > kWaveElems) {
+            // the mirror stage and strides >= 1024 pair elements of different
+            // waves: through LDS, 8 pairs per thread
 #pragma unroll
             for (int r = 0; r < kSortPerThread; ++r) s[slot(base + r)] = v[r];
             __syncthreads();
-            for (int ls = __builtin_ctz(size) - 1; ls >= kWaveShift; --ls) {   // stride = 2^ls >= 1024
+            for (int ls = __builtin_ctz(size) - 1; ls >= kWaveShift; --ls) {
                 const int stride = 1 << ls;
+                const bool mirror = stride == size >> 1;
 #pragma unroll
                 for (int k = 0; k < kSortPerThread / 2; ++k) {
                     const int q = k * kThreads + tid;          // pair q: i has a zero at bit `stride`
                     const int i = ((q >> ls) << (ls + 1)) | (q & (stride - 1));
-                    float a = s[slot(i)], b = s[slot(i + stride)];
-                    cas(a, b, (i & size) == 0);
+                    const int j = mirror ? i ^ (size - 1) : i + stride;
+                    float a = s[slot(i)], b = s[slot(j)];
+                    cas(a, b);
                     s[slot(i)] = a;
-                    s[slot(i + stride)] = b;
+                    s[slot(j)] = b;
                 }
                 __syncthreads();
             }
 #pragma unroll
             for (int r = 0; r < kSortPerThread; ++r) v[r] = s[slot(base + r)];
             __syncthreads();                                   // before the next size overwrites s
+            top = kWaveElems >> 1;
+        } else {
+            // the mirror stage within the wave: element 16 t + r pairs with
+            // element 15 - r of lane t ^ (size/16 - 1)
+            const int m = size / kSortPerThread - 1;
+            const bool lower = (tid & (size / (2 * kSortPerThread))) == 0;
+            float w[kSortPerThread];
+#pragma unroll
+            for (int r = 0; r < kSortPerThread; ++r) w[r] = __shfl_xor(v[kSortPerThread - 1 - r], m);
+#pragma unroll
+            for (int r = 0; r < kSortPerThread; ++r) v[r] = lower ? fminf(v[r], w[r]) : fmaxf(v[r], w[r]);
+            top = size >> 2;
         }
-        const int top = size > kWaveElems ? kWaveElems >> 1 : size >> 1;
         for (int stride = top; stride >= kSortPerThread; stride >>= 1) {
             const int lanes = stride / kSortPerThread;
-            const bool keep_min = ((tid & lanes) == 0) == up;
+            const bool lower = (tid & lanes) == 0;
 #pragma unroll
             for (int r = 0; r < kSortPerThread; ++r) {
                 const float w = __shfl_xor(v[r], lanes);
-                v[r] = keep_min ? fminf(v[r], w) : fmaxf(v[r], w);
+                v[r] = lower ? fminf(v[r], w) : fmaxf(v[r], w);
             }
         }
 #pragma unroll
         for (int stride = kSortPerThread >> 1; stride > 0; stride >>= 1)
 #pragma unroll
             for (int r = 0; r < kSortPerThread; ++r)
-                if ((r & stride) == 0) cas(v[r], v[r + stride], up);
+                if ((r & stride) == 0) cas(v[r], v[r + stride]);
     }
 #pragma unroll
     for (int r = 0; r < kSortPerThread; ++r) s[slot(base + r)] = v[r];
