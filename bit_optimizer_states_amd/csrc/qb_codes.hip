@@ -39,6 +39,11 @@ __device__ __forceinline__ void cas(float& x, float& y)
     y = hi;
 }
 
+// A lane-shuffle stage keeps min(v, w) in the lower lane of a pair and
+// max(v, w) in the upper one: med3(v, w, -inf) and med3(v, w, +inf), one
+// instruction with a per-lane third operand (the values are finite or +inf).
+__device__ __forceinline__ float keep_bound(bool lower) { return lower ? -INFINITY : INFINITY; }
+
 // Bitonic sort (ascending) of the chunk, in the form without directions: the
 // merge of two sorted runs of size/2 into a sorted run of `size` first pairs
 // element i with its mirror i ^ (size - 1), then i with i ^ stride for
@@ -112,22 +117,19 @@ __global__ __launch_bounds__(kThreads) void k_chunk_quantiles(const void* __rest
             // the mirror stage within the wave: element 16 t + r pairs with
             // element 15 - r of lane t ^ (size/16 - 1)
             const int m = size / kSortPerThread - 1;
-            const bool lower = (tid & (size / (2 * kSortPerThread))) == 0;
+            const float keep = keep_bound((tid & (size / (2 * kSortPerThread))) == 0);
             float w[kSortPerThread];
 #pragma unroll
             for (int r = 0; r < kSortPerThread; ++r) w[r] = __shfl_xor(v[kSortPerThread - 1 - r], m);
 #pragma unroll
-            for (int r = 0; r < kSortPerThread; ++r) v[r] = lower ? fminf(v[r], w[r]) : fmaxf(v[r], w[r]);
+            for (int r = 0; r < kSortPerThread; ++r) v[r] = __builtin_amdgcn_fmed3f(v[r], w[r], keep);
             top = size >> 2;
         }
         for (int stride = top; stride >= kSortPerThread; stride >>= 1) {
             const int lanes = stride / kSortPerThread;
-            const bool lower = (tid & lanes) == 0;
+            const float keep = keep_bound((tid & lanes) == 0);
 #pragma unroll
-            for (int r = 0; r < kSortPerThread; ++r) {
-                const float w = __shfl_xor(v[r], lanes);
-                v[r] = lower ? fminf(v[r], w) : fmaxf(v[r], w);
-            }
+            for (int r = 0; r < kSortPerThread; ++r) v[r] = __builtin_amdgcn_fmed3f(v[r], __shfl_xor(v[r], lanes), keep);
         }
 #pragma unroll
         for (int stride = kSortPerThread >> 1; stride > 0; stride >>= 1)
