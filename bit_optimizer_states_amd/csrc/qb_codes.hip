@@ -39,10 +39,47 @@ __device__ __forceinline__ void cas(float& x, float& y)
     y = hi;
 }
 
+// Value of lane ^ M within the wave.  Partners inside a row of 16 lanes come
+// through DPP moves (quad permutations for ^1, ^2, ^3, the row mirrors for ^15
+// and ^7, two of them for ^4 = ^7^3 and ^8 = ^15^7); the others through the
+// LDS crossbar.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int M>
+__device__ __forceinline__ float lane_xor(float x)
+{
+    constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kQuadRev = 0x1B, kRowMirror = 0x140, kHalfMirror = 0x141;
+    if constexpr (M == 1) return dpp<kQuadSwap1>(x);
+    else if constexpr (M == 2) return dpp<kQuadSwap2>(x);
+    else if constexpr (M == 3) return dpp<kQuadRev>(x);
+    else if constexpr (M == 4) return dpp<kQuadRev>(dpp<kHalfMirror>(x));
+    else if constexpr (M == 7) return dpp<kHalfMirror>(x);
+    else if constexpr (M == 8) return dpp<kHalfMirror>(dpp<kRowMirror>(x));
+    else if constexpr (M == 15) return dpp<kRowMirror>(x);
+    else return __shfl_xor(x, M);
+}
+
 // A lane-shuffle stage keeps min(v, w) in the lower lane of a pair and
 // max(v, w) in the upper one: med3(v, w, -inf) and med3(v, w, +inf), one
 // instruction with a per-lane third operand (the values are finite or +inf).
 __device__ __forceinline__ float keep_bound(bool lower) { return lower ? -INFINITY : INFINITY; }
+
+// One lane-shuffle stage: element r of this lane meets element r (MIRROR:
+// element 15 - r) of lane ^ M; the lower lane of the pair keeps the minimum.
+template <int M, bool MIRROR>
+__device__ __forceinline__ void lane_stage(float* v, bool lower)
+{
+    const float keep = keep_bound(lower);
+    float w[kSortPerThread];
+#pragma unroll
+    for (int r = 0; r < kSortPerThread; ++r) w[r] = lane_xor<M>(v[MIRROR ? kSortPerThread - 1 - r : r]);
+#pragma unroll
+    for (int r = 0; r < kSortPerThread; ++r) v[r] = __builtin_amdgcn_fmed3f(v[r], w[r], keep);
+}
 
 // Bitonic sort (ascending) of the chunk, in the form without directions: the
 // merge of two sorted runs of size/2 into a sorted run of `size` first pairs
@@ -116,20 +153,28 @@ __global__ __launch_bounds__(kThreads) void k_chunk_quantiles(const void* __rest
         } else {
             // the mirror stage within the wave: element 16 t + r pairs with
             // element 15 - r of lane t ^ (size/16 - 1)
-            const int m = size / kSortPerThread - 1;
-            const float keep = keep_bound((tid & (size / (2 * kSortPerThread))) == 0);
-            float w[kSortPerThread];
-#pragma unroll
-            for (int r = 0; r < kSortPerThread; ++r) w[r] = __shfl_xor(v[kSortPerThread - 1 - r], m);
-#pragma unroll
-            for (int r = 0; r < kSortPerThread; ++r) v[r] = __builtin_amdgcn_fmed3f(v[r], w[r], keep);
+            const bool lower = (tid & (size / (2 * kSortPerThread))) == 0;
+            switch (size / kSortPerThread - 1) {           // wave-uniform
+            case 1: lane_stage<1, true>(v, lower); break;
+            case 3: lane_stage<3, true>(v, lower); break;
+            case 7: lane_stage<7, true>(v, lower); break;
+            case 15: lane_stage<15, true>(v, lower); break;
+            case 31: lane_stage<31, true>(v, lower); break;
+            default: lane_stage<63, true>(v, lower); break;
+            }
             top = size >> 2;
         }
         for (int stride = top; stride >= kSortPerThread; stride >>= 1) {
             const int lanes = stride / kSortPerThread;
-            const float keep = keep_bound((tid & lanes) == 0);
-#pragma unroll
-            for (int r = 0; r < kSortPerThread; ++r) v[r] = __builtin_amdgcn_fmed3f(v[r], __shfl_xor(v[r], lanes), keep);
+            const bool lower = (tid & lanes) == 0;
+            switch (lanes) {                                   // wave-uniform
+            case 1: lane_stage<1, false>(v, lower); break;
+            case 2: lane_stage<2, false>(v, lower); break;
+            case 4: lane_stage<4, false>(v, lower); break;
+            case 8: lane_stage<8, false>(v, lower); break;
+            case 16: lane_stage<16, false>(v, lower); break;
+            default: lane_stage<32, false>(v, lower); break;
+            }
         }
 #pragma unroll
         for (int stride = kSortPerThread >> 1; stride > 0; stride >>= 1)
