@@ -39,10 +39,10 @@ __device__ __forceinline__ void cas(float& x, float& y)
     y = hi;
 }
 
-// Value of lane ^ M within the wave.  Partners inside a row of 16 lanes come
-// through DPP moves (quad permutations for ^1, ^2, ^3, the row mirrors for ^15
-// and ^7, two of them for ^4 = ^7^3 and ^8 = ^15^7); the others through the
-// LDS crossbar.
+// Value of lane ^ M within the wave: by a DPP move for ^1, ^2, ^3 (quad
+// permutations), ^7 and ^15 (the half-row and row mirrors); by the LDS
+// crossbar otherwise, a swizzle within 32 lanes for ^4, ^8, ^16 (no address
+// operand) and a permute for ^31, ^32, ^63.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {
@@ -56,10 +56,10 @@ __device__ __forceinline__ float lane_xor(float x)
     if constexpr (M == 1) return dpp<kQuadSwap1>(x);
     else if constexpr (M == 2) return dpp<kQuadSwap2>(x);
     else if constexpr (M == 3) return dpp<kQuadRev>(x);
-    else if constexpr (M == 4) return dpp<kQuadRev>(dpp<kHalfMirror>(x));
     else if constexpr (M == 7) return dpp<kHalfMirror>(x);
-    else if constexpr (M == 8) return dpp<kHalfMirror>(dpp<kRowMirror>(x));
     else if constexpr (M == 15) return dpp<kRowMirror>(x);
+    else if constexpr (M == 4 || M == 8 || M == 16)      // swizzle, bit-mask mode: lane ^ M within 32 lanes
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (M << 10) | 0x1F));
     else return __shfl_xor(x, M);
 }
 
