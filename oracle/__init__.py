@@ -52,6 +52,7 @@ def lib():
             "orc_quantize_custom": [vp, i32, i64, vp, i32, vp, vp],
             "orc_dequantize_custom": [vp, vp, vp, i32, i64, vp, i32],
             "orc_estimate_quantiles": [vp, i32, i64, i32, vp],
+            "orc_quantile_averages": [vp, i32, i64, i32, vp],
             "orc_optim8bit_step": [i32, vp, i32, vp, vp, i32, i64, vp, vp, vp, vp, i32, i32],
         }
         for name, argtypes in sig.items():
@@ -319,6 +320,17 @@ def dequantize_custom(codes, scale, cb, blocksize, n, ydt=F32):
     cb = np.ascontiguousarray(cb, dtype=np.float32)
     out = np.zeros(n, dtype=np.float32 if ydt == F32 else np.uint16)
     _check(lib().orc_dequantize_custom(_p(codes), _p(scale), _p(cb), blocksize, n, _p(out), ydt), "dequantize_custom")
+    return out
+
+
+def quantile_averages(x, chunk=QUANTILE_CHUNK, xdt=None):
+    """The 257 quantile estimates A_j of x (binary64): the exact mean over the
+    chunks of each chunk's order statistic at floor(j L / 257), rounded once."""
+    x = np.ascontiguousarray(x)
+    if xdt is None:
+        xdt = _dtype_id(x)
+    out = np.zeros(257, dtype=np.float64)
+    _check(lib().orc_quantile_averages(_p(x), xdt, x.size, chunk, _p(out)), "quantile_averages")
     return out
 
 

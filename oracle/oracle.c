@@ -901,29 +901,122 @@ static int cmp_float_asc(const void* a, const void* b)
 }
 
 /*
- * Quantile code estimated from data (reading of the pages' quantile
- * quantization and fast quantile estimation): the code entries are the
- * midpoints of adjacent quantiles at probabilities j/257, j = 0..256, of the
- * data, normalized so that the largest magnitude is 1.  The quantiles are
- * estimated fast by splitting x into chunks of C consecutive values (the last
- * may be shorter), sorting each chunk on its own and averaging the chunks'
- * order statistics:
- *   E_j(chunk of L sorted values s) = s[floor(j * L / 257)],
- *   A_j = (sum over groups of 256 consecutive chunks, in group order, of the
- *          group's sum of E_j in chunk order) / nchunks               (binary64),
- *   q_i = (A_i + A_{i+1}) / 2,  i = 0..255                           (binary64),
- *   code_i = binary32(q_i / max_k |q_k|)   (all 0 when max_k |q_k| = 0).
- * The entries come out ascending (A is non-decreasing); equal neighbours are
- * possible.  A negative zero in x counts as +0.
+ * Exact sums of binary32 values.  A finite binary32 f is m * 2^(e - 150) with
+ * an integer m < 2^24 and e = max(biased exponent, 1); exponent bin e - 1
+ * accumulates the signed m in int64 (exact for fewer than 2^39 values), so
+ * the sum is the exact integer N = sum_b bin[b] * 2^b, in units of 2^-149.
+ * N is held in two's complement in 16 little-endian 32-bit limbs (|N| < 2^320
+ * for the counts allowed here).
  */
-int orc_estimate_quantiles(const void* x, int xdt, int64_t n, int C, float* out /* [256] */)
+enum { BIG_LIMBS = 16 };
+
+static void f32_bin_add(int64_t* bins /* [254] */, float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t e = (u >> 23) & 0xFF;
+    int64_t m = (int64_t)((u & 0x7FFFFF) | (e ? 0x800000u : 0u));
+    bins[(e ? e : 1) - 1] += (u >> 31) ? -m : m;
+}
+
+/* big += v * 2^sh, v signed (two's complement add of the sign-extended value) */
+static void big_add_shifted(uint32_t* big, int64_t v, int sh)
+{
+    uint32_t add[BIG_LIMBS];
+    uint64_t uv = (uint64_t)v;
+    uint32_t ext = v < 0 ? 0xFFFFFFFFu : 0u;
+    for (int k = 0; k < BIG_LIMBS; k++) add[k] = ext;
+    /* place the 64-bit value at bit sh; limbs above it keep the sign extension */
+    int q = sh / 32, r = sh % 32;
+    for (int k = 0; k < q && k < BIG_LIMBS; k++) add[k] = 0;
+    uint32_t w0 = (uint32_t)uv, w1 = (uint32_t)(uv >> 32);
+    uint32_t parts[3];
+    parts[0] = w0 << r;
+    parts[1] = r ? ((w1 << r) | (w0 >> (32 - r))) : w1;
+    parts[2] = r ? ((ext << r) | (w1 >> (32 - r))) : ext;
+    for (int k = 0; k < 3 && q + k < BIG_LIMBS; k++) add[q + k] = parts[k];
+    uint64_t carry = 0;
+    for (int k = 0; k < BIG_LIMBS; k++) {
+        uint64_t s = (uint64_t)big[k] + add[k] + carry;
+        big[k] = (uint32_t)s;
+        carry = s >> 32;
+    }
+}
+
+/*
+ * The binary64 nearest (ties to even) to N * 2^-149 / d for the exact integer
+ * N (two's complement, destroyed) and 0 < d < 2^32.  |N| * 2^96 is divided by
+ * d in long division; the quotient Q has at least 65 bits when N != 0, so its
+ * top 53 bits, the next bit and a sticky bit (lower bits of Q, remainder)
+ * round it, and the result is (rounded Q) * 2^(shift - 245) in the normal
+ * range of binary64.
+ */
+static double big_div_rn64(uint32_t* big, uint32_t d)
+{
+    int neg = (big[BIG_LIMBS - 1] >> 31) != 0;
+    if (neg) {                                  /* magnitude: two's complement negation */
+        uint64_t carry = 1;
+        for (int k = 0; k < BIG_LIMBS; k++) {
+            uint64_t s = (uint64_t)(uint32_t)~big[k] + carry;
+            big[k] = (uint32_t)s;
+            carry = s >> 32;
+        }
+    }
+    uint32_t num[BIG_LIMBS + 3], quo[BIG_LIMBS + 3];
+    for (int k = 0; k < 3; k++) num[k] = 0;             /* times 2^96 */
+    for (int k = 0; k < BIG_LIMBS; k++) num[k + 3] = big[k];
+    uint64_t rem = 0;
+    for (int k = BIG_LIMBS + 2; k >= 0; k--) {
+        uint64_t cur = (rem << 32) | num[k];
+        quo[k] = (uint32_t)(cur / d);
+        rem = cur % d;
+    }
+    int top = BIG_LIMBS + 2;
+    while (top >= 0 && quo[top] == 0) top--;
+    if (top < 0) return 0.0;
+    int hb = 31;
+    while (!((quo[top] >> hb) & 1u)) hb--;
+    int bitlen = top * 32 + hb + 1;                     /* >= 65 */
+    int shift = bitlen - 53;
+    uint64_t sig = 0;
+    for (int b = bitlen - 1; b >= shift; b--) sig = (sig << 1) | ((quo[b / 32] >> (b % 32)) & 1u);
+    int guard = (quo[(shift - 1) / 32] >> ((shift - 1) % 32)) & 1u;
+    int sticky = rem != 0;
+    for (int b = 0; b < shift - 1 && !sticky; b++) sticky = (quo[b / 32] >> (b % 32)) & 1u;
+    if (guard && (sticky || (sig & 1u))) {
+        sig += 1;
+        if (sig == (1ull << 53)) {
+            sig >>= 1;
+            shift += 1;
+        }
+    }
+    double r = ldexp((double)sig, shift - 245);
+    return neg ? -r : r;
+}
+
+/*
+ * Quantile estimates of the data (reading of the pages' fast quantile
+ * estimation): x is split into chunks of C consecutive values (the last may
+ * be shorter), each chunk is sorted on its own, and the chunks' order
+ * statistics are averaged:
+ *   E_j(chunk of L sorted values s) = s[floor(j * L / 257)],  j = 0..256,
+ *   A_j = the exact arithmetic mean of E_j over the chunks, rounded once to
+ *         the nearest binary64 (ties to even), so it does not depend on the
+ *         order in which the chunks are added.
+ * A negative zero in x counts as +0.
+ */
+int orc_quantile_averages(const void* x, int xdt, int64_t n, int C, double* A /* [257] */)
 {
     if (n < 1 || C < 257) return -1;
     int64_t nch = (n + C - 1) / C;
-    double acc[257], grp[257];
-    for (int j = 0; j < 257; j++) acc[j] = grp[j] = 0.0;
+    if (nch >= ((int64_t)1 << 32)) return -1;
+    int64_t* bins = (int64_t*)calloc((size_t)257 * 254, sizeof(int64_t));
     float* s = (float*)malloc(sizeof(float) * (size_t)C);
-    if (!s) return -1;
+    if (!bins || !s) {
+        free(bins);
+        free(s);
+        return -1;
+    }
     for (int64_t c = 0; c < nch; c++) {
         int64_t lo = c * C, hi = lo + C < n ? lo + C : n;
         int L = (int)(hi - lo);
@@ -932,17 +1025,35 @@ int orc_estimate_quantiles(const void* x, int xdt, int64_t n, int C, float* out 
             s[i] = v == 0.0f ? 0.0f : v;       /* -0 counts as +0: the sort orders numbers */
         }
         qsort(s, (size_t)L, sizeof(float), cmp_float_asc);
-        for (int j = 0; j < 257; j++) grp[j] += (double)s[(int64_t)j * L / 257];
-        if (c % 256 == 255 || c == nch - 1) {          /* a group of 256 chunks ends */
-            for (int j = 0; j < 257; j++) {
-                acc[j] += grp[j];
-                grp[j] = 0.0;
-            }
-        }
+        for (int j = 0; j < 257; j++) f32_bin_add(bins + (size_t)j * 254, s[(int64_t)j * L / 257]);
     }
     free(s);
+    for (int j = 0; j < 257; j++) {
+        uint32_t big[BIG_LIMBS];
+        memset(big, 0, sizeof(big));
+        for (int b = 0; b < 254; b++)
+            if (bins[(size_t)j * 254 + b]) big_add_shifted(big, bins[(size_t)j * 254 + b], b);
+        A[j] = big_div_rn64(big, (uint32_t)nch);
+    }
+    free(bins);
+    return 0;
+}
+
+/*
+ * Quantile code estimated from data (reading of the pages' quantile
+ * quantization and fast quantile estimation): the code entries are the
+ * midpoints of adjacent quantile estimates A_j (orc_quantile_averages, at
+ * probabilities j/257), normalized so that the largest magnitude is 1:
+ *   q_i = (A_i + A_{i+1}) / 2,  i = 0..255                           (binary64),
+ *   code_i = binary32(q_i / max_k |q_k|)   (all 0 when max_k |q_k| = 0).
+ * The entries come out ascending (A is non-decreasing); equal neighbours are
+ * possible.
+ */
+int orc_estimate_quantiles(const void* x, int xdt, int64_t n, int C, float* out /* [256] */)
+{
     double A[257], q[256], m = 0.0;
-    for (int j = 0; j < 257; j++) A[j] = acc[j] / (double)nch;
+    int rc = orc_quantile_averages(x, xdt, n, C, A);
+    if (rc) return rc;
     for (int i = 0; i < 256; i++) {
         q[i] = (A[i] + A[i + 1]) * 0.5;
         if (fabs(q[i]) > m) m = fabs(q[i]);

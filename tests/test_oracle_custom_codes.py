@@ -82,6 +82,94 @@ def test_quantile_code_of_a_uniform_grid_closed_form():
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), chunk
 
 
+def _chunk_stats(x, C):
+    """Each chunk's order statistics s[floor(j L / 257)], j = 0..256, from
+    numpy's sort (an independent library routine); -0 counts as +0."""
+    x = np.where(x == 0, np.float32(0.0), x).astype(np.float32)
+    out = []
+    for lo in range(0, x.size, C):
+        s = np.sort(x[lo:lo + C])
+        L = s.size
+        out.append([s[j * L // 257] for j in range(257)])
+    return np.array(out, dtype=np.float32)
+
+
+def _exact_means(E):
+    """Exact rational mean of each column, rounded once to binary64 (CPython's
+    int / int division is correctly rounded)."""
+    nch = E.shape[0]
+    A = []
+    for j in range(E.shape[1]):
+        s = sum((Fraction(float(v)) for v in E[:, j]), Fraction(0))
+        A.append(s.numerator / (s.denominator * nch))
+    return np.array(A, dtype=np.float64)
+
+
+def _code_from_averages(A):
+    q = [(A[i] + A[i + 1]) * 0.5 for i in range(256)]
+    m = max(abs(v) for v in q)
+    return np.array([np.float32(v / m) if m > 0 else np.float32(0.0) for v in q], dtype=np.float32)
+
+
+def test_quantile_averages_are_exact_means_beyond_256_chunks():
+    """601 chunks (the last ragged) of values spread over 2^-60 .. 2^60 with
+    both signs, zeros and -0: every A_j equals the exact mean rounded once,
+    while a plain binary64 sum in chunk order misses it for some j."""
+    rng = np.random.default_rng(11)
+    C = 257
+    n = C * 600 + 100
+    mag = np.ldexp(rng.uniform(1.0, 2.0, n), rng.integers(-60, 61, n))
+    x = (mag * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+    x[rng.integers(0, n, 500)] = 0.0
+    x[rng.integers(0, n, 500)] = -0.0
+    E = _chunk_stats(x, C)
+    assert E.shape[0] == 601
+    want = _exact_means(E)
+    got = oracle.quantile_averages(x, chunk=C)
+    assert np.array_equal(got.view(np.uint64), want.view(np.uint64))
+    naive = np.array([sum(float(v) for v in E[:, j]) / E.shape[0] for j in range(257)])
+    assert np.any(naive != want), "the data must separate the exact mean from a plain sum"
+    assert np.array_equal(oracle.estimate_quantiles(x, chunk=C).view(np.uint32),
+                          _code_from_averages(want).view(np.uint32))
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_quantile_averages_of_16_bit_inputs(xdt):
+    rng = np.random.default_rng(12)
+    C = 300
+    x32 = (rng.standard_t(3, C * 270 + 17) * 0.02).astype(np.float32)
+    if xdt == "f16":
+        h = x32.astype(np.float16)
+        bits, dt, widened = h.view(np.uint16), oracle.F16, h.astype(np.float32)
+    else:
+        bits = oracle.f32_to_bf16_bits(x32)
+        dt = oracle.BF16
+        widened = (bits.astype(np.uint32) << 16).view(np.float32)
+    want = _exact_means(_chunk_stats(widened, C))
+    got = oracle.quantile_averages(bits, chunk=C, xdt=dt)
+    assert np.array_equal(got.view(np.uint64), want.view(np.uint64))
+
+
+def test_quantile_average_rounding_and_order():
+    C = 257
+    one = np.full(C, 1.0, np.float32)
+    # (1 + 2^-53) / 2 = 0.5 + 2^-54 lies halfway between 0.5 and its successor: to even, 0.5
+    A = oracle.quantile_averages(np.concatenate([one, np.full(C, 2.0 ** -53, np.float32)]), chunk=C)
+    assert np.all(A == 0.5)
+    # (1 + 3 2^-53) / 2 = 0.5 + 1.5 ulp: halfway between 0.5 + 1 ulp (odd) and 0.5 + 2 ulp (even)
+    A = oracle.quantile_averages(np.concatenate([one, np.full(C, 3 * 2.0 ** -53, np.float32)]), chunk=C)
+    assert np.all(A == 0.5 + 2.0 ** -52)
+    # 2^60, 2^-60, -2^60 in this chunk order: a running binary64 sum loses 2^-60
+    big, tiny = np.float32(2.0 ** 60), np.float32(2.0 ** -60)
+    x = np.concatenate([np.full(C, big), np.full(C, tiny), np.full(C, -big)]).astype(np.float32)
+    A = oracle.quantile_averages(x, chunk=C)
+    assert np.all(A == float(Fraction(2) ** -60 / 3))
+    # means cancel exactly to zero: every entry of the code is then 0
+    x = np.concatenate([np.full(C, big), np.full(C, -big)]).astype(np.float32)
+    assert np.all(oracle.quantile_averages(x, chunk=C) == 0.0)
+    assert np.all(oracle.estimate_quantiles(x, chunk=C) == 0.0)
+
+
 def test_quantile_code_invariances():
     rng = np.random.default_rng(8)
     C = oracle.QUANTILE_CHUNK
