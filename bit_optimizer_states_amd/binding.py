@@ -11,8 +11,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# QB_LIBRARY may name another build of the same library (tuning builds)
-LIB_PATH = os.environ.get("QB_LIBRARY") or os.path.join(_HERE, "libqb.so")
+# always the in-tree build: no environment variable can point the binding at
+# another library
+LIB_PATH = os.path.join(_HERE, "libqb.so")
 
 QB_OK, QB_EINVAL, QB_EALIGN, QB_EUNSUPPORTED, QB_EHIP, QB_EWORKSPACE, QB_EINIT = range(7)
 QB_F32, QB_F16, QB_BF16 = 0, 1, 2
@@ -65,6 +66,11 @@ class qb_dequant_tensor(ctypes.Structure):
 _lib = None
 
 
+def loaded_path():
+    """Real path of the shared object the binding has loaded (None before lib())."""
+    return None if _lib is None else os.path.realpath(_lib._name)
+
+
 def lib():
     """The loaded libqb.so (raises OSError if it has not been built)."""
     global _lib
@@ -99,9 +105,10 @@ def lib():
         L.qb_linear_code.argtypes = [vp]
         L.qb_linear_code.restype = i32
         L.qb_prepare_code.argtypes = [vp, vp, vp]
+        L.qb_normalize.argtypes = [vp, i32, i64, vp, i32, vp, vp]
         L.qb_quantile_workspace_bytes.argtypes = [i64]
         L.qb_quantile_workspace_bytes.restype = sz
-        L.qb_estimate_quantiles.argtypes = [vp, i32, i64, vp, vp, sz, vp]
+        L.qb_estimate_quantiles.argtypes = [vp, i32, i64, vp, vp, vp, sz, vp]
         L.qb_quantize_code.argtypes = [vp, i32, i64, vp, i32, vp, vp, vp]
         L.qb_dequantize_code.argtypes = [vp, vp, vp, i32, i64, vp, i32, vp]
         L.qb_multi_tensor_quantize.argtypes = [ctypes.POINTER(qb_quant_tensor), i32, i32, i32, i32, i32, vp, sz, vp]
@@ -110,7 +117,7 @@ def lib():
         for f in (L.qb_quantize, L.qb_dequantize, L.qb_adamw8bit_step, L.qb_multi_tensor_step,
                   L.qb_multi_tensor_dequantize, L.qb_multi_tensor_quantize, L.qb_optimizer8bit_step,
                   L.qb_multi_tensor_optimizer_step, L.qb_prepare_code, L.qb_estimate_quantiles, L.qb_quantize_code,
-                  L.qb_dequantize_code):
+                  L.qb_dequantize_code, L.qb_normalize):
             f.restype = ctypes.c_int
         L.qb_dq_workspace_bytes.argtypes = [i64, i32]
         L.qb_dq_workspace_bytes.restype = sz
@@ -336,12 +343,17 @@ def qb_prepare_code(values, table, stream=None):
     _check(lib().qb_prepare_code(arr, _ptr(table), _stream(stream)), "qb_prepare_code")
 
 
+def qb_normalize(x, n, absmax, blocksize, out, stream=None):
+    _check(lib().qb_normalize(_ptr(x), _dtype(x), int(n), _ptr(absmax), int(blocksize), _ptr(out), _stream(stream)),
+           "qb_normalize")
+
+
 def qb_quantile_workspace_bytes(n):
     return lib().qb_quantile_workspace_bytes(int(n))
 
 
-def qb_estimate_quantiles(x, n, table, ws, stream=None):
-    _check(lib().qb_estimate_quantiles(_ptr(x), _dtype(x), int(n), _ptr(table), _ptr(ws),
+def qb_estimate_quantiles(x, n, table, ws, averages=None, stream=None):
+    _check(lib().qb_estimate_quantiles(_ptr(x), _dtype(x), int(n), _ptr(table), _ptr(averages), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream(stream)), "qb_estimate_quantiles")
 
 

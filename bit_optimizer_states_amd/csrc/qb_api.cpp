@@ -449,6 +449,17 @@ qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int3
     return hip_status(e);
 }
 
+qb_status qb_normalize(const void* x, qb_dtype xdt, int64_t n, const float* absmax, int32_t blocksize, float* out,
+                       void* stream)
+{
+    if (n < 0 || !valid_dtype(xdt) || blocksize < 1) return QB_EINVAL;
+    if (n == 0) return QB_OK;
+    if (!x || !absmax || !out) return QB_EINVAL;
+    if (!aligned16(x) || !aligned16(absmax) || !aligned16(out)) return QB_EALIGN;
+    if ((n + 255) / 256 >= (int64_t(1) << 31)) return QB_EINVAL;
+    return hip_status(launch_normalize(x, (int)xdt, n, absmax, blocksize, out, static_cast<hipStream_t>(stream)));
+}
+
 size_t qb_multi_tensor_quantize_workspace_bytes(const qb_quant_tensor* tensors, int32_t count, int32_t blocksize)
 {
     if (count <= 0 || !tensors || !pow2_block(blocksize)) return 0;
@@ -661,28 +672,27 @@ qb_status qb_dequantize_code(const uint8_t* codes, const float* absmax, const vo
 
 size_t qb_quantile_workspace_bytes(int64_t n)
 {
-    // the chunks' order statistics (float [257][nchunks]), then the group sums
-    // (double [257][ngroups], groups of 256 chunks)
+    // the chunks' order statistics (float [257][nchunks]), then their means
+    // (double [257])
     if (n <= 0) return 0;
     const int64_t nchunks = (n + kQuantileChunk - 1) / kQuantileChunk;
-    const int64_t ngroups = (nchunks + 255) / 256;
-    return round_up((size_t)nchunks * 257 * sizeof(float), 256) + (size_t)ngroups * 257 * sizeof(double);
+    return round_up((size_t)nchunks * 257 * sizeof(float), 256) + 257 * sizeof(double);
 }
 
-qb_status qb_estimate_quantiles(const void* x, qb_dtype xdt, int64_t n, void* table, void* ws, size_t ws_bytes,
-                                void* stream)
+qb_status qb_estimate_quantiles(const void* x, qb_dtype xdt, int64_t n, void* table, double* averages, void* ws,
+                                size_t ws_bytes, void* stream)
 {
     if (n < 1 || !valid_dtype(xdt)) return QB_EINVAL;
     if (!x || !table || !ws) return QB_EINVAL;
-    if (!aligned16(x) || !aligned16(table) || !aligned16(ws)) return QB_EALIGN;
+    if (!aligned16(x) || !aligned16(table) || !aligned16(ws) || (averages && !aligned16(averages))) return QB_EALIGN;
     if ((n + kQuantileChunk - 1) / kQuantileChunk >= (int64_t(1) << 31)) return QB_EINVAL;
     if (ws_bytes < qb_quantile_workspace_bytes(n)) return QB_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t nchunks = (n + kQuantileChunk - 1) / kQuantileChunk;
     float* E = static_cast<float*>(ws);
-    double* S = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up((size_t)nchunks * 257 * sizeof(float), 256));
+    double* A = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up((size_t)nchunks * 257 * sizeof(float), 256));
     hipError_t e = launch_chunk_quantiles(x, (int)xdt, n, E, s);
-    if (e == hipSuccess) e = launch_quantile_code(E, nchunks, S, static_cast<UserCode*>(table), s);
+    if (e == hipSuccess) e = launch_quantile_code(E, nchunks, A, averages, static_cast<UserCode*>(table), s);
     return hip_status(e);
 }
 

@@ -9,13 +9,14 @@
 //      sorts the chunk (bitonic network: 16 values per thread in registers,
 //      lane shuffles within a wave, LDS only across waves) and keeps its 257 order
 //      statistics s[floor(j L / 257)] (L = the chunk's length);
-//   2. k_quantile_groups sums each statistic over groups of 256 consecutive
-//      chunks (binary64, chunk order), and k_quantile_code sums the groups in
-//      group order, divides by the chunk count, forms the midpoints,
-//      normalizes them and writes the code with its decision thresholds and
-//      their bucket index.
+//   2. k_quantile_means: one workgroup per statistic j adds its chunks'
+//      values exactly (integer sums of the significands per binary exponent)
+//      and divides once: A_j = the exact mean, rounded to nearest-even
+//      binary64, whatever the order of the additions;
+//   3. k_quantile_code forms the midpoints, normalizes them and writes the
+//      code with its decision thresholds and their bucket index.
 // Every step is exact or a fixed sequence of IEEE operations, so the result is
-// the same bits on every run (and as the oracle's).
+// the same bits on every run.
 #include "qb_device.h"
 
 namespace qb {
@@ -23,7 +24,7 @@ namespace qb {
 namespace {
 
 constexpr int kSortPerThread = kQuantileChunk / kThreads;   // 16 consecutive elements per thread
-constexpr int kGroup = 256;                                  // chunks per first-level sum
+constexpr int kExpBins = 254;                                // binary32 exponents 1..254 (0 joins 1)
 constexpr int kWaveElems = 64 * kSortPerThread;              // 1024 elements per wave
 constexpr int kWaveShift = 10;
 
@@ -188,19 +189,136 @@ __global__ __launch_bounds__(kThreads) void k_chunk_quantiles(const void* __rest
     for (int j = tid; j < 257; j += kThreads) E[(int64_t)j * nchunks + c] = s[slot((int)((int64_t)j * L / 257))];
 }
 
-// First-level sums: workgroup g adds, for every statistic j, its group's
-// chunks g*256 .. in chunk order (binary64).
-__global__ __launch_bounds__(kThreads) void k_quantile_groups(const float* __restrict__ E, int64_t nchunks,
-                                                              double* __restrict__ S)
+// ---------------------------------------------------------------------------
+// exact mean of each statistic over the chunks
+// ---------------------------------------------------------------------------
+
+// Bits [pos, pos + 128) of the non-negative integer w[0..5] (64-bit words,
+// little-endian), pos >= 0.
+__device__ unsigned __int128 bits128(const unsigned long long* w, int pos)
 {
-    const int64_t g = blockIdx.x, ngroups = gridDim.x;
-    const int64_t c0 = g * kGroup, c1 = c0 + kGroup < nchunks ? c0 + kGroup : nchunks;
-    for (int j = threadIdx.x; j < 257; j += kThreads) {
-        const float* row = E + (int64_t)j * nchunks;
-        double acc = 0.0;
-        for (int64_t c = c0; c < c1; ++c) acc += (double)row[c];
-        S[(int64_t)j * ngroups + g] = acc;
+    unsigned __int128 r = 0;
+    for (int k = 0; k < 2; ++k) {
+        const int b = pos + 64 * k, q = b >> 6, s = b & 63;
+        unsigned long long v = q < 6 ? (w[q] >> s) : 0ull;
+        if (s && q + 1 < 6) v |= w[q + 1] << (64 - s);
+        r |= (unsigned __int128)v << (64 * k);
     }
+    return r;
+}
+
+// N 2^-149 / count rounded once to nearest-even binary64, for the integer
+// N = sum_b bins[b] 2^b (signed bins) and 0 < count < 2^31.  One thread.
+// |N| < 2^310 is formed exactly in 384-bit two's complement; its top 96 bits
+// W (shifted up when |N| is shorter) are divided by count, which leaves a
+// quotient Q of at least 64 bits; Q's top 53 bits, the next one and a sticky
+// bit (Q's lower bits, the remainder, |N|'s bits below the window) round it.
+__device__ double mean_rn64(const long long* bins, const unsigned long long* mask, uint32_t count)
+{
+    unsigned long long w[6] = {0, 0, 0, 0, 0, 0};
+    for (int q = 0; q < 4; ++q) {
+        unsigned long long mk = mask[q];
+        while (mk) {
+            const int b = q * 64 + __ffsll((long long)mk) - 1;
+            mk &= mk - 1;
+            const long long v = bins[b];
+            const unsigned long long ext = v < 0 ? ~0ull : 0ull;   // sign extension above the value
+            const int wi = b >> 6, s = b & 63;
+            const unsigned long long part[3] = {(unsigned long long)v << s,
+                                                s ? ((unsigned long long)v >> (64 - s)) | (ext << s) : ext, ext};
+            unsigned long long carry = 0;
+            for (int k = wi; k < 6; ++k) {
+                const unsigned long long add = k - wi < 3 ? part[k - wi] : ext;
+                const unsigned long long t = w[k] + add;
+                const unsigned long long c1 = t < w[k] ? 1ull : 0ull;
+                w[k] = t + carry;
+                carry = c1 + (w[k] < t ? 1ull : 0ull);
+            }
+        }
+    }
+    const bool neg = (w[5] >> 63) != 0;
+    if (neg) {                                                   // magnitude
+        unsigned long long carry = 1;
+        for (int k = 0; k < 6; ++k) {
+            w[k] = ~w[k] + carry;
+            carry = (carry && w[k] == 0) ? 1ull : 0ull;
+        }
+    }
+    int top = 5;
+    while (top >= 0 && w[top] == 0) --top;
+    if (top < 0) return 0.0;
+    const int L = top * 64 + 63 - __clzll((long long)w[top]);   // top set bit of |N|
+    const int sh = L - 95;                                       // window [sh, sh + 96)
+    unsigned __int128 W;
+    bool low_nz = false;
+    if (sh >= 0) {
+        W = bits128(w, sh) & ((((unsigned __int128)1) << 96) - 1);
+        for (int q = 0; q < 6 && q * 64 < sh; ++q) {
+            const int nbits = sh - q * 64;
+            const unsigned long long mk = nbits >= 64 ? ~0ull : ((1ull << nbits) - 1ull);
+            if (w[q] & mk) low_nz = true;
+        }
+    } else {
+        W = bits128(w, 0) << (-sh);                             // |N| < 2^95: exact
+    }
+    const uint32_t l2 = (uint32_t)(W >> 64), l1 = (uint32_t)(W >> 32), l0 = (uint32_t)W;
+    unsigned long long cur = l2;
+    const unsigned long long q2 = cur / count;
+    unsigned long long r = cur % count;
+    cur = (r << 32) | l1;
+    const unsigned long long q1 = cur / count;
+    r = cur % count;
+    cur = (r << 32) | l0;
+    const unsigned long long q0 = cur / count;
+    r = cur % count;
+    const unsigned __int128 Q = ((unsigned __int128)q2 << 64) + ((unsigned __int128)q1 << 32) + q0;
+    const unsigned long long qhi = (unsigned long long)(Q >> 64), qlo = (unsigned long long)Q;
+    const int H = qhi ? 64 + 63 - __clzll((long long)qhi) : 63 - __clzll((long long)qlo);   // >= 64
+    const int srel = H - 52;
+    const unsigned long long mant = (unsigned long long)(Q >> srel);
+    const bool guard = (unsigned long long)(Q >> (srel - 1)) & 1ull;
+    const unsigned __int128 below = Q & ((((unsigned __int128)1) << (srel - 1)) - 1);
+    const bool up = guard && (below != 0 || r != 0 || low_nz || (mant & 1ull));
+    // value = (mant + up) 2^(srel + sh - 149); the implicit bit of mant
+    // carries into the exponent field
+    const unsigned long long bits = ((unsigned long long)(srel + sh + 925) << 52) + mant + (up ? 1ull : 0ull);
+    const double a = __longlong_as_double((long long)bits);
+    return neg ? -a : a;
+}
+
+// Workgroup j: A[j] = the exact mean of E[j][0 .. nchunks), rounded once.
+// Each thread adds its chunks' significands (signed) into a running sum per
+// exponent, flushing to the LDS bins when the exponent changes; the bins are
+// 64-bit integers, so every order of additions gives the same sums.
+__global__ __launch_bounds__(kThreads) void k_quantile_means(const float* __restrict__ E, int64_t nchunks,
+                                                             double* __restrict__ A)
+{
+    __shared__ long long s_bins[256];
+    __shared__ unsigned long long s_mask[4];
+    const int tid = threadIdx.x;
+    s_bins[tid] = 0;
+    __syncthreads();
+    const float* row = E + (int64_t)blockIdx.x * nchunks;
+    int cur = -1;
+    long long acc = 0;
+    for (int64_t c = tid; c < nchunks; c += kThreads) {
+        const uint32_t u = fbits(row[c]);
+        const uint32_t e = (u >> 23) & 0xFFu;
+        const long long m = (long long)((u & 0x7FFFFFu) | (e ? 0x800000u : 0u));
+        const int b = (int)(e ? e : 1u) - 1;
+        if (b != cur) {
+            if (acc) atomicAdd((unsigned long long*)&s_bins[cur], (unsigned long long)acc);
+            cur = b;
+            acc = 0;
+        }
+        acc += (u >> 31) ? -m : m;
+    }
+    if (acc) atomicAdd((unsigned long long*)&s_bins[cur], (unsigned long long)acc);
+    __syncthreads();
+    const unsigned long long mk = __ballot(tid < kExpBins && s_bins[tid] != 0);
+    if ((tid & 63) == 0) s_mask[tid >> 6] = mk;
+    __syncthreads();
+    if (tid == 0) A[blockIdx.x] = mean_rn64(s_bins, s_mask, (uint32_t)nchunks);
 }
 
 // The next binary32 above finite f (above +-0: the smallest subnormal).
@@ -218,8 +336,8 @@ __device__ float ceil_f32(double d, bool strict)
     return f;
 }
 
-__global__ __launch_bounds__(kThreads) void k_quantile_code(const double* __restrict__ S, int64_t ngroups,
-                                                            int64_t nchunks, UserCode* __restrict__ out)
+__global__ __launch_bounds__(kThreads) void k_quantile_code(const double* __restrict__ Ag,
+                                                            double* __restrict__ averages, UserCode* __restrict__ out)
 {
     __shared__ double A[257];
     __shared__ double q[256];
@@ -228,10 +346,8 @@ __global__ __launch_bounds__(kThreads) void k_quantile_code(const double* __rest
     __shared__ int fb[256];
     const int tid = threadIdx.x;
     for (int j = tid; j < 257; j += kThreads) {
-        const double* row = S + (int64_t)j * ngroups;
-        double acc = 0.0;
-        for (int64_t g = 0; g < ngroups; ++g) acc += row[g];
-        A[j] = acc / (double)nchunks;
+        A[j] = Ag[j];
+        if (averages) averages[j] = A[j];
     }
     __syncthreads();
     const double qi = (A[tid] + A[tid + 1]) * 0.5;
@@ -290,12 +406,12 @@ hipError_t launch_chunk_quantiles(const void* x, int xdt, int64_t n, float* E, h
     }
 }
 
-hipError_t launch_quantile_code(const float* E, int64_t nchunks, double* S, UserCode* out, hipStream_t s)
+hipError_t launch_quantile_code(const float* E, int64_t nchunks, double* A, double* averages, UserCode* out,
+                                hipStream_t s)
 {
-    const int64_t ngroups = (nchunks + kGroup - 1) / kGroup;
-    hipError_t e = launch_kernel(k_quantile_groups, (int)ngroups, s, E, nchunks, S);
+    hipError_t e = launch_kernel(k_quantile_means, 257, s, E, nchunks, A);
     if (e != hipSuccess) return e;
-    return launch_kernel(k_quantile_code, 1, s, (const double*)S, ngroups, nchunks, out);
+    return launch_kernel(k_quantile_code, 1, s, (const double*)A, averages, out);
 }
 
 }  // namespace qb

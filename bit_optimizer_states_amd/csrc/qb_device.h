@@ -348,6 +348,14 @@ __device__ __forceinline__ bool fast_div_ok(float a)
     return a >= 0x1p-60f && a <= 0x1p60f;
 }
 
+// n = x / a as every encoder takes it (|x| <= a): the correctly rounded
+// quotient, 0 when a == 0.  `fast` = fast_div_ok(a), r = rcp_rn(a), both once
+// per block.
+__device__ __forceinline__ float normalize_by_block(float x, float a, float r, bool fast)
+{
+    return fast ? div_by_block(x, a, r) : (a > 0.0f ? x / a : 0.0f);
+}
+
 // RN(1/a) for 2^-60 <= a <= 2^60: the hardware reciprocal (about 1 ulp) and
 // one Newton step with fused multiply-adds.  Checked on gfx950 against the
 // IEEE quotient 1.0f / a for every significand at exponents -60, -20, -1, 0,

@@ -178,8 +178,11 @@ hipError_t launch_dequant_user(const DequantDesc& d, int64_t ntiles, int B, int 
 // sorted on its own; E holds 257 order statistics per chunk ([257][nchunks]),
 // S the binary64 sums per group of 256 chunks ([257][ngroups]).
 constexpr int kQuantileChunk = 4096;
+hipError_t launch_normalize(const void* x, int xdt, int64_t n, const float* absmax, int64_t B, float* out,
+                            hipStream_t s);
 hipError_t launch_chunk_quantiles(const void* x, int xdt, int64_t n, float* E, hipStream_t s);
-hipError_t launch_quantile_code(const float* E, int64_t nchunks, double* S, UserCode* out, hipStream_t s);
+hipError_t launch_quantile_code(const float* E, int64_t nchunks, double* A, double* averages, UserCode* out,
+                                hipStream_t s);
 
 // y [M, N] = x [M, K] W^T in compute dtype xdt (fp32, fp16, bf16; y the same),
 // W [N, K] as 4-bit codes (code4: 0 NF4, 1 FP4) with block size B and either

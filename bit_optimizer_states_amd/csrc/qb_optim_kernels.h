@@ -476,11 +476,11 @@ __global__ __launch_bounds__(kAdamThreads) void k_optim8(TensorDesc single, Tile
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float mm = m1[c * 4 + j];
-                const float nm = fm ? div_by_block(mm, am1, rm) : (am1 > 0.0f ? mm / am1 : 0.0f);
+                const float nm = normalize_by_block(mm, am1, rm, fm);
                 wm |= enc_x(nm) << (8 * j);
                 if constexpr (TWO) {
                     const float vv = v1[c * 4 + j];
-                    const float nv = fv ? div_by_block(vv, av1, rv) : (av1 > 0.0f ? vv / av1 : 0.0f);
+                    const float nv = normalize_by_block(vv, av1, rv, fv);
                     wv |= enc_y(nv) << (8 * j);
                 }
             }

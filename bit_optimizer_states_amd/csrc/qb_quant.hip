@@ -314,8 +314,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
             for (int i = 0; i < G::EPT; ++i) nv[i] = div_by_block(vr[i], a, rc);
         } else {
 #pragma unroll
-            for (int i = 0; i < G::EPT; ++i)
-                nv[i] = fast ? div_by_block(vr[i], a, rc) : (a > 0.0f ? vr[i] / a : 0.0f);
+            for (int i = 0; i < G::EPT; ++i) nv[i] = normalize_by_block(vr[i], a, rc, fast);
         }
 #pragma unroll
         for (int c = 0; c < G::CH; ++c) {
@@ -482,6 +481,42 @@ hipError_t launch_quant_user(const QuantDesc& d, int64_t ntiles, int B, int xdt,
     case 1024: return quant_user_x<1024>(xdt, d, ntiles, code, s);
     case 2048: return quant_user_x<2048>(xdt, d, ntiles, code, s);
     case 4096: return quant_user_x<4096>(xdt, d, ntiles, code, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+namespace {
+
+// The normalized values of block-wise quantization, one element per thread:
+// out[i] = x[i] / absmax[i / B] through the quantize kernels' own quotient
+// (normalize_by_block with the block's rcp_rn and range test).  The
+// correction step turns a quotient -0 into +0 (the encoders take both to the
+// code of 0.0); here a zero quotient takes the sign of x, as IEEE division
+// gives it.
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void k_normalize(const void* __restrict__ x, int64_t n,
+                                                        const float* __restrict__ absmax, int64_t B,
+                                                        float* __restrict__ out)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const float a = absmax[i / B];
+    const float xv = load1<XDT>(x, i);
+    const float nv = normalize_by_block(xv, a, rcp_rn(a), fast_div_ok(a));
+    out[i] = a > 0.0f ? __builtin_copysignf(nv, xv) : nv;
+}
+
+}  // namespace
+
+hipError_t launch_normalize(const void* x, int xdt, int64_t n, const float* absmax, int64_t B, float* out,
+                            hipStream_t s)
+{
+    const int64_t grid = (n + kThreads - 1) / kThreads;
+    if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    switch (xdt) {
+    case DT_F32: return launch_kernel(k_normalize<DT_F32>, (int)grid, s, x, n, absmax, B, out);
+    case DT_F16: return launch_kernel(k_normalize<DT_F16>, (int)grid, s, x, n, absmax, B, out);
+    case DT_BF16: return launch_kernel(k_normalize<DT_BF16>, (int)grid, s, x, n, absmax, B, out);
     default: return hipErrorInvalidValue;
     }
 }

@@ -31,9 +31,11 @@
  *
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers unless marked "host".  The caller
- *     owns every buffer: libqb never allocates device memory, keeps no state
- *     between calls except its constant tables, and is safe to call from
- *     several host threads.
+ *     owns every buffer: libqb never allocates device memory and keeps no state
+ *     between calls except its constant tables.  Every entry point is safe to
+ *     call from several host threads at once, with one exception:
+ *     qb_paged_optimizer_step, whose calls on one device share internal copy
+ *     streams and events and must not overlap in time (see its description).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; no entry point synchronizes the device.
  *   - Arguments are validated before anything is enqueued; on any error
@@ -235,6 +237,26 @@ typedef struct {
  */
 qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int32_t blocksize,
                       uint8_t* codes, float* absmax, const qb_dq* dq, void* stream);
+
+/*
+ * qb_normalize -- the normalized values of block-wise quantization, the step
+ * between the block absmax and the encoding (each block is scaled by its own
+ * absmax: "8-bit Optimizers via Block-wise Quantization" abstract, quoted on
+ * page "Py之bitsandbytes", section 2), computed by the quantize kernels' own
+ * quotient: out[i] = RN(x[i] / absmax[i / blocksize]) in binary32, equal to
+ * IEEE division bit for bit (a zero x keeps its sign), and +0 where that
+ * absmax is 0.  For inspection, e.g. counting values that lie within an ulp
+ * of a code midpoint.
+ *   x          [n] of dtype xdt.
+ *   absmax     [ceil(n/blocksize)] fp32, finite, >= 0, with |x[i]| <=
+ *              absmax[i / blocksize] (as qb_quantize writes it); other values
+ *              give unspecified results.
+ *   blocksize  any value >= 1 (1: one absmax per element).
+ *   out        [n] fp32, fully overwritten.
+ * One kernel.  QB_EINVAL for n < 0, blocksize < 1 or a NULL pointer with n > 0.
+ */
+qb_status qb_normalize(const void* x, qb_dtype xdt, int64_t n, const float* absmax, int32_t blocksize, float* out,
+                       void* stream);
 
 /*
  * qb_multi_tensor_quantize -- qb_quantize on `count` tensors (same input
@@ -446,13 +468,16 @@ size_t qb_paged_workspace_bytes(int64_t page_params, int32_t blocksize);
  *                       QB_EINVAL) -> device table, copied on `stream`.
  *   qb_estimate_quantiles
  *                       device: the quantile code of x[n] straight into a
- *                       device table.  Entries = midpoints of adjacent
- *                       quantiles at j/257 (j = 0..256), normalized to a largest
- *                       magnitude of 1.  The quantiles are averaged in binary64
- *                       over chunks of 4096 consecutive values, each sorted on its
- *                       own (the chunk's order statistic at floor(j L / 257); -0
- *                       counts as +0), summed per group of 256 chunks and then
- *                       over the groups, each in order.  Deterministic.  ws:
+ *                       device table.  The quantiles at j/257 (j = 0..256) are
+ *                       estimated over chunks of 4096 consecutive values, each
+ *                       sorted on its own (the chunk's order statistic at
+ *                       floor(j L / 257), L its length; -0 counts as +0): A_j is
+ *                       the exact mean of the chunks' statistics, rounded once
+ *                       to nearest-even binary64.  Entries = binary32 of
+ *                       q_i / max|q| with q_i = (A_i + A_{i+1}) / 2 (binary64).
+ *                       Deterministic, and independent of the order of the
+ *                       chunks' additions.  averages: NULL, or device double[257]
+ *                       (16-byte aligned) that receives A.  ws:
  *                       qb_quantile_workspace_bytes(n) bytes.  Three kernels.
  *   qb_quantize_code / qb_dequantize_code
  *                       as qb_quantize / qb_dequantize with 8-bit codes (codes:
@@ -462,8 +487,8 @@ size_t    qb_code_table_bytes(void);
 int32_t   qb_linear_code(float* out);
 qb_status qb_prepare_code(const float* values, void* table, void* stream);
 size_t    qb_quantile_workspace_bytes(int64_t n);
-qb_status qb_estimate_quantiles(const void* x, qb_dtype xdt, int64_t n, void* table, void* ws, size_t ws_bytes,
-                                void* stream);
+qb_status qb_estimate_quantiles(const void* x, qb_dtype xdt, int64_t n, void* table, double* averages, void* ws,
+                                size_t ws_bytes, void* stream);
 qb_status qb_quantize_code(const void* x, qb_dtype xdt, int64_t n, const void* table, int32_t blocksize,
                            uint8_t* codes, float* absmax, void* stream);
 qb_status qb_dequantize_code(const uint8_t* codes, const float* absmax, const void* table, int32_t blocksize,

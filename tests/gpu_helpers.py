@@ -1,18 +1,25 @@
 """Helpers for the GPU parity tests: run the HIP path through the C ABI and
 bring results back to the host; the oracle runs on host copies of the same
 input bytes."""
+import os
+
 import numpy as np
 import torch
 
 import oracle
 
 DEV = "cuda:0"
+IN_TREE_LIB = os.path.realpath(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                            "bit_optimizer_states_amd", "libqb.so"))
 TORCH_DT = {oracle.F32: torch.float32, oracle.F16: torch.float16, oracle.BF16: torch.bfloat16}
 
 
 def qb():
+    """The binding, with the in-tree libqb.so loaded (asserted: the parity
+    evidence must come from the library built from these sources)."""
     from bit_optimizer_states_amd import binding
     binding.lib()
+    assert binding.loaded_path() == IN_TREE_LIB, f"loaded {binding.loaded_path()}, expected {IN_TREE_LIB}"
     return binding
 
 

@@ -107,15 +107,39 @@ def test_estimated_quantile_code_equals_oracle(n, dt):
     xd = to_device(xh, TORCH_DT[dt])
     t = torch.empty(L.qb_code_table_bytes(), dtype=torch.uint8, device=DEV)
     ws = torch.empty(L.qb_quantile_workspace_bytes(n), dtype=torch.uint8, device=DEV)
-    L.qb_estimate_quantiles(xd, n, t, ws)
+    avg = torch.empty(257, dtype=torch.float64, device=DEV)
+    L.qb_estimate_quantiles(xd, n, t, ws, averages=avg)
     vals, thr = read_table(t)
     want = oracle.estimate_quantiles(xh, xdt=dt)
     assert np.array_equal(vals.view(np.uint32), want.view(np.uint32))
+    want_avg = oracle.quantile_averages(xh, xdt=dt)
+    assert np.array_equal(avg.cpu().numpy().view(np.uint64), want_avg.view(np.uint64))
     # the device thresholds and bucket index are the host's for the same entries
     host_t = table_of(vals)
     _, host_thr = read_table(host_t)
     assert np.array_equal(thr.view(np.uint32), host_thr.view(np.uint32))
     assert np.array_equal(bucket_index(t), bucket_index(host_t))
+
+
+@pytest.mark.parametrize("nchunks", [257, 601, 2000])
+def test_quantile_averages_are_exact_means_over_many_binades(nchunks):
+    """Order statistics spread over 2^-60 .. 2^60 with both signs, more than
+    256 chunks and a ragged last chunk: every average equals the oracle's exact
+    mean rounded once, bit for bit (a plain binary64 sum misses it)."""
+    L = qb()
+    rng = np.random.default_rng(nchunks)
+    n = 4096 * (nchunks - 1) + 1000
+    mag = np.ldexp(rng.uniform(1.0, 2.0, n), rng.integers(-60, 61, n))
+    xh = (mag * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+    xh[rng.integers(0, n, 2000)] = np.float32(-0.0)
+    t = torch.empty(L.qb_code_table_bytes(), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(L.qb_quantile_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    avg = torch.full((257,), float("nan"), dtype=torch.float64, device=DEV)
+    L.qb_estimate_quantiles(to_device(xh), n, t, ws, averages=avg)
+    want_avg = oracle.quantile_averages(xh)
+    assert np.array_equal(avg.cpu().numpy().view(np.uint64), want_avg.view(np.uint64))
+    vals, _ = read_table(t)
+    assert np.array_equal(vals.view(np.uint32), oracle.estimate_quantiles(xh).view(np.uint32))
 
 
 def test_quantile_code_of_a_uniform_grid():
@@ -140,14 +164,17 @@ def test_estimate_then_quantize_a_large_tensor():
     x = torch.empty(n, device=DEV).normal_(0, 0.02, generator=torch.Generator(device=DEV).manual_seed(3))
     t = torch.empty(L.qb_code_table_bytes(), dtype=torch.uint8, device=DEV)
     ws = torch.empty(L.qb_quantile_workspace_bytes(n), dtype=torch.uint8, device=DEV)
-    L.qb_estimate_quantiles(x, n, t, ws)
+    avg = torch.empty(257, dtype=torch.float64, device=DEV)
+    L.qb_estimate_quantiles(x, n, t, ws, averages=avg)
     codes = torch.empty(n, dtype=torch.uint8, device=DEV)
     absmax = torch.empty(n // B, device=DEV)
     L.qb_quantize_code(x, n, t, B, codes, absmax)
     y = torch.empty(n, device=DEV)
     L.qb_dequantize_code(codes, absmax, t, B, n, y)
     vals, _ = read_table(t)
-    assert np.array_equal(vals, oracle.estimate_quantiles(x.cpu().numpy()))
+    xh = x.cpu().numpy()
+    assert np.array_equal(vals, oracle.estimate_quantiles(xh))
+    assert np.array_equal(avg.cpu().numpy().view(np.uint64), oracle.quantile_averages(xh).view(np.uint64))
     blocks = np.random.default_rng(4).choice(n // B, 256, replace=False)
     idx = torch.from_numpy(blocks).to(DEV)
     xs = x.view(-1, B).index_select(0, idx).cpu().numpy().reshape(-1)

@@ -178,11 +178,14 @@ def test_user_code_and_quantile_kernels_every_instantiation(xdt):
     x_est = host_values(4096 * 3 + 5, xdt, rng, 0.02)
     t = torch.empty(L.qb_code_table_bytes(), dtype=torch.uint8, device=DEV)
     ws = torch.empty(L.qb_quantile_workspace_bytes(x_est.size), dtype=torch.uint8, device=DEV)
-    L.qb_estimate_quantiles(to_device(x_est, TORCH_DT[xdt]), x_est.size, t, ws)
+    avg = torch.empty(257, dtype=torch.float64, device=DEV)
+    L.qb_estimate_quantiles(to_device(x_est, TORCH_DT[xdt]), x_est.size, t, ws, averages=avg)
     torch.cuda.synchronize()
     cb = t.cpu().numpy().view(np.float32)[:256].copy()
     assert np.array_equal(cb.view(np.uint32), oracle.estimate_quantiles(x_est, xdt=xdt).view(np.uint32)), \
         f"xdt={xdt}: estimated quantile code"
+    assert np.array_equal(avg.cpu().numpy().view(np.uint64),
+                          oracle.quantile_averages(x_est, xdt=xdt).view(np.uint64)), f"xdt={xdt}: averages"
     for B in BLOCKS:
         n = 3 * B + 17
         nb = -(-n // B)

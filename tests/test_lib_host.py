@@ -10,8 +10,11 @@
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
+
 import pytest
 
 import oracle
@@ -37,6 +40,25 @@ def test_exports_every_declared_symbol(qb):
     assert len(names) >= 9
     for name in names:
         assert hasattr(qb.lib(), name), name
+
+
+def test_binding_declares_argument_types_of_every_entry_point(qb):
+    """Without argtypes ctypes passes a Python int as a 32-bit C int, which
+    truncates a device pointer: every declared function must have them."""
+    L = qb.lib()
+    for name in declared_functions():
+        f = getattr(L, name)
+        assert f.argtypes is not None, f"{name}: no argtypes in the binding"
+
+
+def test_binding_loads_the_in_tree_library_whatever_the_environment(qb):
+    in_tree = os.path.realpath(os.path.join(ROOT, "bit_optimizer_states_amd", "libqb.so"))
+    assert qb.loaded_path() == in_tree
+    # a stray variable naming another build does not redirect the binding
+    code = ("import bit_optimizer_states_amd.binding as b; b.lib(); print(b.loaded_path())")
+    env = dict(os.environ, QB_LIBRARY="/nonexistent/libqb.so")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == in_tree
 
 
 @pytest.mark.parametrize("code", [0, 1, 2, 3])
@@ -315,6 +337,19 @@ def test_linear_code_equals_oracle(qb):
     assert qb.qb_code_table_bytes() == 6160          # entries, thresholds, bucket index
 
 
+def test_normalize_arguments_rejected_before_launch(qb):
+    L = qb.lib()
+    A = 0x100000
+    assert L.qb_normalize(A, 0, 0, A, 64, A, None) == qb.QB_OK            # n == 0: nothing runs
+    assert L.qb_normalize(A, 0, -1, A, 64, A, None) == qb.QB_EINVAL
+    assert L.qb_normalize(A, 0, 100, A, 0, A, None) == qb.QB_EINVAL        # blocksize < 1
+    assert L.qb_normalize(A, 7, 100, A, 64, A, None) == qb.QB_EINVAL       # dtype
+    assert L.qb_normalize(A, 0, 100, None, 64, A, None) == qb.QB_EINVAL
+    assert L.qb_normalize(A, 0, 100, A, 64, None, None) == qb.QB_EINVAL
+    assert L.qb_normalize(A + 4, 0, 100, A, 64, A, None) == qb.QB_EALIGN
+    assert L.qb_normalize(A, 0, 100, A, 64, A + 8, None) == qb.QB_EALIGN
+
+
 def test_user_code_arguments_rejected_before_launch(qb):
     L = qb.lib()
     A = 0x100000
@@ -335,10 +370,12 @@ def test_user_code_arguments_rejected_before_launch(qb):
     assert L.qb_dequantize_code(A, A, A, 256, 100, A + 2, 2, None) == qb.QB_EALIGN
     ws = L.qb_quantile_workspace_bytes(10000)
     assert ws == -(-(3 * 257 * 4) // 256) * 256 + 257 * 8
-    assert L.qb_estimate_quantiles(A, 0, 0, A, A, ws, None) == qb.QB_EINVAL      # n < 1
-    assert L.qb_estimate_quantiles(A, 0, 10000, A, A, ws - 256, None) == qb.QB_EWORKSPACE
-    assert L.qb_estimate_quantiles(A, 5, 10000, A, A, ws, None) == qb.QB_EINVAL
-    assert L.qb_estimate_quantiles(A, 0, 10000, A + 4, A, ws, None) == qb.QB_EALIGN
+    assert L.qb_estimate_quantiles(A, 0, 0, A, None, A, ws, None) == qb.QB_EINVAL      # n < 1
+    assert L.qb_estimate_quantiles(A, 0, 10000, A, None, A, ws - 8, None) == qb.QB_EWORKSPACE
+    assert L.qb_estimate_quantiles(A, 5, 10000, A, None, A, ws, None) == qb.QB_EINVAL
+    assert L.qb_estimate_quantiles(A, 0, 10000, A + 4, None, A, ws, None) == qb.QB_EALIGN
+    assert L.qb_estimate_quantiles(A, 0, 10000, A, A + 8, A, ws, None) == qb.QB_EALIGN   # averages
+    assert L.qb_quantile_workspace_bytes(4096 * 300) == -(-(300 * 257 * 4) // 256) * 256 + 257 * 8   # no group sums
 
 
 def test_status_strings(qb):
