@@ -82,6 +82,8 @@ def lib():
         L.qb_quantize.argtypes = [vp, i32, i64, i32, i32, vp, vp, ctypes.POINTER(qb_dq), vp]
         L.qb_dequantize.argtypes = [vp, vp, ctypes.POINTER(qb_dq), i32, i32, i64, vp, i32, vp]
         L.qb_adamw8bit_step.argtypes = [vp, vp, i32, i64, vp, vp, vp, vp, i32, ctypes.POINTER(qb_adamw_hparams), vp]
+        L.qb_multi_tensor_step_noalloc.argtypes = [ctypes.POINTER(qb_tensor), i32, i32, i32,
+                                                   ctypes.POINTER(qb_adamw_hparams), vp]
         L.qb_multi_tensor_step.argtypes = [ctypes.POINTER(qb_tensor), i32, i32, i32, ctypes.POINTER(qb_adamw_hparams),
                                            vp, sz, vp]
         L.qb_multi_tensor_dequantize.argtypes = [ctypes.POINTER(qb_dequant_tensor), i32, i32, i32, i32, i32, vp, sz,
@@ -115,6 +117,7 @@ def lib():
         L.qb_multi_tensor_quantize_workspace_bytes.argtypes = [ctypes.POINTER(qb_quant_tensor), i32, i32]
         L.qb_multi_tensor_quantize_workspace_bytes.restype = sz
         for f in (L.qb_quantize, L.qb_dequantize, L.qb_adamw8bit_step, L.qb_multi_tensor_step,
+                  L.qb_multi_tensor_step_noalloc,
                   L.qb_multi_tensor_dequantize, L.qb_multi_tensor_quantize, L.qb_optimizer8bit_step,
                   L.qb_multi_tensor_optimizer_step, L.qb_prepare_code, L.qb_estimate_quantiles, L.qb_quantize_code,
                   L.qb_dequantize_code, L.qb_normalize):
@@ -284,6 +287,12 @@ def qb_multi_tensor_step(table, count, gdt, blocksize, hp, ws, stream=None):
     """table: result of tensor_table(); gdt: QB_F32/QB_F16/QB_BF16; ws: device byte tensor."""
     _check(lib().qb_multi_tensor_step(table, int(count), int(gdt), int(blocksize), ctypes.byref(hp), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)), "qb_multi_tensor_step")
+
+
+def qb_multi_tensor_step_noalloc(table, count, gdt, blocksize, hp, stream=None):
+    """qb_multi_tensor_step with the library's own scratch in place of ws."""
+    _check(lib().qb_multi_tensor_step_noalloc(table, int(count), int(gdt), int(blocksize), ctypes.byref(hp),
+                                              _stream(stream)), "qb_multi_tensor_step_noalloc")
 
 
 def quant_table(entries):

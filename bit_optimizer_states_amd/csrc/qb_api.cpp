@@ -818,6 +818,17 @@ qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype
     return qb_multi_tensor_optimizer_step(&o, tensors, count, QB_F32, gdt, blocksize, ws, ws_bytes, stream);
 }
 
+qb_status qb_multi_tensor_step_noalloc(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
+                                       const qb_adamw_hparams* hp, void* stream)
+{
+    if (!hp || count < 0) return QB_EINVAL;
+    if (count > kScratchMaxTensors || qb_multi_tensor_workspace_bytes(count) > kScratchBytes) return QB_EWORKSPACE;
+    if (count == 0) return QB_OK;
+    void* ws = device_scratch();
+    if (!ws) return QB_EHIP;
+    return qb_multi_tensor_step(tensors, count, gdt, blocksize, hp, ws, kScratchBytes, stream);
+}
+
 size_t qb_paged_workspace_bytes(int64_t page_params, int32_t blocksize)
 {
     if (!pow2_block(blocksize) || page_params <= 0 || page_params % blocksize != 0) return 0;

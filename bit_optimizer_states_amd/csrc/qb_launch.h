@@ -112,6 +112,17 @@ constexpr int64_t max_tile_buckets(int64_t count) { return 2 * count + 64; }
 // Device copy of the constant tables for the current device (uploaded once).
 const QbTables* device_tables();
 
+// The library's own scratch for the allocation-free multi-tensor step: the
+// tables of one multi-tensor launch (descriptors, first tiles, bucket index)
+// of at most kScratchMaxTensors tensors.  device_scratch() is its address on
+// the current device (nullptr on a HIP error).
+constexpr int32_t kScratchMaxTensors = 4096;
+constexpr size_t kScratchBytes = 384 * 1024;
+static_assert((size_t)kScratchMaxTensors * 64 + ((size_t)kScratchMaxTensors + 1) * 8 +
+                      ((size_t)max_tile_buckets(kScratchMaxTensors) + 1) * 4 <= kScratchBytes,
+              "scratch holds the tables of kScratchMaxTensors tensors");
+void* device_scratch();
+
 // CUs x resident workgroups per CU of a kernel, cached per (device, kernel);
 // `query` returns the kernel's resident workgroups per CU.
 int persistent_grid_cap(const void* kernel, int (*query)(const void*));

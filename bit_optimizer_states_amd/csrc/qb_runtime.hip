@@ -30,6 +30,27 @@ const QbTables* device_tables()
     return static_cast<const QbTables*>(addr);
 }
 
+// Scratch of the allocation-free multi-tensor step: a device variable, so
+// every device holds its own copy until the process ends.  Host code must not
+// use the symbol's name as an address; device_scratch() returns the current
+// device's copy, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* device_scratch()
+{
+    static std::mutex mu;
+    static std::map<int, void*> by_device;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = by_device.find(dev);
+    if (it != by_device.end()) return it->second;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    by_device[dev] = ptr;
+    return ptr;
+}
+
 int persistent_grid_cap(const void* kernel, int (*query)(const void*))
 {
     static std::mutex mu;

@@ -32,7 +32,8 @@
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers unless marked "host".  The caller
  *     owns every buffer: libqb never allocates device memory and keeps no state
- *     between calls except its constant tables.  Every entry point is safe to
+ *     between calls except its constant tables (and the one scratch array of
+ *     qb_multi_tensor_step_noalloc).  Every entry point is safe to
  *     call from several host threads at once, with one exception:
  *     qb_paged_optimizer_step, whose calls on one device share internal copy
  *     streams and events and must not overlap in time (see its description).
@@ -370,6 +371,24 @@ qb_status qb_adamw8bit_step(float* p, const void* g, qb_dtype gdt, int64_t n, ui
  */
 qb_status qb_multi_tensor_step(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
                                const qb_adamw_hparams* hp, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qb_multi_tensor_step_noalloc -- qb_multi_tensor_step without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * tensor table goes into the library's own scratch: a device array of 384 KiB
+ * that every GPU the library runs on holds until the process ends.  No device
+ * memory is allocated or freed (no hipMalloc, hipFree or allocating library
+ * call); host-side staging reuses per-thread buffers of the library.
+ *   count     at most 4096 (QB_EWORKSPACE beyond).
+ * Other arguments, the result (bit for bit) and the errors are those of
+ * qb_multi_tensor_step.  Every call on one GPU shares that GPU's scratch,
+ * which keeps the last call's table: calls that overlap in time on one GPU
+ * (other streams, other host threads) race and must not be made; calls on
+ * one stream are ordered and safe.
+ */
+qb_status qb_multi_tensor_step_noalloc(const qb_tensor* tensors, int32_t count, qb_dtype gdt, int32_t blocksize,
+                                       const qb_adamw_hparams* hp, void* stream);
 
 /*
  * qb_optimizer8bit_step -- one fused 8-bit step of optimizer hp->kind (see

@@ -350,6 +350,16 @@ def test_normalize_arguments_rejected_before_launch(qb):
     assert L.qb_normalize(A, 0, 100, A, 64, A + 8, None) == qb.QB_EALIGN
 
 
+def test_noalloc_step_arguments_rejected_before_launch(qb):
+    L = qb.lib()
+    hp = qb.hparams()
+    assert L.qb_multi_tensor_step_noalloc(None, 0, 2, 2048, ctypes.byref(hp), None) == qb.QB_OK
+    assert L.qb_multi_tensor_step_noalloc(None, -1, 2, 2048, ctypes.byref(hp), None) == qb.QB_EINVAL
+    assert L.qb_multi_tensor_step_noalloc(None, 1, 2, 2048, None, None) == qb.QB_EINVAL
+    # beyond the 4096 tensors its scratch holds
+    assert L.qb_multi_tensor_step_noalloc(None, 4097, 2, 2048, ctypes.byref(hp), None) == qb.QB_EWORKSPACE
+
+
 def test_user_code_arguments_rejected_before_launch(qb):
     L = qb.lib()
     A = 0x100000
