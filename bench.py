@@ -12,16 +12,23 @@ One step = one pass of the whole hot path over synthetic inputs resident in HBM:
      grouped call (qb_multi_tensor_quantize: four launches);
   3. dequantization of those 225 NF4 tensors to bf16 in one grouped launch
      (qb_multi_tensor_dequantize);
-  4. a dynamic 8-bit round trip (quantize, then dequantize to fp32; block 2048)
+  4. the same quantize and dequantize with the FP4 code;
+  5. a dynamic 8-bit round trip (quantize, then dequantize to fp32; block 2048)
      of 268,435,456 fp32 values ~0.02 * Student-t(3).
-Two gradient sets alternate between steps (generated before timing).  After
-the timed steps the two 4-bit sweeps are also timed with one qb_quantize /
-qb_dequantize call per tensor (reported under "components", not in `value`).
+Two gradient sets alternate between steps (generated before timing).  Each
+tensor is an allocation of its own (--arena carves them all from one
+allocation at fixed offsets instead; measured 3-6% slower for the AdamW
+step).  After the timed steps: the two NF4 sweeps
+with one qb_quantize / qb_dequantize call per tensor, and the same-process HBM
+ceilings (a device copy, a read and a write of 4 GiB) for comparison.
 
 Prints one JSON line (rank 0).  `value` is the whole step's algorithmic
 traffic divided by its time; the per-part figures (AdamW GB/s and params/s,
 4-bit dequantize GB/s) are under "components"; "roofline" reports the
 dominant kernel (the multi-tensor AdamW step) against the 8 TB/s HBM peak.
+The CPU-baseline leg also counts, over the full tensors, the normalized
+values that lie within one binary32 ulp of a code midpoint and checks every
+block holding one against the oracle.
 """
 import argparse
 import hashlib
@@ -72,7 +79,7 @@ def q4_bytes_per_weight():
 def kernel_source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_optimizer_states_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(n for n in os.listdir(csrc) if os.path.isfile(os.path.join(csrc, n))):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()
@@ -90,51 +97,90 @@ def traffic_per_launch():
     return rec.get("hbm_bytes_per_launch")
 
 
+ARENA_ALIGN = 4096
+
+
+class Arena:
+    """Device tensors carved from ONE allocation at fixed offsets (4 KiB
+    aligned, in the order of `specs`), so the layout is the same in every
+    process.  With arena=False each tensor is its own allocation instead."""
+
+    def __init__(self, torch, dev, specs, arena=True):
+        self.views = []
+        if not arena:
+            self.buf = None
+            self.views = [torch.empty(max(n, 1), dtype=dt, device=dev)[:n] for n, dt in specs]
+            return
+        offs, off = [], 0
+        for n, dt in specs:
+            off = -(-off // ARENA_ALIGN) * ARENA_ALIGN
+            offs.append(off)
+            off += n * torch.empty(0, dtype=dt).element_size()
+        self.buf = torch.empty(max(off, 1), dtype=torch.uint8, device=dev)
+        for (n, dt), o in zip(specs, offs):
+            size = torch.empty(0, dtype=dt).element_size()
+            self.views.append(self.buf[o:o + n * size].view(dt))
+
+
 class Model7B:
     """Device state of the multi-tensor AdamW step and the 4-bit sweep."""
 
-    def __init__(self, torch, qb, inputs, dev, seed, with_w4=True, grad_sets=2):
+    def __init__(self, torch, qb, inputs, dev, seed, with_w4=True, grad_sets=2, arena=True):
         self.t = torch
         shapes = inputs.llama7b_param_shapes()
         self.names = [s[0] for s in shapes]
         self.sizes = [int(np.prod(s[1])) for s in shapes]
+        wshapes = inputs.llama7b_weight_shapes() if with_w4 else []
+        wsizes = [int(np.prod(s)) for _, s in wshapes]
+        f32, u8, bf16, f16 = torch.float32, torch.uint8, torch.bfloat16, torch.float16
+        # every tensor of the step, in layout order
+        specs = []
+        for n in self.sizes:
+            nb = (n + ADAM_BLOCK - 1) // ADAM_BLOCK
+            specs += [(n, f32), (n, u8), (n, u8), (nb, f32), (nb, f32)]
+        for _ in range(grad_sets):
+            specs += [(n, bf16) for n in self.sizes]
+        for n in wsizes:
+            nb = (n + W4_BLOCK - 1) // W4_BLOCK
+            specs += [(n, f16), ((n + 1) // 2, u8), (nb, u8), ((nb + W4_BLOCK2 - 1) // W4_BLOCK2, f32), (4, f32),
+                      (n, bf16)]
+        if with_w4:
+            specs += [(Q8_N, f32), (Q8_N, u8), (Q8_N // Q8_BLOCK, f32), (Q8_N, f32)]
+        total = sum(n * torch.empty(0, dtype=dt).element_size() for n, dt in specs)
+        log(f"allocating {total / 2**30:.1f} GiB for {len(specs)} tensors "
+            f"({'one arena' if arena else 'one allocation each'})")
+        self.arena = Arena(torch, dev, specs, arena)
+        views = iter(self.arena.views)
         self.params = []
         self.grads = [[] for _ in range(grad_sets)]
-        log(f"allocating {len(shapes)} parameter tensors ({sum(self.sizes):,} params)")
+        log(f"filling {len(shapes)} parameter tensors ({sum(self.sizes):,} params)")
         for i, (name, shape) in enumerate(shapes):
-            n = self.sizes[i]
-            nb = (n + ADAM_BLOCK - 1) // ADAM_BLOCK
-            p = inputs.normal(n, 0.02, seed=seed * 1000 + i, device=dev)
-            m = torch.full((n,), 127, dtype=torch.uint8, device=dev)
-            v = torch.full((n,), 127, dtype=torch.uint8, device=dev)
-            am = torch.zeros(nb, dtype=torch.float32, device=dev)
-            av = torch.zeros(nb, dtype=torch.float32, device=dev)
+            p, m, v, am, av = (next(views) for _ in range(5))
+            p.copy_(inputs.normal(self.sizes[i], 0.02, seed=seed * 1000 + i, device=dev))
+            m.fill_(127)
+            v.fill_(127)
+            am.zero_()
+            av.zero_()
             self.params.append((p, m, v, am, av))
-            for k in range(grad_sets):
+        for k in range(grad_sets):
+            for i, (name, shape) in enumerate(shapes):
                 gs = inputs.grad_seed(seed, i, k)
                 if name == "embed":
                     g = inputs.sparse_row_grad(shape[0], shape[1], 0.10, 1e-3, gs, device=dev).reshape(-1)
                 else:
-                    g = inputs.normal(n, 1e-3, gs, device=dev, dtype=torch.bfloat16)
-                self.grads[k].append(g)
+                    g = inputs.normal(self.sizes[i], 1e-3, gs, device=dev, dtype=torch.bfloat16)
+                self.grads[k].append(next(views).copy_(g))
         self.tables = [qb.tensor_table([(p, g, m, v, am, av) for (p, m, v, am, av), g in zip(self.params, gset)])
                        for gset in self.grads]
         self.ws = torch.empty(qb.qb_multi_tensor_workspace_bytes(len(shapes)), dtype=torch.uint8, device=dev)
         self.n_params = sum(self.sizes)
         self.w4 = []
         if with_w4:
-            wshapes = inputs.llama7b_weight_shapes()
-            log(f"allocating {len(wshapes)} fp16 weight tensors for the 4-bit sweep")
+            log(f"filling {len(wshapes)} fp16 weight tensors for the 4-bit sweeps")
             wsmax = 0
-            for j, (name, shape) in enumerate(wshapes):
-                n = int(np.prod(shape))
-                nb = (n + W4_BLOCK - 1) // W4_BLOCK
-                w = inputs.normal(n, 0.02, seed=seed * 7919 + j, device=dev, dtype=torch.float16)
-                codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev)
-                c2 = torch.empty(nb, dtype=torch.uint8, device=dev)
-                a2 = torch.empty((nb + W4_BLOCK2 - 1) // W4_BLOCK2, dtype=torch.float32, device=dev)
-                off = torch.empty(4, dtype=torch.float32, device=dev)
-                y = torch.empty(n, dtype=torch.bfloat16, device=dev)
+            for j, n in enumerate(wsizes):
+                w, codes, c2, a2, off, y = (next(views) for _ in range(6))
+                w.copy_(inputs.normal(n, 0.02, seed=seed * 7919 + j, device=dev, dtype=torch.float16))
                 self.w4.append((n, w, codes, c2, a2, off, y))
                 wsmax = max(wsmax, qb.qb_dq_workspace_bytes(n, W4_BLOCK))
             self.w4_ws = torch.empty(wsmax, dtype=torch.uint8, device=dev)
@@ -151,10 +197,10 @@ class Model7B:
         self.n_w4 = sum(e[0] for e in self.w4)
         self.q8 = None
         if with_w4:
-            log(f"allocating the {Q8_N:,}-value fp32 tensor for the 8-bit round trip")
-            x = inputs.student_t3(Q8_N, 0.02, seed=seed * 31 + 2, device=dev)
-            self.q8 = (x, torch.empty(Q8_N, dtype=torch.uint8, device=dev),
-                       torch.empty(Q8_N // Q8_BLOCK, dtype=torch.float32, device=dev), torch.empty_like(x))
+            log(f"filling the {Q8_N:,}-value fp32 tensor for the 8-bit round trip")
+            x, codes, absmax, y = (next(views) for _ in range(4))
+            x.copy_(inputs.student_t3(Q8_N, 0.02, seed=seed * 31 + 2, device=dev))
+            self.q8 = (x, codes, absmax, y)
 
 
 def run_adam(qb, model, step):
@@ -162,13 +208,12 @@ def run_adam(qb, model, step):
     qb.qb_multi_tensor_step(table, len(table), qb.QB_BF16, ADAM_BLOCK, qb.hparams(step=step, **HP), model.ws)
 
 
-def run_q4(qb, model):
-    qb.qb_multi_tensor_quantize(model.q_table, len(model.w4), qb.QB_F16, qb.QB_NF4, W4_BLOCK, W4_BLOCK2, model.q_ws)
+def run_q4(qb, model, code):
+    qb.qb_multi_tensor_quantize(model.q_table, len(model.w4), qb.QB_F16, code, W4_BLOCK, W4_BLOCK2, model.q_ws)
 
 
-def run_dq4(qb, model):
-    qb.qb_multi_tensor_dequantize(model.d_table, len(model.w4), qb.QB_NF4, W4_BLOCK, W4_BLOCK2, qb.QB_BF16,
-                                  model.d_ws)
+def run_dq4(qb, model, code):
+    qb.qb_multi_tensor_dequantize(model.d_table, len(model.w4), code, W4_BLOCK, W4_BLOCK2, qb.QB_BF16, model.d_ws)
 
 
 def run_q8(qb, model):
@@ -291,6 +336,112 @@ def cpu_baseline(torch, model, seconds_target, rng):
     }
 
 
+CEIL_BYTES = 4 << 30
+
+
+def _stream_lib():
+    """libqb_stream.so: the HBM reference streams (include/qb_stream.h)."""
+    import ctypes
+    path = os.path.join(ROOT, "bit_optimizer_states_amd", "libqb_stream.so")
+    if not os.path.exists(path):
+        raise OSError(f"{path} is missing: build it with bit_optimizer_states_amd/build.py")
+    L = ctypes.CDLL(path)
+    vp, i64, f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    L.qbs_copy.argtypes = [vp, vp, i64, vp]
+    L.qbs_read.argtypes = [vp, i64, f, vp, vp]
+    L.qbs_write.argtypes = [vp, i64, f, vp]
+    for fn in (L.qbs_copy, L.qbs_read, L.qbs_write):
+        fn.restype = ctypes.c_int
+    return L
+
+
+def hbm_ceilings(torch, dev, reps=10):
+    """Same-process HBM ceilings on 4 GiB buffers from the reference streams
+    of libqb_stream.so (the access style of libqb's kernels: one 256-thread
+    workgroup per 4096 floats, 16-byte non-temporal accesses): a copy (4 GiB
+    read + 4 GiB written), a read and a write; mean HIP-event time of `reps`
+    calls on torch's current stream, which is the stream they run on."""
+    L = _stream_lib()
+    n = CEIL_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    sink = torch.empty(256, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"libqb_stream: HIP error {rc}")
+
+    copy_ms = time_calls(torch, lambda: ok(L.qbs_copy(a.data_ptr(), b.data_ptr(), n, s)), reps)
+    read_ms = time_calls(torch, lambda: ok(L.qbs_read(a.data_ptr(), n, float("nan"), sink.data_ptr(), s)), reps)
+    write_ms = time_calls(torch, lambda: ok(L.qbs_write(b.data_ptr(), n, 2.0, s)), reps)
+    del a, b
+    rates = {"copy_GB/s": 2 * CEIL_BYTES / copy_ms / 1e6, "read_GB/s": CEIL_BYTES / read_ms / 1e6,
+             "write_GB/s": CEIL_BYTES / write_ms / 1e6}
+    return {"kernels": "libqb_stream.so (16-byte non-temporal streams)", "buffer_bytes": CEIL_BYTES, **rates,
+            "frac_of_hbm_peak": {k.split("_")[0]: v / HBM_PEAK_GBS for k, v in rates.items()}}
+
+
+def _near_midpoint_mask(torch, nv, mids, ulps):
+    """Values (binary32) within one binary32 ulp of a midpoint of adjacent code
+    entries (mids: ascending binary64, exact; ulps: the ulp at each)."""
+    v = nv.double()
+    k = torch.bucketize(v, mids).clamp_(1, mids.numel() - 1)
+    return ((v - mids[k - 1]).abs() <= ulps[k - 1]) | ((v - mids[k]).abs() <= ulps[k])
+
+
+def _census(torch, qb, oracle, x, xdt, code, B, codes, dev, chunk=1 << 26):
+    """Near-midpoint values of one quantized tensor x (n a multiple of B) and
+    an oracle check of every block that holds one: (count, blocks, differing code bytes)."""
+    v = np.unique(oracle.codebook(code).astype(np.float64))
+    mids_h = (v[:-1] + v[1:]) / 2
+    mids = torch.from_numpy(mids_h).to(dev)
+    ulps = torch.from_numpy(np.spacing(np.abs(mids_h).astype(np.float32)).astype(np.float64)).to(dev)
+    n = x.numel()
+    absmax = x.view(-1, B).abs().amax(1).float()
+    nv = torch.empty(n, dtype=torch.float32, device=dev)
+    qb.qb_normalize(x, n, absmax, B, nv)
+    idx = torch.cat([_near_midpoint_mask(torch, nv[s:s + chunk], mids, ulps).nonzero().flatten() + s
+                     for s in range(0, n, chunk)])
+    del nv
+    blocks = torch.unique(idx // B)
+    differing = 0
+    if blocks.numel():
+        xb = x.view(-1, B).index_select(0, blocks).reshape(-1).cpu()
+        host = xb.numpy() if xb.dtype == torch.float32 else xb.view(torch.int16).numpy().view(np.uint16)
+        want, _ = oracle.quantize_blockwise(host, code, B, xdt=xdt)
+        per = B // 2 if code in (oracle.NF4, oracle.FP4) else B
+        got = codes.view(-1, per).index_select(0, blocks).reshape(-1).cpu().numpy()
+        differing = int(np.count_nonzero(got != want))
+    return int(idx.numel()), int(blocks.numel()), differing
+
+
+def midpoint_census(torch, qb, model):
+    """Over the full tensors of the step's quantize parts: how many normalized
+    values x / absmax (binary32, the kernels' quotient through qb_normalize)
+    lie within one binary32 ulp of a midpoint of adjacent code entries (where
+    a code could hinge on the quotient's last bit), and an oracle check of
+    every block that holds one."""
+    import oracle
+    dev = model.q8[0].device
+    out = {"criterion": "|x/absmax - m| <= ulp32(m) for a midpoint m of two adjacent code entries"}
+    x, codes, _, _ = model.q8
+    c, b, d = _census(torch, qb, oracle, x, oracle.F32, oracle.DYN8, Q8_BLOCK, codes, dev)
+    out["roundtrip8_dyn8_fp32"] = {"elements": Q8_N, "near_midpoint_values": c, "fraction": c / Q8_N,
+                                   "blocks_checked_against_oracle": b, "codes_differing": d}
+    for name, qcode, ocode in (("nf4", qb.QB_NF4, oracle.NF4), ("fp4", qb.QB_FP4, oracle.FP4)):
+        run_q4(qb, model, qcode)
+        torch.cuda.synchronize()
+        tot = [0, 0, 0]
+        for (n, w, wcodes, *_) in model.w4:
+            r = _census(torch, qb, oracle, w, oracle.F16, ocode, W4_BLOCK, wcodes, dev)
+            tot = [t + v for t, v in zip(tot, r)]
+        out[f"quantize4_{name}_nested"] = {"elements": model.n_w4, "near_midpoint_values": tot[0],
+                                           "fraction": tot[0] / model.n_w4, "blocks_checked_against_oracle": tot[1],
+                                           "codes_differing": tot[2]}
+    return out
+
+
 OPTIMIZERS = {  # name: (qb kind, hyperparameters, states)
     "adamw": (0, dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01), 2),
     "adam": (1, dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01), 2),
@@ -383,8 +534,19 @@ def bench_flat(torch, qb, inputs, dev, args):
         evs[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    per_step = [a.elapsed_time(b) for a, b in evs]
+    ms = sorted(per_step)
     med = ms[len(ms) // 2]
+    extra = {}
+    if args.steady:
+        # steady state: the median of steps 11 .. 100 of a run started from fresh states
+        steady = float(np.median(per_step[10:]))
+        extra = {"steady_state_steps": "11-100", "steady_state_ms": steady,
+                 "steps_1_10_ms": per_step[:10], "steps_11_100_ms": {"min": min(per_step[10:]),
+                                                                    "max": max(per_step[10:]),
+                                                                    "p10": float(np.percentile(per_step[10:], 10)),
+                                                                    "p90": float(np.percentile(per_step[10:], 90))}}
+        med = steady
     bpp = optim_bytes_per_param(states) if args.state_bits == 8 else 8 + 2 + 8 * states
     if layerwise:
         bpp += layerwise_extra_bytes_per_param(args.optimizer, args.state_bits)
@@ -392,11 +554,10 @@ def bench_flat(torch, qb, inputs, dev, args):
         bpp -= 4 if not layerwise else 6            # p read + written in 2 bytes (and read in the norm pass)
     nbytes = n * bpp
     call = "one-layer multi-tensor call (norm pass + step)" if layerwise else "single-tensor"
-    extra = {}
     if args.paged:
         call = f"paged (states in pinned host memory, pages of {args.page_params:,} params)"
         state_bytes = n * states * (1 + 4.0 / ADAM_BLOCK)      # each way across PCIe
-        extra = {"pcie_bytes_each_way": state_bytes, "pcie_GB/s_each_way": state_bytes / med / 1e6}
+        extra.update({"pcie_bytes_each_way": state_bytes, "pcie_GB/s_each_way": state_bytes / med / 1e6})
     print(json.dumps({"workload": f"flat 1.5e9 params, {args.param_dtype if args.param_dtype != 'fp32' else 'bf16'} "
                                   f"grads, block 2048, {call} {args.optimizer} "
                                   f"step, {args.state_bits}-bit states"
@@ -554,9 +715,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--arena", action="store_true",
+                    help="carve every tensor of the 7B step from one allocation at fixed offsets (default: one "
+                         "allocation per tensor, measured faster)")
     ap.add_argument("--adam-only", action="store_true", help="time only the multi-tensor AdamW step")
     ap.add_argument("--flat", action="store_true",
                     help="time the single-tensor AdamW step on a flat 1.5e9-parameter buffer instead")
+    ap.add_argument("--steady", action="store_true",
+                    help="--flat as 100 steps from fresh states with no warmup; reports the median of steps 11-100")
     ap.add_argument("--paged", action="store_true",
                     help="--flat with the optimizer states in pinned host memory (qb_paged_optimizer_step)")
     ap.add_argument("--page-params", type=int, default=1 << 26, help="parameters per page of the --paged run")
@@ -593,6 +759,8 @@ def main():
         return copy_calibration(torch, dev)
     qb.lib()
     rng = np.random.default_rng(args.seed)
+    if args.steady:
+        args.flat, args.steps, args.warmup = True, 100, 0
     if args.flat:
         return bench_flat(torch, qb, inputs, dev, args)
     if args.codes:
@@ -601,32 +769,32 @@ def main():
         return bench_matmul(torch, qb, inputs, dev, args)
     if args.roundtrip8:
         return bench_roundtrip8(torch, qb, inputs, dev, args)
-    model = Model7B(torch, qb, inputs, dev, args.seed, with_w4=not args.adam_only)
+    model = Model7B(torch, qb, inputs, dev, args.seed, with_w4=not args.adam_only, arena=args.arena)
     torch.cuda.synchronize()
     log(f"setup done; warmup {args.warmup} steps")
+
+    # the parts of one step, in order: (component, function of the step number)
+    parts = [("adamw8bit_multi_tensor", lambda k: run_adam(qb, model, k))]
+    if not args.adam_only:
+        parts += [("quantize4_nf4_nested", lambda k: run_q4(qb, model, qb.QB_NF4)),
+                  ("dequant4_nf4_nested_bf16", lambda k: run_dq4(qb, model, qb.QB_NF4)),
+                  ("quantize4_fp4_nested", lambda k: run_q4(qb, model, qb.QB_FP4)),
+                  ("dequant4_fp4_nested_bf16", lambda k: run_dq4(qb, model, qb.QB_FP4)),
+                  ("roundtrip8_dyn8_fp32", lambda k: run_q8(qb, model))]
 
     def step(k, ev=None):
         if ev is not None:
             ev[0].record()
-        run_adam(qb, model, k)
-        if ev is not None:
-            ev[1].record()
-        if not args.adam_only:
-            run_q4(qb, model)
+        for j, (_, fn) in enumerate(parts):
+            fn(k)
             if ev is not None:
-                ev[2].record()
-            run_dq4(qb, model)
-            if ev is not None:
-                ev[3].record()
-            run_q8(qb, model)
-            if ev is not None:
-                ev[4].record()
+                ev[j + 1].record()
 
     for k in range(1, args.warmup + 1):
         step(k)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -635,34 +803,39 @@ def main():
     wall = time.perf_counter() - t0
     log("timed region done")
 
-    adam_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    part_ms = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, (name, _) in
+               enumerate(parts)}
+    adam_ms = part_ms["adamw8bit_multi_tensor"]
     adam_bytes = model.n_params * adam_bytes_per_param()
     comps = {"adamw8bit_multi_tensor": {
         "ms": adam_ms, "GB/s": adam_bytes / adam_ms / 1e6, "params_per_s": model.n_params / adam_ms * 1e3,
         "frac_of_hbm_peak": adam_bytes / adam_ms / 1e6 / HBM_PEAK_GBS, "launches_per_step": 1}}
     step_bytes = adam_bytes
     if not args.adam_only:
-        q4_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-        d4_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
         q4_bytes = model.n_w4 * q4_bytes_per_weight()
         d4_bytes = model.n_w4 * w4_bytes_per_weight()
-        comps["quantize4_nf4_nested"] = {"ms": q4_ms, "GB/s": q4_bytes / q4_ms / 1e6,
-                                         "frac_of_hbm_peak": q4_bytes / q4_ms / 1e6 / HBM_PEAK_GBS,
-                                         "launches_per_step": 4, "call": "qb_multi_tensor_quantize"}
-        comps["dequant4_nf4_nested_bf16"] = {"ms": d4_ms, "GB/s": d4_bytes / d4_ms / 1e6,
-                                             "frac_of_hbm_peak": d4_bytes / d4_ms / 1e6 / HBM_PEAK_GBS,
-                                             "launches_per_step": 1, "call": "qb_multi_tensor_dequantize"}
-        q8_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
+        for code in ("nf4", "fp4"):
+            q_ms, d_ms = part_ms[f"quantize4_{code}_nested"], part_ms[f"dequant4_{code}_nested_bf16"]
+            comps[f"quantize4_{code}_nested"] = {"ms": q_ms, "GB/s": q4_bytes / q_ms / 1e6,
+                                                 "frac_of_hbm_peak": q4_bytes / q_ms / 1e6 / HBM_PEAK_GBS,
+                                                 "elements_per_s": model.n_w4 / q_ms * 1e3,
+                                                 "launches_per_step": 4, "call": "qb_multi_tensor_quantize"}
+            comps[f"dequant4_{code}_nested_bf16"] = {"ms": d_ms, "GB/s": d4_bytes / d_ms / 1e6,
+                                                     "frac_of_hbm_peak": d4_bytes / d_ms / 1e6 / HBM_PEAK_GBS,
+                                                     "elements_per_s": model.n_w4 / d_ms * 1e3,
+                                                     "launches_per_step": 1, "call": "qb_multi_tensor_dequantize"}
+            step_bytes += q4_bytes + d4_bytes
+        q8_ms = part_ms["roundtrip8_dyn8_fp32"]
         q8_bytes = Q8_N * 2 * q8_bytes_per_elem()
         comps["roundtrip8_dyn8_fp32"] = {"ms": q8_ms, "GB/s": q8_bytes / q8_ms / 1e6,
                                          "frac_of_hbm_peak": q8_bytes / q8_ms / 1e6 / HBM_PEAK_GBS,
                                          "elements_per_s": Q8_N / q8_ms * 1e3, "launches_per_step": 2,
                                          "call": "qb_quantize + qb_dequantize",
                                          "error": roundtrip_error_stats(torch, model.q8[0], model.q8[3], Q8_BLOCK)}
-        step_bytes += q4_bytes + d4_bytes + q8_bytes
+        step_bytes += q8_bytes
     ms_per_step = wall / args.steps * 1e3
     if not args.adam_only:
-        # the same sweeps with one qb_quantize / qb_dequantize call per tensor (outside the timed step)
+        # the NF4 sweeps with one qb_quantize / qb_dequantize call per tensor (outside the timed step)
         q1 = time_calls(torch, lambda: run_q4_per_tensor(qb, model))
         d1 = time_calls(torch, lambda: run_dq4_per_tensor(qb, model))
         comps["quantize4_nf4_nested_per_tensor_calls"] = {
@@ -671,6 +844,8 @@ def main():
         comps["dequant4_nf4_nested_bf16_per_tensor_calls"] = {
             "ms": d1, "GB/s": d4_bytes / d1 / 1e6, "frac_of_hbm_peak": d4_bytes / d1 / 1e6 / HBM_PEAK_GBS,
             "launches": len(model.w4), "call": "qb_dequantize"}
+    log("measuring the same-process HBM ceilings")
+    ceiling = hbm_ceilings(torch, dev)
     traffic = traffic_per_launch()
     achieved = adam_bytes / adam_ms / 1e6
     out = {
@@ -690,7 +865,7 @@ def main():
             "workload": ("7B decoder (291 tensors, 6,738,415,616 fp32 params, bf16 grads, 10% sparse embedding "
                          "rows): one multi-tensor fused AdamW8bit step, block 2048" +
                          ("" if args.adam_only else
-                          "; + NF4 nested quantize and bf16 dequantize of its 225 fp16 weights "
+                          "; + NF4 and FP4 nested quantize and bf16 dequantize of its 225 fp16 weights "
                           "(6,607,077,376), block 64 / 256; + dynamic 8-bit quantize and fp32 dequantize of "
                           "268,435,456 Student-t(3) values, block 2048")),
             "params": model.n_params,
@@ -698,6 +873,7 @@ def main():
             "adam_blocksize": ADAM_BLOCK,
             "w4_blocksize": W4_BLOCK,
             "w4_blocksize2": W4_BLOCK2,
+            "layout": "one arena, fixed offsets" if args.arena else "one allocation per tensor",
             "parallelism": "single GPU",
         },
         "components": comps,
@@ -711,11 +887,19 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": adam_bytes,
         },
+        "hbm_ceiling_same_process": {**ceiling, "adamw_frac_of_copy": achieved / ceiling["copy_GB/s"],
+                                     **({} if args.adam_only else {
+                                         "dequant4_nf4_frac_of_write": comps["dequant4_nf4_nested_bf16"]["GB/s"] /
+                                                                       ceiling["write_GB/s"]})},
+        "native_library": qb.loaded_path(),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(torch, model, 10.0, rng)
+        if not args.adam_only:
+            log("near-midpoint census over the full quantized tensors")
+            out["near_midpoint"] = midpoint_census(torch, qb, model)
     print(json.dumps(out), flush=True)
 
 

@@ -48,6 +48,22 @@ def _compile(src, build_dir=BUILD, extra=()):
     return obj
 
 
+STREAM_SRC = os.path.join(CSRC, "stream", "qb_stream.hip")
+STREAM_LIB = os.path.join(HERE, "libqb_stream.so")
+
+
+def build_stream(out=STREAM_LIB):
+    """The benchmark's HBM reference streams (libqb_stream.so: copy, read,
+    write), a library of their own: not part of libqb."""
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), *COMMON, "-x", "hip", *DEVICE, "-shared", STREAM_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 def build(jobs=None, out=LIB, extra=()):
     """Compile every source (always) and link the library (libqb.so by
     default; `extra` adds compiler flags); returns its path."""
@@ -67,3 +83,4 @@ def build(jobs=None, out=LIB, extra=()):
 
 if __name__ == "__main__":
     print(build())
+    print(build_stream())

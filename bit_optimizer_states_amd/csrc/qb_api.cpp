@@ -546,7 +546,7 @@ qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* 
     if (st != QB_OK) return st;
     if (!device_tables()) return QB_EINIT;
     const int bits = is4(code) ? 4 : 8;
-    return hip_status(launch_dequant(d, nullptr, dequant_tiles(n, dequant_tile_elems(bits, false)), bits,
+    return hip_status(launch_dequant(d, nullptr, dequant_tiles(n, dequant_tile_elems(bits, false, (int)ydt)), bits,
                                      is4(code) ? code4_index(code) : 0, blocksize, dq ? dq->blocksize2 : 256,
                                      dq != nullptr, (int)ydt, static_cast<hipStream_t>(stream)));
 }
@@ -600,7 +600,7 @@ qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t c
         if (t.n == 0) continue;
         d.tile_begin = tiles;
         table.push_back(d);
-        tiles += dequant_tiles(t.n, dequant_tile_elems(is4(code) ? 4 : 8, true));
+        tiles += dequant_tiles(t.n, dequant_tile_elems(is4(code) ? 4 : 8, true, (int)ydt));
     }
     if (table.empty()) return QB_OK;
     if (tiles >= (int64_t(1) << 31)) return QB_EINVAL;
@@ -666,7 +666,7 @@ qb_status qb_dequantize_code(const uint8_t* codes, const float* absmax, const vo
     DequantDesc d;
     qb_status st = dequant_desc(codes, absmax, nullptr, nullptr, nullptr, 0, n, y, blocksize, &mode, &d);
     if (st != QB_OK) return st;
-    return hip_status(launch_dequant_user(d, dequant_tiles(n, dequant_tile_elems(8, false)), blocksize, (int)ydt,
+    return hip_status(launch_dequant_user(d, dequant_tiles(n, dequant_tile_elems(8, false, (int)ydt)), blocksize, (int)ydt,
                                           static_cast<const UserCode*>(table), static_cast<hipStream_t>(stream)));
 }
 

@@ -9,8 +9,8 @@
 // operations ("Bitsandbytes", section İç içe nicelleştirme).
 //
 // Kernel shape: one 256-thread workgroup per tile of 8192 elements for 4-bit
-// codes and 4096 for 8-bit codes (the best measured on MI355X), in tile
-// order.  A thread takes units
+// codes and 4096 (2048 into binary32) for 8-bit codes (the best measured on
+// MI355X), in tile order.  A thread takes units
 // of E consecutive elements, E = 16 bytes of output (8 for 16-bit outputs, 4
 // for fp32), consecutive lanes on consecutive units, so every load and store
 // instruction of a wave covers one contiguous span.
@@ -42,8 +42,10 @@ namespace {
 #endif
 
 constexpr int kDqThreads = 256;
-static_assert(dequant_tile_elems(4, false) / 64 <= kDqThreads && dequant_tile_elems(4, true) / 64 <= kDqThreads &&
-                  dequant_tile_elems(8, false) / 64 <= kDqThreads,
+static_assert(dequant_tile_elems(4, false, DT_BF16) / 64 <= kDqThreads &&
+                  dequant_tile_elems(4, true, DT_BF16) / 64 <= kDqThreads &&
+                  dequant_tile_elems(8, false, DT_BF16) / 64 <= kDqThreads &&
+                  dequant_tile_elems(8, false, DT_F32) / 64 <= kDqThreads,
               "one thread per block of a tile");
 
 // The E codes of the unit at element offset e (a multiple of E) from base:
@@ -99,7 +101,8 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(DequantDesc single, Tile
     __shared__ float s_dyn[DQ && BITS == 4 && !QB_DQ_DIRECT_DYN ? 256 : 1];
     // a unit is E elements whose output a lane writes with one 16-byte store
     constexpr int E = YDT == DT_F32 ? 4 : 8;
-    constexpr int kDqElems = (int)dequant_tile_elems(BITS, MULTI);
+    constexpr int kDqElems = (int)dequant_tile_elems(BITS, MULTI, YDT);
+    static_assert(kDqElems % (kDqThreads * E) == 0, "whole units per thread");
     constexpr int kDqUnits = kDqElems / (kDqThreads * E);                // units per thread
     __shared__ float s_scale[kDqElems / 64];                            // blocks per tile at B = 64
     const int tid = threadIdx.x;

@@ -28,3 +28,29 @@ def test_algorithmic_byte_counts():
     assert np.isclose(bench.w4_bytes_per_weight(), 2.5159, atol=1e-4)
     # the fused 4-bit product at 4096 x 4096, one row of activations: 8.67 MB
     assert np.isclose(bench.dq4_matmul_bytes(1, 4096, 4096) / 1e6, 8.67, atol=0.01)
+
+
+def test_near_midpoint_mask_counts_one_ulp_on_either_side():
+    mids = torch.tensor([-0.25, 0.5], dtype=torch.float64)
+    ulps = torch.tensor([np.spacing(np.float32(0.25)), np.spacing(np.float32(0.5))], dtype=torch.float64)
+    half = np.float32(0.5)
+    vals = np.array([half, np.nextafter(half, np.float32(1)), np.nextafter(half, np.float32(0)),
+                     np.float32(0.5 + 2 * 2.0 ** -24), np.float32(-0.25), np.float32(0.0), np.float32(0.9)],
+                    dtype=np.float32)
+    got = bench._near_midpoint_mask(torch, torch.from_numpy(vals), mids, ulps).numpy()
+    assert got.tolist() == [True, True, True, False, True, False, False]
+
+
+def test_arena_carves_fixed_aligned_views():
+    f32, u8 = torch.float32, torch.uint8
+    specs = [(5, f32), (3, u8), (7, f32)]
+    a = bench.Arena(torch, "cpu", specs)
+    base = a.buf.data_ptr()
+    offs = [v.data_ptr() - base for v in a.views]
+    assert offs == [0, bench.ARENA_ALIGN, 2 * bench.ARENA_ALIGN]
+    assert [v.numel() for v in a.views] == [5, 3, 7] and [v.dtype for v in a.views] == [f32, u8, f32]
+    a.views[0].fill_(1.0)
+    a.views[2].fill_(2.0)
+    assert float(a.views[0].sum()) == 5.0 and float(a.views[2].sum()) == 14.0
+    b = bench.Arena(torch, "cpu", specs, arena=False)
+    assert b.buf is None and [v.numel() for v in b.views] == [5, 3, 7]

@@ -42,6 +42,18 @@ def test_exports_every_declared_symbol(qb):
         assert hasattr(qb.lib(), name), name
 
 
+def test_stream_library_exports_its_header():
+    """libqb_stream.so (the benchmark's HBM reference streams) exports every
+    function include/qb_stream.h declares."""
+    text = open(os.path.join(ROOT, "include", "qb_stream.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(qbs_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["qbs_copy", "qbs_read", "qbs_write"]
+    L = ctypes.CDLL(os.path.join(ROOT, "bit_optimizer_states_amd", "libqb_stream.so"))
+    for name in names:
+        assert hasattr(L, name), name
+
+
 def test_binding_declares_argument_types_of_every_entry_point(qb):
     """Without argtypes ctypes passes a Python int as a 32-bit C int, which
     truncates a device pointer: every declared function must have them."""
