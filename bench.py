@@ -644,7 +644,7 @@ def bench_roundtrip8(torch, qb, inputs, dev, args):
 
 
 MM_SHAPES = [(4096, 4096), (11008, 4096), (4096, 11008)]      # (N, K) of the 7B projections
-MM_ROWS = [1, 16, 64, 256, 4096]
+MM_ROWS = [1, 16, 64, 256, 1024, 4096]
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 

@@ -159,31 +159,42 @@ __device__ __forceinline__ uint32_t pack_pair(float a, float b)
 // Byte j of a code word holds element 2j (high nibble) and 2j+1 (low); two
 // masks per word turn all eight nibbles into byte offsets into the 16-entry
 // table of code values in LDS.
+// Fragment q (bytes 4q .. 4q+3 of a lane's 16-byte chunk): eight weights.
+template <int XDT>
+__device__ __forceinline__ void dequant_frag(uint32_t word, float a, const float* s_val, Frag<XDT>& f)
+{
+    const char* const tv = reinterpret_cast<const char*>(s_val);
+    uint32_t th = (word >> 2) & 0x3C3C3C3Cu;           // 4 * high nibbles
+    uint32_t tl = (word << 2) & 0x3C3C3C3Cu;           // 4 * low nibbles
+    // Opaque to the compiler (no instruction): it would otherwise fold the
+    // masks into a shift and a mask per nibble, where one bit-field extract
+    // per nibble suffices.
+    asm("" : "+v"(th), "+v"(tl));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float hi = *reinterpret_cast<const float*>(tv + __builtin_amdgcn_ubfe(th, 8 * j, 8)) * a;
+        const float lo = *reinterpret_cast<const float*>(tv + __builtin_amdgcn_ubfe(tl, 8 * j, 8)) * a;
+        if constexpr (XDT == DT_F32) {
+            f.w[2 * j] = hi;
+            f.w[2 * j + 1] = lo;
+        } else {
+            f.w[j] = pack_pair<XDT>(hi, lo);
+        }
+    }
+}
+
+// The 32 weights of a lane's chunk: code value times the block absmax, one
+// binary32 multiply, rounded once to the compute dtype (as qb_dequantize).
+// Byte j of a code word holds element 2j (high nibble) and 2j+1 (low); two
+// masks per word turn all eight nibbles into byte offsets into the 16-entry
+// table of code values in LDS.
 template <int XDT>
 __device__ __forceinline__ void dequant_chunk(const u32x4& cw, float a, const float* s_val, Frag<XDT>* f)
 {
-    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
-    const char* const tv = reinterpret_cast<const char*>(s_val);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {                  // fragment q: bytes 4q .. 4q+3 of the chunk
-        uint32_t th = (words[q] >> 2) & 0x3C3C3C3Cu;           // 4 * high nibbles
-        uint32_t tl = (words[q] << 2) & 0x3C3C3C3Cu;           // 4 * low nibbles
-        // Opaque to the compiler (no instruction): it would otherwise fold
-        // the masks into a shift and a mask per nibble, where one bit-field
-        // extract per nibble suffices.
-        asm("" : "+v"(th), "+v"(tl));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float hi = *reinterpret_cast<const float*>(tv + __builtin_amdgcn_ubfe(th, 8 * j, 8)) * a;
-            const float lo = *reinterpret_cast<const float*>(tv + __builtin_amdgcn_ubfe(tl, 8 * j, 8)) * a;
-            if constexpr (XDT == DT_F32) {
-                f[q].w[2 * j] = hi;
-                f[q].w[2 * j + 1] = lo;
-            } else {
-                f[q].w[j] = pack_pair<XDT>(hi, lo);
-            }
-        }
-    }
+    dequant_frag<XDT>(cw.x, a, s_val, f[0]);
+    dequant_frag<XDT>(cw.y, a, s_val, f[1]);
+    dequant_frag<XDT>(cw.z, a, s_val, f[2]);
+    dequant_frag<XDT>(cw.w, a, s_val, f[3]);
 }
 
 template <int XDT, bool DQ, int MT, bool KF>
@@ -338,6 +349,211 @@ __global__ __launch_bounds__(kMmThreads) void k_dq4_matmul(const void* __restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// many rows of activations: an LDS-tiled product
+// ---------------------------------------------------------------------------
+//
+// For M above the small-batch regime the activations are worth sharing: one
+// workgroup computes a tile of (16 TM) rows x (64 TN) columns of y.  Each
+// step of 128 KH k stages the activation tile (16 TM rows x 128 KH k) in LDS,
+// double-buffered, by direct global-to-LDS loads (no staging registers, no
+// LDS store instructions).  The workgroup has 4 KH waves: wave w takes the columns
+// 16 TN (w % 4) .. 16 TN (w % 4) + 16 TN - 1 and the k half w / 4 of every
+// step (KH = 2), so every wave dequantizes only its own weights, once per
+// workgroup, in registers, straight into MFMA B operands (W never passes
+// through LDS).  With KH = 2 each SIMD holds two waves of the workgroup, and
+// one wave's dequantization overlaps the other's products; their two partial
+// sums meet in LDS at the end.  Per step a wave issues TM x TN x 4 MFMAs
+// (16x16x32, compute dtype bf16 or fp16) against 32 weights per lane and
+// column tile; the next step's activations and codes load meanwhile; one
+// barrier per step.  Lanes use the k order of the small-M kernel within each
+// 128 k (lane group g takes the 32 consecutive k at 32 g, MFMA q their k
+// 8 q .. 8 q + 7), the same for both operands, so the sum is the same set of
+// exact products.
+// Requirements: K a multiple of 128 KH; 16-bit compute dtype.
+
+constexpr int kGmStepK = 128;                      // k per wave and step
+
+
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+
+template <int XDT, bool DQ, int TM, int TN, int KH>
+__global__ __launch_bounds__(256 * KH) void k_dq4_gemm(const void* __restrict__ x, int64_t M, int64_t K,
+                                                       const uint8_t* __restrict__ codes,
+                                                       const float* __restrict__ absmax,
+                                                       const uint8_t* __restrict__ c2,
+                                                       const float* __restrict__ absmax2,
+                                                       const float* __restrict__ offset, int log2B, int log2B2,
+                                                       int code4, int64_t N, void* __restrict__ y,
+                                                       const QbTables* __restrict__ tab)
+{
+    static_assert(XDT != DT_F32, "16-bit compute dtypes only");
+    constexpr int NT = 256 * KH;                      // threads
+    constexpr int BM = 16 * TM;                       // rows of the tile
+    constexpr int BN = 64 * TN;                       // columns of the tile (4 wave columns x 16 TN)
+    constexpr int SK = kGmStepK * KH;                 // k per workgroup step
+    constexpr int PITCH = SK * 2;                     // bytes per LDS row of activations
+    constexpr int RC = SK * 2 / 16;                   // 16-byte chunks per activation row and step
+    constexpr int A_PER = BM * RC / NT;
+    constexpr int NW = NT / 64;
+    static_assert(A_PER * NT == BM * RC, "whole chunks per thread");
+    static_assert(KH == 1 || 4 * TM * TN * 4 * 64 * 4 <= 2 * BM * PITCH, "partial sums fit the LDS tiles");
+    __shared__ __attribute__((aligned(16))) char s_a[2 * BM * PITCH];
+    __shared__ float s_val[16];
+    __shared__ float s_dyn[DQ ? 256 : 1];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wc = wave & 3, h = wave >> 2;           // column quarter, k half
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
+    const int64_t steps = K / SK;
+
+    // rows past M read row M - 1 (their outputs are never stored)
+    const char* const x_base = static_cast<const char*>(x) + m0 * K * 2;
+    // direct loads: the wave's i-th load fills LDS bytes 1024 (i NW + wave)
+    // onwards, 16 per lane; LDS chunk p of row R holds chunk p ^ (R % 16) of
+    // the row (so the 16 rows of an MFMA operand read 16 different banks)
+    uint32_t a_goff[A_PER], a_soff[A_PER];
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+        const int o = (i * NW + wave) * 1024 + 16 * lane, row = o / PITCH, col = (o % PITCH) / 16 ^ (row & 15);
+        const int grow = m0 + row < M ? row : (int)(M - 1 - m0);
+        a_goff[i] = (uint32_t)(grow * K * 2 + col * 16);
+        a_soff[i] = (uint32_t)((i * NW + wave) * 1024);
+    }
+    // weight rows of this lane: column tile j covers rows n0 + 16 (TN wc + j) + r;
+    // the lane's 32 weights of a step start at k 128 h + 32 g
+    const uint8_t* const cw_base = codes + n0 * K / 2;
+    uint32_t cw_off[TN];
+    int64_t e_row[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t nr = 16 * (TN * wc + j) + r;
+        const int64_t rn = n0 + nr < N ? nr : N - 1 - n0;
+        cw_off[j] = (uint32_t)(rn * K / 2 + 64 * h + 16 * g);
+        e_row[j] = (n0 + rn) * K + 128 * h + 32 * g;   // flat index of the lane's first weight of step 0
+    }
+
+    // codes and block constants: those of the step being computed (cw, sc,
+    // sa) and of the next step, loading meanwhile (cwn, scn, san)
+    u32x4 cw[TN], cwn[TN];
+    uint32_t sc[TN], scn[TN];
+    float sa[TN], san[TN];
+    auto load_step = [&](int64_t s) {
+        const char* const xs = x_base + s * SK * 2;
+        char* const dst = s_a + (int)(s & 1) * BM * PITCH;
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i)
+            __builtin_amdgcn_global_load_lds((gptr_t)(xs + a_goff[i]), (lptr_t)(dst + a_soff[i]), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            cwn[j] = ldo<u32x4>(cw_base + s * (SK / 2), cw_off[j]);
+            const int64_t blk = (e_row[j] + s * SK) >> log2B;
+            if constexpr (DQ) {
+                scn[j] = gld<uint8_t>(c2 + blk);
+                san[j] = gld<float>(absmax2 + (blk >> log2B2));
+            } else {
+                san[j] = gld<float>(absmax + blk);
+            }
+        }
+    };
+    // the next step's data has landed (this wave's direct loads included)
+    // and becomes the current one
+    auto next_step = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            cw[j] = cwn[j];
+            sc[j] = DQ ? scn[j] : 0u;
+            sa[j] = san[j];
+        }
+    };
+
+    load_step(0);
+    if (tid < 16) s_val[tid] = (code4 == 0 ? tab->nf4 : tab->fp4)[tid];
+    if constexpr (DQ) {
+        if (tid < 256) s_dyn[tid] = tab->dyn8[tid];
+    }
+    const float mu = DQ ? gld<float>(offset) : 0.0f;
+    next_step();
+    __syncthreads();
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[t][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    Frag<XDT> b[TN][4];
+    auto dequant = [&]() {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const float a = DQ ? s_dyn[sc[j]] * sa[j] + mu : sa[j];   // two rounded operations (nested)
+            dequant_chunk<XDT>(cw[j], a, s_val, b[j]);
+        }
+    };
+    auto products = [&](int buf) {
+        const char* const at = s_a + buf * BM * PITCH + r * PITCH;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                Frag<XDT> af;
+                const int c = 16 * h + 4 * g + q;         // logical 16-byte chunk of the row
+                const u32x4 v = *reinterpret_cast<const u32x4*>(at + t * 16 * PITCH + 16 * (c ^ r));
+                af.w[0] = v.x;
+                af.w[1] = v.y;
+                af.w[2] = v.z;
+                af.w[3] = v.w;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) mma<XDT>(af, b[j][q], acc[t][j]);
+            }
+    };
+    for (int64_t s = 0; s < steps; ++s) {
+        const bool more = s + 1 < steps;
+        dequant();
+        if (more) load_step(s + 1);
+        products((int)(s & 1));
+        if (more) next_step();
+        __syncthreads();
+    }
+
+    if constexpr (KH == 2) {
+        // the k half 1 partial sums through LDS (free after the last barrier)
+        float* const red = reinterpret_cast<float*>(s_a) + wc * (TM * TN * 4 * 64) + lane;
+        if (h == 1) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) red[((t * TN + j) * 4 + i) * 64] = acc[t][j][i];
+        }
+        __syncthreads();
+        if (h == 1) return;
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[t][j][i] += red[((t * TN + j) * 4 + i) * 64];
+    }
+
+    // C of a 16x16 tile: lane (row / 4) * 16 + column, element row % 4
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t nn = n0 + 16 * (TN * wc + j) + r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t m = m0 + 16 * t + 4 * g + i;
+                if (m < M && nn < N) store1<XDT>(y, m * N + nn, acc[t][j][i]);
+            }
+        }
+}
+
 // Enqueue `kernel` on a 2-D grid of kMmThreads-thread workgroups; returns
 // this launch's own status.
 template <typename... KArgs, typename... Args>
@@ -366,11 +582,71 @@ hipError_t mm_as(const void* x, int64_t M, int64_t K, const uint8_t* codes, cons
                      c2, absmax2, offset, log2B, log2B2, code4, N, y, tab);
 }
 
+// The tiled kernel on a grid of (BN-column, BM-row) tiles.
+template <int XDT, bool DQ, int TM, int TN, int KH>
+hipError_t gm_as(const void* x, int64_t M, int64_t K, const uint8_t* codes, const float* absmax, const uint8_t* c2,
+                 const float* absmax2, const float* offset, int log2B, int log2B2, int code4, int64_t N, void* y,
+                 const QbTables* tab, hipStream_t s)
+{
+    const int64_t gx = (N + 64 * TN - 1) / (64 * TN), gy = (M + 16 * TM - 1) / (16 * TM);
+    if (gx >= (int64_t(1) << 31) || gy > 65535) return hipErrorInvalidValue;
+    std::tuple<const void*, int64_t, int64_t, const uint8_t*, const float*, const uint8_t*, const float*,
+               const float*, int, int, int, int64_t, void*, const QbTables*>
+        vals(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab);
+    return std::apply(
+        [&](auto&... v) {
+            void* ptrs[] = {static_cast<void*>(&v)...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(k_dq4_gemm<XDT, DQ, TM, TN, KH>),
+                                   dim3((unsigned)gx, (unsigned)gy), dim3(256 * KH), ptrs, 0, s);
+        },
+        vals);
+}
+
+// Rows of activations from which the tiled kernel takes over (16-bit compute
+// dtypes, K a multiple of 128), and from which it uses the big tile shape.
+#ifndef QB_GM_MIN_M
+#define QB_GM_MIN_M 65
+#endif
+#ifndef QB_GM_BIG_M
+#define QB_GM_BIG_M 512
+#endif
+// tile shapes (16 TM rows x 64 TN columns) below and from QB_GM_BIG_M rows
+#ifndef QB_GM_SMALL_TM
+#define QB_GM_SMALL_TM 4
+#endif
+#ifndef QB_GM_SMALL_TN
+#define QB_GM_SMALL_TN 1
+#endif
+#ifndef QB_GM_BIG_TM
+#define QB_GM_BIG_TM 8
+#endif
+#ifndef QB_GM_BIG_TN
+#define QB_GM_BIG_TN 2
+#endif
+
+template <int XDT, bool DQ, int KH>
+hipError_t gm_kh(int64_t M, const void* x, int64_t K, const uint8_t* codes, const float* absmax, const uint8_t* c2,
+                 const float* absmax2, const float* offset, int log2B, int log2B2, int code4, int64_t N, void* y,
+                 const QbTables* tab, hipStream_t s)
+{
+    if (M >= QB_GM_BIG_M)
+        return gm_as<XDT, DQ, QB_GM_BIG_TM, QB_GM_BIG_TN, KH>(x, M, K, codes, absmax, c2, absmax2, offset, log2B,
+                                                              log2B2, code4, N, y, tab, s);
+    return gm_as<XDT, DQ, QB_GM_SMALL_TM, QB_GM_SMALL_TN, KH>(x, M, K, codes, absmax, c2, absmax2, offset, log2B,
+                                                              log2B2, code4, N, y, tab, s);
+}
+
 template <int XDT, bool DQ>
 hipError_t mm_mt(int64_t M, const void* x, int64_t K, const uint8_t* codes, const float* absmax, const uint8_t* c2,
                  const float* absmax2, const float* offset, int log2B, int log2B2, int code4, int64_t N, void* y,
                  const QbTables* tab, hipStream_t s)
 {
+    if constexpr (XDT != DT_F32) {
+        if (M >= QB_GM_MIN_M && K % (2 * kGmStepK) == 0)
+            return gm_kh<XDT, DQ, 2>(M, x, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);
+        if (M >= QB_GM_MIN_M && K % kGmStepK == 0)
+            return gm_kh<XDT, DQ, 1>(M, x, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);
+    }
     if (M <= 16) return mm_as<XDT, DQ, 1>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);
     if (M <= 32) return mm_as<XDT, DQ, 2>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);
     return mm_as<XDT, DQ, 4>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);

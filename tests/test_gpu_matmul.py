@@ -143,3 +143,57 @@ def test_7b_layer_shapes(M, NK):
     x, codes, scale, nst = make_case(M, K, N, 64, oracle.BF16, True, seed=N + K + M)
     y = run_gpu(x, oracle.BF16, codes, scale, nst, oracle.NF4, 64, N)
     check(y, x, oracle.BF16, codes, scale, oracle.NF4, 64, N, f"7B {N}x{K} M={M}")
+
+
+# the tiled kernel (16-bit compute dtypes, K a multiple of 128, M >= 65): tiles
+# of 64 x 64 below 512 rows, 128 x 128 from 512; ragged M and N, one step of K
+TILED = [(65, 128, 64), (100, 256, 130), (200, 1024, 197), (511, 512, 257), (512, 384, 128), (700, 640, 300),
+         (1000, 1152, 129)]
+
+
+@pytest.mark.parametrize("M,K,N", TILED)
+@pytest.mark.parametrize("xdt", [oracle.BF16, oracle.F16])
+def test_tiled_shapes(M, K, N, xdt):
+    x, codes, scale, _ = make_case(M, K, N, 64, xdt, False, seed=M + 3 * K + N)
+    y = run_gpu(x, xdt, codes, scale, None, oracle.NF4, 64, N)
+    check(y, x, xdt, codes, scale, oracle.NF4, 64, N, f"tiled M={M} K={K} N={N} dt={xdt}")
+
+
+@pytest.mark.parametrize("code", [oracle.NF4, oracle.FP4])
+@pytest.mark.parametrize("B", [64, 256, 4096])
+@pytest.mark.parametrize("nested", [False, True])
+@pytest.mark.parametrize("M", [96, 600])
+def test_tiled_codes_blocks_and_nesting(code, B, nested, M):
+    K, N = 1024, 192
+    x, codes, scale, nst = make_case(M, K, N, B, oracle.BF16, nested, seed=B + code + 5 * nested + M)
+    y = run_gpu(x, oracle.BF16, codes, scale, nst, code, B, N)
+    check(y, x, oracle.BF16, codes, scale, code, B, N, f"tiled M={M} code={code} B={B} nested={nested}")
+
+
+def test_tiled_blocks_spanning_rows():
+    M, K, N, B = 130, 128, 70, 4096                     # B > K: one absmax over parts of several rows
+    x, codes, scale, _ = make_case(M, K, N, B, oracle.BF16, False, seed=19)
+    y = run_gpu(x, oracle.BF16, codes, scale, None, oracle.NF4, B, N)
+    check(y, x, oracle.BF16, codes, scale, oracle.NF4, B, N, "tiled B > K")
+
+
+def test_tiled_repeatable():
+    M, K, N = 640, 2048, 384
+    x, codes, scale, _ = make_case(M, K, N, 64, oracle.BF16, False, seed=23)
+    y1 = run_gpu(x, oracle.BF16, codes, scale, None, oracle.NF4, 64, N)
+    y2 = run_gpu(x, oracle.BF16, codes, scale, None, oracle.NF4, 64, N)
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("M", [256, 1024])
+@pytest.mark.parametrize("NK", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_7b_layer_shapes_many_rows(M, NK):
+    """The 7B projection shapes at 256 and 1024 rows (NF4, nested, B = 64, bf16):
+    every row computed on the GPU; 48 seeded rows (the first, the last and
+    random ones) checked against the oracle's exact product, rows being
+    independent of each other."""
+    N, K = NK
+    x, codes, scale, nst = make_case(M, K, N, 64, oracle.BF16, True, seed=N + K + M)
+    y = run_gpu(x, oracle.BF16, codes, scale, nst, oracle.NF4, 64, N)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).choice(M, 46, replace=False)]))
+    check(y[rows], x[rows], oracle.BF16, codes, scale, oracle.NF4, 64, N, f"7B {N}x{K} M={M} (sampled rows)")
