@@ -645,6 +645,8 @@ def bench_roundtrip8(torch, qb, inputs, dev, args):
 
 MM_SHAPES = [(4096, 4096), (11008, 4096), (4096, 11008)]      # (N, K) of the 7B projections
 MM_ROWS = [1, 16, 64, 256, 1024, 4096]
+MM_GROUPS = [("q/k/v", [4096] * 3, 4096), ("gate/up", [11008] * 2, 4096)]   # projections of one 7B layer sharing x
+MM_GROUP_ROWS = [1, 4, 16]
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -692,6 +694,35 @@ def bench_matmul(torch, qb, inputs, dev, args):
                                   "TFLOP/s": flops / fused / 1e9,
                                   "frac_of_bf16_mfma_peak": flops / fused / 1e9 / MFMA_BF16_PEAK_TFLOPS})
             log(f"N={N} K={K} M={M}: fused {fused * 1e3:.1f} us, unfused {ref * 1e3:.1f} us")
+    # one layer's projections that share x, in one grouped launch against one call per weight
+    out["grouped"] = []
+    for name, Ns, K in MM_GROUPS:
+        ws = []
+        for N in Ns:
+            nb = N * K // W4_BLOCK
+            codes = torch.randint(0, 256, (N * K // 2,), dtype=torch.uint8, device=dev, generator=g)
+            c2 = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=dev, generator=g)
+            a2 = torch.full((-(-nb // W4_BLOCK2),), 0.02, device=dev)
+            mu = torch.full((4,), 0.03, device=dev)
+            ws.append((codes, c2, a2, mu, qb.make_dq(c2, a2, mu, W4_BLOCK2), N))
+        for M in MM_GROUP_ROWS:
+            x = inputs.normal(M * K, 1.0, seed=args.seed + M, device=dev, dtype=torch.bfloat16).view(M, K)
+            ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for *_, N in ws]
+            table = qb.matmul_weights([(w[0], None, w[4], w[5], y) for w, y in zip(ws, ys)])
+            grp = time_back_to_back(torch, lambda: qb.qb_dequant_matmul_grouped(x, table, len(ws), 1, W4_BLOCK,
+                                                                                  W4_BLOCK2), reps=args.steps)
+
+            def singles():
+                for w, y in zip(ws, ys):
+                    qb.qb_dequant_matmul(x, w[0], None, 1, W4_BLOCK, w[5], y, dq=w[4])
+
+            one = time_back_to_back(torch, singles, reps=args.steps)
+            nbytes = sum(dq4_matmul_bytes(M, N, K) for N in Ns) - 2 * M * K * (len(Ns) - 1)
+            out["grouped"].append({"layer": name, "N": Ns, "K": K, "M": M, "grouped_us": grp * 1e3,
+                                   "single_calls_us": one * 1e3, "speedup": one / grp,
+                                   "GB/s": nbytes / grp / 1e6, "frac_of_hbm_peak": nbytes / grp / 1e6 / HBM_PEAK_GBS})
+            log(f"{name} M={M}: grouped {grp * 1e3:.1f} us ({nbytes / grp / 1e6 / HBM_PEAK_GBS:.1%} of HBM peak), "
+                f"{len(Ns)} calls {one * 1e3:.1f} us")
     print(json.dumps(out), flush=True)
 
 

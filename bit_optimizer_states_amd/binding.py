@@ -63,6 +63,14 @@ class qb_dequant_tensor(ctypes.Structure):
                 ("n", ctypes.c_int64)]
 
 
+class qb_matmul_weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p), ("c2", ctypes.c_void_p),
+                ("absmax2", ctypes.c_void_p), ("offset", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64)]
+
+
+QB_MATMUL_GROUP_MAX = 8
+
 _lib = None
 
 
@@ -102,6 +110,9 @@ def lib():
         L.qb_paged_workspace_bytes.restype = sz
         L.qb_dequant_matmul.argtypes = [vp, i32, i64, i64, vp, vp, ctypes.POINTER(qb_dq), i32, i32, i64, vp, vp]
         L.qb_dequant_matmul.restype = ctypes.c_int
+        L.qb_dequant_matmul_grouped.argtypes = [vp, i32, i64, i64, ctypes.POINTER(qb_matmul_weight), i32, i32, i32,
+                                                i32, vp]
+        L.qb_dequant_matmul_grouped.restype = ctypes.c_int
         L.qb_code_table_bytes.argtypes = []
         L.qb_code_table_bytes.restype = sz
         L.qb_linear_code.argtypes = [vp]
@@ -223,6 +234,26 @@ def qb_dequant_matmul(x, codes, absmax, code, blocksize, N, y, dq=None, stream=N
     _check(lib().qb_dequant_matmul(_ptr(x), _dtype(x), int(M), int(K), _ptr(codes), _ptr(absmax),
                                    ctypes.byref(dq) if dq is not None else None, int(code), int(blocksize), int(N),
                                    _ptr(y), _stream(stream)), "qb_dequant_matmul")
+
+
+def matmul_weights(weights):
+    """ctypes array of qb_matmul_weight from (codes, absmax, dq, N, y) tuples
+    (absmax None with a qb_dq, dq None without)."""
+    arr = (qb_matmul_weight * max(len(weights), 1))()
+    for i, (codes, absmax, dq, N, y) in enumerate(weights):
+        arr[i] = qb_matmul_weight(_ptr(codes), _ptr(absmax), dq.codes if dq is not None else None,
+                                  dq.absmax2 if dq is not None else None, dq.offset if dq is not None else None,
+                                  _ptr(y), int(N))
+    return arr
+
+
+def qb_dequant_matmul_grouped(x, table, count, code, blocksize, blocksize2=256, stream=None):
+    """y_i = x W_i^T for the `count` weights of `table` (matmul_weights) in one
+    launch; x [M, K] of the compute dtype."""
+    M, K = x.shape
+    _check(lib().qb_dequant_matmul_grouped(_ptr(x), _dtype(x), int(M), int(K), table, int(count), int(code),
+                                           int(blocksize), int(blocksize2), _stream(stream)),
+           "qb_dequant_matmul_grouped")
 
 
 def optim_hparams(kind, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, dampening=0.0, nesterov=False,

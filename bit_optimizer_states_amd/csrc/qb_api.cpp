@@ -578,6 +578,33 @@ qb_status qb_dequant_matmul(const void* x, qb_dtype xdt, int64_t M, int64_t K, c
                                         static_cast<hipStream_t>(stream)));
 }
 
+qb_status qb_dequant_matmul_grouped(const void* x, qb_dtype xdt, int64_t M, int64_t K, const qb_matmul_weight* weights,
+                                    int32_t count, qb_code code, int32_t blocksize, int32_t blocksize2, void* stream)
+{
+    if (count < 0 || count > QB_MATMUL_GROUP_MAX || M < 0 || K <= 0 || K % 32 != 0 || K >= (int64_t(1) << 24) ||
+        !valid_dtype(xdt) || !is4(code) || !pow2_block(blocksize))
+        return QB_EINVAL;
+    if (count == 0 || M == 0) return QB_OK;
+    if (!weights || !x) return QB_EINVAL;
+    if (!aligned16(x)) return QB_EALIGN;
+    MmWeight w[kMmGroupMax];
+    int n = 0, mode = -1;
+    for (int32_t i = 0; i < count; ++i) {
+        const qb_matmul_weight& t = weights[i];
+        if (t.N < 0 || t.N > INT64_MAX / K) return QB_EINVAL;
+        if (t.N == 0) continue;                        // skipped, whatever its pointers
+        DequantDesc d;
+        qb_status st = dequant_desc(t.codes, t.absmax, t.c2, t.absmax2, t.offset, blocksize2, t.N * K, t.y, blocksize,
+                                    &mode, &d);
+        if (st != QB_OK) return st;
+        w[n++] = MmWeight{t.codes, t.absmax, t.c2, t.absmax2, t.offset, t.y, t.N};
+    }
+    if (n == 0) return QB_OK;
+    if (!device_tables()) return QB_EINIT;
+    return hip_status(launch_dq4_matmul_grouped(x, (int)xdt, M, K, w, n, blocksize, mode == 1 ? blocksize2 : 256,
+                                                code4_index(code), static_cast<hipStream_t>(stream)));
+}
+
 qb_status qb_multi_tensor_dequantize(const qb_dequant_tensor* tensors, int32_t count, qb_code code,
                                      int32_t blocksize, int32_t blocksize2, qb_dtype ydt, void* ws, size_t ws_bytes,
                                      void* stream)

@@ -203,6 +203,25 @@ hipError_t launch_dq4_matmul(const void* x, int xdt, int64_t M, int64_t K, const
                              const uint8_t* c2, const float* absmax2, const float* offset, int B, int B2, int code4,
                              int64_t N, void* y, hipStream_t s);
 
+// One weight of a grouped product: plain (absmax) or nested (c2, absmax2,
+// offset); y [M, N].
+struct MmWeight {
+    const uint8_t* codes;
+    const float* absmax;
+    const uint8_t* c2;
+    const float* absmax2;
+    const float* offset;
+    void* y;
+    int64_t N;
+};
+constexpr int kMmGroupMax = 8;
+
+// launch_dq4_matmul for `count` (1 .. kMmGroupMax) weights against the same x,
+// all plain or all nested, one code and block sizes: one launch in the
+// small-M regime, one launch per weight in the tiled kernel's.
+hipError_t launch_dq4_matmul_grouped(const void* x, int xdt, int64_t M, int64_t K, const MmWeight* w, int count,
+                                     int B, int B2, int code4, hipStream_t s);
+
 // Exact mean of the absmax of one tensor (map == nullptr) or of the `count`
 // tensors of map (second-pass descriptors) into offset[0].
 hipError_t launch_dq_mean(const QuantDesc& single, const TileMap<QuantDesc>* map, int count,

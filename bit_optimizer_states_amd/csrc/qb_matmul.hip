@@ -197,15 +197,14 @@ __device__ __forceinline__ void dequant_chunk(const u32x4& cw, float a, const fl
     dequant_frag<XDT>(cw.w, a, s_val, f[3]);
 }
 
+// One workgroup's tile: output columns 16 ntile .. 16 ntile + 15 of y, rows
+// 16 MT blockIdx.y onwards.
 template <int XDT, bool DQ, int MT, bool KF>
-__global__ __launch_bounds__(kMmThreads) void k_dq4_matmul(const void* __restrict__ x, int64_t M, int64_t K,
-                                                           const uint8_t* __restrict__ codes,
-                                                           const float* __restrict__ absmax,
-                                                           const uint8_t* __restrict__ c2,
-                                                           const float* __restrict__ absmax2,
-                                                           const float* __restrict__ offset, int log2B, int log2B2,
-                                                           int code4, int64_t N, void* __restrict__ y,
-                                                           const QbTables* __restrict__ tab)
+__device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, int64_t K,
+                                        const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
+                                        const uint8_t* __restrict__ c2, const float* __restrict__ absmax2,
+                                        const float* __restrict__ offset, int log2B, int log2B2, int code4, int64_t N,
+                                        void* __restrict__ y, const QbTables* __restrict__ tab, int64_t ntile)
 {
     __shared__ float s_val[16];
     __shared__ float s_dyn[DQ ? 256 : 1];
@@ -213,7 +212,7 @@ __global__ __launch_bounds__(kMmThreads) void k_dq4_matmul(const void* __restric
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: scalar step bases
     const int r = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16, m0 = (int64_t)blockIdx.y * 16 * MT;
+    const int64_t n0 = ntile * 16, m0 = (int64_t)blockIdx.y * 16 * MT;
     // Weight rows past N read row N - 1 instead (their outputs are never
     // stored); activation rows past M are not loaded and stay zero.
     constexpr int ES = XDT == DT_F32 ? 4 : 2;         // bytes per activation
@@ -347,6 +346,42 @@ __global__ __launch_bounds__(kMmThreads) void k_dq4_matmul(const void* __restric
         const int64_t m = m0 + ml, nn = n0 + nl;
         if (m < M && nn < N) store1<XDT>(y, m * N + nn, sum);
     }
+}
+
+template <int XDT, bool DQ, int MT, bool KF>
+__global__ __launch_bounds__(kMmThreads) void k_dq4_matmul(const void* __restrict__ x, int64_t M, int64_t K,
+                                                           const uint8_t* __restrict__ codes,
+                                                           const float* __restrict__ absmax,
+                                                           const uint8_t* __restrict__ c2,
+                                                           const float* __restrict__ absmax2,
+                                                           const float* __restrict__ offset, int log2B, int log2B2,
+                                                           int code4, int64_t N, void* __restrict__ y,
+                                                           const QbTables* __restrict__ tab)
+{
+    mm_tile<XDT, DQ, MT, KF>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab,
+                             (int64_t)blockIdx.x);
+}
+
+// Several weights against the same activations in one launch (the column
+// tiles of weight i are tiles tile0[i] .. tile0[i + 1] - 1 of the grid's x
+// dimension): the same tiles, bit for bit, as one launch per weight.
+struct MmGroup {
+    MmWeight w[kMmGroupMax];
+    int64_t tile0[kMmGroupMax + 1];
+    int count;
+};
+
+template <int XDT, bool DQ, int MT, bool KF>
+__global__ __launch_bounds__(kMmThreads) void k_dq4_matmul_grouped(const void* __restrict__ x, int64_t M, int64_t K,
+                                                                   const MmGroup grp, int log2B, int log2B2,
+                                                                   int code4, const QbTables* __restrict__ tab)
+{
+    const int64_t bx = blockIdx.x;
+    int i = 0;
+    while (i + 1 < grp.count && bx >= grp.tile0[i + 1]) ++i;   // uniform: the kernel arguments are scalar
+    const MmWeight& w = grp.w[i];
+    mm_tile<XDT, DQ, MT, KF>(x, M, K, w.codes, w.absmax, w.c2, w.absmax2, w.offset, log2B, log2B2, code4, w.N, w.y,
+                             tab, bx - grp.tile0[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -674,6 +709,72 @@ hipError_t launch_dq4_matmul(const void* x, int xdt, int64_t M, int64_t K, const
     case DT_F32:
         return dq ? mm_mt<DT_F32, true>(M, x, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s)
                   : mm_mt<DT_F32, false>(M, x, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+namespace {
+
+template <int XDT, bool DQ, int MT>
+hipError_t mmg_as(const void* x, int64_t M, int64_t K, const MmGroup& grp, int log2B, int log2B2, int code4,
+                  const QbTables* tab, hipStream_t s)
+{
+    const int64_t gx = grp.tile0[grp.count], gy = (M + 16 * MT - 1) / (16 * MT);
+    if (gx >= (int64_t(1) << 31) || gy > 65535) return hipErrorInvalidValue;
+    if (K % kMmStepK == 0)
+        return launch_2d(k_dq4_matmul_grouped<XDT, DQ, MT, true>, dim3((unsigned)gx, (unsigned)gy), s, x, M, K, grp,
+                         log2B, log2B2, code4, tab);
+    return launch_2d(k_dq4_matmul_grouped<XDT, DQ, MT, false>, dim3((unsigned)gx, (unsigned)gy), s, x, M, K, grp,
+                     log2B, log2B2, code4, tab);
+}
+
+template <int XDT, bool DQ>
+hipError_t mmg_mt(int64_t M, const void* x, int64_t K, const MmGroup& grp, int log2B, int log2B2, int code4,
+                  const QbTables* tab, hipStream_t s)
+{
+    if (M <= 16) return mmg_as<XDT, DQ, 1>(x, M, K, grp, log2B, log2B2, code4, tab, s);
+    if (M <= 32) return mmg_as<XDT, DQ, 2>(x, M, K, grp, log2B, log2B2, code4, tab, s);
+    return mmg_as<XDT, DQ, 4>(x, M, K, grp, log2B, log2B2, code4, tab, s);
+}
+
+}  // namespace
+
+hipError_t launch_dq4_matmul_grouped(const void* x, int xdt, int64_t M, int64_t K, const MmWeight* w, int count,
+                                     int B, int B2, int code4, hipStream_t s)
+{
+    const bool dq = count > 0 && w[0].c2 != nullptr;
+    // the tiled kernel's regime: one launch per weight (each has tiles enough)
+    if (xdt != DT_F32 && M >= QB_GM_MIN_M && K % kGmStepK == 0) {
+        for (int i = 0; i < count; ++i) {
+            const hipError_t e = launch_dq4_matmul(x, xdt, M, K, w[i].codes, w[i].absmax, w[i].c2, w[i].absmax2,
+                                                   w[i].offset, B, B2, code4, w[i].N, w[i].y, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    const QbTables* tab = device_tables();
+    if (!tab) return hipErrorNotInitialized;
+    if (count < 1 || count > kMmGroupMax) return hipErrorInvalidValue;
+    MmGroup grp{};
+    grp.count = count;
+    for (int i = 0; i < count; ++i) {
+        grp.w[i] = w[i];
+        grp.tile0[i + 1] = grp.tile0[i] + (w[i].N + 15) / 16;
+    }
+    for (int i = count; i < kMmGroupMax; ++i) grp.tile0[i + 1] = grp.tile0[count];
+    int log2B = 0, log2B2 = 0;
+    while ((1 << log2B) < B) ++log2B;
+    while ((1 << log2B2) < B2) ++log2B2;
+    switch (xdt) {
+    case DT_BF16:
+        return dq ? mmg_mt<DT_BF16, true>(M, x, K, grp, log2B, log2B2, code4, tab, s)
+                  : mmg_mt<DT_BF16, false>(M, x, K, grp, log2B, log2B2, code4, tab, s);
+    case DT_F16:
+        return dq ? mmg_mt<DT_F16, true>(M, x, K, grp, log2B, log2B2, code4, tab, s)
+                  : mmg_mt<DT_F16, false>(M, x, K, grp, log2B, log2B2, code4, tab, s);
+    case DT_F32:
+        return dq ? mmg_mt<DT_F32, true>(M, x, K, grp, log2B, log2B2, code4, tab, s)
+                  : mmg_mt<DT_F32, false>(M, x, K, grp, log2B, log2B2, code4, tab, s);
     default: return hipErrorInvalidValue;
     }
 }

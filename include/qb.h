@@ -323,6 +323,46 @@ qb_status qb_dequant_matmul(const void* x, qb_dtype xdt, int64_t M, int64_t K, c
                             void* y, void* stream);
 
 /*
+ * One weight of qb_dequant_matmul_grouped: codes, absmax / nested constants
+ * and y as for qb_dequant_matmul; N its rows (the layer's output features).
+ * A plain weight gives absmax and leaves c2, absmax2, offset NULL; a nested
+ * one gives c2, absmax2, offset (the qb_dq fields) and absmax NULL.
+ */
+typedef struct {
+    const uint8_t* codes;
+    const float*   absmax;
+    const uint8_t* c2;
+    const float*   absmax2;
+    const float*   offset;
+    void*          y;
+    int64_t        N;
+} qb_matmul_weight;
+
+#define QB_MATMUL_GROUP_MAX 8
+
+/*
+ * qb_dequant_matmul_grouped -- qb_dequant_matmul for up to QB_MATMUL_GROUP_MAX
+ * weights that multiply the same activations (a layer's query, key and value
+ * projections; its gate and up projections): y_i = x W_i^T, each y_i bit for
+ * bit the y of a qb_dequant_matmul call on weight i.  Same page citations as
+ * qb_dequant_matmul.
+ *   x, xdt, M, K         as for qb_dequant_matmul (one x for all weights).
+ *   weights              host array of `count` descriptors (read during the
+ *                        call only); every weight is plain or every one is
+ *                        nested (else QB_EUNSUPPORTED); code, blocksize and
+ *                        blocksize2 (nested only) are shared.
+ * Weights with N == 0 are skipped (their pointers are not looked at);
+ * count == 0 or M == 0 is a no-op;
+ * count > QB_MATMUL_GROUP_MAX is QB_EINVAL.  Up to 64 rows of x (and for
+ * binary32 x, or K not a multiple of 128, at any M) the column tiles of all
+ * weights are one kernel launch, so small-batch projections fill the GPU
+ * together; in the LDS-tiled regime it launches once per weight.
+ */
+qb_status qb_dequant_matmul_grouped(const void* x, qb_dtype xdt, int64_t M, int64_t K,
+                                    const qb_matmul_weight* weights, int32_t count, qb_code code,
+                                    int32_t blocksize, int32_t blocksize2, void* stream);
+
+/*
  * qb_multi_tensor_dequantize -- qb_dequantize on `count` tensors in ONE kernel
  * launch (same code, block size, nested block size and output dtype for all;
  * the result equals a loop of single-tensor calls, bit for bit).  Dequantizing

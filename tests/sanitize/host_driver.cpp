@@ -129,6 +129,14 @@ int main()
     // fused 4-bit product
     EXPECT(qb_dequant_matmul(A, QB_BF16, 16, 4096, U, F, nullptr, QB_NF4, 64, 4096, A, nullptr), QB_EINIT);
     EXPECT(qb_dequant_matmul(A, QB_BF16, 16, 4001, U, F, nullptr, QB_NF4, 64, 4096, A, nullptr), QB_EINVAL);
+    // grouped: the full group of eight (one empty, skipped), then one too many
+    qb_matmul_weight wts[QB_MATMUL_GROUP_MAX + 1];
+    for (int i = 0; i <= QB_MATMUL_GROUP_MAX; ++i) wts[i] = qb_matmul_weight{U, F, nullptr, nullptr, nullptr, A, 64 + i};
+    wts[3].N = 0;
+    wts[3].codes = nullptr;
+    EXPECT(qb_dequant_matmul_grouped(A, QB_BF16, 4, 4096, wts, QB_MATMUL_GROUP_MAX, QB_NF4, 64, 256, nullptr), QB_EINIT);
+    EXPECT(qb_dequant_matmul_grouped(A, QB_BF16, 4, 4096, wts, QB_MATMUL_GROUP_MAX + 1, QB_NF4, 64, 256, nullptr),
+           QB_EINVAL);
 
     if (failures) {
         std::fprintf(stderr, "host driver: %d unexpected results\n", failures);

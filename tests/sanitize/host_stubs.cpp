@@ -44,6 +44,11 @@ hipError_t launch_dq4_matmul(const void*, int, int64_t, int64_t, const uint8_t*,
 {
     return hipErrorInvalidValue;
 }
+hipError_t launch_dq4_matmul_grouped(const void*, int, int64_t, int64_t, const MmWeight*, int, int, int, int,
+                                     hipStream_t)
+{
+    return hipErrorInvalidValue;
+}
 hipError_t launch_dq_mean(const QuantDesc&, const TileMap<QuantDesc>*, int, const unsigned long long*, hipStream_t)
 {
     return hipErrorInvalidValue;

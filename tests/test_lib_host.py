@@ -442,6 +442,32 @@ def test_dequant_matmul_arguments_rejected_before_launch(qb):
     assert f(A, BF16, 4, 64, A, A, None, NF4, 64, 10, A + 4, None) == qb.QB_EALIGN
 
 
+def test_grouped_matmul_arguments_rejected_before_launch(qb):
+    L = qb.lib()
+    A = 0x100000
+    W = qb.qb_matmul_weight
+    plain = W(A, A, None, None, None, A, 64)
+    nested = W(A, None, A, A, A, A, 64)
+    tab = lambda *e: (W * len(e))(*e)
+    f = L.qb_dequant_matmul_grouped
+    assert f(A, 2, 1, 256, tab(plain), -1, 1, 64, 256, None) == qb.QB_EINVAL                 # count < 0
+    assert f(A, 2, 1, 256, tab(*[plain] * 9), 9, 1, 64, 256, None) == qb.QB_EINVAL          # above the group limit
+    assert f(A, 2, 1, 256, tab(plain), 0, 1, 64, 256, None) == qb.QB_OK                     # count == 0: no-op
+    assert f(A, 2, 0, 256, tab(plain), 1, 1, 64, 256, None) == qb.QB_OK                     # M == 0: no-op
+    assert f(A, 2, 1, 100, tab(plain), 1, 1, 64, 256, None) == qb.QB_EINVAL                 # K not a multiple of 32
+    assert f(A, 2, 1, 256, tab(plain), 1, 0, 64, 256, None) == qb.QB_EINVAL                 # 8-bit code
+    assert f(A, 2, 1, 256, tab(plain), 1, 1, 100, 256, None) == qb.QB_EINVAL                # blocksize
+    assert f(A, 9, 1, 256, tab(plain), 1, 1, 64, 256, None) == qb.QB_EINVAL                 # dtype
+    assert f(None, 2, 1, 256, tab(plain), 1, 1, 64, 256, None) == qb.QB_EINVAL              # no x
+    assert f(A + 2, 2, 1, 256, tab(plain), 1, 1, 64, 256, None) == qb.QB_EALIGN             # misaligned x
+    assert f(A, 2, 1, 256, tab(plain, nested), 2, 1, 64, 256, None) == qb.QB_EUNSUPPORTED   # mixed nesting
+    assert f(A, 2, 1, 256, tab(nested), 1, 1, 64, 100, None) == qb.QB_EINVAL                # blocksize2
+    assert f(A, 2, 1, 256, tab(W(A, A, None, None, None, A + 8, 64)), 1, 1, 64, 256, None) == qb.QB_EALIGN
+    assert f(A, 2, 1, 256, tab(W(A, A, None, None, None, A, -1)), 1, 1, 64, 256, None) == qb.QB_EINVAL
+    assert f(A, 2, 1, 256, tab(W(None, A, None, None, None, A, 64)), 1, 1, 64, 256, None) == qb.QB_EINVAL
+    assert f(A, 2, 1, 256, tab(W(None, None, None, None, None, None, 0)), 1, 1, 64, 256, None) == qb.QB_OK  # N == 0
+
+
 def test_paged_step_arguments_and_workspace(qb):
     L = qb.lib()
     A, A2 = 0x100000, 0x200000
