@@ -343,6 +343,19 @@ __device__ __forceinline__ float div_by_block(float x, float a, float r)
     return __builtin_fmaf(e, r, q);
 }
 
+// div_by_block of an fp16 x, read by the first two operations as a
+// mixed-precision operand.  x * r is taken as a fused multiply-add onto +0:
+// the same product except that -0 becomes +0, which div_by_block's result
+// for x = -0 is anyway.
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float div_by_block_h(_Float16 x, float a, float r)
+{
+    const float q = __builtin_fmaf((float)x, r, 0.0f);
+    const float e = __builtin_fmaf(-q, a, (float)x);
+    return __builtin_fmaf(e, r, q);
+}
+
 __device__ __forceinline__ bool fast_div_ok(float a)
 {
     return a >= 0x1p-60f && a <= 0x1p60f;
@@ -519,13 +532,30 @@ __device__ __forceinline__ void stage_user_enc(UserEncLds& s, const UserCode* __
     fst.store(s.first, tid);
 }
 
-// 4-bit code (NF4 or FP4 by the table) of a normalized value in [-1, 1]:
-// bucket (int)(16 nv + 16) in [0, 32] (16 nv is exact, so the fused form
-// rounds like the separate operations), then below or above the bucket's one
-// threshold.  |nv| <= 1 holds for every finite input (nv = x / absmax).
-__device__ __forceinline__ uint32_t enc_4bit(float nv, const uint2* __restrict__ lut)
+// 4-bit code of a normalized value in [-1, 1] from the bucket table in LDS:
+// bucket k = 16 nv + 16 rounded to the nearest integer, ties to even, in
+// [0, 32] (one fused multiply-add onto 1.5 * 2^23: the sum's float bits are
+// 0x4B400000 + k, so one shift-and-add gives the entry's byte address), then
+// below or above the bucket's one threshold.  NF4 (codes ascend with the
+// values): the payload is the code below, the code above is one more.  FP4:
+// the payload holds the code below in byte 0 and the one above in byte 1.
+// |nv| <= 1 holds for every finite input (nv = x / absmax).
+__device__ __forceinline__ const uint2& lut4_entry(float nv, const uint2* __restrict__ lut)
 {
-    const uint2 e = lut[(int)__builtin_fmaf(nv, 16.0f, 16.0f)];
+    const uint32_t t = fbits(__builtin_fmaf(nv, 16.0f, 0x1.8p23f + 16.0f));
+    const uint32_t off = (t << 3) - (0x4B400000u << 3);            // 8 k (mod 2^32)
+    return *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(lut) + off);
+}
+
+__device__ __forceinline__ uint32_t enc_nf4(float nv, const uint2* __restrict__ lut)
+{
+    const uint2 e = lut4_entry(nv, lut);
+    return e.y + (nv >= ffrom(e.x) ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t enc_fp4(float nv, const uint2* __restrict__ lut)
+{
+    const uint2 e = lut4_entry(nv, lut);
     return __builtin_amdgcn_ubfe(e.y, nv >= ffrom(e.x) ? 8u : 0u, 8u);
 }
 

@@ -245,12 +245,38 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
     const int bt = tid / G::LPB, l = tid % G::LPB;
     const void* const xt = static_cast<const char*>(d.x) + tbase * (XDT == DT_F32 ? 4 : 2);
 
-    // loads of every sub-tile first
-    float v[G::R][G::EPT];
+    // loads of every sub-tile first.  RAW (4-bit codes of fp16 input): the
+    // halves stay packed two per word; the block maximum is taken on them
+    // with packed fp16 operations and the division reads them through
+    // mixed-precision fused multiply-adds, so no element is converted.
+    constexpr bool RAW = BITS == 4 && XDT == DT_F16 && !SECOND;
+    float v[RAW ? 1 : G::R][RAW ? 1 : G::EPT];
+    uint32_t hw[RAW ? G::R : 1][RAW ? G::EPT / 2 : 1];   // element 2i in the low half of word i
 #pragma unroll
     for (int r = 0; r < G::R; ++r) {
         const uint32_t e0 = (uint32_t)((r * G::BPS + bt) * B + l * G::CW);   // chunk 0 of this thread
-        if (full) {
+        if constexpr (RAW) {
+#pragma unroll
+            for (int c = 0; c < G::CH; ++c) {
+                const uint32_t ec = e0 + c * G::LPB * G::CW;
+                if (full) {
+                    const u32x4 q = gldo<u32x4>(xt, ec * 2u);
+                    hw[r][c * 4] = q.x;
+                    hw[r][c * 4 + 1] = q.y;
+                    hw[r][c * 4 + 2] = q.z;
+                    hw[r][c * 4 + 3] = q.w;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t e = ec + 2 * k;
+                        const uint32_t lo = (int64_t)e < rem ? gld<uint16_t>(static_cast<const uint16_t*>(xt) + e) : 0u;
+                        const uint32_t hi =
+                            (int64_t)e + 1 < rem ? gld<uint16_t>(static_cast<const uint16_t*>(xt) + e + 1) : 0u;
+                        hw[r][c * 4 + k] = lo | (hi << 16);
+                    }
+                }
+            }
+        } else if (full) {
 #pragma unroll
             for (int c = 0; c < G::CH; ++c) load_chunk<XDT, G::CW>(xt, e0 + c * G::LPB * G::CW, &v[r][c * G::CW]);
         } else {
@@ -282,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
     uint32_t packed[G::R][G::CH];
 #pragma unroll
     for (int r = 0; r < G::R; ++r) {
-        float* const vr = v[r];
+        float* const vr = v[RAW ? 0 : r];
         const int64_t blk = blk0 + r * G::BPS + bt;
         if constexpr (SECOND) {
             const uint32_t e0 = (uint32_t)((r * G::BPS + bt) * B + l * G::CW);
@@ -297,8 +323,18 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
         // for finite inputs (measured 2% faster on the 7B NF4 sweep than an
         // integer max of masked bits)
         float mf = 0.0f;
+        if constexpr (RAW) {
+            // |x| of both halves (sign bits cleared), then a packed 16-bit
+            // integer max: for finite inputs the magnitudes order as integers
+            u16x2 m2 = {0, 0};
 #pragma unroll
-        for (int i = 0; i < G::EPT; ++i) mf = __builtin_fmaxf(mf, __builtin_fabsf(vr[i]));
+            for (int i = 0; i < G::EPT / 2; ++i)
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, hw[r][i] & 0x7FFF7FFFu));
+            mf = (float)__builtin_bit_cast(_Float16, m2.x > m2.y ? m2.x : m2.y);
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::EPT; ++i) mf = __builtin_fmaxf(mf, __builtin_fabsf(vr[i]));
+        }
         uint32_t mx = fbits(mf);
         mx = block_max<G>(mx, s_red[r], tid);
         const float a = ffrom(mx);
@@ -309,7 +345,23 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
         const float rc = rcp_rn(a);                      // used only where fast_div_ok(a)
         const bool fast = fast_div_ok(a);
         float nv[G::EPT];
-        if (__all(fast)) {                               // the usual case: one straight-line pass
+        if constexpr (RAW) {
+            if (__all(fast)) {
+#pragma unroll
+                for (int i = 0; i < G::EPT / 2; ++i) {
+                    const h16x2 x2 = __builtin_bit_cast(h16x2, hw[r][i]);
+                    nv[2 * i] = div_by_block_h(x2.x, a, rc);
+                    nv[2 * i + 1] = div_by_block_h(x2.y, a, rc);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < G::EPT / 2; ++i) {
+                    const h16x2 x2 = __builtin_bit_cast(h16x2, hw[r][i]);
+                    nv[2 * i] = normalize_by_block((float)x2.x, a, rc, fast);
+                    nv[2 * i + 1] = normalize_by_block((float)x2.y, a, rc, fast);
+                }
+            }
+        } else if (__all(fast)) {                        // the usual case: one straight-line pass
 #pragma unroll
             for (int i = 0; i < G::EPT; ++i) nv[i] = div_by_block(vr[i], a, rc);
         } else {
@@ -325,10 +377,15 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantDesc single, TileMap<Qu
                     if constexpr (USER) w |= enc_user(nv[c * 4 + j], s_enc) << (8 * j);
                     else w |= enc_dyn8(nv[c * 4 + j], s_enc) << (8 * j);
                 }
+            } else if (code4 == 0) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    w |= ((enc_nf4(nv[c * 8 + 2 * k], s_enc.e) << 4) | enc_nf4(nv[c * 8 + 2 * k + 1], s_enc.e))
+                         << (8 * k);
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    w |= ((enc_4bit(nv[c * 8 + 2 * k], s_enc.e) << 4) | enc_4bit(nv[c * 8 + 2 * k + 1], s_enc.e))
+                    w |= ((enc_fp4(nv[c * 8 + 2 * k], s_enc.e) << 4) | enc_fp4(nv[c * 8 + 2 * k + 1], s_enc.e))
                          << (8 * k);
             }
             packed[r][c] = w;

@@ -188,10 +188,15 @@ int build_udyn8_lut(const float* udyn8, uint8_t* base, uint32_t* thr)
     return 0;
 }
 
+// The device takes the bucket of n in [-1, 1] as 16 n + 16 rounded once to
+// the nearest integer, ties to even (one fused multiply-add onto 1.5 * 2^23,
+// whose float bits then hold the bucket).  In binary64 16 n is exact and the
+// sum can round only far from a tie (near k + 1/2, 16 n has an ulp of at
+// least 2^-25), so nearbyint of the binary64 sum is the same bucket.
 int bucket4(float n)
 {
-    float u = n * 16.0f + 16.0f;
-    int b = (int)u;
+    const double u = (double)n * 16.0 + 16.0;
+    const int b = (int)std::nearbyint(u);
     return b < 0 ? 0 : (b > k4LutN - 1 ? k4LutN - 1 : b);
 }
 
@@ -219,7 +224,10 @@ float bucket_start(int b)
 }
 
 // vals: distinct values ascending; codes: the stored code of each value.
-int build_4bit_lut(const std::vector<float>& vals, const std::vector<uint32_t>& codes, LutEntry* lut)
+// sorted: the codes ascend with the values (NF4), so the code above a
+// threshold is always the one below plus 1 and the payload holds only the
+// code below; otherwise (FP4) it holds both.
+int build_4bit_lut(const std::vector<float>& vals, const std::vector<uint32_t>& codes, bool sorted, LutEntry* lut)
 {
     std::vector<float> t = thresholds(vals);
     const int nt = (int)t.size();
@@ -231,7 +239,8 @@ int build_4bit_lut(const std::vector<float>& vals, const std::vector<uint32_t>& 
         if (k + 1 < nt && t[k + 1] <= hi) return -1;
         lut[b].t = k < nt ? bits_of(t[k]) : 0x7F800000u;
         uint32_t below = codes[k], above = codes[k < nt ? k + 1 : k];
-        lut[b].payload = below | (above << 8);
+        if (sorted && k < nt && t[k] <= hi && above != below + 1) return -1;
+        lut[b].payload = sorted ? below : (below | (above << 8));
     }
     return 0;
 }
@@ -266,7 +275,7 @@ int self_check(const QbTables* T)
         int code = c0 + (x >= float_of(T->dyn8_thr[c0]) ? 1 : 0);
         if (code != nearest(dyn, x)) return -10;
         const LutEntry& f = T->nf4_lut[bucket4(x)];
-        int c4 = (x >= float_of(f.t)) ? (int)((f.payload >> 8) & 0xFF) : (int)(f.payload & 0xFF);
+        const int c4 = (int)f.payload + (x >= float_of(f.t) ? 1 : 0);
         if (c4 != nearest(nf4, x)) return -11;
         // the unsigned encoder on |x|
         const float ax = std::fabs(x);
@@ -296,7 +305,7 @@ int build_tables(QbTables* T)
     std::vector<float> nf4(T->nf4, T->nf4 + 16);
     std::vector<uint32_t> nf4_codes(16);
     for (int i = 0; i < 16; ++i) nf4_codes[i] = (uint32_t)i;
-    if (build_4bit_lut(nf4, nf4_codes, T->nf4_lut) != 0) return -4;
+    if (build_4bit_lut(nf4, nf4_codes, true, T->nf4_lut) != 0) return -4;
 
     // FP4 as a line of 15 distinct values: -mag[7..1], 0, mag[1..7]
     std::vector<float> fp4;
@@ -304,7 +313,7 @@ int build_tables(QbTables* T)
     for (int k = 7; k >= 1; --k) { fp4.push_back(T->fp4[8 + k]); fp4_codes.push_back(8u | (uint32_t)k); }
     fp4.push_back(0.0f); fp4_codes.push_back(0u);
     for (int k = 1; k <= 7; ++k) { fp4.push_back(T->fp4[k]); fp4_codes.push_back((uint32_t)k); }
-    if (build_4bit_lut(fp4, fp4_codes, T->fp4_lut) != 0) return -5;
+    if (build_4bit_lut(fp4, fp4_codes, false, T->fp4_lut) != 0) return -5;
     return self_check(T);
 }
 

@@ -49,7 +49,8 @@ constexpr int user_bucket(float n)
 
 struct LutEntry {
     uint32_t t;        // decision threshold (binary32 bits)
-    uint32_t payload;  // DYN8: 127 + thresholds below the bucket; 4-bit: code below | code above << 8
+    uint32_t payload;  // DYN8: 127 + thresholds below the bucket; NF4: code below (above: + 1);
+                       // FP4: code below | code above << 8
 };
 
 // Dynamic 8-bit encoder.  The code is monotone in n, so with the 255 signed

@@ -585,8 +585,9 @@ int32_t qb_codebook(qb_code code, float* out);
  *         1409 for n < 0; the code is payload + (n >= threshold).
  *   UDYN8: 2817 entries, n >= 0; bucket b = (clamp(bits(n), 2^-22, 1.0) >> 16)
  *         - (bits(2^-22) >> 16); the code is payload + (n >= threshold).
- *   NF4/FP4: bucket b = (int)(n*16 + 16) in binary32 (0..32); the code is byte
- *         0 of payload if n < threshold, else byte 1.
+ *   NF4/FP4: bucket b = n*16 + 16 rounded once to the nearest integer, ties
+ *         to even (0..32); NF4: the code is payload + (n >= threshold); FP4:
+ *         byte 0 of payload if n < threshold, else byte 1.
  * Copies at most `capacity` entries (2*capacity words) into out and returns the
  * table's entry count, or -1 on error.
  */

@@ -105,12 +105,16 @@ def emulate_udyn8(table, x):
     return (pay[b] + (x >= t[b])).astype(np.uint8)
 
 
-def emulate_4bit(table, x):
+def emulate_4bit(table, x, code):
+    """The documented 4-bit encoder: bucket 16 x + 16 rounded to nearest even
+    (exact in binary64 before the rounding), then NF4: payload + (x >= threshold);
+    FP4: byte 0 of the payload below the threshold, byte 1 from it on."""
     t = np.array([e[0] for e in table], dtype=np.uint32).view(np.float32)
     pay = np.array([e[1] for e in table], dtype=np.int64)
     x = x.astype(np.float32)
-    u = (x * np.float32(16.0)).astype(np.float32) + np.float32(16.0)
-    b = np.minimum(u.astype(np.int64), 32)
+    b = np.clip(np.rint(x.astype(np.float64) * 16.0 + 16.0).astype(np.int64), 0, 32)
+    if code == oracle.NF4:
+        return (pay[b] + (x >= t[b])).astype(np.uint8)
     return np.where(x >= t[b], (pay[b] >> 8) & 0xFF, pay[b] & 0xFF).astype(np.uint8)
 
 
@@ -126,7 +130,9 @@ def probe_values(code, rng):
     down = [mids]
     for _ in range(3):
         down.append(np.nextafter(down[-1], np.float32(-2)))
-    edges = np.concatenate(near + down + [cb])
+    # bucket edges of the 4-bit encoder: 16 x + 16 at k + 1/2 (a tie) and one ulp either side
+    ties = ((np.arange(33) - 15.5) / 16).astype(np.float32)
+    edges = np.concatenate(near + down + [cb, ties, np.nextafter(ties, np.float32(2)), np.nextafter(ties, np.float32(-2))])
     x = np.concatenate(vals + [edges, -edges, [0.0, -0.0, 1.0, -1.0, 1e-45, -1e-45, 2.0 ** -22, -(2.0 ** -22)]])
     x = x.astype(np.float32)
     return x[np.abs(x) <= 1]
@@ -157,7 +163,7 @@ def test_udyn8_bucket_encoder_equals_oracle(qb):
 @pytest.mark.parametrize("code", [1, 2])
 def test_4bit_bucket_encoder_equals_oracle(qb, code):
     x = probe_values(code, np.random.default_rng(32 + code))
-    assert np.array_equal(emulate_4bit(qb.qb_encoder_table(code), x), oracle.encode(code, x))
+    assert np.array_equal(emulate_4bit(qb.qb_encoder_table(code), x, code), oracle.encode(code, x))
 
 
 def test_workspace_sizes(qb):
