@@ -167,8 +167,9 @@ def test_4bit_bucket_encoder_equals_oracle(qb, code):
 
 
 def test_workspace_sizes(qb):
-    assert qb.qb_dq_workspace_bytes(64 * 1000, 64) == 16384 + 4096
-    assert qb.qb_dq_workspace_bytes(0, 64) == 16384
+    bins = 64 * 256 * 8                    # 64 copies of 256 uint64 exponent bins
+    assert qb.qb_dq_workspace_bytes(64 * 1000, 64) == bins + 4096
+    assert qb.qb_dq_workspace_bytes(0, 64) == bins
     assert qb.qb_dq_workspace_bytes(100, 63) == 0
     assert qb.qb_multi_tensor_workspace_bytes(291) == 291 * 64 + 292 * 8 + (2 * 291 + 64 + 1) * 4
     assert qb.qb_multi_tensor_workspace_bytes(0) == 0
@@ -242,10 +243,10 @@ def test_grouped_quantize_arguments_rejected_before_launch(qb):
     tab = lambda *e: (qb.qb_quant_tensor * len(e))(*e)
     wsz = L.qb_multi_tensor_quantize_workspace_bytes
     # workspace: tables only without nesting; with nesting two table regions,
-    # 16 KiB of bins per tensor and the fp32 absmax (256-byte rounded)
+    # 128 KiB of bins per tensor and the fp32 absmax (256-byte rounded)
     region = -(-(2 * 64 + 3 * 8 + (2 * 2 + 64 + 1) * 4) // 256) * 256
     assert wsz(tab(plain, plain), 2, 64) == region
-    assert wsz(tab(nested, nested), 2, 64) == 2 * region + 2 * 16384 + 2 * (-(-16 * 4 // 256) * 256)
+    assert wsz(tab(nested, nested), 2, 64) == 2 * region + 2 * 131072 + 2 * (-(-16 * 4 // 256) * 256)
     assert wsz(tab(plain), 1, 100) == 0
     ws = wsz(tab(nested, nested), 2, 64)
     f = L.qb_multi_tensor_quantize
