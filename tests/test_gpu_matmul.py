@@ -197,3 +197,15 @@ def test_7b_layer_shapes_many_rows(M, NK):
     y = run_gpu(x, oracle.BF16, codes, scale, nst, oracle.NF4, 64, N)
     rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).choice(M, 46, replace=False)]))
     check(y[rows], x[rows], oracle.BF16, codes, scale, oracle.NF4, 64, N, f"7B {N}x{K} M={M} (sampled rows)")
+
+
+# every instantiation of the tiled kernel: 64 x 64 and 128 x 128 tiles (M below / from 512), one or two k halves
+# per step (K a multiple of 128 only / of 256), plain and nested, bf16 and fp16
+@pytest.mark.parametrize("M,K", [(100, 384), (100, 512), (600, 384), (600, 512)])
+@pytest.mark.parametrize("xdt", [oracle.BF16, oracle.F16])
+@pytest.mark.parametrize("nested", [False, True])
+def test_tiled_every_instantiation(M, K, xdt, nested):
+    N = 130
+    x, codes, scale, nst = make_case(M, K, N, 64, xdt, nested, seed=M + K + 3 * xdt + 7 * nested)
+    y = run_gpu(x, xdt, codes, scale, nst, oracle.NF4, 64, N)
+    check(y, x, xdt, codes, scale, oracle.NF4, 64, N, f"tiled M={M} K={K} xdt={xdt} nested={nested}")

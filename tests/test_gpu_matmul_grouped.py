@@ -52,7 +52,7 @@ def case(M, K, Ns, xdt, nested, B, seed):
 
 # M: one, two and four m-tiles of the small-M kernel, then the tiled kernel's regime (bf16 / fp16 with K a
 # multiple of 128) where the call launches once per weight; K = 160 keeps the small kernel at every M
-@pytest.mark.parametrize("M", [1, 7, 16, 33, 64, 100, 300])
+@pytest.mark.parametrize("M", [1, 7, 16, 24, 33, 64, 100, 300])
 @pytest.mark.parametrize("K", [512, 160])
 @pytest.mark.parametrize("xdt", [oracle.BF16, oracle.F16, oracle.F32])
 @pytest.mark.parametrize("nested", [False, True])
