@@ -55,6 +55,17 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 #define QB_MM_WAVES 8
 #endif
 
+// One row of activations (decode), 16-bit, K * 2 bytes at most this many: the
+// row is staged in LDS once per workgroup (dynamic LDS of K * 2 bytes), so no
+// activation registers are held per step.  The freed registers go to
+// occupancy: the code loads of one step are in flight per wave where a wave
+// has at most 4 steps of K, two steps beyond (same-process A/B on the 7B
+// projections at M = 1: q/k/v in one launch 13.8 -> 10.8 us, gate/up 22.5 ->
+// 17.0 us; the 11008-deep layer 11.1 -> 10.9 us with two).
+#ifndef QB_MM_XS_BYTES
+#define QB_MM_XS_BYTES 32768
+#endif
+
 constexpr int kMmWaves = QB_MM_WAVES;
 constexpr int kMmThreads = 64 * kMmWaves;
 constexpr int kMmStepK = 128;                // k per wave step: 4 lane groups x 32
@@ -199,16 +210,18 @@ __device__ __forceinline__ void dequant_chunk(const u32x4& cw, float a, const fl
 
 // One workgroup's tile: output columns 16 ntile .. 16 ntile + 15 of y, rows
 // 16 MT blockIdx.y onwards.
-template <int XDT, bool DQ, int MT, bool KF>
+template <int XDT, bool DQ, int MT, bool KF, int XS>
 __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, int64_t K,
                                         const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
                                         const uint8_t* __restrict__ c2, const float* __restrict__ absmax2,
                                         const float* __restrict__ offset, int log2B, int log2B2, int code4, int64_t N,
                                         void* __restrict__ y, const QbTables* __restrict__ tab, int64_t ntile)
 {
+    static_assert(XS == 0 || (MT == 1 && XDT != DT_F32), "staged activations: one 16-bit row");
     __shared__ float s_val[16];
     __shared__ float s_dyn[DQ ? 256 : 1];
     __shared__ float s_red[kMmWaves][MT][4][64];
+    extern __shared__ u32x4 s_x[];                    // XS: the activation row, K * 2 bytes (dynamic)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: scalar step bases
     const int r = lane & 15, g = lane >> 4;
@@ -239,13 +252,13 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
     // The loads of a wave's next PD steps (codes, block constants, and with
     // one m-tile the activations too) are issued ahead of the current step's
     // computation.
-    constexpr bool PX = MT == 1;
-    constexpr int PD = (XDT == DT_F32 && PX) ? 2 : QB_MM_DEPTH;
+    constexpr bool PX = MT == 1 && XS == 0;
+    constexpr int PD = XS ? XS : ((XDT == DT_F32 && PX) ? 2 : QB_MM_DEPTH);
     struct Pre {
         u32x4 cw;
         uint32_t c;
         float a;
-        Frag<XDT> xf[PX ? 4 : 1];
+        Frag<XDT> xf[(PX || XS) ? 4 : 1];
     };
     const int64_t steps = (K + kMmStepK - 1) / kMmStepK;
     float mu = 0.0f;                                  // the nested mean, read with the tables
@@ -273,6 +286,21 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
     };
     auto compute = [&](Pre& p, int64_t s) {
         const bool kin = in_k(s);
+        if constexpr (XS) {
+            // activations of the step from LDS: row 0 only (lanes r == 0)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (r == 0 && kin) {
+                    const u32x4 v = s_x[s * (kMmStepK / 8) + 4 * g + q];
+                    p.xf[q].w[0] = v.x;
+                    p.xf[q].w[1] = v.y;
+                    p.xf[q].w[2] = v.z;
+                    p.xf[q].w[3] = v.w;
+                } else {
+                    frag_zero<XDT>(p.xf[q]);
+                }
+            }
+        }
         Frag<XDT> b[4];
         if (kin) {
             const float a = DQ ? s_dyn[p.c] * p.a + mu : p.a;    // two rounded operations (nested)
@@ -281,7 +309,7 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
 #pragma unroll
             for (int q = 0; q < 4; ++q) frag_zero<XDT>(b[q]);
         }
-        if constexpr (PX) {
+        if constexpr (PX || XS) {
             if (!kin) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) frag_zero<XDT>(p.xf[q]);
@@ -314,7 +342,11 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
         }
         issue(pre[j], wave + (int64_t)kMmWaves * j);
     }
-    // the code tables are staged while the first steps' loads are in flight
+    // the code tables (and the activation row) are staged while the first
+    // steps' loads are in flight
+    if constexpr (XS) {
+        for (int64_t i = tid; i < K / 8; i += kMmThreads) s_x[i] = ldo<u32x4>(x_base, (uint32_t)(i * 16));
+    }
     if (tid < 16) s_val[tid] = (code4 == 0 ? tab->nf4 : tab->fp4)[tid];
     if constexpr (DQ) {
         if (tid < 256) s_dyn[tid] = tab->dyn8[tid];
@@ -348,7 +380,7 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
     }
 }
 
-template <int XDT, bool DQ, int MT, bool KF>
+template <int XDT, bool DQ, int MT, bool KF, int XS>
 __global__ __launch_bounds__(kMmThreads) void k_dq4_matmul(const void* __restrict__ x, int64_t M, int64_t K,
                                                            const uint8_t* __restrict__ codes,
                                                            const float* __restrict__ absmax,
@@ -358,8 +390,8 @@ __global__ __launch_bounds__(kMmThreads) void k_dq4_matmul(const void* __restric
                                                            int code4, int64_t N, void* __restrict__ y,
                                                            const QbTables* __restrict__ tab)
 {
-    mm_tile<XDT, DQ, MT, KF>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab,
-                             (int64_t)blockIdx.x);
+    mm_tile<XDT, DQ, MT, KF, XS>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab,
+                                 (int64_t)blockIdx.x);
 }
 
 // Several weights against the same activations in one launch (the column
@@ -371,7 +403,7 @@ struct MmGroup {
     int count;
 };
 
-template <int XDT, bool DQ, int MT, bool KF>
+template <int XDT, bool DQ, int MT, bool KF, int XS>
 __global__ __launch_bounds__(kMmThreads) void k_dq4_matmul_grouped(const void* __restrict__ x, int64_t M, int64_t K,
                                                                    const MmGroup grp, int log2B, int log2B2,
                                                                    int code4, const QbTables* __restrict__ tab)
@@ -380,8 +412,8 @@ __global__ __launch_bounds__(kMmThreads) void k_dq4_matmul_grouped(const void* _
     int i = 0;
     while (i + 1 < grp.count && bx >= grp.tile0[i + 1]) ++i;   // uniform: the kernel arguments are scalar
     const MmWeight& w = grp.w[i];
-    mm_tile<XDT, DQ, MT, KF>(x, M, K, w.codes, w.absmax, w.c2, w.absmax2, w.offset, log2B, log2B2, code4, w.N, w.y,
-                             tab, bx - grp.tile0[i]);
+    mm_tile<XDT, DQ, MT, KF, XS>(x, M, K, w.codes, w.absmax, w.c2, w.absmax2, w.offset, log2B, log2B2, code4, w.N,
+                                 w.y, tab, bx - grp.tile0[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -592,29 +624,46 @@ __global__ __launch_bounds__(256 * KH) void k_dq4_gemm(const void* __restrict__ 
 // Enqueue `kernel` on a 2-D grid of kMmThreads-thread workgroups; returns
 // this launch's own status.
 template <typename... KArgs, typename... Args>
-hipError_t launch_2d(void (*kernel)(KArgs...), dim3 grid, hipStream_t s, Args&&... args)
+hipError_t launch_2d_lds(void (*kernel)(KArgs...), dim3 grid, size_t lds, hipStream_t s, Args&&... args)
 {
     std::tuple<KArgs...> vals(std::forward<Args>(args)...);
     return std::apply(
         [&](auto&... v) {
             void* ptrs[] = {static_cast<void*>(&v)...};
-            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kMmThreads), ptrs, 0, s);
+            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kMmThreads), ptrs, lds, s);
         },
         vals);
 }
 
-template <int XDT, bool DQ, int MT>
+template <typename... KArgs, typename... Args>
+hipError_t launch_2d(void (*kernel)(KArgs...), dim3 grid, hipStream_t s, Args&&... args)
+{
+    return launch_2d_lds(kernel, grid, 0, s, std::forward<Args>(args)...);
+}
+
+template <int XDT, bool DQ, int MT, int XS = 0>
 hipError_t mm_as(const void* x, int64_t M, int64_t K, const uint8_t* codes, const float* absmax, const uint8_t* c2,
                  const float* absmax2, const float* offset, int log2B, int log2B2, int code4, int64_t N, void* y,
                  const QbTables* tab, hipStream_t s)
 {
     const int64_t gx = (N + 15) / 16, gy = (M + 16 * MT - 1) / (16 * MT);
     if (gx >= (int64_t(1) << 31) || gy > 65535) return hipErrorInvalidValue;
+    const size_t lds = XS ? (size_t)K * 2 : 0;
     if (K % kMmStepK == 0)
-        return launch_2d(k_dq4_matmul<XDT, DQ, MT, true>, dim3((unsigned)gx, (unsigned)gy), s, x, M, K, codes,
-                         absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab);
-    return launch_2d(k_dq4_matmul<XDT, DQ, MT, false>, dim3((unsigned)gx, (unsigned)gy), s, x, M, K, codes, absmax,
-                     c2, absmax2, offset, log2B, log2B2, code4, N, y, tab);
+        return launch_2d_lds(k_dq4_matmul<XDT, DQ, MT, true, XS>, dim3((unsigned)gx, (unsigned)gy), lds, s, x, M, K,
+                             codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab);
+    return launch_2d_lds(k_dq4_matmul<XDT, DQ, MT, false, XS>, dim3((unsigned)gx, (unsigned)gy), lds, s, x, M, K,
+                         codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab);
+}
+
+// One 16-bit activation row that fits the LDS staging buffer: 0, else the
+// prefetch depth in steps (1 while a wave has at most 4 steps of K).
+template <int XDT>
+int stage_x(int64_t M, int64_t K)
+{
+    if (XDT == DT_F32 || M != 1 || K * 2 > QB_MM_XS_BYTES) return 0;
+    const int64_t steps = (K + kMmStepK - 1) / kMmStepK;
+    return (steps + kMmWaves - 1) / kMmWaves <= 4 ? 1 : 2;
 }
 
 // The tiled kernel on a grid of (BN-column, BM-row) tiles.
@@ -682,6 +731,17 @@ hipError_t mm_mt(int64_t M, const void* x, int64_t K, const uint8_t* codes, cons
         if (M >= QB_GM_MIN_M && K % kGmStepK == 0)
             return gm_kh<XDT, DQ, 1>(M, x, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);
     }
+    if constexpr (XDT != DT_F32) {
+        switch (stage_x<XDT>(M, K)) {
+        case 1:
+            return mm_as<XDT, DQ, 1, 1>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab,
+                                        s);
+        case 2:
+            return mm_as<XDT, DQ, 1, 2>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab,
+                                        s);
+        default: break;
+        }
+    }
     if (M <= 16) return mm_as<XDT, DQ, 1>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);
     if (M <= 32) return mm_as<XDT, DQ, 2>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);
     return mm_as<XDT, DQ, 4>(x, M, K, codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab, s);
@@ -715,23 +775,31 @@ hipError_t launch_dq4_matmul(const void* x, int xdt, int64_t M, int64_t K, const
 
 namespace {
 
-template <int XDT, bool DQ, int MT>
+template <int XDT, bool DQ, int MT, int XS = 0>
 hipError_t mmg_as(const void* x, int64_t M, int64_t K, const MmGroup& grp, int log2B, int log2B2, int code4,
                   const QbTables* tab, hipStream_t s)
 {
     const int64_t gx = grp.tile0[grp.count], gy = (M + 16 * MT - 1) / (16 * MT);
     if (gx >= (int64_t(1) << 31) || gy > 65535) return hipErrorInvalidValue;
+    const size_t lds = XS ? (size_t)K * 2 : 0;
     if (K % kMmStepK == 0)
-        return launch_2d(k_dq4_matmul_grouped<XDT, DQ, MT, true>, dim3((unsigned)gx, (unsigned)gy), s, x, M, K, grp,
-                         log2B, log2B2, code4, tab);
-    return launch_2d(k_dq4_matmul_grouped<XDT, DQ, MT, false>, dim3((unsigned)gx, (unsigned)gy), s, x, M, K, grp,
-                     log2B, log2B2, code4, tab);
+        return launch_2d_lds(k_dq4_matmul_grouped<XDT, DQ, MT, true, XS>, dim3((unsigned)gx, (unsigned)gy), lds, s, x,
+                             M, K, grp, log2B, log2B2, code4, tab);
+    return launch_2d_lds(k_dq4_matmul_grouped<XDT, DQ, MT, false, XS>, dim3((unsigned)gx, (unsigned)gy), lds, s, x,
+                         M, K, grp, log2B, log2B2, code4, tab);
 }
 
 template <int XDT, bool DQ>
 hipError_t mmg_mt(int64_t M, const void* x, int64_t K, const MmGroup& grp, int log2B, int log2B2, int code4,
                   const QbTables* tab, hipStream_t s)
 {
+    if constexpr (XDT != DT_F32) {
+        switch (stage_x<XDT>(M, K)) {
+        case 1: return mmg_as<XDT, DQ, 1, 1>(x, M, K, grp, log2B, log2B2, code4, tab, s);
+        case 2: return mmg_as<XDT, DQ, 1, 2>(x, M, K, grp, log2B, log2B2, code4, tab, s);
+        default: break;
+        }
+    }
     if (M <= 16) return mmg_as<XDT, DQ, 1>(x, M, K, grp, log2B, log2B2, code4, tab, s);
     if (M <= 32) return mmg_as<XDT, DQ, 2>(x, M, K, grp, log2B, log2B2, code4, tab, s);
     return mmg_as<XDT, DQ, 4>(x, M, K, grp, log2B, log2B2, code4, tab, s);

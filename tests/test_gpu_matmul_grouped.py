@@ -92,3 +92,15 @@ def test_grouped_7b_projections(M, layer):
     got = grouped(x, oracle.BF16, weights, oracle.NF4, 64)
     for (codes, scale, nst, N), y in zip(weights, got):
         assert np.array_equal(y, run_gpu(x, oracle.BF16, codes, scale, nst, oracle.NF4, 64, N))
+
+
+@pytest.mark.parametrize("K", [5152, 11008])
+@pytest.mark.parametrize("xdt", [oracle.BF16, oracle.F16])
+@pytest.mark.parametrize("nested", [False, True])
+def test_grouped_decode_row_deep(K, xdt, nested):
+    """One row of activations with more than 4 steps of K per wave (two steps of codes in flight)."""
+    x, weights = case(1, K, [48, 130], xdt, nested, 64, seed=K + 5 * xdt + 17 * nested)
+    got = grouped(x, xdt, weights, oracle.NF4, 64)
+    for (codes, scale, nst, N), y in zip(weights, got):
+        assert np.array_equal(y, run_gpu(x, xdt, codes, scale, nst, oracle.NF4, 64, N))
+        check(y, x, xdt, codes, scale, oracle.NF4, 64, N, f"grouped decode K={K} N={N}")
