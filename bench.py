@@ -16,9 +16,8 @@ One step = one pass of the whole hot path over synthetic inputs resident in HBM:
   5. a dynamic 8-bit round trip (quantize, then dequantize to fp32; block 2048)
      of 268,435,456 fp32 values ~0.02 * Student-t(3).
 Two gradient sets alternate between steps (generated before timing).  Each
-tensor is an allocation of its own (--arena carves them all from one
-allocation at fixed offsets instead; measured 3-6% slower for the AdamW
-step).  After the timed steps: the two NF4 sweeps
+tensor is an allocation of its own (--layout chooses another placement, see
+Layout).  After the timed steps: the two NF4 sweeps
 with one qb_quantize / qb_dequantize call per tensor, and the same-process HBM
 ceilings (a device copy, a read and a write of 4 GiB) for comparison.
 
@@ -97,35 +96,68 @@ def traffic_per_launch():
     return rec.get("hbm_bytes_per_launch")
 
 
-ARENA_ALIGN = 4096
+ARENA_ALIGN = 4096          # "arena": every tensor on a 4 KiB boundary, in spec order
+KIND_ALIGN = 1 << 21        # "per-kind": every kind's region on a 2 MiB boundary
+ELEM_ALIGN = 64             # "per-kind": every tensor at a multiple of 64 elements of its region
 
 
-class Arena:
-    """Device tensors carved from ONE allocation at fixed offsets (4 KiB
-    aligned, in the order of `specs`), so the layout is the same in every
-    process.  With arena=False each tensor is its own allocation instead."""
+class Layout:
+    """Device tensors of the 7B step, from `specs` = (elements, dtype, kind) in
+    a fixed order, placed one of three ways:
 
-    def __init__(self, torch, dev, specs, arena=True):
-        self.views = []
-        if not arena:
-            self.buf = None
-            self.views = [torch.empty(max(n, 1), dtype=dt, device=dev)[:n] for n, dt in specs]
+    - "per-kind": ONE allocation holding one region per kind (all parameters,
+      all m codes, all gradients of a set, ...), each region on a 2 MiB
+      boundary, the tensors of a region back to back at multiples of 64
+      elements, so a tensor sits at the same element offset in every region of
+      the same length;
+    - "arena": one allocation, every tensor on a 4 KiB boundary in spec order
+      (the kinds interleaved tensor by tensor);
+    - "per-tensor": one allocation per tensor.
+
+    The multi-tensor AdamW step on the 7B state, all three measured in one
+    process (three boxes): per-kind 14.69 / 14.79 ms, per-tensor 15.81 /
+    14.83 / 14.96 ms, arena 15.54 / 15.58 ms.  But one and the same per-kind
+    layout ran 15.82 and 14.87 ms in two processes on one box: the spread
+    follows the physical pages a process is given, not the virtual layout,
+    so the default stays one allocation per tensor."""
+
+    MODES = ("per-tensor", "per-kind", "arena")
+
+    def __init__(self, torch, dev, specs, mode="per-tensor"):
+        if mode not in self.MODES:
+            raise ValueError(f"layout {mode!r}: one of {self.MODES}")
+        esize = [torch.empty(0, dtype=dt).element_size() for _, dt, _ in specs]
+        self.buf = None
+        if mode == "per-tensor":
+            self.views = [torch.empty(max(n, 1), dtype=dt, device=dev)[:n] for n, dt, _ in specs]
             return
-        offs, off = [], 0
-        for n, dt in specs:
-            off = -(-off // ARENA_ALIGN) * ARENA_ALIGN
-            offs.append(off)
-            off += n * torch.empty(0, dtype=dt).element_size()
+        offs = [0] * len(specs)
+        if mode == "arena":
+            off = 0
+            for i, (n, dt, _) in enumerate(specs):
+                off = -(-off // ARENA_ALIGN) * ARENA_ALIGN
+                offs[i] = off
+                off += n * esize[i]
+        else:
+            kinds = list(dict.fromkeys(k for _, _, k in specs))
+            region, off = {}, 0
+            for k in kinds:
+                off = -(-off // KIND_ALIGN) * KIND_ALIGN
+                region[k] = off
+                off += sum(-(-n // ELEM_ALIGN) * ELEM_ALIGN * esize[i]
+                           for i, (n, _, kk) in enumerate(specs) if kk == k)
+            elem = dict.fromkeys(kinds, 0)
+            for i, (n, dt, k) in enumerate(specs):
+                offs[i] = region[k] + elem[k] * esize[i]
+                elem[k] += -(-n // ELEM_ALIGN) * ELEM_ALIGN
         self.buf = torch.empty(max(off, 1), dtype=torch.uint8, device=dev)
-        for (n, dt), o in zip(specs, offs):
-            size = torch.empty(0, dtype=dt).element_size()
-            self.views.append(self.buf[o:o + n * size].view(dt))
+        self.views = [self.buf[o:o + n * e].view(dt) for (n, dt, _), o, e in zip(specs, offs, esize)]
 
 
 class Model7B:
     """Device state of the multi-tensor AdamW step and the 4-bit sweep."""
 
-    def __init__(self, torch, qb, inputs, dev, seed, with_w4=True, grad_sets=2, arena=True):
+    def __init__(self, torch, qb, inputs, dev, seed, with_w4=True, grad_sets=2, layout="per-tensor"):
         self.t = torch
         shapes = inputs.llama7b_param_shapes()
         self.names = [s[0] for s in shapes]
@@ -137,20 +169,20 @@ class Model7B:
         specs = []
         for n in self.sizes:
             nb = (n + ADAM_BLOCK - 1) // ADAM_BLOCK
-            specs += [(n, f32), (n, u8), (n, u8), (nb, f32), (nb, f32)]
-        for _ in range(grad_sets):
-            specs += [(n, bf16) for n in self.sizes]
+            specs += [(n, f32, "p"), (n, u8, "m"), (n, u8, "v"), (nb, f32, "absmax_m"), (nb, f32, "absmax_v")]
+        for k in range(grad_sets):
+            specs += [(n, bf16, f"g{k}") for n in self.sizes]
         for n in wsizes:
             nb = (n + W4_BLOCK - 1) // W4_BLOCK
-            specs += [(n, f16), ((n + 1) // 2, u8), (nb, u8), ((nb + W4_BLOCK2 - 1) // W4_BLOCK2, f32), (4, f32),
-                      (n, bf16)]
+            specs += [(n, f16, "w4"), ((n + 1) // 2, u8, "w4_codes"), (nb, u8, "w4_c2"),
+                      ((nb + W4_BLOCK2 - 1) // W4_BLOCK2, f32, "w4_absmax2"), (4, f32, "w4_offset"), (n, bf16, "w4_y")]
         if with_w4:
-            specs += [(Q8_N, f32), (Q8_N, u8), (Q8_N // Q8_BLOCK, f32), (Q8_N, f32)]
-        total = sum(n * torch.empty(0, dtype=dt).element_size() for n, dt in specs)
-        log(f"allocating {total / 2**30:.1f} GiB for {len(specs)} tensors "
-            f"({'one arena' if arena else 'one allocation each'})")
-        self.arena = Arena(torch, dev, specs, arena)
-        views = iter(self.arena.views)
+            specs += [(Q8_N, f32, "q8_x"), (Q8_N, u8, "q8_codes"), (Q8_N // Q8_BLOCK, f32, "q8_absmax"),
+                      (Q8_N, f32, "q8_y")]
+        total = sum(n * torch.empty(0, dtype=dt).element_size() for n, dt, _ in specs)
+        log(f"allocating {total / 2**30:.1f} GiB for {len(specs)} tensors (layout {layout})")
+        self.layout = Layout(torch, dev, specs, layout)
+        views = iter(self.layout.views)
         self.params = []
         self.grads = [[] for _ in range(grad_sets)]
         log(f"filling {len(shapes)} parameter tensors ({sum(self.sizes):,} params)")
@@ -746,9 +778,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--arena", action="store_true",
-                    help="carve every tensor of the 7B step from one allocation at fixed offsets (default: one "
-                         "allocation per tensor, measured faster)")
+    ap.add_argument("--layout", choices=Layout.MODES, default="per-tensor",
+                    help="placement of the 7B step's tensors in HBM (see Layout; default: one allocation per "
+                         "tensor)")
     ap.add_argument("--adam-only", action="store_true", help="time only the multi-tensor AdamW step")
     ap.add_argument("--flat", action="store_true",
                     help="time the single-tensor AdamW step on a flat 1.5e9-parameter buffer instead")
@@ -800,7 +832,7 @@ def main():
         return bench_matmul(torch, qb, inputs, dev, args)
     if args.roundtrip8:
         return bench_roundtrip8(torch, qb, inputs, dev, args)
-    model = Model7B(torch, qb, inputs, dev, args.seed, with_w4=not args.adam_only, arena=args.arena)
+    model = Model7B(torch, qb, inputs, dev, args.seed, with_w4=not args.adam_only, layout=args.layout)
     torch.cuda.synchronize()
     log(f"setup done; warmup {args.warmup} steps")
 
@@ -904,7 +936,9 @@ def main():
             "adam_blocksize": ADAM_BLOCK,
             "w4_blocksize": W4_BLOCK,
             "w4_blocksize2": W4_BLOCK2,
-            "layout": "one arena, fixed offsets" if args.arena else "one allocation per tensor",
+            "layout": {"per-kind": "one allocation, one 2 MiB-aligned region per kind of tensor",
+                       "arena": "one allocation, tensors interleaved on 4 KiB boundaries",
+                       "per-tensor": "one allocation per tensor"}[args.layout],
             "parallelism": "single GPU",
         },
         "components": comps,

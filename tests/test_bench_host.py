@@ -1,6 +1,7 @@
 """bench.py's host-side figures (CPU): the per-block round-trip error summary
 and the algorithmic byte counts it reports."""
 import numpy as np
+import pytest
 import torch
 
 import bench
@@ -41,16 +42,23 @@ def test_near_midpoint_mask_counts_one_ulp_on_either_side():
     assert got.tolist() == [True, True, True, False, True, False, False]
 
 
-def test_arena_carves_fixed_aligned_views():
+def test_layouts_place_views_as_documented():
     f32, u8 = torch.float32, torch.uint8
-    specs = [(5, f32), (3, u8), (7, f32)]
-    a = bench.Arena(torch, "cpu", specs)
+    specs = [(5, f32, "p"), (5, u8, "m"), (70, f32, "p"), (70, u8, "m"), (3, f32, "a")]
+    a = bench.Layout(torch, "cpu", specs, "arena")
     base = a.buf.data_ptr()
-    offs = [v.data_ptr() - base for v in a.views]
-    assert offs == [0, bench.ARENA_ALIGN, 2 * bench.ARENA_ALIGN]
-    assert [v.numel() for v in a.views] == [5, 3, 7] and [v.dtype for v in a.views] == [f32, u8, f32]
-    a.views[0].fill_(1.0)
-    a.views[2].fill_(2.0)
-    assert float(a.views[0].sum()) == 5.0 and float(a.views[2].sum()) == 14.0
-    b = bench.Arena(torch, "cpu", specs, arena=False)
-    assert b.buf is None and [v.numel() for v in b.views] == [5, 3, 7]
+    assert [v.data_ptr() - base for v in a.views] == [i * bench.ARENA_ALIGN for i in range(5)]
+    assert [v.numel() for v in a.views] == [5, 5, 70, 70, 3] and [v.dtype for v in a.views] == [f32, u8, f32, u8, f32]
+    k = bench.Layout(torch, "cpu", specs, "per-kind")
+    base = k.buf.data_ptr()
+    offs = [v.data_ptr() - base for v in k.views]
+    # regions on 2 MiB boundaries in order of first appearance; a tensor's element offset is the same in each region
+    rp, rm, ra = 0, bench.KIND_ALIGN, 2 * bench.KIND_ALIGN
+    assert offs == [rp, rm, rp + 64 * 4, rm + 64, ra]
+    for v, n in zip(k.views, [5, 5, 70, 70, 3]):
+        v.fill_(1)
+        assert v.numel() == n and float(v.sum()) == n
+    t = bench.Layout(torch, "cpu", specs, "per-tensor")
+    assert t.buf is None and [v.numel() for v in t.views] == [5, 5, 70, 70, 3]
+    with pytest.raises(ValueError):
+        bench.Layout(torch, "cpu", specs, "interleaved")
