@@ -389,10 +389,11 @@ def _stream_lib():
 
 def hbm_ceilings(torch, dev, reps=10):
     """Same-process HBM ceilings on 4 GiB buffers from the reference streams
-    of libqb_stream.so (the access style of libqb's kernels: one 256-thread
-    workgroup per 4096 floats, 16-byte non-temporal accesses): a copy (4 GiB
-    read + 4 GiB written), a read and a write; mean HIP-event time of `reps`
-    calls on torch's current stream, which is the stream they run on."""
+    of libqb_stream.so (the fastest plain form measured: one 16-byte
+    non-temporal access per thread, 1024 floats per 256-thread workgroup,
+    XCD-contiguous tile order): a copy (4 GiB read + 4 GiB written), a read
+    and a write; mean HIP-event time of `reps` calls on torch's current
+    stream, which is the stream they run on."""
     L = _stream_lib()
     n = CEIL_BYTES // 4
     a = torch.ones(n, dtype=torch.float32, device=dev)
@@ -410,7 +411,7 @@ def hbm_ceilings(torch, dev, reps=10):
     del a, b
     rates = {"copy_GB/s": 2 * CEIL_BYTES / copy_ms / 1e6, "read_GB/s": CEIL_BYTES / read_ms / 1e6,
              "write_GB/s": CEIL_BYTES / write_ms / 1e6}
-    return {"kernels": "libqb_stream.so (16-byte non-temporal streams)", "buffer_bytes": CEIL_BYTES, **rates,
+    return {"kernels": "libqb_stream.so (one 16-byte non-temporal access per thread, XCD-contiguous tiles)", "buffer_bytes": CEIL_BYTES, **rates,
             "frac_of_hbm_peak": {k.split("_")[0]: v / HBM_PEAK_GBS for k, v in rates.items()}}
 
 

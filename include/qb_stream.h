@@ -2,18 +2,19 @@
  * qb_stream.h -- HBM reference streams of the benchmark (libqb_stream.so).
  *
  * Not part of the block-wise quantization library: three plain streaming
- * kernels that bound what a kernel of libqb can reach on the same device, in
- * the same process and with the same access style (one 256-thread workgroup
- * per 4096 floats, 16-byte non-temporal loads and stores, tiles in address
- * order).  The benchmark reports them beside the roofline figures.
+ * kernels that bound what a kernel of libqb can reach on the same device and
+ * in the same process, in the fastest plain form measured on MI355X (one
+ * 16-byte non-temporal access per thread, one 256-thread workgroup per 1024
+ * floats, each XCD on its own contiguous eighth of the buffer).  The
+ * benchmark reports them beside the roofline figures.
  *
  * All pointers are DEVICE pointers, 16-byte aligned, owned by the caller;
- * n (floats) must be a positive multiple of 4096.  Work is enqueued on
+ * n (floats) must be a positive multiple of 1024.  Work is enqueued on
  * `stream` (a hipStream_t, NULL = default stream).  Each call returns 0, or a
  * hipError_t code (invalid arguments: nothing is enqueued).
  *   qbs_copy    dst[i] = src[i]: n floats read, n written.
- *   qbs_read    reads src[0..n); writes sink[0..255] only if a workgroup's
- *               sum of its 4096 values equals `never` exactly (pass a value
+ *   qbs_read    reads src[0..n); writes sink[0..255] only if a thread's sum
+ *               of its 4 values equals `never` exactly (pass a value
  *               the data cannot sum to, e.g. NaN, so nothing is written).
  *   qbs_write   dst[i] = value: n floats written.
  */
