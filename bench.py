@@ -75,10 +75,20 @@ def q4_bytes_per_weight():
     return 2.0 + 0.5 + 1.0 / W4_BLOCK + 4.0 / (W4_BLOCK * W4_BLOCK2)
 
 
-def kernel_source_digest():
+# The sources the AdamW kernel and its multi-tensor launch are built from: the
+# kernel, its device helpers and tables, and the host code that builds the
+# tile map and launches it.
+ADAMW_SOURCES = ("qb_api.cpp", "qb_device.h", "qb_launch.h", "qb_optim.hip", "qb_optim_kernels.h", "qb_tables.h")
+ADAMW_KERNEL = "qb::k_optim8<0, 2048, 2, true, 0, false>"
+
+
+def kernel_source_digest(names=None):
+    """sha256 over the library's sources in csrc/ (file name, then contents, in
+    name order): all of them, or only `names`."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_optimizer_states_amd", "csrc")
-    for name in sorted(n for n in os.listdir(csrc) if os.path.isfile(os.path.join(csrc, n))):
+    every = sorted(n for n in os.listdir(csrc) if os.path.isfile(os.path.join(csrc, n)))
+    for name in (every if names is None else sorted(names)):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()
@@ -86,14 +96,86 @@ def kernel_source_digest():
 
 def traffic_per_launch():
     """HBM bytes per AdamW launch from the committed counter summary, or None if
-    it is missing or the kernel sources changed since it was taken."""
+    it is missing or the AdamW kernel's sources changed since it was taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_digest():
+    if (rec.get("kernel_sources") != list(ADAMW_SOURCES)
+            or rec.get("kernel_source_sha256") != kernel_source_digest(ADAMW_SOURCES)):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_dispatches(run_dir):
+    """{dispatch id: (kernel name, counter summed over its instances)} from the
+    counter_collection.csv that `rocprofv3 --pmc <one counter> -d run_dir`
+    wrote (searched for below run_dir)."""
+    import csv
+    import glob
+    found = sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True))
+    if len(found) != 1:
+        raise SystemExit(f"{run_dir}: expected one *counter_collection.csv, found {found}")
+    agg = {}
+    with open(found[0]) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            name, v = agg.get(d, (r["Kernel_Name"], 0.0))
+            agg[d] = (name, v + float(r["Counter_Value"]))
+    return agg
+
+
+def traffic_summary(bench_fetch, bench_write, copy_fetch, copy_write, out=TRAFFIC_FILE):
+    """Write the AdamW kernel's HBM traffic record from four counter runs (the
+    bench under FETCH_SIZE, then WRITE_SIZE; the copy calibration under each):
+    the mean counter per AdamW dispatch (KiB), scaled by the factor that maps
+    the same counter to the 1 GiB read and 1 GiB written by each of the
+    calibration's five copies (its last five dispatches)."""
+    def factor(run_dir):
+        last = [v for _, (_, v) in sorted(_counter_dispatches(run_dir).items())[-5:]]
+        return (1 << 30) / (float(np.median(last)) * 1024)
+
+    def adamw_kib(run_dir):
+        v = [x for name, x in _counter_dispatches(run_dir).values() if ADAMW_KERNEL in name]
+        if not v:
+            raise SystemExit(f"{run_dir}: no dispatch of {ADAMW_KERNEL}")
+        return float(np.mean(v)), len(v)
+
+    ff, wf = factor(copy_fetch), factor(copy_write)
+    (fk, nf), (wk, nw) = adamw_kib(bench_fetch), adamw_kib(bench_write)
+    from bit_optimizer_states_amd import inputs
+    n = sum(int(np.prod(s)) for _, s in inputs.llama7b_param_shapes())
+    alg = n * adam_bytes_per_param()              # the roofline's algorithmic bytes per launch
+    rec = {
+        "kernel": ADAMW_KERNEL,
+        "workload": f"7B decoder, 291 tensors, {n:,} params, bf16 grads, block {ADAM_BLOCK}",
+        "kernel_sources": list(ADAMW_SOURCES),
+        "kernel_source_sha256": kernel_source_digest(ADAMW_SOURCES),
+        "dispatches": {"fetch": nf, "write": nw},
+        "fetch_size_kib_per_dispatch": fk,
+        "write_size_kib_per_dispatch": wk,
+        "fetch_factor": ff,
+        "write_factor": wf,
+        "hbm_bytes_per_launch": fk * 1024 * ff + wk * 1024 * wf,
+        "algorithmic_bytes_per_launch": float(alg),
+        "how": "from the repository root; the rocprofv3 runs from /tmp with TMPDIR=/tmp and the paths made absolute",
+        "commands": [
+            "timeout -s KILL 400 rocprofv3 --pmc FETCH_SIZE --output-format csv -d " + bench_fetch +
+            " -o run -- python3 bench.py --adam-only --steps 1 --warmup 1 --no-cpu-baseline",
+            "timeout -s KILL 400 rocprofv3 --pmc WRITE_SIZE --output-format csv -d " + bench_write +
+            " -o run -- python3 bench.py --adam-only --steps 1 --warmup 1 --no-cpu-baseline",
+            "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d " + copy_fetch +
+            " -o run -- python3 bench.py --copy-calibration",
+            "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d " + copy_write +
+            " -o run -- python3 bench.py --copy-calibration",
+            "python3 bench.py --traffic-summary " + " ".join((bench_fetch, bench_write, copy_fetch, copy_write)),
+        ],
+    }
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps({k: rec[k] for k in ("hbm_bytes_per_launch", "algorithmic_bytes_per_launch",
+                                          "fetch_factor", "write_factor")}))
 
 
 ARENA_ALIGN = 4096          # "arena": every tensor on a 4 KiB boundary, in spec order
@@ -806,7 +888,12 @@ def main():
                     help="time the fused 4-bit dequantize + product on the 7B projection shapes instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device five times (the reference kernel for HBM counters)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("BENCH_FETCH", "BENCH_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the AdamW kernel's traffic record from four rocprofv3 --pmc output folders "
+                         "(no GPU)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1",
                           "n_gpus_requested": args.gpus}))

@@ -62,3 +62,43 @@ def test_layouts_place_views_as_documented():
     assert t.buf is None and [v.numel() for v in t.views] == [5, 5, 70, 70, 3]
     with pytest.raises(ValueError):
         bench.Layout(torch, "cpu", specs, "interleaved")
+
+
+def _counter_csv(path, rows):
+    """A counter_collection.csv as rocprofv3 writes it: one row per dispatch and
+    counter instance (Dispatch_Id, Kernel_Name, Counter_Value, ...)."""
+    import csv
+    path.mkdir(parents=True)
+    with open(path / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, name, vals in rows:
+            for v in vals:                      # instances (XCDs) of one dispatch
+                w.writerow([d, name, "C", v])
+
+
+def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
+    ak = "void " + bench.ADAMW_KERNEL + "(qb::TensorDesc, ...)"
+    other = "qb::k_dequant<4, 2, true, true, false>"
+    # copy calibration: a fill, then five 1 GiB copies reading 512 MiB-worth (fetch) and 1 GiB (write)
+    _counter_csv(tmp_path / "cf", [(1, "fill", [0.0])] + [(2 + i, "copy", [262144.0, 262144.0]) for i in range(5)])
+    _counter_csv(tmp_path / "cw", [(1, "fill", [1 << 20])] + [(2 + i, "copy", [524288.0, 524288.0]) for i in range(5)])
+    # two AdamW dispatches among other kernels, each instance half of the total
+    _counter_csv(tmp_path / "bf", [(1, other, [5.0]), (2, ak, [1000.0, 1000.0]), (3, ak, [1100.0, 1100.0])])
+    _counter_csv(tmp_path / "bw", [(1, other, [7.0]), (2, ak, [3000.0, 3000.0]), (3, ak, [3000.0, 3000.0])])
+    out = tmp_path / "traffic.json"
+    bench.traffic_summary(*(str(tmp_path / d) for d in ("bf", "bw", "cf", "cw")), out=str(out))
+    import json
+    rec = json.load(open(out))
+    assert np.isclose(rec["fetch_factor"], 2.0) and np.isclose(rec["write_factor"], 1.0)
+    assert np.isclose(rec["fetch_size_kib_per_dispatch"], 2100.0) and rec["dispatches"] == {"fetch": 2, "write": 2}
+    assert np.isclose(rec["hbm_bytes_per_launch"], 2100.0 * 1024 * 2 + 6000.0 * 1024)
+    assert rec["kernel_sources"] == list(bench.ADAMW_SOURCES)
+    assert rec["kernel_source_sha256"] == bench.kernel_source_digest(bench.ADAMW_SOURCES)
+    assert np.isclose(rec["algorithmic_bytes_per_launch"], 6_738_415_616 * bench.adam_bytes_per_param())
+
+
+def test_traffic_digest_covers_only_the_adamw_sources():
+    every = bench.kernel_source_digest()
+    assert bench.kernel_source_digest(bench.ADAMW_SOURCES) != every
+    assert bench.kernel_source_digest(reversed(bench.ADAMW_SOURCES)) == bench.kernel_source_digest(bench.ADAMW_SOURCES)
