@@ -56,7 +56,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 #endif
 
 // One row of activations (decode), 16-bit, K * 2 bytes at most this many: the
-// row is staged in LDS once per workgroup (dynamic LDS of K * 2 bytes), so no
+// row is staged in LDS once per workgroup (dynamic LDS of K * 2 bytes rounded
+// up to whole steps of 128 k, zero past K), so no
 // activation registers are held per step.  The freed registers go to
 // occupancy: the code loads of one step are in flight per wave where a wave
 // has at most 4 steps of K, two steps beyond (same-process A/B on the 7B
@@ -221,7 +222,7 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
     __shared__ float s_val[16];
     __shared__ float s_dyn[DQ ? 256 : 1];
     __shared__ float s_red[kMmWaves][MT][4][64];
-    extern __shared__ u32x4 s_x[];                    // XS: the activation row, K * 2 bytes (dynamic)
+    extern __shared__ u32x4 s_x[];                    // XS: the activation row, whole steps (dynamic)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: scalar step bases
     const int r = lane & 15, g = lane >> 4;
@@ -258,8 +259,13 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
         u32x4 cw;
         uint32_t c;
         float a;
-        Frag<XDT> xf[(PX || XS) ? 4 : 1];
+        Frag<XDT> xf[PX ? 4 : 1];
     };
+    // XS: the step's activations, in lanes r == 0 (row 0 of the tile); the
+    // other lanes' fragments stay zero for the whole loop
+    Frag<XDT> xr[XS ? 4 : 1];
+#pragma unroll
+    for (int q = 0; q < (XS ? 4 : 1); ++q) frag_zero<XDT>(xr[q]);
     const int64_t steps = (K + kMmStepK - 1) / kMmStepK;
     float mu = 0.0f;                                  // the nested mean, read with the tables
     // a lane group's 32 k lie inside K, except in the last step when K is not
@@ -287,17 +293,15 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
     auto compute = [&](Pre& p, int64_t s) {
         const bool kin = in_k(s);
         if constexpr (XS) {
-            // activations of the step from LDS: row 0 only (lanes r == 0)
+            // activations of the step from LDS (zero past K): row 0 only
+            if (r == 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (r == 0 && kin) {
+                for (int q = 0; q < 4; ++q) {
                     const u32x4 v = s_x[s * (kMmStepK / 8) + 4 * g + q];
-                    p.xf[q].w[0] = v.x;
-                    p.xf[q].w[1] = v.y;
-                    p.xf[q].w[2] = v.z;
-                    p.xf[q].w[3] = v.w;
-                } else {
-                    frag_zero<XDT>(p.xf[q]);
+                    xr[q].w[0] = v.x;
+                    xr[q].w[1] = v.y;
+                    xr[q].w[2] = v.z;
+                    xr[q].w[3] = v.w;
                 }
             }
         }
@@ -309,7 +313,10 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
 #pragma unroll
             for (int q = 0; q < 4; ++q) frag_zero<XDT>(b[q]);
         }
-        if constexpr (PX || XS) {
+        if constexpr (XS) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) mma<XDT>(xr[q], b[q], acc[0]);
+        } else if constexpr (PX) {
             if (!kin) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) frag_zero<XDT>(p.xf[q]);
@@ -345,7 +352,9 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
     // the code tables (and the activation row) are staged while the first
     // steps' loads are in flight
     if constexpr (XS) {
-        for (int64_t i = tid; i < K / 8; i += kMmThreads) s_x[i] = ldo<u32x4>(x_base, (uint32_t)(i * 16));
+        // whole steps: the chunks past K (K is a multiple of 32) read as zero
+        for (int64_t i = tid; i < steps * (kMmStepK / 8); i += kMmThreads)
+            s_x[i] = i < K / 8 ? ldo<u32x4>(x_base, (uint32_t)(i * 16)) : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < 16) s_val[tid] = (code4 == 0 ? tab->nf4 : tab->fp4)[tid];
     if constexpr (DQ) {
@@ -648,7 +657,7 @@ hipError_t mm_as(const void* x, int64_t M, int64_t K, const uint8_t* codes, cons
 {
     const int64_t gx = (N + 15) / 16, gy = (M + 16 * MT - 1) / (16 * MT);
     if (gx >= (int64_t(1) << 31) || gy > 65535) return hipErrorInvalidValue;
-    const size_t lds = XS ? (size_t)K * 2 : 0;
+    const size_t lds = XS ? (size_t)((K + kMmStepK - 1) / kMmStepK) * kMmStepK * 2 : 0;
     if (K % kMmStepK == 0)
         return launch_2d_lds(k_dq4_matmul<XDT, DQ, MT, true, XS>, dim3((unsigned)gx, (unsigned)gy), lds, s, x, M, K,
                              codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab);
@@ -781,7 +790,7 @@ hipError_t mmg_as(const void* x, int64_t M, int64_t K, const MmGroup& grp, int l
 {
     const int64_t gx = grp.tile0[grp.count], gy = (M + 16 * MT - 1) / (16 * MT);
     if (gx >= (int64_t(1) << 31) || gy > 65535) return hipErrorInvalidValue;
-    const size_t lds = XS ? (size_t)K * 2 : 0;
+    const size_t lds = XS ? (size_t)((K + kMmStepK - 1) / kMmStepK) * kMmStepK * 2 : 0;
     if (K % kMmStepK == 0)
         return launch_2d_lds(k_dq4_matmul_grouped<XDT, DQ, MT, true, XS>, dim3((unsigned)gx, (unsigned)gy), lds, s, x,
                              M, K, grp, log2B, log2B2, code4, tab);
