@@ -55,17 +55,25 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 #define QB_MM_WAVES 8
 #endif
 
-// One row of activations (decode), 16-bit, K * 2 bytes at most this many: the
-// row is staged in LDS once per workgroup (dynamic LDS of K * 2 bytes rounded
-// up to whole steps of 128 k, zero past K), so no
-// activation registers are held per step.  The freed registers go to
-// occupancy: the code loads of one step are in flight per wave where a wave
-// has at most 4 steps of K, two steps beyond (same-process A/B on the 7B
-// projections at M = 1: q/k/v in one launch 13.8 -> 10.8 us, gate/up 22.5 ->
-// 17.0 us; the 11008-deep layer 11.1 -> 10.9 us with two).
+// A few rows of activations (decode), 16-bit, M * K * 2 bytes at most this
+// many (K rounded up to whole steps of 128 k): the rows are staged in LDS once
+// per workgroup (dynamic LDS, zero past K), so no activation registers are
+// held per step and x is not fetched again from L2 every step.  The freed
+// registers go to occupancy: the code loads of one step are in flight per
+// wave where a wave has at most 4 steps of K, two steps beyond (same-process
+// A/B on the 7B projections at M = 1: q/k/v in one launch 13.8 -> 10.8 us,
+// gate/up 22.5 -> 17.0 us; the 11008-deep layer 11.1 -> 10.9 us with two;
+// at M = 4 against x from L2 every step: q/k/v 15.2 -> 10.6 us, gate/up
+// 26.0 -> 18.9 us).
 #ifndef QB_MM_XS_BYTES
 #define QB_MM_XS_BYTES 32768
 #endif
+// Rows of activations staged this way: up to this many (each row padded by
+// 64 bytes, so the rows of one 16-byte fragment fall in different LDS banks).
+#ifndef QB_MM_XS_ROWS
+#define QB_MM_XS_ROWS 4
+#endif
+constexpr int kXsPad = 4;                     // u32x4 of padding per staged row
 
 constexpr int kMmWaves = QB_MM_WAVES;
 constexpr int kMmThreads = 64 * kMmWaves;
@@ -218,11 +226,11 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
                                         const float* __restrict__ offset, int log2B, int log2B2, int code4, int64_t N,
                                         void* __restrict__ y, const QbTables* __restrict__ tab, int64_t ntile)
 {
-    static_assert(XS == 0 || (MT == 1 && XDT != DT_F32), "staged activations: one 16-bit row");
+    static_assert(XS == 0 || (MT == 1 && XDT != DT_F32), "staged activations: 16-bit rows of one m-tile");
     __shared__ float s_val[16];
     __shared__ float s_dyn[DQ ? 256 : 1];
     __shared__ float s_red[kMmWaves][MT][4][64];
-    extern __shared__ u32x4 s_x[];                    // XS: the activation row, whole steps (dynamic)
+    extern __shared__ u32x4 s_x[];                    // XS: the activation rows, whole steps (dynamic)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: scalar step bases
     const int r = lane & 15, g = lane >> 4;
@@ -261,12 +269,13 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
         float a;
         Frag<XDT> xf[PX ? 4 : 1];
     };
-    // XS: the step's activations, in lanes r == 0 (row 0 of the tile); the
+    // XS: the step's activations, in lanes r < M (the rows of the tile); the
     // other lanes' fragments stay zero for the whole loop
     Frag<XDT> xr[XS ? 4 : 1];
 #pragma unroll
     for (int q = 0; q < (XS ? 4 : 1); ++q) frag_zero<XDT>(xr[q]);
     const int64_t steps = (K + kMmStepK - 1) / kMmStepK;
+    const int xs_rs = (int)steps * (kMmStepK / 8) + kXsPad;     // XS: u32x4 per staged row
     float mu = 0.0f;                                  // the nested mean, read with the tables
     // a lane group's 32 k lie inside K, except in the last step when K is not
     // a multiple of 128 (KF false): such a lane feeds zeros instead
@@ -293,11 +302,11 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
     auto compute = [&](Pre& p, int64_t s) {
         const bool kin = in_k(s);
         if constexpr (XS) {
-            // activations of the step from LDS (zero past K): row 0 only
-            if (r == 0) {
+            // activations of the step from LDS (zero past K): rows r < M
+            if (m_ok[0]) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const u32x4 v = s_x[s * (kMmStepK / 8) + 4 * g + q];
+                    const u32x4 v = s_x[r * xs_rs + s * (kMmStepK / 8) + 4 * g + q];
                     xr[q].w[0] = v.x;
                     xr[q].w[1] = v.y;
                     xr[q].w[2] = v.z;
@@ -352,9 +361,13 @@ __device__ __forceinline__ void mm_tile(const void* __restrict__ x, int64_t M, i
     // the code tables (and the activation row) are staged while the first
     // steps' loads are in flight
     if constexpr (XS) {
-        // whole steps: the chunks past K (K is a multiple of 32) read as zero
-        for (int64_t i = tid; i < steps * (kMmStepK / 8); i += kMmThreads)
-            s_x[i] = i < K / 8 ? ldo<u32x4>(x_base, (uint32_t)(i * 16)) : u32x4{0u, 0u, 0u, 0u};
+        // M rows of whole steps: the chunks past K (K is a multiple of 32)
+        // and the padding read as zero
+        const int kc = (int)(K / 8);
+        for (int i = tid; i < (int)M * xs_rs; i += kMmThreads) {
+            const int row = i / xs_rs, c = i - row * xs_rs;
+            s_x[i] = c < kc ? ldo<u32x4>(x_base, (uint32_t)((row * kc + c) * 16)) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
     if (tid < 16) s_val[tid] = (code4 == 0 ? tab->nf4 : tab->fp4)[tid];
     if constexpr (DQ) {
@@ -650,6 +663,12 @@ hipError_t launch_2d(void (*kernel)(KArgs...), dim3 grid, hipStream_t s, Args&&.
     return launch_2d_lds(kernel, grid, 0, s, std::forward<Args>(args)...);
 }
 
+// LDS bytes of M staged rows of K activations (whole steps, padded rows).
+size_t xs_bytes(int64_t M, int64_t K)
+{
+    return (size_t)M * (size_t)(((K + kMmStepK - 1) / kMmStepK) * (kMmStepK / 8) + kXsPad) * 16;
+}
+
 template <int XDT, bool DQ, int MT, int XS = 0>
 hipError_t mm_as(const void* x, int64_t M, int64_t K, const uint8_t* codes, const float* absmax, const uint8_t* c2,
                  const float* absmax2, const float* offset, int log2B, int log2B2, int code4, int64_t N, void* y,
@@ -657,7 +676,7 @@ hipError_t mm_as(const void* x, int64_t M, int64_t K, const uint8_t* codes, cons
 {
     const int64_t gx = (N + 15) / 16, gy = (M + 16 * MT - 1) / (16 * MT);
     if (gx >= (int64_t(1) << 31) || gy > 65535) return hipErrorInvalidValue;
-    const size_t lds = XS ? (size_t)((K + kMmStepK - 1) / kMmStepK) * kMmStepK * 2 : 0;
+    const size_t lds = XS ? xs_bytes(M, K) : 0;
     if (K % kMmStepK == 0)
         return launch_2d_lds(k_dq4_matmul<XDT, DQ, MT, true, XS>, dim3((unsigned)gx, (unsigned)gy), lds, s, x, M, K,
                              codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab);
@@ -665,12 +684,13 @@ hipError_t mm_as(const void* x, int64_t M, int64_t K, const uint8_t* codes, cons
                          codes, absmax, c2, absmax2, offset, log2B, log2B2, code4, N, y, tab);
 }
 
-// One 16-bit activation row that fits the LDS staging buffer: 0, else the
+// 16-bit activation rows that fit the LDS staging buffer: 0, else the
 // prefetch depth in steps (1 while a wave has at most 4 steps of K).
 template <int XDT>
 int stage_x(int64_t M, int64_t K)
 {
-    if (XDT == DT_F32 || M != 1 || K * 2 > QB_MM_XS_BYTES) return 0;
+    if (XDT == DT_F32 || M < 1 || M > QB_MM_XS_ROWS) return 0;
+    if (M * ((K + kMmStepK - 1) / kMmStepK) * kMmStepK * 2 > QB_MM_XS_BYTES) return 0;    // unpadded bytes
     const int64_t steps = (K + kMmStepK - 1) / kMmStepK;
     return (steps + kMmWaves - 1) / kMmWaves <= 4 ? 1 : 2;
 }
@@ -790,7 +810,7 @@ hipError_t mmg_as(const void* x, int64_t M, int64_t K, const MmGroup& grp, int l
 {
     const int64_t gx = grp.tile0[grp.count], gy = (M + 16 * MT - 1) / (16 * MT);
     if (gx >= (int64_t(1) << 31) || gy > 65535) return hipErrorInvalidValue;
-    const size_t lds = XS ? (size_t)((K + kMmStepK - 1) / kMmStepK) * kMmStepK * 2 : 0;
+    const size_t lds = XS ? xs_bytes(M, K) : 0;
     if (K % kMmStepK == 0)
         return launch_2d_lds(k_dq4_matmul_grouped<XDT, DQ, MT, true, XS>, dim3((unsigned)gx, (unsigned)gy), lds, s, x,
                              M, K, grp, log2B, log2B2, code4, tab);

@@ -211,13 +211,15 @@ def test_tiled_every_instantiation(M, K, xdt, nested):
     check(y, x, xdt, codes, scale, oracle.NF4, 64, N, f"tiled M={M} K={K} xdt={xdt} nested={nested}")
 
 
-# one row of activations (decode): the row is staged in LDS for K * 2 <= 32 KiB, with one step of codes in flight
-# per wave up to 4 steps a wave (K <= 4096), two beyond; K = 16416 exceeds the staging limit
+# up to 4 rows of activations (decode): the rows are staged in LDS while M * K * 2 <= 32 KiB (K rounded up to
+# whole steps of 128), with one step of codes in flight per wave up to 4 steps a wave (K <= 4096), two beyond.
+# Staged: M = 1 up to K = 16384, M = 2 up to 8192, M = 3 up to 5376, M = 4 up to 4096; the others load x per step.
 @pytest.mark.parametrize("K", [160, 4096, 5152, 11008, 16416])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("xdt", [oracle.BF16, oracle.F16])
 @pytest.mark.parametrize("nested", [False, True])
-def test_decode_row(K, xdt, nested):
-    M, N = 1, 40
-    x, codes, scale, nst = make_case(M, K, N, 64, xdt, nested, seed=K + 3 * xdt + 7 * nested)
+def test_decode_rows(K, M, xdt, nested):
+    N = 40
+    x, codes, scale, nst = make_case(M, K, N, 64, xdt, nested, seed=K + 3 * xdt + 7 * nested + 11 * M)
     y = run_gpu(x, xdt, codes, scale, nst, oracle.NF4, 64, N)
-    check(y, x, xdt, codes, scale, oracle.NF4, 64, N, f"decode K={K} xdt={xdt} nested={nested}")
+    check(y, x, xdt, codes, scale, oracle.NF4, 64, N, f"decode M={M} K={K} xdt={xdt} nested={nested}")

@@ -52,7 +52,7 @@ def case(M, K, Ns, xdt, nested, B, seed):
 
 # M: one, two and four m-tiles of the small-M kernel, then the tiled kernel's regime (bf16 / fp16 with K a
 # multiple of 128) where the call launches once per weight; K = 160 keeps the small kernel at every M
-@pytest.mark.parametrize("M", [1, 7, 16, 24, 33, 64, 100, 300])
+@pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 24, 33, 64, 100, 300])
 @pytest.mark.parametrize("K", [512, 160])
 @pytest.mark.parametrize("xdt", [oracle.BF16, oracle.F16, oracle.F32])
 @pytest.mark.parametrize("nested", [False, True])
@@ -81,7 +81,7 @@ def test_grouped_codes_blocks_and_empty_weights(code, B):
         check(y, x, oracle.BF16, codes, scale, code, B, N, f"code={code} B={B} N={N}")
 
 
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 4, 16])
 @pytest.mark.parametrize("layer", ["qkv", "gate_up"])
 def test_grouped_7b_projections(M, layer):
     """A 7B decoder layer's q/k/v (3 x 4096 x 4096) or gate/up (2 x 11008 x 4096)
@@ -95,11 +95,13 @@ def test_grouped_7b_projections(M, layer):
 
 
 @pytest.mark.parametrize("K", [5152, 11008])
+@pytest.mark.parametrize("M", [1, 2])
 @pytest.mark.parametrize("xdt", [oracle.BF16, oracle.F16])
 @pytest.mark.parametrize("nested", [False, True])
-def test_grouped_decode_row_deep(K, xdt, nested):
-    """One row of activations with more than 4 steps of K per wave (two steps of codes in flight)."""
-    x, weights = case(1, K, [48, 130], xdt, nested, 64, seed=K + 5 * xdt + 17 * nested)
+def test_grouped_decode_row_deep(K, M, xdt, nested):
+    """Staged rows of activations with more than 4 steps of K per wave (two steps of codes in flight); M = 2 at
+    K = 11008 exceeds the staging limit."""
+    x, weights = case(M, K, [48, 130], xdt, nested, 64, seed=K + 5 * xdt + 17 * nested + 3 * M)
     got = grouped(x, xdt, weights, oracle.NF4, 64)
     for (codes, scale, nst, N), y in zip(weights, got):
         assert np.array_equal(y, run_gpu(x, xdt, codes, scale, nst, oracle.NF4, 64, N))
