@@ -64,14 +64,16 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // A/B on the 7B projections at M = 1: q/k/v in one launch 13.8 -> 10.8 us,
 // gate/up 22.5 -> 17.0 us; the 11008-deep layer 11.1 -> 10.9 us with two;
 // at M = 4 against x from L2 every step: q/k/v 15.2 -> 10.6 us, gate/up
-// 26.0 -> 18.9 us).
+// 26.0 -> 18.9 us; at M = 8, 64 KiB against 32: q/k/v 17.2 -> 15.1 us,
+// gate/up 29.2 -> 24.3 us.  Staging 16 rows, 128 KiB, leaves one workgroup
+// per CU and is 10-40% slower at M = 12 and 16).
 #ifndef QB_MM_XS_BYTES
-#define QB_MM_XS_BYTES 32768
+#define QB_MM_XS_BYTES 65536
 #endif
 // Rows of activations staged this way: up to this many (each row padded by
 // 64 bytes, so the rows of one 16-byte fragment fall in different LDS banks).
 #ifndef QB_MM_XS_ROWS
-#define QB_MM_XS_ROWS 4
+#define QB_MM_XS_ROWS 8
 #endif
 constexpr int kXsPad = 4;                     // u32x4 of padding per staged row
 

@@ -310,7 +310,7 @@ qb_status qb_dequantize(const uint8_t* codes, const float* absmax, const qb_dq* 
  *           binary32 sum rounded once to xdt.
  * Requirements: K a positive multiple of 32 below 2^24; M, N >= 0 (either 0: no-op).
  * Performance: up to 64 rows of x one wave per 16 weight rows streams W once
- * (up to 4 16-bit rows of at most 32 KiB in all are staged in LDS first);
+ * (up to 8 16-bit rows of at most 64 KiB in all are staged in LDS first);
  * from 65 rows (xdt 16-bit, K a multiple of 128) an LDS-tiled kernel shares x
  * across 64- or 128-row tiles and dequantizes W once per tile.  With M in the
  * thousands, dequantizing once and calling a GEMM library is faster.

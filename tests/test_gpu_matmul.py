@@ -211,11 +211,12 @@ def test_tiled_every_instantiation(M, K, xdt, nested):
     check(y, x, xdt, codes, scale, oracle.NF4, 64, N, f"tiled M={M} K={K} xdt={xdt} nested={nested}")
 
 
-# up to 4 rows of activations (decode): the rows are staged in LDS while M * K * 2 <= 32 KiB (K rounded up to
+# up to 8 rows of activations (decode): the rows are staged in LDS while M * K * 2 <= 64 KiB (K rounded up to
 # whole steps of 128), with one step of codes in flight per wave up to 4 steps a wave (K <= 4096), two beyond.
-# Staged: M = 1 up to K = 16384, M = 2 up to 8192, M = 3 up to 5376, M = 4 up to 4096; the others load x per step.
-@pytest.mark.parametrize("K", [160, 4096, 5152, 11008, 16416])
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+# Staged: M = 1 up to K = 32768, M = 2 up to 16384, M = 3 up to 10880, M = 4 up to 8192, M = 5 up to 6528, M = 8 up
+# to 4096; the others load x per step.
+@pytest.mark.parametrize("K", [160, 4096, 5152, 11008, 33024])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("xdt", [oracle.BF16, oracle.F16])
 @pytest.mark.parametrize("nested", [False, True])
 def test_decode_rows(K, M, xdt, nested):

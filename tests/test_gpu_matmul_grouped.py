@@ -81,7 +81,7 @@ def test_grouped_codes_blocks_and_empty_weights(code, B):
         check(y, x, oracle.BF16, codes, scale, code, B, N, f"code={code} B={B} N={N}")
 
 
-@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
 @pytest.mark.parametrize("layer", ["qkv", "gate_up"])
 def test_grouped_7b_projections(M, layer):
     """A 7B decoder layer's q/k/v (3 x 4096 x 4096) or gate/up (2 x 11008 x 4096)
@@ -95,12 +95,11 @@ def test_grouped_7b_projections(M, layer):
 
 
 @pytest.mark.parametrize("K", [5152, 11008])
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 6])
 @pytest.mark.parametrize("xdt", [oracle.BF16, oracle.F16])
 @pytest.mark.parametrize("nested", [False, True])
 def test_grouped_decode_row_deep(K, M, xdt, nested):
-    """Staged rows of activations with more than 4 steps of K per wave (two steps of codes in flight); M = 2 at
-    K = 11008 exceeds the staging limit."""
+    """Staged rows of activations with more than 4 steps of K per wave (two steps of codes in flight)."""
     x, weights = case(M, K, [48, 130], xdt, nested, 64, seed=K + 5 * xdt + 17 * nested + 3 * M)
     got = grouped(x, xdt, weights, oracle.NF4, 64)
     for (codes, scale, nst, N), y in zip(weights, got):
