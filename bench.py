@@ -761,7 +761,7 @@ def bench_roundtrip8(torch, qb, inputs, dev, args):
 MM_SHAPES = [(4096, 4096), (11008, 4096), (4096, 11008)]      # (N, K) of the 7B projections
 MM_ROWS = [1, 16, 64, 256, 1024, 4096]
 MM_GROUPS = [("q/k/v", [4096] * 3, 4096), ("gate/up", [11008] * 2, 4096)]   # projections of one 7B layer sharing x
-MM_GROUP_ROWS = [1, 4, 16]
+MM_GROUP_ROWS = [1, 4, 8, 16]
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
