@@ -763,6 +763,28 @@ MM_ROWS = [1, 16, 64, 256, 1024, 4096]
 MM_GROUPS = [("q/k/v", [4096] * 3, 4096), ("gate/up", [11008] * 2, 4096)]   # projections of one 7B layer sharing x
 MM_GROUP_ROWS = [1, 4, 8, 16]
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# Successive calls take successive copies of the weights, at least this many bytes of them in all (at most
+# MM_MAX_COPIES copies), so that no call finds its weights in the 256 MB last-level cache (Infinity Cache) of
+# MI355X, as in decoding, where every layer's weights pass once per token.  The same weights every call run
+# 6-10% faster at 26-47 MB (kernel trace, grouped launches at M = 1 and 4).
+MM_ROTATE_BYTES = 640 << 20
+MM_MAX_COPIES = 64
+
+
+def mm_copies(nbytes):
+    """Copies of a weight set of nbytes to rotate through."""
+    return max(2, min(MM_MAX_COPIES, -(-MM_ROTATE_BYTES // int(nbytes))))
+
+
+class Rotation:
+    """Calls fn(i) with i = 0, 1, .., n - 1, 0, 1, .. on successive calls."""
+
+    def __init__(self, n, fn):
+        self.n, self.fn, self.i = n, fn, 0
+
+    def __call__(self):
+        self.fn(self.i)
+        self.i = (self.i + 1) % self.n
 
 
 def dq4_matmul_bytes(M, N, K, block=W4_BLOCK, block2=W4_BLOCK2):
@@ -772,38 +794,47 @@ def dq4_matmul_bytes(M, N, K, block=W4_BLOCK, block2=W4_BLOCK2):
     return N * K / 2 + nb + 4 * -(-nb // block2) + 4 + 2 * M * K + 2 * M * N
 
 
+def nf4_weight(torch, qb, g, dev, N, K):
+    """One N x K NF4 weight with nested constants: (codes, dq, kept tensors).
+    Codes are uniform random bytes and the nested constants fixed values (the
+    kernels have no data-dependent work)."""
+    nb = N * K // W4_BLOCK
+    codes = torch.randint(0, 256, (N * K // 2,), dtype=torch.uint8, device=dev, generator=g)
+    c2 = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=dev, generator=g)
+    a2 = torch.full((-(-nb // W4_BLOCK2),), 0.02, device=dev)
+    mu = torch.full((4,), 0.03, device=dev)
+    return codes, qb.make_dq(c2, a2, mu, W4_BLOCK2), (c2, a2, mu)
+
+
 def bench_matmul(torch, qb, inputs, dev, args):
     """The 4-bit layer product in bf16: qb_dequant_matmul (NF4, nested, B = 64)
     against the unfused route (qb_dequantize to bf16, then torch's matmul) on the
     7B decoder's projection shapes, for M = 1 .. 4096 rows of activations.
-    Codes are uniform random bytes and the nested constants fixed values (the
-    kernels have no data-dependent work)."""
+    Successive calls take successive copies of the weights (mm_copies): no call
+    finds its weights in the last-level cache."""
     g = torch.Generator(device=dev)
     g.manual_seed(args.seed)
-    out = {"workload": "y = x W^T, W NF4 (B = 64, nested B2 = 256), bf16 compute, 7B projection shapes",
+    out = {"workload": "y = x W^T, W NF4 (B = 64, nested B2 = 256), bf16 compute, 7B projection shapes; "
+                       "successive calls on successive copies of the weights, >= 640 MB of them in all",
            "shapes": []}
     for N, K in MM_SHAPES:
-        nb = N * K // W4_BLOCK
-        codes = torch.randint(0, 256, (N * K // 2,), dtype=torch.uint8, device=dev, generator=g)
-        c2 = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=dev, generator=g)
-        a2 = torch.full((-(-nb // W4_BLOCK2),), 0.02, device=dev)
-        mu = torch.full((4,), 0.03, device=dev)
-        dq = qb.make_dq(c2, a2, mu, W4_BLOCK2)
+        copies = [nf4_weight(torch, qb, g, dev, N, K) for _ in range(mm_copies(N * K // 2))]
         w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
         for M in MM_ROWS:
             x = inputs.normal(M * K, 1.0, seed=args.seed + M, device=dev, dtype=torch.bfloat16).view(M, K)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            fused = time_back_to_back(torch, lambda: qb.qb_dequant_matmul(x, codes, None, 1, W4_BLOCK, N, y, dq=dq),
-                                      reps=args.steps)
+            fused = time_back_to_back(torch, Rotation(len(copies), lambda i: qb.qb_dequant_matmul(
+                x, copies[i][0], None, 1, W4_BLOCK, N, y, dq=copies[i][1])), reps=args.steps)
 
-            def unfused():
-                qb.qb_dequantize(codes, None, dq, 1, W4_BLOCK, N * K, w)
+            def unfused(i):
+                qb.qb_dequantize(copies[i][0], None, copies[i][1], 1, W4_BLOCK, N * K, w)
                 torch.matmul(x, w.t(), out=y)
 
-            ref = time_back_to_back(torch, unfused, reps=args.steps)
+            ref = time_back_to_back(torch, Rotation(len(copies), unfused), reps=args.steps)
             nbytes = dq4_matmul_bytes(M, N, K)
             flops = 2.0 * M * N * K
-            out["shapes"].append({"N": N, "K": K, "M": M, "fused_us": fused * 1e3, "unfused_us": ref * 1e3,
+            out["shapes"].append({"N": N, "K": K, "M": M, "weight_copies": len(copies), "fused_us": fused * 1e3,
+                                  "unfused_us": ref * 1e3,
                                   "speedup": ref / fused, "GB/s": nbytes / fused / 1e6,
                                   "frac_of_hbm_peak": nbytes / fused / 1e6 / HBM_PEAK_GBS,
                                   "TFLOP/s": flops / fused / 1e9,
@@ -812,28 +843,22 @@ def bench_matmul(torch, qb, inputs, dev, args):
     # one layer's projections that share x, in one grouped launch against one call per weight
     out["grouped"] = []
     for name, Ns, K in MM_GROUPS:
-        ws = []
-        for N in Ns:
-            nb = N * K // W4_BLOCK
-            codes = torch.randint(0, 256, (N * K // 2,), dtype=torch.uint8, device=dev, generator=g)
-            c2 = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=dev, generator=g)
-            a2 = torch.full((-(-nb // W4_BLOCK2),), 0.02, device=dev)
-            mu = torch.full((4,), 0.03, device=dev)
-            ws.append((codes, c2, a2, mu, qb.make_dq(c2, a2, mu, W4_BLOCK2), N))
+        sets = [[nf4_weight(torch, qb, g, dev, N, K) for N in Ns] for _ in range(mm_copies(sum(Ns) * K // 2))]
         for M in MM_GROUP_ROWS:
             x = inputs.normal(M * K, 1.0, seed=args.seed + M, device=dev, dtype=torch.bfloat16).view(M, K)
-            ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for *_, N in ws]
-            table = qb.matmul_weights([(w[0], None, w[4], w[5], y) for w, y in zip(ws, ys)])
-            grp = time_back_to_back(torch, lambda: qb.qb_dequant_matmul_grouped(x, table, len(ws), 1, W4_BLOCK,
-                                                                                  W4_BLOCK2), reps=args.steps)
+            ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for N in Ns]
+            tables = [qb.matmul_weights([(w[0], None, w[1], N, y) for w, N, y in zip(ws, Ns, ys)]) for ws in sets]
+            grp = time_back_to_back(torch, Rotation(len(sets), lambda i: qb.qb_dequant_matmul_grouped(
+                x, tables[i], len(Ns), 1, W4_BLOCK, W4_BLOCK2)), reps=args.steps)
 
-            def singles():
-                for w, y in zip(ws, ys):
-                    qb.qb_dequant_matmul(x, w[0], None, 1, W4_BLOCK, w[5], y, dq=w[4])
+            def singles(i):
+                for w, N, y in zip(sets[i], Ns, ys):
+                    qb.qb_dequant_matmul(x, w[0], None, 1, W4_BLOCK, N, y, dq=w[1])
 
-            one = time_back_to_back(torch, singles, reps=args.steps)
+            one = time_back_to_back(torch, Rotation(len(sets), singles), reps=args.steps)
             nbytes = sum(dq4_matmul_bytes(M, N, K) for N in Ns) - 2 * M * K * (len(Ns) - 1)
-            out["grouped"].append({"layer": name, "N": Ns, "K": K, "M": M, "grouped_us": grp * 1e3,
+            out["grouped"].append({"layer": name, "N": Ns, "K": K, "M": M, "weight_copies": len(sets),
+                                   "grouped_us": grp * 1e3,
                                    "single_calls_us": one * 1e3, "speedup": one / grp,
                                    "GB/s": nbytes / grp / 1e6, "frac_of_hbm_peak": nbytes / grp / 1e6 / HBM_PEAK_GBS})
             log(f"{name} M={M}: grouped {grp * 1e3:.1f} us ({nbytes / grp / 1e6 / HBM_PEAK_GBS:.1%} of HBM peak), "

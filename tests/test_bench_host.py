@@ -102,3 +102,14 @@ def test_traffic_digest_covers_only_the_adamw_sources():
     every = bench.kernel_source_digest()
     assert bench.kernel_source_digest(bench.ADAMW_SOURCES) != every
     assert bench.kernel_source_digest(reversed(bench.ADAMW_SOURCES)) == bench.kernel_source_digest(bench.ADAMW_SOURCES)
+
+
+def test_matmul_weight_rotation_outgrows_the_last_level_cache():
+    seen = []
+    r = bench.Rotation(3, seen.append)
+    for _ in range(7):
+        r()
+    assert seen == [0, 1, 2, 0, 1, 2, 0]
+    for n in (4096 * 4096 // 2, 11008 * 4096 // 2, 3 * 4096 * 4096 // 2, 2 * 11008 * 4096 // 2):
+        c = bench.mm_copies(n)
+        assert 2 <= c <= bench.MM_MAX_COPIES and c * n >= 2 * (256 << 20)     # twice the cache at least
