@@ -34,9 +34,11 @@
  *     owns every buffer: libqb never allocates device memory and keeps no state
  *     between calls except its constant tables (and the one scratch array of
  *     qb_multi_tensor_step_noalloc).  Every entry point is safe to
- *     call from several host threads at once, with one exception:
- *     qb_paged_optimizer_step, whose calls on one device share internal copy
- *     streams and events and must not overlap in time (see its description).
+ *     call from several host threads at once, with two exceptions whose
+ *     calls on one device must not overlap in time (see their descriptions):
+ *     qb_multi_tensor_step_noalloc, whose calls on one device share its
+ *     scratch array, and qb_paged_optimizer_step, whose calls on one device
+ *     share internal copy streams and events.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; no entry point synchronizes the device.
  *   - Arguments are validated before anything is enqueued; on any error
