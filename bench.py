@@ -45,6 +45,7 @@ if ROOT not in sys.path:
 METRIC = "fused AdamW8bit step GB/s + params/s; 4-bit dequant GB/s (% of HBM peak)"
 HBM_PEAK_GBS = 8000.0
 ADAM_BLOCK = 2048
+DQ4_TILE = 8192            # weights per workgroup of the grouped 4-bit dequantize (and of its access pattern)
 W4_BLOCK, W4_BLOCK2 = 64, 256
 Q8_N, Q8_BLOCK = 268_435_456, 2048
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
@@ -464,9 +465,61 @@ def _stream_lib():
     L.qbs_copy.argtypes = [vp, vp, i64, vp]
     L.qbs_read.argtypes = [vp, i64, f, vp, vp]
     L.qbs_write.argtypes = [vp, i64, f, vp]
-    for fn in (L.qbs_copy, L.qbs_read, L.qbs_write):
+    L.qbs_adamw_pattern.argtypes = [vp, vp, ctypes.c_int, i64, vp]
+    L.qbs_dequant4_pattern.argtypes = [vp, vp, ctypes.c_int, i64, vp]
+    for fn in (L.qbs_copy, L.qbs_read, L.qbs_write, L.qbs_adamw_pattern, L.qbs_dequant4_pattern):
         fn.restype = ctypes.c_int
     return L
+
+
+def _pattern_tables(torch, dev, rows, tile):
+    """Device descriptor array (eight int64 words per tensor: the pointers of
+    `rows`, n, padding) and the device array of first tiles (count + 1) of the
+    access-pattern streams; returns (descs, tile_begin, ntiles)."""
+    words, begins, t = [], [], 0
+    for ptrs, n in rows:
+        words.append(list(ptrs) + [n] + [0] * (7 - len(ptrs)))
+        begins.append(t)
+        t += -(-n // tile)
+    begins.append(t)
+    descs = torch.tensor(np.array(words, dtype=np.int64), device=dev)
+    return descs, torch.tensor(np.array(begins, dtype=np.int64), device=dev), t
+
+
+def access_pattern_ceilings(torch, model, adam_ms, dq_ms, reps=5):
+    """The memory accesses of the AdamW launch and of the NF4 dequantize
+    launch with no arithmetic (libqb_stream.so's access-pattern streams), on
+    the step's own buffers in the same process: what those accesses reach on
+    these physical pages, beside the kernels' own rates.  The AdamW pattern
+    writes every byte back unchanged; the dequantize pattern overwrites y."""
+    L = _stream_lib()
+    dev = model.params[0][0].device
+    s = torch.cuda.current_stream().cuda_stream
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"libqb_stream: HIP error {rc}")
+
+    rows = [((p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), am.data_ptr(), av.data_ptr()), p.numel())
+            for (p, m, v, am, av), g in zip(model.params, model.grads[0])]
+    ad, ab, at = _pattern_tables(torch, dev, rows, ADAM_BLOCK)
+    a_ms = time_calls(torch, lambda: ok(L.qbs_adamw_pattern(ad.data_ptr(), ab.data_ptr(), len(rows), at, s)), reps)
+    adam_bytes = model.n_params * adam_bytes_per_param()
+    out = {"kernels": "libqb_stream.so access-pattern streams on the step's buffers (no arithmetic)",
+           "adamw": {"ms": a_ms, "GB/s": adam_bytes / a_ms / 1e6,
+                     "frac_of_hbm_peak": adam_bytes / a_ms / 1e6 / HBM_PEAK_GBS,
+                     "adamw_frac_of_pattern": a_ms / adam_ms}}
+    if dq_ms is not None:
+        rows = [((codes.data_ptr(), c2.data_ptr(), a2.data_ptr(), off.data_ptr(), y.data_ptr()), n)
+                for (n, _, codes, c2, a2, off, y) in model.w4]
+        dd, db, dt = _pattern_tables(torch, dev, rows, DQ4_TILE)
+        d_ms = time_calls(torch, lambda: ok(L.qbs_dequant4_pattern(dd.data_ptr(), db.data_ptr(), len(rows), dt, s)),
+                          reps)
+        d4_bytes = model.n_w4 * w4_bytes_per_weight()
+        out["dequant4"] = {"ms": d_ms, "GB/s": d4_bytes / d_ms / 1e6,
+                           "frac_of_hbm_peak": d4_bytes / d_ms / 1e6 / HBM_PEAK_GBS,
+                           "dequant4_nf4_frac_of_pattern": d_ms / dq_ms}
+    return out
 
 
 def hbm_ceilings(torch, dev, reps=10):
@@ -1031,6 +1084,8 @@ def main():
             "launches": len(model.w4), "call": "qb_dequantize"}
     log("measuring the same-process HBM ceilings")
     ceiling = hbm_ceilings(torch, dev)
+    patterns = access_pattern_ceilings(torch, model, adam_ms,
+                                       None if args.adam_only else part_ms["dequant4_nf4_nested_bf16"])
     traffic = traffic_per_launch()
     achieved = adam_bytes / adam_ms / 1e6
     out = {
@@ -1078,6 +1133,7 @@ def main():
                                      **({} if args.adam_only else {
                                          "dequant4_nf4_frac_of_write": comps["dequant4_nf4_nested_bf16"]["GB/s"] /
                                                                        ceiling["write_GB/s"]})},
+        "access_pattern_same_buffers": patterns,
         "native_library": qb.loaded_path(),
         "cpu_baseline": None,
     }

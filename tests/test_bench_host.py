@@ -113,3 +113,16 @@ def test_matmul_weight_rotation_outgrows_the_last_level_cache():
     for n in (4096 * 4096 // 2, 11008 * 4096 // 2, 3 * 4096 * 4096 // 2, 2 * 11008 * 4096 // 2):
         c = bench.mm_copies(n)
         assert 2 <= c <= bench.MM_MAX_COPIES and c * n >= 2 * (256 << 20)     # twice the cache at least
+
+
+def test_pattern_tables_pack_descriptors_and_first_tiles():
+    # three tensors of 2048, 2049 and 1 elements at block 2048: 1, 2 and 1 tiles
+    rows = [((11, 12, 13), 2048), ((21, 22, 23), 2049), ((31, 32, 33), 1)]
+    descs, begins, total = bench._pattern_tables(torch, "cpu", rows, 2048)
+    assert total == 4
+    assert begins.tolist() == [0, 1, 3, 4]
+    assert descs.shape == (3, 8) and descs.dtype == torch.int64
+    assert descs[1].tolist() == [21, 22, 23, 2049, 0, 0, 0, 0]
+    # six pointers (the AdamW descriptor): n in the seventh word, one word of padding
+    d6, _, _ = bench._pattern_tables(torch, "cpu", [((1, 2, 3, 4, 5, 6), 7)], 2048)
+    assert d6[0].tolist() == [1, 2, 3, 4, 5, 6, 7, 0]

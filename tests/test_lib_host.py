@@ -48,7 +48,7 @@ def test_stream_library_exports_its_header():
     text = open(os.path.join(ROOT, "include", "qb_stream.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(qbs_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["qbs_copy", "qbs_read", "qbs_write"]
+    assert names == ["qbs_adamw_pattern", "qbs_copy", "qbs_dequant4_pattern", "qbs_read", "qbs_write"]
     L = ctypes.CDLL(os.path.join(ROOT, "bit_optimizer_states_amd", "libqb_stream.so"))
     for name in names:
         assert hasattr(L, name), name
