@@ -132,6 +132,12 @@ void* device_scratch();
 // `query` returns the kernel's resident workgroups per CU.
 int persistent_grid_cap(const void* kernel, int (*query)(const void*));
 
+// Dynamic LDS for `kernel` that brings a workgroup's LDS to a 1/wgs share of a
+// CU's (less 512 bytes of allocation slack), so that at most `wgs` of its
+// workgroups are resident on a CU at once; 0 where its own LDS already allows
+// no more.  Cached per (device, kernel); 0 on a HIP error.
+size_t lds_for_wgs_per_cu(const void* kernel, int wgs);
+
 // Workgroups to launch for a persistent grid-stride kernel: enough to fill
 // every CU at the kernel's occupancy, never more than there are tiles.
 template <class Kernel>
@@ -158,6 +164,20 @@ hipError_t launch_kernel_nt(void (*kernel)(KArgs...), int grid, int threads, hip
         [&](auto&... v) {
             void* ptrs[] = {static_cast<void*>(&v)...};
             return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(threads), ptrs, 0, s);
+        },
+        vals);
+}
+
+// The same with `lds` bytes of dynamic LDS per workgroup.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel_lds(void (*kernel)(KArgs...), int grid, int threads, size_t lds, hipStream_t s,
+                             Args&&... args)
+{
+    std::tuple<KArgs...> vals(std::forward<Args>(args)...);
+    return std::apply(
+        [&](auto&... v) {
+            void* ptrs[] = {static_cast<void*>(&v)...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(threads), ptrs, lds, s);
         },
         vals);
 }

@@ -68,6 +68,29 @@ int persistent_grid_cap(const void* kernel, int (*query)(const void*))
     return cap;
 }
 
+size_t lds_for_wgs_per_cu(const void* kernel, int wgs)
+{
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, size_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || wgs < 1) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    auto key = std::make_pair(dev, kernel);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    size_t dyn = 0;
+    int per_cu = 0;
+    hipFuncAttributes attr{};
+    if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+        hipFuncGetAttributes(&attr, kernel) == hipSuccess && per_cu > 0) {
+        const size_t share = (size_t)per_cu / (size_t)wgs;
+        const size_t target = share > 512 ? share - 512 : 0;
+        dyn = target > attr.sharedSizeBytes ? target - attr.sharedSizeBytes : 0;
+    }
+    cache[key] = dyn;
+    return dyn;
+}
+
 __global__ __launch_bounds__(256) void k_clear_bins(unsigned long long* __restrict__ bins, int64_t nwords)
 {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * 256) bins[i] = 0ull;
