@@ -78,8 +78,9 @@ def q4_bytes_per_weight():
 
 # The sources the AdamW kernel and its multi-tensor launch are built from: the
 # kernel, its device helpers and tables, and the host code that builds the
-# tile map and launches it.
-ADAMW_SOURCES = ("qb_api.cpp", "qb_device.h", "qb_launch.h", "qb_optim.hip", "qb_optim_kernels.h", "qb_tables.h")
+# tile map and sizes and launches it.
+ADAMW_SOURCES = ("qb_api.cpp", "qb_device.h", "qb_launch.h", "qb_optim.hip", "qb_optim_kernels.h", "qb_runtime.hip",
+                 "qb_tables.h")
 ADAMW_KERNEL = "qb::k_optim8<0, 2048, 2, true, 0, false>"
 
 

@@ -41,13 +41,16 @@ namespace qb {
 #endif
 constexpr int kAdamThreads = QB_ADAM_THREADS;
 
-// Resident workgroups per CU of the fused step, held there by reserving LDS
-// at launch (the AdamW step's registers would allow 7, the one-state kinds'
-// 8).  Measured on MI355X, same process and buffers, results bit-identical:
-// 6 is 0.8-1.6% faster than 7 on the 7B AdamW step (four boxes), 0.6-1.1% on
-// AdamW and Adam over a flat 1.5e9 buffer and 3% on Lion, SGD and RMSprop
-// there; 5 and 4 are 2% slower.  The AdamW step's memory accesses alone (no
-// arithmetic) show the same optimum: 3% faster at 6 than at 8.
+// Resident workgroups per CU of the fused step with binary32 parameters, held
+// there by reserving LDS at launch (the AdamW step's registers would allow 7,
+// the one-state kinds' 8).  Measured on MI355X, same process and buffers,
+// results bit-identical: 6 is 0.8-1.6% faster than 7 on the 7B AdamW step
+// (four boxes), 1.1-1.4% on AdamW over a flat 1.5e9 buffer and 2-3% on Lion,
+// SGD and RMSprop there, Adam within +-1%; 5 and 4 are 2% slower.  The AdamW
+// step's memory accesses alone (no arithmetic) show the same optimum: 3%
+// faster at 6 than at 8.  With 16-bit parameters (fewer bytes per element)
+// the cap measured 1-5% slower, so those launches keep the occupancy their
+// resources give.
 #ifndef QB_ADAM_WGS_PER_CU
 #define QB_ADAM_WGS_PER_CU 6
 #endif
@@ -679,26 +682,25 @@ hipError_t optim_as(const OptLaunch& a)
 {
     static_assert(TileA<B>::ELEMS == kAdamThreads * (B >= 4 * kAdamThreads ? B / kAdamThreads : 4), "tile size");
     if (a.ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    constexpr int kWgs = PDT == DT_F32 ? QB_ADAM_WGS_PER_CU : 0;   // 0: no cap
+    auto lds = [](auto kern) { return kWgs ? lds_for_wgs_per_cu(reinterpret_cast<const void*>(kern), kWgs) : 0; };
     if constexpr (opt_layerwise(OPT)) {                   // multi-tensor only (the norms need a workspace)
         if (!a.map) return hipErrorInvalidValue;
         if (a.part)
             return launch_kernel_nt(k_trust_norms<OPT, B, GDT, PDT, UV>, (int)a.ntiles, kAdamThreads, a.s, *a.map, *a.hs,
                                     a.tab, a.part);
         constexpr auto kern = k_optim8<OPT, B, GDT, true, PDT, UV>;
-        return launch_kernel_lds(kern, (int)a.ntiles, kAdamThreads,
-                                 lds_for_wgs_per_cu(reinterpret_cast<const void*>(kern), QB_ADAM_WGS_PER_CU), a.s,
-                                 *a.single, *a.map, *a.hs, a.tab, a.trust);
+        return launch_kernel_lds(kern, (int)a.ntiles, kAdamThreads, lds(kern), a.s, *a.single, *a.map, *a.hs, a.tab,
+                                 a.trust);
     } else {
         if (a.map) {
             constexpr auto kern = k_optim8<OPT, B, GDT, true, PDT, UV>;
-            return launch_kernel_lds(kern, (int)a.ntiles, kAdamThreads,
-                                     lds_for_wgs_per_cu(reinterpret_cast<const void*>(kern), QB_ADAM_WGS_PER_CU),
-                                     a.s, *a.single, *a.map, *a.hs, a.tab, (const float*)nullptr);
+            return launch_kernel_lds(kern, (int)a.ntiles, kAdamThreads, lds(kern), a.s, *a.single, *a.map, *a.hs,
+                                     a.tab, (const float*)nullptr);
         }
         constexpr auto kern = k_optim8<OPT, B, GDT, false, PDT, UV>;
-        return launch_kernel_lds(kern, (int)a.ntiles, kAdamThreads,
-                                 lds_for_wgs_per_cu(reinterpret_cast<const void*>(kern), QB_ADAM_WGS_PER_CU), a.s,
-                                 *a.single, TileMap<TensorDesc>{}, *a.hs, a.tab, (const float*)nullptr);
+        return launch_kernel_lds(kern, (int)a.ntiles, kAdamThreads, lds(kern), a.s, *a.single, TileMap<TensorDesc>{},
+                                 *a.hs, a.tab, (const float*)nullptr);
     }
 }
 
