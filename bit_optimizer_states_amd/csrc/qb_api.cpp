@@ -262,9 +262,9 @@ size_t layerwise_ws_layout(int32_t count, int64_t groups, void* ws, double** par
     return m + pb + round_up((size_t)count * sizeof(float), 256);
 }
 
-int64_t quant_tiles(int64_t n, int32_t B)
+int64_t quant_tiles(int64_t n, int32_t B, int bits)
 {
-    const int64_t t = quant_tile_elems(B);
+    const int64_t t = quant_tile_elems(B, bits);
     return (n + t - 1) / t;
 }
 
@@ -434,7 +434,7 @@ qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int3
     const int bits = is4(code) ? 4 : 8, c4 = is4(code) ? code4_index(code) : 0;
     if (!dq)
         return hip_status(launch_quant(QuantDesc{x, codes, absmax, nullptr, n, 0, {0, 0}}, nullptr,
-                                       quant_tiles(n, blocksize), bits, c4, blocksize, (int)xdt, false, nullptr, s));
+                                       quant_tiles(n, blocksize, bits), bits, c4, blocksize, (int)xdt, false, nullptr, s));
     // nested: bins, then the fp32 absmax, in the workspace
     unsigned long long* bins = static_cast<unsigned long long*>(dq->ws);
     float* first = reinterpret_cast<float*>(static_cast<char*>(dq->ws) + kBinBytes);
@@ -442,10 +442,10 @@ qb_status qb_quantize(const void* x, qb_dtype xdt, int64_t n, qb_code code, int3
     const QuantDesc d2{first, dq->codes, dq->absmax2, dq->offset, nb, 0, {0, 0}};
     hipError_t e = launch_clear_bins(bins, 1, s);
     if (e == hipSuccess)
-        e = launch_quant(d1, nullptr, quant_tiles(n, blocksize), bits, c4, blocksize, (int)xdt, false, bins, s);
+        e = launch_quant(d1, nullptr, quant_tiles(n, blocksize, bits), bits, c4, blocksize, (int)xdt, false, bins, s);
     if (e == hipSuccess) e = launch_dq_mean(d2, nullptr, 1, bins, s);
     if (e == hipSuccess)
-        e = launch_quant(d2, nullptr, quant_tiles(nb, dq->blocksize2), 8, 0, dq->blocksize2, QB_F32, true, nullptr, s);
+        e = launch_quant(d2, nullptr, quant_tiles(nb, dq->blocksize2, 8), 8, 0, dq->blocksize2, QB_F32, true, nullptr, s);
     return hip_status(e);
 }
 
@@ -506,11 +506,11 @@ qb_status qb_multi_tensor_quantize(const qb_quant_tensor* tensors, int32_t count
             temp += round_up((size_t)nb * sizeof(float), 256);
             t1.push_back(QuantDesc{t.x, t.codes, first, nullptr, t.n, tiles1, {0, 0}});
             t2.push_back(QuantDesc{first, t.c2, t.absmax2, t.offset, nb, tiles2, {0, 0}});
-            tiles2 += quant_tiles(nb, blocksize2);
+            tiles2 += quant_tiles(nb, blocksize2, 8);
         } else {
             t1.push_back(QuantDesc{t.x, t.codes, t.absmax, nullptr, t.n, tiles1, {0, 0}});
         }
-        tiles1 += quant_tiles(t.n, blocksize);
+        tiles1 += quant_tiles(t.n, blocksize, is4(code) ? 4 : 8);
     }
     if (t1.empty()) return QB_OK;
     if (tiles1 >= (int64_t(1) << 31)) return QB_EINVAL;
@@ -677,7 +677,7 @@ qb_status qb_quantize_code(const void* x, qb_dtype xdt, int64_t n, const void* t
     int nested = 0;
     qb_status st = check_quant_tensor(x, codes, absmax, nullptr, nullptr, nullptr, n, blocksize, 0, &nested);
     if (st != QB_OK) return st;
-    return hip_status(launch_quant_user(QuantDesc{x, codes, absmax, nullptr, n, 0, {0, 0}}, quant_tiles(n, blocksize),
+    return hip_status(launch_quant_user(QuantDesc{x, codes, absmax, nullptr, n, 0, {0, 0}}, quant_tiles(n, blocksize, 8),
                                         blocksize, (int)xdt, static_cast<const UserCode*>(table),
                                         static_cast<hipStream_t>(stream)));
 }

@@ -9,7 +9,8 @@
 // de LLM", section Etapa 1); the absmax may itself be quantized a second time
 // ("Bitsandbytes", section İç içe nicelleştirme).
 //
-// Kernel shape: one 256-thread workgroup per tile of 4096 elements, launched in
+// Kernel shape: one 256-thread workgroup per tile of 4096 elements (8192 for
+// 4-bit codes), launched in
 // tile order, so the HBM accesses of all resident workgroups form one narrow
 // moving front (measured on MI355X: a copy reaches 6.2 TB/s this way against
 // 4.6 TB/s for a persistent grid-stride loop).  A tile is R sub-tiles of
@@ -50,7 +51,7 @@ struct QGeo {
     static constexpr int BPS = kThreads / LPB;                        // blocks per sub-tile
     static constexpr int CH = EPT / CW;                               // chunks per thread
     static constexpr int SUB = kThreads * EPT;                        // elements per sub-tile
-    static constexpr int ELEMS = (int)quant_tile_elems(B);            // elements per tile
+    static constexpr int ELEMS = (int)quant_tile_elems(B, BITS);      // elements per tile
     static constexpr int R = ELEMS / SUB;                             // sub-tiles per tile
     static constexpr int WPB = LPB > 64 ? LPB / 64 : 1;               // waves per block
     static_assert(R >= 1 && ELEMS == SUB * R && EPT % CW == 0 && LPB <= kThreads, "quantize tile geometry");
